@@ -1,0 +1,222 @@
+"""Benchmark: Mamba-2 SSD forward tokens/s on one MI355X, with the roofline of
+the dominant kernel and the fp64 oracle timed on the host as a CPU baseline.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--mma bf16|f32]
+
+One step = one ssd_forward call (cumsum -> chunk states -> state passing ->
+fused chunk output) over one batch of the workload, inputs resident in HBM.
+Per-kernel durations come from HIP events recorded on the launch stream around
+each ABI call of the same pipeline (a second timed loop).  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+
+def algorithmic_costs(w, in_bytes, y_bytes):
+    """Algorithmic bytes and flops per launch of each kernel (each tensor read
+    or written once; causal interaction terms only; C.B^T once per group)."""
+    B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    nc = L // Q
+    blh = B * L * H
+    st = B * nc * H * N * P
+    k = {}
+    k["chunk_cumsum"] = dict(bytes=4 * blh + 4 * H + 2 * 4 * blh, flops=2 * blh)
+    k["chunk_state"] = dict(bytes=in_bytes * blh * P + in_bytes * B * L * G * N + 2 * 4 * blh + 4 * st,
+                            flops=2 * blh * N * P)
+    k["state_passing"] = dict(bytes=4 * st + 4 * B * H * nc + 4 * st + 4 * B * H * N * P,
+                              flops=2 * st)
+    k["chunk_scan"] = dict(bytes=in_bytes * blh * P + 2 * in_bytes * B * L * G * N + 2 * 4 * blh + 4 * st
+                           + 4 * H + y_bytes * blh * P,
+                           flops=2 * blh * N * P + B * nc * H * Q * (Q + 1) * P + B * nc * G * Q * (Q + 1) * N)
+    return k
+
+
+def cpu_baseline(inp, w, target_s=10.0):
+    """The fp64 oracle on a bounded sample of (b, h) pairs, all host cores."""
+    import numpy as np
+    from oracle import oracle as oracle_mod
+    o = oracle_mod.get()
+    threads = oracle_mod.default_threads()
+    total_pairs = w.batch * w.nheads
+    t0 = time.perf_counter()
+    o.recurrence(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D, pairs=[0], nthreads=1)
+    t1 = time.perf_counter() - t0
+    per_thread = max(1, int(target_s / max(t1, 1e-3)))
+    k = int(min(total_pairs, threads * per_thread))
+    pairs = np.linspace(0, total_pairs - 1, k).round().astype(np.int64)
+    used = min(threads, k)
+    t0 = time.perf_counter()
+    o.recurrence(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D, pairs=pairs, nthreads=used)
+    t = time.perf_counter() - t0
+    tokens_per_s = w.tokens * (k / total_pairs) / t
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{k} of {total_pairs} (batch, head) pairs over the full sequence of the {w.name} "
+                      f"workload in {t:.2f} s; tokens/s scaled by the sampled fraction"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--mma", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-only", default=None,
+                    help="time only this ABI call in the per-kernel loop (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the path has no "
+              "multi-GPU mode to measure", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mamba_ssd_scan_chunk_amd import ops
+    from mamba_ssd_scan_chunk_amd._lib import LIB_PATH
+    from mamba_ssd_scan_chunk_amd.inputs import HEADLINE, WORKLOADS, workload_inputs
+
+    if not os.path.exists(LIB_PATH):
+        from mamba_ssd_scan_chunk_amd import build as hip_build
+        hip_build.build()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    inp = workload_inputs(name)
+    t = inp.to_torch("cuda")
+    sh = ops.shape_of(t, w.chunk)
+    dev = t["x"].device
+    in_bytes = 2 if w.in_dtype == "bf16" else 4
+    y_dtype = w.in_dtype if args.mma == "bf16" else "f32"
+    y_bytes = 2 if y_dtype == "bf16" else 4
+    B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    nc = L // Q
+    y = torch.empty((B, L, H, P), device=dev, dtype=torch.bfloat16 if y_dtype == "bf16" else torch.float32)
+    fin = torch.empty((B, H, N, P), device=dev, dtype=torch.float32)
+    ws = torch.empty(ops.ssd_workspace_bytes(sh), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ops.ssd_forward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], y=y, final_states=fin,
+                        workspace=ws, mma=args.mma)
+
+    # ---- phase 1: whole-path throughput
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    tokens_per_s = w.tokens / (ms_per_step / 1e3)
+
+    # ---- phase 2: per-kernel durations (same pipeline, events on the launch stream)
+    dA = torch.empty((B, H, nc, Q), device=dev, dtype=torch.float32)
+    dtb = torch.empty_like(dA)
+    states = torch.empty((B, nc, H, N, P), device=dev, dtype=torch.float32)
+    calls = {
+        "chunk_cumsum": lambda: ops.ssd_chunk_cumsum(sh, t["dt"], t["A"], dA_cumsum=dA, dt_bhl=dtb),
+        "chunk_state": lambda: ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, states=states, mma=args.mma),
+        "state_passing": lambda: ops.ssd_state_passing(sh, states, dA, carried=states, final_states=fin),
+        "chunk_scan": lambda: ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, states, t["D"], y=y,
+                                                 mma=args.mma),
+    }
+    order = list(calls) if args.kernel_only is None else [args.kernel_only]
+    for _ in range(2):
+        for k in calls:
+            calls[k]()
+    torch.cuda.synchronize()
+    evs = {k: [] for k in order}
+    for _ in range(args.steps):
+        for k in calls:
+            if k in evs:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                calls[k]()
+                b.record(stream)
+                evs[k].append((a, b))
+            else:
+                calls[k]()
+    torch.cuda.synchronize()
+    costs = algorithmic_costs(w, in_bytes, y_bytes)
+    kernels = {}
+    for k, pairs in evs.items():
+        us = 1e3 * sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+        c = costs[k]
+        gbps = c["bytes"] / (us * 1e-6) / 1e9
+        tflops = c["flops"] / (us * 1e-6) / 1e12
+        peak_t = MFMA_PEAK_TFLOPS[args.mma]
+        ai = c["flops"] / c["bytes"]
+        roof_t = min(peak_t, ai * HBM_PEAK_GBPS / 1e3)
+        kernels[k] = {"us": round(us, 2), "alg_bytes": c["bytes"], "alg_flops": c["flops"],
+                      "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                      "TFLOPs": round(tflops, 2), "mfma_peak_frac": round(tflops / peak_t, 4),
+                      "frac_of_roof": round(tflops / roof_t, 4)}
+    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    dk = kernels[dom]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(dk["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None}
+
+    # plain device copy of 1 GiB as the practical HBM ceiling
+    src = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    flops_total = sum(costs[k]["flops"] for k in costs)
+    out = {
+        "metric": "Mamba-2 SSD fwd tokens/s (2.7B-layer shape) + % MFMA / HBM roofline",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if args.mma == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: B={B} L={L} H={H} P={P} N={N} G={G} Q={Q}", "batch": B, "seqlen": L,
+                   "nheads": H, "headdim": P, "dstate": N, "ngroups": G, "chunk": Q, "in_dtype": w.in_dtype,
+                   "y_dtype": y_dtype, "mma": args.mma, "parallelism": "single GPU"},
+        "effective_TFLOPs": round(flops_total / (ms_per_step * 1e-3) / 1e12, 2),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+        "copy_GBps": round(copy_gbps, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

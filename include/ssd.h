@@ -1,0 +1,161 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 chunked-SSD forward.
+ *
+ * Pages cited (by title):
+ *   P1 = "Jane Street ML Engineers Map Mamba-2 Recurrent State Computation to
+ *         Tensor Cores with cuTile" (disconfirmai.com digest of the NVIDIA
+ *         Developer Blog post on Mamba-2 forward kernels in cuTile).
+ *   P3 = "Jane Street and NVIDIA optimize three Mamba-2 forward-pass kernels in
+ *         cuTile" (genainews.tech).
+ *
+ * The operation.  Per batch b and head h, with group g = h / (H/G), the state
+ * h_t (N x P) and output y_t (P) follow
+ *     h_t = exp(dt[b,t,h] A[h]) h_{t-1} + dt[b,t,h] B[b,t,g,:] x[b,t,h,:]^T
+ *     y_t = C[b,t,g,:]^T h_t + D[h] x[b,t,h,:]
+ * evaluated chunk by chunk (chunk length Q, nc = L/Q chunks) in the three
+ * steps P1 describes in its paragraph on the three kernels: a log-space
+ * cumulative sum of the decay term, the jump-formula state advance across
+ * chunks, and the fused output (carried-state term, decayed causally masked
+ * C.B^T interaction applied to x, skip connection).  The state advance is
+ * exported as two calls here: the per-chunk states (parallel over chunks) and
+ * the sequential pass that carries them across chunks.
+ *
+ * Conventions for every call:
+ *   - Every tensor pointer is a DEVICE pointer to dense row-major memory,
+ *     16-byte aligned.  The caller owns all memory; the library allocates
+ *     nothing, keeps no mutable global state and is safe to call from several
+ *     host threads.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Calls are asynchronous: they enqueue kernels and return without
+ *     synchronising.  Buffers must stay valid until the stream reaches them.
+ *   - Every argument check runs on the host BEFORE any HIP call; a failed
+ *     check returns its status and enqueues nothing.  A launch failure is
+ *     reported as SSD_ERR_HIP.  Values are not validated: NaN/Inf propagate.
+ *   - dt, A, D, dA_cumsum, dt_bhl and all states are float32.  x, B and C
+ *     share one input dtype `in` (F32 or BF16).
+ *   - Shape limits of this version (else SSD_ERR_UNSUPPORTED): headdim P and
+ *     dstate N multiples of 16 with N <= 256 and P <= 256; chunk Q in
+ *     {32, 64, 128, 256}; seqlen L a multiple of Q.
+ *
+ * Precision modes (ssd_mma): SSD_MMA_BF16 rounds the matrix-core operands
+ * (the decay-scaled x rows, the decayed interaction tile, the carried state)
+ * to bfloat16, round-to-nearest-even, and accumulates in float32;
+ * SSD_MMA_F32 keeps every operand in float32 (fp32 matrix instructions).
+ */
+#ifndef MAMBA_SSD_H
+#define MAMBA_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_NULL = 1,         /* a required pointer is NULL */
+  SSD_ERR_SHAPE = 2,        /* a size is <= 0, or nheads % ngroups != 0 */
+  SSD_ERR_DTYPE = 3,        /* unknown dtype / mma enum value */
+  SSD_ERR_UNSUPPORTED = 4,  /* valid shape outside this version's limits */
+  SSD_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than ssd_workspace_bytes */
+  SSD_ERR_ALIGN = 6,        /* a pointer is not 16-byte aligned */
+  SSD_ERR_HIP = 7           /* a kernel launch failed */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+typedef enum { SSD_MMA_BF16 = 0, SSD_MMA_F32 = 1 } ssd_mma;
+
+/* B, L, H, P, N, G, Q in the notation above. */
+typedef struct {
+  int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+} ssd_shape;
+
+/*
+ * Log-space decay cumulative sum (P1, paragraph on the three kernels: per
+ * token and per head, the running sum of the decay term inside each chunk;
+ * P1, Blackwell-optimisation paragraph and P3: stored token-contiguous per
+ * (batch, head)).
+ *   dA_cumsum[b,h,c,i] = sum_{k<=i} dt[b,cQ+k,h] * A[h]   (inclusive, fp32)
+ *   dt_bhl[b,h,c,i]    = dt[b,cQ+i,h]                      (optional: NULL skips it)
+ * dt [B,L,H], A [H]  ->  dA_cumsum, dt_bhl [B,H,nc,Q].
+ */
+ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const float* dt, const float* A,
+                            float* dA_cumsum, float* dt_bhl, void* stream);
+
+/*
+ * Per-chunk states by the jump formula with decay (P1, jump-formula
+ * paragraph: with stacked b and x rows the state advance over a chunk is one
+ * matrix product, and pre-multiplying rows by exponentials of the log-space
+ * sums keeps that form):
+ *   states[b,c,h] = sum_{j<Q} exp(G_{Q-1} - G_j) dt_j B_j x_j^T    (N x P)
+ * with G = dA_cumsum[b,h,c,:], dt_j = dt_bhl[b,h,c,j].
+ * x [B,L,H,P], Bm [B,L,G,N] (dtype `in`)  ->  states [B,nc,H,N,P] fp32.
+ */
+ssd_status ssd_chunk_state(const ssd_shape* shape, const void* x, const void* Bm, ssd_dtype in,
+                           const float* dt_bhl, const float* dA_cumsum, float* states,
+                           ssd_mma mma, void* stream);
+
+/*
+ * Inter-chunk state advance (P1, paragraph on the three kernels: a sequential
+ * loop over chunks advancing the hidden state).  Per (b,h):
+ *   run = initial_states[b,h] (zeros when NULL)
+ *   for c in 0..nc-1:  carried[b,c,h] = run;  run = exp(G_{Q-1}(c)) run + chunk_states[b,c,h]
+ *   final_states[b,h] = run
+ * carried may equal chunk_states (in place).  chunk_states, carried
+ * [B,nc,H,N,P]; initial_states, final_states [B,H,N,P]; all fp32.
+ */
+ssd_status ssd_state_passing(const ssd_shape* shape, const float* chunk_states, float* carried,
+                             const float* dA_cumsum, const float* initial_states,
+                             float* final_states, void* stream);
+
+/*
+ * Fused chunk output (P1, compute_out paragraph: carried-state term, decayed
+ * and causally masked interaction matrix C.B^T, skip connection, in one
+ * kernel with the interaction tile kept on chip and the mask applied as a
+ * register-level select).  For token i of chunk c (t = cQ+i):
+ *   y[b,t,h,:] = exp(G_i) C_i^T carried[b,c,h]
+ *              + sum_{j<=i} (C_i . B_j) exp(G_i - G_j) dt_j x[b,cQ+j,h,:]
+ *              + D[h] x[b,t,h,:]
+ * x [B,L,H,P], Bm/Cm [B,L,G,N] (dtype `in`), carried [B,nc,H,N,P] fp32,
+ * D [H] fp32  ->  y [B,L,H,P] in `y_dtype` (F32 or BF16, rounded to nearest even).
+ */
+ssd_status ssd_chunk_scan(const ssd_shape* shape, const void* x, const void* Bm, const void* Cm,
+                          ssd_dtype in, const float* dt_bhl, const float* dA_cumsum,
+                          const float* carried, const float* D, void* y, ssd_dtype y_dtype,
+                          ssd_mma mma, void* stream);
+
+/*
+ * Bytes of device workspace ssd_forward needs for `shape` (dA_cumsum, dt_bhl
+ * and the chunk states, each 256-byte aligned).  Returns 0 for an invalid or
+ * NULL shape.  Pure host computation.
+ */
+size_t ssd_workspace_bytes(const ssd_shape* shape);
+
+/*
+ * One-call forward: ssd_chunk_cumsum -> ssd_chunk_state -> ssd_state_passing
+ * (in place) -> ssd_chunk_scan on one stream, no host synchronisation.
+ * initial_states [B,H,N,P] may be NULL (zeros); final_states [B,H,N,P] may be
+ * NULL (not written).  workspace: device memory of at least
+ * ssd_workspace_bytes(shape) bytes, owned by the caller, contents undefined
+ * after the call.
+ */
+ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+                       const void* Bm, const void* Cm, const float* D, ssd_dtype in,
+                       const float* initial_states, void* y, ssd_dtype y_dtype,
+                       float* final_states, void* workspace, size_t workspace_bytes,
+                       ssd_mma mma, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* ssd_status_string(ssd_status status);
+
+/* SSD_ABI_VERSION of the built library. */
+int ssd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SSD_H */

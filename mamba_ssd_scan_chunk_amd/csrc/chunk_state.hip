@@ -1,0 +1,203 @@
+// chunk_state.hip -- per-chunk states by the decayed jump formula, on MFMA.
+//
+// Page: "Jane Street ML Engineers Map Mamba-2 Recurrent State Computation to
+// Tensor Cores with cuTile" (disconfirmai.com), jump-formula paragraph: with
+// the b and x vectors of a chunk stacked as matrices, the state advance over
+// the chunk is one matrix product, and pre-multiplying rows by exponentials
+// of the log-space sums keeps it one.  For chunk c of (b, h):
+//     S[n][p] = sum_j B[j][n] * w_j * x[j][p],   w_j = exp(G_{Q-1} - G_j) dt_j
+// The decay weight is folded into the x rows (not the B rows) so that the B
+// tile stays the raw input shared by every head of a group; in exact
+// arithmetic the two placements are the same product.
+//
+// Work split: one 256-thread block per (b, c, h, 16/32/64-column slice of P).
+// The contraction runs over the chunk's tokens in steps of 32.  Both operands
+// arrive token-major from HBM, while an MFMA fragment needs 8 consecutive
+// contraction slots per lane, so each step stages them through LDS
+// transposed: a thread loads an 8-token x 8-column block with 16-byte loads,
+// transposes it in registers (scaling the x rows by w_j on the way, in fp32,
+// then rounding to the operand type) and writes 8 16-byte rows of the
+// K-contiguous tiles Bt[n][j] and Xt[p][j].  Wave w then owns output row
+// tiles n = 16*(w + 4*i) and all column tiles of the slice.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+constexpr int kCsThreadsState = 256;
+constexpr int kStateKS = 32;  // tokens per contraction step
+
+template <class Op>
+struct StateCfg {
+  using E = typename OpElem<Op>::type;
+  // LDS row pitch (elements) of the K-contiguous tiles; keeps rows 16-byte
+  // aligned and spreads the 16 rows one fragment read touches over distinct
+  // banks.
+  static constexpr int KP = kStateKS + (Op::kBytes == 2 ? 8 : 4);
+};
+
+template <class Op, int RW, int CT>
+__global__ __launch_bounds__(kCsThreadsState) void chunk_state_kernel(
+    const void* __restrict__ x, const void* __restrict__ Bm, int in_bf16, const float* __restrict__ dt_bhl,
+    const float* __restrict__ dA_cumsum, float* __restrict__ states, int L, int H, int P, int N, int G, int Q,
+    int nc) {
+  using E = typename OpElem<Op>::type;
+  using Frag = typename Op::Frag;
+  constexpr int PT = CT * 16;
+  constexpr int KP = StateCfg<Op>::KP;
+  extern __shared__ __align__(16) unsigned char st_smem[];
+  E* Bt = reinterpret_cast<E*>(st_smem);    // [N][KP]
+  E* Xt = Bt + (size_t)N * KP;               // [PT][KP]
+  float* w_s = reinterpret_cast<float*>(Xt + PT * KP);  // [Q]
+
+  const int npt = P / PT;
+  const int h = blockIdx.x / npt, pt = blockIdx.x - (blockIdx.x / npt) * npt;
+  const int c = blockIdx.y, b = blockIdx.z;
+  const int g = h / (H / G);
+  const int p0 = pt * PT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const bool bf = in_bf16 != 0;
+
+  const int64_t bhc = ((int64_t)b * H + h) * nc + c;
+  const float* Gc = dA_cumsum + bhc * Q;
+  const float* dtc = dt_bhl + bhc * Q;
+  const float glast = Gc[Q - 1];
+  for (int j = tid; j < Q; j += kCsThreadsState) w_s[j] = fast_exp(glast - Gc[j]) * dtc[j];
+
+  f32x4_t acc[RW][CT];
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[i][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int NT = N / 16;
+  const int64_t tok0 = (int64_t)b * L + (int64_t)c * Q;
+  const int nbB = (kStateKS / 8) * (N / 8);
+  const int nbX = (kStateKS / 8) * (PT / 8);
+
+  for (int k0 = 0; k0 < Q; k0 += kStateKS) {
+    __syncthreads();  // previous step's fragment reads are done; w_s is visible
+    for (int blk = tid; blk < nbB + nbX; blk += kCsThreadsState) {
+      float v[8][8];
+      if (blk < nbB) {
+        const int jb = blk & 3, cb = blk >> 2;
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          load8_as_f32(Bm, ((tok0 + k0 + 8 * jb + r) * G + g) * N + 8 * cb, bf, v[r]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          float col[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) col[r] = v[r][q];
+          Lds<Op>::store8(Bt + (8 * cb + q) * KP + 8 * jb, col);
+        }
+      } else {
+        const int bx = blk - nbB;
+        const int jb = bx & 3, cb = bx >> 2;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          load8_as_f32(x, ((tok0 + k0 + 8 * jb + r) * H + h) * P + p0 + 8 * cb, bf, v[r]);
+          const float w = w_s[k0 + 8 * jb + r];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[r][q] *= w;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          float col[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) col[r] = v[r][q];
+          Lds<Op>::store8(Xt + (8 * cb + q) * KP + 8 * jb, col);
+        }
+      }
+    }
+    __syncthreads();
+
+    Frag bfr[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) bfr[ct] = Lds<Op>::load8(Xt + (16 * ct + l16) * KP + 8 * lg);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int rt = wave + 4 * i;
+      if (rt < NT) {
+        const Frag afr = Lds<Op>::load8(Bt + (16 * rt + l16) * KP + 8 * lg);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[i][ct] = Op::mma(afr, bfr[ct], acc[i][ct]);
+      }
+    }
+  }
+
+  float* so = states + (((int64_t)b * nc + c) * H + h) * (int64_t)N * P;
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int rt = wave + 4 * i;
+    if (rt < NT) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          so[(int64_t)(16 * rt + 4 * lg + r) * P + p0 + 16 * ct + l16] = acc[i][ct][r];
+    }
+  }
+}
+
+static int state_ct(int64_t P) { return (P % 64 == 0) ? 4 : (P % 32 == 0) ? 2 : 1; }
+static int state_rw(int64_t N) {
+  const int64_t nt = N / 16;
+  const int64_t rw = (nt + 3) / 4;
+  return rw <= 1 ? 1 : rw <= 2 ? 2 : 4;
+}
+
+size_t chunk_state_lds_bytes(const Dims& d, bool f32_mma) {
+  const int PT = 16 * state_ct(d.P);
+  const size_t eb = f32_mma ? 4 : 2;
+  const size_t KP = f32_mma ? StateCfg<OpF32>::KP : StateCfg<OpBF16>::KP;
+  return eb * KP * (size_t)(d.N + PT) + sizeof(float) * (size_t)d.Q;
+}
+
+template <class Op, int RW, int CT>
+static hipError_t launch_state_inst(const Dims& d, const void* x, const void* Bm, bool in_bf16,
+                                    const float* dt_bhl, const float* dA_cumsum, float* states,
+                                    hipStream_t stream, size_t lds) {
+  auto kern = chunk_state_kernel<Op, RW, CT>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)(d.H * (d.P / (16 * CT))), (unsigned)d.nc, (unsigned)d.B);
+  hipLaunchKernelGGL(kern, grid, dim3(kCsThreadsState), lds, stream, x, Bm, (int)in_bf16, dt_bhl, dA_cumsum,
+                     states, (int)d.L, (int)d.H, (int)d.P, (int)d.N, (int)d.G, (int)d.Q, (int)d.nc);
+  return hipGetLastError();
+}
+
+template <class Op, int RW>
+static hipError_t launch_state_ct(const Dims& d, const void* x, const void* Bm, bool in_bf16,
+                                  const float* dt_bhl, const float* dA_cumsum, float* states,
+                                  hipStream_t stream, size_t lds) {
+  switch (state_ct(d.P)) {
+    case 4: return launch_state_inst<Op, RW, 4>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
+    case 2: return launch_state_inst<Op, RW, 2>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
+    default: return launch_state_inst<Op, RW, 1>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
+  }
+}
+
+template <class Op>
+static hipError_t launch_state_op(const Dims& d, const void* x, const void* Bm, bool in_bf16,
+                                  const float* dt_bhl, const float* dA_cumsum, float* states,
+                                  hipStream_t stream, size_t lds) {
+  switch (state_rw(d.N)) {
+    case 1: return launch_state_ct<Op, 1>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
+    case 2: return launch_state_ct<Op, 2>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
+    default: return launch_state_ct<Op, 4>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
+  }
+}
+
+hipError_t launch_chunk_state(const Dims& d, const void* x, const void* Bm, bool in_bf16,
+                              const float* dt_bhl, const float* dA_cumsum, float* states,
+                              bool f32_mma, hipStream_t stream) {
+  const size_t lds = chunk_state_lds_bytes(d, f32_mma);
+  if (f32_mma) return launch_state_op<OpF32>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
+  return launch_state_op<OpBF16>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
+}
+
+}  // namespace ssd

@@ -1,0 +1,207 @@
+// ssd_api.cpp -- the C ABI declared in include/ssd.h: argument validation
+// (host only, before any HIP call), workspace carving and kernel dispatch.
+#include "ssd.h"
+
+#include <hip/hip_runtime.h>
+
+#include "ssd_launch.hpp"
+
+namespace {
+
+using ssd::Dims;
+
+constexpr size_t kLdsLimit = 160 * 1024;  // gfx950 LDS per workgroup
+constexpr size_t kWsAlign = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Shape checks shared by every call.  Returns SSD_OK and fills `d`.
+ssd_status check_shape(const ssd_shape* s, Dims* d) {
+  if (!s) return SSD_ERR_NULL;
+  if (s->batch <= 0 || s->seqlen <= 0 || s->nheads <= 0 || s->headdim <= 0 || s->dstate <= 0 ||
+      s->ngroups <= 0 || s->chunk <= 0)
+    return SSD_ERR_SHAPE;
+  if (s->nheads % s->ngroups != 0) return SSD_ERR_SHAPE;
+  if (s->headdim % 16 != 0 || s->dstate % 16 != 0 || s->headdim > 256 || s->dstate > 256)
+    return SSD_ERR_UNSUPPORTED;
+  if (s->chunk != 32 && s->chunk != 64 && s->chunk != 128 && s->chunk != 256) return SSD_ERR_UNSUPPORTED;
+  if (s->seqlen % s->chunk != 0) return SSD_ERR_UNSUPPORTED;
+  // keep every element offset comfortably inside 32-bit grid dimensions
+  if (s->seqlen / s->chunk > 65535 || s->batch > 65535 || s->nheads > 65535) return SSD_ERR_UNSUPPORTED;
+  d->B = s->batch; d->L = s->seqlen; d->H = s->nheads; d->P = s->headdim;
+  d->N = s->dstate; d->G = s->ngroups; d->Q = s->chunk; d->nc = s->seqlen / s->chunk;
+  return SSD_OK;
+}
+
+ssd_status check_dtype(ssd_dtype t) { return (t == SSD_F32 || t == SSD_BF16) ? SSD_OK : SSD_ERR_DTYPE; }
+ssd_status check_mma(ssd_mma m) { return (m == SSD_MMA_BF16 || m == SSD_MMA_F32) ? SSD_OK : SSD_ERR_DTYPE; }
+
+ssd_status from_hip(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+#define SSD_TRY(expr)                  \
+  do {                                 \
+    const ssd_status st_ = (expr);     \
+    if (st_ != SSD_OK) return st_;     \
+  } while (0)
+
+ssd_status validate_cumsum(const ssd_shape* shape, const float* dt, const float* A, float* dA_cumsum,
+                           float* dt_bhl, Dims* d) {
+  SSD_TRY(check_shape(shape, d));
+  if (!dt || !A || !dA_cumsum) return SSD_ERR_NULL;
+  if (!aligned16(dt) || !aligned16(A) || !aligned16(dA_cumsum) || (dt_bhl && !aligned16(dt_bhl)))
+    return SSD_ERR_ALIGN;
+  return SSD_OK;
+}
+
+ssd_status validate_state(const ssd_shape* shape, const void* x, const void* Bm, ssd_dtype in,
+                          const float* dt_bhl, const float* dA_cumsum, float* states, ssd_mma mma, Dims* d) {
+  SSD_TRY(check_shape(shape, d));
+  SSD_TRY(check_dtype(in));
+  SSD_TRY(check_mma(mma));
+  if (!x || !Bm || !dt_bhl || !dA_cumsum || !states) return SSD_ERR_NULL;
+  if (!aligned16(x) || !aligned16(Bm) || !aligned16(dt_bhl) || !aligned16(dA_cumsum) || !aligned16(states))
+    return SSD_ERR_ALIGN;
+  if (ssd::chunk_state_lds_bytes(*d, mma == SSD_MMA_F32) > kLdsLimit) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+ssd_status validate_passing(const ssd_shape* shape, const float* chunk_states, float* carried,
+                            const float* dA_cumsum, const float* initial_states, float* final_states, Dims* d) {
+  SSD_TRY(check_shape(shape, d));
+  if (!chunk_states || !carried || !dA_cumsum) return SSD_ERR_NULL;
+  if (!aligned16(chunk_states) || !aligned16(carried) || !aligned16(dA_cumsum) ||
+      (initial_states && !aligned16(initial_states)) || (final_states && !aligned16(final_states)))
+    return SSD_ERR_ALIGN;
+  return SSD_OK;
+}
+
+ssd_status validate_scan(const ssd_shape* shape, const void* x, const void* Bm, const void* Cm, ssd_dtype in,
+                         const float* dt_bhl, const float* dA_cumsum, const float* carried, const float* D,
+                         void* y, ssd_dtype y_dtype, ssd_mma mma, Dims* d) {
+  SSD_TRY(check_shape(shape, d));
+  SSD_TRY(check_dtype(in));
+  SSD_TRY(check_dtype(y_dtype));
+  SSD_TRY(check_mma(mma));
+  if (!x || !Bm || !Cm || !dt_bhl || !dA_cumsum || !carried || !D || !y) return SSD_ERR_NULL;
+  if (!aligned16(x) || !aligned16(Bm) || !aligned16(Cm) || !aligned16(dt_bhl) || !aligned16(dA_cumsum) ||
+      !aligned16(carried) || !aligned16(D) || !aligned16(y))
+    return SSD_ERR_ALIGN;
+  if (ssd::chunk_scan_lds_bytes(*d, mma == SSD_MMA_F32) > kLdsLimit) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+struct WsLayout {
+  size_t dA_off, dt_off, st_off, total;
+};
+
+WsLayout workspace_layout(const Dims& d) {
+  WsLayout w;
+  const size_t bhl = sizeof(float) * (size_t)(d.B * d.H * d.nc * d.Q);
+  const size_t st = sizeof(float) * (size_t)(d.B * d.nc * d.H) * (size_t)(d.N * d.P);
+  w.dA_off = 0;
+  w.dt_off = round_up(w.dA_off + bhl, kWsAlign);
+  w.st_off = round_up(w.dt_off + bhl, kWsAlign);
+  w.total = round_up(w.st_off + st, kWsAlign);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const float* dt, const float* A, float* dA_cumsum,
+                            float* dt_bhl, void* stream) {
+  Dims d;
+  SSD_TRY(validate_cumsum(shape, dt, A, dA_cumsum, dt_bhl, &d));
+  return from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA_cumsum, dt_bhl, (hipStream_t)stream));
+}
+
+ssd_status ssd_chunk_state(const ssd_shape* shape, const void* x, const void* Bm, ssd_dtype in,
+                           const float* dt_bhl, const float* dA_cumsum, float* states, ssd_mma mma,
+                           void* stream) {
+  Dims d;
+  SSD_TRY(validate_state(shape, x, Bm, in, dt_bhl, dA_cumsum, states, mma, &d));
+  return from_hip(ssd::launch_chunk_state(d, x, Bm, in == SSD_BF16, dt_bhl, dA_cumsum, states,
+                                          mma == SSD_MMA_F32, (hipStream_t)stream));
+}
+
+ssd_status ssd_state_passing(const ssd_shape* shape, const float* chunk_states, float* carried,
+                             const float* dA_cumsum, const float* initial_states, float* final_states,
+                             void* stream) {
+  Dims d;
+  SSD_TRY(validate_passing(shape, chunk_states, carried, dA_cumsum, initial_states, final_states, &d));
+  return from_hip(ssd::launch_state_passing(d, chunk_states, carried, dA_cumsum, initial_states, final_states,
+                                            (hipStream_t)stream));
+}
+
+ssd_status ssd_chunk_scan(const ssd_shape* shape, const void* x, const void* Bm, const void* Cm, ssd_dtype in,
+                          const float* dt_bhl, const float* dA_cumsum, const float* carried, const float* D,
+                          void* y, ssd_dtype y_dtype, ssd_mma mma, void* stream) {
+  Dims d;
+  SSD_TRY(validate_scan(shape, x, Bm, Cm, in, dt_bhl, dA_cumsum, carried, D, y, y_dtype, mma, &d));
+  return from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, in == SSD_BF16, dt_bhl, dA_cumsum, carried, D, y,
+                                         y_dtype == SSD_BF16, mma == SSD_MMA_F32, (hipStream_t)stream));
+}
+
+size_t ssd_workspace_bytes(const ssd_shape* shape) {
+  Dims d;
+  if (check_shape(shape, &d) != SSD_OK) return 0;
+  return workspace_layout(d).total;
+}
+
+ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* Bm,
+                       const void* Cm, const float* D, ssd_dtype in, const float* initial_states, void* y,
+                       ssd_dtype y_dtype, float* final_states, void* workspace, size_t workspace_bytes,
+                       ssd_mma mma, void* stream) {
+  Dims d;
+  SSD_TRY(check_shape(shape, &d));
+  SSD_TRY(check_dtype(in));
+  SSD_TRY(check_dtype(y_dtype));
+  SSD_TRY(check_mma(mma));
+  if (!x || !dt || !A || !Bm || !Cm || !D || !y) return SSD_ERR_NULL;
+  if (!workspace) return SSD_ERR_WORKSPACE;
+  const WsLayout ws = workspace_layout(d);
+  if (workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(Bm) || !aligned16(Cm) || !aligned16(D) ||
+      !aligned16(y) || !aligned16(workspace) || (initial_states && !aligned16(initial_states)) ||
+      (final_states && !aligned16(final_states)))
+    return SSD_ERR_ALIGN;
+  if (ssd::chunk_state_lds_bytes(d, mma == SSD_MMA_F32) > kLdsLimit ||
+      ssd::chunk_scan_lds_bytes(d, mma == SSD_MMA_F32) > kLdsLimit)
+    return SSD_ERR_UNSUPPORTED;
+
+  char* base = static_cast<char*>(workspace);
+  float* dA = reinterpret_cast<float*>(base + ws.dA_off);
+  float* dtb = reinterpret_cast<float*>(base + ws.dt_off);
+  float* st = reinterpret_cast<float*>(base + ws.st_off);
+  const hipStream_t s = (hipStream_t)stream;
+  const bool bf = in == SSD_BF16, f32m = mma == SSD_MMA_F32;
+
+  SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
+  SSD_TRY(from_hip(ssd::launch_chunk_state(d, x, Bm, bf, dtb, dA, st, f32m, s)));
+  SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dA, initial_states, final_states, s)));
+  SSD_TRY(from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, D, y, y_dtype == SSD_BF16, f32m, s)));
+  return SSD_OK;
+}
+
+const char* ssd_status_string(ssd_status status) {
+  switch (status) {
+    case SSD_OK: return "SSD_OK: success";
+    case SSD_ERR_NULL: return "SSD_ERR_NULL: a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: a size is not positive or nheads is not a multiple of ngroups";
+    case SSD_ERR_DTYPE: return "SSD_ERR_DTYPE: unknown dtype or mma mode";
+    case SSD_ERR_UNSUPPORTED:
+      return "SSD_ERR_UNSUPPORTED: shape outside this version's limits (P, N multiples of 16 and <= 256; "
+             "chunk in {32,64,128,256}; seqlen a multiple of chunk)";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or smaller than ssd_workspace_bytes";
+    case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP kernel launch failed";
+  }
+  return "unknown ssd_status";
+}
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// ssd_launch.hpp -- host-side launchers of the gfx950 SSD kernels.
+// Shapes are validated by the C ABI layer (ssd_api.cpp) before any of these
+// is called; each launcher only picks the kernel instance, sets its LDS size
+// and enqueues it on `stream`, returning the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct Dims {
+  int64_t B, L, H, P, N, G, Q, nc;
+};
+
+// Dynamic LDS bytes each kernel needs for the given shape (0 = unsupported).
+size_t chunk_state_lds_bytes(const Dims& d, bool f32_mma);
+size_t chunk_scan_lds_bytes(const Dims& d, bool f32_mma);
+
+hipError_t launch_chunk_cumsum(const Dims& d, const float* dt, const float* A, float* dA_cumsum,
+                               float* dt_bhl, hipStream_t stream);
+
+hipError_t launch_chunk_state(const Dims& d, const void* x, const void* Bm, bool in_bf16,
+                              const float* dt_bhl, const float* dA_cumsum, float* states,
+                              bool f32_mma, hipStream_t stream);
+
+hipError_t launch_state_passing(const Dims& d, const float* chunk_states, float* carried,
+                                const float* dA_cumsum, const float* initial_states,
+                                float* final_states, hipStream_t stream);
+
+hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
+                             const float* dt_bhl, const float* dA_cumsum, const float* carried,
+                             const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream);
+
+}  // namespace ssd

@@ -1,0 +1,86 @@
+// state_passing.hip -- inter-chunk state advance, an HBM-bound elementwise scan.
+//
+// Page: "Jane Street ML Engineers Map Mamba-2 Recurrent State Computation to
+// Tensor Cores with cuTile" (disconfirmai.com), paragraph on the three kernels
+// (a sequential loop over chunks carries the hidden state forward) and the
+// jump-formula paragraph (each chunk adds its own state to the decayed
+// previous one).  Per (b, h) and state element e:
+//     run = h0[b,h,e] (or 0)
+//     for c:  carried[b,c,h,e] = run;  run = exp(G_last(b,h,c)) * run + S[b,c,h,e]
+//     final[b,h,e] = run
+//
+// One thread owns 4 consecutive state elements (one float4).  Consecutive
+// threads own consecutive float4s of the same (b, h), so every load and store
+// is a fully coalesced 1 KB wave access.  The chain over chunks is serial per
+// thread, but the S loads do not depend on it: the loop is unrolled by 8 with
+// all 8 loads issued before the 8 dependent updates, keeping 8 x 16 B per
+// thread in flight.  carried may alias S: each location is read before it is
+// written, by the same thread.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+constexpr int kSpThreads = 256;
+constexpr int kSpUnroll = 8;
+
+__global__ __launch_bounds__(kSpThreads) void state_passing_kernel(
+    const float* S, float* carried, const float* __restrict__ dA_cumsum,
+    const float* __restrict__ init, float* __restrict__ fin, int H, int nc, int Q, int64_t np4,
+    int64_t total) {
+  const int64_t id = (int64_t)blockIdx.x * kSpThreads + threadIdx.x;
+  if (id >= total) return;
+  const int64_t bh = id / np4;
+  const int64_t e4 = id - bh * np4;
+  const int64_t b = bh / H, h = bh - b * H;
+
+  float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (init) run = reinterpret_cast<const float4*>(init)[bh * np4 + e4];
+
+  const float* glast = dA_cumsum + bh * nc * Q + (Q - 1);  // chunk c at glast[c*Q]
+  const int64_t cstride = (int64_t)H * np4;                // float4s between chunks
+  const float4* sp = reinterpret_cast<const float4*>(S) + (b * nc * H + h) * np4 + e4;
+  float4* cp = reinterpret_cast<float4*>(carried) + (b * nc * H + h) * np4 + e4;
+
+  int c = 0;
+  for (; c + kSpUnroll <= nc; c += kSpUnroll) {
+    float4 s[kSpUnroll];
+    float dec[kSpUnroll];
+#pragma unroll
+    for (int u = 0; u < kSpUnroll; ++u) {
+      s[u] = sp[(int64_t)(c + u) * cstride];
+      dec[u] = expf(glast[(int64_t)(c + u) * Q]);
+    }
+#pragma unroll
+    for (int u = 0; u < kSpUnroll; ++u) {
+      cp[(int64_t)(c + u) * cstride] = run;
+      run.x = dec[u] * run.x + s[u].x;
+      run.y = dec[u] * run.y + s[u].y;
+      run.z = dec[u] * run.z + s[u].z;
+      run.w = dec[u] * run.w + s[u].w;
+    }
+  }
+  for (; c < nc; ++c) {
+    const float4 s = sp[(int64_t)c * cstride];
+    const float dec = expf(glast[(int64_t)c * Q]);
+    cp[(int64_t)c * cstride] = run;
+    run.x = dec * run.x + s.x;
+    run.y = dec * run.y + s.y;
+    run.z = dec * run.z + s.z;
+    run.w = dec * run.w + s.w;
+  }
+  if (fin) reinterpret_cast<float4*>(fin)[bh * np4 + e4] = run;
+}
+
+hipError_t launch_state_passing(const Dims& d, const float* chunk_states, float* carried,
+                                const float* dA_cumsum, const float* initial_states,
+                                float* final_states, hipStream_t stream) {
+  const int64_t np4 = d.N * d.P / 4;
+  const int64_t total = d.B * d.H * np4;
+  const unsigned blocks = (unsigned)((total + kSpThreads - 1) / kSpThreads);
+  hipLaunchKernelGGL(state_passing_kernel, dim3(blocks), dim3(kSpThreads), 0, stream, chunk_states, carried,
+                     dA_cumsum, initial_states, final_states, (int)d.H, (int)d.nc, (int)d.Q, np4, total);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -1,0 +1,188 @@
+"""Python entry points with the C ABI's names, over torch device tensors.
+
+Each function checks that its tensors are CUDA (HIP) tensors of the expected
+dtype, shape and contiguity, then calls the matching ``ssd_*`` function of
+``libmamba_ssd.so`` on torch's current stream.  Nothing is computed here and
+nothing is copied or converted silently: a mismatch raises ``ValueError``, a
+failed call raises ``SSDError``.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from ._lib import MMA, SSD_BF16, SSD_F32, SSDShape, check, load_library
+
+_DT = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
+_DTNAME = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _shape(s) -> SSDShape:
+    if isinstance(s, SSDShape):
+        return s
+    return SSDShape.make(s["batch"], s["seqlen"], s["nheads"], s["headdim"], s["dstate"], s["ngroups"], s["chunk"])
+
+
+def _dims(sh: SSDShape):
+    nc = -(-sh.seqlen // sh.chunk)
+    return sh.batch, sh.seqlen, sh.nheads, sh.headdim, sh.dstate, sh.ngroups, sh.chunk, nc
+
+
+def _req(t: Optional[torch.Tensor], name: str, shape, dtypes) -> None:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _mma(mma: str) -> int:
+    if mma not in MMA:
+        raise ValueError(f"mma must be one of {list(MMA)}")
+    return MMA[mma]
+
+
+def ssd_chunk_cumsum(shape, dt, A, dA_cumsum=None, dt_bhl=None, with_dt=True, stream=None):
+    """dA_cumsum, dt_bhl [B,H,nc,Q] from dt [B,L,H], A [H] (fp32)."""
+    sh = _shape(shape)
+    B, L, H, P, N, G, Q, nc = _dims(sh)
+    f32 = (torch.float32,)
+    _req(dt, "dt", (B, L, H), f32)
+    _req(A, "A", (H,), f32)
+    if dA_cumsum is None:
+        dA_cumsum = torch.empty((B, H, nc, Q), device=dt.device, dtype=torch.float32)
+    if dt_bhl is None and with_dt:
+        dt_bhl = torch.empty((B, H, nc, Q), device=dt.device, dtype=torch.float32)
+    _req(dA_cumsum, "dA_cumsum", (B, H, nc, Q), f32)
+    if dt_bhl is not None:
+        _req(dt_bhl, "dt_bhl", (B, H, nc, Q), f32)
+    lib = load_library()
+    check(lib.ssd_chunk_cumsum(sh, _ptr(dt), _ptr(A), _ptr(dA_cumsum), _ptr(dt_bhl), _stream(stream)))
+    return dA_cumsum, dt_bhl
+
+
+def ssd_chunk_state(shape, x, Bm, dt_bhl, dA_cumsum, states=None, mma="bf16", stream=None):
+    """Per-chunk states [B,nc,H,N,P] fp32 (jump formula with decay)."""
+    sh = _shape(shape)
+    B, L, H, P, N, G, Q, nc = _dims(sh)
+    io = (torch.float32, torch.bfloat16)
+    _req(x, "x", (B, L, H, P), io)
+    _req(Bm, "Bm", (B, L, G, N), (x.dtype,))
+    _req(dt_bhl, "dt_bhl", (B, H, nc, Q), (torch.float32,))
+    _req(dA_cumsum, "dA_cumsum", (B, H, nc, Q), (torch.float32,))
+    if states is None:
+        states = torch.empty((B, nc, H, N, P), device=x.device, dtype=torch.float32)
+    _req(states, "states", (B, nc, H, N, P), (torch.float32,))
+    lib = load_library()
+    check(lib.ssd_chunk_state(sh, _ptr(x), _ptr(Bm), _DT[x.dtype], _ptr(dt_bhl), _ptr(dA_cumsum),
+                              _ptr(states), _mma(mma), _stream(stream)))
+    return states
+
+
+def ssd_state_passing(shape, chunk_states, dA_cumsum, initial_states=None, carried=None, final_states=None,
+                      in_place=False, stream=None):
+    """Carried states [B,nc,H,N,P] (state entering each chunk) and final
+    states [B,H,N,P].  ``in_place=True`` writes the carried states over
+    ``chunk_states``."""
+    sh = _shape(shape)
+    B, L, H, P, N, G, Q, nc = _dims(sh)
+    f32 = (torch.float32,)
+    _req(chunk_states, "chunk_states", (B, nc, H, N, P), f32)
+    _req(dA_cumsum, "dA_cumsum", (B, H, nc, Q), f32)
+    if initial_states is not None:
+        _req(initial_states, "initial_states", (B, H, N, P), f32)
+    if carried is None:
+        carried = chunk_states if in_place else torch.empty_like(chunk_states)
+    _req(carried, "carried", (B, nc, H, N, P), f32)
+    if final_states is None:
+        final_states = torch.empty((B, H, N, P), device=chunk_states.device, dtype=torch.float32)
+    _req(final_states, "final_states", (B, H, N, P), f32)
+    lib = load_library()
+    check(lib.ssd_state_passing(sh, _ptr(chunk_states), _ptr(carried), _ptr(dA_cumsum), _ptr(initial_states),
+                                _ptr(final_states), _stream(stream)))
+    return carried, final_states
+
+
+def ssd_chunk_scan(shape, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y=None, y_dtype=None, mma="bf16",
+                   stream=None):
+    """y [B,L,H,P] in ``y_dtype`` (default: x's dtype)."""
+    sh = _shape(shape)
+    B, L, H, P, N, G, Q, nc = _dims(sh)
+    io = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _req(x, "x", (B, L, H, P), io)
+    _req(Bm, "Bm", (B, L, G, N), (x.dtype,))
+    _req(Cm, "Cm", (B, L, G, N), (x.dtype,))
+    _req(dt_bhl, "dt_bhl", (B, H, nc, Q), f32)
+    _req(dA_cumsum, "dA_cumsum", (B, H, nc, Q), f32)
+    _req(carried, "carried", (B, nc, H, N, P), f32)
+    _req(D, "D", (H,), f32)
+    ydt = x.dtype if y_dtype is None else (_DTNAME[y_dtype] if isinstance(y_dtype, str) else y_dtype)
+    if y is None:
+        y = torch.empty((B, L, H, P), device=x.device, dtype=ydt)
+    _req(y, "y", (B, L, H, P), io)
+    lib = load_library()
+    check(lib.ssd_chunk_scan(sh, _ptr(x), _ptr(Bm), _ptr(Cm), _DT[x.dtype], _ptr(dt_bhl), _ptr(dA_cumsum),
+                             _ptr(carried), _ptr(D), _ptr(y), _DT[y.dtype], _mma(mma), _stream(stream)))
+    return y
+
+
+def ssd_workspace_bytes(shape) -> int:
+    return int(load_library().ssd_workspace_bytes(_shape(shape)))
+
+
+def ssd_forward(shape, x, dt, A, Bm, Cm, D, initial_states=None, y=None, y_dtype=None, final_states=None,
+                want_final=True, workspace=None, mma="bf16", stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One-call forward.  Returns (y, final_states or None)."""
+    sh = _shape(shape)
+    B, L, H, P, N, G, Q, nc = _dims(sh)
+    io = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _req(x, "x", (B, L, H, P), io)
+    _req(dt, "dt", (B, L, H), f32)
+    _req(A, "A", (H,), f32)
+    _req(Bm, "Bm", (B, L, G, N), (x.dtype,))
+    _req(Cm, "Cm", (B, L, G, N), (x.dtype,))
+    _req(D, "D", (H,), f32)
+    if initial_states is not None:
+        _req(initial_states, "initial_states", (B, H, N, P), f32)
+    ydt = x.dtype if y_dtype is None else (_DTNAME[y_dtype] if isinstance(y_dtype, str) else y_dtype)
+    if y is None:
+        y = torch.empty((B, L, H, P), device=x.device, dtype=ydt)
+    _req(y, "y", (B, L, H, P), io)
+    if final_states is None and want_final:
+        final_states = torch.empty((B, H, N, P), device=x.device, dtype=torch.float32)
+    if final_states is not None:
+        _req(final_states, "final_states", (B, H, N, P), f32)
+    lib = load_library()
+    need = int(lib.ssd_workspace_bytes(sh))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=x.device, dtype=torch.uint8)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    check(lib.ssd_forward(sh, _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _DT[x.dtype],
+                          _ptr(initial_states), _ptr(y), _DT[y.dtype], _ptr(final_states), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _mma(mma), _stream(stream)))
+    return y, final_states
+
+
+def shape_of(inp: Dict[str, torch.Tensor], chunk: int) -> SSDShape:
+    """ssd_shape from x [B,L,H,P] and Bm [B,L,G,N]."""
+    B, L, H, P = inp["x"].shape
+    G, N = inp["Bm"].shape[2], inp["Bm"].shape[3]
+    return SSDShape.make(B, L, H, P, N, G, chunk)

@@ -1,0 +1,147 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+function ``include/ssd.h`` declares, and rejects every invalid argument with
+its documented status before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mamba_ssd_scan_chunk_amd import _lib
+from mamba_ssd_scan_chunk_amd._lib import SSDShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, ALIGN = 0, 1, 2, 3, 4, 5, 6
+FAKE = 0x100000  # a 16-byte-aligned non-null address; never dereferenced (checks fail first)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for n in ["ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward",
+              "ssd_workspace_bytes", "ssd_status_string", "ssd_abi_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
+    assert lib.ssd_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS_NAMES.items():
+        s = lib.ssd_status_string(code).decode()
+        assert s.startswith(name)
+    assert lib.ssd_status_string(99).decode() == "unknown ssd_status"
+
+
+def shape(**kw):
+    d = dict(batch=2, seqlen=512, nheads=4, headdim=64, dstate=128, ngroups=1, chunk=256)
+    d.update(kw)
+    return SSDShape.make(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), SHAPE), (dict(seqlen=0), SHAPE), (dict(nheads=-1), SHAPE), (dict(headdim=0), SHAPE),
+    (dict(dstate=0), SHAPE), (dict(ngroups=0), SHAPE), (dict(chunk=0), SHAPE), (dict(nheads=6, ngroups=4), SHAPE),
+    (dict(headdim=24), UNSUP), (dict(dstate=40), UNSUP), (dict(headdim=272), UNSUP), (dict(dstate=272), UNSUP),
+    (dict(chunk=16), UNSUP), (dict(chunk=96), UNSUP), (dict(chunk=512), UNSUP), (dict(seqlen=500), UNSUP),
+])
+def test_shape_checks(lib, kw, code):
+    s = shape(**kw)
+    assert lib.ssd_chunk_cumsum(s, FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.ssd_chunk_state(s, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, None) == code
+    assert lib.ssd_state_passing(s, FAKE, FAKE, FAKE, None, FAKE, None) == code
+    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, None) == code
+    assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, 1, FAKE, FAKE, 1 << 40, 0,
+                           None) == code
+    assert lib.ssd_workspace_bytes(s) == 0
+
+
+def test_null_shape(lib):
+    assert lib.ssd_chunk_cumsum(None, FAKE, FAKE, FAKE, FAKE, None) == NULL
+    assert lib.ssd_workspace_bytes(None) == 0
+
+
+def test_null_pointers(lib):
+    s = shape()
+    assert lib.ssd_chunk_cumsum(s, None, FAKE, FAKE, FAKE, None) == NULL
+    assert lib.ssd_chunk_cumsum(s, FAKE, None, FAKE, FAKE, None) == NULL
+    assert lib.ssd_chunk_cumsum(s, FAKE, FAKE, None, FAKE, None) == NULL
+    for i in range(5):
+        args = [FAKE] * 5
+        args[i] = None
+        x, Bm, dtb, dA, st = args
+        assert lib.ssd_chunk_state(s, x, Bm, 1, dtb, dA, st, 0, None) == NULL
+    for i in range(3):
+        args = [FAKE] * 3
+        args[i] = None
+        assert lib.ssd_state_passing(s, args[0], args[1], args[2], None, FAKE, None) == NULL
+    for i in range(8):
+        args = [FAKE] * 8
+        args[i] = None
+        x, Bm, Cm, dtb, dA, car, D, y = args
+        assert lib.ssd_chunk_scan(s, x, Bm, Cm, 1, dtb, dA, car, D, y, 1, 0, None) == NULL
+    for i in range(7):
+        args = [FAKE] * 7
+        args[i] = None
+        x, dt, A, Bm, Cm, D, y = args
+        assert lib.ssd_forward(s, x, dt, A, Bm, Cm, D, 1, None, y, 1, None, FAKE, 1 << 40, 0, None) == NULL
+
+
+def test_dtype_and_mma_enums(lib):
+    s = shape()
+    assert lib.ssd_chunk_state(s, FAKE, FAKE, 2, FAKE, FAKE, FAKE, 0, None) == DTYPE
+    assert lib.ssd_chunk_state(s, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 2, None) == DTYPE
+    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 7, 0, None) == DTYPE
+    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1, -1, None) == DTYPE
+    assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, None, FAKE, 1, FAKE, FAKE, 1 << 40, 0,
+                           None) == DTYPE
+
+
+def test_alignment(lib):
+    s = shape()
+    odd = FAKE + 4
+    assert lib.ssd_chunk_cumsum(s, odd, FAKE, FAKE, FAKE, None) == ALIGN
+    assert lib.ssd_chunk_cumsum(s, FAKE, FAKE, FAKE, odd, None) == ALIGN
+    assert lib.ssd_chunk_state(s, FAKE, odd, 1, FAKE, FAKE, FAKE, 0, None) == ALIGN
+    assert lib.ssd_state_passing(s, FAKE, FAKE, FAKE, odd, FAKE, None) == ALIGN
+    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, odd, 1, 0, None) == ALIGN
+    assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, odd, FAKE, 1, FAKE, FAKE, 1 << 40, 0,
+                           None) == ALIGN
+
+
+def test_workspace(lib):
+    s = shape()
+    B, L, H, P, N, Q = 2, 512, 4, 64, 128, 256
+    nc = L // Q
+    bhl = 4 * B * H * nc * Q
+    st = 4 * B * nc * H * N * P
+    ru = lambda v: (v + 255) // 256 * 256
+    expect = ru(ru(ru(bhl) + bhl) + st)
+    assert lib.ssd_workspace_bytes(s) == expect
+    assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, 1, FAKE, None, 1 << 40, 0,
+                           None) == WS
+    assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, 1, FAKE, FAKE, expect - 1, 0,
+                           None) == WS
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from mamba_ssd_scan_chunk_amd import ops
+    s = dict(batch=1, seqlen=64, nheads=2, headdim=16, dstate=16, ngroups=1, chunk=64)
+    with pytest.raises(ValueError):
+        ops.ssd_chunk_cumsum(s, torch.zeros(1, 64, 2), torch.zeros(2))

@@ -1,0 +1,227 @@
+"""GPU parity: every ABI call against the fp64 oracle on the same seeded inputs.
+
+Small shapes span several tiles and every tail the kernels have (partial
+head tile in the cumsum, 16/32-wide P slices, zero-padded state contraction,
+32-token chunks, grouped B/C); each kernel is also checked in isolation by
+feeding it oracle intermediates.  Acceptance (max|err|/max|ref| per tensor):
+1e-6 for the cumsum, 1e-4 for the fp32-MFMA path, 1e-2 for the bf16-operand
+path.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import (TOL_CUMSUM, TOL_PASSING, gpu_forward, make_inputs, oracle, relerr, say, tol_for,
+                        upload)
+from mamba_ssd_scan_chunk_amd import ops
+from mamba_ssd_scan_chunk_amd._lib import SSDError
+from oracle.oracle import dA_cumsum_ref, dt_bhl_ref
+
+pytestmark = pytest.mark.gpu
+
+# (name, B, L, H, P, N, G, Q)
+SHAPES = [
+    ("tiny", 1, 256, 2, 16, 16, 1, 64),
+    ("two_chunks", 2, 512, 4, 64, 128, 1, 256),
+    ("grouped", 1, 256, 6, 32, 64, 2, 64),
+    ("ragged_tiles", 2, 384, 3, 48, 48, 3, 128),
+    ("n256", 1, 256, 4, 64, 256, 2, 128),
+    ("q32_h20", 1, 96, 20, 32, 32, 4, 32),
+    ("p128", 1, 256, 2, 128, 64, 1, 128),
+]
+MODES = [("f32", "f32"), ("bf16", "f32"), ("f32", "bf16"), ("bf16", "bf16")]  # (input dtype, mma)
+
+
+def _inp(shape, in_dtype, seed=0, **kw):
+    name, B, L, H, P, N, G, Q = shape
+    return make_inputs(B, L, H, P, N, G, Q, in_dtype=in_dtype, seed=seed, dt_shift=kw.pop("dt_shift", 1.0), **kw)
+
+
+def _h0(inp, seed=5, scale=1.0):
+    s = inp.shape
+    return (scale * np.random.default_rng(seed).standard_normal(
+        (s["batch"], s["nheads"], s["dstate"], s["headdim"]))).astype(np.float32)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_chunk_cumsum(shape):
+    say(f"chunk_cumsum {shape}")
+    inp = _inp(shape, "f32")
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    torch.cuda.synchronize()
+    ref = dA_cumsum_ref(inp.dt, inp.A, inp.chunk)
+    assert relerr(dA, ref) <= TOL_CUMSUM
+    # all terms share a sign, so the error is also small elementwise
+    g = dA.double().cpu().numpy()
+    assert (np.abs(g - ref) <= TOL_CUMSUM * np.abs(ref) + 1e-30).all()
+    assert np.array_equal(dtb.cpu().numpy(), dt_bhl_ref(inp.dt, inp.chunk).astype(np.float32))
+    # dt_bhl is optional
+    dA2, none = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"], with_dt=False)
+    torch.cuda.synchronize()
+    assert none is None and torch.equal(dA2, dA)
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["-".join(m) for m in MODES])
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_chunk_state(shape, mode):
+    in_dtype, mma = mode
+    say(f"chunk_state {shape} {mode}")
+    inp = _inp(shape, in_dtype, seed=1)
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    S = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma=mma)
+    torch.cuda.synchronize()
+    ref = oracle().chunk_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk)
+    e = relerr(S, ref)
+    say(f"  rel err {e:.3g}")
+    assert e <= tol_for(mma)
+
+
+@pytest.mark.parametrize("with_h0", [False, True])
+@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_state_passing(shape, in_place, with_h0):
+    say(f"state_passing {shape} in_place={in_place} h0={with_h0}")
+    inp = _inp(shape, "f32", seed=2, dt_shift=3.0)  # slow decay: carried states matter
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    o = oracle()
+    S = o.chunk_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk)
+    h0 = _h0(inp) if with_h0 else None
+    Hin, fin = o.carried_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk, h0=h0)
+    dA, _ = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    S_t = torch.from_numpy(S.astype(np.float32)).cuda()
+    h0_t = None if h0 is None else torch.from_numpy(h0).cuda()
+    carried, final = ops.ssd_state_passing(sh, S_t, dA, initial_states=h0_t, in_place=in_place)
+    torch.cuda.synchronize()
+    if in_place:
+        assert carried.data_ptr() == S_t.data_ptr()
+    e1, e2 = relerr(carried, Hin), relerr(final, fin)
+    say(f"  rel err carried {e1:.3g} final {e2:.3g}")
+    assert e1 <= TOL_PASSING and e2 <= TOL_PASSING
+
+
+@pytest.mark.parametrize("y_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", MODES, ids=["-".join(m) for m in MODES])
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_chunk_scan(shape, mode, y_dtype):
+    in_dtype, mma = mode
+    if mma == "f32" and y_dtype == "bf16":
+        pytest.skip("bf16 output rounding alone exceeds the fp32-path bar")
+    say(f"chunk_scan {shape} {mode} y={y_dtype}")
+    inp = _inp(shape, in_dtype, seed=3, dt_shift=2.0)
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    o = oracle()
+    h0 = _h0(inp)
+    Hin, _ = o.carried_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk, h0=h0)
+    yref, _ = o.forward(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D, h0=h0)
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    car = torch.from_numpy(Hin.astype(np.float32)).cuda()
+    y = ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, car, t["D"], y_dtype=y_dtype, mma=mma)
+    torch.cuda.synchronize()
+    e = relerr(y, yref)
+    say(f"  rel err {e:.3g}")
+    assert e <= tol_for(mma)
+
+
+@pytest.mark.parametrize("mode", MODES, ids=["-".join(m) for m in MODES])
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_forward(shape, mode):
+    in_dtype, mma = mode
+    say(f"forward {shape} {mode}")
+    inp = _inp(shape, in_dtype, seed=4, dt_shift=2.0)
+    h0 = _h0(inp)
+    y_dtype = "f32" if mma == "f32" else in_dtype
+    y, fin = gpu_forward(inp, mma, y_dtype=y_dtype, h0=h0)
+    yref, fref = oracle().forward(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D, h0=h0)
+    e1, e2 = relerr(y, yref), relerr(fin, fref)
+    say(f"  rel err y {e1:.3g} final {e2:.3g}")
+    assert e1 <= tol_for(mma) and e2 <= tol_for(mma)
+
+
+# ---------------------------------------------------------------- numerics stress
+STRESS = {
+    # carried state dominates: tiny dt, slow A
+    "slow_decay": dict(dt_shift=7.0, log_a_range=(math.log(0.1), 0.0)),
+    # no decay at all (the jump formula): the state grows over the sequence
+    "zero_decay": dict(A_override=0.0),
+    # memoryless: exp(G) underflows to exactly 0 within a few tokens
+    "fast_decay": dict(dt_shift=-3.0),
+}
+
+
+@pytest.mark.parametrize("mma", ["f32", "bf16"])
+@pytest.mark.parametrize("case", list(STRESS), ids=list(STRESS))
+def test_forward_stress(case, mma):
+    shape = ("stress", 1, 1024, 4, 64, 64, 1, 128)
+    say(f"forward stress {case} {mma}")
+    kw = dict(STRESS[case])
+    inp = _inp(shape, "bf16", seed=6, **kw)
+    h0 = _h0(inp)
+    y, fin = gpu_forward(inp, mma, y_dtype="f32", h0=h0)
+    yref, fref = oracle().forward(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D, h0=h0)
+    e1, e2 = relerr(y, yref), relerr(fin, fref)
+    say(f"  rel err y {e1:.3g} final {e2:.3g}")
+    assert e1 <= tol_for(mma) and e2 <= tol_for(mma)
+
+
+@pytest.mark.parametrize("mma", ["f32", "bf16"])
+def test_split_chaining(mma):
+    """final states of the first part fed as initial states of the second part
+    reproduce the unsplit run (sequence resume)."""
+    say(f"split chaining {mma}")
+    B, L, H, P, N, G, Q = 2, 1024, 4, 64, 128, 1, 256
+    inp = make_inputs(B, L, H, P, N, G, Q, in_dtype="bf16", seed=8, dt_shift=4.0)
+    t = upload(inp)
+    k = 512
+    sh_full = ops.shape_of(t, Q)
+    part = lambda a, lo, hi: a[:, lo:hi].contiguous()
+    sh_half = ops.SSDShape.make(B, k, H, P, N, G, Q)
+    y_full, f_full = ops.ssd_forward(sh_full, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], y_dtype="f32",
+                                     mma=mma)
+    y1, f1 = ops.ssd_forward(sh_half, part(t["x"], 0, k), part(t["dt"], 0, k), t["A"], part(t["Bm"], 0, k),
+                             part(t["Cm"], 0, k), t["D"], y_dtype="f32", mma=mma)
+    y2, f2 = ops.ssd_forward(sh_half, part(t["x"], k, L), part(t["dt"], k, L), t["A"], part(t["Bm"], k, L),
+                             part(t["Cm"], k, L), t["D"], initial_states=f1, y_dtype="f32", mma=mma)
+    torch.cuda.synchronize()
+    yref, fref = oracle().forward(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D)
+    y_cat = torch.cat([y1, y2], dim=1)
+    assert relerr(y_cat, yref) <= tol_for(mma) and relerr(f2, fref) <= tol_for(mma)
+    assert relerr(y_cat, y_full.double().cpu().numpy()) <= tol_for(mma)
+
+
+@pytest.mark.parametrize("mma", ["f32", "bf16"])
+def test_deterministic(mma):
+    """No atomics: two runs give bitwise identical outputs."""
+    say(f"determinism {mma}")
+    inp = make_inputs(2, 1024, 8, 64, 128, 2, 256, in_dtype="bf16", seed=9)
+    y1, f1 = gpu_forward(inp, mma)
+    y2, f2 = gpu_forward(inp, mma)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+def test_errors_raise_through_binding():
+    say("errors")
+    inp = make_inputs(1, 128, 2, 64, 64, 1, 64, in_dtype="bf16", seed=10)
+    t = upload(inp)
+    bad = ops.SSDShape.make(1, 128, 2, 64, 64, 1, 16)  # chunk 16 unsupported
+    with pytest.raises(ValueError):
+        ops.ssd_chunk_cumsum(bad, t["dt"], t["A"], dA_cumsum=torch.empty(1, 2, 8, 64, device="cuda"))
+    with pytest.raises(SSDError) as ei:
+        ops.ssd_chunk_cumsum(bad, t["dt"], t["A"])
+    assert ei.value.code == 4
+    with pytest.raises(ValueError):  # dtype mismatch between x and B
+        ops.ssd_chunk_state(ops.shape_of(t, 64), t["x"], t["Bm"].float(),
+                            torch.empty(1, 2, 2, 64, device="cuda"), torch.empty(1, 2, 2, 64, device="cuda"))
