@@ -296,6 +296,8 @@ static hipError_t launch_scan_op(const Dims& d, const void* x, const void* Bm, c
 hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
                              const float* dt_bhl, const float* dA_cumsum, const float* carried,
                              const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream) {
+  if (chunk_scan_hg_supported(d, in_bf16, f32_mma))
+    return launch_chunk_scan_hg(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream);
   const size_t lds = chunk_scan_lds_bytes(d, f32_mma);
   if (f32_mma)
     return launch_scan_op<OpF32>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, lds);

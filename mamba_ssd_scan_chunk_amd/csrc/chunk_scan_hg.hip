@@ -1,0 +1,531 @@
+// chunk_scan_hg.hip -- fused chunk output, head-group variant (bf16 operands).
+//
+// Page: "Jane Street ML Engineers Map Mamba-2 Recurrent State Computation to
+// Tensor Cores with cuTile" (disconfirmai.com), compute_out paragraph: the
+// interaction tile C.B^T is built on the matrix units (phase 1), decayed and
+// causally masked in registers (phase 2), and fused with the carried-state
+// term and the skip connection; the full interaction matrix never reaches
+// memory.  For token i of chunk c:
+//     y_i = exp(G_i) C_i^T H_in  +  sum_{j<=i} (C_i . B_j) exp(G_i - G_j) dt_j x_j  +  D x_i
+//
+// C.B^T depends only on (batch, chunk, B/C group), not on the head.  One block
+// owns a (b, c, group) and a run of HG heads of that group: it computes the
+// causal C.B^T tiles of the whole chunk ONCE, keeps them in fp32 registers,
+// and reuses them for all HG heads, so the per-head work is the decay, the
+// M.X product and the C.H_in product.
+//
+// Waves and tiles (Q = chunk in {128, 256}, QT = Q/16 row tiles of 16 rows):
+//  * QT/2 waves; wave w owns the row tiles w and QT-1-w, which together hold
+//    QT+1 causal 16x16 sub-tiles whatever w is (balanced work).  The wave's
+//    code is specialised at compile time on w (hg_body<..., W>), so tile
+//    indices, loop trip counts and register slots are constants: no guarded
+//    code, and the CB^T sub-tiles stay in registers for the block's life.
+//  * the CB^T sub-tiles are computed with operand roles swapped (B as the A
+//    operand, C as the B operand), so each lane holds four consecutive j for
+//    one row i; after decay and mask those are directly the A fragment of
+//    M.X (slot e = 4t + r <-> token 32k + 16t + 4lg + r), and x is read from
+//    LDS with the same slot map.
+//  * decay: for the sub-tile pairs below the diagonal pair of row tile t,
+//    exp(G_i - G_j) = exp(G_i - G_R) * exp(G_R - G_j) with the reference row
+//    R = 32 * (t / 2) between j and i, so both factors are <= 1 (no overflow;
+//    an underflowing factor means a negligible product).  The column factor
+//    times dt_j comes from a per-head LDS table, the row factor scales the
+//    accumulator once; only the diagonal pair takes exact per-element
+//    exponentials, behind the causal select.
+//  * the B and C chunks are staged once in LDS (natural [token][n] layout);
+//    C rows are the B operand of CB^T and the A operand of C.H_in.
+// Per head: x (transposed, Xt[p][j]) and H_in (transposed, Ht[p][n]), both
+// rounded to bf16, plus G and dt rows, are staged in LDS.  The next head's
+// tiles are loaded into registers while the current head computes (software
+// pipeline), then written to LDS after a barrier.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+#include <type_traits>
+
+namespace ssd {
+
+constexpr int kHgThreads = 256;  // 4 waves, one per SIMD: up to 512 registers each
+
+template <int Q, int NK, int CT>
+struct HgCfg {
+  static constexpr int QT = Q / 16;
+  static constexpr int NCW = 4;       // compute waves
+  static constexpr int PPW = QT / 8;  // row-tile pairs per wave
+  static constexpr int T = kHgThreads;
+  static constexpr int PT = CT * 16;
+  static constexpr int N = NK * 32;   // this variant needs N == NK*32
+  static constexpr int NPI = N + 8;   // pitch (elements) of n-indexed LDS rows
+  static constexpr int XP = Q + 8;    // pitch of Xt rows
+  static constexpr size_t lds_bs = (size_t)Q * NPI * 2;
+  static constexpr size_t lds_xh = (size_t)PT * XP * 2 + (size_t)PT * NPI * 2;
+  static constexpr size_t lds_a = lds_bs > lds_xh ? lds_bs : lds_xh;  // Bs, later Xt + Ht
+  static constexpr size_t lds_c = (size_t)Q * NPI * 2;                // Cs
+  static constexpr size_t lds_w = sizeof(float) * (size_t)(QT / 2) * Q;  // Ws
+  static constexpr size_t lds_total = lds_a + lds_c + lds_w + 2 * sizeof(float) * Q;
+};
+
+// Row tile ti of wave W: pair p = ti / 2 gives tiles 8p + W (even ti) and
+// 8p + 7 - W (odd ti); each pair holds 16p + 9 causal sub-tiles.
+template <int W>
+constexpr int hg_tile(int ti) { return (ti & 1) ? 8 * (ti >> 1) + 7 - W : 8 * (ti >> 1) + W; }
+template <int W>
+constexpr int hg_slot_base(int ti) {
+  int sb = 0;
+  for (int k = 0; k < ti; ++k) sb += hg_tile<W>(k) + 1;
+  return sb;
+}
+
+struct HgArgs {
+  const void* x;
+  const void* Bm;
+  const void* Cm;
+  const float* dt_bhl;
+  const float* dA_cumsum;
+  const float* carried;
+  const float* D;
+  void* y;
+  int y_bf16, L, H, P, G, nc, HG;
+  int b, c, g, hbase, p0;
+  int64_t tok0;
+};
+
+template <int Q, int NK, int CT, bool IN_BF16, int W>
+__device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, const int tid) {
+  using Cfg = HgCfg<Q, NK, CT>;
+  using Op = OpBF16;
+  using Frag = Op::Frag;
+  constexpr int QT = Cfg::QT, PT = Cfg::PT, N = Cfg::N, NPI = Cfg::NPI, XP = Cfg::XP, T = Cfg::T;
+  constexpr int XW = IN_BF16 ? 8 : 4;        // x elements per 16-byte load
+  constexpr int NXB = (Q / 4) * (PT / XW);   // x prefetch blocks (4 rows x XW cols)
+  constexpr int NHB = (N / 4) * (PT / 4);    // H prefetch blocks (4 n x 4 p)
+  constexpr int XPT = (NXB + T - 1) / T;     // blocks per thread
+  constexpr int HPT = (NHB + T - 1) / T;
+  constexpr int TE = IN_BF16 ? 2 : 4;        // input element bytes
+  constexpr int PPW = Cfg::PPW;
+  constexpr int NSL = PPW == 1 ? 9 : 34;     // CB^T sub-tiles held (sum over the wave's tiles of tile+1)
+
+  uint16_t* Bs = reinterpret_cast<uint16_t*>(smem);                    // [Q][NPI]  (phase 0-1 only)
+  uint16_t* Xt = reinterpret_cast<uint16_t*>(smem);                    // [PT][XP]  (aliases Bs later)
+  uint16_t* Ht = Xt + PT * XP;                                          // [PT][NPI]
+  uint16_t* Cs = reinterpret_cast<uint16_t*>(smem + Cfg::lds_a);        // [Q][NPI]
+  float* Ws = reinterpret_cast<float*>(smem + Cfg::lds_a + Cfg::lds_c);  // [QT/2][Q]
+  float* Gs = Ws + (QT / 2) * Q;                                        // [Q]
+  float* dts = Gs + Q;                                                  // [Q]
+
+  const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int H = a.H, P = a.P, G = a.G, nc = a.nc;
+  const int64_t tok0 = a.tok0;
+  const int HP = H * P;
+
+  // ---- phase 0: B and C chunks -> Bs, Cs (natural [token][n] layout, bf16)
+  {
+    const int64_t bc0 = (tok0 * G + a.g) * N;  // element offset of (token 0 of the chunk, group g)
+    const int GN = G * N;
+    for (int idx = tid; idx < Q * (N / 8); idx += T) {
+      const int j = idx / (N / 8), nb = idx - (idx / (N / 8)) * (N / 8);
+      const int off = j * GN + 8 * nb;
+      float t[8];
+      load8_as_f32(a.Bm, bc0 + off, IN_BF16, t);
+      Lds<Op>::store8(Bs + j * NPI + 8 * nb, t);
+      load8_as_f32(a.Cm, bc0 + off, IN_BF16, t);
+      Lds<Op>::store8(Cs + j * NPI + 8 * nb, t);
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 1: causal CB^T sub-tiles of the wave's row tiles (fp32, registers).
+  // For pair p the wave owns tiles 8p + W and 8p + 7 - W; slots are laid out
+  // tile after tile in that order (hg_slot_base), one per sub-tile js <= tile.
+  f32x4_t cb[NSL];
+#pragma unroll
+  for (int ti = 0; ti < 2 * PPW; ++ti) {
+    const int tile = hg_tile<W>(ti);
+    const int sb = hg_slot_base<W>(ti);
+#pragma unroll
+    for (int js = 0; js <= tile; ++js) {
+      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+        const Frag bf = Lds<Op>::load8(Bs + (16 * js + l16) * NPI + 32 * s + 8 * lg);
+        const Frag cf = Lds<Op>::load8(Cs + (16 * tile + l16) * NPI + 32 * s + 8 * lg);
+        acc = Op::mma(bf, cf, acc);
+      }
+      cb[sb + js] = acc;
+    }
+  }
+
+  // ---- per-head register prefetch: issued before a head's compute,
+  // committed to LDS after it.
+  uint4 xv[XPT][4];   // 4 rows x 16 bytes of x per block
+  float4 hv[HPT][4];  // 4 rows (n) x 4 columns (p) of H_in per block
+  float pg = 0.f, pd = 0.f;
+  auto issue = [&](int h) {
+    const unsigned char* xh =
+        reinterpret_cast<const unsigned char*>(a.x) + ((tok0 * H + h) * (int64_t)P + a.p0) * (int64_t)TE;
+#pragma unroll
+    for (int uu = 0; uu < XPT; ++uu) {
+      const int blk = tid + uu * T;
+      if (blk < NXB) {
+        const int cbk = blk % (PT / XW), rbk = blk / (PT / XW);
+        const int o0 = (4 * rbk) * HP + XW * cbk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          xv[uu][r] = *reinterpret_cast<const uint4*>(xh + (int64_t)(o0 + r * HP) * TE);
+      }
+    }
+    const float* hs = a.carried + (((int64_t)a.b * nc + a.c) * H + h) * (int64_t)(N * P) + a.p0;
+#pragma unroll
+    for (int uu = 0; uu < HPT; ++uu) {
+      const int blk = tid + uu * T;
+      if (blk < NHB) {
+        const int pb = blk % (PT / 4), nb = blk / (PT / 4);
+        const int o0 = (4 * nb) * P + 4 * pb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hv[uu][r] = *reinterpret_cast<const float4*>(hs + o0 + r * P);
+      }
+    }
+    if (tid < Q) {
+      const int64_t bhc = ((int64_t)a.b * H + h) * nc + a.c;
+      pg = a.dA_cumsum[bhc * Q + tid];
+      pd = a.dt_bhl[bhc * Q + tid];
+    }
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int uu = 0; uu < XPT; ++uu) {
+      const int blk = tid + uu * T;
+      if (blk < NXB) {
+        const int cbk = blk % (PT / XW), rbk = blk / (PT / XW);
+        float v[4][XW];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint4 q = xv[uu][r];
+          if constexpr (IN_BF16) {
+            v[r][0] = bf16_bits_to_f32(q.x & 0xffffu); v[r][1] = bf16_bits_to_f32(q.x >> 16);
+            v[r][2] = bf16_bits_to_f32(q.y & 0xffffu); v[r][3] = bf16_bits_to_f32(q.y >> 16);
+            v[r][4] = bf16_bits_to_f32(q.z & 0xffffu); v[r][5] = bf16_bits_to_f32(q.z >> 16);
+            v[r][6] = bf16_bits_to_f32(q.w & 0xffffu); v[r][7] = bf16_bits_to_f32(q.w >> 16);
+          } else {
+            v[r][0] = __uint_as_float(q.x); v[r][1] = __uint_as_float(q.y);
+            v[r][2] = __uint_as_float(q.z); v[r][3] = __uint_as_float(q.w);
+          }
+        }
+#pragma unroll
+        for (int col = 0; col < XW; ++col) {
+          uint2 w;
+          w.x = pack_bf16x2(v[0][col], v[1][col]);
+          w.y = pack_bf16x2(v[2][col], v[3][col]);
+          *reinterpret_cast<uint2*>(Xt + (XW * cbk + col) * XP + 4 * rbk) = w;
+        }
+      }
+    }
+#pragma unroll
+    for (int uu = 0; uu < HPT; ++uu) {
+      const int blk = tid + uu * T;
+      if (blk < NHB) {
+        const int pb = blk % (PT / 4), nb = blk / (PT / 4);
+        uint2 w0, w1, w2, w3;
+        w0.x = pack_bf16x2(hv[uu][0].x, hv[uu][1].x); w0.y = pack_bf16x2(hv[uu][2].x, hv[uu][3].x);
+        w1.x = pack_bf16x2(hv[uu][0].y, hv[uu][1].y); w1.y = pack_bf16x2(hv[uu][2].y, hv[uu][3].y);
+        w2.x = pack_bf16x2(hv[uu][0].z, hv[uu][1].z); w2.y = pack_bf16x2(hv[uu][2].z, hv[uu][3].z);
+        w3.x = pack_bf16x2(hv[uu][0].w, hv[uu][1].w); w3.y = pack_bf16x2(hv[uu][2].w, hv[uu][3].w);
+        *reinterpret_cast<uint2*>(Ht + (4 * pb + 0) * NPI + 4 * nb) = w0;
+        *reinterpret_cast<uint2*>(Ht + (4 * pb + 1) * NPI + 4 * nb) = w1;
+        *reinterpret_cast<uint2*>(Ht + (4 * pb + 2) * NPI + 4 * nb) = w2;
+        *reinterpret_cast<uint2*>(Ht + (4 * pb + 3) * NPI + 4 * nb) = w3;
+      }
+    }
+    if (tid < Q) {
+      Gs[tid] = pg;
+      dts[tid] = pd;
+    }
+  };
+  // Column factors of the off-diagonal sub-tiles: for the reference row
+  // R = 32u, Ws[u][j] = exp(G_R - G_j) dt_j (j < R, so G_R <= G_j and the
+  // factor is <= 1).
+  auto make_w = [&]() {
+    for (int idx = tid; idx < (QT / 2) * Q; idx += T) {
+      const int u = idx / Q, j = idx - (idx / Q) * Q;
+      if (j < 32 * u) Ws[idx] = fast_exp(Gs[32 * u] - Gs[j]) * dts[j];
+    }
+  };
+
+  // One row tile of one head; TILE and SB (slot of its sub-tile js = 0) are
+  // compile-time constants.
+  // `ln` is the lane index laundered through an empty asm at the top of each
+  // head iteration: every lane-dependent address, mask and offset below is
+  // recomputed per head instead of being hoisted out of the head loop, where
+  // hundreds of them would stay live and spill.
+  auto tile_out = [&](auto tile_c, auto sb_c, int h, float dsk, int ln) {
+    constexpr int TILE = decltype(tile_c)::value;
+    constexpr int SB = decltype(sb_c)::value;
+    const int l16 = ln & 15, lg = ln >> 4;
+    constexpr int U = TILE / 2;  // pairs k < U are off-diagonal; pair U holds the diagonal
+    constexpr int R = 32 * U;    // reference row of the factorised decay
+    const float gR = Gs[R];
+    f32x4_t acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // carried-state term C_i . H_in, scaled by exp(G_R) now and by exp(G_i - G_R) below
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      const Frag ca = Lds<Op>::load8(Cs + (16 * TILE + l16) * NPI + 32 * s + 8 * lg);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        acc[ct] = Op::mma(ca, Lds<Op>::load8(Ht + (16 * ct + l16) * NPI + 32 * s + 8 * lg), acc[ct]);
+    }
+    {
+      const float eR = fast_exp(gR);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct] *= eR;
+    }
+    // off-diagonal pairs: M' = CB * Ws[U][j]
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      float m[8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int js = 2 * k + t;
+        const f32x4_t cv = cb[SB + js];
+        const float4 w = *reinterpret_cast<const float4*>(Ws + U * Q + 16 * js + 4 * lg);
+        m[4 * t + 0] = cv[0] * w.x;
+        m[4 * t + 1] = cv[1] * w.y;
+        m[4 * t + 2] = cv[2] * w.z;
+        m[4 * t + 3] = cv[3] * w.w;
+      }
+      const Frag mf = Op::from_f32(m);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const uint16_t* xr = Xt + (16 * ct + l16) * XP + 32 * k + 4 * lg;
+        acc[ct] = Op::mma(mf, Lds<Op>::load4x2(xr, xr + 16), acc[ct]);
+      }
+    }
+    // row factor exp(G_i - G_R) for the output rows this lane holds
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = fast_exp(Gs[16 * TILE + 4 * lg + r] - gR);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct][r] *= e;
+    }
+    // diagonal pair: exact decay, causal select before exp
+    {
+      const int i = 16 * TILE + l16;
+      const float gi = Gs[i];
+      float m[8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int js = 2 * U + t;
+        if (js <= TILE) {
+          const f32x4_t cv = cb[SB + js];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * js + 4 * lg + r;
+            const bool keep = j <= i;
+            const int jc = keep ? j : i;
+            const float dec = fast_exp(keep ? gi - Gs[jc] : -INFINITY) * dts[jc];
+            m[4 * t + r] = keep ? cv[r] * dec : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) m[4 * t + r] = 0.f;
+        }
+      }
+      const Frag mf = Op::from_f32(m);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const uint16_t* xr = Xt + (16 * ct + l16) * XP + 32 * U + 4 * lg;
+        acc[ct] = Op::mma(mf, Lds<Op>::load4x2(xr, xr + 16), acc[ct]);
+      }
+    }
+    // skip connection and store
+    const int64_t ybase = (tok0 * H + h) * (int64_t)P + a.p0;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * TILE + 4 * lg + r;
+        const int off = row * HP + 16 * ct + l16;
+        float xval;
+        if constexpr (IN_BF16)
+          xval = bf16_bits_to_f32(Xt[(16 * ct + l16) * XP + row]);
+        else
+          xval = (reinterpret_cast<const float*>(a.x) + ybase)[off];
+        const float v = acc[ct][r] + dsk * xval;
+        if (a.y_bf16)
+          (reinterpret_cast<uint16_t*>(a.y) + ybase)[off] = (uint16_t)f32_to_bf16_bits(v);
+        else
+          (reinterpret_cast<float*>(a.y) + ybase)[off] = v;
+      }
+    }
+  };
+
+  issue(a.hbase);
+  __syncthreads();  // every wave is done reading Bs before Xt/Ht overwrite it
+  commit();
+  __syncthreads();
+  make_w();
+  __syncthreads();
+
+  for (int hh = 0; hh < a.HG; ++hh) {
+    const int h = a.hbase + hh;
+    if (hh + 1 < a.HG) issue(h + 1);
+    const float dsk = a.D[h];
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    tile_out(std::integral_constant<int, hg_tile<W>(0)>{}, std::integral_constant<int, hg_slot_base<W>(0)>{}, h, dsk, ln);
+    asm volatile("" : "+v"(ln));
+    tile_out(std::integral_constant<int, hg_tile<W>(1)>{}, std::integral_constant<int, hg_slot_base<W>(1)>{}, h, dsk, ln);
+    if constexpr (PPW == 2) {
+      asm volatile("" : "+v"(ln));
+      tile_out(std::integral_constant<int, hg_tile<W>(2)>{}, std::integral_constant<int, hg_slot_base<W>(2)>{}, h, dsk, ln);
+      asm volatile("" : "+v"(ln));
+      tile_out(std::integral_constant<int, hg_tile<W>(3)>{}, std::integral_constant<int, hg_slot_base<W>(3)>{}, h, dsk, ln);
+    }
+    if (hh + 1 < a.HG) {
+      __syncthreads();  // all reads of this head's tiles are done
+      commit();
+      __syncthreads();
+      make_w();
+      __syncthreads();
+    }
+  }
+}
+
+template <int Q, int NK, int CT, bool IN_BF16, int W>
+__device__ __forceinline__ void hg_dispatch(const HgArgs& a, unsigned char* smem, int tid, int wave) {
+  if constexpr (W < HgCfg<Q, NK, CT>::NCW) {
+    if (wave == W)
+      hg_body<Q, NK, CT, IN_BF16, W>(a, smem, tid);
+    else
+      hg_dispatch<Q, NK, CT, IN_BF16, W + 1>(a, smem, tid, wave);
+  }
+}
+
+template <int Q, int NK, int CT, bool IN_BF16>
+__global__ __launch_bounds__(kHgThreads) void chunk_scan_hg_kernel(
+    const void* __restrict__ x, const void* __restrict__ Bm, const void* __restrict__ Cm,
+    const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const float* __restrict__ carried,
+    const float* __restrict__ D, void* __restrict__ y, int y_bf16, int L, int H, int P, int G, int nc, int HG,
+    int nhg, int npt, int remap) {
+  extern __shared__ __align__(16) unsigned char hg_smem[];
+  // block -> (b, c, g, head group, p slice).  With remap != 0 the mapping is
+  // XCD-aware: consecutive logical blocks (same chunk, neighbouring head
+  // groups) land on the same XCD and share its L2 for the B/C chunk.
+  const unsigned nblk = gridDim.x;
+  unsigned bid = blockIdx.x;
+  if (remap) bid = (bid & 7u) * (nblk >> 3) + (bid >> 3);
+  HgArgs a;
+  a.x = x; a.Bm = Bm; a.Cm = Cm; a.dt_bhl = dt_bhl; a.dA_cumsum = dA_cumsum; a.carried = carried; a.D = D; a.y = y;
+  a.y_bf16 = y_bf16; a.L = L; a.H = H; a.P = P; a.G = G; a.nc = nc; a.HG = HG;
+  const int pt = bid % npt;
+  unsigned rest = bid / npt;
+  const int hgi = rest % nhg;
+  rest /= nhg;
+  a.g = rest % G;
+  rest /= G;
+  a.c = rest % nc;
+  a.b = rest / nc;
+  a.hbase = a.g * (H / G) + hgi * HG;
+  a.p0 = pt * HgCfg<Q, NK, CT>::PT;
+  a.tok0 = (int64_t)a.b * L + (int64_t)a.c * Q;
+  hg_dispatch<Q, NK, CT, IN_BF16, 0>(a, hg_smem, threadIdx.x, threadIdx.x >> 6);
+}
+
+// ------------------------------------------------------------------ host side
+static int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+// Heads per block: the largest divisor HG of the group's head count such that
+// the grid still gives every CU at least one block.
+static int pick_heads_per_block(const Dims& d, int npt) {
+  const int64_t hpg = d.H / d.G;
+  const int64_t base = d.B * d.nc * d.G * npt;
+  const int cus = cu_count();
+  int best = 1;
+  for (int64_t k = 1; k <= hpg; ++k) {
+    if (hpg % k) continue;
+    best = (int)(hpg / k);
+    if (base * k >= cus) break;
+  }
+  return best;
+}
+
+template <int Q, int NK, bool IN_BF16>
+static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, const void* Cm, const float* dt_bhl,
+                                 const float* dA_cumsum, const float* carried, const float* D, void* y,
+                                 bool y_bf16, hipStream_t stream) {
+  constexpr int CT = 4;
+  using Cfg = HgCfg<Q, NK, CT>;
+  auto kern = chunk_scan_hg_kernel<Q, NK, CT, IN_BF16>;
+  const size_t lds = Cfg::lds_total;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int threads = Cfg::T;
+  const int npt = (int)(d.P / Cfg::PT);
+  const int HG = pick_heads_per_block(d, npt);
+  const int nhg = (int)(d.H / d.G) / HG;
+  const int64_t nblk = d.B * d.nc * d.G * nhg * npt;
+  const int remap = (nblk % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(threads), lds, stream, x, Bm, Cm, dt_bhl, dA_cumsum, carried,
+                     D, y, (int)y_bf16, (int)d.L, (int)d.H, (int)d.P, (int)d.G, (int)d.nc, HG, nhg, npt, remap);
+  return hipGetLastError();
+}
+
+template <int Q, int NK>
+static bool hg_fits() {
+  using Cfg = HgCfg<Q, NK, 4>;
+  return Cfg::lds_total <= 160 * 1024 && Q <= Cfg::T && (Q == 128 || Q == 256);
+}
+
+bool chunk_scan_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
+  if (f32_mma || !in_bf16) return false;
+  if (d.P % 64 != 0) return false;
+  if (d.nc * d.B * d.G * (d.H / d.G) * (d.P / 64) > 0x7fffffff) return false;
+  const int64_t key = d.Q * 1000 + d.N;
+  switch (key) {
+    case 128 * 1000 + 128: return hg_fits<128, 4>();
+    case 128 * 1000 + 256: return hg_fits<128, 8>();
+    case 256 * 1000 + 128: return hg_fits<256, 4>();
+    default: return false;
+  }
+}
+
+template <bool IN_BF16>
+static hipError_t launch_hg_dtype(const Dims& d, const void* x, const void* Bm, const void* Cm, const float* dt_bhl,
+                                  const float* dA_cumsum, const float* carried, const float* D, void* y, bool y_bf16,
+                                  hipStream_t stream) {
+  const int64_t key = d.Q * 1000 + d.N;
+#define HG_CASE(QQ, NN, KK) \
+  case QQ * 1000 + NN:      \
+    return launch_hg_inst<QQ, KK, IN_BF16>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream);
+  switch (key) {
+    HG_CASE(128, 128, 4)
+    HG_CASE(128, 256, 8)
+    HG_CASE(256, 128, 4)
+    default: return hipErrorInvalidValue;
+  }
+#undef HG_CASE
+}
+
+hipError_t launch_chunk_scan_hg(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
+                                const float* dt_bhl, const float* dA_cumsum, const float* carried, const float* D,
+                                void* y, bool y_bf16, hipStream_t stream) {
+  if (!in_bf16) return hipErrorInvalidValue;
+  return launch_hg_dtype<true>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream);
+}
+
+}  // namespace ssd

@@ -29,6 +29,14 @@ hipError_t launch_state_passing(const Dims& d, const float* chunk_states, float*
                                 const float* dA_cumsum, const float* initial_states,
                                 float* final_states, hipStream_t stream);
 
+// Head-group variant of the fused chunk output (bf16 inputs and operands,
+// (chunk, N) in {(128,128), (128,256), (256,128)}, P a multiple of 64);
+// launch_chunk_scan picks it when supported.
+bool chunk_scan_hg_supported(const Dims& d, bool in_bf16, bool f32_mma);
+hipError_t launch_chunk_scan_hg(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
+                                const float* dt_bhl, const float* dA_cumsum, const float* carried, const float* D,
+                                void* y, bool y_bf16, hipStream_t stream);
+
 hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
                              const float* dt_bhl, const float* dA_cumsum, const float* carried,
                              const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream);
