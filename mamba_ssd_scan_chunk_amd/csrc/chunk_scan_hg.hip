@@ -45,14 +45,13 @@
 
 namespace ssd {
 
-constexpr int kHgThreads = 256;  // 4 waves, one per SIMD: up to 512 registers each
+constexpr int hg_threads(int q) { return q >= 256 ? 512 : 256; }
 
 template <int Q, int NK, int CT>
 struct HgCfg {
   static constexpr int QT = Q / 16;
-  static constexpr int NCW = 4;       // compute waves
-  static constexpr int PPW = QT / 8;  // row-tile pairs per wave
-  static constexpr int T = kHgThreads;
+  static constexpr int NCW = QT / 2;  // compute waves: wave w owns row tiles w and QT-1-w
+  static constexpr int T = hg_threads(Q);
   static constexpr int PT = CT * 16;
   static constexpr int N = NK * 32;   // this variant needs N == NK*32
   static constexpr int NPI = N + 8;   // pitch (elements) of n-indexed LDS rows
@@ -64,17 +63,6 @@ struct HgCfg {
   static constexpr size_t lds_w = sizeof(float) * (size_t)(QT / 2) * Q;  // Ws
   static constexpr size_t lds_total = lds_a + lds_c + lds_w + 2 * sizeof(float) * Q;
 };
-
-// Row tile ti of wave W: pair p = ti / 2 gives tiles 8p + W (even ti) and
-// 8p + 7 - W (odd ti); each pair holds 16p + 9 causal sub-tiles.
-template <int W>
-constexpr int hg_tile(int ti) { return (ti & 1) ? 8 * (ti >> 1) + 7 - W : 8 * (ti >> 1) + W; }
-template <int W>
-constexpr int hg_slot_base(int ti) {
-  int sb = 0;
-  for (int k = 0; k < ti; ++k) sb += hg_tile<W>(k) + 1;
-  return sb;
-}
 
 struct HgArgs {
   const void* x;
@@ -90,7 +78,7 @@ struct HgArgs {
   int64_t tok0;
 };
 
-template <int Q, int NK, int CT, bool IN_BF16, int W>
+template <int Q, int NK, int CT, bool IN_BF16>
 __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, const int tid) {
   using Cfg = HgCfg<Q, NK, CT>;
   using Op = OpBF16;
@@ -102,8 +90,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   constexpr int XPT = (NXB + T - 1) / T;     // blocks per thread
   constexpr int HPT = (NHB + T - 1) / T;
   constexpr int TE = IN_BF16 ? 2 : 4;        // input element bytes
-  constexpr int PPW = Cfg::PPW;
-  constexpr int NSL = PPW == 1 ? 9 : 34;     // CB^T sub-tiles held (sum over the wave's tiles of tile+1)
+  constexpr int NSL = QT + 1;                // CB^T sub-tiles held per wave
 
   uint16_t* Bs = reinterpret_cast<uint16_t*>(smem);                    // [Q][NPI]  (phase 0-1 only)
   uint16_t* Xt = reinterpret_cast<uint16_t*>(smem);                    // [PT][XP]  (aliases Bs later)
@@ -134,25 +121,26 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   }
   __syncthreads();
 
-  // ---- phase 1: causal CB^T sub-tiles of the wave's row tiles (fp32, registers).
-  // For pair p the wave owns tiles 8p + W and 8p + 7 - W; slots are laid out
-  // tile after tile in that order (hg_slot_base), one per sub-tile js <= tile.
+  // ---- phase 1: causal CB^T sub-tiles of the wave's two row tiles (fp32,
+  // registers).  Tile ra = w keeps its sub-tile js at slot js, tile
+  // rb = QT-1-w at slot QT - js; the slots of a sub-tile pair (2k, 2k+1) are
+  // therefore compile-time constants whatever the wave.
+  const int wave = tid >> 6;
+  const int ra = wave, rb = QT - 1 - wave;
   f32x4_t cb[NSL];
 #pragma unroll
-  for (int ti = 0; ti < 2 * PPW; ++ti) {
-    const int tile = hg_tile<W>(ti);
-    const int sb = hg_slot_base<W>(ti);
+  for (int sl = 0; sl < NSL; ++sl) {
+    const bool first = sl <= ra;
+    const int js = first ? sl : QT - sl;
+    const int tile = first ? ra : rb;
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int js = 0; js <= tile; ++js) {
-      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NK; ++s) {
-        const Frag bf = Lds<Op>::load8(Bs + (16 * js + l16) * NPI + 32 * s + 8 * lg);
-        const Frag cf = Lds<Op>::load8(Cs + (16 * tile + l16) * NPI + 32 * s + 8 * lg);
-        acc = Op::mma(bf, cf, acc);
-      }
-      cb[sb + js] = acc;
+    for (int s = 0; s < NK; ++s) {
+      const Frag bf = Lds<Op>::load8(Bs + (16 * js + l16) * NPI + 32 * s + 8 * lg);
+      const Frag cf = Lds<Op>::load8(Cs + (16 * tile + l16) * NPI + 32 * s + 8 * lg);
+      acc = Op::mma(bf, cf, acc);
     }
+    cb[sl] = acc;
   }
 
   // ---- per-head register prefetch: issued before a head's compute,
@@ -253,110 +241,116 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 
   // One row tile of one head; TILE and SB (slot of its sub-tile js = 0) are
   // compile-time constants.
-  // `ln` is the lane index laundered through an empty asm at the top of each
-  // head iteration: every lane-dependent address, mask and offset below is
-  // recomputed per head instead of being hoisted out of the head loop, where
-  // hundreds of them would stay live and spill.
-  auto tile_out = [&](auto tile_c, auto sb_c, int h, float dsk, int ln) {
-    constexpr int TILE = decltype(tile_c)::value;
-    constexpr int SB = decltype(sb_c)::value;
+  // One row tile of one head.  TSEL (0: tile ra, 1: tile rb) fixes the slot
+  // map; the tile index itself is a run-time value, so all waves share one
+  // copy of this code.  `ln` is the lane index laundered through an empty asm
+  // at the top of each head iteration: lane-dependent addresses, masks and
+  // offsets are recomputed per head instead of being hoisted out of the head
+  // loop, where they would stay live and spill.
+  auto tile_out = [&](auto tsel_c, const int tile, int h, float dsk, int ln) {
+    constexpr int TSEL = decltype(tsel_c)::value;
     const int l16 = ln & 15, lg = ln >> 4;
-    constexpr int U = TILE / 2;  // pairs k < U are off-diagonal; pair U holds the diagonal
-    constexpr int R = 32 * U;    // reference row of the factorised decay
+    const int U = tile >> 1;  // pairs k < U are off-diagonal; pair U holds the diagonal
+    const int R = 32 * U;     // reference row of the factorised decay
     const float gR = Gs[R];
     f32x4_t acc[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // carried-state term C_i . H_in, scaled by exp(G_R) now and by exp(G_i - G_R) below
+    // The output tile is accumulated TRANSPOSED, Y^T = H^T C^T + X^T M^T
+    // (operand order swapped, same fragments), so that lane (l16, lg) holds
+    // y[i = 16*tile + l16][p = 16ct + 4lg + r] for r = 0..3: four consecutive
+    // p of one token, written with one 8-byte (bf16) or 16-byte (fp32) store.
+    // carried-state term, scaled by exp(G_R) now and by exp(G_i - G_R) below
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
-      const Frag ca = Lds<Op>::load8(Cs + (16 * TILE + l16) * NPI + 32 * s + 8 * lg);
+      const Frag ca = Lds<Op>::load8(Cs + (16 * tile + l16) * NPI + 32 * s + 8 * lg);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
-        acc[ct] = Op::mma(ca, Lds<Op>::load8(Ht + (16 * ct + l16) * NPI + 32 * s + 8 * lg), acc[ct]);
+        acc[ct] = Op::mma(Lds<Op>::load8(Ht + (16 * ct + l16) * NPI + 32 * s + 8 * lg), ca, acc[ct]);
     }
     {
       const float eR = fast_exp(gR);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) acc[ct] *= eR;
     }
-    // off-diagonal pairs: M' = CB * Ws[U][j]
+    const int i = 16 * tile + l16;  // the token this lane's interaction values and outputs belong to
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      float m[8];
+    for (int k = 0; k < QT / 2; ++k) {
+      if (k < U) {
+        // off-diagonal pair: M' = CB * Ws[U][j]
+        float m[8];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int js = 2 * k + t;
-        const f32x4_t cv = cb[SB + js];
-        const float4 w = *reinterpret_cast<const float4*>(Ws + U * Q + 16 * js + 4 * lg);
-        m[4 * t + 0] = cv[0] * w.x;
-        m[4 * t + 1] = cv[1] * w.y;
-        m[4 * t + 2] = cv[2] * w.z;
-        m[4 * t + 3] = cv[3] * w.w;
-      }
-      const Frag mf = Op::from_f32(m);
+        for (int t = 0; t < 2; ++t) {
+          const int js = 2 * k + t;
+          const f32x4_t cv = cb[TSEL ? (QT - js) : js];
+          const float4 w = *reinterpret_cast<const float4*>(Ws + U * Q + 16 * js + 4 * lg);
+          m[4 * t + 0] = cv[0] * w.x;
+          m[4 * t + 1] = cv[1] * w.y;
+          m[4 * t + 2] = cv[2] * w.z;
+          m[4 * t + 3] = cv[3] * w.w;
+        }
+        const Frag mf = Op::from_f32(m);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const uint16_t* xr = Xt + (16 * ct + l16) * XP + 32 * k + 4 * lg;
-        acc[ct] = Op::mma(mf, Lds<Op>::load4x2(xr, xr + 16), acc[ct]);
-      }
-    }
-    // row factor exp(G_i - G_R) for the output rows this lane holds
+        for (int ct = 0; ct < CT; ++ct) {
+          const uint16_t* xr = Xt + (16 * ct + l16) * XP + 32 * k + 4 * lg;
+          acc[ct] = Op::mma(Lds<Op>::load4x2(xr, xr + 16), mf, acc[ct]);
+        }
+      } else if (k == U) {
+        const float gi = Gs[i];
+        // row factor exp(G_i - G_R)
+        {
+          const float e = fast_exp(gi - gR);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float e = fast_exp(Gs[16 * TILE + 4 * lg + r] - gR);
+          for (int ct = 0; ct < CT; ++ct) acc[ct] *= e;
+        }
+        // diagonal pair: exact decay, causal select before exp
+        float m[8];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) acc[ct][r] *= e;
-    }
-    // diagonal pair: exact decay, causal select before exp
-    {
-      const int i = 16 * TILE + l16;
-      const float gi = Gs[i];
-      float m[8];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int js = 2 * U + t;
-        if (js <= TILE) {
-          const f32x4_t cv = cb[SB + js];
+        for (int t = 0; t < 2; ++t) {
+          const int js = 2 * k + t;
+          const f32x4_t cv = cb[TSEL ? (QT - js) : js];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j = 16 * js + 4 * lg + r;
-            const bool keep = j <= i;
+            const bool keep = (js <= tile) && (j <= i);
             const int jc = keep ? j : i;
             const float dec = fast_exp(keep ? gi - Gs[jc] : -INFINITY) * dts[jc];
             m[4 * t + r] = keep ? cv[r] * dec : 0.f;
           }
-        } else {
+        }
+        const Frag mf = Op::from_f32(m);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) m[4 * t + r] = 0.f;
+        for (int ct = 0; ct < CT; ++ct) {
+          const uint16_t* xr = Xt + (16 * ct + l16) * XP + 32 * k + 4 * lg;
+          acc[ct] = Op::mma(Lds<Op>::load4x2(xr, xr + 16), mf, acc[ct]);
         }
       }
-      const Frag mf = Op::from_f32(m);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const uint16_t* xr = Xt + (16 * ct + l16) * XP + 32 * U + 4 * lg;
-        acc[ct] = Op::mma(mf, Lds<Op>::load4x2(xr, xr + 16), acc[ct]);
-      }
     }
-    // skip connection and store
+    // skip connection and store: y[i][16ct + 4lg .. +3]
     const int64_t ybase = (tok0 * H + h) * (int64_t)P + a.p0;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
+      const int pc = 16 * ct + 4 * lg;
+      const int off = i * HP + pc;
+      float xv[4];
+      if constexpr (IN_BF16) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * TILE + 4 * lg + r;
-        const int off = row * HP + 16 * ct + l16;
-        float xval;
-        if constexpr (IN_BF16)
-          xval = bf16_bits_to_f32(Xt[(16 * ct + l16) * XP + row]);
-        else
-          xval = (reinterpret_cast<const float*>(a.x) + ybase)[off];
-        const float v = acc[ct][r] + dsk * xval;
-        if (a.y_bf16)
-          (reinterpret_cast<uint16_t*>(a.y) + ybase)[off] = (uint16_t)f32_to_bf16_bits(v);
-        else
-          (reinterpret_cast<float*>(a.y) + ybase)[off] = v;
+        for (int r = 0; r < 4; ++r) xv[r] = bf16_bits_to_f32(Xt[(pc + r) * XP + i]);
+      } else {
+        const float4 q = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + ybase + off);
+        xv[0] = q.x; xv[1] = q.y; xv[2] = q.z; xv[3] = q.w;
+      }
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = acc[ct][r] + dsk * xv[r];
+      if (a.y_bf16) {
+        uint2 w;
+        w.x = pack_bf16x2(v[0], v[1]);
+        w.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + ybase + off) = w;
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + ybase + off) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
   };
@@ -374,15 +368,11 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     const float dsk = a.D[h];
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    tile_out(std::integral_constant<int, hg_tile<W>(0)>{}, std::integral_constant<int, hg_slot_base<W>(0)>{}, h, dsk, ln);
+    int wv = wave;
+    asm volatile("" : "+v"(wv));
+    tile_out(std::integral_constant<int, 0>{}, wv, h, dsk, ln);
     asm volatile("" : "+v"(ln));
-    tile_out(std::integral_constant<int, hg_tile<W>(1)>{}, std::integral_constant<int, hg_slot_base<W>(1)>{}, h, dsk, ln);
-    if constexpr (PPW == 2) {
-      asm volatile("" : "+v"(ln));
-      tile_out(std::integral_constant<int, hg_tile<W>(2)>{}, std::integral_constant<int, hg_slot_base<W>(2)>{}, h, dsk, ln);
-      asm volatile("" : "+v"(ln));
-      tile_out(std::integral_constant<int, hg_tile<W>(3)>{}, std::integral_constant<int, hg_slot_base<W>(3)>{}, h, dsk, ln);
-    }
+    tile_out(std::integral_constant<int, 1>{}, QT - 1 - wv, h, dsk, ln);
     if (hh + 1 < a.HG) {
       __syncthreads();  // all reads of this head's tiles are done
       commit();
@@ -393,18 +383,8 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   }
 }
 
-template <int Q, int NK, int CT, bool IN_BF16, int W>
-__device__ __forceinline__ void hg_dispatch(const HgArgs& a, unsigned char* smem, int tid, int wave) {
-  if constexpr (W < HgCfg<Q, NK, CT>::NCW) {
-    if (wave == W)
-      hg_body<Q, NK, CT, IN_BF16, W>(a, smem, tid);
-    else
-      hg_dispatch<Q, NK, CT, IN_BF16, W + 1>(a, smem, tid, wave);
-  }
-}
-
 template <int Q, int NK, int CT, bool IN_BF16>
-__global__ __launch_bounds__(kHgThreads) void chunk_scan_hg_kernel(
+__global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, const void* __restrict__ Cm,
     const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const float* __restrict__ carried,
     const float* __restrict__ D, void* __restrict__ y, int y_bf16, int L, int H, int P, int G, int nc, int HG,
@@ -430,7 +410,7 @@ __global__ __launch_bounds__(kHgThreads) void chunk_scan_hg_kernel(
   a.hbase = a.g * (H / G) + hgi * HG;
   a.p0 = pt * HgCfg<Q, NK, CT>::PT;
   a.tok0 = (int64_t)a.b * L + (int64_t)a.c * Q;
-  hg_dispatch<Q, NK, CT, IN_BF16, 0>(a, hg_smem, threadIdx.x, threadIdx.x >> 6);
+  hg_body<Q, NK, CT, IN_BF16>(a, hg_smem, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ host side
@@ -488,7 +468,7 @@ static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, c
 template <int Q, int NK>
 static bool hg_fits() {
   using Cfg = HgCfg<Q, NK, 4>;
-  return Cfg::lds_total <= 160 * 1024 && Q <= Cfg::T && (Q == 128 || Q == 256);
+  return Cfg::lds_total <= 160 * 1024 && Q <= Cfg::T && 64 * Cfg::NCW <= Cfg::T && (Q == 128 || Q == 256);
 }
 
 bool chunk_scan_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {

@@ -195,6 +195,8 @@ static hipError_t launch_state_op(const Dims& d, const void* x, const void* Bm, 
 hipError_t launch_chunk_state(const Dims& d, const void* x, const void* Bm, bool in_bf16,
                               const float* dt_bhl, const float* dA_cumsum, float* states,
                               bool f32_mma, hipStream_t stream) {
+  if (chunk_state_hg_supported(d, in_bf16, f32_mma))
+    return launch_chunk_state_hg(d, x, Bm, dt_bhl, dA_cumsum, states, stream);
   const size_t lds = chunk_state_lds_bytes(d, f32_mma);
   if (f32_mma) return launch_state_op<OpF32>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
   return launch_state_op<OpBF16>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);

@@ -1,0 +1,248 @@
+// chunk_state_hg.hip -- per-chunk states, head-group variant (bf16 operands).
+//
+// Page: "Jane Street ML Engineers Map Mamba-2 Recurrent State Computation to
+// Tensor Cores with cuTile" (disconfirmai.com), jump-formula paragraph: the
+// state advance over a chunk is one matrix product of the stacked b and x
+// rows, and pre-multiplying rows by exponentials of the log-space sums keeps
+// it one.  For chunk c of (b, h):
+//     S[n][p] = sum_j B[j][n] * w_j * x[j][p],   w_j = exp(G_{Q-1} - G_j) dt_j
+// The weight is folded into the x rows, so the B tile is the raw input shared
+// by every head of a group.
+//
+// One block owns a (b, c, group, 64-column slice of P) and a run of HG heads of
+// that group.  The chunk's B rows are staged ONCE, transposed (Bt[n][j], the
+// token contiguous as the contraction needs), through 8x8 register
+// transposes.  Per head, each thread prefetches 4-token x 8-column blocks of x
+// plus the G and dt of those tokens into registers while the previous head
+// computes; at commit the rows are scaled by w_j in fp32, rounded to bf16 and
+// written transposed (Xt[p][j]).  The output is accumulated transposed,
+// D[p][n] = sum_j Xt[p][j] Bt[n][j], so that each lane holds four consecutive
+// p of one state row n and writes them as one 16-byte store.
+// 4 waves (one per SIMD); wave w owns the state rows n in tiles 2w, 2w+1
+// (N = 128) or 4w..4w+3 (N = 256) for all 4 column tiles of the slice.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+constexpr int kShgThreads = 256;
+
+template <int Q, int N>
+struct ShgCfg {
+  static constexpr int T = kShgThreads;
+  static constexpr int PT = 64;
+  static constexpr int KP = Q + 8;                 // pitch of Bt / Xt rows (elements)
+  static constexpr int NTW = N / 16 / 4;           // state-row tiles per wave
+  static constexpr size_t lds_b = (size_t)N * KP * 2;
+  static constexpr size_t lds_x = (size_t)PT * KP * 2;
+  static constexpr size_t lds_total = lds_b + lds_x;
+};
+
+template <int Q, int N>
+__global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bhl,
+    const float* __restrict__ dA_cumsum, float* __restrict__ states, int L, int H, int P, int G, int nc, int HG,
+    int nhg, int npt, int remap) {
+  using Cfg = ShgCfg<Q, N>;
+  using Op = OpBF16;
+  using Frag = Op::Frag;
+  constexpr int T = Cfg::T, PT = Cfg::PT, KP = Cfg::KP, NTW = Cfg::NTW;
+  constexpr int NXB = (Q / 4) * (PT / 8);  // x prefetch blocks: 4 tokens x 8 columns
+  constexpr int XPT = NXB / T;
+  static_assert(NXB % T == 0, "x blocks must divide evenly");
+
+  extern __shared__ __align__(16) unsigned char shg_smem[];
+  uint16_t* Bt = reinterpret_cast<uint16_t*>(shg_smem);  // [N][KP]
+  uint16_t* Xt = Bt + N * KP;                             // [PT][KP]
+
+  const unsigned nblk = gridDim.x;
+  unsigned bid = blockIdx.x;
+  if (remap) bid = (bid & 7u) * (nblk >> 3) + (bid >> 3);
+  const int pt = bid % npt;
+  unsigned rest = bid / npt;
+  const int hgi = rest % nhg;
+  rest /= nhg;
+  const int g = rest % G;
+  rest /= G;
+  const int c = rest % nc;
+  const int b = rest / nc;
+  const int hbase = g * (H / G) + hgi * HG;
+  const int p0 = pt * PT;
+  const int64_t tok0 = (int64_t)b * L + (int64_t)c * Q;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int HP = H * P;
+
+  // ---- B chunk -> Bt[n][j] (8x8 register transposes, 16-byte loads and stores)
+  {
+    const uint16_t* bsrc = Bm + (tok0 * G + g) * N;
+    const int GN = G * N;
+    for (int blk = tid; blk < (Q / 8) * (N / 8); blk += T) {
+      const int nb = blk % (N / 8), jb = blk / (N / 8);
+      uint4 rows[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) rows[r] = *reinterpret_cast<const uint4*>(bsrc + (8 * jb + r) * GN + 8 * nb);
+      const uint32_t* rw = reinterpret_cast<const uint32_t*>(rows);  // rw[4r + q/2] holds columns 2*(q/2), +1 of row r
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        uint32_t o[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const uint32_t lo = rw[4 * (2 * rr) + q / 2], hi = rw[4 * (2 * rr + 1) + q / 2];
+          o[rr] = (q & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        }
+        *reinterpret_cast<uint4*>(Bt + (8 * nb + q) * KP + 8 * jb) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+
+  // ---- per-head register prefetch of x, G and dt
+  uint4 xv[XPT][4];
+  float4 gv[XPT], dv[XPT];
+  float glast = 0.f;
+  auto issue = [&](int h) {
+    const uint16_t* xs = x + (tok0 * H + h) * (int64_t)P + p0;
+    const int64_t bhc = ((int64_t)b * H + h) * nc + c;
+    const float* gsrc = dA_cumsum + bhc * Q;
+    const float* dsrc = dt_bhl + bhc * Q;
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int blk = tid + u * T;
+      const int cb = blk % (PT / 8), rb = blk / (PT / 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xv[u][r] = *reinterpret_cast<const uint4*>(xs + (4 * rb + r) * HP + 8 * cb);
+      gv[u] = *reinterpret_cast<const float4*>(gsrc + 4 * rb);
+      dv[u] = *reinterpret_cast<const float4*>(dsrc + 4 * rb);
+    }
+    glast = gsrc[Q - 1];
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int blk = tid + u * T;
+      const int cb = blk % (PT / 8), rb = blk / (PT / 8);
+      const float w[4] = {fast_exp(glast - gv[u].x) * dv[u].x, fast_exp(glast - gv[u].y) * dv[u].y,
+                          fast_exp(glast - gv[u].z) * dv[u].z, fast_exp(glast - gv[u].w) * dv[u].w};
+      float v[4][8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint4 q = xv[u][r];
+        v[r][0] = bf16_bits_to_f32(q.x & 0xffffu) * w[r]; v[r][1] = bf16_bits_to_f32(q.x >> 16) * w[r];
+        v[r][2] = bf16_bits_to_f32(q.y & 0xffffu) * w[r]; v[r][3] = bf16_bits_to_f32(q.y >> 16) * w[r];
+        v[r][4] = bf16_bits_to_f32(q.z & 0xffffu) * w[r]; v[r][5] = bf16_bits_to_f32(q.z >> 16) * w[r];
+        v[r][6] = bf16_bits_to_f32(q.w & 0xffffu) * w[r]; v[r][7] = bf16_bits_to_f32(q.w >> 16) * w[r];
+      }
+#pragma unroll
+      for (int col = 0; col < 8; ++col) {
+        uint2 o;
+        o.x = pack_bf16x2(v[0][col], v[1][col]);
+        o.y = pack_bf16x2(v[2][col], v[3][col]);
+        *reinterpret_cast<uint2*>(Xt + (8 * cb + col) * KP + 4 * rb) = o;
+      }
+    }
+  };
+
+  issue(hbase);
+  __syncthreads();  // Bt complete
+  commit();
+  __syncthreads();
+
+  for (int hh = 0; hh < HG; ++hh) {
+    const int h = hbase + hh;
+    if (hh + 1 < HG) issue(h + 1);
+    {
+      // lane index laundered per head: lane-dependent addresses are recomputed
+      // here rather than hoisted out of the head loop
+      int ln = tid & 63;
+      asm volatile("" : "+v"(ln));
+      const int l16 = ln & 15, lg = ln >> 4;
+      f32x4_t acc[NTW][4];
+#pragma unroll
+      for (int i = 0; i < NTW; ++i)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[i][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+      for (int kk = 0; kk < Q / 32; ++kk) {
+        Frag xf[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) xf[ct] = Lds<Op>::load8(Xt + (16 * ct + l16) * KP + 32 * kk + 8 * lg);
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+          const Frag bf = Lds<Op>::load8(Bt + (16 * (NTW * wave + i) + l16) * KP + 32 * kk + 8 * lg);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) acc[i][ct] = Op::mma(xf[ct], bf, acc[i][ct]);
+        }
+      }
+      // lane holds S[n = 16*(NTW*wave + i) + l16][p = p0 + 16ct + 4lg .. +3]
+      float* so = states + (((int64_t)b * nc + c) * H + h) * (int64_t)(N * P) + p0;
+#pragma unroll
+      for (int i = 0; i < NTW; ++i) {
+        const int n = 16 * (NTW * wave + i) + l16;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          *reinterpret_cast<float4*>(so + n * P + 16 * ct + 4 * lg) =
+              make_float4(acc[i][ct][0], acc[i][ct][1], acc[i][ct][2], acc[i][ct][3]);
+      }
+    }
+    if (hh + 1 < HG) {
+      __syncthreads();  // all reads of this head's Xt are done
+      commit();
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host side
+static int shg_cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+bool chunk_state_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
+  if (f32_mma || !in_bf16 || d.P % 64 != 0) return false;
+  return (d.Q == 256 && d.N == 128) || (d.Q == 128 && d.N == 256);
+}
+
+template <int Q, int N>
+static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
+                                  const float* dA_cumsum, float* states, hipStream_t stream) {
+  using Cfg = ShgCfg<Q, N>;
+  auto kern = chunk_state_hg_kernel<Q, N>;
+  const size_t lds = Cfg::lds_total;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int npt = (int)(d.P / Cfg::PT);
+  const int64_t hpg = d.H / d.G;
+  const int64_t base = d.B * d.nc * d.G * npt;
+  int HG = 1;
+  for (int64_t k = 1; k <= hpg; ++k) {
+    if (hpg % k) continue;
+    HG = (int)(hpg / k);
+    if (base * k >= shg_cu_count()) break;
+  }
+  const int nhg = (int)(hpg / HG);
+  const int64_t nblk = base * nhg;
+  const int remap = (nblk % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(Cfg::T), lds, stream, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(Bm), dt_bhl, dA_cumsum, states, (int)d.L, (int)d.H, (int)d.P,
+                     (int)d.G, (int)d.nc, HG, nhg, npt, remap);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_state_hg(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
+                                 const float* dA_cumsum, float* states, hipStream_t stream) {
+  if (d.Q == 256 && d.N == 128) return launch_shg_inst<256, 128>(d, x, Bm, dt_bhl, dA_cumsum, states, stream);
+  if (d.Q == 128 && d.N == 256) return launch_shg_inst<128, 256>(d, x, Bm, dt_bhl, dA_cumsum, states, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssd
