@@ -112,11 +112,18 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     for (int idx = tid; idx < Q * (N / 8); idx += T) {
       const int j = idx / (N / 8), nb = idx - (idx / (N / 8)) * (N / 8);
       const int off = j * GN + 8 * nb;
-      float t[8];
-      load8_as_f32(a.Bm, bc0 + off, IN_BF16, t);
-      Lds<Op>::store8(Bs + j * NPI + 8 * nb, t);
-      load8_as_f32(a.Cm, bc0 + off, IN_BF16, t);
-      Lds<Op>::store8(Cs + j * NPI + 8 * nb, t);
+      if constexpr (IN_BF16) {
+        *reinterpret_cast<uint4*>(Bs + j * NPI + 8 * nb) =
+            *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Bm) + bc0 + off);
+        *reinterpret_cast<uint4*>(Cs + j * NPI + 8 * nb) =
+            *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Cm) + bc0 + off);
+      } else {
+        float t[8];
+        load8_as_f32(a.Bm, bc0 + off, false, t);
+        Lds<Op>::store8(Bs + j * NPI + 8 * nb, t);
+        load8_as_f32(a.Cm, bc0 + off, false, t);
+        Lds<Op>::store8(Cs + j * NPI + 8 * nb, t);
+      }
     }
   }
   __syncthreads();
@@ -185,26 +192,35 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       const int blk = tid + uu * T;
       if (blk < NXB) {
         const int cbk = blk % (PT / XW), rbk = blk / (PT / XW);
-        float v[4][XW];
+        if constexpr (IN_BF16) {
+          // bf16 x: the transpose is a pure 16-bit shuffle, no conversion
+          const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&xv[uu][0]);
+          const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&xv[uu][1]);
+          const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&xv[uu][2]);
+          const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&xv[uu][3]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint4 q = xv[uu][r];
-          if constexpr (IN_BF16) {
-            v[r][0] = bf16_bits_to_f32(q.x & 0xffffu); v[r][1] = bf16_bits_to_f32(q.x >> 16);
-            v[r][2] = bf16_bits_to_f32(q.y & 0xffffu); v[r][3] = bf16_bits_to_f32(q.y >> 16);
-            v[r][4] = bf16_bits_to_f32(q.z & 0xffffu); v[r][5] = bf16_bits_to_f32(q.z >> 16);
-            v[r][6] = bf16_bits_to_f32(q.w & 0xffffu); v[r][7] = bf16_bits_to_f32(q.w >> 16);
-          } else {
+          for (int col = 0; col < 8; ++col) {
+            const int m = col >> 1;
+            uint2 w;
+            w.x = (col & 1) ? pick_hi16(r0[m], r1[m]) : pick_lo16(r0[m], r1[m]);
+            w.y = (col & 1) ? pick_hi16(r2[m], r3[m]) : pick_lo16(r2[m], r3[m]);
+            *reinterpret_cast<uint2*>(Xt + (XW * cbk + col) * XP + 4 * rbk) = w;
+          }
+        } else {
+          float v[4][XW];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint4 q = xv[uu][r];
             v[r][0] = __uint_as_float(q.x); v[r][1] = __uint_as_float(q.y);
             v[r][2] = __uint_as_float(q.z); v[r][3] = __uint_as_float(q.w);
           }
-        }
 #pragma unroll
-        for (int col = 0; col < XW; ++col) {
-          uint2 w;
-          w.x = pack_bf16x2(v[0][col], v[1][col]);
-          w.y = pack_bf16x2(v[2][col], v[3][col]);
-          *reinterpret_cast<uint2*>(Xt + (XW * cbk + col) * XP + 4 * rbk) = w;
+          for (int col = 0; col < XW; ++col) {
+            uint2 w;
+            w.x = pack_bf16x2(v[0][col], v[1][col]);
+            w.y = pack_bf16x2(v[2][col], v[3][col]);
+            *reinterpret_cast<uint2*>(Xt + (XW * cbk + col) * XP + 4 * rbk) = w;
+          }
         }
       }
     }

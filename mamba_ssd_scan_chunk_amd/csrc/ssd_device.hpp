@@ -23,17 +23,23 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Round to nearest even; NaN stays NaN (quiet bit set).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32 (one
+// instruction converts two values).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+// Low (sel = 0) or high (sel = 1) 16-bit halves of two words, packed as
+// (a's half) | (b's half) << 16.
+__device__ __forceinline__ uint32_t pick_lo16(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t pick_hi16(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
 
 // Operand-type traits.  Frag<T>::type holds 8 contraction slots of one lane.
 struct OpBF16 {

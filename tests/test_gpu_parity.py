@@ -136,6 +136,27 @@ def test_chunk_scan(shape, mode, y_dtype):
     assert e <= tol_for(mma)
 
 
+@pytest.mark.parametrize("mma", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[4]], ids=[SHAPES[1][0], SHAPES[4][0]])
+def test_bf16_output_rounding_is_rne(shape, mma):
+    """The bf16 output is the round-to-nearest-even of the fp32 output of the
+    same kernel (same accumulators, only the final conversion differs)."""
+    from mamba_ssd_scan_chunk_amd.inputs import bf16_round
+    say(f"bf16 output rounding {shape} {mma}")
+    inp = _inp(shape, "bf16", seed=12, dt_shift=2.0)
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    S = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma=mma)
+    car, _ = ops.ssd_state_passing(sh, S, dA)
+    y32 = ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, car, t["D"], y_dtype="f32", mma=mma)
+    y16 = ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, car, t["D"], y_dtype="bf16", mma=mma)
+    torch.cuda.synchronize()
+    expect = bf16_round(y32.cpu().numpy())
+    got = y16.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, expect)
+
+
 @pytest.mark.parametrize("mode", MODES, ids=["-".join(m) for m in MODES])
 @pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
 def test_forward(shape, mode):
