@@ -280,10 +280,13 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     // carried-state term, scaled by exp(G_R) now and by exp(G_i - G_R) below
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
+      // all fragments of the step first, then the MFMAs (one LDS round trip per step)
       const Frag ca = Lds<Op>::load8(Cs + (16 * tile + l16) * NPI + 32 * s + 8 * lg);
+      Frag hf[CT];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        acc[ct] = Op::mma(Lds<Op>::load8(Ht + (16 * ct + l16) * NPI + 32 * s + 8 * lg), ca, acc[ct]);
+      for (int ct = 0; ct < CT; ++ct) hf[ct] = Lds<Op>::load8(Ht + (16 * ct + l16) * NPI + 32 * s + 8 * lg);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct] = Op::mma(hf[ct], ca, acc[ct]);
     }
     {
       const float eR = fast_exp(gR);
@@ -294,24 +297,23 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 #pragma unroll
     for (int k = 0; k < QT / 2; ++k) {
       if (k < U) {
-        // off-diagonal pair: M' = CB * Ws[U][j]
-        float m[8];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int js = 2 * k + t;
-          const f32x4_t cv = cb[TSEL ? (QT - js) : js];
-          const float4 w = *reinterpret_cast<const float4*>(Ws + U * Q + 16 * js + 4 * lg);
-          m[4 * t + 0] = cv[0] * w.x;
-          m[4 * t + 1] = cv[1] * w.y;
-          m[4 * t + 2] = cv[2] * w.z;
-          m[4 * t + 3] = cv[3] * w.w;
-        }
-        const Frag mf = Op::from_f32(m);
+        // off-diagonal pair: M' = CB * Ws[U][j].  All LDS reads of the step
+        // are issued before the arithmetic and the MFMAs.
+        Frag xf[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const uint16_t* xr = Xt + (16 * ct + l16) * XP + 32 * k + 4 * lg;
-          acc[ct] = Op::mma(Lds<Op>::load4x2(xr, xr + 16), mf, acc[ct]);
+          xf[ct] = Lds<Op>::load4x2(xr, xr + 16);
         }
+        const float4 w0 = *reinterpret_cast<const float4*>(Ws + U * Q + 32 * k + 4 * lg);
+        const float4 w1 = *reinterpret_cast<const float4*>(Ws + U * Q + 32 * k + 16 + 4 * lg);
+        const f32x4_t c0 = cb[TSEL ? (QT - 2 * k) : 2 * k];
+        const f32x4_t c1 = cb[TSEL ? (QT - 2 * k - 1) : 2 * k + 1];
+        const float m[8] = {c0[0] * w0.x, c0[1] * w0.y, c0[2] * w0.z, c0[3] * w0.w,
+                            c1[0] * w1.x, c1[1] * w1.y, c1[2] * w1.z, c1[3] * w1.w};
+        const Frag mf = Op::from_f32(m);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[ct] = Op::mma(xf[ct], mf, acc[ct]);
       } else if (k == U) {
         const float gi = Gs[i];
         // row factor exp(G_i - G_R)
@@ -336,11 +338,14 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
           }
         }
         const Frag mf = Op::from_f32(m);
+        Frag xf[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const uint16_t* xr = Xt + (16 * ct + l16) * XP + 32 * k + 4 * lg;
-          acc[ct] = Op::mma(Lds<Op>::load4x2(xr, xr + 16), mf, acc[ct]);
+          xf[ct] = Lds<Op>::load4x2(xr, xr + 16);
         }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[ct] = Op::mma(xf[ct], mf, acc[ct]);
       }
     }
     // skip connection and store: y[i][16ct + 4lg .. +3]
@@ -384,8 +389,11 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     const float dsk = a.D[h];
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    // wave index laundered as well, then made wave-uniform (an SGPR), so the
+    // branches on the tile index are scalar branches
     int wv = wave;
     asm volatile("" : "+v"(wv));
+    wv = __builtin_amdgcn_readfirstlane(wv);
     tile_out(std::integral_constant<int, 0>{}, wv, h, dsk, ln);
     asm volatile("" : "+v"(ln));
     tile_out(std::integral_constant<int, 1>{}, QT - 1 - wv, h, dsk, ln);
