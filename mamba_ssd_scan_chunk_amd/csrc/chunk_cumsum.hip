@@ -1,5 +1,5 @@
 // chunk_cumsum.hip -- log-space decay cumulative sum, one segmented wave64 scan
-// per (batch, chunk, head).
+// per (batch, chunk, 4 heads).
 //
 // Page: "Jane Street ML Engineers Map Mamba-2 Recurrent State Computation to
 // Tensor Cores with cuTile" (disconfirmai.com), paragraph on the three kernels
@@ -10,59 +10,64 @@
 //   dA_cumsum[b,h,c,i] = sum_{k<=i} dt[b,cQ+k,h] * A[h]      (fp32, inclusive)
 //   dt_bhl[b,h,c,i]    = dt[b,cQ+i,h]
 //
-// Layout work: dt arrives [B,L,H] (head fastest).  A block reads a Q x 16-head
-// tile with head-contiguous (coalesced) loads, transposes it through LDS, and
-// each wave scans one head's Q values: Q/64 consecutive values per lane are
-// summed serially, then the 64 lane totals are combined with a log-depth
-// (6-step) shuffle scan.  Every output row (one head, one chunk) is written as
-// Q contiguous floats.
+// One wave owns (b, c, heads 4q..4q+3).  Lane l holds the E = Q/64
+// consecutive tokens lE..lE+E-1 of all four heads (16-byte loads of dt when
+// H % 4 == 0), sums them serially, and the 64 lane totals are combined with a
+// log-depth (6-step) shuffle scan per head.  Each lane then writes its E
+// values of each head as one contiguous run, so every output row (one head,
+// one chunk) is written as Q contiguous floats.  No LDS is used.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
 namespace ssd {
 
-constexpr int kCsHeads = 16;
 constexpr int kCsThreads = 256;
 
 __global__ __launch_bounds__(kCsThreads) void chunk_cumsum_kernel(
     const float* __restrict__ dt, const float* __restrict__ A, float* __restrict__ dA_cumsum,
-    float* __restrict__ dt_bhl, int L, int H, int Q, int nc) {
-  extern __shared__ float cs_lds[];
-  const int pitch = Q + 1;
-  float* sa = cs_lds;                     // [16][Q+1]  dt*A
-  float* sd = cs_lds + kCsHeads * pitch;  // [16][Q+1]  dt
-  const int hb = blockIdx.x * kCsHeads;
-  const int c = blockIdx.y;
-  const int b = blockIdx.z;
-  const int nh = min(kCsHeads, H - hb);
-  const int tid = threadIdx.x;
+    float* __restrict__ dt_bhl, int L, int H, int Q, int nc, int nq, int64_t nwaves) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * (kCsThreads / 64) + (threadIdx.x >> 6);
+  if (wid >= nwaves) return;  // whole wave exits together
+  const int q = (int)(wid % nq);
+  const int64_t bc = wid / nq;
+  const int c = (int)(bc % nc);
+  const int b = (int)(bc / nc);
+  const int h0 = 4 * q;
+  const int E = Q >= 64 ? Q / 64 : 1;  // tokens per lane (<= 4 for Q <= 256)
+  const int active = Q / E;            // lanes that hold tokens
+  const bool vec = (H % 4 == 0);       // 16-byte aligned head quadruples
 
-  const int64_t row0 = (int64_t)b * L + (int64_t)c * Q;
-  for (int idx = tid; idx < Q * kCsHeads; idx += kCsThreads) {
-    const int i = idx / kCsHeads, hh = idx % kCsHeads;
-    float v = 0.f, av = 0.f;
-    if (hh < nh) {
-      v = dt[(row0 + i) * H + hb + hh];
-      av = v * A[hb + hh];
-    }
-    sa[hh * pitch + i] = av;
-    sd[hh * pitch + i] = v;
-  }
-  __syncthreads();
-
-  const int wave = tid / 64, lane = tid % 64;
-  const int E = Q >= 64 ? Q / 64 : 1;  // values per lane (<= 4 for Q <= 256)
-  const int active = Q / E;            // lanes that hold values
-  for (int hh = wave; hh < nh; hh += kCsThreads / 64) {
-    float part[4];
-    float run = 0.f;
+  float a[4], A4[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (e < E && lane < active) run += sa[hh * pitch + lane * E + e];
-      part[e] = run;
+  for (int k = 0; k < 4; ++k) A4[k] = (h0 + k < H) ? A[h0 + k] : 0.f;
+
+  float dv[4][4];  // [token e][head k]
+  float run[4] = {0.f, 0.f, 0.f, 0.f};
+  float part[4][4];
+  const int64_t row0 = (int64_t)b * L + (int64_t)c * Q;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bool ok = e < E && lane < active;
+    const int64_t row = row0 + lane * E + e;
+    if (ok && vec) {
+      const float4 v = *reinterpret_cast<const float4*>(dt + row * H + h0);
+      dv[e][0] = v.x; dv[e][1] = v.y; dv[e][2] = v.z; dv[e][3] = v.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dv[e][k] = (ok && h0 + k < H) ? dt[row * H + h0 + k] : 0.f;
     }
-    // inclusive scan of the lane totals, then shift by one lane -> exclusive prefix
-    float tot = run;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[k] = dv[e][k] * A4[k];
+      run[k] += a[k];
+      part[e][k] = run[k];
+    }
+  }
+  // exclusive prefix of the lane totals, per head (inclusive scan shifted by one lane)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float tot = run[k];
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float o = __shfl_up(tot, off, 64);
@@ -70,15 +75,24 @@ __global__ __launch_bounds__(kCsThreads) void chunk_cumsum_kernel(
     }
     float excl = __shfl_up(tot, 1, 64);
     if (lane == 0) excl = 0.f;
-    if (lane < active) {
-      const int64_t orow = (((int64_t)b * H + hb + hh) * nc + c) * Q + lane * E;
+    run[k] = excl;
+  }
+  if (lane < active) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (e < E) dA_cumsum[orow + e] = excl + part[e];
-      if (dt_bhl) {
+    for (int k = 0; k < 4; ++k) {
+      if (h0 + k >= H) continue;
+      const int64_t orow = (((int64_t)b * H + h0 + k) * nc + c) * Q + lane * E;
+      if (E == 4) {
+        *reinterpret_cast<float4*>(dA_cumsum + orow) =
+            make_float4(run[k] + part[0][k], run[k] + part[1][k], run[k] + part[2][k], run[k] + part[3][k]);
+        if (dt_bhl) *reinterpret_cast<float4*>(dt_bhl + orow) = make_float4(dv[0][k], dv[1][k], dv[2][k], dv[3][k]);
+      } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (e < E) dt_bhl[orow + e] = sd[hh * pitch + lane * E + e];
+          if (e < E) {
+            dA_cumsum[orow + e] = run[k] + part[e][k];
+            if (dt_bhl) dt_bhl[orow + e] = dv[e][k];
+          }
       }
     }
   }
@@ -86,10 +100,11 @@ __global__ __launch_bounds__(kCsThreads) void chunk_cumsum_kernel(
 
 hipError_t launch_chunk_cumsum(const Dims& d, const float* dt, const float* A, float* dA_cumsum,
                                float* dt_bhl, hipStream_t stream) {
-  const dim3 grid((unsigned)((d.H + kCsHeads - 1) / kCsHeads), (unsigned)d.nc, (unsigned)d.B);
-  const size_t lds = sizeof(float) * 2 * kCsHeads * (d.Q + 1);
-  hipLaunchKernelGGL(chunk_cumsum_kernel, grid, dim3(kCsThreads), lds, stream, dt, A, dA_cumsum, dt_bhl,
-                     (int)d.L, (int)d.H, (int)d.Q, (int)d.nc);
+  const int nq = (int)((d.H + 3) / 4);
+  const int64_t nwaves = d.B * d.nc * nq;
+  const unsigned blocks = (unsigned)((nwaves + kCsThreads / 64 - 1) / (kCsThreads / 64));
+  hipLaunchKernelGGL(chunk_cumsum_kernel, dim3(blocks), dim3(kCsThreads), 0, stream, dt, A, dA_cumsum, dt_bhl,
+                     (int)d.L, (int)d.H, (int)d.Q, (int)d.nc, nq, nwaves);
   return hipGetLastError();
 }
 

@@ -14,8 +14,9 @@
 // is a fully coalesced 1 KB wave access.  The chain over chunks is serial per
 // thread, but the S loads do not depend on it: the loop is unrolled by 8 with
 // all 8 loads issued before the 8 dependent updates, keeping 8 x 16 B per
-// thread in flight.  carried may alias S: each location is read before it is
-// written, by the same thread.
+// thread in flight, and the next 8 loads are issued before the current 8
+// stores.  carried may alias S: each location is read before it is written,
+// by the same thread.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -42,14 +43,26 @@ __global__ __launch_bounds__(kSpThreads) void state_passing_kernel(
   const float4* sp = reinterpret_cast<const float4*>(S) + (b * nc * H + h) * np4 + e4;
   float4* cp = reinterpret_cast<float4*>(carried) + (b * nc * H + h) * np4 + e4;
 
-  int c = 0;
-  for (; c + kSpUnroll <= nc; c += kSpUnroll) {
-    float4 s[kSpUnroll];
-    float dec[kSpUnroll];
+  // Software pipeline: the loads of chunks c+8..c+15 are issued before the
+  // stores of chunks c..c+7 (distinct addresses, so this also holds in place).
+  float4 s[kSpUnroll], sn[kSpUnroll];
+  float dec[kSpUnroll], decn[kSpUnroll];
+  const int nfull = nc / kSpUnroll;  // full batches
+  if (nfull > 0) {
 #pragma unroll
     for (int u = 0; u < kSpUnroll; ++u) {
-      s[u] = sp[(int64_t)(c + u) * cstride];
-      dec[u] = expf(glast[(int64_t)(c + u) * Q]);
+      s[u] = sp[(int64_t)u * cstride];
+      dec[u] = expf(glast[(int64_t)u * Q]);
+    }
+  }
+  for (int bt = 0; bt < nfull; ++bt) {
+    const int c = bt * kSpUnroll;
+    if (bt + 1 < nfull) {
+#pragma unroll
+      for (int u = 0; u < kSpUnroll; ++u) {
+        sn[u] = sp[(int64_t)(c + kSpUnroll + u) * cstride];
+        decn[u] = expf(glast[(int64_t)(c + kSpUnroll + u) * Q]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kSpUnroll; ++u) {
@@ -59,15 +72,20 @@ __global__ __launch_bounds__(kSpThreads) void state_passing_kernel(
       run.z = dec[u] * run.z + s[u].z;
       run.w = dec[u] * run.w + s[u].w;
     }
+#pragma unroll
+    for (int u = 0; u < kSpUnroll; ++u) {
+      s[u] = sn[u];
+      dec[u] = decn[u];
+    }
   }
-  for (; c < nc; ++c) {
-    const float4 s = sp[(int64_t)c * cstride];
-    const float dec = expf(glast[(int64_t)c * Q]);
+  for (int c = nfull * kSpUnroll; c < nc; ++c) {
+    const float4 sv = sp[(int64_t)c * cstride];
+    const float d1 = expf(glast[(int64_t)c * Q]);
     cp[(int64_t)c * cstride] = run;
-    run.x = dec * run.x + s.x;
-    run.y = dec * run.y + s.y;
-    run.z = dec * run.z + s.z;
-    run.w = dec * run.w + s.w;
+    run.x = d1 * run.x + sv.x;
+    run.y = d1 * run.y + sv.y;
+    run.z = d1 * run.z + sv.z;
+    run.w = d1 * run.w + sv.w;
   }
   if (fin) reinterpret_cast<float4*>(fin)[bh * np4 + e4] = run;
 }
