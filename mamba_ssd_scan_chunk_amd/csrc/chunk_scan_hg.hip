@@ -84,12 +84,11 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   using Op = OpBF16;
   using Frag = Op::Frag;
   constexpr int QT = Cfg::QT, PT = Cfg::PT, N = Cfg::N, NPI = Cfg::NPI, XP = Cfg::XP, T = Cfg::T;
-  constexpr int XW = IN_BF16 ? 8 : 4;        // x elements per 16-byte load
-  constexpr int NXB = (Q / 4) * (PT / XW);   // x prefetch blocks (4 rows x XW cols)
+  static_assert(IN_BF16, "the head-group chunk scan takes bf16 inputs");
+  constexpr int NXB = (Q / 4) * (PT / 8);    // x prefetch blocks (4 tokens x 8 columns)
   constexpr int NHB = (N / 4) * (PT / 4);    // H prefetch blocks (4 n x 4 p)
   constexpr int XPT = (NXB + T - 1) / T;     // blocks per thread
   constexpr int HPT = (NHB + T - 1) / T;
-  constexpr int TE = IN_BF16 ? 2 : 4;        // input element bytes
   constexpr int NSL = QT + 1;                // CB^T sub-tiles held per wave
 
   uint16_t* Bs = reinterpret_cast<uint16_t*>(smem);                    // [Q][NPI]  (phase 0-1 only)
@@ -155,18 +154,32 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   uint4 xv[XPT][4];   // 4 rows x 16 bytes of x per block
   float4 hv[HPT][4];  // 4 rows (n) x 4 columns (p) of H_in per block
   float pg = 0.f, pd = 0.f;
+  // Block -> (row block, column block) maps chosen so that the transposed
+  // LDS writes of each half wave hit distinct banks, while the global reads of
+  // a wave still cover whole 64-byte runs of rows.
+  constexpr int RH = Q / 64;   // x: groups of 16 row blocks
+  constexpr int PH = PT / 16;  // H: groups of 4 column blocks
+  auto xmap = [&](int blk, int& rbk, int& cbk) {
+    const int rest = blk >> 6;
+    rbk = (blk & 15) + 16 * (rest % RH);
+    cbk = ((blk >> 4) & 3) + 4 * (rest / RH);
+  };
+  auto hmap = [&](int blk, int& nb, int& pb) {
+    const int pq = (blk >> 4) & 3, rest = blk >> 6;
+    pb = (pq >> 1) + 2 * (pq & 1) + 4 * (rest % PH);
+    nb = (blk & 15) + 16 * (rest / PH);
+  };
   auto issue = [&](int h) {
-    const unsigned char* xh =
-        reinterpret_cast<const unsigned char*>(a.x) + ((tok0 * H + h) * (int64_t)P + a.p0) * (int64_t)TE;
+    const uint16_t* xh = static_cast<const uint16_t*>(a.x) + (tok0 * H + h) * (int64_t)P + a.p0;
 #pragma unroll
     for (int uu = 0; uu < XPT; ++uu) {
       const int blk = tid + uu * T;
       if (blk < NXB) {
-        const int cbk = blk % (PT / XW), rbk = blk / (PT / XW);
-        const int o0 = (4 * rbk) * HP + XW * cbk;
+        int rbk, cbk;
+        xmap(blk, rbk, cbk);
+        const int o0 = (4 * rbk) * HP + 8 * cbk;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          xv[uu][r] = *reinterpret_cast<const uint4*>(xh + (int64_t)(o0 + r * HP) * TE);
+        for (int r = 0; r < 4; ++r) xv[uu][r] = *reinterpret_cast<const uint4*>(xh + o0 + r * HP);
       }
     }
     const float* hs = a.carried + (((int64_t)a.b * nc + a.c) * H + h) * (int64_t)(N * P) + a.p0;
@@ -174,7 +187,8 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     for (int uu = 0; uu < HPT; ++uu) {
       const int blk = tid + uu * T;
       if (blk < NHB) {
-        const int pb = blk % (PT / 4), nb = blk / (PT / 4);
+        int nb, pb;
+        hmap(blk, nb, pb);
         const int o0 = (4 * nb) * P + 4 * pb;
 #pragma unroll
         for (int r = 0; r < 4; ++r) hv[uu][r] = *reinterpret_cast<const float4*>(hs + o0 + r * P);
@@ -191,36 +205,20 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     for (int uu = 0; uu < XPT; ++uu) {
       const int blk = tid + uu * T;
       if (blk < NXB) {
-        const int cbk = blk % (PT / XW), rbk = blk / (PT / XW);
-        if constexpr (IN_BF16) {
-          // bf16 x: the transpose is a pure 16-bit shuffle, no conversion
-          const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&xv[uu][0]);
-          const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&xv[uu][1]);
-          const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&xv[uu][2]);
-          const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&xv[uu][3]);
+        int rbk, cbk;
+        xmap(blk, rbk, cbk);
+        // bf16 x: the transpose is a pure 16-bit shuffle, no conversion
+        const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&xv[uu][0]);
+        const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&xv[uu][1]);
+        const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&xv[uu][2]);
+        const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&xv[uu][3]);
 #pragma unroll
-          for (int col = 0; col < 8; ++col) {
-            const int m = col >> 1;
-            uint2 w;
-            w.x = (col & 1) ? pick_hi16(r0[m], r1[m]) : pick_lo16(r0[m], r1[m]);
-            w.y = (col & 1) ? pick_hi16(r2[m], r3[m]) : pick_lo16(r2[m], r3[m]);
-            *reinterpret_cast<uint2*>(Xt + (XW * cbk + col) * XP + 4 * rbk) = w;
-          }
-        } else {
-          float v[4][XW];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint4 q = xv[uu][r];
-            v[r][0] = __uint_as_float(q.x); v[r][1] = __uint_as_float(q.y);
-            v[r][2] = __uint_as_float(q.z); v[r][3] = __uint_as_float(q.w);
-          }
-#pragma unroll
-          for (int col = 0; col < XW; ++col) {
-            uint2 w;
-            w.x = pack_bf16x2(v[0][col], v[1][col]);
-            w.y = pack_bf16x2(v[2][col], v[3][col]);
-            *reinterpret_cast<uint2*>(Xt + (XW * cbk + col) * XP + 4 * rbk) = w;
-          }
+        for (int col = 0; col < 8; ++col) {
+          const int m = col >> 1;
+          uint2 w;
+          w.x = (col & 1) ? pick_hi16(r0[m], r1[m]) : pick_lo16(r0[m], r1[m]);
+          w.y = (col & 1) ? pick_hi16(r2[m], r3[m]) : pick_lo16(r2[m], r3[m]);
+          *reinterpret_cast<uint2*>(Xt + (8 * cbk + col) * XP + 4 * rbk) = w;
         }
       }
     }
@@ -228,7 +226,8 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     for (int uu = 0; uu < HPT; ++uu) {
       const int blk = tid + uu * T;
       if (blk < NHB) {
-        const int pb = blk % (PT / 4), nb = blk / (PT / 4);
+        int nb, pb;
+        hmap(blk, nb, pb);
         uint2 w0, w1, w2, w3;
         w0.x = pack_bf16x2(hv[uu][0].x, hv[uu][1].x); w0.y = pack_bf16x2(hv[uu][2].x, hv[uu][3].x);
         w1.x = pack_bf16x2(hv[uu][0].y, hv[uu][1].y); w1.y = pack_bf16x2(hv[uu][2].y, hv[uu][3].y);
@@ -257,42 +256,16 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 
   // One row tile of one head; TILE and SB (slot of its sub-tile js = 0) are
   // compile-time constants.
-  // One row tile of one head.  TSEL (0: tile ra, 1: tile rb) fixes the slot
-  // map; the tile index itself is a run-time value, so all waves share one
-  // copy of this code.  `ln` is the lane index laundered through an empty asm
-  // at the top of each head iteration: lane-dependent addresses, masks and
-  // offsets are recomputed per head instead of being hoisted out of the head
-  // loop, where they would stay live and spill.
-  auto tile_out = [&](auto tsel_c, const int tile, int h, float dsk, int ln) {
+  // Off-diagonal and diagonal steps of one row tile of one head, into acc.
+  // TSEL (0: tile ra, 1: tile rb) fixes the register-slot map; the tile index
+  // itself is a run-time (wave-uniform) value, so all waves share this code.
+  // `ln` is the lane index laundered through an empty asm at the top of each
+  // head iteration: lane-dependent addresses are recomputed per head instead
+  // of being hoisted out of the head loop, where they would stay live.
+  auto steps = [&](auto tsel_c, const int tile, f32x4_t (&acc)[CT], int ln) {
     constexpr int TSEL = decltype(tsel_c)::value;
     const int l16 = ln & 15, lg = ln >> 4;
     const int U = tile >> 1;  // pairs k < U are off-diagonal; pair U holds the diagonal
-    const int R = 32 * U;     // reference row of the factorised decay
-    const float gR = Gs[R];
-    f32x4_t acc[CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // The output tile is accumulated TRANSPOSED, Y^T = H^T C^T + X^T M^T
-    // (operand order swapped, same fragments), so that lane (l16, lg) holds
-    // y[i = 16*tile + l16][p = 16ct + 4lg + r] for r = 0..3: four consecutive
-    // p of one token, written with one 8-byte (bf16) or 16-byte (fp32) store.
-    // carried-state term, scaled by exp(G_R) now and by exp(G_i - G_R) below
-#pragma unroll
-    for (int s = 0; s < NK; ++s) {
-      // all fragments of the step first, then the MFMAs (one LDS round trip per step)
-      const Frag ca = Lds<Op>::load8(Cs + (16 * tile + l16) * NPI + 32 * s + 8 * lg);
-      Frag hf[CT];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) hf[ct] = Lds<Op>::load8(Ht + (16 * ct + l16) * NPI + 32 * s + 8 * lg);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) acc[ct] = Op::mma(hf[ct], ca, acc[ct]);
-    }
-    {
-      const float eR = fast_exp(gR);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) acc[ct] *= eR;
-    }
     const int i = 16 * tile + l16;  // the token this lane's interaction values and outputs belong to
 #pragma unroll
     for (int k = 0; k < QT / 2; ++k) {
@@ -315,56 +288,57 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) acc[ct] = Op::mma(xf[ct], mf, acc[ct]);
       } else if (k == U) {
-        const float gi = Gs[i];
-        // row factor exp(G_i - G_R)
-        {
-          const float e = fast_exp(gi - gR);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) acc[ct] *= e;
-        }
-        // diagonal pair: exact decay, causal select before exp
-        float m[8];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int js = 2 * k + t;
-          const f32x4_t cv = cb[TSEL ? (QT - js) : js];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 16 * js + 4 * lg + r;
-            const bool keep = (js <= tile) && (j <= i);
-            const int jc = keep ? j : i;
-            const float dec = fast_exp(keep ? gi - Gs[jc] : -INFINITY) * dts[jc];
-            m[4 * t + r] = keep ? cv[r] * dec : 0.f;
-          }
-        }
-        const Frag mf = Op::from_f32(m);
         Frag xf[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const uint16_t* xr = Xt + (16 * ct + l16) * XP + 32 * k + 4 * lg;
           xf[ct] = Lds<Op>::load4x2(xr, xr + 16);
         }
+        // G and dt of the lane's 8 tokens j = 32k + 16t + 4lg + r, read as vectors
+        const float4 g0 = *reinterpret_cast<const float4*>(Gs + 32 * k + 4 * lg);
+        const float4 g1 = *reinterpret_cast<const float4*>(Gs + 32 * k + 16 + 4 * lg);
+        const float4 d0 = *reinterpret_cast<const float4*>(dts + 32 * k + 4 * lg);
+        const float4 d1 = *reinterpret_cast<const float4*>(dts + 32 * k + 16 + 4 * lg);
+        const float gi = Gs[i];
+        const float gR = Gs[32 * U];
+        // row factor exp(G_i - G_R) for everything accumulated so far
+        {
+          const float e = fast_exp(gi - gR);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) acc[ct] *= e;
+        }
+        // diagonal pair: exact decay, causal select before exp
+        const float gj[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        const f32x4_t c0 = cb[TSEL ? (QT - 2 * k) : 2 * k];
+        const f32x4_t c1 = (2 * k + 1 <= tile) ? cb[TSEL ? (QT - 2 * k - 1) : 2 * k + 1] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const float cvv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+        float m[8];
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) {
+          const int j = 32 * k + 16 * (e8 >> 2) + 4 * lg + (e8 & 3);
+          const bool keep = j <= i;
+          const float dec = fast_exp(keep ? gi - gj[e8] : -INFINITY) * dj[e8];
+          m[e8] = keep ? cvv[e8] * dec : 0.f;
+        }
+        const Frag mf = Op::from_f32(m);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) acc[ct] = Op::mma(xf[ct], mf, acc[ct]);
       }
     }
-    // skip connection and store: y[i][16ct + 4lg .. +3]
+  };
+  // skip connection and store of one row tile: y[i][16ct + 4lg .. +3]
+  auto store_tile = [&](const int tile, const f32x4_t (&acc)[CT], int h, float dsk, int ln) {
+    const int l16 = ln & 15, lg = ln >> 4;
+    const int i = 16 * tile + l16;
     const int64_t ybase = (tok0 * H + h) * (int64_t)P + a.p0;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const int pc = 16 * ct + 4 * lg;
       const int off = i * HP + pc;
-      float xv[4];
-      if constexpr (IN_BF16) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xv[r] = bf16_bits_to_f32(Xt[(pc + r) * XP + i]);
-      } else {
-        const float4 q = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + ybase + off);
-        xv[0] = q.x; xv[1] = q.y; xv[2] = q.z; xv[3] = q.w;
-      }
       float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = acc[ct][r] + dsk * xv[r];
+      for (int r = 0; r < 4; ++r) v[r] = acc[ct][r] + dsk * bf16_bits_to_f32(Xt[(pc + r) * XP + i]);
       if (a.y_bf16) {
         uint2 w;
         w.x = pack_bf16x2(v[0], v[1]);
@@ -394,9 +368,45 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     int wv = wave;
     asm volatile("" : "+v"(wv));
     wv = __builtin_amdgcn_readfirstlane(wv);
-    tile_out(std::integral_constant<int, 0>{}, wv, h, dsk, ln);
-    asm volatile("" : "+v"(ln));
-    tile_out(std::integral_constant<int, 1>{}, QT - 1 - wv, h, dsk, ln);
+    const int ta = wv, tb = QT - 1 - wv;
+    {
+      const int l16 = ln & 15, lg = ln >> 4;
+      // The output tiles are accumulated TRANSPOSED, Y^T = H^T C^T + X^T M^T
+      // (operand order swapped, same fragments): lane (l16, lg) holds
+      // y[i = 16*tile + l16][p = 16ct + 4lg + r], r = 0..3, written with one
+      // 8-byte store.  Carried-state term first, for both tiles at once (each
+      // H fragment read once per wave), scaled by exp(G_R) now and by
+      // exp(G_i - G_R) at the tile's diagonal step.
+      f32x4_t acc0[CT], acc1[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        acc0[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc1[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+        Frag hf[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) hf[ct] = Lds<Op>::load8(Ht + (16 * ct + l16) * NPI + 32 * s + 8 * lg);
+        const Frag ca0 = Lds<Op>::load8(Cs + (16 * ta + l16) * NPI + 32 * s + 8 * lg);
+        const Frag ca1 = Lds<Op>::load8(Cs + (16 * tb + l16) * NPI + 32 * s + 8 * lg);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          acc0[ct] = Op::mma(hf[ct], ca0, acc0[ct]);
+          acc1[ct] = Op::mma(hf[ct], ca1, acc1[ct]);
+        }
+      }
+      const float e0 = fast_exp(Gs[32 * (ta >> 1)]), e1 = fast_exp(Gs[32 * (tb >> 1)]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        acc0[ct] *= e0;
+        acc1[ct] *= e1;
+      }
+      steps(std::integral_constant<int, 0>{}, ta, acc0, ln);
+      steps(std::integral_constant<int, 1>{}, tb, acc1, ln);
+      store_tile(ta, acc0, h, dsk, ln);
+      store_tile(tb, acc1, h, dsk, ln);
+    }
     if (hh + 1 < a.HG) {
       __syncthreads();  // all reads of this head's tiles are done
       commit();
