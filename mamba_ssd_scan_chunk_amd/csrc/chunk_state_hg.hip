@@ -18,21 +18,21 @@
 // written transposed (Xt[p][j]).  The output is accumulated transposed,
 // D[p][n] = sum_j Xt[p][j] Bt[n][j], so that each lane holds four consecutive
 // p of one state row n and writes them as one 16-byte store.
-// 4 waves (one per SIMD); wave w owns the state rows n in tiles 2w, 2w+1
-// (N = 128) or 4w..4w+3 (N = 256) for all 4 column tiles of the slice.
+// 8 waves (two per SIMD); wave w owns the state rows n in tile w (N = 128)
+// or tiles 2w, 2w+1 (N = 256) for all 4 column tiles of the slice.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
 namespace ssd {
 
-constexpr int kShgThreads = 256;
+constexpr int kShgThreads = 512;
 
 template <int Q, int N>
 struct ShgCfg {
   static constexpr int T = kShgThreads;
   static constexpr int PT = 64;
   static constexpr int KP = Q + 8;                 // pitch of Bt / Xt rows (elements)
-  static constexpr int NTW = N / 16 / 4;           // state-row tiles per wave
+  static constexpr int NTW = N / 16 / 8;           // state-row tiles per wave (8 waves)
   static constexpr size_t lds_b = (size_t)N * KP * 2;
   static constexpr size_t lds_x = (size_t)PT * KP * 2;
   static constexpr size_t lds_total = lds_b + lds_x;
@@ -48,8 +48,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   using Frag = Op::Frag;
   constexpr int T = Cfg::T, PT = Cfg::PT, KP = Cfg::KP, NTW = Cfg::NTW;
   constexpr int NXB = (Q / 4) * (PT / 8);  // x prefetch blocks: 4 tokens x 8 columns
-  constexpr int XPT = NXB / T;
-  static_assert(NXB % T == 0, "x blocks must divide evenly");
+  constexpr int XPT = (NXB + T - 1) / T;
 
   extern __shared__ __align__(16) unsigned char shg_smem[];
   uint16_t* Bt = reinterpret_cast<uint16_t*>(shg_smem);  // [N][KP]
@@ -107,11 +106,13 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       const int blk = tid + u * T;
-      const int cb = blk % (PT / 8), rb = blk / (PT / 8);
+      if (blk < NXB) {
+        const int cb = blk % (PT / 8), rb = blk / (PT / 8);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) xv[u][r] = *reinterpret_cast<const uint4*>(xs + (4 * rb + r) * HP + 8 * cb);
-      gv[u] = *reinterpret_cast<const float4*>(gsrc + 4 * rb);
-      dv[u] = *reinterpret_cast<const float4*>(dsrc + 4 * rb);
+        for (int r = 0; r < 4; ++r) xv[u][r] = *reinterpret_cast<const uint4*>(xs + (4 * rb + r) * HP + 8 * cb);
+        gv[u] = *reinterpret_cast<const float4*>(gsrc + 4 * rb);
+        dv[u] = *reinterpret_cast<const float4*>(dsrc + 4 * rb);
+      }
     }
     glast = gsrc[Q - 1];
   };
@@ -119,6 +120,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       const int blk = tid + u * T;
+      if (blk >= NXB) continue;
       const int cb = blk % (PT / 8), rb = blk / (PT / 8);
       const float w[4] = {fast_exp(glast - gv[u].x) * dv[u].x, fast_exp(glast - gv[u].y) * dv[u].y,
                           fast_exp(glast - gv[u].z) * dv[u].z, fast_exp(glast - gv[u].w) * dv[u].w};
