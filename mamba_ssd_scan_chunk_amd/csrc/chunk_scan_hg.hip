@@ -16,15 +16,17 @@
 //
 // Waves and tiles (Q = chunk in {128, 256}, QT = Q/16 row tiles of 16 rows):
 //  * QT/2 waves; wave w owns the row tiles w and QT-1-w, which together hold
-//    QT+1 causal 16x16 sub-tiles whatever w is (balanced work).  The wave's
-//    code is specialised at compile time on w (hg_body<..., W>), so tile
-//    indices, loop trip counts and register slots are constants: no guarded
-//    code, and the CB^T sub-tiles stay in registers for the block's life.
+//    QT+1 causal 16x16 sub-tiles whatever w is (balanced work).  All waves
+//    run one code path: the tile indices are wave-uniform run-time values
+//    (scalar branches), while the register slot of every sub-tile is a
+//    compile-time constant, so the CB^T sub-tiles stay in registers for the
+//    block's life.
 //  * the CB^T sub-tiles are computed with operand roles swapped (B as the A
 //    operand, C as the B operand), so each lane holds four consecutive j for
 //    one row i; after decay and mask those are directly the A fragment of
-//    M.X (slot e = 4t + r <-> token 32k + 16t + 4lg + r), and x is read from
-//    LDS with the same slot map.
+//    M.X (slot e = 4t + r <-> token 32k + 16t + 4lg + r); x rows are kept in
+//    LDS with the tokens of each 32-token step permuted (xpos) so that the
+//    matching x fragment is one 16-byte read.
 //  * decay: for the sub-tile pairs below the diagonal pair of row tile t,
 //    exp(G_i - G_j) = exp(G_i - G_R) * exp(G_R - G_j) with the reference row
 //    R = 32 * (t / 2) between j and i, so both factors are <= 1 (no overflow;
@@ -54,8 +56,11 @@ struct HgCfg {
   static constexpr int T = hg_threads(Q);
   static constexpr int PT = CT * 16;
   static constexpr int N = NK * 32;   // this variant needs N == NK*32
-  static constexpr int NPI = N + 8;   // pitch (elements) of n-indexed LDS rows
-  static constexpr int XP = Q + 8;    // pitch of Xt rows
+  // Row pitches are 16 elements (8 dwords) past a multiple of 64 dwords: the
+  // 16-byte fragment reads of 16 rows by 4 lane groups then fall in distinct
+  // banks (a 4-dword pad halves the read rate on this LDS).
+  static constexpr int NPI = N + 16;  // pitch (elements) of n-indexed LDS rows
+  static constexpr int XP = Q + 16;   // pitch of Xt rows
   static constexpr size_t lds_bs = (size_t)Q * NPI * 2;
   static constexpr size_t lds_xh = (size_t)PT * XP * 2 + (size_t)PT * NPI * 2;
   static constexpr size_t lds_a = lds_bs > lds_xh ? lds_bs : lds_xh;  // Bs, later Xt + Ht
@@ -77,6 +82,14 @@ struct HgArgs {
   int b, c, g, hbase, p0;
   int64_t tok0;
 };
+
+// Position of token j of the chunk inside an Xt row.  The A-operand fragment
+// of lane (l16, lg) at step k holds tokens 32k + 16t + 4lg + r (t = 0, 1;
+// r = 0..3); storing them at 32k + 8lg + 4t + r makes that fragment one
+// 16-byte read.
+__device__ __forceinline__ int xpos(int j) {
+  return (j & ~31) | ((j & 12) << 1) | ((j & 16) >> 2) | (j & 3);
+}
 
 template <int Q, int NK, int CT, bool IN_BF16>
 __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, const int tid) {
@@ -218,7 +231,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
           uint2 w;
           w.x = (col & 1) ? pick_hi16(r0[m], r1[m]) : pick_lo16(r0[m], r1[m]);
           w.y = (col & 1) ? pick_hi16(r2[m], r3[m]) : pick_lo16(r2[m], r3[m]);
-          *reinterpret_cast<uint2*>(Xt + (8 * cbk + col) * XP + 4 * rbk) = w;
+          *reinterpret_cast<uint2*>(Xt + (8 * cbk + col) * XP + xpos(4 * rbk)) = w;
         }
       }
     }
@@ -274,10 +287,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         // are issued before the arithmetic and the MFMAs.
         Frag xf[CT];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const uint16_t* xr = Xt + (16 * ct + l16) * XP + 32 * k + 4 * lg;
-          xf[ct] = Lds<Op>::load4x2(xr, xr + 16);
-        }
+        for (int ct = 0; ct < CT; ++ct) xf[ct] = Lds<Op>::load8(Xt + (16 * ct + l16) * XP + 32 * k + 8 * lg);
         const float4 w0 = *reinterpret_cast<const float4*>(Ws + U * Q + 32 * k + 4 * lg);
         const float4 w1 = *reinterpret_cast<const float4*>(Ws + U * Q + 32 * k + 16 + 4 * lg);
         const f32x4_t c0 = cb[TSEL ? (QT - 2 * k) : 2 * k];
@@ -290,10 +300,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       } else if (k == U) {
         Frag xf[CT];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const uint16_t* xr = Xt + (16 * ct + l16) * XP + 32 * k + 4 * lg;
-          xf[ct] = Lds<Op>::load4x2(xr, xr + 16);
-        }
+        for (int ct = 0; ct < CT; ++ct) xf[ct] = Lds<Op>::load8(Xt + (16 * ct + l16) * XP + 32 * k + 8 * lg);
         // G and dt of the lane's 8 tokens j = 32k + 16t + 4lg + r, read as vectors
         const float4 g0 = *reinterpret_cast<const float4*>(Gs + 32 * k + 4 * lg);
         const float4 g1 = *reinterpret_cast<const float4*>(Gs + 32 * k + 16 + 4 * lg);
@@ -338,7 +345,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       const int off = i * HP + pc;
       float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = acc[ct][r] + dsk * bf16_bits_to_f32(Xt[(pc + r) * XP + i]);
+      for (int r = 0; r < 4; ++r) v[r] = acc[ct][r] + dsk * bf16_bits_to_f32(Xt[(pc + r) * XP + xpos(i)]);
       if (a.y_bf16) {
         uint2 w;
         w.x = pack_bf16x2(v[0], v[1]);

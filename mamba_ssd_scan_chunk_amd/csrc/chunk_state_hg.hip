@@ -31,7 +31,10 @@ template <int Q, int N>
 struct ShgCfg {
   static constexpr int T = kShgThreads;
   static constexpr int PT = 64;
-  static constexpr int KP = Q + 8;                 // pitch of Bt / Xt rows (elements)
+  // pitch of Bt / Xt rows (elements): 8 dwords past a multiple of 64 dwords,
+  // so the 16-byte fragment reads of 16 rows by 4 lane groups are free of
+  // LDS bank conflicts
+  static constexpr int KP = Q + 16;
   static constexpr int NTW = N / 16 / 8;           // state-row tiles per wave (8 waves)
   static constexpr size_t lds_b = (size_t)N * KP * 2;
   static constexpr size_t lds_x = (size_t)PT * KP * 2;
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     const uint16_t* bsrc = Bm + (tok0 * G + g) * N;
     const int GN = G * N;
     for (int blk = tid; blk < (Q / 8) * (N / 8); blk += T) {
-      const int nb = blk % (N / 8), jb = blk / (N / 8);
+      const int jb = blk % (Q / 8), nb = blk / (Q / 8);  // neighbouring lanes: neighbouring token blocks
       uint4 rows[8];
 #pragma unroll
       for (int r = 0; r < 8; ++r) rows[r] = *reinterpret_cast<const uint4*>(bsrc + (8 * jb + r) * GN + 8 * nb);
@@ -98,6 +101,16 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   uint4 xv[XPT][4];
   float4 gv[XPT], dv[XPT];
   float glast = 0.f;
+  // Block -> (row block rb of 4 tokens, column block cb of 8 columns): the 16
+  // lanes of a quarter wave take consecutive row blocks (their transposed LDS
+  // writes are contiguous), the 4 quarters take neighbouring column blocks
+  // (each global read covers 64-byte runs of 16 rows).
+  constexpr int RH = Q / 64;
+  auto xmap = [&](int blk, int& rb, int& cb) {
+    const int rest = blk >> 6;
+    rb = (blk & 15) + 16 * (rest % RH);
+    cb = ((blk >> 4) & 3) + 4 * (rest / RH);
+  };
   auto issue = [&](int h) {
     const uint16_t* xs = x + (tok0 * H + h) * (int64_t)P + p0;
     const int64_t bhc = ((int64_t)b * H + h) * nc + c;
@@ -107,7 +120,8 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     for (int u = 0; u < XPT; ++u) {
       const int blk = tid + u * T;
       if (blk < NXB) {
-        const int cb = blk % (PT / 8), rb = blk / (PT / 8);
+        int cb, rb;
+        xmap(blk, rb, cb);
 #pragma unroll
         for (int r = 0; r < 4; ++r) xv[u][r] = *reinterpret_cast<const uint4*>(xs + (4 * rb + r) * HP + 8 * cb);
         gv[u] = *reinterpret_cast<const float4*>(gsrc + 4 * rb);
@@ -121,7 +135,8 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     for (int u = 0; u < XPT; ++u) {
       const int blk = tid + u * T;
       if (blk >= NXB) continue;
-      const int cb = blk % (PT / 8), rb = blk / (PT / 8);
+      int cb, rb;
+      xmap(blk, rb, cb);
       const float w[4] = {fast_exp(glast - gv[u].x) * dv[u].x, fast_exp(glast - gv[u].y) * dv[u].y,
                           fast_exp(glast - gv[u].z) * dv[u].z, fast_exp(glast - gv[u].w) * dv[u].w};
       float v[4][8];
