@@ -78,7 +78,7 @@ struct HgArgs {
   const float* carried;
   const float* D;
   void* y;
-  int y_bf16, L, H, P, G, nc, HG;
+  int L, H, P, G, nc, HG;
   int b, c, g, hbase, p0;
   int64_t tok0;
 };
@@ -91,7 +91,7 @@ __device__ __forceinline__ int xpos(int j) {
   return (j & ~31) | ((j & 12) << 1) | ((j & 16) >> 2) | (j & 3);
 }
 
-template <int Q, int NK, int CT, bool IN_BF16>
+template <int Q, int NK, int CT, bool IN_BF16, bool Y_BF16>
 __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, const int tid) {
   using Cfg = HgCfg<Q, NK, CT>;
   using Op = OpBF16;
@@ -103,6 +103,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   constexpr int XPT = (NXB + T - 1) / T;     // blocks per thread
   constexpr int HPT = (NHB + T - 1) / T;
   constexpr int NSL = QT + 1;                // CB^T sub-tiles held per wave
+  static_assert(T % Q == 0 && (Q & (Q - 1)) == 0, "the G/dt staging assumes T is a multiple of Q");
 
   uint16_t* Bs = reinterpret_cast<uint16_t*>(smem);                    // [Q][NPI]  (phase 0-1 only)
   uint16_t* Xt = reinterpret_cast<uint16_t*>(smem);                    // [PT][XP]  (aliases Bs later)
@@ -207,10 +208,12 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         for (int r = 0; r < 4; ++r) hv[uu][r] = *reinterpret_cast<const float4*>(hs + o0 + r * P);
       }
     }
-    if (tid < Q) {
+    {
+      // every thread loads (and later stores) the values of token tid mod Q:
+      // T is a multiple of Q, and branch-free code keeps the memory waits exact
       const int64_t bhc = ((int64_t)a.b * H + h) * nc + a.c;
-      pg = a.dA_cumsum[bhc * Q + tid];
-      pd = a.dt_bhl[bhc * Q + tid];
+      pg = a.dA_cumsum[bhc * Q + (tid & (Q - 1))];
+      pd = a.dt_bhl[bhc * Q + (tid & (Q - 1))];
     }
   };
   auto commit = [&]() {
@@ -252,10 +255,8 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         *reinterpret_cast<uint2*>(Ht + (4 * pb + 3) * NPI + 4 * nb) = w3;
       }
     }
-    if (tid < Q) {
-      Gs[tid] = pg;
-      dts[tid] = pd;
-    }
+    Gs[tid & (Q - 1)] = pg;  // threads tid and tid + Q write the same value
+    dts[tid & (Q - 1)] = pd;
   };
   // Column factors of the off-diagonal sub-tiles: for the reference row
   // R = 32u, Ws[u][j] = exp(G_R - G_j) dt_j (j < R, so G_R <= G_j and the
@@ -346,7 +347,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = acc[ct][r] + dsk * bf16_bits_to_f32(Xt[(pc + r) * XP + xpos(i)]);
-      if (a.y_bf16) {
+      if constexpr (Y_BF16) {
         uint2 w;
         w.x = pack_bf16x2(v[0], v[1]);
         w.y = pack_bf16x2(v[2], v[3]);
@@ -366,7 +367,11 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 
   for (int hh = 0; hh < a.HG; ++hh) {
     const int h = a.hbase + hh;
-    if (hh + 1 < a.HG) issue(h + 1);
+    // The prefetch, commit and column-factor table run on every iteration (the
+    // last one loads its own head again, unused): with no conditional around
+    // them the compiler's memory-counter waits stay exact, so the loads of the
+    // next head remain in flight across the whole compute of this one.
+    issue(hh + 1 < a.HG ? h + 1 : h);
     const float dsk = a.D[h];
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -414,21 +419,22 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       store_tile(ta, acc0, h, dsk, ln);
       store_tile(tb, acc1, h, dsk, ln);
     }
-    if (hh + 1 < a.HG) {
-      __syncthreads();  // all reads of this head's tiles are done
-      commit();
-      __syncthreads();
-      make_w();
-      __syncthreads();
-    }
+    __syncthreads();  // all reads of this head's tiles are done
+    commit();
+    __syncthreads();
+    make_w();
+    __syncthreads();
   }
 }
 
-template <int Q, int NK, int CT, bool IN_BF16>
+// Y_BF16 is a template parameter rather than a run-time flag: a branch around
+// the output stores would make the compiler's memory-counter waits for the
+// prefetched loads conservative (they would also wait for the stores).
+template <int Q, int NK, int CT, bool IN_BF16, bool Y_BF16>
 __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, const void* __restrict__ Cm,
     const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const float* __restrict__ carried,
-    const float* __restrict__ D, void* __restrict__ y, int y_bf16, int L, int H, int P, int G, int nc, int HG,
+    const float* __restrict__ D, void* __restrict__ y, int L, int H, int P, int G, int nc, int HG,
     int nhg, int npt, int remap) {
   extern __shared__ __align__(16) unsigned char hg_smem[];
   // block -> (b, c, g, head group, p slice).  With remap != 0 the mapping is
@@ -439,7 +445,7 @@ __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
   if (remap) bid = (bid & 7u) * (nblk >> 3) + (bid >> 3);
   HgArgs a;
   a.x = x; a.Bm = Bm; a.Cm = Cm; a.dt_bhl = dt_bhl; a.dA_cumsum = dA_cumsum; a.carried = carried; a.D = D; a.y = y;
-  a.y_bf16 = y_bf16; a.L = L; a.H = H; a.P = P; a.G = G; a.nc = nc; a.HG = HG;
+  a.L = L; a.H = H; a.P = P; a.G = G; a.nc = nc; a.HG = HG;
   const int pt = bid % npt;
   unsigned rest = bid / npt;
   const int hgi = rest % nhg;
@@ -451,7 +457,7 @@ __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
   a.hbase = a.g * (H / G) + hgi * HG;
   a.p0 = pt * HgCfg<Q, NK, CT>::PT;
   a.tok0 = (int64_t)a.b * L + (int64_t)a.c * Q;
-  hg_body<Q, NK, CT, IN_BF16>(a, hg_smem, threadIdx.x);
+  hg_body<Q, NK, CT, IN_BF16, Y_BF16>(a, hg_smem, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ host side
@@ -489,7 +495,7 @@ static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, c
                                  bool y_bf16, hipStream_t stream) {
   constexpr int CT = 4;
   using Cfg = HgCfg<Q, NK, CT>;
-  auto kern = chunk_scan_hg_kernel<Q, NK, CT, IN_BF16>;
+  auto kern = y_bf16 ? chunk_scan_hg_kernel<Q, NK, CT, IN_BF16, true> : chunk_scan_hg_kernel<Q, NK, CT, IN_BF16, false>;
   const size_t lds = Cfg::lds_total;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -502,7 +508,7 @@ static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, c
   const int64_t nblk = d.B * d.nc * d.G * nhg * npt;
   const int remap = (nblk % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(threads), lds, stream, x, Bm, Cm, dt_bhl, dA_cumsum, carried,
-                     D, y, (int)y_bf16, (int)d.L, (int)d.H, (int)d.P, (int)d.G, (int)d.nc, HG, nhg, npt, remap);
+                     D, y, (int)d.L, (int)d.H, (int)d.P, (int)d.G, (int)d.nc, HG, nhg, npt, remap);
   return hipGetLastError();
 }
 

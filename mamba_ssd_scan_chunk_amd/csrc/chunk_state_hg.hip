@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       const int blk = tid + u * T;
-      if (blk < NXB) {
+      if (NXB % T == 0 || blk < NXB) {  // the test is compile-time true when the blocks divide evenly
         int cb, rb;
         xmap(blk, rb, cb);
 #pragma unroll
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       const int blk = tid + u * T;
-      if (blk >= NXB) continue;
+      if (NXB % T != 0 && blk >= NXB) continue;
       int cb, rb;
       xmap(blk, rb, cb);
       const float w[4] = {fast_exp(glast - gv[u].x) * dv[u].x, fast_exp(glast - gv[u].y) * dv[u].y,
@@ -165,7 +165,11 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
 
   for (int hh = 0; hh < HG; ++hh) {
     const int h = hbase + hh;
-    if (hh + 1 < HG) issue(h + 1);
+    // The prefetch and the commit run on every iteration (the last one loads
+    // its own head again, unused): with no conditional around them the
+    // compiler's memory-counter waits stay exact, so the loads of the next
+    // head remain in flight across the whole compute of this one.
+    issue(hh + 1 < HG ? h + 1 : h);
     {
       // lane index laundered per head: lane-dependent addresses are recomputed
       // here rather than hoisted out of the head loop
@@ -200,11 +204,9 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
               make_float4(acc[i][ct][0], acc[i][ct][1], acc[i][ct][2], acc[i][ct][3]);
       }
     }
-    if (hh + 1 < HG) {
-      __syncthreads();  // all reads of this head's Xt are done
-      commit();
-      __syncthreads();
-    }
+    __syncthreads();  // all reads of this head's Xt are done
+    commit();
+    __syncthreads();
   }
 }
 
