@@ -268,70 +268,85 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     }
   };
 
-  // One row tile of one head; TILE and SB (slot of its sub-tile js = 0) are
-  // compile-time constants.
-  // Off-diagonal and diagonal steps of one row tile of one head, into acc.
-  // TSEL (0: tile ra, 1: tile rb) fixes the register-slot map; the tile index
-  // itself is a run-time (wave-uniform) value, so all waves share this code.
+  // Sub-tile pair steps of one head for both row tiles of the wave.  TSEL (0:
+  // tile ra, 1: tile rb) fixes the register-slot map of a tile; the tile
+  // indices are run-time, wave-uniform values, so all waves share this code.
+  // Off-diagonal pair k of a tile whose diagonal pair is U: M' = CB * Ws[U][j].
+  auto offdiag = [&](auto tsel_c, const int k, const int U, const Frag (&xf)[CT], f32x4_t (&acc)[CT], int lg) {
+    constexpr int TSEL = decltype(tsel_c)::value;
+    const float4 w0 = *reinterpret_cast<const float4*>(Ws + U * Q + 32 * k + 4 * lg);
+    const float4 w1 = *reinterpret_cast<const float4*>(Ws + U * Q + 32 * k + 16 + 4 * lg);
+    const f32x4_t c0 = cb[TSEL ? (QT - 2 * k) : 2 * k];
+    const f32x4_t c1 = cb[TSEL ? (QT - 2 * k - 1) : 2 * k + 1];
+    const float m[8] = {c0[0] * w0.x, c0[1] * w0.y, c0[2] * w0.z, c0[3] * w0.w,
+                        c1[0] * w1.x, c1[1] * w1.y, c1[2] * w1.z, c1[3] * w1.w};
+    const Frag mf = Op::from_f32(m);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = Op::mma(xf[ct], mf, acc[ct]);
+  };
+  // Diagonal pair k = tile / 2: the row factor exp(G_i - G_R) first scales
+  // everything accumulated so far, then the pair takes exact decays, with the
+  // causal select made before the exponential.
+  auto diag = [&](auto tsel_c, const int k, const int tile, const Frag (&xf)[CT], f32x4_t (&acc)[CT], int l16,
+                  int lg) {
+    constexpr int TSEL = decltype(tsel_c)::value;
+    const int i = 16 * tile + l16;  // the token this lane's interaction values and outputs belong to
+    // G and dt of the lane's 8 tokens j = 32k + 16t + 4lg + r, read as vectors
+    const float4 g0 = *reinterpret_cast<const float4*>(Gs + 32 * k + 4 * lg);
+    const float4 g1 = *reinterpret_cast<const float4*>(Gs + 32 * k + 16 + 4 * lg);
+    const float4 d0 = *reinterpret_cast<const float4*>(dts + 32 * k + 4 * lg);
+    const float4 d1 = *reinterpret_cast<const float4*>(dts + 32 * k + 16 + 4 * lg);
+    const float gi = Gs[i];
+    const float gR = Gs[32 * k];
+    {
+      const float e = fast_exp(gi - gR);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct] *= e;
+    }
+    const float gj[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    const f32x4_t c0 = cb[TSEL ? (QT - 2 * k) : 2 * k];
+    const f32x4_t c1 = (2 * k + 1 <= tile) ? cb[TSEL ? (QT - 2 * k - 1) : 2 * k + 1] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float cvv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    float m[8];
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const int j = 32 * k + 16 * (e8 >> 2) + 4 * lg + (e8 & 3);
+      const bool keep = j <= i;
+      const float dec = fast_exp(keep ? gi - gj[e8] : -INFINITY) * dj[e8];
+      m[e8] = keep ? cvv[e8] * dec : 0.f;
+    }
+    const Frag mf = Op::from_f32(m);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = Op::mma(xf[ct], mf, acc[ct]);
+  };
+  // One pass over the pair index k serves both tiles (ta = w < tb = QT-1-w, so
+  // the diagonal pair of ta comes first): the x fragments of a step are read
+  // once for both, and those of step k+1 are read while step k computes.
   // `ln` is the lane index laundered through an empty asm at the top of each
   // head iteration: lane-dependent addresses are recomputed per head instead
   // of being hoisted out of the head loop, where they would stay live.
-  auto steps = [&](auto tsel_c, const int tile, f32x4_t (&acc)[CT], int ln) {
-    constexpr int TSEL = decltype(tsel_c)::value;
+  auto steps = [&](const int ta, const int tb, f32x4_t (&acc0)[CT], f32x4_t (&acc1)[CT], int ln) {
     const int l16 = ln & 15, lg = ln >> 4;
-    const int U = tile >> 1;  // pairs k < U are off-diagonal; pair U holds the diagonal
-    const int i = 16 * tile + l16;  // the token this lane's interaction values and outputs belong to
+    const int Ua = ta >> 1, Ub = tb >> 1;
+    const uint16_t* xrow = Xt + l16 * XP + 8 * lg;
+    Frag xn[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) xn[ct] = Lds<Op>::load8(xrow + 16 * ct * XP);
 #pragma unroll
     for (int k = 0; k < QT / 2; ++k) {
-      if (k < U) {
-        // off-diagonal pair: M' = CB * Ws[U][j].  All LDS reads of the step
-        // are issued before the arithmetic and the MFMAs.
+      if (k <= Ub) {
         Frag xf[CT];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) xf[ct] = Lds<Op>::load8(Xt + (16 * ct + l16) * XP + 32 * k + 8 * lg);
-        const float4 w0 = *reinterpret_cast<const float4*>(Ws + U * Q + 32 * k + 4 * lg);
-        const float4 w1 = *reinterpret_cast<const float4*>(Ws + U * Q + 32 * k + 16 + 4 * lg);
-        const f32x4_t c0 = cb[TSEL ? (QT - 2 * k) : 2 * k];
-        const f32x4_t c1 = cb[TSEL ? (QT - 2 * k - 1) : 2 * k + 1];
-        const float m[8] = {c0[0] * w0.x, c0[1] * w0.y, c0[2] * w0.z, c0[3] * w0.w,
-                            c1[0] * w1.x, c1[1] * w1.y, c1[2] * w1.z, c1[3] * w1.w};
-        const Frag mf = Op::from_f32(m);
+        for (int ct = 0; ct < CT; ++ct) xf[ct] = xn[ct];
+        if (k + 1 < QT / 2) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[ct] = Op::mma(xf[ct], mf, acc[ct]);
-      } else if (k == U) {
-        Frag xf[CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) xf[ct] = Lds<Op>::load8(Xt + (16 * ct + l16) * XP + 32 * k + 8 * lg);
-        // G and dt of the lane's 8 tokens j = 32k + 16t + 4lg + r, read as vectors
-        const float4 g0 = *reinterpret_cast<const float4*>(Gs + 32 * k + 4 * lg);
-        const float4 g1 = *reinterpret_cast<const float4*>(Gs + 32 * k + 16 + 4 * lg);
-        const float4 d0 = *reinterpret_cast<const float4*>(dts + 32 * k + 4 * lg);
-        const float4 d1 = *reinterpret_cast<const float4*>(dts + 32 * k + 16 + 4 * lg);
-        const float gi = Gs[i];
-        const float gR = Gs[32 * U];
-        // row factor exp(G_i - G_R) for everything accumulated so far
-        {
-          const float e = fast_exp(gi - gR);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) acc[ct] *= e;
+          for (int ct = 0; ct < CT; ++ct) xn[ct] = Lds<Op>::load8(xrow + 16 * ct * XP + 32 * (k + 1));
         }
-        // diagonal pair: exact decay, causal select before exp
-        const float gj[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-        const f32x4_t c0 = cb[TSEL ? (QT - 2 * k) : 2 * k];
-        const f32x4_t c1 = (2 * k + 1 <= tile) ? cb[TSEL ? (QT - 2 * k - 1) : 2 * k + 1] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const float cvv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-        float m[8];
-#pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8) {
-          const int j = 32 * k + 16 * (e8 >> 2) + 4 * lg + (e8 & 3);
-          const bool keep = j <= i;
-          const float dec = fast_exp(keep ? gi - gj[e8] : -INFINITY) * dj[e8];
-          m[e8] = keep ? cvv[e8] * dec : 0.f;
-        }
-        const Frag mf = Op::from_f32(m);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[ct] = Op::mma(xf[ct], mf, acc[ct]);
+        if (k < Ua) offdiag(std::integral_constant<int, 0>{}, k, Ua, xf, acc0, lg);
+        else if (k == Ua) diag(std::integral_constant<int, 0>{}, k, ta, xf, acc0, l16, lg);
+        if (k < Ub) offdiag(std::integral_constant<int, 1>{}, k, Ub, xf, acc1, lg);
+        else diag(std::integral_constant<int, 1>{}, k, tb, xf, acc1, l16, lg);
       }
     }
   };
@@ -414,8 +429,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         acc0[ct] *= e0;
         acc1[ct] *= e1;
       }
-      steps(std::integral_constant<int, 0>{}, ta, acc0, ln);
-      steps(std::integral_constant<int, 1>{}, tb, acc1, ln);
+      steps(ta, tb, acc0, acc1, ln);
       store_tile(ta, acc0, h, dsk, ln);
       store_tile(tb, acc1, h, dsk, ln);
     }

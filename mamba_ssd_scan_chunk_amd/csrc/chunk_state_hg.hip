@@ -10,14 +10,18 @@
 // by every head of a group.
 //
 // One block owns a (b, c, group, 64-column slice of P) and a run of HG heads of
-// that group.  The chunk's B rows are staged ONCE, transposed (Bt[n][j], the
-// token contiguous as the contraction needs), through 8x8 register
-// transposes.  Per head, each thread prefetches 4-token x 8-column blocks of x
-// plus the G and dt of those tokens into registers while the previous head
-// computes; at commit the rows are scaled by w_j in fp32, rounded to bf16 and
-// written transposed (Xt[p][j]).  The output is accumulated transposed,
-// D[p][n] = sum_j Xt[p][j] Bt[n][j], so that each lane holds four consecutive
-// p of one state row n and writes them as one 16-byte store.
+// that group.  Both operands stay in LDS in their natural row-major layout,
+// Bn[j][n] and Xn[j][p] (token-major), and the MFMA fragments, which need the
+// token as the contraction index, are read with the transposing LDS read.
+// The chunk's B rows are staged ONCE (plain 16-byte copies) for all heads.
+// Per head, each thread prefetches 16-byte pieces of x rows (8 consecutive
+// threads cover one 128-byte row slice, so every load is fully coalesced) and
+// the G and dt of those rows into registers while the previous head
+// computes; at commit the pieces are scaled by w_j in fp32, rounded to bf16
+// and written back as 16-byte rows.  The output is accumulated transposed,
+// D[p][n] = sum_j x[j][p] B[j][n] (A operand: x, B operand: B), so that each
+// lane holds four consecutive p of one state row n and writes them as one
+// 16-byte store.
 // 8 waves (two per SIMD); wave w owns the state rows n in tile w (N = 128)
 // or tiles 2w, 2w+1 (N = 256) for all 4 column tiles of the slice.
 #include "ssd_device.hpp"
@@ -31,13 +35,14 @@ template <int Q, int N>
 struct ShgCfg {
   static constexpr int T = kShgThreads;
   static constexpr int PT = 64;
-  // pitch of Bt / Xt rows (elements): 8 dwords past a multiple of 64 dwords,
-  // so the 16-byte fragment reads of 16 rows by 4 lane groups are free of
-  // LDS bank conflicts
-  static constexpr int KP = Q + 16;
-  static constexpr int NTW = N / 16 / 8;           // state-row tiles per wave (8 waves)
-  static constexpr size_t lds_b = (size_t)N * KP * 2;
-  static constexpr size_t lds_x = (size_t)PT * KP * 2;
+  // Row pitches (elements) of Bn and Xn: an odd multiple of 8 dwords modulo
+  // 64, so the transposing reads (per half wave: 8 consecutive rows x 32
+  // bytes) fall in distinct banks.
+  static constexpr int BP = N + 16;
+  static constexpr int XP = PT + 16;
+  static constexpr int NTW = N / 16 / 8;  // state-row tiles per wave (8 waves)
+  static constexpr size_t lds_b = (size_t)Q * BP * 2;
+  static constexpr size_t lds_x = (size_t)Q * XP * 2;
   static constexpr size_t lds_total = lds_b + lds_x;
 };
 
@@ -49,13 +54,14 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   using Cfg = ShgCfg<Q, N>;
   using Op = OpBF16;
   using Frag = Op::Frag;
-  constexpr int T = Cfg::T, PT = Cfg::PT, KP = Cfg::KP, NTW = Cfg::NTW;
-  constexpr int NXB = (Q / 4) * (PT / 8);  // x prefetch blocks: 4 tokens x 8 columns
-  constexpr int XPT = (NXB + T - 1) / T;
+  constexpr int T = Cfg::T, PT = Cfg::PT, BP = Cfg::BP, XP = Cfg::XP, NTW = Cfg::NTW;
+  constexpr int NXB = Q * (PT / 8);  // 16-byte pieces of a head's x slice
+  constexpr int XPT = NXB / T;
+  static_assert(NXB % T == 0 && PT == 64, "x pieces must divide evenly over the block");
 
   extern __shared__ __align__(16) unsigned char shg_smem[];
-  uint16_t* Bt = reinterpret_cast<uint16_t*>(shg_smem);  // [N][KP]
-  uint16_t* Xt = Bt + N * KP;                             // [PT][KP]
+  uint16_t* Bn = reinterpret_cast<uint16_t*>(shg_smem);  // [Q][BP]
+  uint16_t* Xn = Bn + Q * BP;                             // [Q][XP]
 
   const unsigned nblk = gridDim.x;
   unsigned bid = blockIdx.x;
@@ -74,43 +80,29 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   const int tid = threadIdx.x, wave = tid >> 6;
   const int HP = H * P;
 
-  // ---- B chunk -> Bt[n][j] (8x8 register transposes, 16-byte loads and stores)
+  // ---- B chunk -> Bn[j][n] (16-byte copies; a row's pieces go to
+  // consecutive threads)
   {
     const uint16_t* bsrc = Bm + (tok0 * G + g) * N;
     const int GN = G * N;
-    for (int blk = tid; blk < (Q / 8) * (N / 8); blk += T) {
-      const int jb = blk % (Q / 8), nb = blk / (Q / 8);  // neighbouring lanes: neighbouring token blocks
-      uint4 rows[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) rows[r] = *reinterpret_cast<const uint4*>(bsrc + (8 * jb + r) * GN + 8 * nb);
-      const uint32_t* rw = reinterpret_cast<const uint32_t*>(rows);  // rw[4r + q/2] holds columns 2*(q/2), +1 of row r
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        uint32_t o[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const uint32_t lo = rw[4 * (2 * rr) + q / 2], hi = rw[4 * (2 * rr + 1) + q / 2];
-          o[rr] = (q & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        *reinterpret_cast<uint4*>(Bt + (8 * nb + q) * KP + 8 * jb) = make_uint4(o[0], o[1], o[2], o[3]);
-      }
+    for (int blk = tid; blk < Q * (N / 8); blk += T) {
+      const int j = blk / (N / 8), cb = blk % (N / 8);
+      *reinterpret_cast<uint4*>(Bn + j * BP + 8 * cb) = *reinterpret_cast<const uint4*>(bsrc + j * GN + 8 * cb);
     }
   }
 
-  // ---- per-head register prefetch of x, G and dt
-  uint4 xv[XPT][4];
-  float4 gv[XPT], dv[XPT];
-  float glast = 0.f;
-  // Block -> (row block rb of 4 tokens, column block cb of 8 columns): the 16
-  // lanes of a quarter wave take consecutive row blocks (their transposed LDS
-  // writes are contiguous), the 4 quarters take neighbouring column blocks
-  // (each global read covers 64-byte runs of 16 rows).
-  constexpr int RH = Q / 64;
-  auto xmap = [&](int blk, int& rb, int& cb) {
-    const int rest = blk >> 6;
-    rb = (blk & 15) + 16 * (rest % RH);
-    cb = ((blk >> 4) & 3) + 4 * (rest / RH);
+  // ---- per-head register prefetch of x pieces and their G, dt
+  // Piece blk -> (row, 8-column block cb): 8 consecutive threads take the 8
+  // pieces of one row; within a wave the 8 rows are ordered 0,4,1,5,2,6,3,7 so
+  // that the two rows written by a 16-lane group fall in different banks.
+  auto xmap = [&](int blk, int& row, int& cb) {
+    const int lr = (blk >> 3) & 7;
+    row = 8 * (blk >> 6) + (lr >> 1) + 4 * (lr & 1);
+    cb = blk & 7;
   };
+  uint4 xv[XPT];
+  float gv[XPT], dv[XPT];
+  float glast = 0.f;
   auto issue = [&](int h) {
     const uint16_t* xs = x + (tok0 * H + h) * (int64_t)P + p0;
     const int64_t bhc = ((int64_t)b * H + h) * nc + c;
@@ -118,48 +110,32 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     const float* dsrc = dt_bhl + bhc * Q;
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
-      const int blk = tid + u * T;
-      if (NXB % T == 0 || blk < NXB) {  // the test is compile-time true when the blocks divide evenly
-        int cb, rb;
-        xmap(blk, rb, cb);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xv[u][r] = *reinterpret_cast<const uint4*>(xs + (4 * rb + r) * HP + 8 * cb);
-        gv[u] = *reinterpret_cast<const float4*>(gsrc + 4 * rb);
-        dv[u] = *reinterpret_cast<const float4*>(dsrc + 4 * rb);
-      }
+      int row, cb;
+      xmap(tid + u * T, row, cb);
+      xv[u] = *reinterpret_cast<const uint4*>(xs + row * HP + 8 * cb);
+      gv[u] = gsrc[row];
+      dv[u] = dsrc[row];
     }
     glast = gsrc[Q - 1];
   };
   auto commit = [&]() {
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
-      const int blk = tid + u * T;
-      if (NXB % T != 0 && blk >= NXB) continue;
-      int cb, rb;
-      xmap(blk, rb, cb);
-      const float w[4] = {fast_exp(glast - gv[u].x) * dv[u].x, fast_exp(glast - gv[u].y) * dv[u].y,
-                          fast_exp(glast - gv[u].z) * dv[u].z, fast_exp(glast - gv[u].w) * dv[u].w};
-      float v[4][8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint4 q = xv[u][r];
-        v[r][0] = bf16_bits_to_f32(q.x & 0xffffu) * w[r]; v[r][1] = bf16_bits_to_f32(q.x >> 16) * w[r];
-        v[r][2] = bf16_bits_to_f32(q.y & 0xffffu) * w[r]; v[r][3] = bf16_bits_to_f32(q.y >> 16) * w[r];
-        v[r][4] = bf16_bits_to_f32(q.z & 0xffffu) * w[r]; v[r][5] = bf16_bits_to_f32(q.z >> 16) * w[r];
-        v[r][6] = bf16_bits_to_f32(q.w & 0xffffu) * w[r]; v[r][7] = bf16_bits_to_f32(q.w >> 16) * w[r];
-      }
-#pragma unroll
-      for (int col = 0; col < 8; ++col) {
-        uint2 o;
-        o.x = pack_bf16x2(v[0][col], v[1][col]);
-        o.y = pack_bf16x2(v[2][col], v[3][col]);
-        *reinterpret_cast<uint2*>(Xt + (8 * cb + col) * KP + 4 * rb) = o;
-      }
+      int row, cb;
+      xmap(tid + u * T, row, cb);
+      const float w = fast_exp(glast - gv[u]) * dv[u];
+      const uint4 q = xv[u];
+      uint4 o;
+      o.x = pack_bf16x2(bf16_bits_to_f32(q.x & 0xffffu) * w, bf16_bits_to_f32(q.x >> 16) * w);
+      o.y = pack_bf16x2(bf16_bits_to_f32(q.y & 0xffffu) * w, bf16_bits_to_f32(q.y >> 16) * w);
+      o.z = pack_bf16x2(bf16_bits_to_f32(q.z & 0xffffu) * w, bf16_bits_to_f32(q.z >> 16) * w);
+      o.w = pack_bf16x2(bf16_bits_to_f32(q.w & 0xffffu) * w, bf16_bits_to_f32(q.w >> 16) * w);
+      *reinterpret_cast<uint4*>(Xn + row * XP + 8 * cb) = o;
     }
   };
 
   issue(hbase);
-  __syncthreads();  // Bt complete
+  __syncthreads();  // Bn complete
   commit();
   __syncthreads();
 
@@ -185,10 +161,10 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
       for (int kk = 0; kk < Q / 32; ++kk) {
         Frag xf[4];
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) xf[ct] = Lds<Op>::load8(Xt + (16 * ct + l16) * KP + 32 * kk + 8 * lg);
+        for (int ct = 0; ct < 4; ++ct) xf[ct] = lds_frag_tr(Xn + 32 * kk * XP + 16 * ct, XP, ln);
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
-          const Frag bf = Lds<Op>::load8(Bt + (16 * (NTW * wave + i) + l16) * KP + 32 * kk + 8 * lg);
+          const Frag bf = lds_frag_tr(Bn + 32 * kk * BP + 16 * (NTW * wave + i), BP, ln);
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) acc[i][ct] = Op::mma(xf[ct], bf, acc[i][ct]);
         }
@@ -204,7 +180,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
               make_float4(acc[i][ct][0], acc[i][ct][1], acc[i][ct][2], acc[i][ct][3]);
       }
     }
-    __syncthreads();  // all reads of this head's Xt are done
+    __syncthreads();  // all reads of this head's Xn are done
     commit();
     __syncthreads();
   }

@@ -121,6 +121,29 @@ template <> struct Lds<OpF32> {
   }
 };
 
+// ---- transposing fragment reads from row-major LDS tiles (gfx950) ----
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane 16g + i receives as its
+// element r (r = 0..3) the 16-bit word at offset i % 4 of the 8 bytes that
+// lane 16g + 4r + i / 4 addresses (lane layout measured on the hardware).
+__device__ __forceinline__ uint2 lds_read_tr16_b64(const uint16_t* p) {
+  typedef short v4i16_t __attribute__((ext_vector_type(4)));
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+// MFMA fragment of a tile stored row-major [k][col] in LDS, for the operand
+// whose lane index (mod 16) is the column: `tile` points at (row k0, column
+// c0); lane (i = lane % 16, g = lane / 16) receives, as slots 4t + r,
+// tile[k0 + 16t + 4g + r][c0 + i] for t = 0, 1 and r = 0..3.
+__device__ __forceinline__ OpBF16::Frag lds_frag_tr(const uint16_t* tile, int pitch, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const uint16_t* p = tile + (4 * g + (i >> 2)) * pitch + 4 * (i & 3);
+  const uint2 a = lds_read_tr16_b64(p);
+  const uint2 b = lds_read_tr16_b64(p + 16 * pitch);
+  OpBF16::Frag f;
+  f.v = make_uint4(a.x, a.y, b.x, b.y);
+  return f;
+}
+
 template <class Op> struct OpElem;
 template <> struct OpElem<OpBF16> { typedef uint16_t type; };
 template <> struct OpElem<OpF32> { typedef float type; };
