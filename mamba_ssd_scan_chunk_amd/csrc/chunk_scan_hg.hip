@@ -24,9 +24,8 @@
 //  * the CB^T sub-tiles are computed with operand roles swapped (B as the A
 //    operand, C as the B operand), so each lane holds four consecutive j for
 //    one row i; after decay and mask those are directly the A fragment of
-//    M.X (slot e = 4t + r <-> token 32k + 16t + 4lg + r); x rows are kept in
-//    LDS with the tokens of each 32-token step permuted (xpos) so that the
-//    matching x fragment is one 16-byte read.
+//    M.X (slot e = 4t + r <-> token 32k + 16t + 4lg + r), which is exactly
+//    the slot map of the transposing LDS read of the x tile.
 //  * decay: for the sub-tile pairs below the diagonal pair of row tile t,
 //    exp(G_i - G_j) = exp(G_i - G_R) * exp(G_R - G_j) with the reference row
 //    R = 32 * (t / 2) between j and i, so both factors are <= 1 (no overflow;
@@ -34,12 +33,17 @@
 //    times dt_j comes from a per-head LDS table, the row factor scales the
 //    accumulator once; only the diagonal pair takes exact per-element
 //    exponentials, behind the causal select.
-//  * the B and C chunks are staged once in LDS (natural [token][n] layout);
-//    C rows are the B operand of CB^T and the A operand of C.H_in.
-// Per head: x (transposed, Xt[p][j]) and H_in (transposed, Ht[p][n]), both
-// rounded to bf16, plus G and dt rows, are staged in LDS.  The next head's
-// tiles are loaded into registers while the current head computes (software
-// pipeline), then written to LDS after a barrier.
+//  * the B and C chunks are staged once in LDS ([token][n] rows, n permuted
+//    inside each 32-block as npos() states, so that the C fragment of C.H_in
+//    takes the slot map of the transposing read of H_in); C rows are the B
+//    operand of both CB^T and C.H_in.
+// Per head: x (Xn[j][p]) and H_in (Hn[n][p], rounded to bf16) are staged in
+// their natural row-major layouts, plus the G and dt rows; the A-operand
+// fragments (the contraction index down the rows) come from the transposing
+// LDS read.  The next head's rows are loaded into registers (fully coalesced:
+// consecutive threads take consecutive 16-byte pieces of a row) while the
+// current head computes (software pipeline), then written to LDS after a
+// barrier.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -60,10 +64,13 @@ struct HgCfg {
   // 16-byte fragment reads of 16 rows by 4 lane groups then fall in distinct
   // banks (a 4-dword pad halves the read rate on this LDS).
   static constexpr int NPI = N + 16;  // pitch (elements) of n-indexed LDS rows
-  static constexpr int XP = Q + 16;   // pitch of Xt rows
+  // pitch of the p-indexed rows Xn, Hn: an odd multiple of 8 dwords modulo
+  // 64, so a transposing read (per half wave: 8 consecutive rows x 32 bytes)
+  // is free of bank conflicts
+  static constexpr int XNP = PT + 16;
   static constexpr size_t lds_bs = (size_t)Q * NPI * 2;
-  static constexpr size_t lds_xh = (size_t)PT * XP * 2 + (size_t)PT * NPI * 2;
-  static constexpr size_t lds_a = lds_bs > lds_xh ? lds_bs : lds_xh;  // Bs, later Xt + Ht
+  static constexpr size_t lds_xh = (size_t)Q * XNP * 2 + (size_t)N * XNP * 2;
+  static constexpr size_t lds_a = lds_bs > lds_xh ? lds_bs : lds_xh;  // Bs, later Xn + Hn
   static constexpr size_t lds_c = (size_t)Q * NPI * 2;                // Cs
   static constexpr size_t lds_w = sizeof(float) * (size_t)(QT / 2) * Q;  // Ws
   static constexpr size_t lds_total = lds_a + lds_c + lds_w + 2 * sizeof(float) * Q;
@@ -83,12 +90,13 @@ struct HgArgs {
   int64_t tok0;
 };
 
-// Position of token j of the chunk inside an Xt row.  The A-operand fragment
-// of lane (l16, lg) at step k holds tokens 32k + 16t + 4lg + r (t = 0, 1;
-// r = 0..3); storing them at 32k + 8lg + 4t + r makes that fragment one
-// 16-byte read.
-__device__ __forceinline__ int xpos(int j) {
-  return (j & ~31) | ((j & 12) << 1) | ((j & 16) >> 2) | (j & 3);
+// Position of state index n inside a Bs / Cs row.  The transposing read of
+// H_in gives lane (l16, lg) at step s the indices n = 32s + 16t + 4lg + r as
+// slots 4t + r (t = 0, 1; r = 0..3); storing n at 32s + 8lg + 4t + r makes the
+// matching C fragment one 16-byte read.  CB^T reads B and C rows at the same
+// positions, so its contraction is unaffected.
+__device__ __forceinline__ int npos(int n) {
+  return (n & ~31) | ((n & 12) << 1) | ((n & 16) >> 2) | (n & 3);
 }
 
 template <int Q, int NK, int CT, bool IN_BF16, bool Y_BF16>
@@ -96,18 +104,20 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   using Cfg = HgCfg<Q, NK, CT>;
   using Op = OpBF16;
   using Frag = Op::Frag;
-  constexpr int QT = Cfg::QT, PT = Cfg::PT, N = Cfg::N, NPI = Cfg::NPI, XP = Cfg::XP, T = Cfg::T;
+  constexpr int QT = Cfg::QT, PT = Cfg::PT, N = Cfg::N, NPI = Cfg::NPI, XNP = Cfg::XNP, T = Cfg::T;
   static_assert(IN_BF16, "the head-group chunk scan takes bf16 inputs");
-  constexpr int NXB = (Q / 4) * (PT / 8);    // x prefetch blocks (4 tokens x 8 columns)
-  constexpr int NHB = (N / 4) * (PT / 4);    // H prefetch blocks (4 n x 4 p)
-  constexpr int XPT = (NXB + T - 1) / T;     // blocks per thread
-  constexpr int HPT = (NHB + T - 1) / T;
+  static_assert(PT == 64, "the prefetch maps assume a 64-column slice");
+  constexpr int NXB = Q * (PT / 8);          // x prefetch pieces (16 bytes: 8 columns of one token)
+  constexpr int NHB = N * (PT / 4);          // H prefetch pieces (16 bytes: 4 columns of one n)
+  constexpr int XPT = NXB / T;               // pieces per thread
+  constexpr int HPT = NHB / T;
+  static_assert(NXB % T == 0 && NHB % T == 0, "prefetch pieces must divide evenly over the block");
   constexpr int NSL = QT + 1;                // CB^T sub-tiles held per wave
   static_assert(T % Q == 0 && (Q & (Q - 1)) == 0, "the G/dt staging assumes T is a multiple of Q");
 
   uint16_t* Bs = reinterpret_cast<uint16_t*>(smem);                    // [Q][NPI]  (phase 0-1 only)
-  uint16_t* Xt = reinterpret_cast<uint16_t*>(smem);                    // [PT][XP]  (aliases Bs later)
-  uint16_t* Ht = Xt + PT * XP;                                          // [PT][NPI]
+  uint16_t* Xn = reinterpret_cast<uint16_t*>(smem);                    // [Q][XNP]  (aliases Bs later)
+  uint16_t* Hn = Xn + Q * XNP;                                          // [N][XNP]
   uint16_t* Cs = reinterpret_cast<uint16_t*>(smem + Cfg::lds_a);        // [Q][NPI]
   float* Ws = reinterpret_cast<float*>(smem + Cfg::lds_a + Cfg::lds_c);  // [QT/2][Q]
   float* Gs = Ws + (QT / 2) * Q;                                        // [Q]
@@ -118,25 +128,22 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   const int64_t tok0 = a.tok0;
   const int HP = H * P;
 
-  // ---- phase 0: B and C chunks -> Bs, Cs (natural [token][n] layout, bf16)
+  // ---- phase 0: B and C chunks -> Bs, Cs ([token][npos(n)], bf16).  A
+  // 16-byte piece holds n = 8nb .. 8nb+7, whose two 4-element halves land at
+  // npos(8nb) and npos(8nb + 4).
   {
     const int64_t bc0 = (tok0 * G + a.g) * N;  // element offset of (token 0 of the chunk, group g)
     const int GN = G * N;
     for (int idx = tid; idx < Q * (N / 8); idx += T) {
       const int j = idx / (N / 8), nb = idx - (idx / (N / 8)) * (N / 8);
       const int off = j * GN + 8 * nb;
-      if constexpr (IN_BF16) {
-        *reinterpret_cast<uint4*>(Bs + j * NPI + 8 * nb) =
-            *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Bm) + bc0 + off);
-        *reinterpret_cast<uint4*>(Cs + j * NPI + 8 * nb) =
-            *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Cm) + bc0 + off);
-      } else {
-        float t[8];
-        load8_as_f32(a.Bm, bc0 + off, false, t);
-        Lds<Op>::store8(Bs + j * NPI + 8 * nb, t);
-        load8_as_f32(a.Cm, bc0 + off, false, t);
-        Lds<Op>::store8(Cs + j * NPI + 8 * nb, t);
-      }
+      const int q0 = j * NPI + npos(8 * nb), q1 = j * NPI + npos(8 * nb + 4);
+      const uint4 bv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Bm) + bc0 + off);
+      const uint4 cv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Cm) + bc0 + off);
+      *reinterpret_cast<uint2*>(Bs + q0) = make_uint2(bv.x, bv.y);
+      *reinterpret_cast<uint2*>(Bs + q1) = make_uint2(bv.z, bv.w);
+      *reinterpret_cast<uint2*>(Cs + q0) = make_uint2(cv.x, cv.y);
+      *reinterpret_cast<uint2*>(Cs + q1) = make_uint2(cv.z, cv.w);
     }
   }
   __syncthreads();
@@ -165,48 +172,35 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 
   // ---- per-head register prefetch: issued before a head's compute,
   // committed to LDS after it.
-  uint4 xv[XPT][4];   // 4 rows x 16 bytes of x per block
-  float4 hv[HPT][4];  // 4 rows (n) x 4 columns (p) of H_in per block
+  uint4 xv[XPT];   // 16-byte pieces of x rows (8 columns, bf16)
+  float4 hv[HPT];  // 16-byte pieces of H_in rows (4 columns, fp32)
   float pg = 0.f, pd = 0.f;
-  // Block -> (row block, column block) maps chosen so that the transposed
-  // LDS writes of each half wave hit distinct banks, while the global reads of
-  // a wave still cover whole 64-byte runs of rows.
-  constexpr int RH = Q / 64;   // x: groups of 16 row blocks
-  constexpr int PH = PT / 16;  // H: groups of 4 column blocks
-  auto xmap = [&](int blk, int& rbk, int& cbk) {
-    const int rest = blk >> 6;
-    rbk = (blk & 15) + 16 * (rest % RH);
-    cbk = ((blk >> 4) & 3) + 4 * (rest / RH);
+  // x piece blk -> (row, 8-column block cb): 8 consecutive threads take the 8
+  // pieces of one row; within a wave the 8 rows are ordered 0,4,1,5,2,6,3,7 so
+  // that the two rows written by a 16-lane group fall in different banks.
+  auto xmap = [&](int blk, int& row, int& cb) {
+    const int lr = (blk >> 3) & 7;
+    row = 8 * (blk >> 6) + (lr >> 1) + 4 * (lr & 1);
+    cb = blk & 7;
   };
-  auto hmap = [&](int blk, int& nb, int& pb) {
-    const int pq = (blk >> 4) & 3, rest = blk >> 6;
-    pb = (pq >> 1) + 2 * (pq & 1) + 4 * (rest % PH);
-    nb = (blk & 15) + 16 * (rest / PH);
-  };
-  auto issue = [&](int h) {
+  auto issue = [&](int h) __attribute__((always_inline)) {
     const uint16_t* xh = static_cast<const uint16_t*>(a.x) + (tok0 * H + h) * (int64_t)P + a.p0;
 #pragma unroll
     for (int uu = 0; uu < XPT; ++uu) {
       const int blk = tid + uu * T;
-      if (blk < NXB) {
-        int rbk, cbk;
-        xmap(blk, rbk, cbk);
-        const int o0 = (4 * rbk) * HP + 8 * cbk;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xv[uu][r] = *reinterpret_cast<const uint4*>(xh + o0 + r * HP);
+      if (blk < NXB) {  // always true; the block boundary keeps the scheduler from hoisting across it
+        int row, cb;
+        xmap(blk, row, cb);
+        xv[uu] = *reinterpret_cast<const uint4*>(xh + row * HP + 8 * cb);
       }
     }
+    // H_in piece blk -> (n = blk / 16, columns 4 (blk % 16) .. +3): 16
+    // consecutive threads read one 256-byte row
     const float* hs = a.carried + (((int64_t)a.b * nc + a.c) * H + h) * (int64_t)(N * P) + a.p0;
 #pragma unroll
     for (int uu = 0; uu < HPT; ++uu) {
       const int blk = tid + uu * T;
-      if (blk < NHB) {
-        int nb, pb;
-        hmap(blk, nb, pb);
-        const int o0 = (4 * nb) * P + 4 * pb;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hv[uu][r] = *reinterpret_cast<const float4*>(hs + o0 + r * P);
-      }
+      if (blk < NHB) hv[uu] = *reinterpret_cast<const float4*>(hs + (blk >> 4) * P + 4 * (blk & 15));
     }
     {
       // every thread loads (and later stores) the values of token tid mod Q:
@@ -216,44 +210,22 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       pd = a.dt_bhl[bhc * Q + (tid & (Q - 1))];
     }
   };
-  auto commit = [&]() {
+  auto commit = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int uu = 0; uu < XPT; ++uu) {
       const int blk = tid + uu * T;
-      if (blk < NXB) {
-        int rbk, cbk;
-        xmap(blk, rbk, cbk);
-        // bf16 x: the transpose is a pure 16-bit shuffle, no conversion
-        const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&xv[uu][0]);
-        const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&xv[uu][1]);
-        const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&xv[uu][2]);
-        const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&xv[uu][3]);
-#pragma unroll
-        for (int col = 0; col < 8; ++col) {
-          const int m = col >> 1;
-          uint2 w;
-          w.x = (col & 1) ? pick_hi16(r0[m], r1[m]) : pick_lo16(r0[m], r1[m]);
-          w.y = (col & 1) ? pick_hi16(r2[m], r3[m]) : pick_lo16(r2[m], r3[m]);
-          *reinterpret_cast<uint2*>(Xt + (8 * cbk + col) * XP + xpos(4 * rbk)) = w;
-        }
-      }
+      if (blk >= NXB) continue;
+      int row, cb;
+      xmap(blk, row, cb);
+      const uint4 q = xv[uu];  // rebuilt from its components: a whole-struct copy kept xv in scratch
+      *reinterpret_cast<uint4*>(Xn + row * XNP + 8 * cb) = make_uint4(q.x, q.y, q.z, q.w);
     }
 #pragma unroll
     for (int uu = 0; uu < HPT; ++uu) {
       const int blk = tid + uu * T;
-      if (blk < NHB) {
-        int nb, pb;
-        hmap(blk, nb, pb);
-        uint2 w0, w1, w2, w3;
-        w0.x = pack_bf16x2(hv[uu][0].x, hv[uu][1].x); w0.y = pack_bf16x2(hv[uu][2].x, hv[uu][3].x);
-        w1.x = pack_bf16x2(hv[uu][0].y, hv[uu][1].y); w1.y = pack_bf16x2(hv[uu][2].y, hv[uu][3].y);
-        w2.x = pack_bf16x2(hv[uu][0].z, hv[uu][1].z); w2.y = pack_bf16x2(hv[uu][2].z, hv[uu][3].z);
-        w3.x = pack_bf16x2(hv[uu][0].w, hv[uu][1].w); w3.y = pack_bf16x2(hv[uu][2].w, hv[uu][3].w);
-        *reinterpret_cast<uint2*>(Ht + (4 * pb + 0) * NPI + 4 * nb) = w0;
-        *reinterpret_cast<uint2*>(Ht + (4 * pb + 1) * NPI + 4 * nb) = w1;
-        *reinterpret_cast<uint2*>(Ht + (4 * pb + 2) * NPI + 4 * nb) = w2;
-        *reinterpret_cast<uint2*>(Ht + (4 * pb + 3) * NPI + 4 * nb) = w3;
-      }
+      if (blk >= NHB) continue;
+      *reinterpret_cast<uint2*>(Hn + (blk >> 4) * XNP + 4 * (blk & 15)) =
+          make_uint2(pack_bf16x2(hv[uu].x, hv[uu].y), pack_bf16x2(hv[uu].z, hv[uu].w));
     }
     Gs[tid & (Q - 1)] = pg;  // threads tid and tid + Q write the same value
     dts[tid & (Q - 1)] = pd;
@@ -261,7 +233,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // Column factors of the off-diagonal sub-tiles: for the reference row
   // R = 32u, Ws[u][j] = exp(G_R - G_j) dt_j (j < R, so G_R <= G_j and the
   // factor is <= 1).
-  auto make_w = [&]() {
+  auto make_w = [&]() __attribute__((always_inline)) {
     for (int idx = tid; idx < (QT / 2) * Q; idx += T) {
       const int u = idx / Q, j = idx - (idx / Q) * Q;
       if (j < 32 * u) Ws[idx] = fast_exp(Gs[32 * u] - Gs[j]) * dts[j];
@@ -329,10 +301,9 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   auto steps = [&](const int ta, const int tb, f32x4_t (&acc0)[CT], f32x4_t (&acc1)[CT], int ln) {
     const int l16 = ln & 15, lg = ln >> 4;
     const int Ua = ta >> 1, Ub = tb >> 1;
-    const uint16_t* xrow = Xt + l16 * XP + 8 * lg;
     Frag xn[CT];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) xn[ct] = Lds<Op>::load8(xrow + 16 * ct * XP);
+    for (int ct = 0; ct < CT; ++ct) xn[ct] = lds_frag_tr(Xn + 16 * ct, XNP, ln);
 #pragma unroll
     for (int k = 0; k < QT / 2; ++k) {
       if (k <= Ub) {
@@ -341,7 +312,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         for (int ct = 0; ct < CT; ++ct) xf[ct] = xn[ct];
         if (k + 1 < QT / 2) {
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) xn[ct] = Lds<Op>::load8(xrow + 16 * ct * XP + 32 * (k + 1));
+          for (int ct = 0; ct < CT; ++ct) xn[ct] = lds_frag_tr(Xn + 32 * (k + 1) * XNP + 16 * ct, XNP, ln);
         }
         if (k < Ua) offdiag(std::integral_constant<int, 0>{}, k, Ua, xf, acc0, lg);
         else if (k == Ua) diag(std::integral_constant<int, 0>{}, k, ta, xf, acc0, l16, lg);
@@ -360,8 +331,11 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       const int pc = 16 * ct + 4 * lg;
       const int off = i * HP + pc;
       float v[4];
+      const uint2 xq = *reinterpret_cast<const uint2*>(Xn + i * XNP + pc);  // x[i][pc .. pc+3]
+      const float xr[4] = {bf16_bits_to_f32(xq.x & 0xffffu), bf16_bits_to_f32(xq.x >> 16),
+                           bf16_bits_to_f32(xq.y & 0xffffu), bf16_bits_to_f32(xq.y >> 16)};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = acc[ct][r] + dsk * bf16_bits_to_f32(Xt[(pc + r) * XP + xpos(i)]);
+      for (int r = 0; r < 4; ++r) v[r] = acc[ct][r] + dsk * xr[r];
       if constexpr (Y_BF16) {
         uint2 w;
         w.x = pack_bf16x2(v[0], v[1]);
@@ -374,7 +348,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   };
 
   issue(a.hbase);
-  __syncthreads();  // every wave is done reading Bs before Xt/Ht overwrite it
+  __syncthreads();  // every wave is done reading Bs before Xn/Hn overwrite it
   commit();
   __syncthreads();
   make_w();
@@ -414,7 +388,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       for (int s = 0; s < NK; ++s) {
         Frag hf[CT];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) hf[ct] = Lds<Op>::load8(Ht + (16 * ct + l16) * NPI + 32 * s + 8 * lg);
+        for (int ct = 0; ct < CT; ++ct) hf[ct] = lds_frag_tr(Hn + 32 * s * XNP + 16 * ct, XNP, ln);
         const Frag ca0 = Lds<Op>::load8(Cs + (16 * ta + l16) * NPI + 32 * s + 8 * lg);
         const Frag ca1 = Lds<Op>::load8(Cs + (16 * tb + l16) * NPI + 32 * s + 8 * lg);
 #pragma unroll

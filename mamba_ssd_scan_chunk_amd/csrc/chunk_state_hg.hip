@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   uint4 xv[XPT];
   float gv[XPT], dv[XPT];
   float glast = 0.f;
-  auto issue = [&](int h) {
+  auto issue = [&](int h) __attribute__((always_inline)) {
     const uint16_t* xs = x + (tok0 * H + h) * (int64_t)P + p0;
     const int64_t bhc = ((int64_t)b * H + h) * nc + c;
     const float* gsrc = dA_cumsum + bhc * Q;
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     }
     glast = gsrc[Q - 1];
   };
-  auto commit = [&]() {
+  auto commit = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       int row, cb;
