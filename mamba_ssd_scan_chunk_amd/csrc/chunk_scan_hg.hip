@@ -183,7 +183,14 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     row = 8 * (blk >> 6) + (lr >> 1) + 4 * (lr & 1);
     cb = blk & 7;
   };
-  auto issue = [&](int h) __attribute__((always_inline)) {
+  // Column-factor table rows handled by this thread: entry tid + T*m of Ws is
+  // (u, j) = (tid / Q + (T / Q) * m, tid % Q); the reference G_{32u} is the
+  // same for the whole wave (Q >= 64), so it is a scalar load.
+  constexpr int NWM = (QT / 2) * Q / T;
+  static_assert(((QT / 2) * Q) % T == 0, "column-factor entries must divide evenly over the block");
+  float gref[NWM];
+  // x pieces and the token's G, dt (issued at the top of a head) ...
+  auto issue_x = [&](int h) __attribute__((always_inline)) {
     const uint16_t* xh = static_cast<const uint16_t*>(a.x) + (tok0 * H + h) * (int64_t)P + a.p0;
 #pragma unroll
     for (int uu = 0; uu < XPT; ++uu) {
@@ -194,6 +201,18 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         xv[uu] = *reinterpret_cast<const uint4*>(xh + row * HP + 8 * cb);
       }
     }
+    // every thread loads (and later stores) the values of token tid mod Q:
+    // T is a multiple of Q, and branch-free code keeps the memory waits exact
+    const int64_t bhc = ((int64_t)a.b * H + h) * nc + a.c;
+    pg = a.dA_cumsum[bhc * Q + (tid & (Q - 1))];
+    pd = a.dt_bhl[bhc * Q + (tid & (Q - 1))];
+    const int uq = __builtin_amdgcn_readfirstlane(tid / Q);
+#pragma unroll
+    for (int m = 0; m < NWM; ++m) gref[m] = a.dA_cumsum[bhc * Q + 32 * (uq + (T / Q) * m)];
+  };
+  // ... and H_in pieces (issued after the C.H_in product, spreading the
+  // vector-memory issue over the head)
+  auto issue_h = [&](int h) __attribute__((always_inline)) {
     // H_in piece blk -> (n = blk / 16, columns 4 (blk % 16) .. +3): 16
     // consecutive threads read one 256-byte row
     const float* hs = a.carried + (((int64_t)a.b * nc + a.c) * H + h) * (int64_t)(N * P) + a.p0;
@@ -201,13 +220,6 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     for (int uu = 0; uu < HPT; ++uu) {
       const int blk = tid + uu * T;
       if (blk < NHB) hv[uu] = *reinterpret_cast<const float4*>(hs + (blk >> 4) * P + 4 * (blk & 15));
-    }
-    {
-      // every thread loads (and later stores) the values of token tid mod Q:
-      // T is a multiple of Q, and branch-free code keeps the memory waits exact
-      const int64_t bhc = ((int64_t)a.b * H + h) * nc + a.c;
-      pg = a.dA_cumsum[bhc * Q + (tid & (Q - 1))];
-      pd = a.dt_bhl[bhc * Q + (tid & (Q - 1))];
     }
   };
   auto commit = [&]() __attribute__((always_inline)) {
@@ -229,16 +241,13 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     }
     Gs[tid & (Q - 1)] = pg;  // threads tid and tid + Q write the same value
     dts[tid & (Q - 1)] = pd;
+    // Column factors of the off-diagonal sub-tiles: for the reference row
+    // R = 32u, Ws[u][j] = exp(G_R - G_j) dt_j, read only for j < R (so
+    // G_R <= G_j and the factor is <= 1); entries with j >= R are unused.
+#pragma unroll
+    for (int m = 0; m < NWM; ++m) Ws[tid + T * m] = fast_exp(gref[m] - pg) * pd;
   };
-  // Column factors of the off-diagonal sub-tiles: for the reference row
-  // R = 32u, Ws[u][j] = exp(G_R - G_j) dt_j (j < R, so G_R <= G_j and the
-  // factor is <= 1).
-  auto make_w = [&]() __attribute__((always_inline)) {
-    for (int idx = tid; idx < (QT / 2) * Q; idx += T) {
-      const int u = idx / Q, j = idx - (idx / Q) * Q;
-      if (j < 32 * u) Ws[idx] = fast_exp(Gs[32 * u] - Gs[j]) * dts[j];
-    }
-  };
+
 
   // Sub-tile pair steps of one head for both row tiles of the wave.  TSEL (0:
   // tile ra, 1: tile rb) fixes the register-slot map of a tile; the tile
@@ -347,20 +356,20 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     }
   };
 
-  issue(a.hbase);
+  issue_x(a.hbase);
+  issue_h(a.hbase);
   __syncthreads();  // every wave is done reading Bs before Xn/Hn overwrite it
   commit();
-  __syncthreads();
-  make_w();
   __syncthreads();
 
   for (int hh = 0; hh < a.HG; ++hh) {
     const int h = a.hbase + hh;
-    // The prefetch, commit and column-factor table run on every iteration (the
-    // last one loads its own head again, unused): with no conditional around
-    // them the compiler's memory-counter waits stay exact, so the loads of the
-    // next head remain in flight across the whole compute of this one.
-    issue(hh + 1 < a.HG ? h + 1 : h);
+    // The prefetch and commit run on every iteration (the last one loads its
+    // own head again, unused): with no conditional around them the compiler's
+    // memory-counter waits stay exact, so the loads of the next head remain in
+    // flight across the whole compute of this one.
+    const int hn = hh + 1 < a.HG ? h + 1 : h;
+    issue_x(hn);
     const float dsk = a.D[h];
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -397,6 +406,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
           acc1[ct] = Op::mma(hf[ct], ca1, acc1[ct]);
         }
       }
+      issue_h(hn);
       const float e0 = fast_exp(Gs[32 * (ta >> 1)]), e1 = fast_exp(Gs[32 * (tb >> 1)]);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
@@ -409,8 +419,6 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     }
     __syncthreads();  // all reads of this head's tiles are done
     commit();
-    __syncthreads();
-    make_w();
     __syncthreads();
   }
 }
