@@ -252,8 +252,12 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // Sub-tile pair steps of one head for both row tiles of the wave.  TSEL (0:
   // tile ra, 1: tile rb) fixes the register-slot map of a tile; the tile
   // indices are run-time, wave-uniform values, so all waves share this code.
+  // The helpers only build the M fragment of a pair; each tile has a single
+  // MFMA site per step, so its accumulators are updated in place (alternative
+  // MFMA sites per branch made the compiler copy accumulators at every merge,
+  // each copy waiting for the MFMA results).
   // Off-diagonal pair k of a tile whose diagonal pair is U: M' = CB * Ws[U][j].
-  auto offdiag = [&](auto tsel_c, const int k, const int U, const Frag (&xf)[CT], f32x4_t (&acc)[CT], int lg) {
+  auto offdiag_frag = [&](auto tsel_c, const int k, const int U, int lg) -> Frag {
     constexpr int TSEL = decltype(tsel_c)::value;
     const float4 w0 = *reinterpret_cast<const float4*>(Ws + U * Q + 32 * k + 4 * lg);
     const float4 w1 = *reinterpret_cast<const float4*>(Ws + U * Q + 32 * k + 16 + 4 * lg);
@@ -261,15 +265,12 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     const f32x4_t c1 = cb[TSEL ? (QT - 2 * k - 1) : 2 * k + 1];
     const float m[8] = {c0[0] * w0.x, c0[1] * w0.y, c0[2] * w0.z, c0[3] * w0.w,
                         c1[0] * w1.x, c1[1] * w1.y, c1[2] * w1.z, c1[3] * w1.w};
-    const Frag mf = Op::from_f32(m);
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[ct] = Op::mma(xf[ct], mf, acc[ct]);
+    return Op::from_f32(m);
   };
   // Diagonal pair k = tile / 2: the row factor exp(G_i - G_R) first scales
-  // everything accumulated so far, then the pair takes exact decays, with the
-  // causal select made before the exponential.
-  auto diag = [&](auto tsel_c, const int k, const int tile, const Frag (&xf)[CT], f32x4_t (&acc)[CT], int l16,
-                  int lg) {
+  // everything accumulated so far (in place), then the pair takes exact
+  // decays, with the causal select made before the exponential.
+  auto diag_frag = [&](auto tsel_c, const int k, const int tile, f32x4_t (&acc)[CT], int l16, int lg) -> Frag {
     constexpr int TSEL = decltype(tsel_c)::value;
     const int i = 16 * tile + l16;  // the token this lane's interaction values and outputs belong to
     // G and dt of the lane's 8 tokens j = 32k + 16t + 4lg + r, read as vectors
@@ -297,9 +298,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       const float dec = fast_exp(keep ? gi - gj[e8] : -INFINITY) * dj[e8];
       m[e8] = keep ? cvv[e8] * dec : 0.f;
     }
-    const Frag mf = Op::from_f32(m);
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[ct] = Op::mma(xf[ct], mf, acc[ct]);
+    return Op::from_f32(m);
   };
   // One pass over the pair index k serves both tiles (ta = w < tb = QT-1-w, so
   // the diagonal pair of ta comes first): the x fragments of a step are read
@@ -323,10 +322,18 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) xn[ct] = lds_frag_tr(Xn + 32 * (k + 1) * XNP + 16 * ct, XNP, ln);
         }
-        if (k < Ua) offdiag(std::integral_constant<int, 0>{}, k, Ua, xf, acc0, lg);
-        else if (k == Ua) diag(std::integral_constant<int, 0>{}, k, ta, xf, acc0, l16, lg);
-        if (k < Ub) offdiag(std::integral_constant<int, 1>{}, k, Ub, xf, acc1, lg);
-        else diag(std::integral_constant<int, 1>{}, k, tb, xf, acc1, l16, lg);
+        if (k <= Ua) {
+          Frag mfa;
+          if (k < Ua) mfa = offdiag_frag(std::integral_constant<int, 0>{}, k, Ua, lg);
+          else mfa = diag_frag(std::integral_constant<int, 0>{}, k, ta, acc0, l16, lg);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) acc0[ct] = Op::mma(xf[ct], mfa, acc0[ct]);
+        }
+        Frag mfb;
+        if (k < Ub) mfb = offdiag_frag(std::integral_constant<int, 1>{}, k, Ub, lg);
+        else mfb = diag_frag(std::integral_constant<int, 1>{}, k, tb, acc1, l16, lg);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc1[ct] = Op::mma(xf[ct], mfb, acc1[ct]);
       }
     }
   };
