@@ -23,9 +23,11 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
 
-def algorithmic_costs(w, in_bytes, y_bytes):
+def algorithmic_costs(w, in_bytes, y_bytes, carried_bytes=4):
     """Algorithmic bytes and flops per launch of each kernel (each tensor read
-    or written once; causal interaction terms only; C.B^T once per group)."""
+    or written once; causal interaction terms only; C.B^T once per group).
+    ``carried_bytes`` is the element size of the carried states handed from the
+    state passing to the chunk scan (2 on the bf16-operand path)."""
     B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     nc = L // Q
     blh = B * L * H
@@ -34,9 +36,9 @@ def algorithmic_costs(w, in_bytes, y_bytes):
     k["chunk_cumsum"] = dict(bytes=4 * blh + 4 * H + 2 * 4 * blh, flops=2 * blh)
     k["chunk_state"] = dict(bytes=in_bytes * blh * P + in_bytes * B * L * G * N + 2 * 4 * blh + 4 * st,
                             flops=2 * blh * N * P)
-    k["state_passing"] = dict(bytes=4 * st + 4 * B * H * nc + 4 * st + 4 * B * H * N * P,
+    k["state_passing"] = dict(bytes=4 * st + 4 * B * H * nc + carried_bytes * st + 4 * B * H * N * P,
                               flops=2 * st)
-    k["chunk_scan"] = dict(bytes=in_bytes * blh * P + 2 * in_bytes * B * L * G * N + 2 * 4 * blh + 4 * st
+    k["chunk_scan"] = dict(bytes=in_bytes * blh * P + 2 * in_bytes * B * L * G * N + 2 * 4 * blh + carried_bytes * st
                            + 4 * H + y_bytes * blh * P,
                            flops=2 * blh * N * P + B * nc * H * Q * (Q + 1) * P + B * nc * G * Q * (Q + 1) * N)
     return k
@@ -163,15 +165,20 @@ def main():
     ms_per_step = ms_total / args.steps
     tokens_per_s = w.tokens / (ms_per_step / 1e3)
 
-    # ---- phase 2: per-kernel durations (same pipeline, events on the launch stream)
+    # ---- phase 2: per-kernel durations of the same pipeline ssd_forward runs
+    # (bf16-operand path: carried states handed over as bf16, fp32 path: fp32
+    # in place), events on the launch stream
     dA = torch.empty((B, H, nc, Q), device=dev, dtype=torch.float32)
     dtb = torch.empty_like(dA)
     states = torch.empty((B, nc, H, N, P), device=dev, dtype=torch.float32)
+    carried_bytes = 2 if args.mma == "bf16" else 4
+    carried = (torch.empty((B, nc, H, N, P), device=dev, dtype=torch.bfloat16) if carried_bytes == 2
+               else states)
     calls = {
         "chunk_cumsum": lambda: ops.ssd_chunk_cumsum(sh, t["dt"], t["A"], dA_cumsum=dA, dt_bhl=dtb),
         "chunk_state": lambda: ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, states=states, mma=args.mma),
-        "state_passing": lambda: ops.ssd_state_passing(sh, states, dA, carried=states, final_states=fin),
-        "chunk_scan": lambda: ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, states, t["D"], y=y,
+        "state_passing": lambda: ops.ssd_state_passing(sh, states, dA, carried=carried, final_states=fin),
+        "chunk_scan": lambda: ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, carried, t["D"], y=y,
                                                  mma=args.mma),
     }
     order = list(calls) if args.kernel_only is None else [args.kernel_only]
@@ -191,7 +198,7 @@ def main():
             else:
                 calls[k]()
     torch.cuda.synchronize()
-    costs = algorithmic_costs(w, in_bytes, y_bytes)
+    costs = algorithmic_costs(w, in_bytes, y_bytes, carried_bytes)
     kernels = {}
     for k, pairs in evs.items():
         us = 1e3 * sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)

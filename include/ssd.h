@@ -31,8 +31,10 @@
  *   - Every argument check runs on the host BEFORE any HIP call; a failed
  *     check returns its status and enqueues nothing.  A launch failure is
  *     reported as SSD_ERR_HIP.  Values are not validated: NaN/Inf propagate.
- *   - dt, A, D, dA_cumsum, dt_bhl and all states are float32.  x, B and C
- *     share one input dtype `in` (F32 or BF16).
+ *   - dt, A, D, dA_cumsum, dt_bhl, the chunk states, initial and final
+ *     states are float32; the carried states are F32 or BF16 (the caller's
+ *     choice, `carried_dtype`).  x, B and C share one input dtype `in` (F32
+ *     or BF16).
  *   - Shape limits of this version (else SSD_ERR_UNSUPPORTED): headdim P and
  *     dstate N multiples of 16 with N <= 256 and P <= 256; chunk Q in
  *     {32, 64, 128, 256}; seqlen L a multiple of Q.
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 typedef enum {
   SSD_OK = 0,
@@ -104,12 +106,15 @@ ssd_status ssd_chunk_state(const ssd_shape* shape, const void* x, const void* Bm
  *   run = initial_states[b,h] (zeros when NULL)
  *   for c in 0..nc-1:  carried[b,c,h] = run;  run = exp(G_{Q-1}(c)) run + chunk_states[b,c,h]
  *   final_states[b,h] = run
- * carried may equal chunk_states (in place).  chunk_states, carried
- * [B,nc,H,N,P]; initial_states, final_states [B,H,N,P]; all fp32.
+ * The recurrence runs in fp32.  carried is written as fp32
+ * (carried_dtype = SSD_F32; it may then equal chunk_states: in place) or
+ * rounded to bf16, nearest even (SSD_BF16; it must then be a separate
+ * buffer, else SSD_ERR_UNSUPPORTED).  chunk_states, carried [B,nc,H,N,P];
+ * initial_states, final_states [B,H,N,P] fp32.
  */
-ssd_status ssd_state_passing(const ssd_shape* shape, const float* chunk_states, float* carried,
-                             const float* dA_cumsum, const float* initial_states,
-                             float* final_states, void* stream);
+ssd_status ssd_state_passing(const ssd_shape* shape, const float* chunk_states, void* carried,
+                             ssd_dtype carried_dtype, const float* dA_cumsum,
+                             const float* initial_states, float* final_states, void* stream);
 
 /*
  * Fused chunk output (P1, compute_out paragraph: carried-state term, decayed
@@ -119,24 +124,33 @@ ssd_status ssd_state_passing(const ssd_shape* shape, const float* chunk_states, 
  *   y[b,t,h,:] = exp(G_i) C_i^T carried[b,c,h]
  *              + sum_{j<=i} (C_i . B_j) exp(G_i - G_j) dt_j x[b,cQ+j,h,:]
  *              + D[h] x[b,t,h,:]
- * x [B,L,H,P], Bm/Cm [B,L,G,N] (dtype `in`), carried [B,nc,H,N,P] fp32,
- * D [H] fp32  ->  y [B,L,H,P] in `y_dtype` (F32 or BF16, rounded to nearest even).
+ * x [B,L,H,P], Bm/Cm [B,L,G,N] (dtype `in`), carried [B,nc,H,N,P] in
+ * `carried_dtype`, D [H] fp32  ->  y [B,L,H,P] in `y_dtype` (F32 or BF16,
+ * rounded to nearest even).  With SSD_MMA_BF16 the carried state is rounded
+ * to bf16 as a matrix operand anyway, so BF16 carried states written by
+ * ssd_state_passing give bit-identical results with half the traffic.
  */
 ssd_status ssd_chunk_scan(const ssd_shape* shape, const void* x, const void* Bm, const void* Cm,
                           ssd_dtype in, const float* dt_bhl, const float* dA_cumsum,
-                          const float* carried, const float* D, void* y, ssd_dtype y_dtype,
-                          ssd_mma mma, void* stream);
+                          const void* carried, ssd_dtype carried_dtype, const float* D, void* y,
+                          ssd_dtype y_dtype, ssd_mma mma, void* stream);
 
 /*
- * Bytes of device workspace ssd_forward needs for `shape` (dA_cumsum, dt_bhl
- * and the chunk states, each 256-byte aligned).  Returns 0 for an invalid or
- * NULL shape.  Pure host computation.
+ * Bytes of device workspace ssd_forward needs for `shape`: dA_cumsum and
+ * dt_bhl (fp32 [B,H,nc,Q] each), the chunk states (fp32 [B,nc,H,N,P]) and a
+ * bf16 copy of the carried states ([B,nc,H,N,P]), each 256-byte aligned.
+ * Returns 0 for an invalid or NULL shape.  Pure host computation.
  */
 size_t ssd_workspace_bytes(const ssd_shape* shape);
 
 /*
  * One-call forward: ssd_chunk_cumsum -> ssd_chunk_state -> ssd_state_passing
- * (in place) -> ssd_chunk_scan on one stream, no host synchronisation.
+ * -> ssd_chunk_scan on one stream, no host synchronisation.  With
+ * SSD_MMA_BF16 the carried states go from the state passing to the chunk scan
+ * as bf16 (the matrix-operand values the chunk scan uses either way); with
+ * SSD_MMA_F32 the state passing runs in place on the fp32 chunk states.
+ * Results are bit-identical to the four calls made separately with those
+ * carried dtypes.
  * initial_states [B,H,N,P] may be NULL (zeros); final_states [B,H,N,P] may be
  * NULL (not written).  workspace: device memory of at least
  * ssd_workspace_bytes(shape) bytes, owned by the caller, contents undefined

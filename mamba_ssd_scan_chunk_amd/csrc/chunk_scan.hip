@@ -50,9 +50,9 @@ struct ScanCfg {
 template <class Op, int NK, int CT>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, const void* __restrict__ Cm, int in_bf16,
-    const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const float* __restrict__ carried,
-    const float* __restrict__ D, void* __restrict__ y, int y_bf16, int L, int H, int P, int N, int G, int Q,
-    int nc) {
+    const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const void* __restrict__ carried,
+    int h_bf16, const float* __restrict__ D, void* __restrict__ y, int y_bf16, int L, int H, int P, int N, int G,
+    int Q, int nc) {
   using E = typename OpElem<Op>::type;
   using Frag = typename Op::Frag;
   constexpr int PT = CT * 16;
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 
   // H_in -> Ht[p][n] (zero for padded n >= N), by 8x8 register transposes.
   {
-    const float* hs = carried + (((int64_t)b * nc + c) * H + h) * (int64_t)N * P + p0;
+    const int64_t hoff = (((int64_t)b * nc + c) * H + h) * (int64_t)N * P + p0;
     const int nbn = NK * 4;  // 8-row blocks along n (padded)
     for (int blk = tid; blk < nbn * (PT / 8); blk += kScanThreads) {
       const int bn = blk % nbn, bp = blk / nbn;
@@ -100,10 +100,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
       for (int r = 0; r < 8; ++r) {
         const int n = 8 * bn + r;
         if (n < N) {
-          const float4* src = reinterpret_cast<const float4*>(hs + (int64_t)n * P + 8 * bp);
-          const float4 a = src[0], b4 = src[1];
-          v[r][0] = a.x; v[r][1] = a.y; v[r][2] = a.z; v[r][3] = a.w;
-          v[r][4] = b4.x; v[r][5] = b4.y; v[r][6] = b4.z; v[r][7] = b4.w;
+          // fp32 or bf16 carried states (bf16 widens exactly)
+          load8_as_f32(carried, hoff + (int64_t)n * P + 8 * bp, h_bf16 != 0, v[r]);
         } else {
 #pragma unroll
           for (int q = 0; q < 8; ++q) v[r][q] = 0.f;
@@ -255,8 +253,8 @@ size_t chunk_scan_lds_bytes(const Dims& d, bool f32_mma) {
 
 template <class Op, int NK, int CT>
 static hipError_t launch_scan_inst(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
-                                   const float* dt_bhl, const float* dA_cumsum, const float* carried,
-                                   const float* D, void* y, bool y_bf16, hipStream_t stream, size_t lds) {
+                                   const float* dt_bhl, const float* dA_cumsum, const void* carried,
+                                   bool h_bf16, const float* D, void* y, bool y_bf16, hipStream_t stream, size_t lds) {
   auto kern = chunk_scan_kernel<Op, NK, CT>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -265,43 +263,43 @@ static hipError_t launch_scan_inst(const Dims& d, const void* x, const void* Bm,
   const int64_t nrg = d.Q > kScanRows ? d.Q / kScanRows : 1;
   const dim3 grid((unsigned)(d.H * (d.P / (16 * CT))), (unsigned)(nrg * d.nc), (unsigned)d.B);
   hipLaunchKernelGGL(kern, grid, dim3(kScanThreads), lds, stream, x, Bm, Cm, (int)in_bf16, dt_bhl, dA_cumsum,
-                     carried, D, y, (int)y_bf16, (int)d.L, (int)d.H, (int)d.P, (int)d.N, (int)d.G, (int)d.Q,
+                     carried, (int)h_bf16, D, y, (int)y_bf16, (int)d.L, (int)d.H, (int)d.P, (int)d.N, (int)d.G, (int)d.Q,
                      (int)d.nc);
   return hipGetLastError();
 }
 
 template <class Op, int NK>
 static hipError_t launch_scan_ct(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
-                                 const float* dt_bhl, const float* dA_cumsum, const float* carried,
-                                 const float* D, void* y, bool y_bf16, hipStream_t stream, size_t lds) {
+                                 const float* dt_bhl, const float* dA_cumsum, const void* carried,
+                                 bool h_bf16, const float* D, void* y, bool y_bf16, hipStream_t stream, size_t lds) {
   switch (scan_ct(d.P)) {
-    case 4: return launch_scan_inst<Op, NK, 4>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, lds);
-    case 2: return launch_scan_inst<Op, NK, 2>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, lds);
-    default: return launch_scan_inst<Op, NK, 1>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, lds);
+    case 4: return launch_scan_inst<Op, NK, 4>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
+    case 2: return launch_scan_inst<Op, NK, 2>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
+    default: return launch_scan_inst<Op, NK, 1>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
   }
 }
 
 template <class Op>
 static hipError_t launch_scan_op(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
-                                 const float* dt_bhl, const float* dA_cumsum, const float* carried,
-                                 const float* D, void* y, bool y_bf16, hipStream_t stream, size_t lds) {
+                                 const float* dt_bhl, const float* dA_cumsum, const void* carried,
+                                 bool h_bf16, const float* D, void* y, bool y_bf16, hipStream_t stream, size_t lds) {
   switch (scan_nk(d.N)) {
-    case 1: return launch_scan_ct<Op, 1>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, lds);
-    case 2: return launch_scan_ct<Op, 2>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, lds);
-    case 4: return launch_scan_ct<Op, 4>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, lds);
-    default: return launch_scan_ct<Op, 8>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, lds);
+    case 1: return launch_scan_ct<Op, 1>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
+    case 2: return launch_scan_ct<Op, 2>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
+    case 4: return launch_scan_ct<Op, 4>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
+    default: return launch_scan_ct<Op, 8>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
   }
 }
 
 hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
-                             const float* dt_bhl, const float* dA_cumsum, const float* carried,
+                             const float* dt_bhl, const float* dA_cumsum, const void* carried, bool h_bf16,
                              const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream) {
   if (chunk_scan_hg_supported(d, in_bf16, f32_mma))
-    return launch_chunk_scan_hg(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream);
+    return launch_chunk_scan_hg(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream);
   const size_t lds = chunk_scan_lds_bytes(d, f32_mma);
   if (f32_mma)
-    return launch_scan_op<OpF32>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, lds);
-  return launch_scan_op<OpBF16>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, lds);
+    return launch_scan_op<OpF32>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
+  return launch_scan_op<OpBF16>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
 }
 
 }  // namespace ssd

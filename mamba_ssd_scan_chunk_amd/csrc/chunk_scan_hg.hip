@@ -82,7 +82,7 @@ struct HgArgs {
   const void* Cm;
   const float* dt_bhl;
   const float* dA_cumsum;
-  const float* carried;
+  const void* carried;  // fp32, or bf16 bits when H_BF16
   const float* D;
   void* y;
   int L, H, P, G, nc, HG;
@@ -99,16 +99,17 @@ __device__ __forceinline__ int npos(int n) {
   return (n & ~31) | ((n & 12) << 1) | ((n & 16) >> 2) | (n & 3);
 }
 
-template <int Q, int NK, int CT, bool IN_BF16, bool Y_BF16>
+template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16>
 __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, const int tid) {
   using Cfg = HgCfg<Q, NK, CT>;
   using Op = OpBF16;
   using Frag = Op::Frag;
   constexpr int QT = Cfg::QT, PT = Cfg::PT, N = Cfg::N, NPI = Cfg::NPI, XNP = Cfg::XNP, T = Cfg::T;
-  static_assert(IN_BF16, "the head-group chunk scan takes bf16 inputs");
   static_assert(PT == 64, "the prefetch maps assume a 64-column slice");
   constexpr int NXB = Q * (PT / 8);          // x prefetch pieces (16 bytes: 8 columns of one token)
-  constexpr int NHB = N * (PT / 4);          // H prefetch pieces (16 bytes: 4 columns of one n)
+  // H prefetch pieces (16 bytes: 4 fp32 or 8 bf16 columns of one n)
+  constexpr int HCOL = H_BF16 ? 8 : 4;
+  constexpr int NHB = N * (PT / HCOL);
   constexpr int XPT = NXB / T;               // pieces per thread
   constexpr int HPT = NHB / T;
   static_assert(NXB % T == 0 && NHB % T == 0, "prefetch pieces must divide evenly over the block");
@@ -173,7 +174,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // ---- per-head register prefetch: issued before a head's compute,
   // committed to LDS after it.
   uint4 xv[XPT];   // 16-byte pieces of x rows (8 columns, bf16)
-  float4 hv[HPT];  // 16-byte pieces of H_in rows (4 columns, fp32)
+  uint4 hv[HPT];   // 16-byte pieces of H_in rows (4 fp32 or 8 bf16 columns)
   float pg = 0.f, pd = 0.f;
   // x piece blk -> (row, 8-column block cb): 8 consecutive threads take the 8
   // pieces of one row; within a wave the 8 rows are ordered 0,4,1,5,2,6,3,7 so
@@ -213,13 +214,18 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // ... and H_in pieces (issued after the C.H_in product, spreading the
   // vector-memory issue over the head)
   auto issue_h = [&](int h) __attribute__((always_inline)) {
-    // H_in piece blk -> (n = blk / 16, columns 4 (blk % 16) .. +3): 16
-    // consecutive threads read one 256-byte row
-    const float* hs = a.carried + (((int64_t)a.b * nc + a.c) * H + h) * (int64_t)(N * P) + a.p0;
+    // H_in piece blk -> (n = blk / (PT / HCOL), columns HCOL * (blk % (PT / HCOL)) ..):
+    // consecutive threads read one row
+    const int64_t hoff = (((int64_t)a.b * nc + a.c) * H + h) * (int64_t)(N * P) + a.p0;
 #pragma unroll
     for (int uu = 0; uu < HPT; ++uu) {
       const int blk = tid + uu * T;
-      if (blk < NHB) hv[uu] = *reinterpret_cast<const float4*>(hs + (blk >> 4) * P + 4 * (blk & 15));
+      const int n = blk / (PT / HCOL), col = HCOL * (blk % (PT / HCOL));
+      if constexpr (H_BF16) {
+        if (blk < NHB) hv[uu] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.carried) + hoff + n * P + col);
+      } else {
+        if (blk < NHB) hv[uu] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.carried) + hoff + n * P + col);
+      }
     }
   };
   auto commit = [&]() __attribute__((always_inline)) {
@@ -236,8 +242,15 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     for (int uu = 0; uu < HPT; ++uu) {
       const int blk = tid + uu * T;
       if (blk >= NHB) continue;
-      *reinterpret_cast<uint2*>(Hn + (blk >> 4) * XNP + 4 * (blk & 15)) =
-          make_uint2(pack_bf16x2(hv[uu].x, hv[uu].y), pack_bf16x2(hv[uu].z, hv[uu].w));
+      const int n = blk / (PT / HCOL), col = HCOL * (blk % (PT / HCOL));
+      const uint4 q = hv[uu];
+      if constexpr (H_BF16) {
+        *reinterpret_cast<uint4*>(Hn + n * XNP + col) = make_uint4(q.x, q.y, q.z, q.w);
+      } else {
+        *reinterpret_cast<uint2*>(Hn + n * XNP + col) =
+            make_uint2(pack_bf16x2(__uint_as_float(q.x), __uint_as_float(q.y)),
+                       pack_bf16x2(__uint_as_float(q.z), __uint_as_float(q.w)));
+      }
     }
     Gs[tid & (Q - 1)] = pg;  // threads tid and tid + Q write the same value
     dts[tid & (Q - 1)] = pd;
@@ -433,10 +446,10 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 // Y_BF16 is a template parameter rather than a run-time flag: a branch around
 // the output stores would make the compiler's memory-counter waits for the
 // prefetched loads conservative (they would also wait for the stores).
-template <int Q, int NK, int CT, bool IN_BF16, bool Y_BF16>
+template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16>
 __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, const void* __restrict__ Cm,
-    const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const float* __restrict__ carried,
+    const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const void* __restrict__ carried,
     const float* __restrict__ D, void* __restrict__ y, int L, int H, int P, int G, int nc, int HG,
     int nhg, int npt, int remap) {
   extern __shared__ __align__(16) unsigned char hg_smem[];
@@ -460,7 +473,7 @@ __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
   a.hbase = a.g * (H / G) + hgi * HG;
   a.p0 = pt * HgCfg<Q, NK, CT>::PT;
   a.tok0 = (int64_t)a.b * L + (int64_t)a.c * Q;
-  hg_body<Q, NK, CT, IN_BF16, Y_BF16>(a, hg_smem, threadIdx.x);
+  hg_body<Q, NK, CT, H_BF16, Y_BF16>(a, hg_smem, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ host side
@@ -492,13 +505,13 @@ static int pick_heads_per_block(const Dims& d, int npt) {
   return best;
 }
 
-template <int Q, int NK, bool IN_BF16>
+template <int Q, int NK, bool H_BF16>
 static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, const void* Cm, const float* dt_bhl,
-                                 const float* dA_cumsum, const float* carried, const float* D, void* y,
+                                 const float* dA_cumsum, const void* carried, const float* D, void* y,
                                  bool y_bf16, hipStream_t stream) {
   constexpr int CT = 4;
   using Cfg = HgCfg<Q, NK, CT>;
-  auto kern = y_bf16 ? chunk_scan_hg_kernel<Q, NK, CT, IN_BF16, true> : chunk_scan_hg_kernel<Q, NK, CT, IN_BF16, false>;
+  auto kern = y_bf16 ? chunk_scan_hg_kernel<Q, NK, CT, H_BF16, true> : chunk_scan_hg_kernel<Q, NK, CT, H_BF16, false>;
   const size_t lds = Cfg::lds_total;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -534,14 +547,14 @@ bool chunk_scan_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
   }
 }
 
-template <bool IN_BF16>
+template <bool H_BF16>
 static hipError_t launch_hg_dtype(const Dims& d, const void* x, const void* Bm, const void* Cm, const float* dt_bhl,
-                                  const float* dA_cumsum, const float* carried, const float* D, void* y, bool y_bf16,
+                                  const float* dA_cumsum, const void* carried, const float* D, void* y, bool y_bf16,
                                   hipStream_t stream) {
   const int64_t key = d.Q * 1000 + d.N;
 #define HG_CASE(QQ, NN, KK) \
   case QQ * 1000 + NN:      \
-    return launch_hg_inst<QQ, KK, IN_BF16>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream);
+    return launch_hg_inst<QQ, KK, H_BF16>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream);
   switch (key) {
     HG_CASE(128, 128, 4)
     HG_CASE(128, 256, 8)
@@ -552,10 +565,11 @@ static hipError_t launch_hg_dtype(const Dims& d, const void* x, const void* Bm, 
 }
 
 hipError_t launch_chunk_scan_hg(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
-                                const float* dt_bhl, const float* dA_cumsum, const float* carried, const float* D,
-                                void* y, bool y_bf16, hipStream_t stream) {
+                                const float* dt_bhl, const float* dA_cumsum, const void* carried, bool carried_bf16,
+                                const float* D, void* y, bool y_bf16, hipStream_t stream) {
   if (!in_bf16) return hipErrorInvalidValue;
-  return launch_hg_dtype<true>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream);
+  if (carried_bf16) return launch_hg_dtype<true>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream);
+  return launch_hg_dtype<false>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream);
 }
 
 }  // namespace ssd

@@ -67,10 +67,14 @@ ssd_status validate_state(const ssd_shape* shape, const void* x, const void* Bm,
   return SSD_OK;
 }
 
-ssd_status validate_passing(const ssd_shape* shape, const float* chunk_states, float* carried,
-                            const float* dA_cumsum, const float* initial_states, float* final_states, Dims* d) {
+ssd_status validate_passing(const ssd_shape* shape, const float* chunk_states, void* carried,
+                            ssd_dtype carried_dtype, const float* dA_cumsum, const float* initial_states,
+                            float* final_states, Dims* d) {
   SSD_TRY(check_shape(shape, d));
+  SSD_TRY(check_dtype(carried_dtype));
   if (!chunk_states || !carried || !dA_cumsum) return SSD_ERR_NULL;
+  // bf16 carried states are narrower than the chunk states: no in-place form
+  if (carried_dtype == SSD_BF16 && carried == static_cast<const void*>(chunk_states)) return SSD_ERR_UNSUPPORTED;
   if (!aligned16(chunk_states) || !aligned16(carried) || !aligned16(dA_cumsum) ||
       (initial_states && !aligned16(initial_states)) || (final_states && !aligned16(final_states)))
     return SSD_ERR_ALIGN;
@@ -78,10 +82,11 @@ ssd_status validate_passing(const ssd_shape* shape, const float* chunk_states, f
 }
 
 ssd_status validate_scan(const ssd_shape* shape, const void* x, const void* Bm, const void* Cm, ssd_dtype in,
-                         const float* dt_bhl, const float* dA_cumsum, const float* carried, const float* D,
-                         void* y, ssd_dtype y_dtype, ssd_mma mma, Dims* d) {
+                         const float* dt_bhl, const float* dA_cumsum, const void* carried, ssd_dtype carried_dtype,
+                         const float* D, void* y, ssd_dtype y_dtype, ssd_mma mma, Dims* d) {
   SSD_TRY(check_shape(shape, d));
   SSD_TRY(check_dtype(in));
+  SSD_TRY(check_dtype(carried_dtype));
   SSD_TRY(check_dtype(y_dtype));
   SSD_TRY(check_mma(mma));
   if (!x || !Bm || !Cm || !dt_bhl || !dA_cumsum || !carried || !D || !y) return SSD_ERR_NULL;
@@ -93,7 +98,7 @@ ssd_status validate_scan(const ssd_shape* shape, const void* x, const void* Bm, 
 }
 
 struct WsLayout {
-  size_t dA_off, dt_off, st_off, total;
+  size_t dA_off, dt_off, st_off, hb_off, total;
 };
 
 WsLayout workspace_layout(const Dims& d) {
@@ -103,7 +108,8 @@ WsLayout workspace_layout(const Dims& d) {
   w.dA_off = 0;
   w.dt_off = round_up(w.dA_off + bhl, kWsAlign);
   w.st_off = round_up(w.dt_off + bhl, kWsAlign);
-  w.total = round_up(w.st_off + st, kWsAlign);
+  w.hb_off = round_up(w.st_off + st, kWsAlign);  // bf16 carried states (half the bytes of st)
+  w.total = round_up(w.hb_off + st / 2, kWsAlign);
   return w;
 }
 
@@ -127,21 +133,26 @@ ssd_status ssd_chunk_state(const ssd_shape* shape, const void* x, const void* Bm
                                           mma == SSD_MMA_F32, (hipStream_t)stream));
 }
 
-ssd_status ssd_state_passing(const ssd_shape* shape, const float* chunk_states, float* carried,
-                             const float* dA_cumsum, const float* initial_states, float* final_states,
-                             void* stream) {
+ssd_status ssd_state_passing(const ssd_shape* shape, const float* chunk_states, void* carried,
+                             ssd_dtype carried_dtype, const float* dA_cumsum, const float* initial_states,
+                             float* final_states, void* stream) {
   Dims d;
-  SSD_TRY(validate_passing(shape, chunk_states, carried, dA_cumsum, initial_states, final_states, &d));
-  return from_hip(ssd::launch_state_passing(d, chunk_states, carried, dA_cumsum, initial_states, final_states,
-                                            (hipStream_t)stream));
+  SSD_TRY(validate_passing(shape, chunk_states, carried, carried_dtype, dA_cumsum, initial_states, final_states,
+                           &d));
+  if (carried_dtype == SSD_BF16)
+    return from_hip(ssd::launch_state_passing_bf16(d, chunk_states, static_cast<uint16_t*>(carried), dA_cumsum,
+                                                   initial_states, final_states, (hipStream_t)stream));
+  return from_hip(ssd::launch_state_passing(d, chunk_states, static_cast<float*>(carried), dA_cumsum,
+                                            initial_states, final_states, (hipStream_t)stream));
 }
 
 ssd_status ssd_chunk_scan(const ssd_shape* shape, const void* x, const void* Bm, const void* Cm, ssd_dtype in,
-                          const float* dt_bhl, const float* dA_cumsum, const float* carried, const float* D,
-                          void* y, ssd_dtype y_dtype, ssd_mma mma, void* stream) {
+                          const float* dt_bhl, const float* dA_cumsum, const void* carried, ssd_dtype carried_dtype,
+                          const float* D, void* y, ssd_dtype y_dtype, ssd_mma mma, void* stream) {
   Dims d;
-  SSD_TRY(validate_scan(shape, x, Bm, Cm, in, dt_bhl, dA_cumsum, carried, D, y, y_dtype, mma, &d));
-  return from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, in == SSD_BF16, dt_bhl, dA_cumsum, carried, D, y,
+  SSD_TRY(validate_scan(shape, x, Bm, Cm, in, dt_bhl, dA_cumsum, carried, carried_dtype, D, y, y_dtype, mma, &d));
+  return from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, in == SSD_BF16, dt_bhl, dA_cumsum, carried,
+                                         carried_dtype == SSD_BF16, D, y,
                                          y_dtype == SSD_BF16, mma == SSD_MMA_F32, (hipStream_t)stream));
 }
 
@@ -181,8 +192,18 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, c
 
   SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
   SSD_TRY(from_hip(ssd::launch_chunk_state(d, x, Bm, bf, dtb, dA, st, f32m, s)));
-  SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dA, initial_states, final_states, s)));
-  SSD_TRY(from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, D, y, y_dtype == SSD_BF16, f32m, s)));
+  if (!f32m) {
+    // bf16 matrix operands: hand the chunk scan the carried states already
+    // rounded to bf16 (the operand values it would round them to)
+    uint16_t* hb = reinterpret_cast<uint16_t*>(base + ws.hb_off);
+    SSD_TRY(from_hip(ssd::launch_state_passing_bf16(d, st, hb, dA, initial_states, final_states, s)));
+    SSD_TRY(from_hip(
+        ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, hb, true, D, y, y_dtype == SSD_BF16, f32m, s)));
+  } else {
+    SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dA, initial_states, final_states, s)));
+    SSD_TRY(from_hip(
+        ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, false, D, y, y_dtype == SSD_BF16, f32m, s)));
+  }
   return SSD_OK;
 }
 

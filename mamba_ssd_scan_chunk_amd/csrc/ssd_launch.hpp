@@ -35,17 +35,24 @@ hipError_t launch_chunk_state_hg(const Dims& d, const void* x, const void* Bm, c
 hipError_t launch_state_passing(const Dims& d, const float* chunk_states, float* carried,
                                 const float* dA_cumsum, const float* initial_states,
                                 float* final_states, hipStream_t stream);
+// Same recurrence; the carried states are written rounded to bf16 (RNE) into a
+// separate buffer (same [B,nc,H,N,P] layout); final states stay fp32.
+hipError_t launch_state_passing_bf16(const Dims& d, const float* chunk_states, uint16_t* carried_bf16,
+                                     const float* dA_cumsum, const float* initial_states,
+                                     float* final_states, hipStream_t stream);
 
 // Head-group variant of the fused chunk output (bf16 inputs and operands,
 // (chunk, N) in {(128,128), (128,256), (256,128)}, P a multiple of 64);
-// launch_chunk_scan picks it when supported.
+// launch_chunk_scan picks it when supported.  `carried` holds fp32 values, or
+// bf16 bits (already rounded to nearest even) when carried_bf16 is set.
 bool chunk_scan_hg_supported(const Dims& d, bool in_bf16, bool f32_mma);
 hipError_t launch_chunk_scan_hg(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
-                                const float* dt_bhl, const float* dA_cumsum, const float* carried, const float* D,
-                                void* y, bool y_bf16, hipStream_t stream);
+                                const float* dt_bhl, const float* dA_cumsum, const void* carried, bool carried_bf16,
+                                const float* D, void* y, bool y_bf16, hipStream_t stream);
 
+// `carried` holds fp32 values, or bf16 bits when carried_bf16 is set.
 hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
-                             const float* dt_bhl, const float* dA_cumsum, const float* carried,
+                             const float* dt_bhl, const float* dA_cumsum, const void* carried, bool carried_bf16,
                              const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream);
 
 }  // namespace ssd

@@ -17,6 +17,11 @@
 // thread in flight, and the next 8 loads are issued before the current 8
 // stores.  carried may alias S: each location is read before it is written,
 // by the same thread.
+//
+// A second instantiation writes the carried states rounded to bf16 (round to
+// nearest even, 8-byte stores) into a separate buffer: the bf16-operand chunk
+// scan rounds them to exactly these values anyway, so the one-call forward
+// uses it to halve the carried-state traffic without changing any result.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -25,8 +30,10 @@ namespace ssd {
 constexpr int kSpThreads = 256;
 constexpr int kSpUnroll = 8;
 
+// carried element type: float (may alias S) or bf16 bits (separate buffer)
+template <bool CBF16>
 __global__ __launch_bounds__(kSpThreads) void state_passing_kernel(
-    const float* S, float* carried, const float* __restrict__ dA_cumsum,
+    const float* S, void* carried_v, const float* __restrict__ dA_cumsum,
     const float* __restrict__ init, float* __restrict__ fin, int H, int nc, int Q, int64_t np4,
     int64_t total) {
   const int64_t id = (int64_t)blockIdx.x * kSpThreads + threadIdx.x;
@@ -41,7 +48,13 @@ __global__ __launch_bounds__(kSpThreads) void state_passing_kernel(
   const float* glast = dA_cumsum + bh * nc * Q + (Q - 1);  // chunk c at glast[c*Q]
   const int64_t cstride = (int64_t)H * np4;                // float4s between chunks
   const float4* sp = reinterpret_cast<const float4*>(S) + (b * nc * H + h) * np4 + e4;
-  float4* cp = reinterpret_cast<float4*>(carried) + (b * nc * H + h) * np4 + e4;
+  const int64_t coff = (b * nc * H + h) * np4 + e4;  // in units of 4 elements
+  auto put = [&](int64_t c, const float4& v) {
+    if constexpr (CBF16)
+      reinterpret_cast<uint2*>(carried_v)[coff + c * cstride] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    else
+      reinterpret_cast<float4*>(carried_v)[coff + c * cstride] = v;
+  };
 
   // Software pipeline: the loads of chunks c+8..c+15 are issued before the
   // stores of chunks c..c+7 (distinct addresses, so this also holds in place).
@@ -66,7 +79,7 @@ __global__ __launch_bounds__(kSpThreads) void state_passing_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kSpUnroll; ++u) {
-      cp[(int64_t)(c + u) * cstride] = run;
+      put(c + u, run);
       run.x = dec[u] * run.x + s[u].x;
       run.y = dec[u] * run.y + s[u].y;
       run.z = dec[u] * run.z + s[u].z;
@@ -81,7 +94,7 @@ __global__ __launch_bounds__(kSpThreads) void state_passing_kernel(
   for (int c = nfull * kSpUnroll; c < nc; ++c) {
     const float4 sv = sp[(int64_t)c * cstride];
     const float d1 = expf(glast[(int64_t)c * Q]);
-    cp[(int64_t)c * cstride] = run;
+    put(c, run);
     run.x = d1 * run.x + sv.x;
     run.y = d1 * run.y + sv.y;
     run.z = d1 * run.z + sv.z;
@@ -90,15 +103,27 @@ __global__ __launch_bounds__(kSpThreads) void state_passing_kernel(
   if (fin) reinterpret_cast<float4*>(fin)[bh * np4 + e4] = run;
 }
 
-hipError_t launch_state_passing(const Dims& d, const float* chunk_states, float* carried,
-                                const float* dA_cumsum, const float* initial_states,
-                                float* final_states, hipStream_t stream) {
+template <bool CBF16>
+static hipError_t launch_sp(const Dims& d, const float* chunk_states, void* carried, const float* dA_cumsum,
+                            const float* initial_states, float* final_states, hipStream_t stream) {
   const int64_t np4 = d.N * d.P / 4;
   const int64_t total = d.B * d.H * np4;
   const unsigned blocks = (unsigned)((total + kSpThreads - 1) / kSpThreads);
-  hipLaunchKernelGGL(state_passing_kernel, dim3(blocks), dim3(kSpThreads), 0, stream, chunk_states, carried,
+  hipLaunchKernelGGL(state_passing_kernel<CBF16>, dim3(blocks), dim3(kSpThreads), 0, stream, chunk_states, carried,
                      dA_cumsum, initial_states, final_states, (int)d.H, (int)d.nc, (int)d.Q, np4, total);
   return hipGetLastError();
+}
+
+hipError_t launch_state_passing(const Dims& d, const float* chunk_states, float* carried,
+                                const float* dA_cumsum, const float* initial_states,
+                                float* final_states, hipStream_t stream) {
+  return launch_sp<false>(d, chunk_states, carried, dA_cumsum, initial_states, final_states, stream);
+}
+
+hipError_t launch_state_passing_bf16(const Dims& d, const float* chunk_states, uint16_t* carried_bf16,
+                                     const float* dA_cumsum, const float* initial_states,
+                                     float* final_states, hipStream_t stream) {
+  return launch_sp<true>(d, chunk_states, carried_bf16, dA_cumsum, initial_states, final_states, stream);
 }
 
 }  // namespace ssd

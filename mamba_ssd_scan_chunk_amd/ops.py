@@ -95,10 +95,11 @@ def ssd_chunk_state(shape, x, Bm, dt_bhl, dA_cumsum, states=None, mma="bf16", st
 
 
 def ssd_state_passing(shape, chunk_states, dA_cumsum, initial_states=None, carried=None, final_states=None,
-                      in_place=False, stream=None):
-    """Carried states [B,nc,H,N,P] (state entering each chunk) and final
-    states [B,H,N,P].  ``in_place=True`` writes the carried states over
-    ``chunk_states``."""
+                      in_place=False, carried_dtype="f32", stream=None):
+    """Carried states [B,nc,H,N,P] (state entering each chunk) in
+    ``carried_dtype`` ("f32" or "bf16", rounded to nearest even; a given
+    ``carried`` tensor's dtype wins) and fp32 final states [B,H,N,P].
+    ``in_place=True`` writes fp32 carried states over ``chunk_states``."""
     sh = _shape(shape)
     B, L, H, P, N, G, Q, nc = _dims(sh)
     f32 = (torch.float32,)
@@ -107,14 +108,18 @@ def ssd_state_passing(shape, chunk_states, dA_cumsum, initial_states=None, carri
     if initial_states is not None:
         _req(initial_states, "initial_states", (B, H, N, P), f32)
     if carried is None:
-        carried = chunk_states if in_place else torch.empty_like(chunk_states)
-    _req(carried, "carried", (B, nc, H, N, P), f32)
+        cdt = _DTNAME[carried_dtype] if isinstance(carried_dtype, str) else carried_dtype
+        if in_place:
+            carried = chunk_states
+        else:
+            carried = torch.empty((B, nc, H, N, P), device=chunk_states.device, dtype=cdt)
+    _req(carried, "carried", (B, nc, H, N, P), (torch.float32, torch.bfloat16))
     if final_states is None:
         final_states = torch.empty((B, H, N, P), device=chunk_states.device, dtype=torch.float32)
     _req(final_states, "final_states", (B, H, N, P), f32)
     lib = load_library()
-    check(lib.ssd_state_passing(sh, _ptr(chunk_states), _ptr(carried), _ptr(dA_cumsum), _ptr(initial_states),
-                                _ptr(final_states), _stream(stream)))
+    check(lib.ssd_state_passing(sh, _ptr(chunk_states), _ptr(carried), _DT[carried.dtype], _ptr(dA_cumsum),
+                                _ptr(initial_states), _ptr(final_states), _stream(stream)))
     return carried, final_states
 
 
@@ -130,7 +135,7 @@ def ssd_chunk_scan(shape, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y=None, y_dt
     _req(Cm, "Cm", (B, L, G, N), (x.dtype,))
     _req(dt_bhl, "dt_bhl", (B, H, nc, Q), f32)
     _req(dA_cumsum, "dA_cumsum", (B, H, nc, Q), f32)
-    _req(carried, "carried", (B, nc, H, N, P), f32)
+    _req(carried, "carried", (B, nc, H, N, P), (torch.float32, torch.bfloat16))
     _req(D, "D", (H,), f32)
     ydt = x.dtype if y_dtype is None else (_DTNAME[y_dtype] if isinstance(y_dtype, str) else y_dtype)
     if y is None:
@@ -138,7 +143,8 @@ def ssd_chunk_scan(shape, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y=None, y_dt
     _req(y, "y", (B, L, H, P), io)
     lib = load_library()
     check(lib.ssd_chunk_scan(sh, _ptr(x), _ptr(Bm), _ptr(Cm), _DT[x.dtype], _ptr(dt_bhl), _ptr(dA_cumsum),
-                             _ptr(carried), _ptr(D), _ptr(y), _DT[y.dtype], _mma(mma), _stream(stream)))
+                             _ptr(carried), _DT[carried.dtype], _ptr(D), _ptr(y), _DT[y.dtype], _mma(mma),
+                             _stream(stream)))
     return y
 
 

@@ -38,7 +38,7 @@ def test_header_declares_the_abi():
 def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
-    assert lib.ssd_abi_version() == 1
+    assert lib.ssd_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -64,8 +64,8 @@ def test_shape_checks(lib, kw, code):
     s = shape(**kw)
     assert lib.ssd_chunk_cumsum(s, FAKE, FAKE, FAKE, FAKE, None) == code
     assert lib.ssd_chunk_state(s, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, None) == code
-    assert lib.ssd_state_passing(s, FAKE, FAKE, FAKE, None, FAKE, None) == code
-    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, None) == code
+    assert lib.ssd_state_passing(s, FAKE, FAKE, 0, FAKE, None, FAKE, None) == code
+    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1, 0, None) == code
     assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, 1, FAKE, FAKE, 1 << 40, 0,
                            None) == code
     assert lib.ssd_workspace_bytes(s) == 0
@@ -89,12 +89,14 @@ def test_null_pointers(lib):
     for i in range(3):
         args = [FAKE] * 3
         args[i] = None
-        assert lib.ssd_state_passing(s, args[0], args[1], args[2], None, FAKE, None) == NULL
+        assert lib.ssd_state_passing(s, args[0], args[1], 0, args[2], None, FAKE, None) == NULL
+        assert lib.ssd_state_passing(s, args[0], args[1], 1, args[2], None, FAKE, None) == NULL
     for i in range(8):
         args = [FAKE] * 8
         args[i] = None
         x, Bm, Cm, dtb, dA, car, D, y = args
-        assert lib.ssd_chunk_scan(s, x, Bm, Cm, 1, dtb, dA, car, D, y, 1, 0, None) == NULL
+        assert lib.ssd_chunk_scan(s, x, Bm, Cm, 1, dtb, dA, car, 0, D, y, 1, 0, None) == NULL
+        assert lib.ssd_chunk_scan(s, x, Bm, Cm, 1, dtb, dA, car, 1, D, y, 1, 0, None) == NULL
     for i in range(7):
         args = [FAKE] * 7
         args[i] = None
@@ -106,8 +108,10 @@ def test_dtype_and_mma_enums(lib):
     s = shape()
     assert lib.ssd_chunk_state(s, FAKE, FAKE, 2, FAKE, FAKE, FAKE, 0, None) == DTYPE
     assert lib.ssd_chunk_state(s, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 2, None) == DTYPE
-    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 7, 0, None) == DTYPE
-    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1, -1, None) == DTYPE
+    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 7, 0, None) == DTYPE
+    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1, -1, None) == DTYPE
+    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 3, FAKE, FAKE, 1, 0, None) == DTYPE
+    assert lib.ssd_state_passing(s, FAKE, FAKE, 2, FAKE, None, FAKE, None) == DTYPE
     assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, None, FAKE, 1, FAKE, FAKE, 1 << 40, 0,
                            None) == DTYPE
 
@@ -118,10 +122,21 @@ def test_alignment(lib):
     assert lib.ssd_chunk_cumsum(s, odd, FAKE, FAKE, FAKE, None) == ALIGN
     assert lib.ssd_chunk_cumsum(s, FAKE, FAKE, FAKE, odd, None) == ALIGN
     assert lib.ssd_chunk_state(s, FAKE, odd, 1, FAKE, FAKE, FAKE, 0, None) == ALIGN
-    assert lib.ssd_state_passing(s, FAKE, FAKE, FAKE, odd, FAKE, None) == ALIGN
-    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, odd, 1, 0, None) == ALIGN
+    assert lib.ssd_state_passing(s, FAKE, FAKE, 0, FAKE, odd, FAKE, None) == ALIGN
+    assert lib.ssd_state_passing(s, FAKE, odd, 1, FAKE, None, FAKE, None) == ALIGN
+    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, FAKE, odd, 1, 0, None) == ALIGN
+    assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, odd, 1, FAKE, FAKE, 1, 0, None) == ALIGN
     assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, odd, FAKE, 1, FAKE, FAKE, 1 << 40, 0,
                            None) == ALIGN
+
+
+def test_bf16_carried_has_no_in_place_form(lib):
+    """bf16 carried states are narrower than the fp32 chunk states: writing
+    them over the chunk states would race, so that call is refused before any
+    HIP call; the fp32 in-place form stays valid (checked up to the launch on
+    the GPU side)."""
+    s = shape()
+    assert lib.ssd_state_passing(s, FAKE, FAKE, 1, FAKE, None, FAKE, None) == UNSUP
 
 
 def test_workspace(lib):
@@ -131,7 +146,7 @@ def test_workspace(lib):
     bhl = 4 * B * H * nc * Q
     st = 4 * B * nc * H * N * P
     ru = lambda v: (v + 255) // 256 * 256
-    expect = ru(ru(ru(bhl) + bhl) + st)
+    expect = ru(ru(ru(ru(bhl) + bhl) + st) + st // 2)  # dA, dt_bhl, chunk states, bf16 carried states
     assert lib.ssd_workspace_bytes(s) == expect
     assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, 1, FAKE, None, 1 << 40, 0,
                            None) == WS

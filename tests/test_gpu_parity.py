@@ -112,6 +112,36 @@ def test_state_passing(shape, in_place, with_h0):
     assert e1 <= TOL_PASSING and e2 <= TOL_PASSING
 
 
+@pytest.mark.parametrize("with_h0", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_state_passing_bf16_carried(shape, with_h0):
+    """bf16 carried states are the fp32 recurrence rounded to nearest even:
+    bit-equal to rounding the fp32 variant's carried states, and within the
+    bf16 rounding bound of the oracle; the final states stay fp32."""
+    from mamba_ssd_scan_chunk_amd.inputs import bf16_round
+    say(f"state_passing bf16 carried {shape} h0={with_h0}")
+    inp = _inp(shape, "f32", seed=2, dt_shift=3.0)
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    o = oracle()
+    S = o.chunk_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk)
+    h0 = _h0(inp) if with_h0 else None
+    Hin, fin = o.carried_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk, h0=h0)
+    dA, _ = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    S_t = torch.from_numpy(S.astype(np.float32)).cuda()
+    h0_t = None if h0 is None else torch.from_numpy(h0).cuda()
+    c32, f32_ = ops.ssd_state_passing(sh, S_t, dA, initial_states=h0_t)
+    c16, f16_ = ops.ssd_state_passing(sh, S_t, dA, initial_states=h0_t, carried_dtype="bf16")
+    torch.cuda.synchronize()
+    assert c16.dtype == torch.bfloat16
+    got = c16.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, bf16_round(c32.cpu().numpy()))
+    assert torch.equal(f16_, f32_)
+    e1, e2 = relerr(c16.float(), Hin), relerr(f16_, fin)
+    say(f"  rel err carried(bf16) {e1:.3g} final {e2:.3g}")
+    assert e1 <= 2.0 ** -8 and e2 <= TOL_PASSING
+
+
 @pytest.mark.parametrize("y_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", MODES, ids=["-".join(m) for m in MODES])
 @pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
@@ -134,6 +164,16 @@ def test_chunk_scan(shape, mode, y_dtype):
     e = relerr(y, yref)
     say(f"  rel err {e:.3g}")
     assert e <= tol_for(mma)
+    # bf16 carried states: on the bf16 path they are the matrix operands the
+    # kernel rounds fp32 carried states to, so y is bit-identical; on the fp32
+    # path they widen exactly and stay within the bf16 bar
+    y16 = ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, car.to(torch.bfloat16), t["D"],
+                             y_dtype=y_dtype, mma=mma)
+    torch.cuda.synchronize()
+    if mma == "bf16":
+        assert torch.equal(y16, y)
+    else:
+        assert relerr(y16, yref) <= tol_for("bf16")
 
 
 @pytest.mark.parametrize("mma", ["f32", "bf16"])
@@ -221,6 +261,40 @@ def test_split_chaining(mma):
     y_cat = torch.cat([y1, y2], dim=1)
     assert relerr(y_cat, yref) <= tol_for(mma) and relerr(f2, fref) <= tol_for(mma)
     assert relerr(y_cat, y_full.double().cpu().numpy()) <= tol_for(mma)
+
+
+# (name, B, L, H, P, N, G, Q): shapes of the bf16 head-group kernels, where the
+# one-call forward hands the carried states to the chunk scan as bf16
+HG_SHAPES = [
+    ("q256_n128", 2, 768, 6, 64, 128, 2, 256),
+    ("q128_n256", 1, 512, 4, 128, 256, 2, 128),
+    ("q128_n128", 2, 384, 3, 64, 128, 1, 128),
+    ("generic_q64", 1, 256, 6, 32, 64, 2, 64),  # the generic chunk-scan kernel
+]
+
+
+@pytest.mark.parametrize("y_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", HG_SHAPES, ids=[s[0] for s in HG_SHAPES])
+def test_forward_bitwise_equals_split_calls(shape, y_dtype):
+    """On the bf16 path the one-call forward passes the carried states to the
+    chunk scan rounded to bf16, exactly the operand values the chunk scan
+    rounds fp32 carried states to: y and the final states must equal the four
+    split calls bit for bit."""
+    say(f"forward vs split calls {shape} y {y_dtype}")
+    inp = _inp(shape, "bf16", seed=12, dt_shift=2.0)
+    h0 = torch.from_numpy(_h0(inp)).cuda()
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    y_f, fin_f = ops.ssd_forward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], initial_states=h0,
+                                 y_dtype=y_dtype, mma="bf16")
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    S = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma="bf16")
+    for cdt in ["f32", "bf16"]:
+        car, fin_s = ops.ssd_state_passing(sh, S, dA, initial_states=h0, carried_dtype=cdt)
+        y_s = ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, car, t["D"], y_dtype=y_dtype, mma="bf16")
+        torch.cuda.synchronize()
+        assert torch.equal(y_f, y_s), cdt
+        assert torch.equal(fin_f, fin_s), cdt
 
 
 @pytest.mark.parametrize("mma", ["f32", "bf16"])
