@@ -252,13 +252,15 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
                        pack_bf16x2(__uint_as_float(q.z), __uint_as_float(q.w)));
       }
     }
-    Gs[tid & (Q - 1)] = pg;  // threads tid and tid + Q write the same value
+    // G is kept in base-2 units (G log2 e) on chip: every use is an exponential
+    const float pg2 = pg * kLog2e;
+    Gs[tid & (Q - 1)] = pg2;  // threads tid and tid + Q write the same value
     dts[tid & (Q - 1)] = pd;
     // Column factors of the off-diagonal sub-tiles: for the reference row
     // R = 32u, Ws[u][j] = exp(G_R - G_j) dt_j, read only for j < R (so
     // G_R <= G_j and the factor is <= 1); entries with j >= R are unused.
 #pragma unroll
-    for (int m = 0; m < NWM; ++m) Ws[tid + T * m] = fast_exp(gref[m] - pg) * pd;
+    for (int m = 0; m < NWM; ++m) Ws[tid + T * m] = fast_exp2(gref[m] * kLog2e - pg2) * pd;
   };
 
 
@@ -282,7 +284,11 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   };
   // Diagonal pair k = tile / 2: the row factor exp(G_i - G_R) first scales
   // everything accumulated so far (in place), then the pair takes exact
-  // decays, with the causal select made before the exponential.
+  // decays, with the causal select made before the exponential: a masked
+  // entry gets exp(-inf) = 0, which zeroes its finite C.B^T value.  (The
+  // upper sub-tile of an even tile, whose slot holds the other tile's values,
+  // is zeroed outright; that select also keeps the register allocator from
+  // copying the accumulators.)
   auto diag_frag = [&](auto tsel_c, const int k, const int tile, f32x4_t (&acc)[CT], int l16, int lg) -> Frag {
     constexpr int TSEL = decltype(tsel_c)::value;
     const int i = 16 * tile + l16;  // the token this lane's interaction values and outputs belong to
@@ -291,10 +297,10 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     const float4 g1 = *reinterpret_cast<const float4*>(Gs + 32 * k + 16 + 4 * lg);
     const float4 d0 = *reinterpret_cast<const float4*>(dts + 32 * k + 4 * lg);
     const float4 d1 = *reinterpret_cast<const float4*>(dts + 32 * k + 16 + 4 * lg);
-    const float gi = Gs[i];
+    const float gi = Gs[i];  // base-2 units
     const float gR = Gs[32 * k];
     {
-      const float e = fast_exp(gi - gR);
+      const float e = fast_exp2(gi - gR);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) acc[ct] *= e;
     }
@@ -307,9 +313,8 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 #pragma unroll
     for (int e8 = 0; e8 < 8; ++e8) {
       const int j = 32 * k + 16 * (e8 >> 2) + 4 * lg + (e8 & 3);
-      const bool keep = j <= i;
-      const float dec = fast_exp(keep ? gi - gj[e8] : -INFINITY) * dj[e8];
-      m[e8] = keep ? cvv[e8] * dec : 0.f;
+      const float dec = fast_exp2(j <= i ? gi - gj[e8] : -INFINITY);
+      m[e8] = cvv[e8] * dj[e8] * dec;
     }
     return Op::from_f32(m);
   };
@@ -427,7 +432,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         }
       }
       issue_h(hn);
-      const float e0 = fast_exp(Gs[32 * (ta >> 1)]), e1 = fast_exp(Gs[32 * (tb >> 1)]);
+      const float e0 = fast_exp2(Gs[32 * (ta >> 1)]), e1 = fast_exp2(Gs[32 * (tb >> 1)]);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         acc0[ct] *= e0;

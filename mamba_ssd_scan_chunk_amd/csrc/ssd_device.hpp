@@ -173,5 +173,9 @@ __device__ __forceinline__ float load1_as_f32(const void* base, int64_t elem, bo
 // exp via the hardware exp2 (v_exp_f32); relative error ~4e-6 worst case over
 // the ranges used here, and exact 1 at 0.
 __device__ __forceinline__ float fast_exp(float v) { return __expf(v); }
+// 2^v on the hardware exponential (one v_exp_f32): for log-space sums kept in
+// base-2 units (pre-multiplied by log2(e)), saving the scaling multiply.
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace ssd
