@@ -38,13 +38,11 @@ __global__ __launch_bounds__(kCsThreads) void chunk_cumsum_kernel(
   const int active = Q / E;            // lanes that hold tokens
   const bool vec = (H % 4 == 0);       // 16-byte aligned head quadruples
 
-  float a[4], A4[4];
+  float A4[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) A4[k] = (h0 + k < H) ? A[h0 + k] : 0.f;
 
   float dv[4][4];  // [token e][head k]
-  float run[4] = {0.f, 0.f, 0.f, 0.f};
-  float part[4][4];
   const int64_t row0 = (int64_t)b * L + (int64_t)c * Q;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -57,25 +55,13 @@ __global__ __launch_bounds__(kCsThreads) void chunk_cumsum_kernel(
 #pragma unroll
       for (int k = 0; k < 4; ++k) dv[e][k] = (ok && h0 + k < H) ? dt[row * H + h0 + k] : 0.f;
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      a[k] = dv[e][k] * A4[k];
-      run[k] += a[k];
-      part[e][k] = run[k];
-    }
   }
-  // exclusive prefix of the lane totals, per head (inclusive scan shifted by one lane)
+  // per head: running sum inside the lane, then the lane offsets by a shuffle scan
+  float gv[4][4];  // [head k][token e]
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    float tot = run[k];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(tot, off, 64);
-      if (lane >= off) tot += o;
-    }
-    float excl = __shfl_up(tot, 1, 64);
-    if (lane == 0) excl = 0.f;
-    run[k] = excl;
+    const float d4[4] = {dv[0][k], dv[1][k], dv[2][k], dv[3][k]};
+    chunk_cumsum_lane(d4, E, A4[k], lane, gv[k]);
   }
   if (lane < active) {
 #pragma unroll
@@ -83,14 +69,13 @@ __global__ __launch_bounds__(kCsThreads) void chunk_cumsum_kernel(
       if (h0 + k >= H) continue;
       const int64_t orow = (((int64_t)b * H + h0 + k) * nc + c) * Q + lane * E;
       if (E == 4) {
-        *reinterpret_cast<float4*>(dA_cumsum + orow) =
-            make_float4(run[k] + part[0][k], run[k] + part[1][k], run[k] + part[2][k], run[k] + part[3][k]);
+        *reinterpret_cast<float4*>(dA_cumsum + orow) = make_float4(gv[k][0], gv[k][1], gv[k][2], gv[k][3]);
         if (dt_bhl) *reinterpret_cast<float4*>(dt_bhl + orow) = make_float4(dv[0][k], dv[1][k], dv[2][k], dv[3][k]);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (e < E) {
-            dA_cumsum[orow + e] = run[k] + part[e][k];
+            dA_cumsum[orow + e] = gv[k][e];
             if (dt_bhl) dt_bhl[orow + e] = dv[e][k];
           }
       }

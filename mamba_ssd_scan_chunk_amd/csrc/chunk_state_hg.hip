@@ -46,11 +46,16 @@ struct ShgCfg {
   static constexpr size_t lds_total = lds_b + lds_x;
 };
 
-template <int Q, int N>
+// FUSE: the block also computes the log-space sums of its heads and chunk
+// from dt and A (the cumulative-sum step, same arithmetic as that kernel),
+// keeps them in LDS, and writes dA_cumsum / dt_bhl for the later steps;
+// otherwise it reads them.
+template <int Q, int N, bool FUSE>
 __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bhl,
-    const float* __restrict__ dA_cumsum, float* __restrict__ states, int L, int H, int P, int G, int nc, int HG,
-    int nhg, int npt, int remap) {
+    const float* __restrict__ dA_cumsum, const float* __restrict__ dt_raw, const float* __restrict__ Avec,
+    float* __restrict__ dA_out, float* __restrict__ dt_out, float* __restrict__ states, int L, int H, int P, int G,
+    int nc, int HG, int nhg, int npt, int remap) {
   using Cfg = ShgCfg<Q, N>;
   using Op = OpBF16;
   using Frag = Op::Frag;
@@ -62,6 +67,8 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   extern __shared__ __align__(16) unsigned char shg_smem[];
   uint16_t* Bn = reinterpret_cast<uint16_t*>(shg_smem);  // [Q][BP]
   uint16_t* Xn = Bn + Q * BP;                             // [Q][XP]
+  float* Gsa = reinterpret_cast<float*>(Xn + Q * XP);     // [HG][Q] log-space sums (FUSE)
+  float* Dsa = Gsa + HG * Q;                               // [HG][Q] dt (FUSE)
 
   const unsigned nblk = gridDim.x;
   unsigned bid = blockIdx.x;
@@ -80,17 +87,6 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   const int tid = threadIdx.x, wave = tid >> 6;
   const int HP = H * P;
 
-  // ---- B chunk -> Bn[j][n] (16-byte copies; a row's pieces go to
-  // consecutive threads)
-  {
-    const uint16_t* bsrc = Bm + (tok0 * G + g) * N;
-    const int GN = G * N;
-    for (int blk = tid; blk < Q * (N / 8); blk += T) {
-      const int j = blk / (N / 8), cb = blk % (N / 8);
-      *reinterpret_cast<uint4*>(Bn + j * BP + 8 * cb) = *reinterpret_cast<const uint4*>(bsrc + j * GN + 8 * cb);
-    }
-  }
-
   // ---- per-head register prefetch of x pieces and their G, dt
   // Piece blk -> (row, 8-column block cb): 8 consecutive threads take the 8
   // pieces of one row; within a wave the 8 rows are ordered 0,4,1,5,2,6,3,7 so
@@ -103,26 +99,41 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   uint4 xv[XPT];
   float gv[XPT], dv[XPT];
   float glast = 0.f;
+  int hcur = 0;  // FUSE: head (within the group) of the prefetched pieces
   auto issue = [&](int h) __attribute__((always_inline)) {
     const uint16_t* xs = x + (tok0 * H + h) * (int64_t)P + p0;
-    const int64_t bhc = ((int64_t)b * H + h) * nc + c;
-    const float* gsrc = dA_cumsum + bhc * Q;
-    const float* dsrc = dt_bhl + bhc * Q;
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       int row, cb;
       xmap(tid + u * T, row, cb);
       xv[u] = *reinterpret_cast<const uint4*>(xs + row * HP + 8 * cb);
-      gv[u] = gsrc[row];
-      dv[u] = dsrc[row];
     }
-    glast = gsrc[Q - 1];
+    if constexpr (FUSE) {
+      hcur = h - hbase;
+    } else {
+      const int64_t bhc = ((int64_t)b * H + h) * nc + c;
+      const float* gsrc = dA_cumsum + bhc * Q;
+      const float* dsrc = dt_bhl + bhc * Q;
+#pragma unroll
+      for (int u = 0; u < XPT; ++u) {
+        int row, cb;
+        xmap(tid + u * T, row, cb);
+        gv[u] = gsrc[row];
+        dv[u] = dsrc[row];
+      }
+      glast = gsrc[Q - 1];
+    }
   };
   auto commit = [&]() __attribute__((always_inline)) {
+    if constexpr (FUSE) glast = Gsa[hcur * Q + Q - 1];
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       int row, cb;
       xmap(tid + u * T, row, cb);
+      if constexpr (FUSE) {
+        gv[u] = Gsa[hcur * Q + row];
+        dv[u] = Dsa[hcur * Q + row];
+      }
       const float w = fast_exp(glast - gv[u]) * dv[u];
       const uint4 q = xv[u];
       uint4 o;
@@ -134,7 +145,65 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     }
   };
 
+  // the first head's x pieces are in flight while B (and, with FUSE, the
+  // cumulative sums) are staged
   issue(hbase);
+
+  // ---- B chunk -> Bn[j][n] (16-byte copies; a row's pieces go to
+  // consecutive threads)
+  {
+    const uint16_t* bsrc = Bm + (tok0 * G + g) * N;
+    const int GN = G * N;
+    for (int blk = tid; blk < Q * (N / 8); blk += T) {
+      const int j = blk / (N / 8), cb = blk % (N / 8);
+      *reinterpret_cast<uint4*>(Bn + j * BP + 8 * cb) = *reinterpret_cast<const uint4*>(bsrc + j * GN + 8 * cb);
+    }
+  }
+
+  if constexpr (FUSE) {
+    // ---- cumulative-sum step for the block's heads: dt rows -> LDS, one wave
+    // per head scans the chunk (chunk_cumsum_lane), pt == 0 blocks write the
+    // sums and dt rows for the state passing and the chunk scan
+    if ((HG & 3) == 0 && (H & 3) == 0 && (hbase & 3) == 0) {
+      // 16-byte loads: 4 heads of one token
+      const int hq = HG / 4;
+      for (int idx = tid; idx < Q * hq; idx += T) {
+        const int i = idx / hq, q4 = idx - i * hq;
+        const float4 v = *reinterpret_cast<const float4*>(dt_raw + (tok0 + i) * H + hbase + 4 * q4);
+        Dsa[(4 * q4 + 0) * Q + i] = v.x;
+        Dsa[(4 * q4 + 1) * Q + i] = v.y;
+        Dsa[(4 * q4 + 2) * Q + i] = v.z;
+        Dsa[(4 * q4 + 3) * Q + i] = v.w;
+      }
+    } else {
+      for (int idx = tid; idx < Q * HG; idx += T) {
+        const int i = idx / HG, hh = idx - i * HG;
+        Dsa[hh * Q + i] = dt_raw[(tok0 + i) * H + hbase + hh];
+      }
+    }
+    __syncthreads();
+    constexpr int E = Q / 64;
+    const int lane = tid & 63;
+    for (int hh = wave; hh < HG; hh += T / 64) {
+      float d4[4], g4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d4[e] = e < E ? Dsa[hh * Q + E * lane + e] : 0.f;
+      chunk_cumsum_lane(d4, E, Avec[hbase + hh], lane, g4);
+#pragma unroll
+      for (int e = 0; e < E; ++e) Gsa[hh * Q + E * lane + e] = g4[e];
+    }
+    __syncthreads();
+    if (pt == 0) {
+      // rows of Q floats per head, written as 16-byte pieces
+      for (int idx = tid; idx < HG * (Q / 4); idx += T) {
+        const int hh = idx / (Q / 4), i4 = idx - hh * (Q / 4);
+        const int64_t o = (((int64_t)b * H + hbase + hh) * nc + c) * Q + 4 * i4;
+        *reinterpret_cast<float4*>(dA_out + o) = *reinterpret_cast<const float4*>(Gsa + hh * Q + 4 * i4);
+        *reinterpret_cast<float4*>(dt_out + o) = *reinterpret_cast<const float4*>(Dsa + hh * Q + 4 * i4);
+      }
+    }
+  }
+
   __syncthreads();  // Bn complete
   commit();
   __syncthreads();
@@ -205,38 +274,55 @@ bool chunk_state_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
   return (d.Q == 256 && d.N == 128) || (d.Q == 128 && d.N == 256);
 }
 
-template <int Q, int N>
+template <int Q, int N, bool FUSE>
 static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
-                                  const float* dA_cumsum, float* states, hipStream_t stream) {
+                                  const float* dA_cumsum, const float* dt_raw, const float* A, float* dA_out,
+                                  float* dt_out, float* states, hipStream_t stream) {
   using Cfg = ShgCfg<Q, N>;
-  auto kern = chunk_state_hg_kernel<Q, N>;
-  const size_t lds = Cfg::lds_total;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  auto kern = chunk_state_hg_kernel<Q, N, FUSE>;
+  // with FUSE the block also holds the sums and dt rows of its heads in LDS
+  const int64_t cap = FUSE ? (int64_t)((160 * 1024 - Cfg::lds_total) / (8 * Q)) : (int64_t)1 << 30;
   const int npt = (int)(d.P / Cfg::PT);
   const int64_t hpg = d.H / d.G;
   const int64_t base = d.B * d.nc * d.G * npt;
   int HG = 1;
   for (int64_t k = 1; k <= hpg; ++k) {
-    if (hpg % k) continue;
+    if (hpg % k || hpg / k > cap) continue;
     HG = (int)(hpg / k);
     if (base * k >= shg_cu_count()) break;
+  }
+  const size_t lds = Cfg::lds_total + (FUSE ? (size_t)8 * Q * HG : 0);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
   }
   const int nhg = (int)(hpg / HG);
   const int64_t nblk = base * nhg;
   const int remap = (nblk % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(Cfg::T), lds, stream, static_cast<const uint16_t*>(x),
-                     static_cast<const uint16_t*>(Bm), dt_bhl, dA_cumsum, states, (int)d.L, (int)d.H, (int)d.P,
-                     (int)d.G, (int)d.nc, HG, nhg, npt, remap);
+                     static_cast<const uint16_t*>(Bm), dt_bhl, dA_cumsum, dt_raw, A, dA_out, dt_out, states,
+                     (int)d.L, (int)d.H, (int)d.P, (int)d.G, (int)d.nc, HG, nhg, npt, remap);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_state_hg(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
                                  const float* dA_cumsum, float* states, hipStream_t stream) {
-  if (d.Q == 256 && d.N == 128) return launch_shg_inst<256, 128>(d, x, Bm, dt_bhl, dA_cumsum, states, stream);
-  if (d.Q == 128 && d.N == 256) return launch_shg_inst<128, 256>(d, x, Bm, dt_bhl, dA_cumsum, states, stream);
+  if (d.Q == 256 && d.N == 128)
+    return launch_shg_inst<256, 128, false>(d, x, Bm, dt_bhl, dA_cumsum, nullptr, nullptr, nullptr, nullptr,
+                                            states, stream);
+  if (d.Q == 128 && d.N == 256)
+    return launch_shg_inst<128, 256, false>(d, x, Bm, dt_bhl, dA_cumsum, nullptr, nullptr, nullptr, nullptr,
+                                            states, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_state_cumsum_hg(const Dims& d, const void* x, const void* Bm, const float* dt,
+                                        const float* A, float* dA_cumsum, float* dt_bhl, float* states,
+                                        hipStream_t stream) {
+  if (d.Q == 256 && d.N == 128)
+    return launch_shg_inst<256, 128, true>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl, states, stream);
+  if (d.Q == 128 && d.N == 256)
+    return launch_shg_inst<128, 256, true>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl, states, stream);
   return hipErrorInvalidValue;
 }
 

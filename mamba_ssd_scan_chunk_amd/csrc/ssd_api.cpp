@@ -190,8 +190,13 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, c
   const hipStream_t s = (hipStream_t)stream;
   const bool bf = in == SSD_BF16, f32m = mma == SSD_MMA_F32;
 
-  SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
-  SSD_TRY(from_hip(ssd::launch_chunk_state(d, x, Bm, bf, dtb, dA, st, f32m, s)));
+  if (ssd::chunk_state_hg_supported(d, bf, f32m)) {
+    // the head-group chunk-state kernel computes the cumulative sums itself
+    SSD_TRY(from_hip(ssd::launch_chunk_state_cumsum_hg(d, x, Bm, dt, A, dA, dtb, st, s)));
+  } else {
+    SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
+    SSD_TRY(from_hip(ssd::launch_chunk_state(d, x, Bm, bf, dtb, dA, st, f32m, s)));
+  }
   if (!f32m) {
     // bf16 matrix operands: hand the chunk scan the carried states already
     // rounded to bf16 (the operand values it would round them to)

@@ -173,6 +173,32 @@ __device__ __forceinline__ float load1_as_f32(const void* base, int64_t elem, bo
 // exp via the hardware exp2 (v_exp_f32); relative error ~4e-6 worst case over
 // the ranges used here, and exact 1 at 0.
 __device__ __forceinline__ float fast_exp(float v) { return __expf(v); }
+// In-chunk inclusive cumulative sum of dt*A for one head, one wave: lane l
+// holds the E (<= 4) consecutive tokens E*l .. E*l+E-1 (d[e], e < E), sums
+// them with a running fused multiply-add, and a 6-step inclusive shuffle scan
+// of the 64 lane totals supplies each lane's offset.  out[e] = G at token
+// E*l + e.  Shared by the cumulative-sum kernel and the fused chunk-state
+// prologue, which therefore produce identical bits.
+__device__ __forceinline__ void chunk_cumsum_lane(const float (&d)[4], int E, float a, int lane, float (&out)[4]) {
+  float part[4];
+  float run = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (e < E) run = fmaf(d[e], a, run);
+    part[e] = run;
+  }
+  float tot = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float o = __shfl_up(tot, off, 64);
+    if (lane >= off) tot += o;
+  }
+  float excl = __shfl_up(tot, 1, 64);
+  if (lane == 0) excl = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = excl + part[e];
+}
+
 // 2^v on the hardware exponential (one v_exp_f32): for log-space sums kept in
 // base-2 units (pre-multiplied by log2(e)), saving the scaling multiply.
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }

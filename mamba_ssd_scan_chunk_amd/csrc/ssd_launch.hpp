@@ -31,6 +31,12 @@ hipError_t launch_chunk_state(const Dims& d, const void* x, const void* Bm, bool
 bool chunk_state_hg_supported(const Dims& d, bool in_bf16, bool f32_mma);
 hipError_t launch_chunk_state_hg(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
                                  const float* dA_cumsum, float* states, hipStream_t stream);
+// The same kernel with the cumulative-sum step fused in front: it reads dt and
+// A, writes dA_cumsum and dt_bhl (bit-identical to launch_chunk_cumsum) and
+// the chunk states.  Same support as chunk_state_hg_supported.
+hipError_t launch_chunk_state_cumsum_hg(const Dims& d, const void* x, const void* Bm, const float* dt,
+                                        const float* A, float* dA_cumsum, float* dt_bhl, float* states,
+                                        hipStream_t stream);
 
 hipError_t launch_state_passing(const Dims& d, const float* chunk_states, float* carried,
                                 const float* dA_cumsum, const float* initial_states,
