@@ -5,6 +5,9 @@ the dominant kernel and the fp64 oracle timed on the host as a CPU baseline.
 
 One step = one ssd_forward call (cumsum -> chunk states -> state passing ->
 fused chunk output) over one batch of the workload, inputs resident in HBM.
+Warm-up runs at least W steps and at least --min-warmup-s seconds of steps
+(GPU clocks ramp under sustained load: a few milliseconds of warm-up measure
+the ramp, not the steady state); both counts are reported.
 Per-kernel durations come from HIP events recorded on the launch stream around
 each ABI call of the same pipeline (a second timed loop).  Prints ONE JSON line.
 """
@@ -104,8 +107,10 @@ def cpu_baseline(inp, w, target_s=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--min-warmup-s", type=float, default=0.3,
+                    help="warm-up also lasts at least this long (seconds of back-to-back steps)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--mma", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -150,8 +155,13 @@ def main():
                         workspace=ws, mma=args.mma)
 
     # ---- phase 1: whole-path throughput
-    for _ in range(args.warmup):
+    warm_run = 0
+    warm0 = time.perf_counter()
+    while warm_run < args.warmup or time.perf_counter() - warm0 < args.min_warmup_s:
         step()
+        warm_run += 1
+        if warm_run % 16 == 0:
+            torch.cuda.synchronize()  # keep the wall clock in step with the GPU
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -243,6 +253,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_run,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
