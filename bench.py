@@ -41,6 +41,9 @@ def algorithmic_costs(w, in_bytes, y_bytes, carried_bytes=4):
                             flops=2 * blh * N * P)
     k["state_passing"] = dict(bytes=4 * st + 4 * B * H * nc + carried_bytes * st + 4 * B * H * N * P,
                               flops=2 * st)
+    k["chunk_state_passing"] = dict(bytes=in_bytes * blh * P + in_bytes * B * L * G * N + 2 * 4 * blh
+                                    + carried_bytes * st + 4 * B * H * N * P,
+                                    flops=2 * blh * N * P + 2 * st)
     k["chunk_scan"] = dict(bytes=in_bytes * blh * P + 2 * in_bytes * B * L * G * N + 2 * 4 * blh + carried_bytes * st
                            + 4 * H + y_bytes * blh * P,
                            flops=2 * blh * N * P + B * nc * H * Q * (Q + 1) * P + B * nc * G * Q * (Q + 1) * N)
@@ -51,6 +54,7 @@ KERNEL_SOURCES = {
     "chunk_cumsum": ["chunk_cumsum.hip"],
     "chunk_state": ["chunk_state_hg.hip", "chunk_state.hip"],
     "state_passing": ["state_passing.hip"],
+    "chunk_state_passing": ["state_fused.hip"],
     "chunk_scan": ["chunk_scan_hg.hip", "chunk_scan.hip"],
 }
 
@@ -184,13 +188,26 @@ def main():
     carried_bytes = 2 if args.mma == "bf16" else 4
     carried = (torch.empty((B, nc, H, N, P), device=dev, dtype=torch.bfloat16) if carried_bytes == 2
                else states)
-    calls = {
-        "chunk_cumsum": lambda: ops.ssd_chunk_cumsum(sh, t["dt"], t["A"], dA_cumsum=dA, dt_bhl=dtb),
-        "chunk_state": lambda: ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, states=states, mma=args.mma),
-        "state_passing": lambda: ops.ssd_state_passing(sh, states, dA, carried=carried, final_states=fin),
-        "chunk_scan": lambda: ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, carried, t["D"], y=y,
-                                                 mma=args.mma),
-    }
+    # ssd_forward takes the fused state path (chunk states never stored) where
+    # it is supported and has at least two blocks per compute unit; the other
+    # state path, where supported, is timed too (reported under "other_path")
+    fused_ok = args.mma == "bf16" and N % 64 == 0 and P % 64 == 0 and w.in_dtype == "bf16"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    fused = fused_ok and B * H * (N // 64) * (P // 64) >= 2 * cus
+    fused_call = lambda: ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA, carried=carried,
+                                                     final_states=fin, mma=args.mma)
+    calls = {"chunk_cumsum": lambda: ops.ssd_chunk_cumsum(sh, t["dt"], t["A"], dA_cumsum=dA, dt_bhl=dtb)}
+    if fused:
+        calls["chunk_state_passing"] = fused_call
+    else:
+        calls["chunk_state"] = lambda: ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, states=states,
+                                                           mma=args.mma)
+        calls["state_passing"] = lambda: ops.ssd_state_passing(sh, states, dA, carried=carried, final_states=fin)
+    calls["chunk_scan"] = lambda: ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, carried, t["D"], y=y,
+                                                     mma=args.mma)
+    forward_kernels = list(calls)
+    if fused_ok and not fused:
+        calls["chunk_state_passing"] = fused_call
     order = list(calls) if args.kernel_only is None else [args.kernel_only]
     for _ in range(2):
         for k in calls:
@@ -222,6 +239,7 @@ def main():
                       "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
                       "TFLOPs": round(tflops, 2), "mfma_peak_frac": round(tflops / peak_t, 4),
                       "frac_of_roof": round(tflops / roof_t, 4)}
+    other = {k: kernels.pop(k) for k in list(kernels) if k not in forward_kernels and len(kernels) > 1}
     dom = max(kernels, key=lambda k: kernels[k]["us"])
     dk = kernels[dom]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -267,6 +285,8 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "kernels": kernels,
+        "state_path": "fused" if fused else "two-kernel",
+        "other_path": other,
         "copy_GBps": round(copy_gbps, 1),
     }
     if not args.no_cpu_baseline:

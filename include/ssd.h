@@ -117,6 +117,29 @@ ssd_status ssd_state_passing(const ssd_shape* shape, const float* chunk_states, 
                              const float* initial_states, float* final_states, void* stream);
 
 /*
+ * Fused state path (P1, paragraph on the three kernels: the state pass walks
+ * the chunks in order with one matrix product per chunk and the running state
+ * on chip): ssd_chunk_state and ssd_state_passing in one call, without
+ * writing the chunk states anywhere.  Per (b,h):
+ *   run = initial_states[b,h] (zeros when NULL)
+ *   for c in 0..nc-1:  carried[b,c,h] = run;
+ *                      run = exp(G_{Q-1}(c)) run + sum_{j<Q} exp(G_{Q-1} - G_j) dt_j B_j x_j^T
+ *   final_states[b,h] = run   (final_states may be NULL: not written)
+ * Where ssd_chunk_state uses its head-group kernel (bf16, chunk 256 with
+ * N = 128 or chunk 128 with N = 256) the results are bit-identical to
+ * ssd_chunk_state followed by ssd_state_passing with the same carried_dtype;
+ * elsewhere they differ from it only by the order of the fp32 sums.
+ * x [B,L,H,P], Bm [B,L,G,N]
+ * (dtype `in`), dt_bhl and dA_cumsum [B,H,nc,Q], carried [B,nc,H,N,P] in
+ * carried_dtype, initial/final states [B,H,N,P] fp32.  Supported: in = BF16,
+ * mma = SSD_MMA_BF16, N and P multiples of 64 (else SSD_ERR_UNSUPPORTED).
+ */
+ssd_status ssd_chunk_state_passing(const ssd_shape* shape, const void* x, const void* Bm, ssd_dtype in,
+                                   const float* dt_bhl, const float* dA_cumsum,
+                                   const float* initial_states, void* carried, ssd_dtype carried_dtype,
+                                   float* final_states, ssd_mma mma, void* stream);
+
+/*
  * Fused chunk output (P1, compute_out paragraph: carried-state term, decayed
  * and causally masked interaction matrix C.B^T, skip connection, in one
  * kernel with the interaction tile kept on chip and the mask applied as a
@@ -149,8 +172,11 @@ size_t ssd_workspace_bytes(const ssd_shape* shape);
  * SSD_MMA_BF16 the carried states go from the state passing to the chunk scan
  * as bf16 (the matrix-operand values the chunk scan uses either way); with
  * SSD_MMA_F32 the state passing runs in place on the fp32 chunk states.
- * Results are bit-identical to the four calls made separately with those
- * carried dtypes.
+ * Where ssd_chunk_state_passing supports the shape and launches at least two
+ * blocks per compute unit of the current device (B*H*(N/64)*(P/64) >= 2 x
+ * units), the two middle steps are that fused call instead.  Results are
+ * bit-identical to the separate calls of the path taken, with those carried
+ * dtypes.
  * initial_states [B,H,N,P] may be NULL (zeros); final_states [B,H,N,P] may be
  * NULL (not written).  workspace: device memory of at least
  * ssd_workspace_bytes(shape) bytes, owned by the caller, contents undefined

@@ -19,8 +19,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmamba_ssd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "chunk_state_hg.hip", "state_passing.hip", "chunk_scan.hip",
-           "chunk_scan_hg.hip", "ssd_api.cpp"]
+SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "chunk_state_hg.hip", "state_passing.hip", "state_fused.hip",
+           "chunk_scan.hip", "chunk_scan_hg.hip", "ssd_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

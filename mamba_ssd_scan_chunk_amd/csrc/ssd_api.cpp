@@ -146,6 +146,24 @@ ssd_status ssd_state_passing(const ssd_shape* shape, const float* chunk_states, 
                                             initial_states, final_states, (hipStream_t)stream));
 }
 
+ssd_status ssd_chunk_state_passing(const ssd_shape* shape, const void* x, const void* Bm, ssd_dtype in,
+                                   const float* dt_bhl, const float* dA_cumsum, const float* initial_states,
+                                   void* carried, ssd_dtype carried_dtype, float* final_states, ssd_mma mma,
+                                   void* stream) {
+  Dims d;
+  SSD_TRY(check_shape(shape, &d));
+  SSD_TRY(check_dtype(in));
+  SSD_TRY(check_dtype(carried_dtype));
+  SSD_TRY(check_mma(mma));
+  if (!x || !Bm || !dt_bhl || !dA_cumsum || !carried) return SSD_ERR_NULL;
+  if (!aligned16(x) || !aligned16(Bm) || !aligned16(dt_bhl) || !aligned16(dA_cumsum) || !aligned16(carried) ||
+      (initial_states && !aligned16(initial_states)) || (final_states && !aligned16(final_states)))
+    return SSD_ERR_ALIGN;
+  if (!ssd::state_fused_supported(d, in == SSD_BF16, mma == SSD_MMA_F32)) return SSD_ERR_UNSUPPORTED;
+  return from_hip(ssd::launch_state_fused(d, x, Bm, dt_bhl, dA_cumsum, initial_states, carried,
+                                          carried_dtype == SSD_BF16, final_states, (hipStream_t)stream));
+}
+
 ssd_status ssd_chunk_scan(const ssd_shape* shape, const void* x, const void* Bm, const void* Cm, ssd_dtype in,
                           const float* dt_bhl, const float* dA_cumsum, const void* carried, ssd_dtype carried_dtype,
                           const float* D, void* y, ssd_dtype y_dtype, ssd_mma mma, void* stream) {
@@ -160,6 +178,19 @@ size_t ssd_workspace_bytes(const ssd_shape* shape) {
   Dims d;
   if (check_shape(shape, &d) != SSD_OK) return 0;
   return workspace_layout(d).total;
+}
+
+// ssd_forward's state step: the fused kernel (chunk states stay on chip) or
+// the two-kernel path (fp32 chunk states through memory).  The fused kernel
+// walks the chunks in sequence inside each block, so it only pays off with
+// enough blocks to keep every compute unit busy: at least two per unit
+// (measured: 2048 blocks on 256 units 24% faster per forward, 320 blocks 8%
+// slower).
+static bool prefer_fused_state(const Dims& d) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return false;
+  return ssd::state_fused_blocks(d) >= 2 * (int64_t)cus;
 }
 
 ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* Bm,
@@ -190,6 +221,16 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, c
   const hipStream_t s = (hipStream_t)stream;
   const bool bf = in == SSD_BF16, f32m = mma == SSD_MMA_F32;
 
+  if (ssd::state_fused_supported(d, bf, f32m) && prefer_fused_state(d)) {
+    // fused state path: the chunk states never reach memory; the carried
+    // states go to the chunk scan as bf16 (its matrix-operand values)
+    uint16_t* hb = reinterpret_cast<uint16_t*>(base + ws.hb_off);
+    SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
+    SSD_TRY(from_hip(ssd::launch_state_fused(d, x, Bm, dtb, dA, initial_states, hb, true, final_states, s)));
+    SSD_TRY(from_hip(
+        ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, hb, true, D, y, y_dtype == SSD_BF16, f32m, s)));
+    return SSD_OK;
+  }
   if (ssd::chunk_state_hg_supported(d, bf, f32m)) {
     // the head-group chunk-state kernel computes the cumulative sums itself
     SSD_TRY(from_hip(ssd::launch_chunk_state_cumsum_hg(d, x, Bm, dt, A, dA, dtb, st, s)));

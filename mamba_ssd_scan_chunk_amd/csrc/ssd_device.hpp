@@ -204,4 +204,16 @@ __device__ __forceinline__ void chunk_cumsum_lane(const float (&d)[4], int E, fl
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Streaming (non-temporal) vector stores: the lines are not kept in L2.  Only
+// for outputs whose writes fill whole lines within a short time; scattered
+// partial-line writes this way cost more than through L2.
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_stream(float* p, float4 v) {
+  __builtin_nontemporal_store(f32x4v_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4v_t*>(p));
+}
+__device__ __forceinline__ void store_stream(uint16_t* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4v_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v_t*>(p));
+}
+
 }  // namespace ssd

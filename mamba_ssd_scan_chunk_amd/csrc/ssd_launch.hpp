@@ -47,6 +47,17 @@ hipError_t launch_state_passing_bf16(const Dims& d, const float* chunk_states, u
                                      const float* dA_cumsum, const float* initial_states,
                                      float* final_states, hipStream_t stream);
 
+// Fused state path: chunk states and the inter-chunk advance in one pass (the
+// chunk states stay on chip); carried and final states are bit-identical to
+// launch_chunk_state + launch_state_passing.  bf16 inputs and operands,
+// N and P multiples of 64, chunk in {32, 64, 128, 256}.
+bool state_fused_supported(const Dims& d, bool in_bf16, bool f32_mma);
+// Blocks the fused state kernel launches for the shape (each walks all chunks).
+int64_t state_fused_blocks(const Dims& d);
+hipError_t launch_state_fused(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
+                              const float* dA_cumsum, const float* initial_states, void* carried, bool carried_bf16,
+                              float* final_states, hipStream_t stream);
+
 // Head-group variant of the fused chunk output (bf16 inputs and operands,
 // (chunk, N) in {(128,128), (128,256), (256,128)}, P a multiple of 64);
 // launch_chunk_scan picks it when supported.  `carried` holds fp32 values, or

@@ -1,0 +1,329 @@
+// state_fused.hip -- chunk states and the inter-chunk state advance in one
+// pass (the fused state path): the chunk states never reach memory.
+//
+// Page: "Jane Street ML Engineers Map Mamba-2 Recurrent State Computation to
+// Tensor Cores with cuTile" (disconfirmai.com), paragraph on the three kernels
+// (the state pass walks the chunks in order, one matrix product per chunk,
+// the running state kept on chip) and the jump-formula paragraph (each
+// chunk's state is one product of the stacked, exponentially pre-multiplied
+// b and x rows).  Per (b, h), with G = dA_cumsum[b,h,c,:], dt = dt_bhl[b,h,c,:]:
+//     H_0 = initial state (or 0)
+//     for c = 0..nc-1:
+//         carried[b,c,h] = H_c
+//         S_c     = sum_j exp(G_{Q-1} - G_j) dt_j B_j x_j^T          (N x P)
+//         H_{c+1} = exp(G_{Q-1}) H_c + S_c
+//     final[b,h] = H_nc
+//
+// Block = (b, h, 64 state rows n, 64 columns p), 8 waves.  Wave w owns the
+// rows 16 (w % 4) .. +15 of the block's n range and the columns 32 (w / 4)
+// .. +31; the running state of those 16 x 32 elements lives in registers in
+// the MFMA accumulator layout (lane: row l16, columns 16ct + 4lg .. +3).  Per
+// chunk the x rows (scaled by w_j = exp(G_{Q-1} - G_j) dt_j, rounded to bf16)
+// and the raw B rows are staged in LDS in their natural token-major layouts,
+// and the MFMA fragments (token = contraction index) come from the transposing
+// LDS read, as in the head-group chunk-state kernel.  The state recurrence
+// makes the chunks of one block strictly sequential, so the block hides the
+// memory latency itself: the x rows of the next two chunks (and the B rows of
+// the next one) are in flight in registers while the current chunk is staged
+// and multiplied, and two blocks share a compute unit.  S_c is accumulated from the same operands in the same
+// order as the head-group chunk-state kernel, and the update is the same fused
+// multiply-add as the state-passing kernel, so carried and final states are
+// bit-identical to the two-call path.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+template <int Q, int WAVES>
+struct SfCfg {
+  static constexpr int T = 64 * WAVES;
+  static constexpr int NB = 64, PT = 64;  // state rows and columns of a block
+  // wave grid: WN waves along n (RT 16-row tiles each) x 2 along p (two
+  // 16-column tiles each)
+  static constexpr int WN = WAVES / 2, RT = 4 / WN;
+  // row pitches (elements) of Xn and Bn: odd multiples of 8 dwords modulo 64,
+  // so the transposing reads (8 consecutive rows x 32 bytes per half wave)
+  // fall in distinct banks
+  static constexpr int XP = PT + 16, BP = NB + 16;
+  // 8 threads cover a row's 128-byte slice; LT threads load, RPT rows each
+  static constexpr int LT = Q * 8 < T ? Q * 8 : T;
+  static constexpr int RPT = Q * 8 / LT;
+  static constexpr size_t lds_total = (size_t)Q * XP * 2 + (size_t)Q * BP * 2;
+};
+
+template <int Q, int WAVES, bool CBF16>
+__global__ __launch_bounds__(64 * WAVES, WAVES / 2) void state_fused_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bhl,
+    const float* __restrict__ dA_cumsum, const float* __restrict__ init, void* __restrict__ carried,
+    float* __restrict__ fin, int L, int H, int P, int N, int G, int nc, int nnb, int npt, int remap) {
+  using Cfg = SfCfg<Q, WAVES>;
+  using Op = OpBF16;
+  using Frag = Op::Frag;
+  constexpr int XP = Cfg::XP, BP = Cfg::BP, RPT = Cfg::RPT, LT = Cfg::LT, NB = Cfg::NB, PT = Cfg::PT;
+  constexpr int WN = Cfg::WN, RT = Cfg::RT;
+  constexpr int KU = WAVES == 8 ? 1 : 2;  // unroll of the contraction loop (register budget)
+  static_assert(Q % 32 == 0 && RPT >= 1, "chunk must be a multiple of 32");
+
+  extern __shared__ __align__(16) unsigned char sf_smem[];
+  uint16_t* Xn = reinterpret_cast<uint16_t*>(sf_smem);  // [Q][XP]  w-scaled x rows of the chunk
+  uint16_t* Bn = Xn + Q * XP;                            // [Q][BP]  B rows of the chunk (the block's n)
+
+  // block -> (b, h, p slice, n block); with remap the n blocks of one (b, h)
+  // (same x rows) land on one XCD and share its L2
+  const unsigned nblk = gridDim.x;
+  unsigned bid = blockIdx.x;
+  if (remap) bid = (bid & 7u) * (nblk >> 3) + (bid >> 3);
+  const int nb = bid % nnb;
+  unsigned rest = bid / nnb;
+  const int pt = rest % npt;
+  rest /= npt;
+  const int h = rest % H;
+  const int b = rest / H;
+  const int g = h / (H / G);
+  const int n0 = nb * NB, p0 = pt * PT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wn = wave % WN, wp = wave / WN;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int HP = H * P, GN = G * N;
+  const int64_t bh = (int64_t)b * H + h;
+  const int64_t NP = (int64_t)N * P;
+
+  // ---- running state H[n = n0 + 16 (RT wn + rt) + l16][p = p0 + 32 wp + 16 ct + 4 lg .. +3]
+  const int64_t soff = (int64_t)(n0 + 16 * RT * wn + l16) * P + p0 + 32 * wp + 4 * lg;  // within one state
+  float4 hs[RT][2];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+      hs[rt][ct] = init ? *reinterpret_cast<const float4*>(init + bh * NP + soff + 16 * (rt * P + ct))
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+
+  // ---- per-chunk register prefetch.  Loader thread t takes the 16-byte column
+  // piece t % 8 of rows RPT (t / 8) .. + RPT - 1 of x (64 columns of head h)
+  // and of B (64 state indices of group g), plus those rows' G and dt; threads
+  // past LT (short chunks only) load nothing.  x runs two chunks ahead in two
+  // register sets used alternately; B (shared by all heads of the group,
+  // mostly L2 hits) runs one chunk ahead and is issued first, so each wait on
+  // the in-order load counter covers exactly what the next staging needs.  G
+  // and dt travel with x where the register budget allows (4 waves), else
+  // with B.
+  constexpr bool GD2 = WAVES == 4;
+  const bool loader = LT == Cfg::T || tid < LT;
+  const int rbase = RPT * ((loader ? tid : 0) >> 3), cbp = tid & 7;
+  struct GSet {
+    float gv[RPT], dv[RPT], glast;
+  };
+  struct XSet {
+    uint4 xv[RPT];
+    GSet g;  // used when GD2
+  };
+  XSet sa, sb;
+  GSet g1;  // used when !GD2
+  uint4 bv[RPT];
+  auto load_g = [&](GSet& gs, int c) __attribute__((always_inline)) {
+    const float* gsrc = dA_cumsum + (bh * nc + c) * Q;
+    const float* dsrc = dt_bhl + (bh * nc + c) * Q;
+    gs.glast = gsrc[Q - 1];
+    if (!loader) return;
+    if constexpr (RPT % 4 == 0) {
+#pragma unroll
+      for (int u = 0; u < RPT; u += 4) {
+        const float4 g4 = *reinterpret_cast<const float4*>(gsrc + rbase + u);
+        const float4 d4 = *reinterpret_cast<const float4*>(dsrc + rbase + u);
+        gs.gv[u] = g4.x; gs.gv[u + 1] = g4.y; gs.gv[u + 2] = g4.z; gs.gv[u + 3] = g4.w;
+        gs.dv[u] = d4.x; gs.dv[u + 1] = d4.y; gs.dv[u + 2] = d4.z; gs.dv[u + 3] = d4.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) {
+        gs.gv[u] = gsrc[rbase + u];
+        gs.dv[u] = dsrc[rbase + u];
+      }
+    }
+  };
+  auto issue_x = [&](XSet& st, int c) __attribute__((always_inline)) {
+    if (loader) {
+      const int64_t tok0 = (int64_t)b * L + (int64_t)c * Q;
+      const uint16_t* xs = x + (tok0 * H + h) * (int64_t)P + p0 + 8 * cbp;
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) st.xv[u] = *reinterpret_cast<const uint4*>(xs + (rbase + u) * HP);
+    }
+    if constexpr (GD2) load_g(st.g, c);
+  };
+  auto issue_b = [&](int c) __attribute__((always_inline)) {
+    if (loader) {
+      const int64_t tok0 = (int64_t)b * L + (int64_t)c * Q;
+      const uint16_t* bs = Bm + (tok0 * G + g) * (int64_t)N + n0 + 8 * cbp;
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) bv[u] = *reinterpret_cast<const uint4*>(bs + (rbase + u) * GN);
+    }
+    if constexpr (!GD2) load_g(g1, c);
+  };
+  // stage a prefetched chunk: x rows scaled by w_j in fp32 and rounded to
+  // bf16 (the same arithmetic as the head-group chunk-state kernel), B raw
+  auto commit = [&](const XSet& st) __attribute__((always_inline)) {
+    if (!loader) return;
+    const GSet& gs = GD2 ? st.g : g1;
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+      const int row = rbase + u;
+      const float w = fast_exp(gs.glast - gs.gv[u]) * gs.dv[u];
+      const uint4 q = st.xv[u];
+      uint4 o;
+      o.x = pack_bf16x2(bf16_bits_to_f32(q.x & 0xffffu) * w, bf16_bits_to_f32(q.x >> 16) * w);
+      o.y = pack_bf16x2(bf16_bits_to_f32(q.y & 0xffffu) * w, bf16_bits_to_f32(q.y >> 16) * w);
+      o.z = pack_bf16x2(bf16_bits_to_f32(q.z & 0xffffu) * w, bf16_bits_to_f32(q.z >> 16) * w);
+      o.w = pack_bf16x2(bf16_bits_to_f32(q.w & 0xffffu) * w, bf16_bits_to_f32(q.w >> 16) * w);
+      *reinterpret_cast<uint4*>(Xn + row * XP + 8 * cbp) = o;
+      const uint4 bq = bv[u];
+      *reinterpret_cast<uint4*>(Bn + row * BP + 8 * cbp) = make_uint4(bq.x, bq.y, bq.z, bq.w);
+    }
+  };
+  // carried[b, c, h] = H_c (the running state), rounded to bf16 or fp32.  In
+  // bf16 the lane pairs (lg, lg ^ 1) first trade halves, so that each lane
+  // holds 8 consecutive columns of its row (even lg: tile 0, odd lg: tile 1)
+  // and one 16-byte store per lane writes the wave's 16 rows x 64 bytes.
+  auto store_carried = [&](int c) __attribute__((always_inline)) {
+    const int64_t coff = ((int64_t)b * nc + c) * H + h;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if constexpr (CBF16) {
+        const uint2 t0 = make_uint2(pack_bf16x2(hs[rt][0].x, hs[rt][0].y), pack_bf16x2(hs[rt][0].z, hs[rt][0].w));
+        const uint2 t1 = make_uint2(pack_bf16x2(hs[rt][1].x, hs[rt][1].y), pack_bf16x2(hs[rt][1].z, hs[rt][1].w));
+        const bool odd = lg & 1;
+        const uint2 give = odd ? t0 : t1;
+        uint2 got;
+        got.x = (uint32_t)__shfl_xor((int)give.x, 16, 64);
+        got.y = (uint32_t)__shfl_xor((int)give.y, 16, 64);
+        const uint4 v = odd ? make_uint4(got.x, got.y, t1.x, t1.y) : make_uint4(t0.x, t0.y, got.x, got.y);
+        // even lg: columns 4 lg .. +7 of tile 0; odd lg: 16 + 4 (lg - 1) .. +7
+        const int64_t o = coff * NP + soff + 16 * rt * P + (odd ? 16 - 4 : 0);
+        store_stream(static_cast<uint16_t*>(carried) + o, v);
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          store_stream(static_cast<float*>(carried) + coff * NP + soff + 16 * (rt * P + ct), hs[rt][ct]);
+      }
+    }
+  };
+  // one chunk: stage it, refill B with chunk c + 1 and `st` with chunk
+  // c + 2 (past the end, the last chunk again, unused: no data-dependent
+  // branch around the loads keeps the memory waits exact), store carried =
+  // H_c, accumulate S_c, advance H.  The memory counter retires in order, so
+  // the carried stores are issued after the loads (pinned there by a
+  // scheduling barrier): the next staging then waits for its own rows only,
+  // not for the stores to be acknowledged.
+  auto chunk = [&](XSet& st, int c) __attribute__((always_inline)) {
+    __syncthreads();  // the previous chunk's fragment reads are done
+    commit(st);
+    const float gl = GD2 ? st.g.glast : g1.glast;  // G_{Q-1} of chunk c
+    __syncthreads();
+    issue_b(c + 1 < nc ? c + 1 : nc - 1);
+    issue_x(st, c + 2 < nc ? c + 2 : nc - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_carried(c);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    f32x4_t acc[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll KU
+    for (int kk = 0; kk < Q / 32; ++kk) {
+      Frag xf[2], bf[RT];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) xf[ct] = lds_frag_tr(Xn + 32 * kk * XP + 32 * wp + 16 * ct, XP, ln);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) bf[rt] = lds_frag_tr(Bn + 32 * kk * BP + 16 * (RT * wn + rt), BP, ln);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = Op::mma(xf[ct], bf[rt], acc[rt][ct]);
+    }
+    // H_{c+1} = exp(G_{Q-1}) H_c + S_c
+    const float dec = expf(gl);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        hs[rt][ct].x = fmaf(dec, hs[rt][ct].x, acc[rt][ct][0]);
+        hs[rt][ct].y = fmaf(dec, hs[rt][ct].y, acc[rt][ct][1]);
+        hs[rt][ct].z = fmaf(dec, hs[rt][ct].z, acc[rt][ct][2]);
+        hs[rt][ct].w = fmaf(dec, hs[rt][ct].w, acc[rt][ct][3]);
+      }
+  };
+
+  // prologue: the same issue sequence as a chunk body (x, B, x, stores),
+  // so the first staging's wait matches the steady state; chunk 0 stores H_0
+  // again (the same values)
+  issue_x(sa, 0);
+  issue_b(0);
+  issue_x(sb, nc > 1 ? 1 : 0);
+  __builtin_amdgcn_sched_barrier(0);
+  store_carried(0);
+  int c = 0;
+  for (; c + 1 < nc; c += 2) {
+    chunk(sa, c);
+    chunk(sb, c + 1);
+  }
+  if (c < nc) chunk(sa, c);
+  if (fin) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        *reinterpret_cast<float4*>(fin + bh * NP + soff + 16 * (rt * P + ct)) = hs[rt][ct];
+  }
+}
+
+// ------------------------------------------------------------------ host side
+bool state_fused_supported(const Dims& d, bool in_bf16, bool f32_mma) {
+  return in_bf16 && !f32_mma && d.N % 64 == 0 && d.P % 64 == 0 &&
+         (d.Q == 32 || d.Q == 64 || d.Q == 128 || d.Q == 256);
+}
+
+int64_t state_fused_blocks(const Dims& d) { return d.B * d.H * (d.N / 64) * (d.P / 64); }
+
+template <int Q, bool CBF16, int WAVES = 8>
+static hipError_t launch_sf_inst(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
+                                 const float* dA_cumsum, const float* init, void* carried, float* fin,
+                                 hipStream_t stream) {
+  using Cfg = SfCfg<Q, WAVES>;
+  auto kern = state_fused_kernel<Q, WAVES, CBF16>;
+  const size_t lds = Cfg::lds_total;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int nnb = (int)(d.N / Cfg::NB), npt = (int)(d.P / Cfg::PT);
+  const int64_t nblk = d.B * d.H * npt * nnb;
+  const int remap = (nblk % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(Cfg::T), lds, stream, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(Bm), dt_bhl, dA_cumsum, init, carried, fin, (int)d.L, (int)d.H,
+                     (int)d.P, (int)d.N, (int)d.G, (int)d.nc, nnb, npt, remap);
+  return hipGetLastError();
+}
+
+template <bool CBF16>
+static hipError_t launch_sf_q(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
+                              const float* dA_cumsum, const float* init, void* carried, float* fin,
+                              hipStream_t stream) {
+  switch (d.Q) {
+    case 32: return launch_sf_inst<32, CBF16>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
+    case 64: return launch_sf_inst<64, CBF16>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
+    case 128: return launch_sf_inst<128, CBF16>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
+    case 256: return launch_sf_inst<256, CBF16>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_state_fused(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
+                              const float* dA_cumsum, const float* initial_states, void* carried, bool carried_bf16,
+                              float* final_states, hipStream_t stream) {
+  if (carried_bf16)
+    return launch_sf_q<true>(d, x, Bm, dt_bhl, dA_cumsum, initial_states, carried, final_states, stream);
+  return launch_sf_q<false>(d, x, Bm, dt_bhl, dA_cumsum, initial_states, carried, final_states, stream);
+}
+
+}  // namespace ssd

@@ -80,10 +80,10 @@ __global__ __launch_bounds__(kSpThreads) void state_passing_kernel(
 #pragma unroll
     for (int u = 0; u < kSpUnroll; ++u) {
       put(c + u, run);
-      run.x = dec[u] * run.x + s[u].x;
-      run.y = dec[u] * run.y + s[u].y;
-      run.z = dec[u] * run.z + s[u].z;
-      run.w = dec[u] * run.w + s[u].w;
+      run.x = fmaf(dec[u], run.x, s[u].x);  // explicit fused multiply-add: the fused
+      run.y = fmaf(dec[u], run.y, s[u].y);  // state path repeats these bits exactly
+      run.z = fmaf(dec[u], run.z, s[u].z);
+      run.w = fmaf(dec[u], run.w, s[u].w);
     }
 #pragma unroll
     for (int u = 0; u < kSpUnroll; ++u) {
@@ -95,10 +95,10 @@ __global__ __launch_bounds__(kSpThreads) void state_passing_kernel(
     const float4 sv = sp[(int64_t)c * cstride];
     const float d1 = expf(glast[(int64_t)c * Q]);
     put(c, run);
-    run.x = d1 * run.x + sv.x;
-    run.y = d1 * run.y + sv.y;
-    run.z = d1 * run.z + sv.z;
-    run.w = d1 * run.w + sv.w;
+    run.x = fmaf(d1, run.x, sv.x);
+    run.y = fmaf(d1, run.y, sv.y);
+    run.z = fmaf(d1, run.z, sv.z);
+    run.w = fmaf(d1, run.w, sv.w);
   }
   if (fin) reinterpret_cast<float4*>(fin)[bh * np4 + e4] = run;
 }

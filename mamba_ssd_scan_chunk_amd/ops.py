@@ -123,6 +123,37 @@ def ssd_state_passing(shape, chunk_states, dA_cumsum, initial_states=None, carri
     return carried, final_states
 
 
+def ssd_chunk_state_passing(shape, x, Bm, dt_bhl, dA_cumsum, initial_states=None, carried=None,
+                            final_states=None, carried_dtype="f32", want_final=True, mma="bf16", stream=None):
+    """Fused state path: carried states [B,nc,H,N,P] in ``carried_dtype`` and
+    fp32 final states [B,H,N,P] (None when ``want_final`` is false), without
+    materialising the chunk states; bit-identical to ssd_chunk_state followed
+    by ssd_state_passing."""
+    sh = _shape(shape)
+    B, L, H, P, N, G, Q, nc = _dims(sh)
+    io = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _req(x, "x", (B, L, H, P), io)
+    _req(Bm, "Bm", (B, L, G, N), (x.dtype,))
+    _req(dt_bhl, "dt_bhl", (B, H, nc, Q), f32)
+    _req(dA_cumsum, "dA_cumsum", (B, H, nc, Q), f32)
+    if initial_states is not None:
+        _req(initial_states, "initial_states", (B, H, N, P), f32)
+    if carried is None:
+        cdt = _DTNAME[carried_dtype] if isinstance(carried_dtype, str) else carried_dtype
+        carried = torch.empty((B, nc, H, N, P), device=x.device, dtype=cdt)
+    _req(carried, "carried", (B, nc, H, N, P), (torch.float32, torch.bfloat16))
+    if final_states is None and want_final:
+        final_states = torch.empty((B, H, N, P), device=x.device, dtype=torch.float32)
+    if final_states is not None:
+        _req(final_states, "final_states", (B, H, N, P), f32)
+    lib = load_library()
+    check(lib.ssd_chunk_state_passing(sh, _ptr(x), _ptr(Bm), _DT[x.dtype], _ptr(dt_bhl), _ptr(dA_cumsum),
+                                      _ptr(initial_states), _ptr(carried), _DT[carried.dtype],
+                                      _ptr(final_states), _mma(mma), _stream(stream)))
+    return carried, final_states
+
+
 def ssd_chunk_scan(shape, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y=None, y_dtype=None, mma="bf16",
                    stream=None):
     """y [B,L,H,P] in ``y_dtype`` (default: x's dtype)."""

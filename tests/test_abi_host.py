@@ -130,6 +130,32 @@ def test_alignment(lib):
                            None) == ALIGN
 
 
+def test_chunk_state_passing_checks(lib):
+    """The fused state path validates like the calls it fuses and refuses what
+    its kernel does not cover, all before any HIP call."""
+    s = shape()
+    for i in range(5):
+        args = [FAKE] * 5
+        args[i] = None
+        x, Bm, dtb, dA, car = args
+        assert lib.ssd_chunk_state_passing(s, x, Bm, 1, dtb, dA, None, car, 1, FAKE, 0, None) == NULL
+    assert lib.ssd_chunk_state_passing(s, FAKE, FAKE, 2, FAKE, FAKE, None, FAKE, 1, FAKE, 0, None) == DTYPE
+    assert lib.ssd_chunk_state_passing(s, FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 5, FAKE, 0, None) == DTYPE
+    assert lib.ssd_chunk_state_passing(s, FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 1, FAKE, 3, None) == DTYPE
+    odd = FAKE + 4
+    assert lib.ssd_chunk_state_passing(s, FAKE, FAKE, 1, FAKE, FAKE, odd, FAKE, 1, FAKE, 0, None) == ALIGN
+    assert lib.ssd_chunk_state_passing(s, FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 1, odd, 0, None) == ALIGN
+    # fp32 inputs, fp32 matrix operands, N or P not a multiple of 64: not covered
+    assert lib.ssd_chunk_state_passing(s, FAKE, FAKE, 0, FAKE, FAKE, None, FAKE, 1, FAKE, 0, None) == UNSUP
+    assert lib.ssd_chunk_state_passing(s, FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 1, FAKE, 1, None) == UNSUP
+    assert lib.ssd_chunk_state_passing(shape(dstate=48), FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 1, FAKE, 0,
+                                       None) == UNSUP
+    assert lib.ssd_chunk_state_passing(shape(headdim=32), FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 1, FAKE, 0,
+                                       None) == UNSUP
+    assert lib.ssd_chunk_state_passing(shape(batch=0), FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 1, FAKE, 0,
+                                       None) == SHAPE
+
+
 def test_bf16_carried_has_no_in_place_form(lib):
     """bf16 carried states are narrower than the fp32 chunk states: writing
     them over the chunk states would race, so that call is refused before any

@@ -288,13 +288,118 @@ def test_forward_bitwise_equals_split_calls(shape, y_dtype):
     y_f, fin_f = ops.ssd_forward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], initial_states=h0,
                                  y_dtype=y_dtype, mma="bf16")
     dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    name, B, L, H, P, N, G, Q = shape
+    # the forward's state step is either the two-call path or (N, P multiples
+    # of 64) the fused state call; the outputs must equal one of them exactly
     S = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma="bf16")
+    fused_ok = N % 64 == 0 and P % 64 == 0
     for cdt in ["f32", "bf16"]:
-        car, fin_s = ops.ssd_state_passing(sh, S, dA, initial_states=h0, carried_dtype=cdt)
-        y_s = ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, car, t["D"], y_dtype=y_dtype, mma="bf16")
+        states = [ops.ssd_state_passing(sh, S, dA, initial_states=h0, carried_dtype=cdt)]
+        if fused_ok:
+            states.append(ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA, initial_states=h0,
+                                                      carried_dtype=cdt))
+        match = False
+        for car, fin_s in states:
+            y_s = ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, car, t["D"], y_dtype=y_dtype,
+                                     mma="bf16")
+            torch.cuda.synchronize()
+            match = match or (torch.equal(y_f, y_s) and torch.equal(fin_f, fin_s))
+        assert match, cdt
+
+
+# (name, B, L, H, P, N, G, Q): shapes of the fused state path (N, P multiples of 64)
+FUSED_SHAPES = [
+    ("q256_n128", 2, 768, 6, 64, 128, 2, 256),
+    ("q128_n256", 1, 512, 4, 128, 256, 2, 128),
+    ("q128_n128", 2, 384, 3, 64, 128, 1, 128),
+    ("q64_n64", 1, 320, 5, 64, 64, 5, 64),
+    ("q32_p128", 1, 96, 2, 128, 64, 1, 32),
+]
+
+
+@pytest.mark.parametrize("carried_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("with_h0", [False, True])
+@pytest.mark.parametrize("shape", FUSED_SHAPES, ids=[s[0] for s in FUSED_SHAPES])
+def test_chunk_state_passing(shape, with_h0, carried_dtype):
+    """Fused state path against the oracle; on the shapes of the head-group
+    chunk-state kernel (same fragment order) also bit for bit against the two
+    calls it fuses."""
+    say(f"chunk_state_passing {shape} h0={with_h0} carried={carried_dtype}")
+    name, B, L, H, P, N, G, Q = shape
+    inp = _inp(shape, "bf16", seed=13, dt_shift=3.0)
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    o = oracle()
+    h0 = _h0(inp) if with_h0 else None
+    h0_t = None if h0 is None else torch.from_numpy(h0).cuda()
+    Hin, fin = o.carried_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk, h0=h0)
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    car, fin_g = ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA, initial_states=h0_t,
+                                             carried_dtype=carried_dtype)
+    torch.cuda.synchronize()
+    e1, e2 = relerr(car.float(), Hin), relerr(fin_g, fin)
+    say(f"  rel err carried {e1:.3g} final {e2:.3g}")
+    assert e1 <= tol_for("bf16") and e2 <= tol_for("bf16")
+    if (Q, N) in ((256, 128), (128, 256)):
+        S = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma="bf16")
+        car2, fin2 = ops.ssd_state_passing(sh, S, dA, initial_states=h0_t, carried_dtype=carried_dtype)
         torch.cuda.synchronize()
-        assert torch.equal(y_f, y_s), cdt
-        assert torch.equal(fin_f, fin_s), cdt
+        assert torch.equal(car, car2) and torch.equal(fin_g, fin2)
+
+
+def test_forward_state_path_choice():
+    """ssd_forward takes the fused state path when it has at least two blocks
+    per compute unit (4 x 64 heads x 2 state blocks = 512 here), else the
+    two-kernel path; either way y and the final states match the oracle, and
+    bit for bit the composition of the ABI calls of the path it takes (at
+    chunk 64 the two state paths round differently, so the check tells them
+    apart)."""
+    shape = ("fwd_path", 4, 256, 64, 64, 128, 8, 64)
+    say(f"forward state path choice {shape}")
+    name, B, L, H, P, N, G, Q = shape
+    inp = _inp(shape, "bf16", seed=15, dt_shift=2.0)
+    h0 = _h0(inp)
+    y, fin = gpu_forward(inp, "bf16", y_dtype="bf16", h0=h0)
+    yref, fref = oracle().forward(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D, h0=h0)
+    e1, e2 = relerr(y, yref), relerr(fin, fref)
+    say(f"  rel err y {e1:.3g} final {e2:.3g}")
+    assert e1 <= tol_for("bf16") and e2 <= tol_for("bf16")
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    h0_t = torch.from_numpy(h0).cuda()
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    fused = B * H * (N // 64) * (P // 64) >= 2 * cus
+    if fused:
+        car, fin_s = ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA, initial_states=h0_t,
+                                                 carried_dtype="bf16")
+    else:
+        S = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma="bf16")
+        car, fin_s = ops.ssd_state_passing(sh, S, dA, initial_states=h0_t, carried_dtype="bf16")
+    y_s = ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, car, t["D"], y_dtype="bf16", mma="bf16")
+    torch.cuda.synchronize()
+    say(f"  {cus} compute units: {'fused' if fused else 'two-kernel'} state path expected")
+    assert torch.equal(y, y_s) and torch.equal(fin, fin_s)
+
+
+def test_chunk_state_passing_unsupported_and_no_final():
+    say("chunk_state_passing unsupported / no final")
+    inp = make_inputs(1, 128, 2, 48, 64, 1, 64, in_dtype="bf16", seed=14)  # P = 48: not a multiple of 64
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    with pytest.raises(SSDError):
+        ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA)
+    inp = make_inputs(1, 128, 2, 64, 64, 1, 64, in_dtype="bf16", seed=14)
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    with pytest.raises(SSDError):
+        ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA, mma="f32")
+    car, fin = ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA, want_final=False)
+    car2, fin2 = ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA)
+    torch.cuda.synchronize()
+    assert fin is None and torch.equal(car, car2)
 
 
 @pytest.mark.parametrize("mma", ["f32", "bf16"])
