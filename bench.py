@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--mma", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-batch", type=int, default=64,
+                    help="sequences in the timed single-token decode step (0: skip it)")
     ap.add_argument("--kernel-only", default=None,
                     help="time only this ABI call in the per-kernel loop (for profiling)")
     args = ap.parse_args()
@@ -245,6 +247,36 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(dk["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None}
 
+    # Single-token decode step at the same layer shape: DECODE_BATCH sequences,
+    # one token each, fp32 state advanced in place (8 N P bytes per (b, h)).
+    dec = None
+    if args.decode_batch > 0:
+        DB = args.decode_batch
+        g = torch.Generator(device=dev).manual_seed(7)
+        io_dt = torch.bfloat16 if w.in_dtype == "bf16" else torch.float32
+        xd = torch.randn((DB, H, P), device=dev, generator=g).to(io_dt)
+        dtd = torch.nn.functional.softplus(torch.randn((DB, H), device=dev, generator=g) - 2.0)
+        Bd = torch.randn((DB, G, N), device=dev, generator=g).to(io_dt)
+        Cd = torch.randn((DB, G, N), device=dev, generator=g).to(io_dt)
+        sd = torch.randn((DB, H, N, P), device=dev, generator=g)
+        yd = torch.empty((DB, H, P), device=dev, dtype=io_dt)
+        step_d = lambda: ops.ssd_decode_step(xd, dtd, t["A"], Bd, Cd, t["D"], sd, y=yd)
+        for _ in range(20):
+            step_d()
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.steps):
+            step_d()
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dus = 1e3 * d0.elapsed_time(d1) / args.steps
+        dbytes = 8 * DB * H * N * P + xd.element_size() * (2 * DB * H * P + 2 * DB * G * N) + 4 * DB * H + 8 * H
+        dec = {"batch": DB, "us": round(dus, 2), "tokens_per_s": round(DB / (dus * 1e-6), 1),
+               "alg_bytes": dbytes, "GBps": round(dbytes / (dus * 1e-6) / 1e9, 1),
+               "hbm_frac": round(dbytes / (dus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+        del xd, dtd, Bd, Cd, sd, yd
+
     # One elementwise copy of 512 MiB (a single kernel dispatch): its measured
     # rate is the practical HBM ceiling, and under rocprofv3 --pmc its
     # FETCH_SIZE / WRITE_SIZE per dispatch (known to be 512 MiB each)
@@ -288,6 +320,7 @@ def main():
         "state_path": "fused" if fused else "two-kernel",
         "other_path": other,
         "copy_GBps": round(copy_gbps, 1),
+        "decode_step": dec,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w)

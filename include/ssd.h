@@ -159,6 +159,28 @@ ssd_status ssd_chunk_scan(const ssd_shape* shape, const void* x, const void* Bm,
                           ssd_dtype y_dtype, ssd_mma mma, void* stream);
 
 /*
+ * Single-token recurrent step, the decode form of the same recurrence (P1,
+ * opening paragraph: a fixed-size hidden state updated once per token, so
+ * each new token costs the same; jump-formula paragraph: the update is a
+ * decay of the state plus the outer product of b and x).  Per (b,h), with
+ * g = h / (H/G):
+ *   r = exp(dt[b,h] A[h])
+ *   state[b,h] = r state[b,h] + dt[b,h] Bm[b,g,:] x[b,h,:]^T      (N x P, fp32, in place)
+ *   y[b,h,:]   = Cm[b,g,:]^T state[b,h] + D[h] x[b,h,:]
+ * i.e. ssd_forward over one token with initial_states = state, final_states
+ * written back into state.  shape->seqlen must be 1; shape->chunk is not
+ * used.  x [B,H,P] and Bm, Cm [B,G,N] in `in`; dt [B,H], A [H], D [H] fp32;
+ * state [B,H,N,P] fp32 (read, then overwritten: caller-owned, must not
+ * alias the other arguments); y [B,H,P] in y_dtype (bf16 rounded to nearest
+ * even).  Supported: P a multiple of 4, P <= 1024 (else
+ * SSD_ERR_UNSUPPORTED); other shape errors as for the other calls.  All
+ * pointers 16-byte aligned.  Asynchronous on `stream`.
+ */
+ssd_status ssd_decode_step(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+                           const void* Bm, const void* Cm, const float* D, ssd_dtype in, float* state,
+                           void* y, ssd_dtype y_dtype, void* stream);
+
+/*
  * Bytes of device workspace ssd_forward needs for `shape`: dA_cumsum and
  * dt_bhl (fp32 [B,H,nc,Q] each), the chunk states (fp32 [B,nc,H,N,P]) and a
  * bf16 copy of the carried states ([B,nc,H,N,P]), each 256-byte aligned.

@@ -164,6 +164,26 @@ ssd_status ssd_chunk_state_passing(const ssd_shape* shape, const void* x, const 
                                           carried_dtype == SSD_BF16, final_states, (hipStream_t)stream));
 }
 
+ssd_status ssd_decode_step(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* Bm,
+                           const void* Cm, const float* D, ssd_dtype in, float* state, void* y, ssd_dtype y_dtype,
+                           void* stream) {
+  if (!shape) return SSD_ERR_NULL;
+  const ssd_shape* s = shape;
+  if (s->batch <= 0 || s->nheads <= 0 || s->headdim <= 0 || s->dstate <= 0 || s->ngroups <= 0 || s->seqlen != 1)
+    return SSD_ERR_SHAPE;
+  if (s->nheads % s->ngroups != 0) return SSD_ERR_SHAPE;
+  SSD_TRY(check_dtype(in));
+  SSD_TRY(check_dtype(y_dtype));
+  if (!ssd::decode_step_supported(s->headdim)) return SSD_ERR_UNSUPPORTED;
+  if (s->batch * s->nheads > 0x7fffffff || s->dstate > 0x7fffffff / s->headdim) return SSD_ERR_UNSUPPORTED;
+  if (!x || !dt || !A || !Bm || !Cm || !D || !state || !y) return SSD_ERR_NULL;
+  if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(Bm) || !aligned16(Cm) || !aligned16(D) ||
+      !aligned16(state) || !aligned16(y))
+    return SSD_ERR_ALIGN;
+  return from_hip(ssd::launch_decode_step(s->batch, s->nheads, s->headdim, s->dstate, s->ngroups, x, dt, A, Bm, Cm,
+                                          D, in == SSD_BF16, state, y, y_dtype == SSD_BF16, (hipStream_t)stream));
+}
+
 ssd_status ssd_chunk_scan(const ssd_shape* shape, const void* x, const void* Bm, const void* Cm, ssd_dtype in,
                           const float* dt_bhl, const float* dA_cumsum, const void* carried, ssd_dtype carried_dtype,
                           const float* D, void* y, ssd_dtype y_dtype, ssd_mma mma, void* stream) {

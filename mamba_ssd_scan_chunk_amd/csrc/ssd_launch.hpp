@@ -72,4 +72,11 @@ hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* Bm, const
                              const float* dt_bhl, const float* dA_cumsum, const void* carried, bool carried_bf16,
                              const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream);
 
+// Single-token recurrent step: state [Bn,H,N,P] fp32 updated in place, y
+// [Bn,H,P].  Supported for P a multiple of 4 up to 1024.
+bool decode_step_supported(int64_t P);
+hipError_t launch_decode_step(int64_t Bn, int64_t H, int64_t P, int64_t N, int64_t G, const void* x,
+                              const float* dt, const float* A, const void* Bm, const void* Cm, const float* D,
+                              bool in_bf16, float* state, void* y, bool y_bf16, hipStream_t stream);
+
 }  // namespace ssd

@@ -179,6 +179,34 @@ def ssd_chunk_scan(shape, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y=None, y_dt
     return y
 
 
+def ssd_decode_step(x, dt, A, Bm, Cm, D, state, y=None, y_dtype=None, stream=None):
+    """One token per sequence: ``state`` [B,H,N,P] fp32 is advanced in place,
+    returns y [B,H,P] in ``y_dtype`` (default: x's dtype).  x [B,H,P], dt
+    [B,H], A [H], Bm/Cm [B,G,N] (x's dtype), D [H]."""
+    if x.dim() != 3 or Bm.dim() != 3 or state.dim() != 4:
+        raise ValueError("x must be [B,H,P], Bm/Cm [B,G,N], state [B,H,N,P]")
+    B, H, P = x.shape
+    G, N = Bm.shape[1], Bm.shape[2]
+    io = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _req(x, "x", (B, H, P), io)
+    _req(dt, "dt", (B, H), f32)
+    _req(A, "A", (H,), f32)
+    _req(Bm, "Bm", (B, G, N), (x.dtype,))
+    _req(Cm, "Cm", (B, G, N), (x.dtype,))
+    _req(D, "D", (H,), f32)
+    _req(state, "state", (B, H, N, P), f32)
+    ydt = x.dtype if y_dtype is None else (_DTNAME[y_dtype] if isinstance(y_dtype, str) else y_dtype)
+    if y is None:
+        y = torch.empty((B, H, P), device=x.device, dtype=ydt)
+    _req(y, "y", (B, H, P), io)
+    sh = SSDShape.make(B, 1, H, P, N, G, 1)
+    lib = load_library()
+    check(lib.ssd_decode_step(sh, _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _DT[x.dtype],
+                              _ptr(state), _ptr(y), _DT[y.dtype], _stream(stream)))
+    return y
+
+
 def ssd_workspace_bytes(shape) -> int:
     return int(load_library().ssd_workspace_bytes(_shape(shape)))
 

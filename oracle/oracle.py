@@ -16,8 +16,9 @@ paragraph: the update is an outer product b x^T plus a multiplicative decay):
     h_t = exp(dt_t * A_h) * h_{t-1} + dt_t * B_t x_t^T      (N x P per head)
     y_t = C_t^T h_t + D_h * x_t
 
-This module loads that library through ctypes and adds two definitional
-helpers that need no recurrence:
+This module loads that library through ctypes (``Oracle.decode_step`` is the
+same recurrence over one token) and adds two definitional helpers that need no
+recurrence:
 
 * ``dA_cumsum_ref``: the in-chunk inclusive sum of dt*A (P1 paragraph on the
   three kernels: per-token, per-head cumulative sums of the decay term inside
@@ -128,6 +129,18 @@ class Oracle:
         y, fin, _ = self.recurrence(x, dt, A, Bm, Cm, D, h0, nthreads=nthreads)
         y = y.reshape(Bsz, H, L, P).transpose(0, 2, 1, 3)
         return np.ascontiguousarray(y), fin.reshape(Bsz, H, N, P)
+
+    def decode_step(self, x, dt, A, Bm, Cm, D, state, nthreads=None):
+        """One token per sequence (P1 opening paragraph: the fixed-size state
+        is updated once per token): the recurrence run over a single token
+        from ``state``.  x [B,H,P], dt [B,H], Bm/Cm [B,G,N], state [B,H,N,P].
+        Returns (y [B,H,P], new state [B,H,N,P]) in fp64; no arithmetic of its
+        own beyond the recurrence."""
+        Bsz, H, P = x.shape
+        G, N = Bm.shape[1], Bm.shape[2]
+        y, fin = self.forward(np.asarray(x)[:, None], np.asarray(dt)[:, None], A, np.asarray(Bm)[:, None],
+                              np.asarray(Cm)[:, None], D, h0=state, nthreads=nthreads)
+        return y[:, 0], fin
 
     def forward_pairs(self, x, dt, A, Bm, Cm, D, pairs, h0=None, chunk=0, nthreads=None):
         """y [npairs,L,P], final [npairs,N,P] and (if chunk>0) the states entering

@@ -138,6 +138,23 @@ def pin_split_chaining(o):
     return e <= TOL, f"max rel err {e:.3g}"
 
 
+def pin_decode_chain(o):
+    """Single-token steps (``Oracle.decode_step``, P1 opening paragraph: the
+    state is updated once per token) chained from an initial state reproduce
+    the brute-force semiseparable form over the whole sequence, token by token
+    and in the final state (groups and skip included)."""
+    inp = make_inputs(2, 12, 4, 3, 5, 2, 4, seed=41, dt_shift=0.5)
+    h0 = _h0(inp)
+    ys, fs = forms.semiseparable_forward(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D, h0)
+    st = h0
+    worst = 0.0
+    for t in range(inp.x.shape[1]):
+        y, st = o.decode_step(inp.x[:, t], inp.dt[:, t], inp.A, inp.Bm[:, t], inp.Cm[:, t], inp.D, st)
+        worst = max(worst, rel(y, ys[:, t]))
+    worst = max(worst, rel(st, fs))
+    return worst <= TOL, f"max rel err {worst:.3g}"
+
+
 def pin_linearity(o):
     """y and the final state are linear in x (with dt, A, B, C, D fixed)."""
     a = make_inputs(1, 30, 2, 4, 3, 1, 6, seed=23)
@@ -230,6 +247,6 @@ def pin_golden(o):
 
 
 ALL_PINS = [pin_semiseparable, pin_zero_decay, pin_geometric, pin_single_token, pin_skip_only,
-            pin_chunk_invariance, pin_chunk_intermediates, pin_split_chaining, pin_linearity,
+            pin_chunk_invariance, pin_chunk_intermediates, pin_split_chaining, pin_decode_chain, pin_linearity,
             pin_causality, pin_head_permutation, pin_group_expansion, pin_memoryless,
             pin_pairs_and_threads, pin_golden]

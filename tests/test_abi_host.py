@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     for n in ["ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward",
-              "ssd_workspace_bytes", "ssd_status_string", "ssd_abi_version"]:
+              "ssd_chunk_state_passing", "ssd_decode_step", "ssd_workspace_bytes", "ssd_status_string",
+              "ssd_abi_version"]:
         assert n in names
 
 
@@ -154,6 +155,30 @@ def test_chunk_state_passing_checks(lib):
                                        None) == UNSUP
     assert lib.ssd_chunk_state_passing(shape(batch=0), FAKE, FAKE, 1, FAKE, FAKE, None, FAKE, 1, FAKE, 0,
                                        None) == SHAPE
+
+
+def test_decode_step_checks(lib):
+    """The decode step takes one token per sequence (seqlen 1; chunk unused)
+    and validates like the other calls, before any HIP call."""
+    s = shape(seqlen=1, chunk=0)
+    args = [FAKE] * 8
+    for i in range(8):
+        a = list(args)
+        a[i] = None
+        x, dt, A, Bm, Cm, D, st, y = a
+        assert lib.ssd_decode_step(s, x, dt, A, Bm, Cm, D, 1, st, y, 1, None) == NULL
+    assert lib.ssd_decode_step(None, *args[:6], 1, FAKE, FAKE, 1, None) == NULL
+    assert lib.ssd_decode_step(shape(seqlen=2), *args[:6], 1, FAKE, FAKE, 1, None) == SHAPE
+    assert lib.ssd_decode_step(shape(seqlen=1, nheads=6, ngroups=4), *args[:6], 1, FAKE, FAKE, 1, None) == SHAPE
+    assert lib.ssd_decode_step(shape(seqlen=1, batch=0), *args[:6], 1, FAKE, FAKE, 1, None) == SHAPE
+    assert lib.ssd_decode_step(s, *args[:6], 2, FAKE, FAKE, 1, None) == DTYPE
+    assert lib.ssd_decode_step(s, *args[:6], 1, FAKE, FAKE, 9, None) == DTYPE
+    assert lib.ssd_decode_step(shape(seqlen=1, headdim=6), *args[:6], 1, FAKE, FAKE, 1, None) == UNSUP
+    assert lib.ssd_decode_step(shape(seqlen=1, headdim=1028), *args[:6], 1, FAKE, FAKE, 1, None) == UNSUP
+    # shapes the chunked calls refuse are fine here: P = 20, N = 7, any chunk value
+    odd = FAKE + 4
+    assert lib.ssd_decode_step(shape(seqlen=1, headdim=20, dstate=7), *args[:6], 1, odd, FAKE, 1, None) == ALIGN
+    assert lib.ssd_decode_step(s, odd, *args[1:6], 1, FAKE, FAKE, 1, None) == ALIGN
 
 
 def test_bf16_carried_has_no_in_place_form(lib):
