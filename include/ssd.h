@@ -12,7 +12,7 @@
  * h_t (N x P) and output y_t (P) follow
  *     h_t = exp(dt[b,t,h] A[h]) h_{t-1} + dt[b,t,h] B[b,t,g,:] x[b,t,h,:]^T
  *     y_t = C[b,t,g,:]^T h_t + D[h] x[b,t,h,:]
- * evaluated chunk by chunk (chunk length Q, nc = L/Q chunks) in the three
+ * evaluated chunk by chunk (chunk length Q, nc = ceil(L/Q) chunks) in the three
  * steps P1 describes in its paragraph on the three kernels: a log-space
  * cumulative sum of the decay term, the jump-formula state advance across
  * chunks, and the fused output (carried-state term, decayed causally masked
@@ -37,7 +37,11 @@
  *     or BF16).
  *   - Shape limits of this version (else SSD_ERR_UNSUPPORTED): headdim P and
  *     dstate N multiples of 16 with N <= 256 and P <= 256; chunk Q in
- *     {32, 64, 128, 256}; seqlen L a multiple of Q.
+ *     {32, 64, 128, 256}.  L need not be a multiple of Q: the last chunk is
+ *     then ragged (L - (nc-1) Q tokens).  The per-chunk layouts keep Q
+ *     positions per chunk; positions past the end of the sequence count as
+ *     tokens with dt = 0 (dt_bhl 0, dA_cumsum constant at its last value),
+ *     which adds nothing to any state or output.
  *
  * Precision modes (ssd_mma): SSD_MMA_BF16 rounds the matrix-core operands
  * (the decay-scaled x rows, the decayed interaction tile, the carried state)

@@ -9,6 +9,7 @@
 //
 //   dA_cumsum[b,h,c,i] = sum_{k<=i} dt[b,cQ+k,h] * A[h]      (fp32, inclusive)
 //   dt_bhl[b,h,c,i]    = dt[b,cQ+i,h]
+// with dt = 0 for tokens cQ+i >= L (ragged last chunk).
 //
 // One wave owns (b, c, heads 4q..4q+3).  Lane l holds the E = Q/64
 // consecutive tokens lE..lE+E-1 of all four heads (16-byte loads of dt when
@@ -44,9 +45,12 @@ __global__ __launch_bounds__(kCsThreads) void chunk_cumsum_kernel(
 
   float dv[4][4];  // [token e][head k]
   const int64_t row0 = (int64_t)b * L + (int64_t)c * Q;
+  // tokens past the end of the sequence (a ragged last chunk) count as dt = 0:
+  // dt_bhl is 0 there and dA_cumsum stays at its last value
+  const int nvalid = L - c * Q;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const bool ok = e < E && lane < active;
+    const bool ok = e < E && lane < active && lane * E + e < nvalid;
     const int64_t row = row0 + lane * E + e;
     if (ok && vec) {
       const float4 v = *reinterpret_cast<const float4*>(dt + row * H + h0);

@@ -83,6 +83,10 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 
   const int64_t bhc = ((int64_t)b * H + h) * nc + c;
   const int64_t tok0 = (int64_t)b * L + (int64_t)c * Q;
+  // Rows past the end of the sequence (ragged last chunk) re-read the last
+  // row: their dt = 0 zeroes them as interaction columns, and their outputs
+  // are not stored.
+  const int rmax = min(Q, L - c * Q) - 1;
 
   for (int j = tid; j < row_end; j += kScanThreads) {
     Gs[j] = dA_cumsum[bhc * Q + j];
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const int n = 32 * s + 8 * lg;
     if (active && n < N) {
       float t[8];
-      load8_as_f32(Cm, ((tok0 + i0 + l16) * G + g) * N + n, bf, t);
+      load8_as_f32(Cm, ((tok0 + min(i0 + l16, rmax)) * G + g) * N + n, bf, t);
       cf[s] = Op::from_f32(t);
     } else {
       cf[s] = Op::zero();
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
       const int n = 8 * nb;
       float t[8];
       if (n < N) {
-        load8_as_f32(Bm, ((tok0 + j0 + j) * G + g) * N + n, bf, t);
+        load8_as_f32(Bm, ((tok0 + min(j0 + j, rmax)) * G + g) * N + n, bf, t);
       } else {
 #pragma unroll
         for (int q = 0; q < 8; ++q) t[q] = 0.f;
@@ -173,7 +177,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
       const int jb = blk & 3, pb = blk >> 2;
       float v[8][8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) load8_as_f32(x, ((tok0 + j0 + 8 * jb + r) * H + h) * P + p0 + 8 * pb, bf, v[r]);
+      for (int r = 0; r < 8; ++r)
+        load8_as_f32(x, ((tok0 + min(j0 + 8 * jb + r, rmax)) * H + h) * P + p0 + 8 * pb, bf, v[r]);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         float col[8];
@@ -226,6 +231,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        if (i0 + 4 * lg + r > rmax) continue;
         const int64_t off = ((tok0 + i0 + 4 * lg + r) * H + h) * P + p0 + 16 * ct + l16;
         const float v = acc[ct][r] + dsk * load1_as_f32(x, off, bf);
         if (y_bf16)

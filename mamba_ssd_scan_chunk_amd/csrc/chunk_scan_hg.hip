@@ -99,7 +99,7 @@ __device__ __forceinline__ int npos(int n) {
   return (n & ~31) | ((n & 12) << 1) | ((n & 16) >> 2) | (n & 3);
 }
 
-template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16>
+template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED>
 __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, const int tid) {
   using Cfg = HgCfg<Q, NK, CT>;
   using Op = OpBF16;
@@ -128,6 +128,11 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   const int H = a.H, P = a.P, G = a.G, nc = a.nc;
   const int64_t tok0 = a.tok0;
   const int HP = H * P;
+  // RAGGED (L % Q != 0): rows past the end of the sequence re-read its last
+  // row (their dt = 0 zeroes them as interaction columns) and their outputs
+  // are not stored
+  const int rmax = RAGGED ? min(Q, a.L - a.c * Q) - 1 : Q - 1;
+  auto rowc = [&](int r) { return RAGGED ? min(r, rmax) : r; };
 
   // ---- phase 0: B and C chunks -> Bs, Cs ([token][npos(n)], bf16).  A
   // 16-byte piece holds n = 8nb .. 8nb+7, whose two 4-element halves land at
@@ -137,7 +142,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     const int GN = G * N;
     for (int idx = tid; idx < Q * (N / 8); idx += T) {
       const int j = idx / (N / 8), nb = idx - (idx / (N / 8)) * (N / 8);
-      const int off = j * GN + 8 * nb;
+      const int off = rowc(j) * GN + 8 * nb;
       const int q0 = j * NPI + npos(8 * nb), q1 = j * NPI + npos(8 * nb + 4);
       const uint4 bv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Bm) + bc0 + off);
       const uint4 cv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Cm) + bc0 + off);
@@ -199,7 +204,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       if (blk < NXB) {  // always true; the block boundary keeps the scheduler from hoisting across it
         int row, cb;
         xmap(blk, row, cb);
-        xv[uu] = *reinterpret_cast<const uint4*>(xh + row * HP + 8 * cb);
+        xv[uu] = *reinterpret_cast<const uint4*>(xh + rowc(row) * HP + 8 * cb);
       }
     }
     // every thread loads (and later stores) the values of token tid mod Q:
@@ -359,6 +364,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   auto store_tile = [&](const int tile, const f32x4_t (&acc)[CT], int h, float dsk, int ln) {
     const int l16 = ln & 15, lg = ln >> 4;
     const int i = 16 * tile + l16;
+    if (RAGGED && i > rmax) return;
     const int64_t ybase = (tok0 * H + h) * (int64_t)P + a.p0;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -451,7 +457,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 // Y_BF16 is a template parameter rather than a run-time flag: a branch around
 // the output stores would make the compiler's memory-counter waits for the
 // prefetched loads conservative (they would also wait for the stores).
-template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16>
+template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED>
 __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, const void* __restrict__ Cm,
     const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const void* __restrict__ carried,
@@ -478,7 +484,7 @@ __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
   a.hbase = a.g * (H / G) + hgi * HG;
   a.p0 = pt * HgCfg<Q, NK, CT>::PT;
   a.tok0 = (int64_t)a.b * L + (int64_t)a.c * Q;
-  hg_body<Q, NK, CT, H_BF16, Y_BF16>(a, hg_smem, threadIdx.x);
+  hg_body<Q, NK, CT, H_BF16, Y_BF16, RAGGED>(a, hg_smem, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ host side
@@ -516,7 +522,11 @@ static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, c
                                  bool y_bf16, hipStream_t stream) {
   constexpr int CT = 4;
   using Cfg = HgCfg<Q, NK, CT>;
-  auto kern = y_bf16 ? chunk_scan_hg_kernel<Q, NK, CT, H_BF16, true> : chunk_scan_hg_kernel<Q, NK, CT, H_BF16, false>;
+  const bool ragged = d.L % Q != 0;
+  auto kern = y_bf16 ? (ragged ? chunk_scan_hg_kernel<Q, NK, CT, H_BF16, true, true>
+                               : chunk_scan_hg_kernel<Q, NK, CT, H_BF16, true, false>)
+                     : (ragged ? chunk_scan_hg_kernel<Q, NK, CT, H_BF16, false, true>
+                               : chunk_scan_hg_kernel<Q, NK, CT, H_BF16, false, false>);
   const size_t lds = Cfg::lds_total;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -73,6 +73,9 @@ __global__ __launch_bounds__(kCsThreadsState) void chunk_state_kernel(
 
   const int NT = N / 16;
   const int64_t tok0 = (int64_t)b * L + (int64_t)c * Q;
+  // rows past the end of the sequence (ragged last chunk) re-read the last
+  // one; their weight w = exp(.) * dt is 0
+  const int rmax = min(Q, L - c * Q) - 1;
   const int nbB = (kStateKS / 8) * (N / 8);
   const int nbX = (kStateKS / 8) * (PT / 8);
 
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(kCsThreadsState) void chunk_state_kernel(
         const int jb = blk & 3, cb = blk >> 2;
 #pragma unroll
         for (int r = 0; r < 8; ++r)
-          load8_as_f32(Bm, ((tok0 + k0 + 8 * jb + r) * G + g) * N + 8 * cb, bf, v[r]);
+          load8_as_f32(Bm, ((tok0 + min(k0 + 8 * jb + r, rmax)) * G + g) * N + 8 * cb, bf, v[r]);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           float col[8];
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(kCsThreadsState) void chunk_state_kernel(
         const int jb = bx & 3, cb = bx >> 2;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          load8_as_f32(x, ((tok0 + k0 + 8 * jb + r) * H + h) * P + p0 + 8 * cb, bf, v[r]);
+          load8_as_f32(x, ((tok0 + min(k0 + 8 * jb + r, rmax)) * H + h) * P + p0 + 8 * cb, bf, v[r]);
           const float w = w_s[k0 + 8 * jb + r];
 #pragma unroll
           for (int q = 0; q < 8; ++q) v[r][q] *= w;

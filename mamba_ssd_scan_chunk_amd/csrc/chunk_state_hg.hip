@@ -86,6 +86,9 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   const int64_t tok0 = (int64_t)b * L + (int64_t)c * Q;
   const int tid = threadIdx.x, wave = tid >> 6;
   const int HP = H * P;
+  // last token row of the chunk inside the sequence: rows past it (ragged last
+  // chunk) re-read this one, and their dt = 0 zeroes their contribution
+  const int rmax = min(Q, L - c * Q) - 1;
 
   // ---- per-head register prefetch of x pieces and their G, dt
   // Piece blk -> (row, 8-column block cb): 8 consecutive threads take the 8
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     for (int u = 0; u < XPT; ++u) {
       int row, cb;
       xmap(tid + u * T, row, cb);
-      xv[u] = *reinterpret_cast<const uint4*>(xs + row * HP + 8 * cb);
+      xv[u] = *reinterpret_cast<const uint4*>(xs + min(row, rmax) * HP + 8 * cb);
     }
     if constexpr (FUSE) {
       hcur = h - hbase;
@@ -156,7 +159,8 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     const int GN = G * N;
     for (int blk = tid; blk < Q * (N / 8); blk += T) {
       const int j = blk / (N / 8), cb = blk % (N / 8);
-      *reinterpret_cast<uint4*>(Bn + j * BP + 8 * cb) = *reinterpret_cast<const uint4*>(bsrc + j * GN + 8 * cb);
+      *reinterpret_cast<uint4*>(Bn + j * BP + 8 * cb) =
+          *reinterpret_cast<const uint4*>(bsrc + min(j, rmax) * GN + 8 * cb);
     }
   }
 
@@ -169,7 +173,8 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
       const int hq = HG / 4;
       for (int idx = tid; idx < Q * hq; idx += T) {
         const int i = idx / hq, q4 = idx - i * hq;
-        const float4 v = *reinterpret_cast<const float4*>(dt_raw + (tok0 + i) * H + hbase + 4 * q4);
+        const float4 v = i <= rmax ? *reinterpret_cast<const float4*>(dt_raw + (tok0 + i) * H + hbase + 4 * q4)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
         Dsa[(4 * q4 + 0) * Q + i] = v.x;
         Dsa[(4 * q4 + 1) * Q + i] = v.y;
         Dsa[(4 * q4 + 2) * Q + i] = v.z;
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     } else {
       for (int idx = tid; idx < Q * HG; idx += T) {
         const int i = idx / HG, hh = idx - i * HG;
-        Dsa[hh * Q + i] = dt_raw[(tok0 + i) * H + hbase + hh];
+        Dsa[hh * Q + i] = i <= rmax ? dt_raw[(tok0 + i) * H + hbase + hh] : 0.f;
       }
     }
     __syncthreads();

@@ -27,11 +27,12 @@ ssd_status check_shape(const ssd_shape* s, Dims* d) {
   if (s->headdim % 16 != 0 || s->dstate % 16 != 0 || s->headdim > 256 || s->dstate > 256)
     return SSD_ERR_UNSUPPORTED;
   if (s->chunk != 32 && s->chunk != 64 && s->chunk != 128 && s->chunk != 256) return SSD_ERR_UNSUPPORTED;
-  if (s->seqlen % s->chunk != 0) return SSD_ERR_UNSUPPORTED;
+  // a ragged last chunk (seqlen % chunk != 0) is allowed: nc = ceil(seqlen / chunk)
+  const int64_t nc = (s->seqlen + s->chunk - 1) / s->chunk;
   // keep every element offset comfortably inside 32-bit grid dimensions
-  if (s->seqlen / s->chunk > 65535 || s->batch > 65535 || s->nheads > 65535) return SSD_ERR_UNSUPPORTED;
+  if (nc > 65535 || s->batch > 65535 || s->nheads > 65535) return SSD_ERR_UNSUPPORTED;
   d->B = s->batch; d->L = s->seqlen; d->H = s->nheads; d->P = s->headdim;
-  d->N = s->dstate; d->G = s->ngroups; d->Q = s->chunk; d->nc = s->seqlen / s->chunk;
+  d->N = s->dstate; d->G = s->ngroups; d->Q = s->chunk; d->nc = nc;
   return SSD_OK;
 }
 

@@ -144,18 +144,20 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void state_fused_kernel(
   auto issue_x = [&](XSet& st, int c) __attribute__((always_inline)) {
     if (loader) {
       const int64_t tok0 = (int64_t)b * L + (int64_t)c * Q;
+      const int rmax = min(Q, L - c * Q) - 1;  // rows past the sequence end re-read the last (dt = 0 there)
       const uint16_t* xs = x + (tok0 * H + h) * (int64_t)P + p0 + 8 * cbp;
 #pragma unroll
-      for (int u = 0; u < RPT; ++u) st.xv[u] = *reinterpret_cast<const uint4*>(xs + (rbase + u) * HP);
+      for (int u = 0; u < RPT; ++u) st.xv[u] = *reinterpret_cast<const uint4*>(xs + min(rbase + u, rmax) * HP);
     }
     if constexpr (GD2) load_g(st.g, c);
   };
   auto issue_b = [&](int c) __attribute__((always_inline)) {
     if (loader) {
       const int64_t tok0 = (int64_t)b * L + (int64_t)c * Q;
+      const int rmax = min(Q, L - c * Q) - 1;
       const uint16_t* bs = Bm + (tok0 * G + g) * (int64_t)N + n0 + 8 * cbp;
 #pragma unroll
-      for (int u = 0; u < RPT; ++u) bv[u] = *reinterpret_cast<const uint4*>(bs + (rbase + u) * GN);
+      for (int u = 0; u < RPT; ++u) bv[u] = *reinterpret_cast<const uint4*>(bs + min(rbase + u, rmax) * GN);
     }
     if constexpr (!GD2) load_g(g1, c);
   };

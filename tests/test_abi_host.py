@@ -59,7 +59,7 @@ def shape(**kw):
     (dict(batch=0), SHAPE), (dict(seqlen=0), SHAPE), (dict(nheads=-1), SHAPE), (dict(headdim=0), SHAPE),
     (dict(dstate=0), SHAPE), (dict(ngroups=0), SHAPE), (dict(chunk=0), SHAPE), (dict(nheads=6, ngroups=4), SHAPE),
     (dict(headdim=24), UNSUP), (dict(dstate=40), UNSUP), (dict(headdim=272), UNSUP), (dict(dstate=272), UNSUP),
-    (dict(chunk=16), UNSUP), (dict(chunk=96), UNSUP), (dict(chunk=512), UNSUP), (dict(seqlen=500), UNSUP),
+    (dict(chunk=16), UNSUP), (dict(chunk=96), UNSUP), (dict(chunk=512), UNSUP),
 ])
 def test_shape_checks(lib, kw, code):
     s = shape(**kw)
@@ -188,6 +188,18 @@ def test_bf16_carried_has_no_in_place_form(lib):
     the GPU side)."""
     s = shape()
     assert lib.ssd_state_passing(s, FAKE, FAKE, 1, FAKE, None, FAKE, None) == UNSUP
+
+
+def test_ragged_last_chunk_is_a_valid_shape(lib):
+    """seqlen need not be a multiple of chunk: nc = ceil(L / Q) chunks of Q
+    positions (the workspace is sized for them; no call is launched here)."""
+    B, L, H, P, N, Q = 2, 500, 4, 64, 128, 256
+    nc = 2
+    bhl = 4 * B * H * nc * Q
+    st = 4 * B * nc * H * N * P
+    ru = lambda v: (v + 255) // 256 * 256
+    assert lib.ssd_workspace_bytes(shape(seqlen=L)) == ru(ru(ru(ru(bhl) + bhl) + st) + st // 2)
+    assert lib.ssd_workspace_bytes(shape(seqlen=1)) > 0
 
 
 def test_workspace(lib):

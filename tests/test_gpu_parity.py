@@ -30,6 +30,10 @@ SHAPES = [
     ("n256", 1, 256, 4, 64, 256, 2, 128),
     ("q32_h20", 1, 96, 20, 32, 32, 4, 32),
     ("p128", 1, 256, 2, 128, 64, 1, 128),
+    # ragged last chunk (L % Q != 0): head-group kernels, then generic ones
+    ("ragged_q256", 2, 300, 4, 64, 128, 1, 256),
+    ("ragged_q128_n256", 1, 130, 4, 64, 256, 2, 128),
+    ("ragged_q64", 1, 200, 3, 48, 48, 3, 64),
 ]
 MODES = [("f32", "f32"), ("bf16", "f32"), ("f32", "bf16"), ("bf16", "bf16")]  # (input dtype, mma)
 
@@ -60,6 +64,11 @@ def test_chunk_cumsum(shape):
     dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
     torch.cuda.synchronize()
     ref = dA_cumsum_ref(inp.dt, inp.A, inp.chunk)
+    # positions past a ragged end hold the last valid sum (the ABI's layout
+    # convention: missing tokens count as dt = 0)
+    name, B, L, H, P, N, G, Q = shape
+    nc, q = -(-L // Q), L - (-(-L // Q) - 1) * Q
+    ref[:, :, nc - 1, q:] = ref[:, :, nc - 1, q - 1:q]
     assert relerr(dA, ref) <= TOL_CUMSUM
     # all terms share a sign, so the error is also small elementwise
     g = dA.double().cpu().numpy()
@@ -238,23 +247,25 @@ def test_forward_stress(case, mma):
     assert e1 <= tol_for(mma) and e2 <= tol_for(mma)
 
 
+@pytest.mark.parametrize("L,k", [(1024, 512), (1000, 333)], ids=["aligned", "ragged"])
 @pytest.mark.parametrize("mma", ["f32", "bf16"])
-def test_split_chaining(mma):
+def test_split_chaining(mma, L, k):
     """final states of the first part fed as initial states of the second part
-    reproduce the unsplit run (sequence resume)."""
-    say(f"split chaining {mma}")
-    B, L, H, P, N, G, Q = 2, 1024, 4, 64, 128, 1, 256
+    reproduce the unsplit run (sequence resume), also when the split and the
+    ends are not chunk-aligned (every part then has a ragged last chunk)."""
+    say(f"split chaining {mma} L={L} k={k}")
+    B, H, P, N, G, Q = 2, 4, 64, 128, 1, 256
     inp = make_inputs(B, L, H, P, N, G, Q, in_dtype="bf16", seed=8, dt_shift=4.0)
     t = upload(inp)
-    k = 512
     sh_full = ops.shape_of(t, Q)
     part = lambda a, lo, hi: a[:, lo:hi].contiguous()
     sh_half = ops.SSDShape.make(B, k, H, P, N, G, Q)
+    sh_rest = ops.SSDShape.make(B, L - k, H, P, N, G, Q)
     y_full, f_full = ops.ssd_forward(sh_full, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], y_dtype="f32",
                                      mma=mma)
     y1, f1 = ops.ssd_forward(sh_half, part(t["x"], 0, k), part(t["dt"], 0, k), t["A"], part(t["Bm"], 0, k),
                              part(t["Cm"], 0, k), t["D"], y_dtype="f32", mma=mma)
-    y2, f2 = ops.ssd_forward(sh_half, part(t["x"], k, L), part(t["dt"], k, L), t["A"], part(t["Bm"], k, L),
+    y2, f2 = ops.ssd_forward(sh_rest, part(t["x"], k, L), part(t["dt"], k, L), t["A"], part(t["Bm"], k, L),
                              part(t["Cm"], k, L), t["D"], initial_states=f1, y_dtype="f32", mma=mma)
     torch.cuda.synchronize()
     yref, fref = oracle().forward(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D)
@@ -266,6 +277,7 @@ def test_split_chaining(mma):
 # (name, B, L, H, P, N, G, Q): shapes of the bf16 head-group kernels, where the
 # one-call forward hands the carried states to the chunk scan as bf16
 HG_SHAPES = [
+    ("ragged_q256", 2, 300, 6, 64, 128, 2, 256),
     ("q256_n128", 2, 768, 6, 64, 128, 2, 256),
     ("q128_n256", 1, 512, 4, 128, 256, 2, 128),
     ("q128_n128", 2, 384, 3, 64, 128, 1, 128),
@@ -309,6 +321,8 @@ def test_forward_bitwise_equals_split_calls(shape, y_dtype):
 
 # (name, B, L, H, P, N, G, Q): shapes of the fused state path (N, P multiples of 64)
 FUSED_SHAPES = [
+    ("ragged_q256", 2, 300, 6, 64, 128, 2, 256),
+    ("ragged_q64", 1, 100, 2, 64, 64, 1, 64),
     ("q256_n128", 2, 768, 6, 64, 128, 2, 256),
     ("q128_n256", 1, 512, 4, 128, 256, 2, 128),
     ("q128_n128", 2, 384, 3, 64, 128, 1, 128),
