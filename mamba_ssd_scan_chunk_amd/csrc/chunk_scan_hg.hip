@@ -366,6 +366,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     const int i = 16 * tile + l16;
     if (RAGGED && i > rmax) return;
     const int64_t ybase = (tok0 * H + h) * (int64_t)P + a.p0;
+    uint2 w[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const int pc = 16 * ct + 4 * lg;
@@ -377,13 +378,18 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = acc[ct][r] + dsk * xr[r];
       if constexpr (Y_BF16) {
-        uint2 w;
-        w.x = pack_bf16x2(v[0], v[1]);
-        w.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + ybase + off) = w;
+        w[ct].x = pack_bf16x2(v[0], v[1]);
+        w[ct].y = pack_bf16x2(v[2], v[3]);
       } else {
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + ybase + off) = make_float4(v[0], v[1], v[2], v[3]);
       }
+    }
+    if constexpr (Y_BF16) {
+      // column tiles paired (0,1), (2,3): one 16-byte store per pair and lane
+#pragma unroll
+      for (int cp = 0; cp < CT / 2; ++cp)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.y) + ybase + i * HP + 32 * cp + pair_tiles_col(lg)) =
+            pair_tiles_16b(w[2 * cp], w[2 * cp + 1]);
     }
   };
 

@@ -204,6 +204,21 @@ __device__ __forceinline__ void chunk_cumsum_lane(const float (&d)[4], int E, fl
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 constexpr float kLog2e = 1.4426950408889634f;
 
+// 16-byte rows from MFMA accumulator tiles.  In the 16x16 accumulator layout
+// lane (l16, lg) holds 4 consecutive columns 4lg .. 4lg+3 of row l16 for each
+// column tile.  Given two column tiles t0 (columns 0..15) and t1 (16..31) of
+// the same rows, packed as 2 dwords each, one v_permlane16_swap per dword
+// trades them between the lane-row pairs (lg, lg ^ 1): afterwards each lane
+// holds 8 consecutive columns -- lg even: 4lg .. 4lg+7 of t0, lg odd:
+// 4(lg-1) .. +7 of t1, i.e. column 4lg + 12 (lg & 1) relative to t0 -- as
+// the returned uint4, ready for one 16-byte store.
+__device__ __forceinline__ uint4 pair_tiles_16b(uint2 t0, uint2 t1) {
+  const auto a = __builtin_amdgcn_permlane16_swap(t0.x, t1.x, false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(t0.y, t1.y, false, false);
+  return make_uint4(a[0], b[0], a[1], b[1]);
+}
+__device__ __forceinline__ int pair_tiles_col(int lg) { return 4 * lg + 12 * (lg & 1); }
+
 // Streaming (non-temporal) vector stores: the lines are not kept in L2.  Only
 // for outputs whose writes fill whole lines within a short time; scattered
 // partial-line writes this way cost more than through L2.

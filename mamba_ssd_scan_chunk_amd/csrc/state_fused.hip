@@ -182,9 +182,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void state_fused_kernel(
     }
   };
   // carried[b, c, h] = H_c (the running state), rounded to bf16 or fp32.  In
-  // bf16 the lane pairs (lg, lg ^ 1) first trade halves, so that each lane
-  // holds 8 consecutive columns of its row (even lg: tile 0, odd lg: tile 1)
-  // and one 16-byte store per lane writes the wave's 16 rows x 64 bytes.
+  // bf16 the lane-row pairs (lg, lg ^ 1) first trade halves (pair_tiles_16b),
+  // so that one 16-byte store per lane writes the wave's 16 rows x 64 bytes.
   auto store_carried = [&](int c) __attribute__((always_inline)) {
     const int64_t coff = ((int64_t)b * nc + c) * H + h;
 #pragma unroll
@@ -192,15 +191,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void state_fused_kernel(
       if constexpr (CBF16) {
         const uint2 t0 = make_uint2(pack_bf16x2(hs[rt][0].x, hs[rt][0].y), pack_bf16x2(hs[rt][0].z, hs[rt][0].w));
         const uint2 t1 = make_uint2(pack_bf16x2(hs[rt][1].x, hs[rt][1].y), pack_bf16x2(hs[rt][1].z, hs[rt][1].w));
-        const bool odd = lg & 1;
-        const uint2 give = odd ? t0 : t1;
-        uint2 got;
-        got.x = (uint32_t)__shfl_xor((int)give.x, 16, 64);
-        got.y = (uint32_t)__shfl_xor((int)give.y, 16, 64);
-        const uint4 v = odd ? make_uint4(got.x, got.y, t1.x, t1.y) : make_uint4(t0.x, t0.y, got.x, got.y);
-        // even lg: columns 4 lg .. +7 of tile 0; odd lg: 16 + 4 (lg - 1) .. +7
-        const int64_t o = coff * NP + soff + 16 * rt * P + (odd ? 16 - 4 : 0);
-        store_stream(static_cast<uint16_t*>(carried) + o, v);
+        // soff holds column 4 lg; the paired row starts at 4 lg + 12 (lg & 1)
+        const int64_t o = coff * NP + soff + 16 * rt * P + 12 * (lg & 1);
+        store_stream(static_cast<uint16_t*>(carried) + o, pair_tiles_16b(t0, t1));
       } else {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
