@@ -73,7 +73,24 @@ struct HgCfg {
   static constexpr size_t lds_a = lds_bs > lds_xh ? lds_bs : lds_xh;  // Bs, later Xn + Hn
   static constexpr size_t lds_c = (size_t)Q * NPI * 2;                // Cs
   static constexpr size_t lds_w = sizeof(float) * (size_t)(QT / 2) * Q;  // Ws
-  static constexpr size_t lds_total = lds_a + lds_c + lds_w + 2 * sizeof(float) * Q;
+  // DB (N = 128): the per-head tiles are double-buffered -- two buffers of
+  // Xn, Hn, Ws, Gs, dts, both aliasing the phase-0/1 Bs + Cs area, with the
+  // C fragments of C.H_in kept in registers -- so a head needs one barrier
+  // instead of two.  N = 256 keeps the single-buffer layout (its C fragments
+  // would not fit in registers).
+  static constexpr bool DB = NK == 4;
+  static constexpr size_t lds_buf = lds_xh + lds_w + 2 * sizeof(float) * Q;  // one buffer
+  static constexpr size_t lds_db = 2 * lds_bs > 2 * lds_buf ? 2 * lds_bs : 2 * lds_buf;
+  static constexpr size_t lds_total = DB ? lds_db : lds_a + lds_c + lds_w + 2 * sizeof(float) * Q;
+};
+
+// LDS tiles of one head: x, H_in, the column-factor table, G and dt
+struct HgBuf {
+  uint16_t* Xn;  // [Q][XNP]
+  uint16_t* Hn;  // [N][XNP]
+  float* Ws;     // [QT/2][Q]
+  float* Gs;     // [Q]
+  float* dts;    // [Q]
 };
 
 struct HgArgs {
@@ -116,13 +133,28 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   constexpr int NSL = QT + 1;                // CB^T sub-tiles held per wave
   static_assert(T % Q == 0 && (Q & (Q - 1)) == 0, "the G/dt staging assumes T is a multiple of Q");
 
-  uint16_t* Bs = reinterpret_cast<uint16_t*>(smem);                    // [Q][NPI]  (phase 0-1 only)
-  uint16_t* Xn = reinterpret_cast<uint16_t*>(smem);                    // [Q][XNP]  (aliases Bs later)
-  uint16_t* Hn = Xn + Q * XNP;                                          // [N][XNP]
-  uint16_t* Cs = reinterpret_cast<uint16_t*>(smem + Cfg::lds_a);        // [Q][NPI]
-  float* Ws = reinterpret_cast<float*>(smem + Cfg::lds_a + Cfg::lds_c);  // [QT/2][Q]
-  float* Gs = Ws + (QT / 2) * Q;                                        // [Q]
-  float* dts = Gs + Q;                                                  // [Q]
+  constexpr bool DB = Cfg::DB;
+  uint16_t* Bs = reinterpret_cast<uint16_t*>(smem);                                  // [Q][NPI]  (phase 0-1 only)
+  uint16_t* Cs = reinterpret_cast<uint16_t*>(smem + (DB ? Cfg::lds_bs : Cfg::lds_a));  // [Q][NPI]
+  // buffer k of the per-head tiles (single buffer: Xn, Hn alias Bs; Ws, Gs,
+  // dts follow Cs)
+  auto hbuf = [&](int k) -> HgBuf {
+    HgBuf r;
+    if constexpr (DB) {
+      unsigned char* base = smem + (size_t)k * Cfg::lds_buf;
+      r.Xn = reinterpret_cast<uint16_t*>(base);
+      r.Hn = r.Xn + Q * XNP;
+      r.Ws = reinterpret_cast<float*>(base + Cfg::lds_xh);
+    } else {
+      r.Xn = reinterpret_cast<uint16_t*>(smem);
+      r.Hn = r.Xn + Q * XNP;
+      r.Ws = reinterpret_cast<float*>(smem + Cfg::lds_a + Cfg::lds_c);
+    }
+    r.Gs = r.Ws + (QT / 2) * Q;
+    r.dts = r.Gs + Q;
+    return r;
+  };
+  HgBuf cur = hbuf(0);  // the tiles of the head being computed
 
   const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int H = a.H, P = a.P, G = a.G, nc = a.nc;
@@ -174,6 +206,15 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       acc = Op::mma(bf, cf, acc);
     }
     cb[sl] = acc;
+  }
+  // DB: the C fragments of the wave's two row tiles for C.H_in, in registers
+  Frag cfa[DB ? NK : 1], cfb[DB ? NK : 1];
+  if constexpr (DB) {
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      cfa[s] = Lds<Op>::load8(Cs + (16 * ra + l16) * NPI + 32 * s + 8 * lg);
+      cfb[s] = Lds<Op>::load8(Cs + (16 * rb + l16) * NPI + 32 * s + 8 * lg);
+    }
   }
 
   // ---- per-head register prefetch: issued before a head's compute,
@@ -233,7 +274,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       }
     }
   };
-  auto commit = [&]() __attribute__((always_inline)) {
+  auto commit = [&](const HgBuf& t) __attribute__((always_inline)) {
 #pragma unroll
     for (int uu = 0; uu < XPT; ++uu) {
       const int blk = tid + uu * T;
@@ -241,7 +282,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       int row, cb;
       xmap(blk, row, cb);
       const uint4 q = xv[uu];  // rebuilt from its components: a whole-struct copy kept xv in scratch
-      *reinterpret_cast<uint4*>(Xn + row * XNP + 8 * cb) = make_uint4(q.x, q.y, q.z, q.w);
+      *reinterpret_cast<uint4*>(t.Xn + row * XNP + 8 * cb) = make_uint4(q.x, q.y, q.z, q.w);
     }
 #pragma unroll
     for (int uu = 0; uu < HPT; ++uu) {
@@ -250,22 +291,22 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       const int n = blk / (PT / HCOL), col = HCOL * (blk % (PT / HCOL));
       const uint4 q = hv[uu];
       if constexpr (H_BF16) {
-        *reinterpret_cast<uint4*>(Hn + n * XNP + col) = make_uint4(q.x, q.y, q.z, q.w);
+        *reinterpret_cast<uint4*>(t.Hn + n * XNP + col) = make_uint4(q.x, q.y, q.z, q.w);
       } else {
-        *reinterpret_cast<uint2*>(Hn + n * XNP + col) =
+        *reinterpret_cast<uint2*>(t.Hn + n * XNP + col) =
             make_uint2(pack_bf16x2(__uint_as_float(q.x), __uint_as_float(q.y)),
                        pack_bf16x2(__uint_as_float(q.z), __uint_as_float(q.w)));
       }
     }
     // G is kept in base-2 units (G log2 e) on chip: every use is an exponential
     const float pg2 = pg * kLog2e;
-    Gs[tid & (Q - 1)] = pg2;  // threads tid and tid + Q write the same value
-    dts[tid & (Q - 1)] = pd;
+    t.Gs[tid & (Q - 1)] = pg2;  // threads tid and tid + Q write the same value
+    t.dts[tid & (Q - 1)] = pd;
     // Column factors of the off-diagonal sub-tiles: for the reference row
     // R = 32u, Ws[u][j] = exp(G_R - G_j) dt_j, read only for j < R (so
     // G_R <= G_j and the factor is <= 1); entries with j >= R are unused.
 #pragma unroll
-    for (int m = 0; m < NWM; ++m) Ws[tid + T * m] = fast_exp2(gref[m] * kLog2e - pg2) * pd;
+    for (int m = 0; m < NWM; ++m) t.Ws[tid + T * m] = fast_exp2(gref[m] * kLog2e - pg2) * pd;
   };
 
 
@@ -279,8 +320,8 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // Off-diagonal pair k of a tile whose diagonal pair is U: M' = CB * Ws[U][j].
   auto offdiag_frag = [&](auto tsel_c, const int k, const int U, int lg) -> Frag {
     constexpr int TSEL = decltype(tsel_c)::value;
-    const float4 w0 = *reinterpret_cast<const float4*>(Ws + U * Q + 32 * k + 4 * lg);
-    const float4 w1 = *reinterpret_cast<const float4*>(Ws + U * Q + 32 * k + 16 + 4 * lg);
+    const float4 w0 = *reinterpret_cast<const float4*>(cur.Ws + U * Q + 32 * k + 4 * lg);
+    const float4 w1 = *reinterpret_cast<const float4*>(cur.Ws + U * Q + 32 * k + 16 + 4 * lg);
     const f32x4_t c0 = cb[TSEL ? (QT - 2 * k) : 2 * k];
     const f32x4_t c1 = cb[TSEL ? (QT - 2 * k - 1) : 2 * k + 1];
     const float m[8] = {c0[0] * w0.x, c0[1] * w0.y, c0[2] * w0.z, c0[3] * w0.w,
@@ -298,12 +339,12 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     constexpr int TSEL = decltype(tsel_c)::value;
     const int i = 16 * tile + l16;  // the token this lane's interaction values and outputs belong to
     // G and dt of the lane's 8 tokens j = 32k + 16t + 4lg + r, read as vectors
-    const float4 g0 = *reinterpret_cast<const float4*>(Gs + 32 * k + 4 * lg);
-    const float4 g1 = *reinterpret_cast<const float4*>(Gs + 32 * k + 16 + 4 * lg);
-    const float4 d0 = *reinterpret_cast<const float4*>(dts + 32 * k + 4 * lg);
-    const float4 d1 = *reinterpret_cast<const float4*>(dts + 32 * k + 16 + 4 * lg);
-    const float gi = Gs[i];  // base-2 units
-    const float gR = Gs[32 * k];
+    const float4 g0 = *reinterpret_cast<const float4*>(cur.Gs + 32 * k + 4 * lg);
+    const float4 g1 = *reinterpret_cast<const float4*>(cur.Gs + 32 * k + 16 + 4 * lg);
+    const float4 d0 = *reinterpret_cast<const float4*>(cur.dts + 32 * k + 4 * lg);
+    const float4 d1 = *reinterpret_cast<const float4*>(cur.dts + 32 * k + 16 + 4 * lg);
+    const float gi = cur.Gs[i];  // base-2 units
+    const float gR = cur.Gs[32 * k];
     {
       const float e = fast_exp2(gi - gR);
 #pragma unroll
@@ -334,7 +375,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     const int Ua = ta >> 1, Ub = tb >> 1;
     Frag xn[CT];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) xn[ct] = lds_frag_tr(Xn + 16 * ct, XNP, ln);
+    for (int ct = 0; ct < CT; ++ct) xn[ct] = lds_frag_tr(cur.Xn + 16 * ct, XNP, ln);
 #pragma unroll
     for (int k = 0; k < QT / 2; ++k) {
       if (k <= Ub) {
@@ -343,7 +384,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         for (int ct = 0; ct < CT; ++ct) xf[ct] = xn[ct];
         if (k + 1 < QT / 2) {
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) xn[ct] = lds_frag_tr(Xn + 32 * (k + 1) * XNP + 16 * ct, XNP, ln);
+          for (int ct = 0; ct < CT; ++ct) xn[ct] = lds_frag_tr(cur.Xn + 32 * (k + 1) * XNP + 16 * ct, XNP, ln);
         }
         if (k <= Ua) {
           Frag mfa;
@@ -372,7 +413,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       const int pc = 16 * ct + 4 * lg;
       const int off = i * HP + pc;
       float v[4];
-      const uint2 xq = *reinterpret_cast<const uint2*>(Xn + i * XNP + pc);  // x[i][pc .. pc+3]
+      const uint2 xq = *reinterpret_cast<const uint2*>(cur.Xn + i * XNP + pc);  // x[i][pc .. pc+3]
       const float xr[4] = {bf16_bits_to_f32(xq.x & 0xffffu), bf16_bits_to_f32(xq.x >> 16),
                            bf16_bits_to_f32(xq.y & 0xffffu), bf16_bits_to_f32(xq.y >> 16)};
 #pragma unroll
@@ -395,12 +436,13 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 
   issue_x(a.hbase);
   issue_h(a.hbase);
-  __syncthreads();  // every wave is done reading Bs before Xn/Hn overwrite it
-  commit();
+  __syncthreads();  // every wave is done reading Bs (and Cs, with DB) before the tiles overwrite them
+  commit(hbuf(0));
   __syncthreads();
 
   for (int hh = 0; hh < a.HG; ++hh) {
     const int h = a.hbase + hh;
+    cur = hbuf(DB ? (hh & 1) : 0);
     // The prefetch and commit run on every iteration (the last one loads its
     // own head again, unused): with no conditional around them the compiler's
     // memory-counter waits stay exact, so the loads of the next head remain in
@@ -434,9 +476,9 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       for (int s = 0; s < NK; ++s) {
         Frag hf[CT];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) hf[ct] = lds_frag_tr(Hn + 32 * s * XNP + 16 * ct, XNP, ln);
-        const Frag ca0 = Lds<Op>::load8(Cs + (16 * ta + l16) * NPI + 32 * s + 8 * lg);
-        const Frag ca1 = Lds<Op>::load8(Cs + (16 * tb + l16) * NPI + 32 * s + 8 * lg);
+        for (int ct = 0; ct < CT; ++ct) hf[ct] = lds_frag_tr(cur.Hn + 32 * s * XNP + 16 * ct, XNP, ln);
+        const Frag ca0 = DB ? cfa[DB ? s : 0] : Lds<Op>::load8(Cs + (16 * ta + l16) * NPI + 32 * s + 8 * lg);
+        const Frag ca1 = DB ? cfb[DB ? s : 0] : Lds<Op>::load8(Cs + (16 * tb + l16) * NPI + 32 * s + 8 * lg);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           acc0[ct] = Op::mma(hf[ct], ca0, acc0[ct]);
@@ -444,7 +486,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         }
       }
       issue_h(hn);
-      const float e0 = fast_exp2(Gs[32 * (ta >> 1)]), e1 = fast_exp2(Gs[32 * (tb >> 1)]);
+      const float e0 = fast_exp2(cur.Gs[32 * (ta >> 1)]), e1 = fast_exp2(cur.Gs[32 * (tb >> 1)]);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         acc0[ct] *= e0;
@@ -454,9 +496,16 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       store_tile(ta, acc0, h, dsk, ln);
       store_tile(tb, acc1, h, dsk, ln);
     }
-    __syncthreads();  // all reads of this head's tiles are done
-    commit();
-    __syncthreads();
+    if constexpr (DB) {
+      // the other buffer was last read by the previous head, which every wave
+      // finished before the previous barrier
+      commit(hbuf((hh + 1) & 1));
+      __syncthreads();
+    } else {
+      __syncthreads();  // all reads of this head's tiles are done
+      commit(cur);
+      __syncthreads();
+    }
   }
 }
 
