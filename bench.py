@@ -120,6 +120,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-batch", type=int, default=64,
                     help="sequences in the timed single-token decode step (0: skip it)")
+    ap.add_argument("--no-cumsum-sweep", dest="cumsum_sweep", action="store_false",
+                    help="skip the chunk_cumsum bandwidth-vs-length sweep")
     ap.add_argument("--kernel-only", default=None,
                     help="time only this ABI call in the per-kernel loop (for profiling)")
     args = ap.parse_args()
@@ -277,6 +279,35 @@ def main():
                "hbm_frac": round(dbytes / (dus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
         del xd, dtd, Bd, Cd, sd, yd
 
+    # ssd_chunk_cumsum alone against sequence length at the workload's B and H:
+    # at the headline (B L H = 1.3 M tokens x heads, 15.7 MB) launch and ramp
+    # dominate; the sweep shows where the kernel reaches the HBM roofline.
+    sweep = []
+    if args.cumsum_sweep:
+        for Ls in (L, 4 * L, 16 * L, 64 * L):
+            Ls = (Ls // Q) * Q
+            shs = ops.SSDShape.make(B, Ls, H, P, N, G, Q)
+            dts = torch.rand((B, Ls, H), device=dev) * 0.5
+            dAs = torch.empty((B, H, Ls // Q, Q), device=dev)
+            dtbs = torch.empty_like(dAs)
+            call = lambda: ops.ssd_chunk_cumsum(shs, dts, t["A"], dA_cumsum=dAs, dt_bhl=dtbs)
+            for _ in range(10):
+                call()
+            torch.cuda.synchronize()
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 50
+            s0.record(stream)
+            for _ in range(reps):
+                call()
+            s1.record(stream)
+            torch.cuda.synchronize()
+            sus = 1e3 * s0.elapsed_time(s1) / reps
+            sbytes = 12 * B * Ls * H + 4 * H
+            sweep.append({"seqlen": Ls, "MB": round(sbytes / 1e6, 1), "us": round(sus, 2),
+                          "GBps": round(sbytes / (sus * 1e-6) / 1e9, 1),
+                          "hbm_frac": round(sbytes / (sus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
+            del dts, dAs, dtbs
+
     # One elementwise copy of 512 MiB (a single kernel dispatch): its measured
     # rate is the practical HBM ceiling, and under rocprofv3 --pmc its
     # FETCH_SIZE / WRITE_SIZE per dispatch (known to be 512 MiB each)
@@ -321,6 +352,7 @@ def main():
         "other_path": other,
         "copy_GBps": round(copy_gbps, 1),
         "decode_step": dec,
+        "cumsum_sweep": sweep,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w)
