@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--mma", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="forwards timed one by one after a 1 GiB cache flush (0: skip)")
     ap.add_argument("--decode-batch", type=int, default=64,
                     help="sequences in the timed single-token decode step (0: skip it)")
     ap.add_argument("--no-cumsum-sweep", dest="cumsum_sweep", action="store_false",
@@ -182,6 +184,27 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
     tokens_per_s = w.tokens / (ms_per_step / 1e3)
+
+    # Cold-cache forwards (reported beside the line, not as its value): before
+    # each timed forward, 1 GiB (four times the last-level cache) is written
+    # outside the timed region, so inputs and intermediates come from HBM.
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+        cold_ms = []
+        for _ in range(args.cold_steps):
+            flush.fill_(1.0)
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            step()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold_ms.append(c0.elapsed_time(c1))
+        del flush
+        cold_ms.sort()
+        med = cold_ms[len(cold_ms) // 2]
+        cold = {"steps": args.cold_steps, "ms_median": round(med, 5), "ms_min": round(cold_ms[0], 5),
+                "tokens_per_s_median": round(w.tokens / (med / 1e3), 1)}
 
     # ---- phase 2: per-kernel durations of the same pipeline ssd_forward runs
     # (bf16-operand path: carried states handed over as bf16, fp32 path: fp32
@@ -351,6 +374,7 @@ def main():
         "state_path": "fused" if fused else "two-kernel",
         "other_path": other,
         "copy_GBps": round(copy_gbps, 1),
+        "cold_cache": cold,
         "decode_step": dec,
         "cumsum_sweep": sweep,
     }
