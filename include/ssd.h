@@ -214,6 +214,31 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, c
                        float* final_states, void* workspace, size_t workspace_bytes,
                        ssd_mma mma, void* stream);
 
+/*
+ * Packed sequences.  Several sequences share a batch row: seq_idx [B,L]
+ * (int32, device) names each token's sequence, and the recurrence restarts
+ * from a zero state wherever seq_idx[b,t] != seq_idx[b,t-1].  This follows
+ * from the recurrence's definition applied to each sequence on its own (the
+ * pages speak of one sequence at a time): every output is that of its own
+ * sequence run alone; initial_states[b] (may be NULL: zeros) applies to the
+ * first sequence of row b, and final_states[b] (may be NULL) is the state
+ * after the last token of row b (its last sequence).  Same arguments and
+ * support as ssd_forward otherwise, always through the two-kernel state
+ * path; the workspace must hold ssd_workspace_bytes_varlen(shape) bytes.
+ * Implementation: per chunk position, the start of its sequence inside the
+ * chunk masks the interaction tile and the carried-state term; each chunk
+ * state collects the chunk's last sequence only, and the state passing
+ * restarts where that sequence began inside the chunk.
+ */
+ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+                              const void* Bm, const void* Cm, const float* D, ssd_dtype in,
+                              const int32_t* seq_idx, const float* initial_states, void* y,
+                              ssd_dtype y_dtype, float* final_states, void* workspace,
+                              size_t workspace_bytes, ssd_mma mma, void* stream);
+
+/* Workspace bytes ssd_forward_varlen needs (0 for an invalid or NULL shape). */
+size_t ssd_workspace_bytes_varlen(const ssd_shape* shape);
+
 /* Static, NUL-terminated description of a status code. */
 const char* ssd_status_string(ssd_status status);
 

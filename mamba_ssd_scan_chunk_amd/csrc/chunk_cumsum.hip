@@ -95,6 +95,98 @@ __global__ __launch_bounds__(kCsThreads) void chunk_cumsum_kernel(
   }
 }
 
+// Packed sequences: seq_idx[b, t] (int32, non-decreasing along t) names the
+// sequence of each token, and the recurrence restarts from a zero state where
+// it changes.  Per (b, chunk, position i) this writes
+//     seq_start[b, c, i] = the largest k <= i with a sequence start at cQ + k,
+//                          or -1 when token cQ + i continues the sequence that
+//                          was running before the chunk (the first sequence of
+//                          a row counts as running: it starts from the
+//                          initial state)
+// (positions past the end of a ragged last chunk repeat the last valid one).
+// The later kernels read it as masks: token j reaches token i in the chunk
+// iff j >= seq_start[i], and only tokens with seq_start = -1 see the carried
+// state.  One wave per (b, c); lane l holds positions E l .. E l + E - 1 and
+// an inclusive max-scan across the lanes completes the running maximum.
+__global__ __launch_bounds__(64) void seq_start_kernel(const int* __restrict__ seq_idx, int* __restrict__ seq_start,
+                                                       int L, int Q, int nc) {
+  const int lane = threadIdx.x;
+  const int c = blockIdx.x % nc, b = blockIdx.x / nc;
+  const int E = Q >= 64 ? Q / 64 : 1;
+  const int active = Q / E;
+  const int nvalid = min(Q, L - c * Q);
+  const int* sq = seq_idx + (int64_t)b * L + (int64_t)c * Q;
+  int run = -1;
+  int loc[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = lane * E + e;
+    if (e < E && lane < active && i < nvalid) {
+      const int t = c * Q + i;
+      if (t > 0 && sq[i] != (i > 0 ? sq[i - 1] : sq[-1])) run = i;
+    }
+    loc[e] = run;
+  }
+  // inclusive max-scan of the lane maxima (log-depth)
+  int tot = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(tot, off, 64);
+    if (lane >= off) tot = max(tot, o);
+  }
+  int excl = __shfl_up(tot, 1, 64);
+  if (lane == 0) excl = -1;
+  int out[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = max(excl, loc[e]);
+  // positions past nvalid: the running maximum already stops growing there
+  // (no boundary is recorded past nvalid), so they repeat the last valid value
+  if (lane < active) {
+    int* o = seq_start + ((int64_t)b * nc + c) * Q + lane * E;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < E) o[e] = out[e];
+  }
+}
+
+hipError_t launch_seq_start(const Dims& d, const int* seq_idx, int* seq_start, hipStream_t stream) {
+  hipLaunchKernelGGL(seq_start_kernel, dim3((unsigned)(d.B * d.nc)), dim3(64), 0, stream, seq_idx, seq_start,
+                     (int)d.L, (int)d.Q, (int)d.nc);
+  return hipGetLastError();
+}
+
+// Packed sequences, inputs of the state steps (per (b, h, c) row of Q):
+//   dt_last[i] = dt_bhl[i] where token i belongs to the chunk's last sequence
+//                (i >= seq_start[Q-1]), else 0 -- so the chunk state collects
+//                that sequence only;
+//   dA_pass    = dA_cumsum, except at i = Q-1 where -inf stands in when the
+//                chunk's last sequence started inside the chunk -- so the
+//                state passing decays the incoming state to exactly 0 there.
+__global__ __launch_bounds__(256) void varlen_prep_kernel(const float* __restrict__ dA_cumsum,
+                                                          const float* __restrict__ dt_bhl,
+                                                          const int* __restrict__ seq_start,
+                                                          float* __restrict__ dA_pass, float* __restrict__ dt_last,
+                                                          int H, int Q, int nc, int64_t nrows) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // element of [B,H,nc,Q]
+  if (e >= nrows * Q) return;
+  const int i = (int)(e % Q);
+  const int64_t row = e / Q;  // (b * H + h) * nc + c
+  const int c = (int)(row % nc);
+  const int64_t b = row / nc / H;
+  const int st_last = seq_start[(b * nc + c) * Q + Q - 1];
+  dt_last[e] = i >= st_last ? dt_bhl[e] : 0.f;
+  dA_pass[e] = (i == Q - 1 && st_last >= 0) ? -INFINITY : dA_cumsum[e];
+}
+
+hipError_t launch_varlen_prep(const Dims& d, const float* dA_cumsum, const float* dt_bhl, const int* seq_start,
+                              float* dA_pass, float* dt_last, hipStream_t stream) {
+  const int64_t nrows = d.B * d.H * d.nc;
+  const int64_t n = nrows * d.Q;
+  hipLaunchKernelGGL(varlen_prep_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, dA_cumsum, dt_bhl,
+                     seq_start, dA_pass, dt_last, (int)d.H, (int)d.Q, (int)d.nc, nrows);
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk_cumsum(const Dims& d, const float* dt, const float* A, float* dA_cumsum,
                                float* dt_bhl, hipStream_t stream) {
   const int nhb = (int)((d.H + kCsHeads - 1) / kCsHeads);

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, const void* __restrict__ Cm, int in_bf16,
     const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const void* __restrict__ carried,
     int h_bf16, const float* __restrict__ D, void* __restrict__ y, int y_bf16, int L, int H, int P, int N, int G,
-    int Q, int nc) {
+    int Q, int nc, const int* __restrict__ seq_start) {
   using E = typename OpElem<Op>::type;
   using Frag = typename Op::Frag;
   constexpr int PT = CT * 16;
@@ -64,6 +64,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
   E* Xt = Bs + kScanKS * NPI;             // [PT][XP]   x of the column step, transposed
   float* Gs = reinterpret_cast<float*>(Xt + PT * XP);  // [Q]
   float* dts = Gs + Q;                                  // [Q]
+  // packed sequences (seq_start != NULL): per row, the first token of its
+  // sequence inside the chunk, or -1 when it continues from before the chunk
+  int* Sts = reinterpret_cast<int*>(dts + Q);  // [Q]
 
   const int npt = P / PT;
   const int nrg = Q > kScanRows ? Q / kScanRows : 1;
@@ -91,6 +94,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
   for (int j = tid; j < row_end; j += kScanThreads) {
     Gs[j] = dA_cumsum[bhc * Q + j];
     dts[j] = dt_bhl[bhc * Q + j];
+    Sts[j] = seq_start ? seq_start[((int64_t)b * nc + c) * Q + j] : -1;
   }
 
   // H_in -> Ht[p][n] (zero for padded n >= N), by 8x8 register transposes.
@@ -141,6 +145,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
   for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   float gi = 0.f;  // G of row i0 + l16 (interaction-tile column index)
+  int sti = -1;    // first token of that row's sequence in the chunk (-1: before it)
   if (active) {
     // carried-state term: acc = C_rows . H_in, rows then scaled by exp(G_i)
 #pragma unroll
@@ -150,11 +155,13 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         acc[ct] = Op::mma(cf[s], Lds<Op>::load8(Ht + (16 * ct + l16) * NPI + 32 * s + 8 * lg), acc[ct]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float e = fast_exp(Gs[i0 + 4 * lg + r]);
+      // a row that starts its sequence inside the chunk does not see the carried state
+      const float e = Sts[i0 + 4 * lg + r] < 0 ? fast_exp(Gs[i0 + 4 * lg + r]) : 0.f;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) acc[ct][r] *= e;
     }
     gi = Gs[i0 + l16];
+    sti = Sts[i0 + l16];
   }
 
   for (int j0 = 0; j0 < row_end; j0 += kScanKS) {
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j = js0 + 4 * lg + r;
-            const bool keep = j <= i;
+            const bool keep = j <= i && j >= sti;  // causal, and inside row i's sequence
             const int jc = keep ? j : i;
             const float dec = fast_exp(keep ? gi - Gs[jc] : -INFINITY) * dts[jc];
             m[4 * t + r] = keep ? cb[r] * dec : 0.f;
@@ -254,13 +261,14 @@ size_t chunk_scan_lds_bytes(const Dims& d, bool f32_mma) {
   const size_t pad = f32_mma ? ScanCfg<OpF32>::PAD : ScanCfg<OpBF16>::PAD;
   const size_t npi = 32 * scan_nk(d.N) + pad;
   const size_t xp = kScanKS + pad;
-  return eb * (PT * npi + kScanKS * npi + PT * xp) + 2 * sizeof(float) * (size_t)d.Q;
+  return eb * (PT * npi + kScanKS * npi + PT * xp) + 3 * sizeof(float) * (size_t)d.Q;
 }
 
 template <class Op, int NK, int CT>
 static hipError_t launch_scan_inst(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
                                    const float* dt_bhl, const float* dA_cumsum, const void* carried,
-                                   bool h_bf16, const float* D, void* y, bool y_bf16, hipStream_t stream, size_t lds) {
+                                   bool h_bf16, const float* D, void* y, bool y_bf16, const int* seq_start,
+                                   hipStream_t stream, size_t lds) {
   auto kern = chunk_scan_kernel<Op, NK, CT>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -270,42 +278,46 @@ static hipError_t launch_scan_inst(const Dims& d, const void* x, const void* Bm,
   const dim3 grid((unsigned)(d.H * (d.P / (16 * CT))), (unsigned)(nrg * d.nc), (unsigned)d.B);
   hipLaunchKernelGGL(kern, grid, dim3(kScanThreads), lds, stream, x, Bm, Cm, (int)in_bf16, dt_bhl, dA_cumsum,
                      carried, (int)h_bf16, D, y, (int)y_bf16, (int)d.L, (int)d.H, (int)d.P, (int)d.N, (int)d.G, (int)d.Q,
-                     (int)d.nc);
+                     (int)d.nc, seq_start);
   return hipGetLastError();
 }
 
 template <class Op, int NK>
 static hipError_t launch_scan_ct(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
                                  const float* dt_bhl, const float* dA_cumsum, const void* carried,
-                                 bool h_bf16, const float* D, void* y, bool y_bf16, hipStream_t stream, size_t lds) {
+                                 bool h_bf16, const float* D, void* y, bool y_bf16, const int* seq_start,
+                                 hipStream_t stream, size_t lds) {
   switch (scan_ct(d.P)) {
-    case 4: return launch_scan_inst<Op, NK, 4>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
-    case 2: return launch_scan_inst<Op, NK, 2>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
-    default: return launch_scan_inst<Op, NK, 1>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
+    case 4: return launch_scan_inst<Op, NK, 4>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, seq_start, stream, lds);
+    case 2: return launch_scan_inst<Op, NK, 2>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, seq_start, stream, lds);
+    default: return launch_scan_inst<Op, NK, 1>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, seq_start, stream, lds);
   }
 }
 
 template <class Op>
 static hipError_t launch_scan_op(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
                                  const float* dt_bhl, const float* dA_cumsum, const void* carried,
-                                 bool h_bf16, const float* D, void* y, bool y_bf16, hipStream_t stream, size_t lds) {
+                                 bool h_bf16, const float* D, void* y, bool y_bf16, const int* seq_start,
+                                 hipStream_t stream, size_t lds) {
   switch (scan_nk(d.N)) {
-    case 1: return launch_scan_ct<Op, 1>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
-    case 2: return launch_scan_ct<Op, 2>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
-    case 4: return launch_scan_ct<Op, 4>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
-    default: return launch_scan_ct<Op, 8>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
+    case 1: return launch_scan_ct<Op, 1>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, seq_start, stream, lds);
+    case 2: return launch_scan_ct<Op, 2>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, seq_start, stream, lds);
+    case 4: return launch_scan_ct<Op, 4>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, seq_start, stream, lds);
+    default: return launch_scan_ct<Op, 8>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, seq_start, stream, lds);
   }
 }
 
 hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
                              const float* dt_bhl, const float* dA_cumsum, const void* carried, bool h_bf16,
-                             const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream) {
+                             const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream,
+                             const int* seq_start) {
   if (chunk_scan_hg_supported(d, in_bf16, f32_mma))
-    return launch_chunk_scan_hg(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream);
+    return launch_chunk_scan_hg(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream,
+                                seq_start);
   const size_t lds = chunk_scan_lds_bytes(d, f32_mma);
   if (f32_mma)
-    return launch_scan_op<OpF32>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
-  return launch_scan_op<OpBF16>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream, lds);
+    return launch_scan_op<OpF32>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, seq_start, stream, lds);
+  return launch_scan_op<OpBF16>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, seq_start, stream, lds);
 }
 
 }  // namespace ssd

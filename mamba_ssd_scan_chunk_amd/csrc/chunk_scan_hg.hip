@@ -82,6 +82,7 @@ struct HgCfg {
   static constexpr size_t lds_buf = lds_xh + lds_w + 2 * sizeof(float) * Q;  // one buffer
   static constexpr size_t lds_db = 2 * lds_bs > 2 * lds_buf ? 2 * lds_bs : 2 * lds_buf;
   static constexpr size_t lds_total = DB ? lds_db : lds_a + lds_c + lds_w + 2 * sizeof(float) * Q;
+  static constexpr size_t lds_varlen = lds_total + sizeof(int) * Q;  // + the seq-start row (packed sequences)
 };
 
 // LDS tiles of one head: x, H_in, the column-factor table, G and dt
@@ -101,6 +102,7 @@ struct HgArgs {
   const float* dA_cumsum;
   const void* carried;  // fp32, or bf16 bits when H_BF16
   const float* D;
+  const int* seq_start;  // packed sequences (VARLEN): [B,nc,Q]
   void* y;
   int L, H, P, G, nc, HG;
   int b, c, g, hbase, p0;
@@ -116,7 +118,7 @@ __device__ __forceinline__ int npos(int n) {
   return (n & ~31) | ((n & 12) << 1) | ((n & 16) >> 2) | (n & 3);
 }
 
-template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED>
+template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED, bool VARLEN>
 __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, const int tid) {
   using Cfg = HgCfg<Q, NK, CT>;
   using Op = OpBF16;
@@ -155,6 +157,10 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     return r;
   };
   HgBuf cur = hbuf(0);  // the tiles of the head being computed
+  // VARLEN: per row of the chunk, the first token of its sequence inside the
+  // chunk (-1: the sequence runs in from before the chunk); a row sees column
+  // j only if j >= that, and sees the carried state only if it is -1
+  int* Sts = reinterpret_cast<int*>(smem + Cfg::lds_total);
 
   const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int H = a.H, P = a.P, G = a.G, nc = a.nc;
@@ -166,6 +172,8 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   const int rmax = RAGGED ? min(Q, a.L - a.c * Q) - 1 : Q - 1;
   auto rowc = [&](int r) { return RAGGED ? min(r, rmax) : r; };
 
+  if constexpr (VARLEN)
+    for (int j = tid; j < Q; j += T) Sts[j] = a.seq_start[((int64_t)a.b * a.nc + a.c) * Q + j];
   // ---- phase 0: B and C chunks -> Bs, Cs ([token][npos(n)], bf16).  A
   // 16-byte piece holds n = 8nb .. 8nb+7, whose two 4-element halves land at
   // npos(8nb) and npos(8nb + 4).
@@ -318,14 +326,19 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // MFMA sites per branch made the compiler copy accumulators at every merge,
   // each copy waiting for the MFMA results).
   // Off-diagonal pair k of a tile whose diagonal pair is U: M' = CB * Ws[U][j].
-  auto offdiag_frag = [&](auto tsel_c, const int k, const int U, int lg) -> Frag {
+  auto offdiag_frag = [&](auto tsel_c, const int k, const int U, int lg, int sti) -> Frag {
     constexpr int TSEL = decltype(tsel_c)::value;
     const float4 w0 = *reinterpret_cast<const float4*>(cur.Ws + U * Q + 32 * k + 4 * lg);
     const float4 w1 = *reinterpret_cast<const float4*>(cur.Ws + U * Q + 32 * k + 16 + 4 * lg);
     const f32x4_t c0 = cb[TSEL ? (QT - 2 * k) : 2 * k];
     const f32x4_t c1 = cb[TSEL ? (QT - 2 * k - 1) : 2 * k + 1];
-    const float m[8] = {c0[0] * w0.x, c0[1] * w0.y, c0[2] * w0.z, c0[3] * w0.w,
-                        c1[0] * w1.x, c1[1] * w1.y, c1[2] * w1.z, c1[3] * w1.w};
+    float m[8] = {c0[0] * w0.x, c0[1] * w0.y, c0[2] * w0.z, c0[3] * w0.w,
+                  c1[0] * w1.x, c1[1] * w1.y, c1[2] * w1.z, c1[3] * w1.w};
+    if constexpr (VARLEN) {
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8)
+        if (32 * k + 16 * (e8 >> 2) + 4 * lg + (e8 & 3) < sti) m[e8] = 0.f;
+    }
     return Op::from_f32(m);
   };
   // Diagonal pair k = tile / 2: the row factor exp(G_i - G_R) first scales
@@ -335,7 +348,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // upper sub-tile of an even tile, whose slot holds the other tile's values,
   // is zeroed outright; that select also keeps the register allocator from
   // copying the accumulators.)
-  auto diag_frag = [&](auto tsel_c, const int k, const int tile, f32x4_t (&acc)[CT], int l16, int lg) -> Frag {
+  auto diag_frag = [&](auto tsel_c, const int k, const int tile, f32x4_t (&acc)[CT], int l16, int lg, int sti) -> Frag {
     constexpr int TSEL = decltype(tsel_c)::value;
     const int i = 16 * tile + l16;  // the token this lane's interaction values and outputs belong to
     // G and dt of the lane's 8 tokens j = 32k + 16t + 4lg + r, read as vectors
@@ -359,7 +372,8 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 #pragma unroll
     for (int e8 = 0; e8 < 8; ++e8) {
       const int j = 32 * k + 16 * (e8 >> 2) + 4 * lg + (e8 & 3);
-      const float dec = fast_exp2(j <= i ? gi - gj[e8] : -INFINITY);
+      const bool keep = VARLEN ? (j <= i && j >= sti) : j <= i;
+      const float dec = fast_exp2(keep ? gi - gj[e8] : -INFINITY);
       m[e8] = cvv[e8] * dj[e8] * dec;
     }
     return Op::from_f32(m);
@@ -373,6 +387,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   auto steps = [&](const int ta, const int tb, f32x4_t (&acc0)[CT], f32x4_t (&acc1)[CT], int ln) {
     const int l16 = ln & 15, lg = ln >> 4;
     const int Ua = ta >> 1, Ub = tb >> 1;
+    const int sta = VARLEN ? Sts[16 * ta + l16] : -1, stb = VARLEN ? Sts[16 * tb + l16] : -1;
     Frag xn[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) xn[ct] = lds_frag_tr(cur.Xn + 16 * ct, XNP, ln);
@@ -388,14 +403,14 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         }
         if (k <= Ua) {
           Frag mfa;
-          if (k < Ua) mfa = offdiag_frag(std::integral_constant<int, 0>{}, k, Ua, lg);
-          else mfa = diag_frag(std::integral_constant<int, 0>{}, k, ta, acc0, l16, lg);
+          if (k < Ua) mfa = offdiag_frag(std::integral_constant<int, 0>{}, k, Ua, lg, sta);
+          else mfa = diag_frag(std::integral_constant<int, 0>{}, k, ta, acc0, l16, lg, sta);
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) acc0[ct] = Op::mma(xf[ct], mfa, acc0[ct]);
         }
         Frag mfb;
-        if (k < Ub) mfb = offdiag_frag(std::integral_constant<int, 1>{}, k, Ub, lg);
-        else mfb = diag_frag(std::integral_constant<int, 1>{}, k, tb, acc1, l16, lg);
+        if (k < Ub) mfb = offdiag_frag(std::integral_constant<int, 1>{}, k, Ub, lg, stb);
+        else mfb = diag_frag(std::integral_constant<int, 1>{}, k, tb, acc1, l16, lg, stb);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) acc1[ct] = Op::mma(xf[ct], mfb, acc1[ct]);
       }
@@ -486,7 +501,13 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         }
       }
       issue_h(hn);
-      const float e0 = fast_exp2(cur.Gs[32 * (ta >> 1)]), e1 = fast_exp2(cur.Gs[32 * (tb >> 1)]);
+      float e0 = fast_exp2(cur.Gs[32 * (ta >> 1)]), e1 = fast_exp2(cur.Gs[32 * (tb >> 1)]);
+      if constexpr (VARLEN) {
+        // rows that start their sequence inside the chunk do not see the carried state
+        const int l16c = ln & 15;
+        if (Sts[16 * ta + l16c] >= 0) e0 = 0.f;
+        if (Sts[16 * tb + l16c] >= 0) e1 = 0.f;
+      }
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         acc0[ct] *= e0;
@@ -512,12 +533,12 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 // Y_BF16 is a template parameter rather than a run-time flag: a branch around
 // the output stores would make the compiler's memory-counter waits for the
 // prefetched loads conservative (they would also wait for the stores).
-template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED>
+template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED, bool VARLEN>
 __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, const void* __restrict__ Cm,
     const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const void* __restrict__ carried,
     const float* __restrict__ D, void* __restrict__ y, int L, int H, int P, int G, int nc, int HG,
-    int nhg, int npt, int remap) {
+    int nhg, int npt, int remap, const int* __restrict__ seq_start) {
   extern __shared__ __align__(16) unsigned char hg_smem[];
   // block -> (b, c, g, head group, p slice).  With remap != 0 the mapping is
   // XCD-aware: consecutive logical blocks (same chunk, neighbouring head
@@ -527,6 +548,7 @@ __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
   if (remap) bid = (bid & 7u) * (nblk >> 3) + (bid >> 3);
   HgArgs a;
   a.x = x; a.Bm = Bm; a.Cm = Cm; a.dt_bhl = dt_bhl; a.dA_cumsum = dA_cumsum; a.carried = carried; a.D = D; a.y = y;
+  a.seq_start = seq_start;
   a.L = L; a.H = H; a.P = P; a.G = G; a.nc = nc; a.HG = HG;
   const int pt = bid % npt;
   unsigned rest = bid / npt;
@@ -539,7 +561,7 @@ __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
   a.hbase = a.g * (H / G) + hgi * HG;
   a.p0 = pt * HgCfg<Q, NK, CT>::PT;
   a.tok0 = (int64_t)a.b * L + (int64_t)a.c * Q;
-  hg_body<Q, NK, CT, H_BF16, Y_BF16, RAGGED>(a, hg_smem, threadIdx.x);
+  hg_body<Q, NK, CT, H_BF16, Y_BF16, RAGGED, VARLEN>(a, hg_smem, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ host side
@@ -571,18 +593,25 @@ static int pick_heads_per_block(const Dims& d, int npt) {
   return best;
 }
 
+template <int Q, int NK, bool H_BF16, bool Y_BF16>
+static auto pick_hg_kernel(bool ragged, bool varlen) {
+  // packed sequences take the guarded-store instance too (their last chunk
+  // may be ragged as well)
+  if (varlen) return chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, true, true>;
+  return ragged ? chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, true, false>
+                : chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, false, false>;
+}
+
 template <int Q, int NK, bool H_BF16>
 static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, const void* Cm, const float* dt_bhl,
                                  const float* dA_cumsum, const void* carried, const float* D, void* y,
-                                 bool y_bf16, hipStream_t stream) {
+                                 bool y_bf16, hipStream_t stream, const int* seq_start) {
   constexpr int CT = 4;
   using Cfg = HgCfg<Q, NK, CT>;
-  const bool ragged = d.L % Q != 0;
-  auto kern = y_bf16 ? (ragged ? chunk_scan_hg_kernel<Q, NK, CT, H_BF16, true, true>
-                               : chunk_scan_hg_kernel<Q, NK, CT, H_BF16, true, false>)
-                     : (ragged ? chunk_scan_hg_kernel<Q, NK, CT, H_BF16, false, true>
-                               : chunk_scan_hg_kernel<Q, NK, CT, H_BF16, false, false>);
-  const size_t lds = Cfg::lds_total;
+  const bool ragged = d.L % Q != 0, varlen = seq_start != nullptr;
+  auto kern = y_bf16 ? pick_hg_kernel<Q, NK, H_BF16, true>(ragged, varlen)
+                     : pick_hg_kernel<Q, NK, H_BF16, false>(ragged, varlen);
+  const size_t lds = varlen ? Cfg::lds_varlen : Cfg::lds_total;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -594,14 +623,14 @@ static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, c
   const int64_t nblk = d.B * d.nc * d.G * nhg * npt;
   const int remap = (nblk % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(threads), lds, stream, x, Bm, Cm, dt_bhl, dA_cumsum, carried,
-                     D, y, (int)d.L, (int)d.H, (int)d.P, (int)d.G, (int)d.nc, HG, nhg, npt, remap);
+                     D, y, (int)d.L, (int)d.H, (int)d.P, (int)d.G, (int)d.nc, HG, nhg, npt, remap, seq_start);
   return hipGetLastError();
 }
 
 template <int Q, int NK>
 static bool hg_fits() {
   using Cfg = HgCfg<Q, NK, 4>;
-  return Cfg::lds_total <= 160 * 1024 && Q <= Cfg::T && 64 * Cfg::NCW <= Cfg::T && (Q == 128 || Q == 256);
+  return Cfg::lds_varlen <= 160 * 1024 && Q <= Cfg::T && 64 * Cfg::NCW <= Cfg::T && (Q == 128 || Q == 256);
 }
 
 bool chunk_scan_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
@@ -620,11 +649,11 @@ bool chunk_scan_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
 template <bool H_BF16>
 static hipError_t launch_hg_dtype(const Dims& d, const void* x, const void* Bm, const void* Cm, const float* dt_bhl,
                                   const float* dA_cumsum, const void* carried, const float* D, void* y, bool y_bf16,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, const int* seq_start) {
   const int64_t key = d.Q * 1000 + d.N;
 #define HG_CASE(QQ, NN, KK) \
   case QQ * 1000 + NN:      \
-    return launch_hg_inst<QQ, KK, H_BF16>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream);
+    return launch_hg_inst<QQ, KK, H_BF16>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
   switch (key) {
     HG_CASE(128, 128, 4)
     HG_CASE(128, 256, 8)
@@ -636,10 +665,11 @@ static hipError_t launch_hg_dtype(const Dims& d, const void* x, const void* Bm, 
 
 hipError_t launch_chunk_scan_hg(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
                                 const float* dt_bhl, const float* dA_cumsum, const void* carried, bool carried_bf16,
-                                const float* D, void* y, bool y_bf16, hipStream_t stream) {
+                                const float* D, void* y, bool y_bf16, hipStream_t stream, const int* seq_start) {
   if (!in_bf16) return hipErrorInvalidValue;
-  if (carried_bf16) return launch_hg_dtype<true>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream);
-  return launch_hg_dtype<false>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream);
+  if (carried_bf16)
+    return launch_hg_dtype<true>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
+  return launch_hg_dtype<false>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
 }
 
 }  // namespace ssd

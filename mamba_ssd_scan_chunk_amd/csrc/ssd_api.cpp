@@ -100,6 +100,9 @@ ssd_status validate_scan(const ssd_shape* shape, const void* x, const void* Bm, 
 
 struct WsLayout {
   size_t dA_off, dt_off, st_off, hb_off, total;
+  // ssd_forward_varlen also: sequence starts (int32 [B,nc,Q]), dA_cumsum for
+  // the state passing and dt masked to each chunk's last sequence (fp32 [B,H,nc,Q])
+  size_t ss_off, dAp_off, dtl_off, total_varlen;
 };
 
 WsLayout workspace_layout(const Dims& d) {
@@ -111,6 +114,10 @@ WsLayout workspace_layout(const Dims& d) {
   w.st_off = round_up(w.dt_off + bhl, kWsAlign);
   w.hb_off = round_up(w.st_off + st, kWsAlign);  // bf16 carried states (half the bytes of st)
   w.total = round_up(w.hb_off + st / 2, kWsAlign);
+  w.ss_off = w.total;
+  w.dAp_off = round_up(w.ss_off + sizeof(int32_t) * (size_t)(d.B * d.nc * d.Q), kWsAlign);
+  w.dtl_off = round_up(w.dAp_off + bhl, kWsAlign);
+  w.total_varlen = round_up(w.dtl_off + bhl, kWsAlign);
   return w;
 }
 
@@ -201,6 +208,12 @@ size_t ssd_workspace_bytes(const ssd_shape* shape) {
   return workspace_layout(d).total;
 }
 
+size_t ssd_workspace_bytes_varlen(const ssd_shape* shape) {
+  Dims d;
+  if (check_shape(shape, &d) != SSD_OK) return 0;
+  return workspace_layout(d).total_varlen;
+}
+
 // ssd_forward's state step: the fused kernel (chunk states stay on chip) or
 // the two-kernel path (fp32 chunk states through memory).  The fused kernel
 // walks the chunks in sequence inside each block, so it only pays off with
@@ -270,6 +283,57 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, c
     SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dA, initial_states, final_states, s)));
     SSD_TRY(from_hip(
         ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, false, D, y, y_dtype == SSD_BF16, f32m, s)));
+  }
+  return SSD_OK;
+}
+
+ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+                              const void* Bm, const void* Cm, const float* D, ssd_dtype in, const int32_t* seq_idx,
+                              const float* initial_states, void* y, ssd_dtype y_dtype, float* final_states,
+                              void* workspace, size_t workspace_bytes, ssd_mma mma, void* stream) {
+  Dims d;
+  SSD_TRY(check_shape(shape, &d));
+  SSD_TRY(check_dtype(in));
+  SSD_TRY(check_dtype(y_dtype));
+  SSD_TRY(check_mma(mma));
+  if (!x || !dt || !A || !Bm || !Cm || !D || !y || !seq_idx) return SSD_ERR_NULL;
+  if (!workspace) return SSD_ERR_WORKSPACE;
+  const WsLayout ws = workspace_layout(d);
+  if (workspace_bytes < ws.total_varlen) return SSD_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(Bm) || !aligned16(Cm) || !aligned16(D) ||
+      !aligned16(y) || !aligned16(seq_idx) || !aligned16(workspace) ||
+      (initial_states && !aligned16(initial_states)) || (final_states && !aligned16(final_states)))
+    return SSD_ERR_ALIGN;
+  if (ssd::chunk_state_lds_bytes(d, mma == SSD_MMA_F32) > kLdsLimit ||
+      ssd::chunk_scan_lds_bytes(d, mma == SSD_MMA_F32) > kLdsLimit)
+    return SSD_ERR_UNSUPPORTED;
+
+  char* base = static_cast<char*>(workspace);
+  float* dA = reinterpret_cast<float*>(base + ws.dA_off);
+  float* dtb = reinterpret_cast<float*>(base + ws.dt_off);
+  float* st = reinterpret_cast<float*>(base + ws.st_off);
+  int* sst = reinterpret_cast<int*>(base + ws.ss_off);
+  float* dAp = reinterpret_cast<float*>(base + ws.dAp_off);
+  float* dtl = reinterpret_cast<float*>(base + ws.dtl_off);
+  const hipStream_t s = (hipStream_t)stream;
+  const bool bf = in == SSD_BF16, f32m = mma == SSD_MMA_F32;
+
+  // the two-kernel state path, fed with the packed-sequence masks: chunk
+  // states of each chunk's last sequence only, and a state passing that
+  // restarts where a sequence starts inside a chunk
+  SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
+  SSD_TRY(from_hip(ssd::launch_seq_start(d, seq_idx, sst, s)));
+  SSD_TRY(from_hip(ssd::launch_varlen_prep(d, dA, dtb, sst, dAp, dtl, s)));
+  SSD_TRY(from_hip(ssd::launch_chunk_state(d, x, Bm, bf, dtl, dA, st, f32m, s)));
+  if (!f32m) {
+    uint16_t* hb = reinterpret_cast<uint16_t*>(base + ws.hb_off);
+    SSD_TRY(from_hip(ssd::launch_state_passing_bf16(d, st, hb, dAp, initial_states, final_states, s)));
+    SSD_TRY(from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, hb, true, D, y, y_dtype == SSD_BF16, f32m,
+                                            s, sst)));
+  } else {
+    SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dAp, initial_states, final_states, s)));
+    SSD_TRY(from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, false, D, y, y_dtype == SSD_BF16, f32m,
+                                            s, sst)));
   }
   return SSD_OK;
 }

@@ -20,6 +20,13 @@ size_t chunk_scan_lds_bytes(const Dims& d, bool f32_mma);
 
 hipError_t launch_chunk_cumsum(const Dims& d, const float* dt, const float* A, float* dA_cumsum,
                                float* dt_bhl, hipStream_t stream);
+// Packed sequences: seq_start [B,nc,Q] int32 from seq_idx [B,L] (see chunk_cumsum.hip).
+hipError_t launch_seq_start(const Dims& d, const int* seq_idx, int* seq_start, hipStream_t stream);
+// Packed sequences: dt masked to each chunk's last sequence (for the chunk
+// states) and dA_cumsum with -inf at a chunk's last position where the state
+// restarts inside the chunk (for the state passing).
+hipError_t launch_varlen_prep(const Dims& d, const float* dA_cumsum, const float* dt_bhl, const int* seq_start,
+                              float* dA_pass, float* dt_last, hipStream_t stream);
 
 hipError_t launch_chunk_state(const Dims& d, const void* x, const void* Bm, bool in_bf16,
                               const float* dt_bhl, const float* dA_cumsum, float* states,
@@ -65,12 +72,16 @@ hipError_t launch_state_fused(const Dims& d, const void* x, const void* Bm, cons
 bool chunk_scan_hg_supported(const Dims& d, bool in_bf16, bool f32_mma);
 hipError_t launch_chunk_scan_hg(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
                                 const float* dt_bhl, const float* dA_cumsum, const void* carried, bool carried_bf16,
-                                const float* D, void* y, bool y_bf16, hipStream_t stream);
+                                const float* D, void* y, bool y_bf16, hipStream_t stream,
+                                const int* seq_start = nullptr);
 
 // `carried` holds fp32 values, or bf16 bits when carried_bf16 is set.
+// seq_start (packed sequences, [B,nc,Q] from launch_seq_start, or NULL):
+// interaction and carried-state terms are masked to each row's sequence.
 hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
                              const float* dt_bhl, const float* dA_cumsum, const void* carried, bool carried_bf16,
-                             const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream);
+                             const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream,
+                             const int* seq_start = nullptr);
 
 // Single-token recurrent step: state [Bn,H,N,P] fp32 updated in place, y
 // [Bn,H,P].  Supported for P a multiple of 4 up to 1024.

@@ -31,8 +31,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     for n in ["ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward",
-              "ssd_chunk_state_passing", "ssd_decode_step", "ssd_workspace_bytes", "ssd_status_string",
-              "ssd_abi_version"]:
+              "ssd_chunk_state_passing", "ssd_decode_step", "ssd_forward_varlen", "ssd_workspace_bytes",
+              "ssd_workspace_bytes_varlen", "ssd_status_string", "ssd_abi_version"]:
         assert n in names
 
 
@@ -179,6 +179,27 @@ def test_decode_step_checks(lib):
     odd = FAKE + 4
     assert lib.ssd_decode_step(shape(seqlen=1, headdim=20, dstate=7), *args[:6], 1, odd, FAKE, 1, None) == ALIGN
     assert lib.ssd_decode_step(s, odd, *args[1:6], 1, FAKE, FAKE, 1, None) == ALIGN
+
+
+def test_forward_varlen_checks(lib):
+    """The packed-sequence forward validates like ssd_forward, needs seq_idx,
+    and its own (larger) workspace."""
+    s = shape()
+    B, L, H, P, N, Q = 2, 512, 4, 64, 128, 256
+    nc = 2
+    bhl = 4 * B * H * nc * Q
+    ru = lambda v: (v + 255) // 256 * 256
+    base = lib.ssd_workspace_bytes(s)
+    need = ru(ru(ru(base + 4 * B * nc * Q) + bhl) + bhl)
+    assert lib.ssd_workspace_bytes_varlen(s) == need
+    assert lib.ssd_workspace_bytes_varlen(None) == 0
+    a = [FAKE] * 6  # x, dt, A, Bm, Cm, D
+    assert lib.ssd_forward_varlen(s, *a, 1, None, None, FAKE, 1, FAKE, FAKE, need, 0, None) == NULL
+    assert lib.ssd_forward_varlen(s, *a, 1, FAKE, None, FAKE, 1, FAKE, FAKE, need - 1, 0, None) == WS
+    assert lib.ssd_forward_varlen(s, *a, 1, FAKE, None, FAKE, 1, FAKE, None, need, 0, None) == WS
+    assert lib.ssd_forward_varlen(s, *a, 1, FAKE + 4, None, FAKE, 1, FAKE, FAKE, need, 0, None) == ALIGN
+    assert lib.ssd_forward_varlen(s, *a, 7, FAKE, None, FAKE, 1, FAKE, FAKE, need, 0, None) == DTYPE
+    assert lib.ssd_forward_varlen(shape(headdim=24), *a, 1, FAKE, None, FAKE, 1, FAKE, FAKE, need, 0, None) == UNSUP
 
 
 def test_bf16_carried_has_no_in_place_form(lib):

@@ -463,3 +463,64 @@ def test_errors_raise_through_binding():
     with pytest.raises(ValueError):  # dtype mismatch between x and B
         ops.ssd_chunk_state(ops.shape_of(t, 64), t["x"], t["Bm"].float(),
                             torch.empty(1, 2, 2, 64, device="cuda"), torch.empty(1, 2, 2, 64, device="cuda"))
+
+
+# ---------------------------------------------------------------- packed sequences
+# (name, B, H, P, N, G, Q, sequence lengths per row): boundaries at chunk starts,
+# inside chunks, sequences shorter than a chunk, one spanning several chunks
+PACKED = [
+    ("hg_q256", 2, 4, 64, 128, 1, 256, [[256, 100, 1, 155, 300], [812]]),
+    ("hg_q128_n256", 1, 4, 64, 256, 2, 128, [[5, 123, 128, 60, 200]]),
+    ("generic_q64", 2, 3, 48, 48, 3, 64, [[64, 64, 10, 54, 100], [33, 31, 1, 1, 1, 1, 224]]),
+]
+
+
+def _packed_seq_idx(rows, L):
+    idx = np.zeros((len(rows), L), dtype=np.int32)
+    for b, lens in enumerate(rows):
+        assert sum(lens) == L
+        idx[b] = np.repeat(np.arange(len(lens), dtype=np.int32), lens)
+    return idx
+
+
+@pytest.mark.parametrize("with_h0", [False, True])
+@pytest.mark.parametrize("mma", ["f32", "bf16"])
+@pytest.mark.parametrize("case", PACKED, ids=[c[0] for c in PACKED])
+def test_forward_packed_sequences(case, mma, with_h0):
+    """Every sequence of a packed row gives the outputs of its own run from a
+    zero state (the row's first one from the row's initial state), and the
+    final state is that of the row's last sequence."""
+    name, B, H, P, N, G, Q, rows = case
+    L = sum(rows[0])
+    say(f"packed sequences {name} {mma} h0={with_h0}")
+    in_dtype = "bf16" if mma == "bf16" else "f32"
+    inp = make_inputs(B, L, H, P, N, G, Q, in_dtype=in_dtype, seed=17, dt_shift=2.0)
+    t = upload(inp)
+    sh = ops.shape_of(t, Q)
+    sq = torch.from_numpy(_packed_seq_idx(rows, L)).cuda()
+    h0 = _h0(inp) if with_h0 else None
+    h0_t = None if h0 is None else torch.from_numpy(h0).cuda()
+    y, fin = ops.ssd_forward_varlen(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], sq,
+                                    initial_states=h0_t, y_dtype="f32", mma=mma)
+    torch.cuda.synchronize()
+    o = oracle()
+    for b, lens in enumerate(rows):
+        s0 = 0
+        for k, n in enumerate(lens):
+            sl = lambda a: np.ascontiguousarray(a[b:b + 1, s0:s0 + n])
+            hk = h0[b:b + 1] if (h0 is not None and k == 0) else None
+            yref, fref = o.forward(sl(inp.x), sl(inp.dt), inp.A, sl(inp.Bm), sl(inp.Cm), inp.D, h0=hk)
+            e = relerr(y[b:b + 1, s0:s0 + n], yref)
+            assert e <= tol_for(mma), (b, k, n, e)
+            s0 += n
+        ef = relerr(fin[b:b + 1], fref)
+        say(f"  row {b}: {len(lens)} sequences, final rel err {ef:.3g}")
+        assert ef <= tol_for(mma)
+    # one sequence per row reproduces the plain forward bit for bit
+    one = torch.zeros((B, L), dtype=torch.int32, device="cuda")
+    y1, f1 = ops.ssd_forward_varlen(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], one,
+                                    initial_states=h0_t, y_dtype="f32", mma=mma)
+    y2, f2 = ops.ssd_forward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], initial_states=h0_t,
+                             y_dtype="f32", mma=mma)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
