@@ -222,7 +222,12 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, c
  * pages speak of one sequence at a time): every output is that of its own
  * sequence run alone; initial_states[b] (may be NULL: zeros) applies to the
  * first sequence of row b, and final_states[b] (may be NULL) is the state
- * after the last token of row b (its last sequence).  Same arguments and
+ * after the last token of row b (its last sequence).  For s < nseq,
+ * seq_states[s] ([nseq,H,N,P] fp32) receives the state after token
+ * seq_last[s] (int64 device array of flattened indices b*L + t) of that
+ * token's sequence -- for serving, each sequence's last token, to continue
+ * it with ssd_decode_step; an index outside [0, B*L) leaves its entry
+ * untouched.  nseq = 0 allows seq_last, seq_states NULL.  Same arguments and
  * support as ssd_forward otherwise, always through the two-kernel state
  * path; the workspace must hold ssd_workspace_bytes_varlen(shape) bytes.
  * Implementation: per chunk position, the start of its sequence inside the
@@ -233,7 +238,8 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, c
 ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float* dt, const float* A,
                               const void* Bm, const void* Cm, const float* D, ssd_dtype in,
                               const int32_t* seq_idx, const float* initial_states, void* y,
-                              ssd_dtype y_dtype, float* final_states, void* workspace,
+                              ssd_dtype y_dtype, float* final_states, int64_t nseq,
+                              const int64_t* seq_last, float* seq_states, void* workspace,
                               size_t workspace_bytes, ssd_mma mma, void* stream);
 
 /* Workspace bytes ssd_forward_varlen needs (0 for an invalid or NULL shape). */

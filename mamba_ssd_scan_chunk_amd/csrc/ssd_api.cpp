@@ -290,16 +290,20 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, c
 ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float* dt, const float* A,
                               const void* Bm, const void* Cm, const float* D, ssd_dtype in, const int32_t* seq_idx,
                               const float* initial_states, void* y, ssd_dtype y_dtype, float* final_states,
-                              void* workspace, size_t workspace_bytes, ssd_mma mma, void* stream) {
+                              int64_t nseq, const int64_t* seq_last, float* seq_states, void* workspace,
+                              size_t workspace_bytes, ssd_mma mma, void* stream) {
   Dims d;
   SSD_TRY(check_shape(shape, &d));
   SSD_TRY(check_dtype(in));
   SSD_TRY(check_dtype(y_dtype));
   SSD_TRY(check_mma(mma));
   if (!x || !dt || !A || !Bm || !Cm || !D || !y || !seq_idx) return SSD_ERR_NULL;
+  if (nseq < 0 || nseq > 0x7fffffff / (d.H * ((d.N + 31) / 32) * ((d.P + 31) / 32))) return SSD_ERR_SHAPE;
+  if (nseq > 0 && (!seq_last || !seq_states)) return SSD_ERR_NULL;
   if (!workspace) return SSD_ERR_WORKSPACE;
   const WsLayout ws = workspace_layout(d);
   if (workspace_bytes < ws.total_varlen) return SSD_ERR_WORKSPACE;
+  if (nseq > 0 && (!aligned16(seq_last) || !aligned16(seq_states))) return SSD_ERR_ALIGN;
   if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(Bm) || !aligned16(Cm) || !aligned16(D) ||
       !aligned16(y) || !aligned16(seq_idx) || !aligned16(workspace) ||
       (initial_states && !aligned16(initial_states)) || (final_states && !aligned16(final_states)))
@@ -325,16 +329,12 @@ ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float
   SSD_TRY(from_hip(ssd::launch_seq_start(d, seq_idx, sst, s)));
   SSD_TRY(from_hip(ssd::launch_varlen_prep(d, dA, dtb, sst, dAp, dtl, s)));
   SSD_TRY(from_hip(ssd::launch_chunk_state(d, x, Bm, bf, dtl, dA, st, f32m, s)));
-  if (!f32m) {
-    uint16_t* hb = reinterpret_cast<uint16_t*>(base + ws.hb_off);
-    SSD_TRY(from_hip(ssd::launch_state_passing_bf16(d, st, hb, dAp, initial_states, final_states, s)));
-    SSD_TRY(from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, hb, true, D, y, y_dtype == SSD_BF16, f32m,
-                                            s, sst)));
-  } else {
-    SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dAp, initial_states, final_states, s)));
-    SSD_TRY(from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, false, D, y, y_dtype == SSD_BF16, f32m,
-                                            s, sst)));
-  }
+  // fp32 carried states in place on both paths: the per-sequence states read
+  // them, and the chunk scan rounds them to its operand precision itself
+  SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dAp, initial_states, final_states, s)));
+  SSD_TRY(from_hip(ssd::launch_varlen_states(d, x, Bm, bf, dtb, dA, sst, st, nseq, seq_last, seq_states, s)));
+  SSD_TRY(from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, false, D, y, y_dtype == SSD_BF16, f32m,
+                                          s, sst)));
   return SSD_OK;
 }
 

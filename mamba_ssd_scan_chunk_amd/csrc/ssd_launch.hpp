@@ -83,6 +83,13 @@ hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* Bm, const
                              const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream,
                              const int* seq_start = nullptr);
 
+// Packed sequences: the state after token last_token[s] (flattened b*L+t) of
+// its sequence, for s < nseq -> out [nseq,H,N,P] fp32; carried = the fp32
+// states entering each chunk [B,nc,H,N,P].
+hipError_t launch_varlen_states(const Dims& d, const void* x, const void* Bm, bool in_bf16, const float* dt_bhl,
+                                const float* dA_cumsum, const int* seq_start, const float* carried,
+                                int64_t nseq, const int64_t* last_token, float* out, hipStream_t stream);
+
 // Single-token recurrent step: state [Bn,H,N,P] fp32 updated in place, y
 // [Bn,H,P].  Supported for P a multiple of 4 up to 1024.
 bool decode_step_supported(int64_t P);

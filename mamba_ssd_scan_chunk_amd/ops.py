@@ -247,11 +247,13 @@ def ssd_forward(shape, x, dt, A, Bm, Cm, D, initial_states=None, y=None, y_dtype
 
 
 def ssd_forward_varlen(shape, x, dt, A, Bm, Cm, D, seq_idx, initial_states=None, y=None, y_dtype=None,
-                       final_states=None, want_final=True, workspace=None, mma="bf16",
-                       stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                       final_states=None, want_final=True, seq_last=None, seq_states=None, workspace=None,
+                       mma="bf16", stream=None):
     """One-call forward over packed sequences: seq_idx [B,L] int32 names each
     token's sequence; the state restarts from zero wherever it changes along
-    a row.  Returns (y, final_states of each row's last sequence or None)."""
+    a row.  Returns (y, final_states of each row's last sequence or None) and,
+    when seq_last (int64 [nseq] flattened token indices b*L+t) is given, also
+    seq_states [nseq,H,N,P]: the state after each of those tokens."""
     sh = _shape(shape)
     B, L, H, P, N, G, Q, nc = _dims(sh)
     io = (torch.float32, torch.bfloat16)
@@ -273,6 +275,13 @@ def ssd_forward_varlen(shape, x, dt, A, Bm, Cm, D, seq_idx, initial_states=None,
         final_states = torch.empty((B, H, N, P), device=x.device, dtype=torch.float32)
     if final_states is not None:
         _req(final_states, "final_states", (B, H, N, P), f32)
+    nseq = 0
+    if seq_last is not None:
+        _req(seq_last, "seq_last", (seq_last.numel(),), (torch.int64,))
+        nseq = seq_last.numel()
+        if seq_states is None:
+            seq_states = torch.empty((nseq, H, N, P), device=x.device, dtype=torch.float32)
+        _req(seq_states, "seq_states", (nseq, H, N, P), f32)
     lib = load_library()
     need = int(lib.ssd_workspace_bytes_varlen(sh))
     if workspace is None:
@@ -281,8 +290,11 @@ def ssd_forward_varlen(shape, x, dt, A, Bm, Cm, D, seq_idx, initial_states=None,
         raise ValueError("workspace must be a contiguous GPU tensor")
     check(lib.ssd_forward_varlen(sh, _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _DT[x.dtype],
                                  _ptr(seq_idx), _ptr(initial_states), _ptr(y), _DT[y.dtype], _ptr(final_states),
+                                 nseq, _ptr(seq_last if nseq else None), _ptr(seq_states if nseq else None),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _mma(mma),
                                  _stream(stream)))
+    if seq_last is not None:
+        return y, final_states, seq_states
     return y, final_states
 
 

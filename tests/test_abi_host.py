@@ -194,12 +194,19 @@ def test_forward_varlen_checks(lib):
     assert lib.ssd_workspace_bytes_varlen(s) == need
     assert lib.ssd_workspace_bytes_varlen(None) == 0
     a = [FAKE] * 6  # x, dt, A, Bm, Cm, D
-    assert lib.ssd_forward_varlen(s, *a, 1, None, None, FAKE, 1, FAKE, FAKE, need, 0, None) == NULL
-    assert lib.ssd_forward_varlen(s, *a, 1, FAKE, None, FAKE, 1, FAKE, FAKE, need - 1, 0, None) == WS
-    assert lib.ssd_forward_varlen(s, *a, 1, FAKE, None, FAKE, 1, FAKE, None, need, 0, None) == WS
-    assert lib.ssd_forward_varlen(s, *a, 1, FAKE + 4, None, FAKE, 1, FAKE, FAKE, need, 0, None) == ALIGN
-    assert lib.ssd_forward_varlen(s, *a, 7, FAKE, None, FAKE, 1, FAKE, FAKE, need, 0, None) == DTYPE
-    assert lib.ssd_forward_varlen(shape(headdim=24), *a, 1, FAKE, None, FAKE, 1, FAKE, FAKE, need, 0, None) == UNSUP
+    call = lambda sh, in_, sq, ws, wsb, nseq=0, last=None, st=None, mma=0: lib.ssd_forward_varlen(
+        sh, *a, in_, sq, None, FAKE, 1, FAKE, nseq, last, st, ws, wsb, mma, None)
+    assert call(s, 1, None, FAKE, need) == NULL
+    assert call(s, 1, FAKE, FAKE, need - 1) == WS
+    assert call(s, 1, FAKE, None, need) == WS
+    assert call(s, 1, FAKE + 4, FAKE, need) == ALIGN
+    assert call(s, 7, FAKE, FAKE, need) == DTYPE
+    assert call(shape(headdim=24), 1, FAKE, FAKE, need) == UNSUP
+    # requested per-sequence states need both arrays, aligned, and nseq >= 0
+    assert call(s, 1, FAKE, FAKE, need, nseq=3, last=None, st=FAKE) == NULL
+    assert call(s, 1, FAKE, FAKE, need, nseq=3, last=FAKE, st=None) == NULL
+    assert call(s, 1, FAKE, FAKE, need, nseq=3, last=FAKE + 8, st=FAKE) == ALIGN
+    assert call(s, 1, FAKE, FAKE, need, nseq=-1) == SHAPE
 
 
 def test_bf16_carried_has_no_in_place_form(lib):

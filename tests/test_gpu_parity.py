@@ -500,8 +500,21 @@ def test_forward_packed_sequences(case, mma, with_h0):
     sq = torch.from_numpy(_packed_seq_idx(rows, L)).cuda()
     h0 = _h0(inp) if with_h0 else None
     h0_t = None if h0 is None else torch.from_numpy(h0).cuda()
-    y, fin = ops.ssd_forward_varlen(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], sq,
-                                    initial_states=h0_t, y_dtype="f32", mma=mma)
+    # per-sequence states: after every sequence's last token, and after a token
+    # inside each sequence longer than 2 (its middle)
+    last, probes = [], []
+    for b, lens in enumerate(rows):
+        s0 = 0
+        for k, n in enumerate(lens):
+            last.append(b * L + s0 + n - 1)
+            probes.append((b, k, s0, n))
+            if n > 2:
+                last.append(b * L + s0 + n // 2 - 1)
+                probes.append((b, k, s0, n // 2))
+            s0 += n
+    last_t = torch.tensor(last, dtype=torch.int64, device="cuda")
+    y, fin, sst = ops.ssd_forward_varlen(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], sq,
+                                         initial_states=h0_t, y_dtype="f32", mma=mma, seq_last=last_t)
     torch.cuda.synchronize()
     o = oracle()
     for b, lens in enumerate(rows):
@@ -516,6 +529,15 @@ def test_forward_packed_sequences(case, mma, with_h0):
         ef = relerr(fin[b:b + 1], fref)
         say(f"  row {b}: {len(lens)} sequences, final rel err {ef:.3g}")
         assert ef <= tol_for(mma)
+    # the states after the requested tokens
+    worst = 0.0
+    for q, (b, k, s0, n) in enumerate(probes):
+        sl = lambda a: np.ascontiguousarray(a[b:b + 1, s0:s0 + n])
+        hk = h0[b:b + 1] if (h0 is not None and k == 0) else None
+        _, sref = o.forward(sl(inp.x), sl(inp.dt), inp.A, sl(inp.Bm), sl(inp.Cm), inp.D, h0=hk)
+        worst = max(worst, relerr(sst[q:q + 1], sref))
+    say(f"  {len(probes)} requested states: worst rel err {worst:.3g}")
+    assert worst <= tol_for(mma)
     # one sequence per row reproduces the plain forward bit for bit
     one = torch.zeros((B, L), dtype=torch.int32, device="cuda")
     y1, f1 = ops.ssd_forward_varlen(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], one,
