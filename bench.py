@@ -122,6 +122,8 @@ def main():
                     help="forwards timed one by one after a 1 GiB cache flush (0: skip)")
     ap.add_argument("--decode-batch", type=int, default=64,
                     help="sequences in the timed single-token decode step (0: skip it)")
+    ap.add_argument("--backward-steps", type=int, default=10,
+                    help="gradient calls (ssd_backward) timed at the workload (0: skip)")
     ap.add_argument("--no-cumsum-sweep", dest="cumsum_sweep", action="store_false",
                     help="skip the chunk_cumsum bandwidth-vs-length sweep")
     ap.add_argument("--kernel-only", default=None,
@@ -302,6 +304,31 @@ def main():
                "hbm_frac": round(dbytes / (dus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
         del xd, dtd, Bd, Cd, sd, yd
 
+    # Gradient call at the same workload (dy in the input dtype, dL/dfinal
+    # given): every product runs as an fp32 chunked pass, so this is reported
+    # beside the forward, not as the headline.
+    bwd = None
+    if args.backward_steps > 0:
+        g = torch.Generator(device=dev).manual_seed(9)
+        dyb = torch.randn((B, L, H, P), device=dev, generator=g).to(t["x"].dtype)
+        dfb = torch.randn((B, H, N, P), device=dev, generator=g)
+        wsb = torch.empty(ops.ssd_backward_workspace_bytes(sh), device=dev, dtype=torch.uint8)
+        step_b = lambda: ops.ssd_backward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], dyb, dfinal=dfb,
+                                          workspace=wsb)
+        for _ in range(2):
+            step_b()
+        torch.cuda.synchronize()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(args.backward_steps):
+            step_b()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bms = b0.elapsed_time(b1) / args.backward_steps
+        bwd = {"steps": args.backward_steps, "ms": round(bms, 4), "tokens_per_s": round(B * L / (bms * 1e-3), 1),
+               "workspace_GB": round(wsb.numel() / 1e9, 2), "vs_forward_ms": round(bms / ms_per_step, 2)}
+        del dyb, dfb, wsb
+
     # ssd_chunk_cumsum alone against sequence length at the workload's B and H:
     # at the headline (B L H = 1.3 M tokens x heads, 15.7 MB) launch and ramp
     # dominate; the sweep shows where the kernel reaches the HBM roofline.
@@ -376,6 +403,7 @@ def main():
         "copy_GBps": round(copy_gbps, 1),
         "cold_cache": cold,
         "decode_step": dec,
+        "backward": bwd,
         "cumsum_sweep": sweep,
     }
     if not args.no_cpu_baseline:

@@ -245,6 +245,40 @@ ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float
 /* Workspace bytes ssd_forward_varlen needs (0 for an invalid or NULL shape). */
 size_t ssd_workspace_bytes_varlen(const ssd_shape* shape);
 
+/*
+ * Gradients of ssd_forward (the same recurrence; no packed sequences) for a
+ * loss whose derivative is dy (dL/dy, [B,L,H,P], dtype dy_dtype) and dfinal
+ * (dL/d final_states, [B,H,N,P] fp32, or NULL: zero).  The pages only preview
+ * a backward pass, without its formulas: what is computed is the derivative
+ * of the recurrence (page "Jane Street ML Engineers Map Mamba-2 Recurrent
+ * State Computation to Tensor Cores with cuTile", opening and jump-formula
+ * paragraphs) with the adjoint state g_t = dL/dh_t, which obeys the same
+ * recurrence backwards in time (g_t = C_t dy_t^T + exp(dt_{t+1} A) g_{t+1}):
+ *   dx_t  = D dy_t + dt_t B_t^T g_t          dB_t = sum over the group's heads of dt_t g_t x_t
+ *   dC_t  = sum over the group's heads of h_t dy_t
+ *   ddt_t = A exp(dt_t A) <g_t, h_{t-1}> + B_t^T g_t x_t
+ *   dA    = sum_t dt_t exp(dt_t A) <g_t, h_{t-1}>,  dD = sum_t dy_t . x_t
+ *   dinitial = exp(dt_0 A) g_0
+ * ddt is the derivative with respect to the dt given to the forward.
+ * Inputs as for ssd_forward (x, Bm, Cm of dtype `in`; initial_states may be
+ * NULL).  Outputs, all fp32 and device: dx like x, ddt [B,L,H], dA [H],
+ * dB and dC [B,L,G,N], dD [H], dinitial [B,H,N,P] (may be NULL: not written).
+ * Every product runs as a chunked forward pass of this library's kernels in
+ * fp32 arithmetic with fp32 matrix operands (the forward recomputed, the
+ * adjoint, and both with the state transposed), followed by elementwise
+ * combining kernels.  workspace (device, 16-byte aligned) of at least
+ * ssd_backward_workspace_bytes(shape) bytes; it also requires the chunk
+ * kernels' fp32 form for both (P, N) and (N, P).  Errors as for ssd_forward.
+ */
+ssd_status ssd_backward(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* Bm,
+                        const void* Cm, const float* D, ssd_dtype in, const float* initial_states, const void* dy,
+                        ssd_dtype dy_dtype, const float* dfinal, float* dx, float* ddt, float* dA, float* dB,
+                        float* dC, float* dD, float* dinitial, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Workspace bytes ssd_backward needs (0 for an invalid or NULL shape). */
+size_t ssd_backward_workspace_bytes(const ssd_shape* shape);
+
 /* Static, NUL-terminated description of a status code. */
 const char* ssd_status_string(ssd_status status);
 

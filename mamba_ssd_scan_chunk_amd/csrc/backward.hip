@@ -1,0 +1,436 @@
+// backward.hip -- gradients of the SSD forward, composed from forward passes.
+//
+// Page: "Jane Street ML Engineers Map Mamba-2 Recurrent State Computation to
+// Tensor Cores with cuTile" (disconfirmai.com): the backward pass is
+// previewed, not published.  What is computed is the derivative of the same
+// recurrence (opening and jump-formula paragraphs),
+//     h_t = r_t h_{t-1} + dt_t B_t x_t^T,  r_t = exp(dt_t A),  y_t = C_t^T h_t + D x_t,
+// for a loss with dL/dy = dy and dL/dh_{L-1} = dfinal.  The adjoint state
+// g_t = dL/dh_t satisfies g_t = C_t dy_t^T + r_{t+1} g_{t+1}: read backwards in
+// time that is again this recurrence, with the decay of each step taken from
+// dt_{t+1} (none at the last token), input scale 1, B-role C, x-role dy and
+// initial state dfinal.  So every product below is a chunked forward run by the
+// existing kernels (fp32 operands and fp32 matrix cores), and the glue here
+// only reverses, widens, expands and combines:
+//   (0) forward:                      y0_t = C_t^T h_t, carried states h
+//   (1) adjoint, reversed:            y1 = B_t^T g_t            -> dx = dt y1 + D dy;  final = g_0
+//   (2) adjoint transposed, reversed: y2 = g_t x_t  (N-vector)  -> dB, beta_t = B_t . g_t x_t
+//   (3) forward transposed:           y3 = h_t dy_t (N-vector)  -> dC
+// The reversed passes run over nc*Q steps, the sequence padded at its far end
+// (zero inputs, no decay), so that their chunk edges fall on the forward's.
+// The log-decay gradient needs q_t = <g_t, h_t>, since
+//   dL/d(dt_t A) = r_t <g_t, h_{t-1}> = q_t - dt_t beta_t,
+//   ddt_t = A dL/d(dt_t A) + beta_t,  dA = sum_t dt_t dL/d(dt_t A).
+// Within a chunk q follows q_{t+1} = q_t - dy_t . y0_t + dt_{t+1} beta_{t+1};
+// that sum has no decay, so its rounding would pile up over a whole sequence.
+// Each chunk therefore starts from an exact anchor, the inner product of the
+// carried states at its first token, <g_{kQ}, h_{kQ-1}>, which both state
+// passes already hold.  dD = sum_t dy_t . x_t and dh0 = r_0 g_0.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+// out[b, s, k, e] = in[b, t(s), k / (KO / KI), e] in fp32 for s < Lout, with
+// t(s) = s, or Lout-1-s when reversing; rows with t >= Lin are zero.  KO/KI
+// maps output slots to input slots (heads -> groups when expanding B or C).
+__global__ __launch_bounds__(256) void gather_rows_kernel(const void* __restrict__ in, int in_bf16,
+                                                          float* __restrict__ out, int Lin, int Lout, int KO, int KI,
+                                                          int E, int reverse, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int e = (int)(i % E);
+  int64_t r = i / E;
+  const int k = (int)(r % KO);
+  r /= KO;
+  const int s = (int)(r % Lout);
+  const int64_t b = r / Lout;
+  const int t = reverse ? Lout - 1 - s : s;
+  const int ki = k / (KO / KI);
+  out[i] = t < Lin ? load1_as_f32(in, ((b * Lin + t) * KI + ki) * E + e, in_bf16 != 0) : 0.f;
+}
+
+// dt of the reversed adjoint over Lp steps: step s carries token t = Lp-1-s and
+// decays by dt_{t+1}, so dts[b, s, h] = dt[b, Lp - s, h] where Lp - s < L, else 0.
+__global__ __launch_bounds__(256) void shift_reverse_dt_kernel(const float* __restrict__ dt, float* __restrict__ dts,
+                                                               int L, int Lp, int H, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int h = (int)(i % H);
+  const int64_t r = i / H;
+  const int s = (int)(r % Lp);
+  const int64_t b = r / Lp;
+  const int idx = Lp - s;
+  dts[i] = idx < L ? dt[(b * L + idx) * H + h] : 0.f;
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, float v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// [B*H][R][C] -> [B*H][C][R]
+__global__ __launch_bounds__(256) void transpose_states_kernel(const float* __restrict__ in, float* __restrict__ out,
+                                                               int R, int C, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // output element
+  if (i >= n) return;
+  const int r = (int)(i % R);
+  const int64_t q = i / R;
+  const int c = (int)(q % C);
+  const int64_t m = q / C;
+  out[i] = in[(m * R + r) * C + c];
+}
+
+// anc[b, h, k] = <g_{kQ}, h_{kQ-1}>: for k >= 1 the adjoint's carried state
+// entering its reversed chunk nc-k and the forward's carried state entering
+// chunk k; for k = 0 the adjoint's final state (g_0) and the initial state
+// (zero when absent).  One block per (b, k, h); states are [B, nc, H, N*P].
+__global__ __launch_bounds__(256) void anchor_dot_kernel(const float* __restrict__ fwd_carried,
+                                                         const float* __restrict__ adj_carried,
+                                                         const float* __restrict__ adj_final,
+                                                         const float* __restrict__ h0, float* __restrict__ anc, int H,
+                                                         int nc, int64_t NP) {
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x % H;
+  const int k = (blockIdx.x / H) % nc;
+  const int64_t b = blockIdx.x / H / nc;
+  const float* gp = k == 0 ? adj_final + (b * H + h) * NP : adj_carried + ((b * nc + (nc - k)) * H + h) * NP;
+  const float* hp = k == 0 ? (h0 ? h0 + (b * H + h) * NP : nullptr) : fwd_carried + ((b * nc + k) * H + h) * NP;
+  float sum = 0.f;
+  if (hp)
+    for (int64_t e = 4 * tid; e < NP; e += 4 * 256) {
+      const float4 gv = *reinterpret_cast<const float4*>(gp + e);
+      const float4 hv = *reinterpret_cast<const float4*>(hp + e);
+      sum = fmaf(gv.x, hv.x, fmaf(gv.y, hv.y, fmaf(gv.z, hv.z, fmaf(gv.w, hv.w, sum))));
+    }
+  red[tid] = sum;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) anc[(b * H + h) * nc + k] = red[0];
+}
+
+// Per (b, t, h): dx, beta_t = B_t . (g_t x_t), v_t = dy_t . y0_t, u_t = dy_t . x_t.
+// One wave per (b, t, h); y1 and y2 are in reversed time over Lp steps.
+__global__ __launch_bounds__(256) void combine_token_kernel(
+    const float* __restrict__ dy, const float* __restrict__ xf, const float* __restrict__ Bf,
+    const float* __restrict__ dt, const float* __restrict__ D, const float* __restrict__ y0,
+    const float* __restrict__ y1, const float* __restrict__ y2, float* __restrict__ dx, float* __restrict__ beta,
+    float* __restrict__ v, float* __restrict__ u, int L, int Lp, int H, int P, int N, int G, int64_t nrows) {
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);  // (b * L + t) * H + h
+  const int lane = threadIdx.x & 63;
+  if (row >= nrows) return;
+  const int h = (int)(row % H);
+  const int64_t bt = row / H;
+  const int t = (int)(bt % L);
+  const int64_t b = bt / L;
+  const int g = h / (H / G);
+  const int64_t rrow = (b * Lp + (Lp - 1 - t)) * H + h;  // the same token in reversed time
+  const float dtv = dt[row], dh = D[h];
+  float sv = 0.f, su = 0.f, sb = 0.f;
+  for (int p = lane; p < P; p += 64) {
+    const float dyv = dy[row * P + p], xv = xf[row * P + p];
+    dx[row * P + p] = fmaf(dtv, y1[rrow * P + p], dh * dyv);
+    sv = fmaf(dyv, y0[row * P + p], sv);
+    su = fmaf(dyv, xv, su);
+  }
+  for (int n = lane; n < N; n += 64) sb = fmaf(Bf[(bt * G + g) * N + n], y2[rrow * N + n], sb);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    sv += __shfl_xor(sv, off, 64);
+    su += __shfl_xor(su, off, 64);
+    sb += __shfl_xor(sb, off, 64);
+  }
+  if (lane == 0) {
+    v[row] = sv;
+    u[row] = su;
+    beta[row] = sb;
+  }
+}
+
+// dB[b,t,g,n] = sum_{h in g} dt[b,t,h] y2[b, Lp-1-t, h, n];  dC[b,t,g,n] = sum_{h in g} y3[b,t,h,n]
+__global__ __launch_bounds__(256) void combine_group_kernel(const float* __restrict__ dt, const float* __restrict__ y2,
+                                                            const float* __restrict__ y3, float* __restrict__ dB,
+                                                            float* __restrict__ dC, int L, int Lp, int H, int N,
+                                                            int G, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // element of [B,L,G,N]
+  if (i >= n) return;
+  const int e = (int)(i % N);
+  int64_t r = i / N;
+  const int g = (int)(r % G);
+  const int64_t bt = r / G;
+  const int t = (int)(bt % L);
+  const int64_t b = bt / L;
+  const int hpg = H / G;
+  float sb = 0.f, sc = 0.f;
+  for (int k = 0; k < hpg; ++k) {
+    const int h = g * hpg + k;
+    sb = fmaf(dt[bt * H + h], y2[((b * Lp + (Lp - 1 - t)) * H + h) * N + e], sb);
+    sc += y3[(bt * H + h) * N + e];
+  }
+  dB[i] = sb;
+  dC[i] = sc;
+}
+
+// One wave per (b, h, chunk k): q over the chunk's tokens from its anchor,
+//   q_{t0} = r_{t0} anc + dt_{t0} beta_{t0},  q_t = q_{t-1} - v_{t-1} + dt_t beta_t,
+// as a wave prefix sum (each lane a run of up to Q/64 tokens); then ddt and the
+// chunk's shares of dA and dD.
+constexpr int kBwdMaxPer = 4;  // Q <= 256
+__global__ __launch_bounds__(256) void chunk_grad_kernel(const float* __restrict__ dt, const float* __restrict__ A,
+                                                         const float* __restrict__ beta, const float* __restrict__ v,
+                                                         const float* __restrict__ u, const float* __restrict__ anc,
+                                                         float* __restrict__ ddt, float* __restrict__ dA_part,
+                                                         float* __restrict__ dD_part, int L, int H, int Q, int nc,
+                                                         int64_t nwaves) {
+  const int64_t w = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);  // (b * H + h) * nc + k
+  const int lane = threadIdx.x & 63;
+  if (w >= nwaves) return;
+  const int k = (int)(w % nc);
+  const int64_t bh = w / nc;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  const float a = A[h];
+  const int t0 = k * Q, t1 = min(L, t0 + Q);
+  const int per = (Q + 63) / 64;
+  auto at = [&](int t) -> int64_t { return (b * L + t) * H + h; };
+  float z[kBwdMaxPer], dtv[kBwdMaxPer], be[kBwdMaxPer];
+  float run = 0.f;
+#pragma unroll
+  for (int j = 0; j < kBwdMaxPer; ++j) {
+    const int t = t0 + lane * per + j;
+    z[j] = dtv[j] = be[j] = 0.f;
+    if (j < per && t < t1) {
+      dtv[j] = dt[at(t)];
+      be[j] = beta[at(t)];
+      z[j] = t == t0 ? fmaf(expf(dtv[j] * a), anc[w], dtv[j] * be[j]) : dtv[j] * be[j] - v[at(t - 1)];
+    }
+    run += z[j];
+    z[j] = run;  // inclusive prefix within the lane's run
+  }
+  // exclusive scan of the run totals over the lanes
+  float incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  const float excl = incl - run;
+  float sa = 0.f, sd = 0.f;
+#pragma unroll
+  for (int j = 0; j < kBwdMaxPer; ++j) {
+    const int t = t0 + lane * per + j;
+    if (j < per && t < t1) {
+      const float q = excl + z[j];
+      const float dla = q - dtv[j] * be[j];
+      ddt[at(t)] = fmaf(a, dla, be[j]);
+      sa = fmaf(dtv[j], dla, sa);
+      sd += u[at(t)];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    sa += __shfl_xor(sa, off, 64);
+    sd += __shfl_xor(sd, off, 64);
+  }
+  if (lane == 0) {
+    dA_part[w] = sa;
+    dD_part[w] = sd;
+  }
+}
+
+// dh0[b, h] = exp(dt[b, 0, h] A[h]) g_0[b, h]
+__global__ __launch_bounds__(256) void dh0_kernel(const float* __restrict__ dt, const float* __restrict__ A,
+                                                  const float* __restrict__ g0, float* __restrict__ dh0, int L, int H,
+                                                  int64_t NP, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t bh = i / NP;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  dh0[i] = expf(dt[b * L * H + h] * A[h]) * g0[i];
+}
+
+// dA[h] = sum_{b,k} dA_part[b, h, k];  dD[h] likewise
+__global__ __launch_bounds__(256) void combine_heads_kernel(const float* __restrict__ dA_part,
+                                                            const float* __restrict__ dD_part, float* __restrict__ dA,
+                                                            float* __restrict__ dD, int B, int H, int nc) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  float sa = 0.f, sd = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int k = 0; k < nc; ++k) {
+      sa += dA_part[((int64_t)b * H + h) * nc + k];
+      sd += dD_part[((int64_t)b * H + h) * nc + k];
+    }
+  dA[h] = sa;
+  dD[h] = sd;
+}
+
+// ------------------------------------------------------------------ host side
+namespace {
+unsigned nblocks(int64_t n, int per = 256) { return (unsigned)((n + per - 1) / per); }
+size_t ru(size_t v) { return (v + 255) / 256 * 256; }
+
+// Workspace pieces, in order (all fp32).  Forward time: L tokens; reversed: Lp = nc*Q steps.
+enum BwdBuf {
+  kXf, kBf, kCf, kDyF, kBExp,                         // forward-time operands
+  kDyRev, kXRev, kBRev, kCRev, kCExpRev, kDtRev,      // reversed operands
+  kOnes, kZeroD, kH0T, kDfT,
+  kY0, kDA0, kDt0, kSt0,                              // (0)
+  kDA1, kDt1, kSt1, kY1, kFin1,                       // (1)
+  kSt2, kY2,                                          // (2)
+  kSt3, kY3,                                          // (3)
+  kAnc, kBeta, kV, kU, kDAp, kDDp, kNumBwd
+};
+
+struct BwdLayout {
+  size_t off[kNumBwd];
+  size_t total;
+};
+
+BwdLayout bwd_layout(const Dims& d) {
+  const size_t f = sizeof(float), B = d.B, L = d.L, Lp = d.nc * d.Q, H = d.H, P = d.P, N = d.N, G = d.G;
+  const size_t chunk_q = f * B * H * d.nc * d.Q, states = f * B * d.nc * H * N * P, bhnp = f * B * H * N * P;
+  size_t sz[kNumBwd] = {};
+  sz[kXf] = sz[kDyF] = f * B * L * H * P;
+  sz[kBf] = sz[kCf] = f * B * L * G * N;
+  sz[kBExp] = f * B * L * H * N;
+  sz[kDyRev] = sz[kXRev] = f * B * Lp * H * P;
+  sz[kBRev] = sz[kCRev] = f * B * Lp * G * N;
+  sz[kCExpRev] = f * B * Lp * H * N;
+  sz[kDtRev] = f * B * Lp * H;
+  sz[kOnes] = sz[kDA0] = sz[kDt0] = sz[kDA1] = sz[kDt1] = chunk_q;
+  sz[kZeroD] = f * H;
+  sz[kH0T] = sz[kDfT] = sz[kFin1] = bhnp;
+  sz[kSt0] = sz[kSt1] = sz[kSt2] = sz[kSt3] = states;
+  sz[kY0] = f * B * L * H * P;
+  sz[kY1] = f * B * Lp * H * P;
+  sz[kY2] = f * B * Lp * H * N;
+  sz[kY3] = f * B * L * H * N;
+  sz[kBeta] = sz[kV] = sz[kU] = f * B * L * H;
+  sz[kAnc] = sz[kDAp] = sz[kDDp] = f * B * H * d.nc;
+  BwdLayout w;
+  size_t o = 0;
+  for (int i = 0; i < kNumBwd; ++i) {
+    w.off[i] = o;
+    o = ru(o + sz[i]);
+  }
+  w.total = o;
+  return w;
+}
+}  // namespace
+
+size_t backward_workspace_bytes(const Dims& d) { return bwd_layout(d).total; }
+
+#define BWD_TRY(expr)                \
+  do {                               \
+    const hipError_t e_ = (expr);    \
+    if (e_ != hipSuccess) return e_; \
+  } while (0)
+
+hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const float* A, const void* Bm,
+                           const void* Cm, const float* D, bool in_bf16, const float* initial_states,
+                           const void* dy_in, bool dy_bf16, const float* dfinal, float* dx, float* ddt, float* dA,
+                           float* dB, float* dC, float* dD, float* dinit, void* workspace, hipStream_t s) {
+  const BwdLayout w = bwd_layout(d);
+  char* base = static_cast<char*>(workspace);
+  auto F = [&](int k) { return reinterpret_cast<float*>(base + w.off[k]); };
+  const int L = (int)d.L, Lp = (int)(d.nc * d.Q), H = (int)d.H, P = (int)d.P, N = (int)d.N, G = (int)d.G;
+  const int bf = in_bf16 ? 1 : 0;
+  const int64_t nxhp = d.B * d.L * d.H * d.P, nbgn = d.B * d.L * d.G * d.N, nbhn = d.B * d.L * d.H * d.N;
+  const int64_t rxhp = d.B * Lp * d.H * d.P, rbgn = d.B * Lp * d.G * d.N, rbhn = d.B * Lp * d.H * d.N;
+  // the reversed passes: Lp steps (whole chunks); the transposed ones: P and N
+  // swapped, one group per head
+  Dims dR = d;
+  dR.L = Lp;
+  Dims dT = d;
+  dT.N = d.P;
+  dT.P = d.N;
+  dT.G = d.H;
+  Dims dRT = dT;
+  dRT.L = Lp;
+
+  // ---- operands in fp32: forward order, reversed, and expanded per head
+  const float* dy = static_cast<const float*>(dy_in);
+  if (dy_bf16) {
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(nxhp)), dim3(256), 0, s, dy_in, 1, F(kDyF), L, L, H, H, P,
+                       0, nxhp);
+    dy = F(kDyF);
+  }
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(nxhp)), dim3(256), 0, s, x, bf, F(kXf), L, L, H, H, P, 0, nxhp);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(nbgn)), dim3(256), 0, s, Bm, bf, F(kBf), L, L, G, G, N, 0, nbgn);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(nbgn)), dim3(256), 0, s, Cm, bf, F(kCf), L, L, G, G, N, 0, nbgn);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(nbhn)), dim3(256), 0, s, Bm, bf, F(kBExp), L, L, H, G, N, 0,
+                     nbhn);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(rxhp)), dim3(256), 0, s, dy, 0, F(kDyRev), L, Lp, H, H, P, 1,
+                     rxhp);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(rxhp)), dim3(256), 0, s, x, bf, F(kXRev), L, Lp, H, H, P, 1,
+                     rxhp);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(rbgn)), dim3(256), 0, s, Bm, bf, F(kBRev), L, Lp, G, G, N, 1,
+                     rbgn);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(rbgn)), dim3(256), 0, s, Cm, bf, F(kCRev), L, Lp, G, G, N, 1,
+                     rbgn);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(rbhn)), dim3(256), 0, s, Cm, bf, F(kCExpRev), L, Lp, H, G, N,
+                     1, rbhn);
+  const int64_t nblh = d.B * d.L * d.H, rblh = d.B * Lp * d.H;
+  hipLaunchKernelGGL(shift_reverse_dt_kernel, dim3(nblocks(rblh)), dim3(256), 0, s, dt, F(kDtRev), L, Lp, H, rblh);
+  const int64_t nq = d.B * d.H * d.nc * d.Q;
+  hipLaunchKernelGGL(fill_kernel, dim3(nblocks(nq)), dim3(256), 0, s, F(kOnes), 1.f, nq);
+  hipLaunchKernelGGL(fill_kernel, dim3(nblocks(d.H)), dim3(256), 0, s, F(kZeroD), 0.f, (int64_t)d.H);
+  const int64_t nnp = d.B * d.H * d.N * d.P;
+  if (initial_states)
+    hipLaunchKernelGGL(transpose_states_kernel, dim3(nblocks(nnp)), dim3(256), 0, s, initial_states, F(kH0T), N, P,
+                       nnp);
+  if (dfinal)
+    hipLaunchKernelGGL(transpose_states_kernel, dim3(nblocks(nnp)), dim3(256), 0, s, dfinal, F(kDfT), N, P, nnp);
+  BWD_TRY(hipGetLastError());
+
+  // ---- (0) forward: y0 = C^T h (no skip term), carried states
+  BWD_TRY(launch_chunk_cumsum(d, dt, A, F(kDA0), F(kDt0), s));
+  BWD_TRY(launch_chunk_state(d, F(kXf), F(kBf), false, F(kDt0), F(kDA0), F(kSt0), true, s));
+  BWD_TRY(launch_state_passing(d, F(kSt0), F(kSt0), F(kDA0), initial_states, nullptr, s));
+  BWD_TRY(launch_chunk_scan(d, F(kXf), F(kBf), F(kCf), false, F(kDt0), F(kDA0), F(kSt0), false, F(kZeroD), F(kY0),
+                            false, true, s));
+
+  // ---- (1) adjoint in reversed time: decay from the shifted dt, input scale 1
+  BWD_TRY(launch_chunk_cumsum(dR, F(kDtRev), A, F(kDA1), F(kDt1), s));
+  BWD_TRY(launch_chunk_state(dR, F(kDyRev), F(kCRev), false, F(kOnes), F(kDA1), F(kSt1), true, s));
+  BWD_TRY(launch_state_passing(dR, F(kSt1), F(kSt1), F(kDA1), dfinal, F(kFin1), s));
+  BWD_TRY(launch_chunk_scan(dR, F(kDyRev), F(kCRev), F(kBRev), false, F(kOnes), F(kDA1), F(kSt1), false, F(kZeroD),
+                            F(kY1), false, true, s));
+
+  // ---- (2) adjoint transposed (state P x N per head: B-role dy, x-role C, C-role x)
+  BWD_TRY(launch_chunk_state(dRT, F(kCExpRev), F(kDyRev), false, F(kOnes), F(kDA1), F(kSt2), true, s));
+  BWD_TRY(launch_state_passing(dRT, F(kSt2), F(kSt2), F(kDA1), dfinal ? F(kDfT) : nullptr, nullptr, s));
+  BWD_TRY(launch_chunk_scan(dRT, F(kCExpRev), F(kDyRev), F(kXRev), false, F(kOnes), F(kDA1), F(kSt2), false,
+                            F(kZeroD), F(kY2), false, true, s));
+
+  // ---- (3) forward transposed (B-role x, x-role B, C-role dy): y3_t = h_t dy_t
+  BWD_TRY(launch_chunk_state(dT, F(kBExp), F(kXf), false, F(kDt0), F(kDA0), F(kSt3), true, s));
+  BWD_TRY(launch_state_passing(dT, F(kSt3), F(kSt3), F(kDA0), initial_states ? F(kH0T) : nullptr, nullptr, s));
+  BWD_TRY(launch_chunk_scan(dT, F(kBExp), F(kXf), dy, false, F(kDt0), F(kDA0), F(kSt3), false, F(kZeroD), F(kY3),
+                            false, true, s));
+
+  // ---- combine
+  hipLaunchKernelGGL(anchor_dot_kernel, dim3((unsigned)(d.B * d.nc * d.H)), dim3(256), 0, s, F(kSt0), F(kSt1),
+                     F(kFin1), initial_states, F(kAnc), H, (int)d.nc, d.N * d.P);
+  hipLaunchKernelGGL(combine_token_kernel, dim3(nblocks(nblh, 4)), dim3(256), 0, s, dy, F(kXf), F(kBf), dt, D,
+                     F(kY0), F(kY1), F(kY2), dx, F(kBeta), F(kV), F(kU), L, Lp, H, P, N, G, nblh);
+  hipLaunchKernelGGL(combine_group_kernel, dim3(nblocks(nbgn)), dim3(256), 0, s, dt, F(kY2), F(kY3), dB, dC, L, Lp,
+                     H, N, G, nbgn);
+  const int64_t nw = d.B * d.H * d.nc;
+  hipLaunchKernelGGL(chunk_grad_kernel, dim3(nblocks(nw, 4)), dim3(256), 0, s, dt, A, F(kBeta), F(kV), F(kU),
+                     F(kAnc), ddt, F(kDAp), F(kDDp), L, H, (int)d.Q, (int)d.nc, nw);
+  if (dinit)
+    hipLaunchKernelGGL(dh0_kernel, dim3(nblocks(nnp)), dim3(256), 0, s, dt, A, F(kFin1), dinit, L, H, d.N * d.P,
+                       nnp);
+  hipLaunchKernelGGL(combine_heads_kernel, dim3(nblocks(d.H)), dim3(256), 0, s, F(kDAp), F(kDDp), dA, dD, (int)d.B,
+                     H, (int)d.nc);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -338,6 +338,46 @@ ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float
   return SSD_OK;
 }
 
+size_t ssd_backward_workspace_bytes(const ssd_shape* shape) {
+  Dims d;
+  if (check_shape(shape, &d) != SSD_OK) return 0;
+  return ssd::backward_workspace_bytes(d);
+}
+
+ssd_status ssd_backward(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* Bm,
+                        const void* Cm, const float* D, ssd_dtype in, const float* initial_states, const void* dy,
+                        ssd_dtype dy_dtype, const float* dfinal, float* dx, float* ddt, float* dA, float* dB,
+                        float* dC, float* dD, float* dinitial, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  Dims d;
+  SSD_TRY(check_shape(shape, &d));
+  SSD_TRY(check_dtype(in));
+  SSD_TRY(check_dtype(dy_dtype));
+  if (!x || !dt || !A || !Bm || !Cm || !D || !dy || !dx || !ddt || !dA || !dB || !dC || !dD) return SSD_ERR_NULL;
+  if (!workspace) return SSD_ERR_WORKSPACE;
+  if (workspace_bytes < ssd::backward_workspace_bytes(d)) return SSD_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(Bm) || !aligned16(Cm) || !aligned16(D) ||
+      !aligned16(dy) || !aligned16(dx) || !aligned16(ddt) || !aligned16(dA) || !aligned16(dB) || !aligned16(dC) ||
+      !aligned16(dD) || !aligned16(workspace) || (initial_states && !aligned16(initial_states)) ||
+      (dfinal && !aligned16(dfinal)) || (dinitial && !aligned16(dinitial)))
+    return SSD_ERR_ALIGN;
+  // the transposed passes run the chunk kernels with P and N swapped and one
+  // group per head
+  Dims dT = d;
+  dT.P = d.N;
+  dT.N = d.P;
+  dT.G = d.H;
+  if (ssd::chunk_state_lds_bytes(d, true) > kLdsLimit || ssd::chunk_scan_lds_bytes(d, true) > kLdsLimit ||
+      ssd::chunk_state_lds_bytes(dT, true) > kLdsLimit || ssd::chunk_scan_lds_bytes(dT, true) > kLdsLimit)
+    return SSD_ERR_UNSUPPORTED;
+  // elementwise launches of 256 threads per block over B*L*H*max(P,N) elements
+  const int64_t wide = d.P > d.N ? d.P : d.N;
+  if (d.B * d.L * d.H > (int64_t(1) << 39) / wide) return SSD_ERR_UNSUPPORTED;
+  return from_hip(ssd::launch_backward(d, x, dt, A, Bm, Cm, D, in == SSD_BF16, initial_states, dy,
+                                       dy_dtype == SSD_BF16, dfinal, dx, ddt, dA, dB, dC, dD, dinitial, workspace,
+                                       (hipStream_t)stream));
+}
+
 const char* ssd_status_string(ssd_status status) {
   switch (status) {
     case SSD_OK: return "SSD_OK: success";
@@ -346,7 +386,7 @@ const char* ssd_status_string(ssd_status status) {
     case SSD_ERR_DTYPE: return "SSD_ERR_DTYPE: unknown dtype or mma mode";
     case SSD_ERR_UNSUPPORTED:
       return "SSD_ERR_UNSUPPORTED: shape outside this version's limits (P, N multiples of 16 and <= 256; "
-             "chunk in {32,64,128,256}; seqlen a multiple of chunk)";
+             "chunk in {32,64,128,256})";
     case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or smaller than ssd_workspace_bytes";
     case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: a pointer is not 16-byte aligned";
     case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP kernel launch failed";

@@ -97,4 +97,11 @@ hipError_t launch_decode_step(int64_t Bn, int64_t H, int64_t P, int64_t N, int64
                               const float* dt, const float* A, const void* Bm, const void* Cm, const float* D,
                               bool in_bf16, float* state, void* y, bool y_bf16, hipStream_t stream);
 
+// Gradients of the forward (see backward.hip); fp32 outputs, fp32 arithmetic.
+size_t backward_workspace_bytes(const Dims& d);
+hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const float* A, const void* Bm,
+                           const void* Cm, const float* D, bool in_bf16, const float* initial_states,
+                           const void* dy, bool dy_bf16, const float* dfinal, float* dx, float* ddt, float* dA,
+                           float* dB, float* dC, float* dD, float* dinit, void* workspace, hipStream_t stream);
+
 }  // namespace ssd

@@ -298,6 +298,49 @@ def ssd_forward_varlen(shape, x, dt, A, Bm, Cm, D, seq_idx, initial_states=None,
     return y, final_states
 
 
+def ssd_backward(shape, x, dt, A, Bm, Cm, D, dy, initial_states=None, dfinal=None, want_dinitial=True,
+                 workspace=None, stream=None) -> Dict[str, Optional[torch.Tensor]]:
+    """Gradients of ``ssd_forward`` for dL/dy = dy and dL/dfinal = dfinal
+    (None: zero).  Returns fp32 tensors dx, ddt, dA, dB, dC, dD and dinitial
+    (None unless ``want_dinitial``)."""
+    sh = _shape(shape)
+    B, L, H, P, N, G, Q, nc = _dims(sh)
+    io = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _req(x, "x", (B, L, H, P), io)
+    _req(dt, "dt", (B, L, H), f32)
+    _req(A, "A", (H,), f32)
+    _req(Bm, "Bm", (B, L, G, N), (x.dtype,))
+    _req(Cm, "Cm", (B, L, G, N), (x.dtype,))
+    _req(D, "D", (H,), f32)
+    _req(dy, "dy", (B, L, H, P), io)
+    if initial_states is not None:
+        _req(initial_states, "initial_states", (B, H, N, P), f32)
+    if dfinal is not None:
+        _req(dfinal, "dfinal", (B, H, N, P), f32)
+    dev = x.device
+    out = {"dx": torch.empty((B, L, H, P), device=dev), "ddt": torch.empty((B, L, H), device=dev),
+           "dA": torch.empty((H,), device=dev), "dB": torch.empty((B, L, G, N), device=dev),
+           "dC": torch.empty((B, L, G, N), device=dev), "dD": torch.empty((H,), device=dev),
+           "dinitial": torch.empty((B, H, N, P), device=dev) if want_dinitial else None}
+    lib = load_library()
+    need = int(lib.ssd_backward_workspace_bytes(sh))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    check(lib.ssd_backward(sh, _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _DT[x.dtype],
+                           _ptr(initial_states), _ptr(dy), _DT[dy.dtype], _ptr(dfinal), _ptr(out["dx"]),
+                           _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                           _ptr(out["dinitial"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream(stream)))
+    return out
+
+
+def ssd_backward_workspace_bytes(shape) -> int:
+    return int(load_library().ssd_backward_workspace_bytes(_shape(shape)))
+
+
 def shape_of(inp: Dict[str, torch.Tensor], chunk: int) -> SSDShape:
     """ssd_shape from x [B,L,H,P] and Bm [B,L,G,N]."""
     B, L, H, P = inp["x"].shape

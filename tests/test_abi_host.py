@@ -32,7 +32,8 @@ def test_header_declares_the_abi():
     names = declared_functions()
     for n in ["ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward",
               "ssd_chunk_state_passing", "ssd_decode_step", "ssd_forward_varlen", "ssd_workspace_bytes",
-              "ssd_workspace_bytes_varlen", "ssd_status_string", "ssd_abi_version"]:
+              "ssd_workspace_bytes_varlen", "ssd_backward", "ssd_backward_workspace_bytes", "ssd_status_string",
+              "ssd_abi_version"]:
         assert n in names
 
 
@@ -207,6 +208,40 @@ def test_forward_varlen_checks(lib):
     assert call(s, 1, FAKE, FAKE, need, nseq=3, last=FAKE, st=None) == NULL
     assert call(s, 1, FAKE, FAKE, need, nseq=3, last=FAKE + 8, st=FAKE) == ALIGN
     assert call(s, 1, FAKE, FAKE, need, nseq=-1) == SHAPE
+
+
+def test_backward_checks(lib):
+    """The gradient call validates shape, dtypes, required pointers, its
+    workspace and alignment before any HIP call; dfinal, initial_states and
+    dinitial are optional."""
+    s = shape()
+    B, L, H, P, N, Q = 2, 512, 4, 64, 128, 256
+    need = lib.ssd_backward_workspace_bytes(s)
+    # at least: the recomputed forward's and the adjoint's chunk states, fp32
+    assert need >= 2 * 4 * B * (L // Q) * H * N * P
+    assert lib.ssd_backward_workspace_bytes(None) == 0
+    assert lib.ssd_backward_workspace_bytes(shape(batch=0)) == 0
+    a = [FAKE] * 6  # x, dt, A, Bm, Cm, D
+
+    def call(sh, in_=1, dy=FAKE, dy_t=1, outs=None, ws=FAKE, wsb=need, h0=None, dfin=None, dinit=None):
+        o = [FAKE] * 6 if outs is None else outs  # dx, ddt, dA, dB, dC, dD
+        return lib.ssd_backward(sh, *a, in_, h0, dy, dy_t, dfin, *o, dinit, ws, wsb, None)
+
+    assert call(s, dy=None) == NULL
+    for k in range(6):
+        o = [FAKE] * 6
+        o[k] = None
+        assert call(s, outs=o) == NULL
+    assert call(s, ws=None) == WS
+    assert call(s, wsb=need - 1) == WS
+    assert call(s, in_=7) == DTYPE
+    assert call(s, dy_t=7) == DTYPE
+    assert call(s, dy=FAKE + 4) == ALIGN
+    assert call(s, dinit=FAKE + 8) == ALIGN
+    assert call(s, dfin=FAKE + 2) == ALIGN
+    assert call(s, h0=FAKE + 2) == ALIGN
+    assert call(shape(headdim=24), wsb=1 << 40) == UNSUP
+    assert call(shape(nheads=6, ngroups=4)) == SHAPE
 
 
 def test_bf16_carried_has_no_in_place_form(lib):
