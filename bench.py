@@ -108,6 +108,37 @@ def cpu_baseline(inp, w, target_s=10.0):
                       f"workload in {t:.2f} s; tokens/s scaled by the sampled fraction"}
 
 
+def time_backward(ops, torch, t, sh, steps, fwd_ms=None, modes=("bf16", "f32")):
+    """ssd_backward at the workload (dy in the input dtype, dL/dfinal given),
+    `steps` calls per matrix-operand mode after two untimed ones."""
+    B, L, H, P = t["x"].shape
+    N = t["Bm"].shape[3]
+    dev, stream = t["x"].device, torch.cuda.current_stream()
+    g = torch.Generator(device=dev).manual_seed(9)
+    dyb = torch.randn((B, L, H, P), device=dev, generator=g).to(t["x"].dtype)
+    dfb = torch.randn((B, H, N, P), device=dev, generator=g)
+    wsb = torch.empty(ops.ssd_backward_workspace_bytes(sh), device=dev, dtype=torch.uint8)
+    out = {"steps": steps, "workspace_GB": round(wsb.numel() / 1e9, 2)}
+    for bm in modes:
+        step_b = lambda: ops.ssd_backward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], dyb, dfinal=dfb,
+                                          workspace=wsb, mma=bm)
+        for _ in range(2):
+            step_b()
+        torch.cuda.synchronize()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(steps):
+            step_b()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bms = b0.elapsed_time(b1) / steps
+        out[f"mma_{bm}"] = {"ms": round(bms, 4), "tokens_per_s": round(B * L / (bms * 1e-3), 1)}
+        if fwd_ms:
+            out[f"mma_{bm}"]["vs_forward_ms"] = round(bms / fwd_ms, 2)
+    del dyb, dfb, wsb
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +155,8 @@ def main():
                     help="sequences in the timed single-token decode step (0: skip it)")
     ap.add_argument("--backward-steps", type=int, default=10,
                     help="gradient calls (ssd_backward) timed at the workload (0: skip)")
+    ap.add_argument("--backward-only", default=None, choices=["bf16", "f32"],
+                    help="time only ssd_backward in this operand mode (--backward-steps calls) and print that")
     ap.add_argument("--no-cumsum-sweep", dest="cumsum_sweep", action="store_false",
                     help="skip the chunk_cumsum bandwidth-vs-length sweep")
     ap.add_argument("--kernel-only", default=None,
@@ -161,6 +194,10 @@ def main():
     fin = torch.empty((B, H, N, P), device=dev, dtype=torch.float32)
     ws = torch.empty(ops.ssd_workspace_bytes(sh), device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream()
+    if args.backward_only:
+        bwd = time_backward(ops, torch, t, sh, max(args.backward_steps, 1), modes=(args.backward_only,))
+        print(json.dumps({"workload": name, "backward": bwd}), flush=True)
+        return
 
     def step():
         ops.ssd_forward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], y=y, final_states=fin,
@@ -304,30 +341,8 @@ def main():
                "hbm_frac": round(dbytes / (dus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
         del xd, dtd, Bd, Cd, sd, yd
 
-    # Gradient call at the same workload (dy in the input dtype, dL/dfinal
-    # given): every product runs as an fp32 chunked pass, so this is reported
-    # beside the forward, not as the headline.
-    bwd = None
-    if args.backward_steps > 0:
-        g = torch.Generator(device=dev).manual_seed(9)
-        dyb = torch.randn((B, L, H, P), device=dev, generator=g).to(t["x"].dtype)
-        dfb = torch.randn((B, H, N, P), device=dev, generator=g)
-        wsb = torch.empty(ops.ssd_backward_workspace_bytes(sh), device=dev, dtype=torch.uint8)
-        step_b = lambda: ops.ssd_backward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], dyb, dfinal=dfb,
-                                          workspace=wsb)
-        for _ in range(2):
-            step_b()
-        torch.cuda.synchronize()
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b0.record(stream)
-        for _ in range(args.backward_steps):
-            step_b()
-        b1.record(stream)
-        torch.cuda.synchronize()
-        bms = b0.elapsed_time(b1) / args.backward_steps
-        bwd = {"steps": args.backward_steps, "ms": round(bms, 4), "tokens_per_s": round(B * L / (bms * 1e-3), 1),
-               "workspace_GB": round(wsb.numel() / 1e9, 2), "vs_forward_ms": round(bms / ms_per_step, 2)}
-        del dyb, dfb, wsb
+    # Gradient call at the same workload, reported beside the forward.
+    bwd = time_backward(ops, torch, t, sh, args.backward_steps, ms_per_step) if args.backward_steps > 0 else None
 
     # ssd_chunk_cumsum alone against sequence length at the workload's B and H:
     # at the headline (B L H = 1.3 M tokens x heads, 15.7 MB) launch and ramp

@@ -263,18 +263,21 @@ size_t ssd_workspace_bytes_varlen(const ssd_shape* shape);
  * Inputs as for ssd_forward (x, Bm, Cm of dtype `in`; initial_states may be
  * NULL).  Outputs, all fp32 and device: dx like x, ddt [B,L,H], dA [H],
  * dB and dC [B,L,G,N], dD [H], dinitial [B,H,N,P] (may be NULL: not written).
- * Every product runs as a chunked forward pass of this library's kernels in
- * fp32 arithmetic with fp32 matrix operands (the forward recomputed, the
- * adjoint, and both with the state transposed), followed by elementwise
- * combining kernels.  workspace (device, 16-byte aligned) of at least
- * ssd_backward_workspace_bytes(shape) bytes; it also requires the chunk
- * kernels' fp32 form for both (P, N) and (N, P).  Errors as for ssd_forward.
+ * Every product runs as a chunked forward pass of this library's kernels (the
+ * forward recomputed, the adjoint, and both with the state transposed),
+ * followed by elementwise combining kernels.  mma selects the matrix-core
+ * operands of those passes as for ssd_forward: SSD_MMA_F32 (fp32 operands) or
+ * SSD_MMA_BF16 (operands rounded to bf16 to nearest even, fp32 accumulation,
+ * several times faster and about 1e-2 relative accuracy); states, sums and
+ * outputs are fp32 in both.  workspace (device, 16-byte aligned) of at least
+ * ssd_backward_workspace_bytes(shape) bytes; the shape must also be supported
+ * by the chunk scan with P and N swapped.  Errors as for ssd_forward.
  */
 ssd_status ssd_backward(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* Bm,
                         const void* Cm, const float* D, ssd_dtype in, const float* initial_states, const void* dy,
                         ssd_dtype dy_dtype, const float* dfinal, float* dx, float* ddt, float* dA, float* dB,
                         float* dC, float* dD, float* dinitial, void* workspace, size_t workspace_bytes,
-                        void* stream);
+                        ssd_mma mma, void* stream);
 
 /* Workspace bytes ssd_backward needs (0 for an invalid or NULL shape). */
 size_t ssd_backward_workspace_bytes(const ssd_shape* shape);

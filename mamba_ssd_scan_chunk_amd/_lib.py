@@ -52,7 +52,7 @@ _SIGNATURES = {
                                           _P, ctypes.c_size_t, _E, _P]),
     "ssd_forward": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _E, _P, _P, _E, _P, _P, ctypes.c_size_t, _E, _P]),
     "ssd_backward": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _E, _P, _P, _E, _P, _P, _P, _P, _P, _P, _P, _P,
-                                    _P, ctypes.c_size_t, _P]),
+                                    _P, ctypes.c_size_t, _E, _P]),
     "ssd_backward_workspace_bytes": (ctypes.c_size_t, [_S]),
     "ssd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ssd_abi_version": (ctypes.c_int, []),

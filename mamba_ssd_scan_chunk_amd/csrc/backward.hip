@@ -18,6 +18,9 @@
 //   (3) forward transposed:           y3 = h_t dy_t (N-vector)  -> dC
 // The reversed passes run over nc*Q steps, the sequence padded at its far end
 // (zero inputs, no decay), so that their chunk edges fall on the forward's.
+// The transposed passes need no state computation of their own: their carried
+// states are the transposes of those of (0) and (1).  Operands are fp32, or
+// bf16 (rounded to nearest even) when the matrix cores take bf16.
 // The log-decay gradient needs q_t = <g_t, h_t>, since
 //   dL/d(dt_t A) = r_t <g_t, h_{t-1}> = q_t - dt_t beta_t,
 //   ddt_t = A dL/d(dt_t A) + beta_t,  dA = sum_t dt_t dL/d(dt_t A).
@@ -31,23 +34,44 @@
 
 namespace ssd {
 
-// out[b, s, k, e] = in[b, t(s), k / (KO / KI), e] in fp32 for s < Lout, with
-// t(s) = s, or Lout-1-s when reversing; rows with t >= Lin are zero.  KO/KI
-// maps output slots to input slots (heads -> groups when expanding B or C).
+// out[b, s, k, e] = in[b, t(s), k / (KO / KI), e] for s < Lout, with t(s) = s,
+// or Lout-1-s when reversing; rows with t >= Lin are zero.  KO/KI maps output
+// slots to input slots (heads -> groups when expanding B or C per head).  One
+// block per output row (b, s); 4-element groups (E is a multiple of 16).
+// Output fp32, or bf16 rounded to nearest even (exact for bf16 input).
+template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const void* __restrict__ in, int in_bf16,
-                                                          float* __restrict__ out, int Lin, int Lout, int KO, int KI,
-                                                          int E, int reverse, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int e = (int)(i % E);
-  int64_t r = i / E;
-  const int k = (int)(r % KO);
-  r /= KO;
-  const int s = (int)(r % Lout);
-  const int64_t b = r / Lout;
+                                                          void* __restrict__ out, int Lin, int Lout, int KO, int KI,
+                                                          int E, int reverse) {
+  const int64_t row = blockIdx.x;  // b * Lout + s
+  const int64_t b = row / Lout;
+  const int s = (int)(row - b * Lout);
   const int t = reverse ? Lout - 1 - s : s;
-  const int ki = k / (KO / KI);
-  out[i] = t < Lin ? load1_as_f32(in, ((b * Lin + t) * KI + ki) * E + e, in_bf16 != 0) : 0.f;
+  const int E4 = E / 4, W4 = KO * E4, per = KO / KI;
+  const int64_t src_row = (b * Lin + t) * KI;
+  for (int j = threadIdx.x; j < W4; j += 256) {
+    const int k = j / E4, e4 = j - k * E4;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < Lin) {
+      const int64_t src = (src_row + k / per) * E + 4 * e4;
+      if (in_bf16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(in) + src);
+        v[0] = bf16_bits_to_f32(u.x & 0xffffu);
+        v[1] = bf16_bits_to_f32(u.x >> 16);
+        v[2] = bf16_bits_to_f32(u.y & 0xffffu);
+        v[3] = bf16_bits_to_f32(u.y >> 16);
+      } else {
+        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(in) + src);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+      }
+    }
+    const int64_t dst = row * KO * E + 4 * (int64_t)j;
+    if constexpr (OUT_BF16)
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + dst) =
+          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    else
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + dst) = make_float4(v[0], v[1], v[2], v[3]);
+  }
 }
 
 // dt of the reversed adjoint over Lp steps: step s carries token t = Lp-1-s and
@@ -69,16 +93,20 @@ __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, float 
   if (i < n) p[i] = v;
 }
 
-// [B*H][R][C] -> [B*H][C][R]
-__global__ __launch_bounds__(256) void transpose_states_kernel(const float* __restrict__ in, float* __restrict__ out,
-                                                               int R, int C, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // output element
-  if (i >= n) return;
-  const int r = (int)(i % R);
-  const int64_t q = i / R;
-  const int c = (int)(q % C);
-  const int64_t m = q / C;
-  out[i] = in[(m * R + r) * C + c];
+// Per matrix m: out[m][c][r] = in[m][r][c] for R x C matrices (R, C multiples
+// of 16), through a 16 x 17 LDS tile; one 256-thread block per 16 x 16 tile.
+__global__ __launch_bounds__(256) void transpose_tiles_kernel(const float* __restrict__ in, float* __restrict__ out,
+                                                              int R, int C) {
+  __shared__ float tile[16][17];
+  const int tr = R / 16, tc = C / 16;
+  const int64_t m = blockIdx.x / (tr * tc);
+  const int rem = (int)(blockIdx.x - m * tr * tc);
+  const int r0 = 16 * (rem / tc), c0 = 16 * (rem % tc);
+  const int i = threadIdx.x >> 4, j = threadIdx.x & 15;
+  const int64_t base = m * R * C;
+  tile[i][j] = in[base + (int64_t)(r0 + i) * C + c0 + j];
+  __syncthreads();
+  out[base + (int64_t)(c0 + i) * R + r0 + j] = tile[j][i];
 }
 
 // anc[b, h, k] = <g_{kQ}, h_{kQ-1}>: for k >= 1 the adjoint's carried state
@@ -116,7 +144,7 @@ __global__ __launch_bounds__(256) void anchor_dot_kernel(const float* __restrict
 // Per (b, t, h): dx, beta_t = B_t . (g_t x_t), v_t = dy_t . y0_t, u_t = dy_t . x_t.
 // One wave per (b, t, h); y1 and y2 are in reversed time over Lp steps.
 __global__ __launch_bounds__(256) void combine_token_kernel(
-    const float* __restrict__ dy, const float* __restrict__ xf, const float* __restrict__ Bf,
+    const void* __restrict__ dy, int dy_bf16, const void* __restrict__ x, const void* __restrict__ Bm, int in_bf16,
     const float* __restrict__ dt, const float* __restrict__ D, const float* __restrict__ y0,
     const float* __restrict__ y1, const float* __restrict__ y2, float* __restrict__ dx, float* __restrict__ beta,
     float* __restrict__ v, float* __restrict__ u, int L, int Lp, int H, int P, int N, int G, int64_t nrows) {
@@ -132,12 +160,12 @@ __global__ __launch_bounds__(256) void combine_token_kernel(
   const float dtv = dt[row], dh = D[h];
   float sv = 0.f, su = 0.f, sb = 0.f;
   for (int p = lane; p < P; p += 64) {
-    const float dyv = dy[row * P + p], xv = xf[row * P + p];
+    const float dyv = load1_as_f32(dy, row * P + p, dy_bf16 != 0), xv = load1_as_f32(x, row * P + p, in_bf16 != 0);
     dx[row * P + p] = fmaf(dtv, y1[rrow * P + p], dh * dyv);
     sv = fmaf(dyv, y0[row * P + p], sv);
     su = fmaf(dyv, xv, su);
   }
-  for (int n = lane; n < N; n += 64) sb = fmaf(Bf[(bt * G + g) * N + n], y2[rrow * N + n], sb);
+  for (int n = lane; n < N; n += 64) sb = fmaf(load1_as_f32(Bm, (bt * G + g) * N + n, in_bf16 != 0), y2[rrow * N + n], sb);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     sv += __shfl_xor(sv, off, 64);
@@ -275,11 +303,12 @@ namespace {
 unsigned nblocks(int64_t n, int per = 256) { return (unsigned)((n + per - 1) / per); }
 size_t ru(size_t v) { return (v + 255) / 256 * 256; }
 
-// Workspace pieces, in order (all fp32).  Forward time: L tokens; reversed: Lp = nc*Q steps.
+// Workspace pieces, in order; operand copies are sized for fp32 (bf16 copies
+// use the first half).  Forward time: L tokens; reversed: Lp = nc*Q steps.
 enum BwdBuf {
-  kXf, kBf, kCf, kDyF, kBExp,                         // forward-time operands
+  kXo, kBo, kCo, kDyo, kBExp,                         // forward-time operands
   kDyRev, kXRev, kBRev, kCRev, kCExpRev, kDtRev,      // reversed operands
-  kOnes, kZeroD, kH0T, kDfT,
+  kOnes, kZeroD,
   kY0, kDA0, kDt0, kSt0,                              // (0)
   kDA1, kDt1, kSt1, kY1, kFin1,                       // (1)
   kSt2, kY2,                                          // (2)
@@ -296,8 +325,8 @@ BwdLayout bwd_layout(const Dims& d) {
   const size_t f = sizeof(float), B = d.B, L = d.L, Lp = d.nc * d.Q, H = d.H, P = d.P, N = d.N, G = d.G;
   const size_t chunk_q = f * B * H * d.nc * d.Q, states = f * B * d.nc * H * N * P, bhnp = f * B * H * N * P;
   size_t sz[kNumBwd] = {};
-  sz[kXf] = sz[kDyF] = f * B * L * H * P;
-  sz[kBf] = sz[kCf] = f * B * L * G * N;
+  sz[kXo] = sz[kDyo] = f * B * L * H * P;
+  sz[kBo] = sz[kCo] = f * B * L * G * N;
   sz[kBExp] = f * B * L * H * N;
   sz[kDyRev] = sz[kXRev] = f * B * Lp * H * P;
   sz[kBRev] = sz[kCRev] = f * B * Lp * G * N;
@@ -305,7 +334,7 @@ BwdLayout bwd_layout(const Dims& d) {
   sz[kDtRev] = f * B * Lp * H;
   sz[kOnes] = sz[kDA0] = sz[kDt0] = sz[kDA1] = sz[kDt1] = chunk_q;
   sz[kZeroD] = f * H;
-  sz[kH0T] = sz[kDfT] = sz[kFin1] = bhnp;
+  sz[kFin1] = bhnp;
   sz[kSt0] = sz[kSt1] = sz[kSt2] = sz[kSt3] = states;
   sz[kY0] = f * B * L * H * P;
   sz[kY1] = f * B * Lp * H * P;
@@ -334,15 +363,14 @@ size_t backward_workspace_bytes(const Dims& d) { return bwd_layout(d).total; }
 
 hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const float* A, const void* Bm,
                            const void* Cm, const float* D, bool in_bf16, const float* initial_states,
-                           const void* dy_in, bool dy_bf16, const float* dfinal, float* dx, float* ddt, float* dA,
-                           float* dB, float* dC, float* dD, float* dinit, void* workspace, hipStream_t s) {
+                           const void* dy, bool dy_bf16, const float* dfinal, float* dx, float* ddt, float* dA,
+                           float* dB, float* dC, float* dD, float* dinit, bool f32_mma, void* workspace,
+                           hipStream_t s) {
   const BwdLayout w = bwd_layout(d);
   char* base = static_cast<char*>(workspace);
   auto F = [&](int k) { return reinterpret_cast<float*>(base + w.off[k]); };
+  auto V = [&](int k) { return static_cast<void*>(base + w.off[k]); };
   const int L = (int)d.L, Lp = (int)(d.nc * d.Q), H = (int)d.H, P = (int)d.P, N = (int)d.N, G = (int)d.G;
-  const int bf = in_bf16 ? 1 : 0;
-  const int64_t nxhp = d.B * d.L * d.H * d.P, nbgn = d.B * d.L * d.G * d.N, nbhn = d.B * d.L * d.H * d.N;
-  const int64_t rxhp = d.B * Lp * d.H * d.P, rbgn = d.B * Lp * d.G * d.N, rbhn = d.B * Lp * d.H * d.N;
   // the reversed passes: Lp steps (whole chunks); the transposed ones: P and N
   // swapped, one group per head
   Dims dR = d;
@@ -354,77 +382,75 @@ hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const 
   Dims dRT = dT;
   dRT.L = Lp;
 
-  // ---- operands in fp32: forward order, reversed, and expanded per head
-  const float* dy = static_cast<const float*>(dy_in);
-  if (dy_bf16) {
-    hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(nxhp)), dim3(256), 0, s, dy_in, 1, F(kDyF), L, L, H, H, P,
-                       0, nxhp);
-    dy = F(kDyF);
-  }
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(nxhp)), dim3(256), 0, s, x, bf, F(kXf), L, L, H, H, P, 0, nxhp);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(nbgn)), dim3(256), 0, s, Bm, bf, F(kBf), L, L, G, G, N, 0, nbgn);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(nbgn)), dim3(256), 0, s, Cm, bf, F(kCf), L, L, G, G, N, 0, nbgn);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(nbhn)), dim3(256), 0, s, Bm, bf, F(kBExp), L, L, H, G, N, 0,
-                     nbhn);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(rxhp)), dim3(256), 0, s, dy, 0, F(kDyRev), L, Lp, H, H, P, 1,
-                     rxhp);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(rxhp)), dim3(256), 0, s, x, bf, F(kXRev), L, Lp, H, H, P, 1,
-                     rxhp);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(rbgn)), dim3(256), 0, s, Bm, bf, F(kBRev), L, Lp, G, G, N, 1,
-                     rbgn);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(rbgn)), dim3(256), 0, s, Cm, bf, F(kCRev), L, Lp, G, G, N, 1,
-                     rbgn);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(nblocks(rbhn)), dim3(256), 0, s, Cm, bf, F(kCExpRev), L, Lp, H, G, N,
-                     1, rbhn);
+  // ---- matrix operands in the operand type: the caller's arrays where they
+  // already have it, else converted; reversed and per-head copies always
+  const bool op_bf16 = !f32_mma;
+  auto gather = [&](const void* src, int src_bf16, int k, int Lout, int KO, int KI, int E, int reverse) {
+    if (op_bf16)
+      hipLaunchKernelGGL(gather_rows_kernel<true>, dim3((unsigned)(d.B * Lout)), dim3(256), 0, s, src, src_bf16, V(k),
+                         L, Lout, KO, KI, E, reverse);
+    else
+      hipLaunchKernelGGL(gather_rows_kernel<false>, dim3((unsigned)(d.B * Lout)), dim3(256), 0, s, src, src_bf16,
+                         V(k), L, Lout, KO, KI, E, reverse);
+    return static_cast<const void*>(V(k));
+  };
+  const int ib = in_bf16 ? 1 : 0, db = dy_bf16 ? 1 : 0;
+  const void* xo = in_bf16 == op_bf16 ? x : gather(x, ib, kXo, L, H, H, P, 0);
+  const void* Bo = in_bf16 == op_bf16 ? Bm : gather(Bm, ib, kBo, L, G, G, N, 0);
+  const void* Co = in_bf16 == op_bf16 ? Cm : gather(Cm, ib, kCo, L, G, G, N, 0);
+  const void* dyo = dy_bf16 == op_bf16 ? dy : gather(dy, db, kDyo, L, H, H, P, 0);
+  const void* BExp = gather(Bm, ib, kBExp, L, H, G, N, 0);
+  const void* DyRev = gather(dy, db, kDyRev, Lp, H, H, P, 1);
+  const void* XRev = gather(x, ib, kXRev, Lp, H, H, P, 1);
+  const void* BRev = gather(Bm, ib, kBRev, Lp, G, G, N, 1);
+  const void* CRev = gather(Cm, ib, kCRev, Lp, G, G, N, 1);
+  const void* CExpRev = gather(Cm, ib, kCExpRev, Lp, H, G, N, 1);
   const int64_t nblh = d.B * d.L * d.H, rblh = d.B * Lp * d.H;
   hipLaunchKernelGGL(shift_reverse_dt_kernel, dim3(nblocks(rblh)), dim3(256), 0, s, dt, F(kDtRev), L, Lp, H, rblh);
   const int64_t nq = d.B * d.H * d.nc * d.Q;
   hipLaunchKernelGGL(fill_kernel, dim3(nblocks(nq)), dim3(256), 0, s, F(kOnes), 1.f, nq);
   hipLaunchKernelGGL(fill_kernel, dim3(nblocks(d.H)), dim3(256), 0, s, F(kZeroD), 0.f, (int64_t)d.H);
-  const int64_t nnp = d.B * d.H * d.N * d.P;
-  if (initial_states)
-    hipLaunchKernelGGL(transpose_states_kernel, dim3(nblocks(nnp)), dim3(256), 0, s, initial_states, F(kH0T), N, P,
-                       nnp);
-  if (dfinal)
-    hipLaunchKernelGGL(transpose_states_kernel, dim3(nblocks(nnp)), dim3(256), 0, s, dfinal, F(kDfT), N, P, nnp);
   BWD_TRY(hipGetLastError());
 
-  // ---- (0) forward: y0 = C^T h (no skip term), carried states
+  // ---- (0) forward: y0 = C^T h (no skip term), fp32 carried states
   BWD_TRY(launch_chunk_cumsum(d, dt, A, F(kDA0), F(kDt0), s));
-  BWD_TRY(launch_chunk_state(d, F(kXf), F(kBf), false, F(kDt0), F(kDA0), F(kSt0), true, s));
+  BWD_TRY(launch_chunk_state(d, xo, Bo, op_bf16, F(kDt0), F(kDA0), F(kSt0), f32_mma, s));
   BWD_TRY(launch_state_passing(d, F(kSt0), F(kSt0), F(kDA0), initial_states, nullptr, s));
-  BWD_TRY(launch_chunk_scan(d, F(kXf), F(kBf), F(kCf), false, F(kDt0), F(kDA0), F(kSt0), false, F(kZeroD), F(kY0),
-                            false, true, s));
+  BWD_TRY(launch_chunk_scan(d, xo, Bo, Co, op_bf16, F(kDt0), F(kDA0), F(kSt0), false, F(kZeroD), F(kY0), false,
+                            f32_mma, s));
 
   // ---- (1) adjoint in reversed time: decay from the shifted dt, input scale 1
   BWD_TRY(launch_chunk_cumsum(dR, F(kDtRev), A, F(kDA1), F(kDt1), s));
-  BWD_TRY(launch_chunk_state(dR, F(kDyRev), F(kCRev), false, F(kOnes), F(kDA1), F(kSt1), true, s));
+  BWD_TRY(launch_chunk_state(dR, DyRev, CRev, op_bf16, F(kOnes), F(kDA1), F(kSt1), f32_mma, s));
   BWD_TRY(launch_state_passing(dR, F(kSt1), F(kSt1), F(kDA1), dfinal, F(kFin1), s));
-  BWD_TRY(launch_chunk_scan(dR, F(kDyRev), F(kCRev), F(kBRev), false, F(kOnes), F(kDA1), F(kSt1), false, F(kZeroD),
-                            F(kY1), false, true, s));
+  BWD_TRY(launch_chunk_scan(dR, DyRev, CRev, BRev, op_bf16, F(kOnes), F(kDA1), F(kSt1), false, F(kZeroD), F(kY1),
+                            false, f32_mma, s));
 
-  // ---- (2) adjoint transposed (state P x N per head: B-role dy, x-role C, C-role x)
-  BWD_TRY(launch_chunk_state(dRT, F(kCExpRev), F(kDyRev), false, F(kOnes), F(kDA1), F(kSt2), true, s));
-  BWD_TRY(launch_state_passing(dRT, F(kSt2), F(kSt2), F(kDA1), dfinal ? F(kDfT) : nullptr, nullptr, s));
-  BWD_TRY(launch_chunk_scan(dRT, F(kCExpRev), F(kDyRev), F(kXRev), false, F(kOnes), F(kDA1), F(kSt2), false,
-                            F(kZeroD), F(kY2), false, true, s));
+  // ---- (2) adjoint transposed (state P x N per head: x-role C, B-role dy, C-role x);
+  //      its carried states are those of (1), transposed
+  const int64_t nmat = d.B * d.nc * d.H, tiles = (d.N / 16) * (d.P / 16);
+  hipLaunchKernelGGL(transpose_tiles_kernel, dim3((unsigned)(nmat * tiles)), dim3(256), 0, s, F(kSt1), F(kSt2), N, P);
+  BWD_TRY(launch_chunk_scan(dRT, CExpRev, DyRev, XRev, op_bf16, F(kOnes), F(kDA1), F(kSt2), false, F(kZeroD),
+                            F(kY2), false, f32_mma, s));
 
-  // ---- (3) forward transposed (B-role x, x-role B, C-role dy): y3_t = h_t dy_t
-  BWD_TRY(launch_chunk_state(dT, F(kBExp), F(kXf), false, F(kDt0), F(kDA0), F(kSt3), true, s));
-  BWD_TRY(launch_state_passing(dT, F(kSt3), F(kSt3), F(kDA0), initial_states ? F(kH0T) : nullptr, nullptr, s));
-  BWD_TRY(launch_chunk_scan(dT, F(kBExp), F(kXf), dy, false, F(kDt0), F(kDA0), F(kSt3), false, F(kZeroD), F(kY3),
-                            false, true, s));
+  // ---- (3) forward transposed (x-role B, B-role x, C-role dy): y3_t = h_t dy_t;
+  //      its carried states are those of (0), transposed
+  hipLaunchKernelGGL(transpose_tiles_kernel, dim3((unsigned)(nmat * tiles)), dim3(256), 0, s, F(kSt0), F(kSt3), N, P);
+  BWD_TRY(launch_chunk_scan(dT, BExp, xo, dyo, op_bf16, F(kDt0), F(kDA0), F(kSt3), false, F(kZeroD), F(kY3), false,
+                            f32_mma, s));
 
   // ---- combine
   hipLaunchKernelGGL(anchor_dot_kernel, dim3((unsigned)(d.B * d.nc * d.H)), dim3(256), 0, s, F(kSt0), F(kSt1),
                      F(kFin1), initial_states, F(kAnc), H, (int)d.nc, d.N * d.P);
-  hipLaunchKernelGGL(combine_token_kernel, dim3(nblocks(nblh, 4)), dim3(256), 0, s, dy, F(kXf), F(kBf), dt, D,
+  hipLaunchKernelGGL(combine_token_kernel, dim3(nblocks(nblh, 4)), dim3(256), 0, s, dy, db, x, Bm, ib, dt, D,
                      F(kY0), F(kY1), F(kY2), dx, F(kBeta), F(kV), F(kU), L, Lp, H, P, N, G, nblh);
+  const int64_t nbgn = d.B * d.L * d.G * d.N;
   hipLaunchKernelGGL(combine_group_kernel, dim3(nblocks(nbgn)), dim3(256), 0, s, dt, F(kY2), F(kY3), dB, dC, L, Lp,
                      H, N, G, nbgn);
   const int64_t nw = d.B * d.H * d.nc;
   hipLaunchKernelGGL(chunk_grad_kernel, dim3(nblocks(nw, 4)), dim3(256), 0, s, dt, A, F(kBeta), F(kV), F(kU),
                      F(kAnc), ddt, F(kDAp), F(kDDp), L, H, (int)d.Q, (int)d.nc, nw);
+  const int64_t nnp = d.B * d.H * d.N * d.P;
   if (dinit)
     hipLaunchKernelGGL(dh0_kernel, dim3(nblocks(nnp)), dim3(256), 0, s, dt, A, F(kFin1), dinit, L, H, d.N * d.P,
                        nnp);

@@ -73,12 +73,12 @@ struct HgCfg {
   static constexpr size_t lds_a = lds_bs > lds_xh ? lds_bs : lds_xh;  // Bs, later Xn + Hn
   static constexpr size_t lds_c = (size_t)Q * NPI * 2;                // Cs
   static constexpr size_t lds_w = sizeof(float) * (size_t)(QT / 2) * Q;  // Ws
-  // DB (N = 128): the per-head tiles are double-buffered -- two buffers of
-  // Xn, Hn, Ws, Gs, dts, both aliasing the phase-0/1 Bs + Cs area, with the
-  // C fragments of C.H_in kept in registers -- so a head needs one barrier
-  // instead of two.  N = 256 keeps the single-buffer layout (its C fragments
-  // would not fit in registers).
-  static constexpr bool DB = NK == 4;
+  // DB (N = 64, 128): the per-head tiles are double-buffered -- two buffers
+  // of Xn, Hn, Ws, Gs, dts, both aliasing the phase-0/1 Bs + Cs area, with
+  // the C fragments of C.H_in kept in registers -- so a head needs one
+  // barrier instead of two.  N = 256 keeps the single-buffer layout (its C
+  // fragments would not fit in registers).
+  static constexpr bool DB = NK == 2 || NK == 4;
   static constexpr size_t lds_buf = lds_xh + lds_w + 2 * sizeof(float) * Q;  // one buffer
   static constexpr size_t lds_db = 2 * lds_bs > 2 * lds_buf ? 2 * lds_bs : 2 * lds_buf;
   static constexpr size_t lds_total = DB ? lds_db : lds_a + lds_c + lds_w + 2 * sizeof(float) * Q;
@@ -639,8 +639,10 @@ bool chunk_scan_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
   if (d.nc * d.B * d.G * (d.H / d.G) * (d.P / 64) > 0x7fffffff) return false;
   const int64_t key = d.Q * 1000 + d.N;
   switch (key) {
+    case 128 * 1000 + 64: return hg_fits<128, 2>();
     case 128 * 1000 + 128: return hg_fits<128, 4>();
     case 128 * 1000 + 256: return hg_fits<128, 8>();
+    case 256 * 1000 + 64: return hg_fits<256, 2>();
     case 256 * 1000 + 128: return hg_fits<256, 4>();
     default: return false;
   }
@@ -655,8 +657,10 @@ static hipError_t launch_hg_dtype(const Dims& d, const void* x, const void* Bm, 
   case QQ * 1000 + NN:      \
     return launch_hg_inst<QQ, KK, H_BF16>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
   switch (key) {
+    HG_CASE(128, 64, 2)
     HG_CASE(128, 128, 4)
     HG_CASE(128, 256, 8)
+    HG_CASE(256, 64, 2)
     HG_CASE(256, 128, 4)
     default: return hipErrorInvalidValue;
   }

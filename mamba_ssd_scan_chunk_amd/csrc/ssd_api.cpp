@@ -348,11 +348,12 @@ ssd_status ssd_backward(const ssd_shape* shape, const void* x, const float* dt, 
                         const void* Cm, const float* D, ssd_dtype in, const float* initial_states, const void* dy,
                         ssd_dtype dy_dtype, const float* dfinal, float* dx, float* ddt, float* dA, float* dB,
                         float* dC, float* dD, float* dinitial, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        ssd_mma mma, void* stream) {
   Dims d;
   SSD_TRY(check_shape(shape, &d));
   SSD_TRY(check_dtype(in));
   SSD_TRY(check_dtype(dy_dtype));
+  SSD_TRY(check_mma(mma));
   if (!x || !dt || !A || !Bm || !Cm || !D || !dy || !dx || !ddt || !dA || !dB || !dC || !dD) return SSD_ERR_NULL;
   if (!workspace) return SSD_ERR_WORKSPACE;
   if (workspace_bytes < ssd::backward_workspace_bytes(d)) return SSD_ERR_WORKSPACE;
@@ -367,15 +368,16 @@ ssd_status ssd_backward(const ssd_shape* shape, const void* x, const float* dt, 
   dT.P = d.N;
   dT.N = d.P;
   dT.G = d.H;
-  if (ssd::chunk_state_lds_bytes(d, true) > kLdsLimit || ssd::chunk_scan_lds_bytes(d, true) > kLdsLimit ||
-      ssd::chunk_state_lds_bytes(dT, true) > kLdsLimit || ssd::chunk_scan_lds_bytes(dT, true) > kLdsLimit)
+  const bool f32m = mma == SSD_MMA_F32;
+  if (ssd::chunk_state_lds_bytes(d, f32m) > kLdsLimit || ssd::chunk_scan_lds_bytes(d, f32m) > kLdsLimit ||
+      ssd::chunk_scan_lds_bytes(dT, f32m) > kLdsLimit)
     return SSD_ERR_UNSUPPORTED;
   // elementwise launches of 256 threads per block over B*L*H*max(P,N) elements
   const int64_t wide = d.P > d.N ? d.P : d.N;
   if (d.B * d.L * d.H > (int64_t(1) << 39) / wide) return SSD_ERR_UNSUPPORTED;
   return from_hip(ssd::launch_backward(d, x, dt, A, Bm, Cm, D, in == SSD_BF16, initial_states, dy,
-                                       dy_dtype == SSD_BF16, dfinal, dx, ddt, dA, dB, dC, dD, dinitial, workspace,
-                                       (hipStream_t)stream));
+                                       dy_dtype == SSD_BF16, dfinal, dx, ddt, dA, dB, dC, dD, dinitial, f32m,
+                                       workspace, (hipStream_t)stream));
 }
 
 const char* ssd_status_string(ssd_status status) {

@@ -66,7 +66,7 @@ hipError_t launch_state_fused(const Dims& d, const void* x, const void* Bm, cons
                               float* final_states, hipStream_t stream);
 
 // Head-group variant of the fused chunk output (bf16 inputs and operands,
-// (chunk, N) in {(128,128), (128,256), (256,128)}, P a multiple of 64);
+// (chunk, N) in {(128,64), (128,128), (128,256), (256,64), (256,128)}, P a multiple of 64);
 // launch_chunk_scan picks it when supported.  `carried` holds fp32 values, or
 // bf16 bits (already rounded to nearest even) when carried_bf16 is set.
 bool chunk_scan_hg_supported(const Dims& d, bool in_bf16, bool f32_mma);
@@ -97,11 +97,12 @@ hipError_t launch_decode_step(int64_t Bn, int64_t H, int64_t P, int64_t N, int64
                               const float* dt, const float* A, const void* Bm, const void* Cm, const float* D,
                               bool in_bf16, float* state, void* y, bool y_bf16, hipStream_t stream);
 
-// Gradients of the forward (see backward.hip); fp32 outputs, fp32 arithmetic.
+// Gradients of the forward (see backward.hip); fp32 outputs and accumulation.
 size_t backward_workspace_bytes(const Dims& d);
 hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const float* A, const void* Bm,
                            const void* Cm, const float* D, bool in_bf16, const float* initial_states,
                            const void* dy, bool dy_bf16, const float* dfinal, float* dx, float* ddt, float* dA,
-                           float* dB, float* dC, float* dD, float* dinit, void* workspace, hipStream_t stream);
+                           float* dB, float* dC, float* dD, float* dinit, bool f32_mma, void* workspace,
+                           hipStream_t stream);
 
 }  // namespace ssd

@@ -299,10 +299,11 @@ def ssd_forward_varlen(shape, x, dt, A, Bm, Cm, D, seq_idx, initial_states=None,
 
 
 def ssd_backward(shape, x, dt, A, Bm, Cm, D, dy, initial_states=None, dfinal=None, want_dinitial=True,
-                 workspace=None, stream=None) -> Dict[str, Optional[torch.Tensor]]:
+                 workspace=None, mma="f32", stream=None) -> Dict[str, Optional[torch.Tensor]]:
     """Gradients of ``ssd_forward`` for dL/dy = dy and dL/dfinal = dfinal
     (None: zero).  Returns fp32 tensors dx, ddt, dA, dB, dC, dD and dinitial
-    (None unless ``want_dinitial``)."""
+    (None unless ``want_dinitial``).  ``mma``: "f32" (fp32 matrix operands) or
+    "bf16" (bf16 operands, fp32 accumulation; faster, ~1e-2 relative)."""
     sh = _shape(shape)
     B, L, H, P, N, G, Q, nc = _dims(sh)
     io = (torch.float32, torch.bfloat16)
@@ -333,7 +334,7 @@ def ssd_backward(shape, x, dt, A, Bm, Cm, D, dy, initial_states=None, dfinal=Non
                            _ptr(initial_states), _ptr(dy), _DT[dy.dtype], _ptr(dfinal), _ptr(out["dx"]),
                            _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
                            _ptr(out["dinitial"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                           _stream(stream)))
+                           _mma(mma), _stream(stream)))
     return out
 
 

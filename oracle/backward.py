@@ -36,18 +36,22 @@ from __future__ import annotations
 import numpy as np
 
 
-def backward(x, dt, A, Bm, Cm, D, dy, h0=None, dfinal=None):
+def backward(x, dt, A, Bm, Cm, D, dy, h0=None, dfinal=None, terms=False):
     """Gradients of L = sum(dy * y) + sum(dfinal * final) w.r.t. every input.
 
     Shapes: x [B,L,H,P], dt [B,L,H], A [H], Bm/Cm [B,L,G,N], D [H], dy like x,
     h0 and dfinal [B,H,N,P] or None.  Returns a dict of fp64 arrays dx, ddt,
-    dA, dB, dC, dD, dh0 with the inputs' shapes."""
+    dA, dB, dC, dD, dh0 with the inputs' shapes.  With ``terms``, also the
+    per-token pieces of ddt and dA, both [B,L,H]: "dlogr" = dL/d(dt_t A) =
+    r_t <g_t, h_{t-1}> and "beta" = B_t^T g_t x_t (ddt = A dlogr + beta,
+    dA = sum dt dlogr); tests use their magnitudes to scale error bars."""
     x, dt, A, Bm, Cm, D, dy = (np.asarray(a, dtype=np.float64) for a in (x, dt, A, Bm, Cm, D, dy))
     Bsz, L, H, P = x.shape
     G, N = Bm.shape[2], Bm.shape[3]
     hpg = H // G
     out = {"dx": np.zeros_like(x), "ddt": np.zeros_like(dt), "dA": np.zeros(H), "dB": np.zeros_like(Bm),
            "dC": np.zeros_like(Cm), "dD": np.zeros(H), "dh0": np.zeros((Bsz, H, N, P))}
+    dlogr, beta = np.zeros_like(dt), np.zeros_like(dt)
     for b in range(Bsz):
         for h in range(H):
             g = h // hpg
@@ -67,9 +71,12 @@ def backward(x, dt, A, Bm, Cm, D, dy, h0=None, dfinal=None):
                 gx = gst @ x[b, t, h]
                 out["dB"][b, t, g] += dt[b, t, h] * gx
                 gh = float(np.sum(gst * hprev))
+                dlogr[b, t, h], beta[b, t, h] = r[t] * gh, float(Bm[b, t, g] @ gx)
                 out["ddt"][b, t, h] = A[h] * r[t] * gh + float(Bm[b, t, g] @ gx)
                 out["dA"][h] += dt[b, t, h] * r[t] * gh
                 out["dD"][h] += float(dy[b, t, h] @ x[b, t, h])
                 gst = r[t] * gst
             out["dh0"][b, h] = gst
+    if terms:
+        out["dlogr"], out["beta"] = dlogr, beta
     return out

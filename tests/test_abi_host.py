@@ -217,15 +217,15 @@ def test_backward_checks(lib):
     s = shape()
     B, L, H, P, N, Q = 2, 512, 4, 64, 128, 256
     need = lib.ssd_backward_workspace_bytes(s)
-    # at least: the recomputed forward's and the adjoint's chunk states, fp32
-    assert need >= 2 * 4 * B * (L // Q) * H * N * P
+    # at least: the chunk states of the four passes, fp32
+    assert need >= 4 * 4 * B * (L // Q) * H * N * P
     assert lib.ssd_backward_workspace_bytes(None) == 0
     assert lib.ssd_backward_workspace_bytes(shape(batch=0)) == 0
     a = [FAKE] * 6  # x, dt, A, Bm, Cm, D
 
-    def call(sh, in_=1, dy=FAKE, dy_t=1, outs=None, ws=FAKE, wsb=need, h0=None, dfin=None, dinit=None):
+    def call(sh, in_=1, dy=FAKE, dy_t=1, outs=None, ws=FAKE, wsb=need, h0=None, dfin=None, dinit=None, mma=0):
         o = [FAKE] * 6 if outs is None else outs  # dx, ddt, dA, dB, dC, dD
-        return lib.ssd_backward(sh, *a, in_, h0, dy, dy_t, dfin, *o, dinit, ws, wsb, None)
+        return lib.ssd_backward(sh, *a, in_, h0, dy, dy_t, dfin, *o, dinit, ws, wsb, mma, None)
 
     assert call(s, dy=None) == NULL
     for k in range(6):
@@ -236,6 +236,7 @@ def test_backward_checks(lib):
     assert call(s, wsb=need - 1) == WS
     assert call(s, in_=7) == DTYPE
     assert call(s, dy_t=7) == DTYPE
+    assert call(s, mma=5) == DTYPE
     assert call(s, dy=FAKE + 4) == ALIGN
     assert call(s, dinit=FAKE + 8) == ALIGN
     assert call(s, dfin=FAKE + 2) == ALIGN

@@ -69,6 +69,21 @@ def test_backward_without_h0_or_dfinal():
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_backward_terms_compose_ddt_and_dA():
+    """The per-token pieces returned with terms=True recompose the pinned ddt
+    and dA (ddt = A dlogr + beta, dA = sum over tokens of dt dlogr), and
+    asking for them changes no gradient."""
+    v, dy, dfin = _problem(7)
+    g = bwd_mod.backward(v["x"], v["dt"], v["A"], v["Bm"], v["Cm"], v["D"], dy, h0=v["h0"], dfinal=dfin, terms=True)
+    g0 = bwd_mod.backward(v["x"], v["dt"], v["A"], v["Bm"], v["Cm"], v["D"], dy, h0=v["h0"], dfinal=dfin)
+    for k in g0:
+        assert np.array_equal(g[k], g0[k]), k
+    ddt = v["A"][None, None, :] * g["dlogr"] + g["beta"]
+    assert np.allclose(ddt, g["ddt"], rtol=1e-12, atol=1e-12 * np.abs(g["ddt"]).max())
+    dA = (v["dt"] * g["dlogr"]).sum(axis=(0, 1))
+    assert np.allclose(dA, g["dA"], rtol=1e-12, atol=1e-12 * np.abs(g["dA"]).max())
+
+
 # (text in backward.py, replacement, what the mistake is)
 MUTATIONS = [
     ("gst += np.outer(Cm[b, t, g], dy[b, t, h])", "gst += np.outer(Bm[b, t, g], dy[b, t, h])", "C replaced by B in the adjoint"),

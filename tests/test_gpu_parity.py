@@ -34,6 +34,7 @@ SHAPES = [
     ("ragged_q256", 2, 300, 4, 64, 128, 1, 256),
     ("ragged_q128_n256", 1, 130, 4, 64, 256, 2, 128),
     ("ragged_q64", 1, 200, 3, 48, 48, 3, 64),
+    ("ragged_q256_n64", 2, 600, 4, 64, 64, 2, 256),
 ]
 MODES = [("f32", "f32"), ("bf16", "f32"), ("f32", "bf16"), ("bf16", "bf16")]  # (input dtype, mma)
 
@@ -305,6 +306,8 @@ HG_SHAPES = [
     ("q256_n128", 2, 768, 6, 64, 128, 2, 256),
     ("q128_n256", 1, 512, 4, 128, 256, 2, 128),
     ("q128_n128", 2, 384, 3, 64, 128, 1, 128),
+    ("q256_n64", 2, 512, 4, 64, 64, 1, 256),
+    ("ragged_q128_n64", 1, 300, 4, 128, 64, 2, 128),
     ("generic_q64", 1, 256, 6, 32, 64, 2, 64),  # the generic chunk-scan kernel
 ]
 
