@@ -94,19 +94,24 @@ __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, float 
 }
 
 // Per matrix m: out[m][c][r] = in[m][r][c] for R x C matrices (R, C multiples
-// of 16), through a 16 x 17 LDS tile; one 256-thread block per 16 x 16 tile.
+// of TS), through a TS x (TS+1) LDS tile; one 256-thread block per tile, rows
+// read and written as whole TS-element segments.
+template <int TS>
 __global__ __launch_bounds__(256) void transpose_tiles_kernel(const float* __restrict__ in, float* __restrict__ out,
                                                               int R, int C) {
-  __shared__ float tile[16][17];
-  const int tr = R / 16, tc = C / 16;
+  __shared__ float tile[TS][TS + 1];
+  constexpr int RPP = 256 / TS;  // rows per pass
+  const int tr = R / TS, tc = C / TS;
   const int64_t m = blockIdx.x / (tr * tc);
   const int rem = (int)(blockIdx.x - m * tr * tc);
-  const int r0 = 16 * (rem / tc), c0 = 16 * (rem % tc);
-  const int i = threadIdx.x >> 4, j = threadIdx.x & 15;
+  const int r0 = TS * (rem / tc), c0 = TS * (rem % tc);
+  const int i = threadIdx.x / TS, j = threadIdx.x % TS;
   const int64_t base = m * R * C;
-  tile[i][j] = in[base + (int64_t)(r0 + i) * C + c0 + j];
+#pragma unroll
+  for (int k = 0; k < TS; k += RPP) tile[i + k][j] = in[base + (int64_t)(r0 + i + k) * C + c0 + j];
   __syncthreads();
-  out[base + (int64_t)(c0 + i) * R + r0 + j] = tile[j][i];
+#pragma unroll
+  for (int k = 0; k < TS; k += RPP) out[base + (int64_t)(c0 + i + k) * R + r0 + j] = tile[j][i + k];
 }
 
 // anc[b, h, k] = <g_{kQ}, h_{kQ-1}>: for k >= 1 the adjoint's carried state
@@ -141,16 +146,27 @@ __global__ __launch_bounds__(256) void anchor_dot_kernel(const float* __restrict
   if (tid == 0) anc[(b * H + h) * nc + k] = red[0];
 }
 
+// 4 consecutive elements (16-byte aligned group) as fp32
+__device__ __forceinline__ float4 load4_f32(const void* base, int64_t elem, bool bf16) {
+  if (bf16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + elem);
+    return make_float4(bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16), bf16_bits_to_f32(u.y & 0xffffu),
+                       bf16_bits_to_f32(u.y >> 16));
+  }
+  return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+}
+
 // Per (b, t, h): dx, beta_t = B_t . (g_t x_t), v_t = dy_t . y0_t, u_t = dy_t . x_t.
-// One wave per (b, t, h); y1 and y2 are in reversed time over Lp steps.
+// 16 lanes per (b, t, h) row, 4-element groups (P, N multiples of 16), four
+// rows per wave; y1 and y2 are in reversed time over Lp steps.
 __global__ __launch_bounds__(256) void combine_token_kernel(
     const void* __restrict__ dy, int dy_bf16, const void* __restrict__ x, const void* __restrict__ Bm, int in_bf16,
     const float* __restrict__ dt, const float* __restrict__ D, const float* __restrict__ y0,
     const float* __restrict__ y1, const float* __restrict__ y2, float* __restrict__ dx, float* __restrict__ beta,
     float* __restrict__ v, float* __restrict__ u, int L, int Lp, int H, int P, int N, int G, int64_t nrows) {
-  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);  // (b * L + t) * H + h
-  const int lane = threadIdx.x & 63;
-  if (row >= nrows) return;
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 16) + (threadIdx.x >> 4);  // (b * L + t) * H + h
+  const int l16 = threadIdx.x & 15;
+  if (row >= nrows) return;  // whole 16-lane groups leave together
   const int h = (int)(row % H);
   const int64_t bt = row / H;
   const int t = (int)(bt % L);
@@ -159,20 +175,28 @@ __global__ __launch_bounds__(256) void combine_token_kernel(
   const int64_t rrow = (b * Lp + (Lp - 1 - t)) * H + h;  // the same token in reversed time
   const float dtv = dt[row], dh = D[h];
   float sv = 0.f, su = 0.f, sb = 0.f;
-  for (int p = lane; p < P; p += 64) {
-    const float dyv = load1_as_f32(dy, row * P + p, dy_bf16 != 0), xv = load1_as_f32(x, row * P + p, in_bf16 != 0);
-    dx[row * P + p] = fmaf(dtv, y1[rrow * P + p], dh * dyv);
-    sv = fmaf(dyv, y0[row * P + p], sv);
-    su = fmaf(dyv, xv, su);
+  for (int p = 4 * l16; p < P; p += 64) {
+    const float4 dyv = load4_f32(dy, row * P + p, dy_bf16 != 0), xv = load4_f32(x, row * P + p, in_bf16 != 0);
+    const float4 a1 = *reinterpret_cast<const float4*>(y1 + rrow * P + p);
+    const float4 a0 = *reinterpret_cast<const float4*>(y0 + row * P + p);
+    *reinterpret_cast<float4*>(dx + row * P + p) =
+        make_float4(fmaf(dtv, a1.x, dh * dyv.x), fmaf(dtv, a1.y, dh * dyv.y), fmaf(dtv, a1.z, dh * dyv.z),
+                    fmaf(dtv, a1.w, dh * dyv.w));
+    sv = fmaf(dyv.x, a0.x, fmaf(dyv.y, a0.y, fmaf(dyv.z, a0.z, fmaf(dyv.w, a0.w, sv))));
+    su = fmaf(dyv.x, xv.x, fmaf(dyv.y, xv.y, fmaf(dyv.z, xv.z, fmaf(dyv.w, xv.w, su))));
   }
-  for (int n = lane; n < N; n += 64) sb = fmaf(load1_as_f32(Bm, (bt * G + g) * N + n, in_bf16 != 0), y2[rrow * N + n], sb);
+  for (int n = 4 * l16; n < N; n += 64) {
+    const float4 bv = load4_f32(Bm, (bt * G + g) * N + n, in_bf16 != 0);
+    const float4 a2 = *reinterpret_cast<const float4*>(y2 + rrow * N + n);
+    sb = fmaf(bv.x, a2.x, fmaf(bv.y, a2.y, fmaf(bv.z, a2.z, fmaf(bv.w, a2.w, sb))));
+  }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    sv += __shfl_xor(sv, off, 64);
-    su += __shfl_xor(su, off, 64);
-    sb += __shfl_xor(sb, off, 64);
+  for (int off = 8; off > 0; off >>= 1) {
+    sv += __shfl_xor(sv, off, 16);
+    su += __shfl_xor(su, off, 16);
+    sb += __shfl_xor(sb, off, 16);
   }
-  if (lane == 0) {
+  if (l16 == 0) {
     v[row] = sv;
     u[row] = su;
     beta[row] = sb;
@@ -428,21 +452,29 @@ hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const 
 
   // ---- (2) adjoint transposed (state P x N per head: x-role C, B-role dy, C-role x);
   //      its carried states are those of (1), transposed
-  const int64_t nmat = d.B * d.nc * d.H, tiles = (d.N / 16) * (d.P / 16);
-  hipLaunchKernelGGL(transpose_tiles_kernel, dim3((unsigned)(nmat * tiles)), dim3(256), 0, s, F(kSt1), F(kSt2), N, P);
+  const int64_t nmat = d.B * d.nc * d.H;
+  auto transpose = [&](const float* src, float* dst) {
+    if (d.N % 32 == 0 && d.P % 32 == 0)
+      hipLaunchKernelGGL(transpose_tiles_kernel<32>, dim3((unsigned)(nmat * (d.N / 32) * (d.P / 32))), dim3(256), 0,
+                         s, src, dst, N, P);
+    else
+      hipLaunchKernelGGL(transpose_tiles_kernel<16>, dim3((unsigned)(nmat * (d.N / 16) * (d.P / 16))), dim3(256), 0,
+                         s, src, dst, N, P);
+  };
+  transpose(F(kSt1), F(kSt2));
   BWD_TRY(launch_chunk_scan(dRT, CExpRev, DyRev, XRev, op_bf16, F(kOnes), F(kDA1), F(kSt2), false, F(kZeroD),
                             F(kY2), false, f32_mma, s));
 
   // ---- (3) forward transposed (x-role B, B-role x, C-role dy): y3_t = h_t dy_t;
   //      its carried states are those of (0), transposed
-  hipLaunchKernelGGL(transpose_tiles_kernel, dim3((unsigned)(nmat * tiles)), dim3(256), 0, s, F(kSt0), F(kSt3), N, P);
+  transpose(F(kSt0), F(kSt3));
   BWD_TRY(launch_chunk_scan(dT, BExp, xo, dyo, op_bf16, F(kDt0), F(kDA0), F(kSt3), false, F(kZeroD), F(kY3), false,
                             f32_mma, s));
 
   // ---- combine
   hipLaunchKernelGGL(anchor_dot_kernel, dim3((unsigned)(d.B * d.nc * d.H)), dim3(256), 0, s, F(kSt0), F(kSt1),
                      F(kFin1), initial_states, F(kAnc), H, (int)d.nc, d.N * d.P);
-  hipLaunchKernelGGL(combine_token_kernel, dim3(nblocks(nblh, 4)), dim3(256), 0, s, dy, db, x, Bm, ib, dt, D,
+  hipLaunchKernelGGL(combine_token_kernel, dim3(nblocks(nblh, 16)), dim3(256), 0, s, dy, db, x, Bm, ib, dt, D,
                      F(kY0), F(kY1), F(kY2), dx, F(kBeta), F(kV), F(kU), L, Lp, H, P, N, G, nblh);
   const int64_t nbgn = d.B * d.L * d.G * d.N;
   hipLaunchKernelGGL(combine_group_kernel, dim3(nblocks(nbgn)), dim3(256), 0, s, dt, F(kY2), F(kY3), dB, dC, L, Lp,
