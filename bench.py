@@ -108,6 +108,18 @@ def cpu_baseline(inp, w, target_s=10.0):
                       f"workload in {t:.2f} s; tokens/s scaled by the sampled fraction"}
 
 
+def spin_cycles(torch, stream, us):
+    """Argument of torch.cuda._sleep (a bounded GPU spin) lasting about `us`
+    microseconds on this GPU, measured once."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    torch.cuda._sleep(1_000_000)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return int(1_000_000 * us / max(a.elapsed_time(b) * 1e3, 1.0))
+
+
 def time_backward(ops, torch, t, sh, steps, fwd_ms=None, modes=("bf16", "f32")):
     """ssd_backward at the workload (dy in the input dtype, dL/dfinal given),
     `steps` calls per matrix-operand mode after two untimed ones."""
@@ -279,8 +291,14 @@ def main():
         for k in calls:
             calls[k]()
     torch.cuda.synchronize()
+    # Each timed step starts with a bounded GPU spin (~300 us) that keeps the
+    # GPU busy while the host queues the step's calls and events, so every
+    # event pair brackets GPU time only: no host submission gap inflates the
+    # small kernels.
+    spin = spin_cycles(torch, stream, 300)
     evs = {k: [] for k in order}
     for _ in range(args.steps):
+        torch.cuda._sleep(spin)
         for k in calls:
             if k in evs:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -361,6 +379,7 @@ def main():
             torch.cuda.synchronize()
             s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = 50
+            torch.cuda._sleep(spin_cycles(torch, stream, 2000))  # the host queues all reps meanwhile
             s0.record(stream)
             for _ in range(reps):
                 call()
