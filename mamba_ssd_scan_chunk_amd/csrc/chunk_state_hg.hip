@@ -274,9 +274,16 @@ static int shg_cu_count() {
   return n;
 }
 
+// (chunk, N) pairs with an instance: N >= 128 (a 16-row state tile per wave
+// and per 128 rows of N) and the B and x tiles within the LDS
+#define SHG_SHAPES(X) X(64, 128) X(128, 128) X(256, 128) X(64, 256) X(128, 256)
+
 bool chunk_state_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
   if (f32_mma || !in_bf16 || d.P % 64 != 0) return false;
-  return (d.Q == 256 && d.N == 128) || (d.Q == 128 && d.N == 256);
+#define SHG_MATCH(QQ, NN) if (d.Q == QQ && d.N == NN) return ShgCfg<QQ, NN>::lds_total + 8 * QQ <= 160 * 1024;
+  SHG_SHAPES(SHG_MATCH)
+#undef SHG_MATCH
+  return false;
 }
 
 template <int Q, int N, bool FUSE>
@@ -312,22 +319,23 @@ static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, 
 
 hipError_t launch_chunk_state_hg(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
                                  const float* dA_cumsum, float* states, hipStream_t stream) {
-  if (d.Q == 256 && d.N == 128)
-    return launch_shg_inst<256, 128, false>(d, x, Bm, dt_bhl, dA_cumsum, nullptr, nullptr, nullptr, nullptr,
-                                            states, stream);
-  if (d.Q == 128 && d.N == 256)
-    return launch_shg_inst<128, 256, false>(d, x, Bm, dt_bhl, dA_cumsum, nullptr, nullptr, nullptr, nullptr,
-                                            states, stream);
+#define SHG_LAUNCH(QQ, NN)                                                                                  \
+  if (d.Q == QQ && d.N == NN)                                                                               \
+    return launch_shg_inst<QQ, NN, false>(d, x, Bm, dt_bhl, dA_cumsum, nullptr, nullptr, nullptr, nullptr, \
+                                          states, stream);
+  SHG_SHAPES(SHG_LAUNCH)
+#undef SHG_LAUNCH
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_state_cumsum_hg(const Dims& d, const void* x, const void* Bm, const float* dt,
                                         const float* A, float* dA_cumsum, float* dt_bhl, float* states,
                                         hipStream_t stream) {
-  if (d.Q == 256 && d.N == 128)
-    return launch_shg_inst<256, 128, true>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl, states, stream);
-  if (d.Q == 128 && d.N == 256)
-    return launch_shg_inst<128, 256, true>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl, states, stream);
+#define SHG_LAUNCH(QQ, NN) \
+  if (d.Q == QQ && d.N == NN) \
+    return launch_shg_inst<QQ, NN, true>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl, states, stream);
+  SHG_SHAPES(SHG_LAUNCH)
+#undef SHG_LAUNCH
   return hipErrorInvalidValue;
 }
 

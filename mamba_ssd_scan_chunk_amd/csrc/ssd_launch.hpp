@@ -33,7 +33,7 @@ hipError_t launch_chunk_state(const Dims& d, const void* x, const void* Bm, bool
                               bool f32_mma, hipStream_t stream);
 
 // Head-group variant of the chunk states (bf16 inputs and operands,
-// (chunk, N) in {(256,128), (128,256)}, P a multiple of 64); launch_chunk_state
+// (chunk, N) in {(64,128), (128,128), (256,128), (64,256), (128,256)}, P a multiple of 64); launch_chunk_state
 // picks it when supported.
 bool chunk_state_hg_supported(const Dims& d, bool in_bf16, bool f32_mma);
 hipError_t launch_chunk_state_hg(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,

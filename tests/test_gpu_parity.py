@@ -35,6 +35,8 @@ SHAPES = [
     ("ragged_q128_n256", 1, 130, 4, 64, 256, 2, 128),
     ("ragged_q64", 1, 200, 3, 48, 48, 3, 64),
     ("ragged_q256_n64", 2, 600, 4, 64, 64, 2, 256),
+    ("ragged_q64_n128", 2, 300, 4, 64, 128, 2, 64),
+    ("q64_n256", 1, 192, 2, 64, 256, 1, 64),
 ]
 MODES = [("f32", "f32"), ("bf16", "f32"), ("f32", "bf16"), ("bf16", "bf16")]  # (input dtype, mma)
 
@@ -355,6 +357,7 @@ FUSED_SHAPES = [
     ("q128_n128", 2, 384, 3, 64, 128, 1, 128),
     ("q64_n64", 1, 320, 5, 64, 64, 5, 64),
     ("q32_p128", 1, 96, 2, 128, 64, 1, 32),
+    ("q64_n128", 1, 256, 4, 64, 128, 2, 64),
 ]
 
 
