@@ -12,8 +12,9 @@ taken from the oracle's per-token pieces: ddt against max_t of
 |A| (|dlogr_t| + 2 dt_t |beta_t|) + |beta_t|, and dA_h against
 sum_{b,t} dt (|dlogr| + 2 dt |beta|) of its head.
 
-At the 2.7B-layer shape the oracle runs on sampled (batch, head) slices (dx,
-ddt, dinitial of those slices, and dA of the sampled heads over both rows),
+At full size (the 2.7B-layer and grouped workloads) the oracle runs on sampled
+(batch, head) slices (dx, ddt, dinitial of those slices; dA of a sampled head
+over every row),
 and the rest is checked by identities that hold at any size:
   * per token, C_t . dC_t = sum_h dy_t . (y_t - D_h x_t)     (dC_t = sum_h h_t dy_t)
   * per token, B_t . dB_t = sum_h x_t . (dx_t - D_h dy_t)    (both equal sum_h dt_t B_t^T g_t x_t)
@@ -151,12 +152,15 @@ def _close(lhs, rhs, scale, tol):
 
 
 @pytest.mark.parametrize("mma", ["f32", "bf16"])
-def test_backward_headline_shape_sampled_and_identities(mma):
-    """The 2.7B-layer shape (B=2, L=8192, H=80, P=64, N=128, Q=256, bf16 inputs)."""
-    inp = workload_inputs("mamba2_2p7b_layer")
+@pytest.mark.parametrize("workload", ["mamba2_2p7b_layer", "grouped_n256"])
+def test_backward_full_size_sampled_and_identities(workload, mma):
+    """Full-size workloads: the 2.7B-layer shape (B=2, L=8192, H=80, P=64,
+    N=128, G=1, Q=256) and the grouped one (B=8, L=4096, H=64, P=64, N=256,
+    G=8, Q=128), bf16 inputs."""
+    inp = workload_inputs(workload)
     B, L, H, P = inp.x.shape
     N, G = inp.Bm.shape[3], inp.Bm.shape[2]
-    say(f"backward at the 2.7B-layer shape B={B} L={L} H={H} P={P} N={N} mma={mma}")
+    say(f"backward at {workload} B={B} L={L} H={H} P={P} N={N} G={G} mma={mma}")
     rng = np.random.default_rng(67)
     dy = rng.standard_normal(inp.x.shape).astype(np.float32)
     h0 = rng.standard_normal((B, H, N, P)).astype(np.float32)
