@@ -99,13 +99,19 @@ def cpu_baseline(inp, w, target_s=10.0):
     k = int(min(total_pairs, threads * per_thread))
     pairs = np.linspace(0, total_pairs - 1, k).round().astype(np.int64)
     used = min(threads, k)
+    # when every pair fits in the time target, whole passes repeat until it is reached
+    passes = 0
     t0 = time.perf_counter()
-    o.recurrence(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D, pairs=pairs, nthreads=used)
-    t = time.perf_counter() - t0
-    tokens_per_s = w.tokens * (k / total_pairs) / t
+    while True:
+        o.recurrence(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D, pairs=pairs, nthreads=used)
+        passes += 1
+        t = time.perf_counter() - t0
+        if k < total_pairs or t >= target_s:
+            break
+    tokens_per_s = passes * w.tokens * (k / total_pairs) / t
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": used, "kind": "oracle",
             "sample": f"{k} of {total_pairs} (batch, head) pairs over the full sequence of the {w.name} "
-                      f"workload in {t:.2f} s; tokens/s scaled by the sampled fraction"}
+                      f"workload, {passes} pass(es) in {t:.2f} s; tokens/s scaled by the sampled fraction"}
 
 
 def spin_cycles(torch, stream, us):
