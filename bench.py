@@ -26,20 +26,21 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
 
-def algorithmic_costs(w, in_bytes, y_bytes, carried_bytes=4):
+def algorithmic_costs(w, in_bytes, y_bytes, carried_bytes=4, states_bytes=4):
     """Algorithmic bytes and flops per launch of each kernel (each tensor read
     or written once; causal interaction terms only; C.B^T once per group).
     ``carried_bytes`` is the element size of the carried states handed from the
-    state passing to the chunk scan (2 on the bf16-operand path)."""
+    state passing to the chunk scan and ``states_bytes`` that of the chunk
+    states (both 2 on the bf16-operand path)."""
     B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     nc = L // Q
     blh = B * L * H
     st = B * nc * H * N * P
     k = {}
     k["chunk_cumsum"] = dict(bytes=4 * blh + 4 * H + 2 * 4 * blh, flops=2 * blh)
-    k["chunk_state"] = dict(bytes=in_bytes * blh * P + in_bytes * B * L * G * N + 2 * 4 * blh + 4 * st,
+    k["chunk_state"] = dict(bytes=in_bytes * blh * P + in_bytes * B * L * G * N + 2 * 4 * blh + states_bytes * st,
                             flops=2 * blh * N * P)
-    k["state_passing"] = dict(bytes=4 * st + 4 * B * H * nc + carried_bytes * st + 4 * B * H * N * P,
+    k["state_passing"] = dict(bytes=states_bytes * st + 4 * B * H * nc + carried_bytes * st + 4 * B * H * N * P,
                               flops=2 * st)
     k["chunk_state_passing"] = dict(bytes=in_bytes * blh * P + in_bytes * B * L * G * N + 2 * 4 * blh
                                     + carried_bytes * st + 4 * B * H * N * P,
@@ -264,21 +265,23 @@ def main():
                 "tokens_per_s_median": round(w.tokens / (med / 1e3), 1)}
 
     # ---- phase 2: per-kernel durations of the same pipeline ssd_forward runs
-    # (bf16-operand path: carried states handed over as bf16, fp32 path: fp32
-    # in place), events on the launch stream
+    # (bf16-operand path: chunk states stored as bf16, carried states written
+    # over them as bf16; fp32 path: fp32 in place), events on the launch stream
     dA = torch.empty((B, H, nc, Q), device=dev, dtype=torch.float32)
     dtb = torch.empty_like(dA)
-    states = torch.empty((B, nc, H, N, P), device=dev, dtype=torch.float32)
-    carried_bytes = 2 if args.mma == "bf16" else 4
-    carried = (torch.empty((B, nc, H, N, P), device=dev, dtype=torch.bfloat16) if carried_bytes == 2
-               else states)
+    carried_bytes = states_bytes = 2 if args.mma == "bf16" else 4
+    states = torch.empty((B, nc, H, N, P), device=dev,
+                         dtype=torch.bfloat16 if states_bytes == 2 else torch.float32)
+    carried = states
+    # the fused state path writes its bf16 carried states to a buffer of its own
+    carried_fused = torch.empty((B, nc, H, N, P), device=dev, dtype=torch.bfloat16) if args.mma == "bf16" else states
     # ssd_forward takes the fused state path (chunk states never stored) where
     # it is supported and has at least two blocks per compute unit; the other
     # state path, where supported, is timed too (reported under "other_path")
     fused_ok = args.mma == "bf16" and N % 64 == 0 and P % 64 == 0 and w.in_dtype == "bf16"
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     fused = fused_ok and B * H * (N // 64) * (P // 64) >= 2 * cus
-    fused_call = lambda: ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA, carried=carried,
+    fused_call = lambda: ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA, carried=carried_fused,
                                                      final_states=fin, mma=args.mma)
     calls = {"chunk_cumsum": lambda: ops.ssd_chunk_cumsum(sh, t["dt"], t["A"], dA_cumsum=dA, dt_bhl=dtb)}
     if fused:
@@ -287,8 +290,9 @@ def main():
         calls["chunk_state"] = lambda: ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, states=states,
                                                            mma=args.mma)
         calls["state_passing"] = lambda: ops.ssd_state_passing(sh, states, dA, carried=carried, final_states=fin)
-    calls["chunk_scan"] = lambda: ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, carried, t["D"], y=y,
-                                                     mma=args.mma)
+    scan_carried = carried_fused if fused else carried
+    calls["chunk_scan"] = lambda: ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, scan_carried, t["D"],
+                                                     y=y, mma=args.mma)
     forward_kernels = list(calls)
     if fused_ok and not fused:
         calls["chunk_state_passing"] = fused_call
@@ -315,7 +319,7 @@ def main():
             else:
                 calls[k]()
     torch.cuda.synchronize()
-    costs = algorithmic_costs(w, in_bytes, y_bytes, carried_bytes)
+    costs = algorithmic_costs(w, in_bytes, y_bytes, carried_bytes, states_bytes)
     kernels = {}
     for k, pairs in evs.items():
         us = 1e3 * sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)

@@ -31,9 +31,10 @@
  *   - Every argument check runs on the host BEFORE any HIP call; a failed
  *     check returns its status and enqueues nothing.  A launch failure is
  *     reported as SSD_ERR_HIP.  Values are not validated: NaN/Inf propagate.
- *   - dt, A, D, dA_cumsum, dt_bhl, the chunk states, initial and final
- *     states are float32; the carried states are F32 or BF16 (the caller's
- *     choice, `carried_dtype`).  x, B and C share one input dtype `in` (F32
+ *   - dt, A, D, dA_cumsum, dt_bhl, initial and final states are float32; the
+ *     chunk states and the carried states are F32 or BF16 (the caller's
+ *     choice, `states_dtype` and `carried_dtype`; BF16 values are the fp32
+ *     results rounded to nearest even).  x, B and C share one input dtype `in` (F32
  *     or BF16).
  *   - Shape limits of this version (else SSD_ERR_UNSUPPORTED): headdim P and
  *     dstate N multiples of 16 with N <= 256 and P <= 256; chunk Q in
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 typedef enum {
   SSD_OK = 0,
@@ -98,10 +99,12 @@ ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const float* dt, const float
  * sums keeps that form):
  *   states[b,c,h] = sum_{j<Q} exp(G_{Q-1} - G_j) dt_j B_j x_j^T    (N x P)
  * with G = dA_cumsum[b,h,c,:], dt_j = dt_bhl[b,h,c,j].
- * x [B,L,H,P], Bm [B,L,G,N] (dtype `in`)  ->  states [B,nc,H,N,P] fp32.
+ * x [B,L,H,P], Bm [B,L,G,N] (dtype `in`)  ->  states [B,nc,H,N,P], stored as
+ * fp32 (states_dtype = SSD_F32) or rounded from the fp32 accumulators to
+ * bf16, nearest even (SSD_BF16).
  */
 ssd_status ssd_chunk_state(const ssd_shape* shape, const void* x, const void* Bm, ssd_dtype in,
-                           const float* dt_bhl, const float* dA_cumsum, float* states,
+                           const float* dt_bhl, const float* dA_cumsum, void* states, ssd_dtype states_dtype,
                            ssd_mma mma, void* stream);
 
 /*
@@ -110,14 +113,16 @@ ssd_status ssd_chunk_state(const ssd_shape* shape, const void* x, const void* Bm
  *   run = initial_states[b,h] (zeros when NULL)
  *   for c in 0..nc-1:  carried[b,c,h] = run;  run = exp(G_{Q-1}(c)) run + chunk_states[b,c,h]
  *   final_states[b,h] = run
- * The recurrence runs in fp32.  carried is written as fp32
- * (carried_dtype = SSD_F32; it may then equal chunk_states: in place) or
- * rounded to bf16, nearest even (SSD_BF16; it must then be a separate
- * buffer, else SSD_ERR_UNSUPPORTED).  chunk_states, carried [B,nc,H,N,P];
+ * The recurrence runs in fp32 whatever the storage dtypes: chunk_states
+ * (states_dtype F32, or BF16 widened exactly) are added to an fp32 running
+ * state.  carried is written as fp32 (carried_dtype = SSD_F32) or rounded to
+ * bf16, nearest even (SSD_BF16).  carried may equal chunk_states (in place)
+ * when the two dtypes match; aliasing with different dtypes returns
+ * SSD_ERR_UNSUPPORTED.  chunk_states, carried [B,nc,H,N,P];
  * initial_states, final_states [B,H,N,P] fp32.
  */
-ssd_status ssd_state_passing(const ssd_shape* shape, const float* chunk_states, void* carried,
-                             ssd_dtype carried_dtype, const float* dA_cumsum,
+ssd_status ssd_state_passing(const ssd_shape* shape, const void* chunk_states, ssd_dtype states_dtype,
+                             void* carried, ssd_dtype carried_dtype, const float* dA_cumsum,
                              const float* initial_states, float* final_states, void* stream);
 
 /*
@@ -131,8 +136,9 @@ ssd_status ssd_state_passing(const ssd_shape* shape, const float* chunk_states, 
  *   final_states[b,h] = run   (final_states may be NULL: not written)
  * Where ssd_chunk_state uses its head-group kernel (bf16, chunk 256 with
  * N = 128 or chunk 128 with N = 256) the results are bit-identical to
- * ssd_chunk_state followed by ssd_state_passing with the same carried_dtype;
- * elsewhere they differ from it only by the order of the fp32 sums.
+ * ssd_chunk_state with fp32 states followed by ssd_state_passing with the
+ * same carried_dtype; elsewhere they differ from it only by the order of the
+ * fp32 sums.
  * x [B,L,H,P], Bm [B,L,G,N]
  * (dtype `in`), dt_bhl and dA_cumsum [B,H,nc,Q], carried [B,nc,H,N,P] in
  * carried_dtype, initial/final states [B,H,N,P] fp32.  Supported: in = BF16,
@@ -195,14 +201,16 @@ size_t ssd_workspace_bytes(const ssd_shape* shape);
 /*
  * One-call forward: ssd_chunk_cumsum -> ssd_chunk_state -> ssd_state_passing
  * -> ssd_chunk_scan on one stream, no host synchronisation.  With
- * SSD_MMA_BF16 the carried states go from the state passing to the chunk scan
- * as bf16 (the matrix-operand values the chunk scan uses either way); with
- * SSD_MMA_F32 the state passing runs in place on the fp32 chunk states.
+ * SSD_MMA_BF16 the chunk states are stored as bf16 (states_dtype = SSD_BF16)
+ * and the state passing writes the carried states in place over them as bf16
+ * (the matrix-operand values the chunk scan uses either way); the recurrence
+ * and the final states stay fp32.  With SSD_MMA_F32 everything is fp32 and
+ * the state passing runs in place on the chunk states.
  * Where ssd_chunk_state_passing supports the shape and launches at least two
  * blocks per compute unit of the current device (B*H*(N/64)*(P/64) >= 2 x
- * units), the two middle steps are that fused call instead.  Results are
- * bit-identical to the separate calls of the path taken, with those carried
- * dtypes.
+ * units), the two middle steps are that fused call instead (chunk states
+ * never stored, so no bf16 rounding of them).  Results are bit-identical to
+ * the separate calls of the path taken, with those state and carried dtypes.
  * initial_states [B,H,N,P] may be NULL (zeros); final_states [B,H,N,P] may be
  * NULL (not written).  workspace: device memory of at least
  * ssd_workspace_bytes(shape) bytes, owned by the caller, contents undefined
@@ -229,7 +237,9 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, c
  * it with ssd_decode_step; an index outside [0, B*L) leaves its entry
  * untouched.  nseq = 0 allows seq_last, seq_states NULL.  Same arguments and
  * support as ssd_forward otherwise, always through the two-kernel state
- * path; the workspace must hold ssd_workspace_bytes_varlen(shape) bytes.
+ * path (bf16 chunk states with SSD_MMA_BF16, as in ssd_forward; the carried
+ * states stay fp32 here); the workspace must hold
+ * ssd_workspace_bytes_varlen(shape) bytes.
  * Implementation: per chunk position, the start of its sequence inside the
  * chunk masks the interaction tile and the carried-state term; each chunk
  * state collects the chunk's last sequence only, and the state passing

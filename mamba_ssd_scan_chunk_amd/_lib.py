@@ -41,8 +41,8 @@ _E = ctypes.c_int  # enums
 
 _SIGNATURES = {
     "ssd_chunk_cumsum": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
-    "ssd_chunk_state": (ctypes.c_int, [_S, _P, _P, _E, _P, _P, _P, _E, _P]),
-    "ssd_state_passing": (ctypes.c_int, [_S, _P, _P, _E, _P, _P, _P, _P]),
+    "ssd_chunk_state": (ctypes.c_int, [_S, _P, _P, _E, _P, _P, _P, _E, _E, _P]),
+    "ssd_state_passing": (ctypes.c_int, [_S, _P, _E, _P, _E, _P, _P, _P, _P]),
     "ssd_chunk_scan": (ctypes.c_int, [_S, _P, _P, _P, _E, _P, _P, _P, _E, _P, _P, _E, _E, _P]),
     "ssd_chunk_state_passing": (ctypes.c_int, [_S, _P, _P, _E, _P, _P, _P, _P, _E, _P, _E, _P]),
     "ssd_decode_step": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _E, _P, _P, _E, _P]),

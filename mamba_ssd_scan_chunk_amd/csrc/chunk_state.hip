@@ -39,8 +39,8 @@ struct StateCfg {
 template <class Op, int RW, int CT>
 __global__ __launch_bounds__(kCsThreadsState) void chunk_state_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, int in_bf16, const float* __restrict__ dt_bhl,
-    const float* __restrict__ dA_cumsum, float* __restrict__ states, int L, int H, int P, int N, int G, int Q,
-    int nc) {
+    const float* __restrict__ dA_cumsum, void* __restrict__ states, int states_bf16, int L, int H, int P, int N,
+    int G, int Q, int nc) {
   using E = typename OpElem<Op>::type;
   using Frag = typename Op::Frag;
   constexpr int PT = CT * 16;
@@ -130,7 +130,8 @@ __global__ __launch_bounds__(kCsThreadsState) void chunk_state_kernel(
     }
   }
 
-  float* so = states + (((int64_t)b * nc + c) * H + h) * (int64_t)N * P;
+  // fp32 states, or (states_bf16) rounded to bf16, nearest even
+  const int64_t so = (((int64_t)b * nc + c) * H + h) * (int64_t)N * P;
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
     const int rt = wave + 4 * i;
@@ -138,8 +139,13 @@ __global__ __launch_bounds__(kCsThreadsState) void chunk_state_kernel(
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          so[(int64_t)(16 * rt + 4 * lg + r) * P + p0 + 16 * ct + l16] = acc[i][ct][r];
+        for (int r = 0; r < 4; ++r) {
+          const int64_t e = so + (int64_t)(16 * rt + 4 * lg + r) * P + p0 + 16 * ct + l16;
+          if (states_bf16)
+            static_cast<uint16_t*>(states)[e] = (uint16_t)f32_to_bf16_bits(acc[i][ct][r]);
+          else
+            static_cast<float*>(states)[e] = acc[i][ct][r];
+        }
     }
   }
 }
@@ -160,8 +166,8 @@ size_t chunk_state_lds_bytes(const Dims& d, bool f32_mma) {
 
 template <class Op, int RW, int CT>
 static hipError_t launch_state_inst(const Dims& d, const void* x, const void* Bm, bool in_bf16,
-                                    const float* dt_bhl, const float* dA_cumsum, float* states,
-                                    hipStream_t stream, size_t lds) {
+                                    const float* dt_bhl, const float* dA_cumsum, void* states,
+                                    bool states_bf16, hipStream_t stream, size_t lds) {
   auto kern = chunk_state_kernel<Op, RW, CT>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -169,40 +175,46 @@ static hipError_t launch_state_inst(const Dims& d, const void* x, const void* Bm
   }
   const dim3 grid((unsigned)(d.H * (d.P / (16 * CT))), (unsigned)d.nc, (unsigned)d.B);
   hipLaunchKernelGGL(kern, grid, dim3(kCsThreadsState), lds, stream, x, Bm, (int)in_bf16, dt_bhl, dA_cumsum,
-                     states, (int)d.L, (int)d.H, (int)d.P, (int)d.N, (int)d.G, (int)d.Q, (int)d.nc);
+                     states, (int)states_bf16, (int)d.L, (int)d.H, (int)d.P, (int)d.N, (int)d.G, (int)d.Q, (int)d.nc);
   return hipGetLastError();
 }
 
 template <class Op, int RW>
 static hipError_t launch_state_ct(const Dims& d, const void* x, const void* Bm, bool in_bf16,
-                                  const float* dt_bhl, const float* dA_cumsum, float* states,
-                                  hipStream_t stream, size_t lds) {
+                                  const float* dt_bhl, const float* dA_cumsum, void* states,
+                                  bool states_bf16, hipStream_t stream, size_t lds) {
   switch (state_ct(d.P)) {
-    case 4: return launch_state_inst<Op, RW, 4>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
-    case 2: return launch_state_inst<Op, RW, 2>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
-    default: return launch_state_inst<Op, RW, 1>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
+    case 4: return launch_state_inst<Op, RW, 4>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
+    case 2: return launch_state_inst<Op, RW, 2>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
+    default: return launch_state_inst<Op, RW, 1>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
   }
 }
 
 template <class Op>
 static hipError_t launch_state_op(const Dims& d, const void* x, const void* Bm, bool in_bf16,
-                                  const float* dt_bhl, const float* dA_cumsum, float* states,
-                                  hipStream_t stream, size_t lds) {
+                                  const float* dt_bhl, const float* dA_cumsum, void* states,
+                                  bool states_bf16, hipStream_t stream, size_t lds) {
   switch (state_rw(d.N)) {
-    case 1: return launch_state_ct<Op, 1>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
-    case 2: return launch_state_ct<Op, 2>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
-    default: return launch_state_ct<Op, 4>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
+    case 1: return launch_state_ct<Op, 1>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
+    case 2: return launch_state_ct<Op, 2>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
+    default: return launch_state_ct<Op, 4>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
   }
 }
 
 hipError_t launch_chunk_state(const Dims& d, const void* x, const void* Bm, bool in_bf16,
                               const float* dt_bhl, const float* dA_cumsum, float* states,
                               bool f32_mma, hipStream_t stream) {
+  return launch_chunk_state_any(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, false, f32_mma, stream);
+}
+
+hipError_t launch_chunk_state_any(const Dims& d, const void* x, const void* Bm, bool in_bf16,
+                                  const float* dt_bhl, const float* dA_cumsum, void* states, bool states_bf16,
+                                  bool f32_mma, hipStream_t stream) {
   if (chunk_state_hg_supported(d, in_bf16, f32_mma))
-    return launch_chunk_state_hg(d, x, Bm, dt_bhl, dA_cumsum, states, stream);
+    return launch_chunk_state_hg(d, x, Bm, dt_bhl, dA_cumsum, states, states_bf16, stream);
   const size_t lds = chunk_state_lds_bytes(d, f32_mma);
-  if (f32_mma) return launch_state_op<OpF32>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
-  return launch_state_op<OpBF16>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, stream, lds);
+  if (f32_mma) return launch_state_op<OpF32>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
+  return launch_state_op<OpBF16>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
 }
 
 }  // namespace ssd

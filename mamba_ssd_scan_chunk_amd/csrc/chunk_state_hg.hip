@@ -50,11 +50,13 @@ struct ShgCfg {
 // from dt and A (the cumulative-sum step, same arithmetic as that kernel),
 // keeps them in LDS, and writes dA_cumsum / dt_bhl for the later steps;
 // otherwise it reads them.
-template <int Q, int N, bool FUSE>
+// SBF16: the states are stored rounded to bf16 (nearest even, 8-byte stores
+// of four consecutive p) instead of fp32.
+template <int Q, int N, bool FUSE, bool SBF16>
 __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bhl,
     const float* __restrict__ dA_cumsum, const float* __restrict__ dt_raw, const float* __restrict__ Avec,
-    float* __restrict__ dA_out, float* __restrict__ dt_out, float* __restrict__ states, int L, int H, int P, int G,
+    float* __restrict__ dA_out, float* __restrict__ dt_out, void* __restrict__ states, int L, int H, int P, int G,
     int nc, int HG, int nhg, int npt, int remap) {
   using Cfg = ShgCfg<Q, N>;
   using Op = OpBF16;
@@ -244,14 +246,19 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
         }
       }
       // lane holds S[n = 16*(NTW*wave + i) + l16][p = p0 + 16ct + 4lg .. +3]
-      float* so = states + (((int64_t)b * nc + c) * H + h) * (int64_t)(N * P) + p0;
+      const int64_t so = (((int64_t)b * nc + c) * H + h) * (int64_t)(N * P) + p0;
 #pragma unroll
       for (int i = 0; i < NTW; ++i) {
         const int n = 16 * (NTW * wave + i) + l16;
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-          *reinterpret_cast<float4*>(so + n * P + 16 * ct + 4 * lg) =
-              make_float4(acc[i][ct][0], acc[i][ct][1], acc[i][ct][2], acc[i][ct][3]);
+        for (int ct = 0; ct < 4; ++ct) {
+          if constexpr (SBF16)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(states) + so + n * P + 16 * ct + 4 * lg) =
+                make_uint2(pack_bf16x2(acc[i][ct][0], acc[i][ct][1]), pack_bf16x2(acc[i][ct][2], acc[i][ct][3]));
+          else
+            *reinterpret_cast<float4*>(static_cast<float*>(states) + so + n * P + 16 * ct + 4 * lg) =
+                make_float4(acc[i][ct][0], acc[i][ct][1], acc[i][ct][2], acc[i][ct][3]);
+        }
       }
     }
     __syncthreads();  // all reads of this head's Xn are done
@@ -286,12 +293,12 @@ bool chunk_state_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
   return false;
 }
 
-template <int Q, int N, bool FUSE>
+template <int Q, int N, bool FUSE, bool SBF16>
 static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
                                   const float* dA_cumsum, const float* dt_raw, const float* A, float* dA_out,
-                                  float* dt_out, float* states, hipStream_t stream) {
+                                  float* dt_out, void* states, hipStream_t stream) {
   using Cfg = ShgCfg<Q, N>;
-  auto kern = chunk_state_hg_kernel<Q, N, FUSE>;
+  auto kern = chunk_state_hg_kernel<Q, N, FUSE, SBF16>;
   // with FUSE the block also holds the sums and dt rows of its heads in LDS
   const int64_t cap = FUSE ? (int64_t)((160 * 1024 - Cfg::lds_total) / (8 * Q)) : (int64_t)1 << 30;
   const int npt = (int)(d.P / Cfg::PT);
@@ -318,22 +325,28 @@ static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, 
 }
 
 hipError_t launch_chunk_state_hg(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
-                                 const float* dA_cumsum, float* states, hipStream_t stream) {
+                                 const float* dA_cumsum, void* states, bool states_bf16, hipStream_t stream) {
 #define SHG_LAUNCH(QQ, NN)                                                                                  \
   if (d.Q == QQ && d.N == NN)                                                                               \
-    return launch_shg_inst<QQ, NN, false>(d, x, Bm, dt_bhl, dA_cumsum, nullptr, nullptr, nullptr, nullptr, \
-                                          states, stream);
+    return states_bf16 ? launch_shg_inst<QQ, NN, false, true>(d, x, Bm, dt_bhl, dA_cumsum, nullptr, nullptr, \
+                                                              nullptr, nullptr, states, stream)              \
+                       : launch_shg_inst<QQ, NN, false, false>(d, x, Bm, dt_bhl, dA_cumsum, nullptr, nullptr, \
+                                                               nullptr, nullptr, states, stream);
   SHG_SHAPES(SHG_LAUNCH)
 #undef SHG_LAUNCH
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_state_cumsum_hg(const Dims& d, const void* x, const void* Bm, const float* dt,
-                                        const float* A, float* dA_cumsum, float* dt_bhl, float* states,
-                                        hipStream_t stream) {
-#define SHG_LAUNCH(QQ, NN) \
-  if (d.Q == QQ && d.N == NN) \
-    return launch_shg_inst<QQ, NN, true>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl, states, stream);
+                                        const float* A, float* dA_cumsum, float* dt_bhl, void* states,
+                                        bool states_bf16, hipStream_t stream) {
+#define SHG_LAUNCH(QQ, NN)                                                                                     \
+  if (d.Q == QQ && d.N == NN)                                                                                  \
+    return states_bf16                                                                                         \
+               ? launch_shg_inst<QQ, NN, true, true>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl, states, \
+                                                     stream)                                                   \
+               : launch_shg_inst<QQ, NN, true, false>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl,       \
+                                                      states, stream);
   SHG_SHAPES(SHG_LAUNCH)
 #undef SHG_LAUNCH
   return hipErrorInvalidValue;

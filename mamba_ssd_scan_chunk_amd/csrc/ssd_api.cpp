@@ -57,9 +57,11 @@ ssd_status validate_cumsum(const ssd_shape* shape, const float* dt, const float*
 }
 
 ssd_status validate_state(const ssd_shape* shape, const void* x, const void* Bm, ssd_dtype in,
-                          const float* dt_bhl, const float* dA_cumsum, float* states, ssd_mma mma, Dims* d) {
+                          const float* dt_bhl, const float* dA_cumsum, void* states, ssd_dtype states_dtype,
+                          ssd_mma mma, Dims* d) {
   SSD_TRY(check_shape(shape, d));
   SSD_TRY(check_dtype(in));
+  SSD_TRY(check_dtype(states_dtype));
   SSD_TRY(check_mma(mma));
   if (!x || !Bm || !dt_bhl || !dA_cumsum || !states) return SSD_ERR_NULL;
   if (!aligned16(x) || !aligned16(Bm) || !aligned16(dt_bhl) || !aligned16(dA_cumsum) || !aligned16(states))
@@ -68,14 +70,15 @@ ssd_status validate_state(const ssd_shape* shape, const void* x, const void* Bm,
   return SSD_OK;
 }
 
-ssd_status validate_passing(const ssd_shape* shape, const float* chunk_states, void* carried,
+ssd_status validate_passing(const ssd_shape* shape, const void* chunk_states, ssd_dtype states_dtype, void* carried,
                             ssd_dtype carried_dtype, const float* dA_cumsum, const float* initial_states,
                             float* final_states, Dims* d) {
   SSD_TRY(check_shape(shape, d));
+  SSD_TRY(check_dtype(states_dtype));
   SSD_TRY(check_dtype(carried_dtype));
   if (!chunk_states || !carried || !dA_cumsum) return SSD_ERR_NULL;
-  // bf16 carried states are narrower than the chunk states: no in-place form
-  if (carried_dtype == SSD_BF16 && carried == static_cast<const void*>(chunk_states)) return SSD_ERR_UNSUPPORTED;
+  // in place only between equal element sizes
+  if (carried_dtype != states_dtype && carried == chunk_states) return SSD_ERR_UNSUPPORTED;
   if (!aligned16(chunk_states) || !aligned16(carried) || !aligned16(dA_cumsum) ||
       (initial_states && !aligned16(initial_states)) || (final_states && !aligned16(final_states)))
     return SSD_ERR_ALIGN;
@@ -133,25 +136,23 @@ ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const float* dt, const float
 }
 
 ssd_status ssd_chunk_state(const ssd_shape* shape, const void* x, const void* Bm, ssd_dtype in,
-                           const float* dt_bhl, const float* dA_cumsum, float* states, ssd_mma mma,
-                           void* stream) {
+                           const float* dt_bhl, const float* dA_cumsum, void* states, ssd_dtype states_dtype,
+                           ssd_mma mma, void* stream) {
   Dims d;
-  SSD_TRY(validate_state(shape, x, Bm, in, dt_bhl, dA_cumsum, states, mma, &d));
-  return from_hip(ssd::launch_chunk_state(d, x, Bm, in == SSD_BF16, dt_bhl, dA_cumsum, states,
-                                          mma == SSD_MMA_F32, (hipStream_t)stream));
+  SSD_TRY(validate_state(shape, x, Bm, in, dt_bhl, dA_cumsum, states, states_dtype, mma, &d));
+  return from_hip(ssd::launch_chunk_state_any(d, x, Bm, in == SSD_BF16, dt_bhl, dA_cumsum, states,
+                                              states_dtype == SSD_BF16, mma == SSD_MMA_F32, (hipStream_t)stream));
 }
 
-ssd_status ssd_state_passing(const ssd_shape* shape, const float* chunk_states, void* carried,
-                             ssd_dtype carried_dtype, const float* dA_cumsum, const float* initial_states,
-                             float* final_states, void* stream) {
+ssd_status ssd_state_passing(const ssd_shape* shape, const void* chunk_states, ssd_dtype states_dtype,
+                             void* carried, ssd_dtype carried_dtype, const float* dA_cumsum,
+                             const float* initial_states, float* final_states, void* stream) {
   Dims d;
-  SSD_TRY(validate_passing(shape, chunk_states, carried, carried_dtype, dA_cumsum, initial_states, final_states,
-                           &d));
-  if (carried_dtype == SSD_BF16)
-    return from_hip(ssd::launch_state_passing_bf16(d, chunk_states, static_cast<uint16_t*>(carried), dA_cumsum,
-                                                   initial_states, final_states, (hipStream_t)stream));
-  return from_hip(ssd::launch_state_passing(d, chunk_states, static_cast<float*>(carried), dA_cumsum,
-                                            initial_states, final_states, (hipStream_t)stream));
+  SSD_TRY(validate_passing(shape, chunk_states, states_dtype, carried, carried_dtype, dA_cumsum, initial_states,
+                           final_states, &d));
+  return from_hip(ssd::launch_state_passing_any(d, chunk_states, states_dtype == SSD_BF16, carried,
+                                                carried_dtype == SSD_BF16, dA_cumsum, initial_states, final_states,
+                                                (hipStream_t)stream));
 }
 
 ssd_status ssd_chunk_state_passing(const ssd_shape* shape, const void* x, const void* Bm, ssd_dtype in,
@@ -265,20 +266,22 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, c
         ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, hb, true, D, y, y_dtype == SSD_BF16, f32m, s)));
     return SSD_OK;
   }
+  // bf16 matrix operands: the chunk states pass through memory as bf16 and
+  // the state passing (fp32 recurrence) writes the carried states in place
+  // over them, rounded to bf16 -- the operand values the chunk scan would
+  // round them to; fp32 matrix operands: fp32 throughout
+  const bool sbf = !f32m;
   if (ssd::chunk_state_hg_supported(d, bf, f32m)) {
     // the head-group chunk-state kernel computes the cumulative sums itself
-    SSD_TRY(from_hip(ssd::launch_chunk_state_cumsum_hg(d, x, Bm, dt, A, dA, dtb, st, s)));
+    SSD_TRY(from_hip(ssd::launch_chunk_state_cumsum_hg(d, x, Bm, dt, A, dA, dtb, st, sbf, s)));
   } else {
     SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
-    SSD_TRY(from_hip(ssd::launch_chunk_state(d, x, Bm, bf, dtb, dA, st, f32m, s)));
+    SSD_TRY(from_hip(ssd::launch_chunk_state_any(d, x, Bm, bf, dtb, dA, st, sbf, f32m, s)));
   }
-  if (!f32m) {
-    // bf16 matrix operands: hand the chunk scan the carried states already
-    // rounded to bf16 (the operand values it would round them to)
-    uint16_t* hb = reinterpret_cast<uint16_t*>(base + ws.hb_off);
-    SSD_TRY(from_hip(ssd::launch_state_passing_bf16(d, st, hb, dA, initial_states, final_states, s)));
+  if (sbf) {
+    SSD_TRY(from_hip(ssd::launch_state_passing_any(d, st, true, st, true, dA, initial_states, final_states, s)));
     SSD_TRY(from_hip(
-        ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, hb, true, D, y, y_dtype == SSD_BF16, f32m, s)));
+        ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, true, D, y, y_dtype == SSD_BF16, f32m, s)));
   } else {
     SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dA, initial_states, final_states, s)));
     SSD_TRY(from_hip(
@@ -328,10 +331,18 @@ ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float
   SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
   SSD_TRY(from_hip(ssd::launch_seq_start(d, seq_idx, sst, s)));
   SSD_TRY(from_hip(ssd::launch_varlen_prep(d, dA, dtb, sst, dAp, dtl, s)));
-  SSD_TRY(from_hip(ssd::launch_chunk_state(d, x, Bm, bf, dtl, dA, st, f32m, s)));
-  // fp32 carried states in place on both paths: the per-sequence states read
-  // them, and the chunk scan rounds them to its operand precision itself
-  SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dAp, initial_states, final_states, s)));
+  // fp32 carried states on both paths: the per-sequence states read them, and
+  // the chunk scan rounds them to its operand precision itself.  With bf16
+  // matrix operands the chunk states pass through memory as bf16 (in the
+  // bf16 carried-state area), exactly as in ssd_forward.
+  if (!f32m) {
+    uint16_t* sb = reinterpret_cast<uint16_t*>(base + ws.hb_off);
+    SSD_TRY(from_hip(ssd::launch_chunk_state_any(d, x, Bm, bf, dtl, dA, sb, true, f32m, s)));
+    SSD_TRY(from_hip(ssd::launch_state_passing_any(d, sb, true, st, false, dAp, initial_states, final_states, s)));
+  } else {
+    SSD_TRY(from_hip(ssd::launch_chunk_state(d, x, Bm, bf, dtl, dA, st, f32m, s)));
+    SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dAp, initial_states, final_states, s)));
+  }
   SSD_TRY(from_hip(ssd::launch_varlen_states(d, x, Bm, bf, dtb, dA, sst, st, nseq, seq_last, seq_states, s)));
   SSD_TRY(from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, false, D, y, y_dtype == SSD_BF16, f32m,
                                           s, sst)));

@@ -31,19 +31,24 @@ hipError_t launch_varlen_prep(const Dims& d, const float* dA_cumsum, const float
 hipError_t launch_chunk_state(const Dims& d, const void* x, const void* Bm, bool in_bf16,
                               const float* dt_bhl, const float* dA_cumsum, float* states,
                               bool f32_mma, hipStream_t stream);
+// The same with the states stored as fp32 or (states_bf16) rounded to bf16,
+// nearest even.
+hipError_t launch_chunk_state_any(const Dims& d, const void* x, const void* Bm, bool in_bf16,
+                                  const float* dt_bhl, const float* dA_cumsum, void* states, bool states_bf16,
+                                  bool f32_mma, hipStream_t stream);
 
 // Head-group variant of the chunk states (bf16 inputs and operands,
 // (chunk, N) in {(64,128), (128,128), (256,128), (64,256), (128,256)}, P a multiple of 64); launch_chunk_state
 // picks it when supported.
 bool chunk_state_hg_supported(const Dims& d, bool in_bf16, bool f32_mma);
 hipError_t launch_chunk_state_hg(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
-                                 const float* dA_cumsum, float* states, hipStream_t stream);
+                                 const float* dA_cumsum, void* states, bool states_bf16, hipStream_t stream);
 // The same kernel with the cumulative-sum step fused in front: it reads dt and
 // A, writes dA_cumsum and dt_bhl (bit-identical to launch_chunk_cumsum) and
 // the chunk states.  Same support as chunk_state_hg_supported.
 hipError_t launch_chunk_state_cumsum_hg(const Dims& d, const void* x, const void* Bm, const float* dt,
-                                        const float* A, float* dA_cumsum, float* dt_bhl, float* states,
-                                        hipStream_t stream);
+                                        const float* A, float* dA_cumsum, float* dt_bhl, void* states,
+                                        bool states_bf16, hipStream_t stream);
 
 hipError_t launch_state_passing(const Dims& d, const float* chunk_states, float* carried,
                                 const float* dA_cumsum, const float* initial_states,
@@ -53,6 +58,12 @@ hipError_t launch_state_passing(const Dims& d, const float* chunk_states, float*
 hipError_t launch_state_passing_bf16(const Dims& d, const float* chunk_states, uint16_t* carried_bf16,
                                      const float* dA_cumsum, const float* initial_states,
                                      float* final_states, hipStream_t stream);
+// Any combination of chunk-state and carried dtypes (fp32 or bf16 bits); the
+// recurrence runs in fp32.  carried may equal chunk_states when both dtypes
+// match.
+hipError_t launch_state_passing_any(const Dims& d, const void* chunk_states, bool states_bf16, void* carried,
+                                    bool carried_bf16, const float* dA_cumsum, const float* initial_states,
+                                    float* final_states, hipStream_t stream);
 
 // Fused state path: chunk states and the inter-chunk advance in one pass (the
 // chunk states stay on chip); carried and final states are bit-identical to

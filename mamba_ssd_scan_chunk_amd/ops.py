@@ -76,8 +76,10 @@ def ssd_chunk_cumsum(shape, dt, A, dA_cumsum=None, dt_bhl=None, with_dt=True, st
     return dA_cumsum, dt_bhl
 
 
-def ssd_chunk_state(shape, x, Bm, dt_bhl, dA_cumsum, states=None, mma="bf16", stream=None):
-    """Per-chunk states [B,nc,H,N,P] fp32 (jump formula with decay)."""
+def ssd_chunk_state(shape, x, Bm, dt_bhl, dA_cumsum, states=None, mma="bf16", states_dtype="f32", stream=None):
+    """Per-chunk states [B,nc,H,N,P] (jump formula with decay), stored in
+    ``states_dtype`` ("f32", or "bf16" rounded to nearest even; a given
+    ``states`` tensor's dtype wins)."""
     sh = _shape(shape)
     B, L, H, P, N, G, Q, nc = _dims(sh)
     io = (torch.float32, torch.bfloat16)
@@ -86,11 +88,12 @@ def ssd_chunk_state(shape, x, Bm, dt_bhl, dA_cumsum, states=None, mma="bf16", st
     _req(dt_bhl, "dt_bhl", (B, H, nc, Q), (torch.float32,))
     _req(dA_cumsum, "dA_cumsum", (B, H, nc, Q), (torch.float32,))
     if states is None:
-        states = torch.empty((B, nc, H, N, P), device=x.device, dtype=torch.float32)
-    _req(states, "states", (B, nc, H, N, P), (torch.float32,))
+        sdt = _DTNAME[states_dtype] if isinstance(states_dtype, str) else states_dtype
+        states = torch.empty((B, nc, H, N, P), device=x.device, dtype=sdt)
+    _req(states, "states", (B, nc, H, N, P), io)
     lib = load_library()
     check(lib.ssd_chunk_state(sh, _ptr(x), _ptr(Bm), _DT[x.dtype], _ptr(dt_bhl), _ptr(dA_cumsum),
-                              _ptr(states), _mma(mma), _stream(stream)))
+                              _ptr(states), _DT[states.dtype], _mma(mma), _stream(stream)))
     return states
 
 
@@ -98,12 +101,14 @@ def ssd_state_passing(shape, chunk_states, dA_cumsum, initial_states=None, carri
                       in_place=False, carried_dtype="f32", stream=None):
     """Carried states [B,nc,H,N,P] (state entering each chunk) in
     ``carried_dtype`` ("f32" or "bf16", rounded to nearest even; a given
-    ``carried`` tensor's dtype wins) and fp32 final states [B,H,N,P].
-    ``in_place=True`` writes fp32 carried states over ``chunk_states``."""
+    ``carried`` tensor's dtype wins) and fp32 final states [B,H,N,P], from
+    chunk states in fp32 or bf16 (the recurrence runs in fp32).
+    ``in_place=True`` writes the carried states over ``chunk_states``, in
+    their dtype."""
     sh = _shape(shape)
     B, L, H, P, N, G, Q, nc = _dims(sh)
     f32 = (torch.float32,)
-    _req(chunk_states, "chunk_states", (B, nc, H, N, P), f32)
+    _req(chunk_states, "chunk_states", (B, nc, H, N, P), (torch.float32, torch.bfloat16))
     _req(dA_cumsum, "dA_cumsum", (B, H, nc, Q), f32)
     if initial_states is not None:
         _req(initial_states, "initial_states", (B, H, N, P), f32)
@@ -118,8 +123,8 @@ def ssd_state_passing(shape, chunk_states, dA_cumsum, initial_states=None, carri
         final_states = torch.empty((B, H, N, P), device=chunk_states.device, dtype=torch.float32)
     _req(final_states, "final_states", (B, H, N, P), f32)
     lib = load_library()
-    check(lib.ssd_state_passing(sh, _ptr(chunk_states), _ptr(carried), _DT[carried.dtype], _ptr(dA_cumsum),
-                                _ptr(initial_states), _ptr(final_states), _stream(stream)))
+    check(lib.ssd_state_passing(sh, _ptr(chunk_states), _DT[chunk_states.dtype], _ptr(carried), _DT[carried.dtype],
+                                _ptr(dA_cumsum), _ptr(initial_states), _ptr(final_states), _stream(stream)))
     return carried, final_states
 
 

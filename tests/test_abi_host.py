@@ -40,7 +40,7 @@ def test_header_declares_the_abi():
 def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
-    assert lib.ssd_abi_version() == 2
+    assert lib.ssd_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -65,8 +65,8 @@ def shape(**kw):
 def test_shape_checks(lib, kw, code):
     s = shape(**kw)
     assert lib.ssd_chunk_cumsum(s, FAKE, FAKE, FAKE, FAKE, None) == code
-    assert lib.ssd_chunk_state(s, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, None) == code
-    assert lib.ssd_state_passing(s, FAKE, FAKE, 0, FAKE, None, FAKE, None) == code
+    assert lib.ssd_chunk_state(s, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, 0, None) == code
+    assert lib.ssd_state_passing(s, FAKE, 0, FAKE, 0, FAKE, None, FAKE, None) == code
     assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1, 0, None) == code
     assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, 1, FAKE, FAKE, 1 << 40, 0,
                            None) == code
@@ -87,12 +87,14 @@ def test_null_pointers(lib):
         args = [FAKE] * 5
         args[i] = None
         x, Bm, dtb, dA, st = args
-        assert lib.ssd_chunk_state(s, x, Bm, 1, dtb, dA, st, 0, None) == NULL
+        assert lib.ssd_chunk_state(s, x, Bm, 1, dtb, dA, st, 0, 0, None) == NULL
+        assert lib.ssd_chunk_state(s, x, Bm, 1, dtb, dA, st, 1, 0, None) == NULL
     for i in range(3):
         args = [FAKE] * 3
         args[i] = None
-        assert lib.ssd_state_passing(s, args[0], args[1], 0, args[2], None, FAKE, None) == NULL
-        assert lib.ssd_state_passing(s, args[0], args[1], 1, args[2], None, FAKE, None) == NULL
+        for sdt in (0, 1):
+            assert lib.ssd_state_passing(s, args[0], sdt, args[1], 0, args[2], None, FAKE, None) == NULL
+            assert lib.ssd_state_passing(s, args[0], sdt, args[1], 1, args[2], None, FAKE, None) == NULL
     for i in range(8):
         args = [FAKE] * 8
         args[i] = None
@@ -108,12 +110,14 @@ def test_null_pointers(lib):
 
 def test_dtype_and_mma_enums(lib):
     s = shape()
-    assert lib.ssd_chunk_state(s, FAKE, FAKE, 2, FAKE, FAKE, FAKE, 0, None) == DTYPE
-    assert lib.ssd_chunk_state(s, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 2, None) == DTYPE
+    assert lib.ssd_chunk_state(s, FAKE, FAKE, 2, FAKE, FAKE, FAKE, 0, 0, None) == DTYPE
+    assert lib.ssd_chunk_state(s, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, 2, None) == DTYPE
+    assert lib.ssd_chunk_state(s, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 2, 0, None) == DTYPE
     assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 7, 0, None) == DTYPE
     assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1, -1, None) == DTYPE
     assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 3, FAKE, FAKE, 1, 0, None) == DTYPE
-    assert lib.ssd_state_passing(s, FAKE, FAKE, 2, FAKE, None, FAKE, None) == DTYPE
+    assert lib.ssd_state_passing(s, FAKE, 0, FAKE, 2, FAKE, None, FAKE, None) == DTYPE
+    assert lib.ssd_state_passing(s, FAKE, 3, FAKE, 0, FAKE, None, FAKE, None) == DTYPE
     assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, None, FAKE, 1, FAKE, FAKE, 1 << 40, 0,
                            None) == DTYPE
 
@@ -123,9 +127,11 @@ def test_alignment(lib):
     odd = FAKE + 4
     assert lib.ssd_chunk_cumsum(s, odd, FAKE, FAKE, FAKE, None) == ALIGN
     assert lib.ssd_chunk_cumsum(s, FAKE, FAKE, FAKE, odd, None) == ALIGN
-    assert lib.ssd_chunk_state(s, FAKE, odd, 1, FAKE, FAKE, FAKE, 0, None) == ALIGN
-    assert lib.ssd_state_passing(s, FAKE, FAKE, 0, FAKE, odd, FAKE, None) == ALIGN
-    assert lib.ssd_state_passing(s, FAKE, odd, 1, FAKE, None, FAKE, None) == ALIGN
+    assert lib.ssd_chunk_state(s, FAKE, odd, 1, FAKE, FAKE, FAKE, 0, 0, None) == ALIGN
+    assert lib.ssd_chunk_state(s, FAKE, FAKE, 1, FAKE, FAKE, odd, 1, 0, None) == ALIGN
+    assert lib.ssd_state_passing(s, FAKE, 0, FAKE, 0, FAKE, odd, FAKE, None) == ALIGN
+    assert lib.ssd_state_passing(s, FAKE, 0, odd, 1, FAKE, None, FAKE, None) == ALIGN
+    assert lib.ssd_state_passing(s, odd, 1, FAKE + 16, 1, FAKE, None, FAKE, None) == ALIGN
     assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, FAKE, odd, 1, 0, None) == ALIGN
     assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, odd, 1, FAKE, FAKE, 1, 0, None) == ALIGN
     assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, odd, FAKE, 1, FAKE, FAKE, 1 << 40, 0,
@@ -245,13 +251,14 @@ def test_backward_checks(lib):
     assert call(shape(nheads=6, ngroups=4)) == SHAPE
 
 
-def test_bf16_carried_has_no_in_place_form(lib):
-    """bf16 carried states are narrower than the fp32 chunk states: writing
-    them over the chunk states would race, so that call is refused before any
-    HIP call; the fp32 in-place form stays valid (checked up to the launch on
-    the GPU side)."""
+def test_mixed_dtype_state_passing_has_no_in_place_form(lib):
+    """Carried states of another element size than the chunk states cannot be
+    written over them (the two layouts would race), so those calls are refused
+    before any HIP call; the in-place forms with matching dtypes (fp32 -> fp32,
+    bf16 -> bf16) stay valid (exercised on the GPU side)."""
     s = shape()
-    assert lib.ssd_state_passing(s, FAKE, FAKE, 1, FAKE, None, FAKE, None) == UNSUP
+    assert lib.ssd_state_passing(s, FAKE, 0, FAKE, 1, FAKE, None, FAKE, None) == UNSUP
+    assert lib.ssd_state_passing(s, FAKE, 1, FAKE, 0, FAKE, None, FAKE, None) == UNSUP
 
 
 def test_ragged_last_chunk_is_a_valid_shape(lib):

@@ -100,6 +100,65 @@ def test_chunk_state(shape, mode):
     assert e <= tol_for(mma)
 
 
+@pytest.mark.parametrize("mode", MODES, ids=["-".join(m) for m in MODES])
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_chunk_state_bf16_storage(shape, mode):
+    """Chunk states stored as bf16 are the fp32 states of the same call rounded
+    to nearest even (the accumulators are the same; only the store differs),
+    on every kernel instance, and within the bf16 bound of the oracle."""
+    from mamba_ssd_scan_chunk_amd.inputs import bf16_round
+    in_dtype, mma = mode
+    say(f"chunk_state bf16 storage {shape} {mode}")
+    inp = _inp(shape, in_dtype, seed=1)
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    S32 = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma=mma)
+    S16 = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma=mma, states_dtype="bf16")
+    torch.cuda.synchronize()
+    assert S16.dtype == torch.bfloat16
+    got = S16.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, bf16_round(S32.cpu().numpy()))
+    ref = oracle().chunk_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk)
+    e = relerr(S16.float(), ref)
+    say(f"  rel err {e:.3g}")
+    assert e <= tol_for(mma) + 2.0 ** -8
+
+
+@pytest.mark.parametrize("with_h0", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_state_passing_bf16_chunk_states(shape, with_h0):
+    """The state passing over bf16 chunk states widens them exactly and runs
+    the same fp32 recurrence: bit-equal to the fp32 call over the widened
+    values, for fp32 and bf16 carried states and for the bf16 in-place form;
+    within the bf16 bound of the oracle."""
+    say(f"state_passing bf16 chunk states {shape} h0={with_h0}")
+    inp = _inp(shape, "f32", seed=2, dt_shift=3.0)
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    o = oracle()
+    S = o.chunk_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk)
+    h0 = _h0(inp) if with_h0 else None
+    Hin, fin = o.carried_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk, h0=h0)
+    dA, _ = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    S16 = torch.from_numpy(S.astype(np.float32)).cuda().to(torch.bfloat16)
+    S16w = S16.float()
+    h0_t = None if h0 is None else torch.from_numpy(h0).cuda()
+    c_ref32, f_ref = ops.ssd_state_passing(sh, S16w, dA, initial_states=h0_t)
+    c_ref16, _ = ops.ssd_state_passing(sh, S16w, dA, initial_states=h0_t, carried_dtype="bf16")
+    c32, f1 = ops.ssd_state_passing(sh, S16, dA, initial_states=h0_t, carried_dtype="f32")
+    c16, f2 = ops.ssd_state_passing(sh, S16, dA, initial_states=h0_t, carried_dtype="bf16")
+    S16b = S16.clone()
+    c16i, f3 = ops.ssd_state_passing(sh, S16b, dA, initial_states=h0_t, in_place=True)
+    torch.cuda.synchronize()
+    assert c16i.data_ptr() == S16b.data_ptr() and c16i.dtype == torch.bfloat16
+    assert torch.equal(c32, c_ref32) and torch.equal(c16, c_ref16) and torch.equal(c16i, c_ref16)
+    assert torch.equal(f1, f_ref) and torch.equal(f2, f_ref) and torch.equal(f3, f_ref)
+    e1, e2 = relerr(c32, Hin), relerr(f1, fin)
+    say(f"  rel err carried {e1:.3g} final {e2:.3g}")
+    assert e1 <= 2.0 ** -8 and e2 <= 2.0 ** -8
+
+
 @pytest.mark.parametrize("with_h0", [False, True])
 @pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
@@ -317,10 +376,11 @@ HG_SHAPES = [
 @pytest.mark.parametrize("y_dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", HG_SHAPES, ids=[s[0] for s in HG_SHAPES])
 def test_forward_bitwise_equals_split_calls(shape, y_dtype):
-    """On the bf16 path the one-call forward passes the carried states to the
-    chunk scan rounded to bf16, exactly the operand values the chunk scan
-    rounds fp32 carried states to: y and the final states must equal the four
-    split calls bit for bit."""
+    """On the bf16 path the one-call forward stores the chunk states as bf16
+    and passes the carried states to the chunk scan rounded to bf16, exactly
+    the operand values the chunk scan rounds fp32 carried states to: y and the
+    final states must equal the split calls (bf16 chunk states, either carried
+    dtype, or the fused state call) bit for bit."""
     say(f"forward vs split calls {shape} y {y_dtype}")
     inp = _inp(shape, "bf16", seed=12, dt_shift=2.0)
     h0 = torch.from_numpy(_h0(inp)).cuda()
@@ -332,7 +392,7 @@ def test_forward_bitwise_equals_split_calls(shape, y_dtype):
     name, B, L, H, P, N, G, Q = shape
     # the forward's state step is either the two-call path or (N, P multiples
     # of 64) the fused state call; the outputs must equal one of them exactly
-    S = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma="bf16")
+    S = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma="bf16", states_dtype="bf16")
     fused_ok = N % 64 == 0 and P % 64 == 0
     for cdt in ["f32", "bf16"]:
         states = [ops.ssd_state_passing(sh, S, dA, initial_states=h0, carried_dtype=cdt)]
@@ -418,8 +478,8 @@ def test_forward_state_path_choice():
         car, fin_s = ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA, initial_states=h0_t,
                                                  carried_dtype="bf16")
     else:
-        S = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma="bf16")
-        car, fin_s = ops.ssd_state_passing(sh, S, dA, initial_states=h0_t, carried_dtype="bf16")
+        S = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma="bf16", states_dtype="bf16")
+        car, fin_s = ops.ssd_state_passing(sh, S, dA, initial_states=h0_t, in_place=True)
     y_s = ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, car, t["D"], y_dtype="bf16", mma="bf16")
     torch.cuda.synchronize()
     say(f"  {cus} compute units: {'fused' if fused else 'two-kernel'} state path expected")
