@@ -178,6 +178,8 @@ def main():
                     help="time only ssd_backward in this operand mode (--backward-steps calls) and print that")
     ap.add_argument("--no-cumsum-sweep", dest="cumsum_sweep", action="store_false",
                     help="skip the chunk_cumsum bandwidth-vs-length sweep")
+    ap.add_argument("--kernel-reps", type=int, default=4,
+                    help="back-to-back launches of each call between one pair of events in the per-kernel rows")
     ap.add_argument("--kernel-only", default=None,
                     help="time only this ABI call in the per-kernel loop (for profiling)")
     args = ap.parse_args()
@@ -296,16 +298,27 @@ def main():
     forward_kernels = list(calls)
     if fused_ok and not fused:
         calls["chunk_state_passing"] = fused_call
+    if fused:  # the two-kernel state path, timed beside the fused one
+        calls["chunk_state"] = lambda: ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, states=states,
+                                                           mma=args.mma)
+        calls["state_passing"] = lambda: ops.ssd_state_passing(sh, states, dA, carried=carried, final_states=fin)
     order = list(calls) if args.kernel_only is None else [args.kernel_only]
     for _ in range(2):
         for k in calls:
             calls[k]()
     torch.cuda.synchronize()
-    # Each timed step starts with a bounded GPU spin (~300 us) that keeps the
+    # Each timed step starts with a bounded GPU spin (~1 ms) that keeps the
     # GPU busy while the host queues the step's calls and events, so every
     # event pair brackets GPU time only: no host submission gap inflates the
-    # small kernels.
-    spin = spin_cycles(torch, stream, 300)
+    # small kernels.  Each pair brackets REPS back-to-back launches of one call
+    # (the dispatch gap between a kernel and the event before it would
+    # otherwise count against short kernels); the per-launch time is the
+    # pair's time over REPS.  The other state path (not part of the forward
+    # here) is timed one launch per pair: repeated, its input rows would stay
+    # in the last-level cache between launches, unlike in any forward.
+    reps = max(1, args.kernel_reps)
+    kreps = {k: (reps if k in forward_kernels else 1) for k in calls}
+    spin = spin_cycles(torch, stream, 1000)
     evs = {k: [] for k in order}
     for _ in range(args.steps):
         torch.cuda._sleep(spin)
@@ -313,7 +326,8 @@ def main():
             if k in evs:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                calls[k]()
+                for _r in range(kreps[k]):
+                    calls[k]()
                 b.record(stream)
                 evs[k].append((a, b))
             else:
@@ -322,7 +336,7 @@ def main():
     costs = algorithmic_costs(w, in_bytes, y_bytes, carried_bytes, states_bytes)
     kernels = {}
     for k, pairs in evs.items():
-        us = 1e3 * sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+        us = 1e3 * sum(a.elapsed_time(b) for a, b in pairs) / (len(pairs) * kreps[k])
         c = costs[k]
         gbps = c["bytes"] / (us * 1e-6) / 1e9
         tflops = c["flops"] / (us * 1e-6) / 1e12
