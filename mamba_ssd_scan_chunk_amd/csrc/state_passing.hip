@@ -31,7 +31,6 @@
 namespace ssd {
 
 constexpr int kSpThreads = 256;
-constexpr int kSpUnroll = 8;
 
 // EPT consecutive state elements of one thread in fp32 or bf16 storage:
 // the raw vector moved by one load or store (16 bytes, except 4 fp32 -> 16 and
@@ -100,7 +99,9 @@ struct SpVec<8, false> {
 
 // One thread owns EPT consecutive state elements: 4 with fp32 chunk states
 // (16-byte loads), 8 with bf16 chunk states (16-byte loads as well).
-template <bool SBF16, bool CBF16, int EPT, int TPB>
+// U chunks per batch: U loads per thread are in flight while the previous
+// batch's updates run.
+template <bool SBF16, bool CBF16, int EPT, int TPB, int U>
 __global__ __launch_bounds__(TPB) void state_passing_kernel(
     const void* S, void* carried_v, const float* __restrict__ dA_cumsum,
     const float* __restrict__ init, float* __restrict__ fin, int H, int nc, int Q, int64_t npv,
@@ -131,39 +132,39 @@ __global__ __launch_bounds__(TPB) void state_passing_kernel(
     for (int k = 0; k < EPT; ++k) run[k] = fmaf(d, run[k], sv[k]);  // explicit fused multiply-add: the
   };                                                                    // fused state path repeats these bits
 
-  // Software pipeline: the loads of chunks c+8..c+15 are issued before the
-  // stores of chunks c..c+7 (distinct addresses, so this also holds in place).
-  Raw s[kSpUnroll], sn[kSpUnroll];
-  float dec[kSpUnroll], decn[kSpUnroll];
-  const int nfull = nc / kSpUnroll;  // full batches
+  // Software pipeline: the loads of chunks c+U..c+2U-1 are issued before the
+  // stores of chunks c..c+U-1 (distinct addresses, so this also holds in place).
+  Raw s[U], sn[U];
+  float dec[U], decn[U];
+  const int nfull = nc / U;  // full batches
   if (nfull > 0) {
 #pragma unroll
-    for (int u = 0; u < kSpUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       s[u] = In::load(S, e0 + (int64_t)u * cstride);
       dec[u] = expf(glast[(int64_t)u * Q]);
     }
   }
   for (int bt = 0; bt < nfull; ++bt) {
-    const int c = bt * kSpUnroll;
+    const int c = bt * U;
     if (bt + 1 < nfull) {
 #pragma unroll
-      for (int u = 0; u < kSpUnroll; ++u) {
-        sn[u] = In::load(S, e0 + (int64_t)(c + kSpUnroll + u) * cstride);
-        decn[u] = expf(glast[(int64_t)(c + kSpUnroll + u) * Q]);
+      for (int u = 0; u < U; ++u) {
+        sn[u] = In::load(S, e0 + (int64_t)(c + U + u) * cstride);
+        decn[u] = expf(glast[(int64_t)(c + U + u) * Q]);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kSpUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       Out::store(carried_v, e0 + (int64_t)(c + u) * cstride, run);
       step(s[u], dec[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kSpUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       s[u] = sn[u];
       dec[u] = decn[u];
     }
   }
-  for (int c = nfull * kSpUnroll; c < nc; ++c) {
+  for (int c = nfull * U; c < nc; ++c) {
     const Raw sv = In::load(S, e0 + (int64_t)c * cstride);
     const float d1 = expf(glast[(int64_t)c * Q]);
     Out::store(carried_v, e0 + (int64_t)c * cstride, run);
@@ -182,9 +183,15 @@ static hipError_t launch_sp(const Dims& d, const void* chunk_states, void* carri
   const int64_t npv = d.N * d.P / EPT;
   const int64_t total = d.B * d.H * npv;
   const unsigned blocks = (unsigned)((total + TPB - 1) / TPB);
-  hipLaunchKernelGGL((state_passing_kernel<SBF16, CBF16, EPT, TPB>), dim3(blocks), dim3(TPB), 0, stream,
-                     chunk_states, carried, dA_cumsum, initial_states, final_states, (int)d.H, (int)d.nc, (int)d.Q,
-                     npv, total);
+  // With fewer than 4 waves per compute unit (long sequences of few heads)
+  // the bytes in flight set the rate: batches of 16 chunks instead of 8.
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const bool deep = (total + 63) / 64 < 4 * (int64_t)cus && d.nc >= 32;
+  auto kern = deep ? state_passing_kernel<SBF16, CBF16, EPT, TPB, 16> : state_passing_kernel<SBF16, CBF16, EPT, TPB, 8>;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(TPB), 0, stream, chunk_states, carried, dA_cumsum, initial_states,
+                     final_states, (int)d.H, (int)d.nc, (int)d.Q, npv, total);
   return hipGetLastError();
 }
 

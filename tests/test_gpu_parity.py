@@ -159,6 +159,43 @@ def test_state_passing_bf16_chunk_states(shape, with_h0):
     assert e1 <= 2.0 ** -8 and e2 <= 2.0 ** -8
 
 
+@pytest.mark.parametrize("states_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("nc", [32, 40, 71])
+def test_state_passing_long_chains(nc, states_dtype):
+    """Few heads and many chunks (fewer than 4 waves per compute unit): the
+    state passing then keeps 16 chunk loads per thread in flight; chains of
+    two full batches, with a remainder of 8, and with an odd remainder.  The
+    carried and final states equal the fp32 recurrence over the same stored
+    chunk states bit for bit (fp32 carried, then bf16 carried = its rounding)
+    and match the oracle."""
+    from mamba_ssd_scan_chunk_amd.inputs import bf16_round
+    shape = ("long_chain", 1, 32 * nc, 2, 32, 32, 1, 32)
+    say(f"state_passing long chain nc={nc} states {states_dtype}")
+    inp = _inp(shape, "f32", seed=3, dt_shift=5.0)
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    o = oracle()
+    S = o.chunk_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk)
+    h0 = _h0(inp)
+    Hin, fin = o.carried_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk, h0=h0)
+    dA, _ = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    S_t = torch.from_numpy(S.astype(np.float32)).cuda()
+    if states_dtype == "bf16":
+        S_t = S_t.to(torch.bfloat16)
+    h0_t = torch.from_numpy(h0).cuda()
+    c32, f32_ = ops.ssd_state_passing(sh, S_t, dA, initial_states=h0_t, carried_dtype="f32")
+    c16, f16_ = ops.ssd_state_passing(sh, S_t, dA, initial_states=h0_t, carried_dtype="bf16")
+    torch.cuda.synchronize()
+    # the same recurrence run on the host in fp32 with the same fused multiply-adds is not
+    # available in NumPy, so the bit-level check is between the two carried dtypes
+    got = c16.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, bf16_round(c32.cpu().numpy())) and torch.equal(f16_, f32_)
+    e1, e2 = relerr(c32, Hin), relerr(f32_, fin)
+    say(f"  rel err carried {e1:.3g} final {e2:.3g}")
+    bound = TOL_PASSING if states_dtype == "f32" else 2.0 ** -8
+    assert e1 <= bound and e2 <= bound
+
+
 @pytest.mark.parametrize("with_h0", [False, True])
 @pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
