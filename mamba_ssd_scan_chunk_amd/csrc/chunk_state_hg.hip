@@ -22,8 +22,10 @@
 // D[p][n] = sum_j x[j][p] B[j][n] (A operand: x, B operand: B), so that each
 // lane holds four consecutive p of one state row n and writes them as one
 // 16-byte store.
-// 8 waves (two per SIMD); wave w owns the state rows n in tile w (N = 128)
-// or tiles 2w, 2w+1 (N = 256) for all 4 column tiles of the slice.
+// 8 waves (two per SIMD) in a 4 x 2 grid: wave w owns the state rows of
+// tiles NTW (w % 4) .. +NTW-1 (NTW = N / 64) and the column tiles 2 (w / 4),
+// +1 of the slice; the B fragments of its rows stay in registers for all the
+// block's heads, so per head a wave reads only its half of the x tile.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -40,7 +42,10 @@ struct ShgCfg {
   // bytes) fall in distinct banks.
   static constexpr int BP = N + 16;
   static constexpr int XP = PT + 16;
-  static constexpr int NTW = N / 16 / 8;  // state-row tiles per wave (8 waves)
+  // wave grid: 4 waves along n (NTW 16-row tiles each) x 2 along p (two
+  // 16-column tiles each)
+  static constexpr int NTW = N / 16 / 4;
+  static constexpr int KS = Q / 32;  // 32-token contraction steps
   static constexpr size_t lds_b = (size_t)Q * BP * 2;
   static constexpr size_t lds_x = (size_t)Q * XP * 2;
   static constexpr size_t lds_total = lds_b + lds_x;
@@ -61,7 +66,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   using Cfg = ShgCfg<Q, N>;
   using Op = OpBF16;
   using Frag = Op::Frag;
-  constexpr int T = Cfg::T, PT = Cfg::PT, BP = Cfg::BP, XP = Cfg::XP, NTW = Cfg::NTW;
+  constexpr int T = Cfg::T, PT = Cfg::PT, BP = Cfg::BP, XP = Cfg::XP, NTW = Cfg::NTW, KS = Cfg::KS;
   constexpr int NXB = Q * (PT / 8);  // 16-byte pieces of a head's x slice
   constexpr int XPT = NXB / T;
   static_assert(NXB % T == 0 && PT == 64, "x pieces must divide evenly over the block");
@@ -212,6 +217,16 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   }
 
   __syncthreads();  // Bn complete
+  // The B rows are the same for every head of the block: each wave keeps the
+  // fragments of its state rows in registers for the whole head loop, so per
+  // head only the x tile is read from LDS (a quarter of it per wave pair of
+  // columns instead of all of it per wave).
+  const int wn = wave & 3, wp = wave >> 2;
+  Frag bfr[NTW][KS];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i)
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) bfr[i][kk] = lds_frag_tr(Bn + 32 * kk * BP + 16 * (NTW * wn + i), BP, tid & 63);
   commit();
   __syncthreads();
 
@@ -228,35 +243,34 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
       int ln = tid & 63;
       asm volatile("" : "+v"(ln));
       const int l16 = ln & 15, lg = ln >> 4;
-      f32x4_t acc[NTW][4];
+      f32x4_t acc[NTW][2];
 #pragma unroll
       for (int i = 0; i < NTW; ++i)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[i][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-      for (int kk = 0; kk < Q / 32; ++kk) {
-        Frag xf[4];
+        for (int ct = 0; ct < 2; ++ct) acc[i][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) xf[ct] = lds_frag_tr(Xn + 32 * kk * XP + 16 * ct, XP, ln);
+      for (int kk = 0; kk < KS; ++kk) {
+        Frag xf[2];
 #pragma unroll
-        for (int i = 0; i < NTW; ++i) {
-          const Frag bf = lds_frag_tr(Bn + 32 * kk * BP + 16 * (NTW * wave + i), BP, ln);
+        for (int ct = 0; ct < 2; ++ct) xf[ct] = lds_frag_tr(Xn + 32 * kk * XP + 16 * (2 * wp + ct), XP, ln);
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) acc[i][ct] = Op::mma(xf[ct], bf, acc[i][ct]);
-        }
+        for (int i = 0; i < NTW; ++i)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) acc[i][ct] = Op::mma(xf[ct], bfr[i][kk], acc[i][ct]);
       }
-      // lane holds S[n = 16*(NTW*wave + i) + l16][p = p0 + 16ct + 4lg .. +3]
+      // lane holds S[n = 16*(NTW*wn + i) + l16][p = p0 + 16(2wp + ct) + 4lg .. +3]
       const int64_t so = (((int64_t)b * nc + c) * H + h) * (int64_t)(N * P) + p0;
 #pragma unroll
       for (int i = 0; i < NTW; ++i) {
-        const int n = 16 * (NTW * wave + i) + l16;
+        const int n = 16 * (NTW * wn + i) + l16;
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
+        for (int ct = 0; ct < 2; ++ct) {
+          const int pc = 16 * (2 * wp + ct) + 4 * lg;
           if constexpr (SBF16)
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(states) + so + n * P + 16 * ct + 4 * lg) =
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(states) + so + n * P + pc) =
                 make_uint2(pack_bf16x2(acc[i][ct][0], acc[i][ct][1]), pack_bf16x2(acc[i][ct][2], acc[i][ct][3]));
           else
-            *reinterpret_cast<float4*>(static_cast<float*>(states) + so + n * P + 16 * ct + 4 * lg) =
+            *reinterpret_cast<float4*>(static_cast<float*>(states) + so + n * P + pc) =
                 make_float4(acc[i][ct][0], acc[i][ct][1], acc[i][ct][2], acc[i][ct][3]);
         }
       }
