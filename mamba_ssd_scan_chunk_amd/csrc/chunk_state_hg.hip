@@ -70,6 +70,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   constexpr int NXB = Q * (PT / 8);  // 16-byte pieces of a head's x slice
   constexpr int XPT = NXB / T;
   static_assert(NXB % T == 0 && PT == 64, "x pieces must divide evenly over the block");
+  static_assert(BP >= XP, "the second x buffer lives in the Bn area");
 
   extern __shared__ __align__(16) unsigned char shg_smem[];
   uint16_t* Bn = reinterpret_cast<uint16_t*>(shg_smem);  // [Q][BP]
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
       glast = gsrc[Q - 1];
     }
   };
-  auto commit = [&]() __attribute__((always_inline)) {
+  auto commit = [&](uint16_t* dst) __attribute__((always_inline)) {
     if constexpr (FUSE) glast = Gsa[hcur * Q + Q - 1];
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
       o.y = pack_bf16x2(bf16_bits_to_f32(q.y & 0xffffu) * w, bf16_bits_to_f32(q.y >> 16) * w);
       o.z = pack_bf16x2(bf16_bits_to_f32(q.z & 0xffffu) * w, bf16_bits_to_f32(q.z >> 16) * w);
       o.w = pack_bf16x2(bf16_bits_to_f32(q.w & 0xffffu) * w, bf16_bits_to_f32(q.w >> 16) * w);
-      *reinterpret_cast<uint4*>(Xn + row * XP + 8 * cb) = o;
+      *reinterpret_cast<uint4*>(dst + row * XP + 8 * cb) = o;
     }
   };
 
@@ -227,11 +228,16 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   for (int i = 0; i < NTW; ++i)
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) bfr[i][kk] = lds_frag_tr(Bn + 32 * kk * BP + 16 * (NTW * wn + i), BP, tid & 63);
-  commit();
-  __syncthreads();
+  commit(Xn);
+  __syncthreads();  // every wave holds its B fragments: the Bn area is free from here on
 
+  // x tiles double-buffered: head hh computes from one buffer while head
+  // hh + 1 is committed to the other (the first lies in the Bn area), so a
+  // head needs one barrier
   for (int hh = 0; hh < HG; ++hh) {
     const int h = hbase + hh;
+    uint16_t* const xcur = (hh & 1) ? Bn : Xn;
+    uint16_t* const xnext = (hh & 1) ? Xn : Bn;
     // The prefetch and the commit run on every iteration (the last one loads
     // its own head again, unused): with no conditional around them the
     // compiler's memory-counter waits stay exact, so the loads of the next
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
       for (int kk = 0; kk < KS; ++kk) {
         Frag xf[2];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) xf[ct] = lds_frag_tr(Xn + 32 * kk * XP + 16 * (2 * wp + ct), XP, ln);
+        for (int ct = 0; ct < 2; ++ct) xf[ct] = lds_frag_tr(xcur + 32 * kk * XP + 16 * (2 * wp + ct), XP, ln);
 #pragma unroll
         for (int i = 0; i < NTW; ++i)
 #pragma unroll
@@ -275,8 +281,9 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
         }
       }
     }
-    __syncthreads();  // all reads of this head's Xn are done
-    commit();
+    // the other buffer was last read by the previous head, which every wave
+    // finished before the previous barrier
+    commit(xnext);
     __syncthreads();
   }
 }
