@@ -192,8 +192,11 @@ ssd_status ssd_decode_step(const ssd_shape* shape, const void* x, const float* d
 
 /*
  * Bytes of device workspace ssd_forward needs for `shape`: dA_cumsum and
- * dt_bhl (fp32 [B,H,nc,Q] each), the chunk states (fp32 [B,nc,H,N,P]) and a
- * bf16 copy of the carried states ([B,nc,H,N,P]), each 256-byte aligned.
+ * dt_bhl (fp32 [B,H,nc,Q] each), a chunk-state area sized for fp32
+ * [B,nc,H,N,P] (the bf16-operand path uses half of it, for bf16 chunk states
+ * and then the bf16 carried states written over them) and a bf16
+ * carried-state buffer ([B,nc,H,N,P], used by the fused state path), each
+ * 256-byte aligned.
  * Returns 0 for an invalid or NULL shape.  Pure host computation.
  */
 size_t ssd_workspace_bytes(const ssd_shape* shape);
