@@ -282,7 +282,8 @@ def main():
     # state path, where supported, is timed too (reported under "other_path")
     fused_ok = args.mma == "bf16" and N % 64 == 0 and P % 64 == 0 and w.in_dtype == "bf16"
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    fused = fused_ok and B * H * (N // 64) * (P // 64) >= 2 * cus
+    rows = 128 if (N % 128 == 0 and Q <= 128) else 64  # state rows per block of the fused kernel
+    fused = fused_ok and B * H * (N // rows) * (P // 64) >= 2 * cus
     fused_call = lambda: ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA, carried=carried_fused,
                                                      final_states=fin, mma=args.mma)
     calls = {"chunk_cumsum": lambda: ops.ssd_chunk_cumsum(sh, t["dt"], t["A"], dA_cumsum=dA, dt_bhl=dtb)}

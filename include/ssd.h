@@ -210,8 +210,9 @@ size_t ssd_workspace_bytes(const ssd_shape* shape);
  * and the final states stay fp32.  With SSD_MMA_F32 everything is fp32 and
  * the state passing runs in place on the chunk states.
  * Where ssd_chunk_state_passing supports the shape and launches at least two
- * blocks per compute unit of the current device (B*H*(N/64)*(P/64) >= 2 x
- * units), the two middle steps are that fused call instead (chunk states
+ * blocks per compute unit of the current device (B*H*(N/R)*(P/64) >= 2 x
+ * units, with R = 128 state rows per block when N % 128 == 0 and Q <= 128,
+ * else R = 64), the two middle steps are that fused call instead (chunk states
  * never stored, so no bf16 rounding of them).  Results are bit-identical to
  * the separate calls of the path taken, with those state and carried dtypes.
  * initial_states [B,H,N,P] may be NULL (zeros); final_states [B,H,N,P] may be

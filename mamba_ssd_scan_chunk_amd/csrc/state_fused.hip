@@ -14,10 +14,13 @@
 //         H_{c+1} = exp(G_{Q-1}) H_c + S_c
 //     final[b,h] = H_nc
 //
-// Block = (b, h, 64 state rows n, 64 columns p), 8 waves.  Wave w owns the
-// rows 16 (w % 4) .. +15 of the block's n range and the columns 32 (w / 4)
-// .. +31; the running state of those 16 x 32 elements lives in registers in
-// the MFMA accumulator layout (lane: row l16, columns 16ct + 4lg .. +3).  Per
+// Block = (b, h, NB state rows n, 64 columns p), 8 waves, NB = 128 where N
+// allows it and the chunk has at most 128 tokens (each chunk's x rows are
+// then staged by half as many blocks), else 64.  Wave w owns the RT = NB / 64
+// row tiles 16 RT (w % 4) .. +16 RT - 1 of the block's n range and the
+// columns 32 (w / 4) .. +31; the running state of those elements lives in
+// registers in the MFMA accumulator layout (lane: row l16, columns
+// 16ct + 4lg .. +3).  Per
 // chunk the x rows (scaled by w_j = exp(G_{Q-1} - G_j) dt_j, rounded to bf16)
 // and the raw B rows are staged in LDS in their natural token-major layouts,
 // and the MFMA fragments (token = contraction index) come from the transposing
@@ -34,13 +37,14 @@
 
 namespace ssd {
 
-template <int Q, int WAVES>
+template <int Q, int WAVES, int NB_ = 64>
 struct SfCfg {
   static constexpr int T = 64 * WAVES;
-  static constexpr int NB = 64, PT = 64;  // state rows and columns of a block
+  static constexpr int NB = NB_, PT = 64;  // state rows (64 or 128) and columns of a block
+  static constexpr int NBP = NB / 64;      // 16-byte B pieces per row and loader thread
   // wave grid: WN waves along n (RT 16-row tiles each) x 2 along p (two
   // 16-column tiles each)
-  static constexpr int WN = WAVES / 2, RT = 4 / WN;
+  static constexpr int WN = WAVES / 2, RT = NB / 16 / WN;
   // row pitches (elements) of Xn and Bn: odd multiples of 8 dwords modulo 64,
   // so the transposing reads (8 consecutive rows x 32 bytes per half wave)
   // fall in distinct banks
@@ -51,16 +55,16 @@ struct SfCfg {
   static constexpr size_t lds_total = (size_t)Q * XP * 2 + (size_t)Q * BP * 2;
 };
 
-template <int Q, int WAVES, bool CBF16>
+template <int Q, int WAVES, bool CBF16, int NB_>
 __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void state_fused_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bhl,
     const float* __restrict__ dA_cumsum, const float* __restrict__ init, void* __restrict__ carried,
     float* __restrict__ fin, int L, int H, int P, int N, int G, int nc, int nnb, int npt, int remap) {
-  using Cfg = SfCfg<Q, WAVES>;
+  using Cfg = SfCfg<Q, WAVES, NB_>;
   using Op = OpBF16;
   using Frag = Op::Frag;
   constexpr int XP = Cfg::XP, BP = Cfg::BP, RPT = Cfg::RPT, LT = Cfg::LT, NB = Cfg::NB, PT = Cfg::PT;
-  constexpr int WN = Cfg::WN, RT = Cfg::RT;
+  constexpr int WN = Cfg::WN, RT = Cfg::RT, NBP = Cfg::NBP;
   constexpr int KU = WAVES == 8 ? 1 : 2;  // unroll of the contraction loop (register budget)
   static_assert(Q % 32 == 0 && RPT >= 1, "chunk must be a multiple of 32");
 
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void state_fused_kernel(
   };
   XSet sa, sb;
   GSet g1;  // used when !GD2
-  uint4 bv[RPT];
+  uint4 bv[RPT][NBP];
   auto load_g = [&](GSet& gs, int c) __attribute__((always_inline)) {
     const float* gsrc = dA_cumsum + (bh * nc + c) * Q;
     const float* dsrc = dt_bhl + (bh * nc + c) * Q;
@@ -157,7 +161,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void state_fused_kernel(
       const int rmax = min(Q, L - c * Q) - 1;
       const uint16_t* bs = Bm + (tok0 * G + g) * (int64_t)N + n0 + 8 * cbp;
 #pragma unroll
-      for (int u = 0; u < RPT; ++u) bv[u] = *reinterpret_cast<const uint4*>(bs + min(rbase + u, rmax) * GN);
+      for (int u = 0; u < RPT; ++u)
+#pragma unroll
+        for (int q = 0; q < NBP; ++q)
+          bv[u][q] = *reinterpret_cast<const uint4*>(bs + 64 * q + min(rbase + u, rmax) * GN);
     }
     if constexpr (!GD2) load_g(g1, c);
   };
@@ -177,8 +184,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void state_fused_kernel(
       o.z = pack_bf16x2(bf16_bits_to_f32(q.z & 0xffffu) * w, bf16_bits_to_f32(q.z >> 16) * w);
       o.w = pack_bf16x2(bf16_bits_to_f32(q.w & 0xffffu) * w, bf16_bits_to_f32(q.w >> 16) * w);
       *reinterpret_cast<uint4*>(Xn + row * XP + 8 * cbp) = o;
-      const uint4 bq = bv[u];
-      *reinterpret_cast<uint4*>(Bn + row * BP + 8 * cbp) = make_uint4(bq.x, bq.y, bq.z, bq.w);
+#pragma unroll
+      for (int q = 0; q < NBP; ++q) {
+        const uint4 bq = bv[u][q];
+        *reinterpret_cast<uint4*>(Bn + row * BP + 64 * q + 8 * cbp) = make_uint4(bq.x, bq.y, bq.z, bq.w);
+      }
     }
   };
   // carried[b, c, h] = H_c (the running state), rounded to bf16 or fp32.  In
@@ -278,14 +288,19 @@ bool state_fused_supported(const Dims& d, bool in_bf16, bool f32_mma) {
          (d.Q == 32 || d.Q == 64 || d.Q == 128 || d.Q == 256);
 }
 
-int64_t state_fused_blocks(const Dims& d) { return d.B * d.H * (d.N / 64) * (d.P / 64); }
+// State rows per block: 128 where N allows it and the chunk is at most 128
+// tokens (each chunk's x rows are then staged by half as many blocks; at 256
+// tokens the larger tiles would not fit the register budget), else 64.
+int state_fused_rows(const Dims& d) { return (d.N % 128 == 0 && d.Q <= 128) ? 128 : 64; }
 
-template <int Q, bool CBF16, int WAVES = 8>
+int64_t state_fused_blocks(const Dims& d) { return d.B * d.H * (d.N / state_fused_rows(d)) * (d.P / 64); }
+
+template <int Q, bool CBF16, int NB, int WAVES = 8>
 static hipError_t launch_sf_inst(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
                                  const float* dA_cumsum, const float* init, void* carried, float* fin,
                                  hipStream_t stream) {
-  using Cfg = SfCfg<Q, WAVES>;
-  auto kern = state_fused_kernel<Q, WAVES, CBF16>;
+  using Cfg = SfCfg<Q, WAVES, NB>;
+  auto kern = state_fused_kernel<Q, WAVES, CBF16, NB>;
   const size_t lds = Cfg::lds_total;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -304,11 +319,19 @@ template <bool CBF16>
 static hipError_t launch_sf_q(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
                               const float* dA_cumsum, const float* init, void* carried, float* fin,
                               hipStream_t stream) {
+  if (state_fused_rows(d) == 128) {
+    switch (d.Q) {
+      case 32: return launch_sf_inst<32, CBF16, 128>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
+      case 64: return launch_sf_inst<64, CBF16, 128>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
+      case 128: return launch_sf_inst<128, CBF16, 128>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (d.Q) {
-    case 32: return launch_sf_inst<32, CBF16>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
-    case 64: return launch_sf_inst<64, CBF16>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
-    case 128: return launch_sf_inst<128, CBF16>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
-    case 256: return launch_sf_inst<256, CBF16>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
+    case 32: return launch_sf_inst<32, CBF16, 64>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
+    case 64: return launch_sf_inst<64, CBF16, 64>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
+    case 128: return launch_sf_inst<128, CBF16, 64>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
+    case 256: return launch_sf_inst<256, CBF16, 64>(d, x, Bm, dt_bhl, dA_cumsum, init, carried, fin, stream);
     default: return hipErrorInvalidValue;
   }
 }

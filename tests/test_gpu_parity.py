@@ -490,12 +490,13 @@ def test_chunk_state_passing(shape, with_h0, carried_dtype):
 
 def test_forward_state_path_choice():
     """ssd_forward takes the fused state path when it has at least two blocks
-    per compute unit (4 x 64 heads x 2 state blocks = 512 here), else the
-    two-kernel path; either way y and the final states match the oracle, and
-    bit for bit the composition of the ABI calls of the path it takes (at
-    chunk 64 the two state paths round differently, so the check tells them
-    apart)."""
-    shape = ("fwd_path", 4, 256, 64, 64, 128, 8, 64)
+    per compute unit (blocks of 128 state rows where N is a multiple of 128
+    and the chunk at most 128 tokens, else 64: 8 x 64 heads x 1 row block =
+    512 here), else the two-kernel path; either way y and the final states
+    match the oracle, and bit for bit the composition of the ABI calls of the
+    path it takes (at chunk 64 the two state paths round differently, so the
+    check tells them apart)."""
+    shape = ("fwd_path", 8, 256, 64, 64, 128, 8, 64)
     say(f"forward state path choice {shape}")
     name, B, L, H, P, N, G, Q = shape
     inp = _inp(shape, "bf16", seed=15, dt_shift=2.0)
@@ -510,7 +511,8 @@ def test_forward_state_path_choice():
     h0_t = torch.from_numpy(h0).cuda()
     dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    fused = B * H * (N // 64) * (P // 64) >= 2 * cus
+    rows = 128 if (N % 128 == 0 and Q <= 128) else 64
+    fused = B * H * (N // rows) * (P // 64) >= 2 * cus
     if fused:
         car, fin_s = ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA, initial_states=h0_t,
                                                  carried_dtype="bf16")
