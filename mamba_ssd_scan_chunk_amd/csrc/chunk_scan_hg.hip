@@ -565,25 +565,13 @@ __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
 }
 
 // ------------------------------------------------------------------ host side
-static int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
-  return n;
-}
 
 // Heads per block: the largest divisor HG of the group's head count such that
 // the grid still gives every CU at least one block.
 static int pick_heads_per_block(const Dims& d, int npt) {
   const int64_t hpg = d.H / d.G;
   const int64_t base = d.B * d.nc * d.G * npt;
-  const int cus = cu_count();
+  const int cus = device_cu_count();
   int best = 1;
   for (int64_t k = 1; k <= hpg; ++k) {
     if (hpg % k) continue;

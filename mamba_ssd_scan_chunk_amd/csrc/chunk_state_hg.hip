@@ -289,18 +289,6 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
 }
 
 // ------------------------------------------------------------------ host side
-static int shg_cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
-  return n;
-}
 
 // (chunk, N) pairs with an instance: N >= 128 (a 16-row state tile per wave
 // and per 128 rows of N) and the B and x tiles within the LDS
@@ -329,7 +317,7 @@ static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, 
   for (int64_t k = 1; k <= hpg; ++k) {
     if (hpg % k || hpg / k > cap) continue;
     HG = (int)(hpg / k);
-    if (base * k >= shg_cu_count()) break;
+    if (base * k >= device_cu_count()) break;
   }
   const size_t lds = Cfg::lds_total + (FUSE ? (size_t)8 * Q * HG : 0);
   if (lds > 65536) {

@@ -4,7 +4,32 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "ssd_launch.hpp"
+
+namespace ssd {
+
+// Compute units of the current device, queried once per device and kept in
+// an atomic per device (the calls may come from several host threads); 256
+// (an MI355X) when the query fails.
+int device_cu_count() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const bool cached = dev >= 0 && dev < kMaxDev;
+  if (cached) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  if (cached) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+}  // namespace ssd
 
 namespace {
 
@@ -222,10 +247,7 @@ size_t ssd_workspace_bytes_varlen(const ssd_shape* shape) {
 // (measured: 2048 blocks on 256 units 24% faster per forward, 320 blocks 8%
 // slower).
 static bool prefer_fused_state(const Dims& d) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return false;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return false;
-  return ssd::state_fused_blocks(d) >= 2 * (int64_t)cus;
+  return ssd::state_fused_blocks(d) >= 2 * (int64_t)ssd::device_cu_count();
 }
 
 ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* Bm,

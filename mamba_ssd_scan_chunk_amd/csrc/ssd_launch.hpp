@@ -18,6 +18,10 @@ struct Dims {
 size_t chunk_state_lds_bytes(const Dims& d, bool f32_mma);
 size_t chunk_scan_lds_bytes(const Dims& d, bool f32_mma);
 
+// Compute units of the current device (cached per device, thread-safe; 256
+// when the query fails).  Used to size grids and pick kernel variants.
+int device_cu_count();
+
 hipError_t launch_chunk_cumsum(const Dims& d, const float* dt, const float* A, float* dA_cumsum,
                                float* dt_bhl, hipStream_t stream);
 // Packed sequences: seq_start [B,nc,Q] int32 from seq_idx [B,L] (see chunk_cumsum.hip).

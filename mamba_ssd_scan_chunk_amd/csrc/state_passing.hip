@@ -185,9 +185,7 @@ static hipError_t launch_sp(const Dims& d, const void* chunk_states, void* carri
   const unsigned blocks = (unsigned)((total + TPB - 1) / TPB);
   // With fewer than 4 waves per compute unit (long sequences of few heads)
   // the bytes in flight set the rate: batches of 16 chunks instead of 8.
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int cus = device_cu_count();
   const bool deep = (total + 63) / 64 < 4 * (int64_t)cus && d.nc >= 32;
   auto kern = deep ? state_passing_kernel<SBF16, CBF16, EPT, TPB, 16> : state_passing_kernel<SBF16, CBF16, EPT, TPB, 8>;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(TPB), 0, stream, chunk_states, carried, dA_cumsum, initial_states,
