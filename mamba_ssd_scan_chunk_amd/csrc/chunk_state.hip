@@ -10,7 +10,9 @@
 // tile stays the raw input shared by every head of a group; in exact
 // arithmetic the two placements are the same product.
 //
-// Work split: one 256-thread block per (b, c, h, 16/32/64-column slice of P).
+// Work split: one 256-thread block per (b, c, HPB heads of one group,
+// 16/32/64-column slice of P).  The B rows of a step are staged once for the
+// block's HPB heads (B does not depend on the head).
 // The contraction runs over the chunk's tokens in steps of 32.  Both operands
 // arrive token-major from HBM, while an MFMA fragment needs 8 consecutive
 // contraction slots per lane, so each step stages them through LDS
@@ -21,6 +23,8 @@
 // tiles n = 16*(w + 4*i) and all column tiles of the slice.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
+
+#include <type_traits>
 
 namespace ssd {
 
@@ -36,7 +40,7 @@ struct StateCfg {
   static constexpr int KP = kStateKS + (Op::kBytes == 2 ? 8 : 4);
 };
 
-template <class Op, int RW, int CT>
+template <class Op, int RW, int CT, int HPB>
 __global__ __launch_bounds__(kCsThreadsState) void chunk_state_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, int in_bf16, const float* __restrict__ dt_bhl,
     const float* __restrict__ dA_cumsum, void* __restrict__ states, int states_bf16, int L, int H, int P, int N,
@@ -47,29 +51,32 @@ __global__ __launch_bounds__(kCsThreadsState) void chunk_state_kernel(
   constexpr int KP = StateCfg<Op>::KP;
   extern __shared__ __align__(16) unsigned char st_smem[];
   E* Bt = reinterpret_cast<E*>(st_smem);    // [N][KP]
-  E* Xt = Bt + (size_t)N * KP;               // [PT][KP]
-  float* w_s = reinterpret_cast<float*>(Xt + PT * KP);  // [Q]
+  E* Xt = Bt + (size_t)N * KP;               // [HPB][PT][KP]
+  float* w_s = reinterpret_cast<float*>(Xt + HPB * PT * KP);  // [HPB][Q]
 
   const int npt = P / PT;
-  const int h = blockIdx.x / npt, pt = blockIdx.x - (blockIdx.x / npt) * npt;
+  const int h0 = (blockIdx.x / npt) * HPB, pt = blockIdx.x - (blockIdx.x / npt) * npt;
   const int c = blockIdx.y, b = blockIdx.z;
-  const int g = h / (H / G);
+  const int g = h0 / (H / G);
   const int p0 = pt * PT;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;
   const bool bf = in_bf16 != 0;
 
-  const int64_t bhc = ((int64_t)b * H + h) * nc + c;
-  const float* Gc = dA_cumsum + bhc * Q;
-  const float* dtc = dt_bhl + bhc * Q;
-  const float glast = Gc[Q - 1];
-  for (int j = tid; j < Q; j += kCsThreadsState) w_s[j] = fast_exp(glast - Gc[j]) * dtc[j];
+  for (int idx = tid; idx < HPB * Q; idx += kCsThreadsState) {
+    const int hp = idx / Q, j = idx - (idx / Q) * Q;
+    const int64_t bhc = ((int64_t)b * H + h0 + hp) * nc + c;
+    const float* Gc = dA_cumsum + bhc * Q;
+    w_s[idx] = fast_exp(Gc[Q - 1] - Gc[j]) * dt_bhl[bhc * Q + j];
+  }
 
-  f32x4_t acc[RW][CT];
+  f32x4_t acc[HPB][RW][CT];
 #pragma unroll
-  for (int i = 0; i < RW; ++i)
+  for (int hp = 0; hp < HPB; ++hp)
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[i][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[hp][i][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int NT = N / 16;
   const int64_t tok0 = (int64_t)b * L + (int64_t)c * Q;
@@ -81,7 +88,7 @@ __global__ __launch_bounds__(kCsThreadsState) void chunk_state_kernel(
 
   for (int k0 = 0; k0 < Q; k0 += kStateKS) {
     __syncthreads();  // previous step's fragment reads are done; w_s is visible
-    for (int blk = tid; blk < nbB + nbX; blk += kCsThreadsState) {
+    for (int blk = tid; blk < nbB + HPB * nbX; blk += kCsThreadsState) {
       float v[8][8];
       if (blk < nbB) {
         const int jb = blk & 3, cb = blk >> 2;
@@ -96,12 +103,12 @@ __global__ __launch_bounds__(kCsThreadsState) void chunk_state_kernel(
           Lds<Op>::store8(Bt + (8 * cb + q) * KP + 8 * jb, col);
         }
       } else {
-        const int bx = blk - nbB;
+        const int hp = (blk - nbB) / nbX, bx = (blk - nbB) - hp * nbX;
         const int jb = bx & 3, cb = bx >> 2;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          load8_as_f32(x, ((tok0 + min(k0 + 8 * jb + r, rmax)) * H + h) * P + p0 + 8 * cb, bf, v[r]);
-          const float w = w_s[k0 + 8 * jb + r];
+          load8_as_f32(x, ((tok0 + min(k0 + 8 * jb + r, rmax)) * H + h0 + hp) * P + p0 + 8 * cb, bf, v[r]);
+          const float w = w_s[hp * Q + k0 + 8 * jb + r];
 #pragma unroll
           for (int q = 0; q < 8; ++q) v[r][q] *= w;
         }
@@ -110,42 +117,48 @@ __global__ __launch_bounds__(kCsThreadsState) void chunk_state_kernel(
           float col[8];
 #pragma unroll
           for (int r = 0; r < 8; ++r) col[r] = v[r][q];
-          Lds<Op>::store8(Xt + (8 * cb + q) * KP + 8 * jb, col);
+          Lds<Op>::store8(Xt + (hp * PT + 8 * cb + q) * KP + 8 * jb, col);
         }
       }
     }
     __syncthreads();
 
-    Frag bfr[CT];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) bfr[ct] = Lds<Op>::load8(Xt + (16 * ct + l16) * KP + 8 * lg);
+    for (int hp = 0; hp < HPB; ++hp) {
+      Frag bfr[CT];
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const int rt = wave + 4 * i;
-      if (rt < NT) {
-        const Frag afr = Lds<Op>::load8(Bt + (16 * rt + l16) * KP + 8 * lg);
+      for (int ct = 0; ct < CT; ++ct) bfr[ct] = Lds<Op>::load8(Xt + (hp * PT + 16 * ct + l16) * KP + 8 * lg);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[i][ct] = Op::mma(afr, bfr[ct], acc[i][ct]);
+      for (int i = 0; i < RW; ++i) {
+        const int rt = wave + 4 * i;
+        if (rt < NT) {
+          const Frag afr = Lds<Op>::load8(Bt + (16 * rt + l16) * KP + 8 * lg);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) acc[hp][i][ct] = Op::mma(afr, bfr[ct], acc[hp][i][ct]);
+        }
       }
     }
   }
 
   // fp32 states, or (states_bf16) rounded to bf16, nearest even
-  const int64_t so = (((int64_t)b * nc + c) * H + h) * (int64_t)N * P;
 #pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    const int rt = wave + 4 * i;
-    if (rt < NT) {
+  for (int hp = 0; hp < HPB; ++hp) {
+    const int64_t so = (((int64_t)b * nc + c) * H + h0 + hp) * (int64_t)N * P;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+    for (int i = 0; i < RW; ++i) {
+      const int rt = wave + 4 * i;
+      if (rt < NT) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t e = so + (int64_t)(16 * rt + 4 * lg + r) * P + p0 + 16 * ct + l16;
-          if (states_bf16)
-            static_cast<uint16_t*>(states)[e] = (uint16_t)f32_to_bf16_bits(acc[i][ct][r]);
-          else
-            static_cast<float*>(states)[e] = acc[i][ct][r];
-        }
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t e = so + (int64_t)(16 * rt + 4 * lg + r) * P + p0 + 16 * ct + l16;
+            if (states_bf16)
+              static_cast<uint16_t*>(states)[e] = (uint16_t)f32_to_bf16_bits(acc[hp][i][ct][r]);
+            else
+              static_cast<float*>(states)[e] = acc[hp][i][ct][r];
+          }
+      }
     }
   }
 }
@@ -157,47 +170,74 @@ static int state_rw(int64_t N) {
   return rw <= 1 ? 1 : rw <= 2 ? 2 : 4;
 }
 
-size_t chunk_state_lds_bytes(const Dims& d, bool f32_mma) {
+static size_t state_lds_bytes_hpb(const Dims& d, bool f32_mma, int hpb) {
   const int PT = 16 * state_ct(d.P);
   const size_t eb = f32_mma ? 4 : 2;
   const size_t KP = f32_mma ? StateCfg<OpF32>::KP : StateCfg<OpBF16>::KP;
-  return eb * KP * (size_t)(d.N + PT) + sizeof(float) * (size_t)d.Q;
+  return eb * KP * (size_t)(d.N + hpb * PT) + sizeof(float) * (size_t)(hpb * d.Q);
 }
 
-template <class Op, int RW, int CT>
-static hipError_t launch_state_inst(const Dims& d, const void* x, const void* Bm, bool in_bf16,
-                                    const float* dt_bhl, const float* dA_cumsum, void* states,
-                                    bool states_bf16, hipStream_t stream, size_t lds) {
-  auto kern = chunk_state_kernel<Op, RW, CT>;
+// the one-head form; the launcher takes HPB = 4 only where that also fits
+size_t chunk_state_lds_bytes(const Dims& d, bool f32_mma) { return state_lds_bytes_hpb(d, f32_mma, 1); }
+
+// Heads per block: 4 where they divide the group, the LDS holds their tiles
+// and the grid still has two blocks per compute unit, else 1.
+static int state_hpb(const Dims& d, bool f32_mma) {
+  const int64_t hpg = d.H / d.G;
+  const int PT = 16 * state_ct(d.P);
+  const int64_t blocks4 = d.B * d.nc * (d.H / 4) * (d.P / PT);
+  if (hpg % 4 == 0 && state_lds_bytes_hpb(d, f32_mma, 4) <= 160 * 1024 && blocks4 >= 2 * (int64_t)device_cu_count())
+    return 4;
+  return 1;
+}
+
+template <class Op, int RW, int CT, int HPB>
+static hipError_t launch_state_hpb(const Dims& d, const void* x, const void* Bm, bool in_bf16,
+                                   const float* dt_bhl, const float* dA_cumsum, void* states,
+                                   bool states_bf16, hipStream_t stream) {
+  auto kern = chunk_state_kernel<Op, RW, CT, HPB>;
+  const size_t lds = state_lds_bytes_hpb(d, std::is_same<Op, OpF32>::value, HPB);
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const dim3 grid((unsigned)(d.H * (d.P / (16 * CT))), (unsigned)d.nc, (unsigned)d.B);
+  const dim3 grid((unsigned)(d.H / HPB * (d.P / (16 * CT))), (unsigned)d.nc, (unsigned)d.B);
   hipLaunchKernelGGL(kern, grid, dim3(kCsThreadsState), lds, stream, x, Bm, (int)in_bf16, dt_bhl, dA_cumsum,
                      states, (int)states_bf16, (int)d.L, (int)d.H, (int)d.P, (int)d.N, (int)d.G, (int)d.Q, (int)d.nc);
   return hipGetLastError();
 }
 
+template <class Op, int RW, int CT>
+static hipError_t launch_state_inst(const Dims& d, const void* x, const void* Bm, bool in_bf16,
+                                    const float* dt_bhl, const float* dA_cumsum, void* states,
+                                    bool states_bf16, hipStream_t stream) {
+  // four heads' accumulators fit the register budget up to 8 tiles per wave
+  if constexpr (RW * CT <= 8) {
+    if (state_hpb(d, std::is_same<Op, OpF32>::value) == 4)
+      return launch_state_hpb<Op, RW, CT, 4>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream);
+  }
+  return launch_state_hpb<Op, RW, CT, 1>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream);
+}
+
 template <class Op, int RW>
 static hipError_t launch_state_ct(const Dims& d, const void* x, const void* Bm, bool in_bf16,
                                   const float* dt_bhl, const float* dA_cumsum, void* states,
-                                  bool states_bf16, hipStream_t stream, size_t lds) {
+                                  bool states_bf16, hipStream_t stream) {
   switch (state_ct(d.P)) {
-    case 4: return launch_state_inst<Op, RW, 4>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
-    case 2: return launch_state_inst<Op, RW, 2>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
-    default: return launch_state_inst<Op, RW, 1>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
+    case 4: return launch_state_inst<Op, RW, 4>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream);
+    case 2: return launch_state_inst<Op, RW, 2>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream);
+    default: return launch_state_inst<Op, RW, 1>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream);
   }
 }
 
 template <class Op>
 static hipError_t launch_state_op(const Dims& d, const void* x, const void* Bm, bool in_bf16,
                                   const float* dt_bhl, const float* dA_cumsum, void* states,
-                                  bool states_bf16, hipStream_t stream, size_t lds) {
+                                  bool states_bf16, hipStream_t stream) {
   switch (state_rw(d.N)) {
-    case 1: return launch_state_ct<Op, 1>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
-    case 2: return launch_state_ct<Op, 2>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
-    default: return launch_state_ct<Op, 4>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
+    case 1: return launch_state_ct<Op, 1>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream);
+    case 2: return launch_state_ct<Op, 2>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream);
+    default: return launch_state_ct<Op, 4>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream);
   }
 }
 
@@ -212,9 +252,8 @@ hipError_t launch_chunk_state_any(const Dims& d, const void* x, const void* Bm, 
                                   bool f32_mma, hipStream_t stream) {
   if (chunk_state_hg_supported(d, in_bf16, f32_mma))
     return launch_chunk_state_hg(d, x, Bm, dt_bhl, dA_cumsum, states, states_bf16, stream);
-  const size_t lds = chunk_state_lds_bytes(d, f32_mma);
-  if (f32_mma) return launch_state_op<OpF32>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
-  return launch_state_op<OpBF16>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream, lds);
+  if (f32_mma) return launch_state_op<OpF32>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream);
+  return launch_state_op<OpBF16>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream);
 }
 
 }  // namespace ssd
