@@ -100,6 +100,30 @@ def test_chunk_state(shape, mode):
     assert e <= tol_for(mma)
 
 
+@pytest.mark.parametrize("mode", [("f32", "f32"), ("bf16", "f32"), ("f32", "bf16")], ids=["f32-f32", "bf16-f32", "f32-bf16"])
+def test_chunk_state_head_sharing(mode):
+    """The generic chunk-state kernel serves four heads of a group per block
+    (one staged B tile for all four) once the grid still has two blocks per
+    compute unit: 8 x 32 chunks x 2 head quads = 512 blocks here, the
+    threshold on a 256-unit GPU.  Against the oracle, fp32 and bf16 states."""
+    shape = ("head_sharing", 8, 2048, 8, 64, 32, 1, 64)
+    in_dtype, mma = mode
+    say(f"chunk_state head sharing {shape} {mode}")
+    inp = _inp(shape, in_dtype, seed=31)
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    S = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma=mma)
+    S16 = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma=mma, states_dtype="bf16")
+    torch.cuda.synchronize()
+    from mamba_ssd_scan_chunk_amd.inputs import bf16_round
+    assert np.array_equal(S16.view(torch.int16).cpu().numpy().view(np.uint16), bf16_round(S.cpu().numpy()))
+    ref = oracle().chunk_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk)
+    e = relerr(S, ref)
+    say(f"  rel err {e:.3g}")
+    assert e <= tol_for(mma)
+
+
 @pytest.mark.parametrize("mode", MODES, ids=["-".join(m) for m in MODES])
 @pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
 def test_chunk_state_bf16_storage(shape, mode):
