@@ -177,19 +177,32 @@ template <bool SBF16, bool CBF16>
 static hipError_t launch_sp(const Dims& d, const void* chunk_states, void* carried, const float* dA_cumsum,
                             const float* initial_states, float* final_states, hipStream_t stream) {
   // 8 elements per thread for bf16 chunk states (N * P is a multiple of 256),
-  // in blocks of half the size, so the grid has as many blocks as with 4
-  constexpr int EPT = SBF16 ? 8 : 4;
-  constexpr int TPB = SBF16 ? kSpThreads / 2 : kSpThreads;
-  const int64_t npv = d.N * d.P / EPT;
-  const int64_t total = d.B * d.H * npv;
-  const unsigned blocks = (unsigned)((total + TPB - 1) / TPB);
+  // in blocks of half the size, so the grid has as many blocks as with 4.
   // With fewer than 4 waves per compute unit (long sequences of few heads)
-  // the bytes in flight set the rate: batches of 16 chunks instead of 8.
+  // the parallelism sets the rate: batches of 16 chunks instead of 8, and
+  // bf16 chunk states at 4 elements per thread (twice the waves, the same
+  // bytes in flight).
   const int cus = device_cu_count();
-  const bool deep = (total + 63) / 64 < 4 * (int64_t)cus && d.nc >= 32;
-  auto kern = deep ? state_passing_kernel<SBF16, CBF16, EPT, TPB, 16> : state_passing_kernel<SBF16, CBF16, EPT, TPB, 8>;
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(TPB), 0, stream, chunk_states, carried, dA_cumsum, initial_states,
-                     final_states, (int)d.H, (int)d.nc, (int)d.Q, npv, total);
+  const int64_t waves8 = (d.B * d.H * (d.N * d.P / (SBF16 ? 8 : 4)) + 63) / 64;
+  const bool deep = waves8 < 4 * (int64_t)cus && d.nc >= 32;
+  if (deep) {
+    constexpr int EPT = 4, TPB = kSpThreads;
+    const int64_t npv = d.N * d.P / EPT;
+    const int64_t total = d.B * d.H * npv;
+    const unsigned blocks = (unsigned)((total + TPB - 1) / TPB);
+    hipLaunchKernelGGL((state_passing_kernel<SBF16, CBF16, EPT, TPB, 16>), dim3(blocks), dim3(TPB), 0, stream,
+                       chunk_states, carried, dA_cumsum, initial_states, final_states, (int)d.H, (int)d.nc, (int)d.Q,
+                       npv, total);
+  } else {
+    constexpr int EPT = SBF16 ? 8 : 4;
+    constexpr int TPB = SBF16 ? kSpThreads / 2 : kSpThreads;
+    const int64_t npv = d.N * d.P / EPT;
+    const int64_t total = d.B * d.H * npv;
+    const unsigned blocks = (unsigned)((total + TPB - 1) / TPB);
+    hipLaunchKernelGGL((state_passing_kernel<SBF16, CBF16, EPT, TPB, 8>), dim3(blocks), dim3(TPB), 0, stream,
+                       chunk_states, carried, dA_cumsum, initial_states, final_states, (int)d.H, (int)d.nc, (int)d.Q,
+                       npv, total);
+  }
   return hipGetLastError();
 }
 
