@@ -40,6 +40,10 @@ def algorithmic_costs(w, in_bytes, y_bytes, carried_bytes=4, states_bytes=4):
     k["chunk_cumsum"] = dict(bytes=4 * blh + 4 * H + 2 * 4 * blh, flops=2 * blh)
     k["chunk_state"] = dict(bytes=in_bytes * blh * P + in_bytes * B * L * G * N + 2 * 4 * blh + states_bytes * st,
                             flops=2 * blh * N * P)
+    # the forward's first step: cumulative sums computed inside the chunk-state
+    # kernel (reads dt and A, writes dA_cumsum and dt_bhl instead of reading them)
+    k["chunk_cumsum_state"] = dict(bytes=in_bytes * blh * P + in_bytes * B * L * G * N + 4 * blh + 4 * H + 2 * 4 * blh
+                                   + states_bytes * st, flops=2 * blh * N * P + 2 * blh)
     k["state_passing"] = dict(bytes=states_bytes * st + 4 * B * H * nc + carried_bytes * st + 4 * B * H * N * P,
                               flops=2 * st)
     k["chunk_state_passing"] = dict(bytes=in_bytes * blh * P + in_bytes * B * L * G * N + 2 * 4 * blh
@@ -53,6 +57,7 @@ def algorithmic_costs(w, in_bytes, y_bytes, carried_bytes=4, states_bytes=4):
 
 KERNEL_SOURCES = {
     "chunk_cumsum": ["chunk_cumsum.hip"],
+    "chunk_cumsum_state": ["chunk_state_hg.hip", "chunk_state.hip", "chunk_cumsum.hip"],
     "chunk_state": ["chunk_state_hg.hip", "chunk_state.hip"],
     "state_passing": ["state_passing.hip"],
     "chunk_state_passing": ["state_fused.hip"],
@@ -86,9 +91,24 @@ def measured_traffic(workload, kernel):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, w, target_s=10.0):
-    """The fp64 oracle on a bounded sample of (b, h) pairs, all host cores."""
+def cpu_model():
+    """Host CPU model name (Linux /proc/cpuinfo), or the platform string."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(inp, w, target_s=10.0, single_core=("tiny_f32", "mamba2_130m_layer")):
+    """The fp64 oracle on a bounded sample of (b, h) pairs, all host cores;
+    also one whole pass over the small workloads on ONE core."""
     import numpy as np
+    from mamba_ssd_scan_chunk_amd.inputs import WORKLOADS, workload_inputs
     from oracle import oracle as oracle_mod
     o = oracle_mod.get()
     threads = oracle_mod.default_threads()
@@ -110,9 +130,19 @@ def cpu_baseline(inp, w, target_s=10.0):
         if k < total_pairs or t >= target_s:
             break
     tokens_per_s = passes * w.tokens * (k / total_pairs) / t
+    one = {}
+    for name in single_core:
+        wi = WORKLOADS[name]
+        si = workload_inputs(name)
+        t0 = time.perf_counter()
+        o.recurrence(si.x, si.dt, si.A, si.Bm, si.Cm, si.D, nthreads=1)
+        ts = time.perf_counter() - t0
+        one[name] = {"s": round(ts, 4), "tokens_per_s": round(wi.tokens / ts, 1),
+                     "sample": "every (batch, head) pair over the full sequence, one pass, 1 thread"}
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": used, "kind": "oracle",
             "sample": f"{k} of {total_pairs} (batch, head) pairs over the full sequence of the {w.name} "
-                      f"workload, {passes} pass(es) in {t:.2f} s; tokens/s scaled by the sampled fraction"}
+                      f"workload, {passes} pass(es) in {t:.2f} s; tokens/s scaled by the sampled fraction",
+            "cpu_model": cpu_model(), "single_core": one}
 
 
 def spin_cycles(torch, stream, us):
@@ -158,6 +188,62 @@ def time_backward(ops, torch, t, sh, steps, fwd_ms=None, modes=("bf16", "f32")):
     return out
 
 
+def time_fp32_path(ops, torch, t, sh, w, stream, steps):
+    """ssd_forward with fp32 matrix operands (fp32 y) at the workload, and its
+    chunk-state and chunk-scan kernels against the fp32 matrix-core peak."""
+    B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    nc = -(-L // Q)
+    dev = t["x"].device
+    y = torch.empty((B, L, H, P), device=dev, dtype=torch.float32)
+    fin = torch.empty((B, H, N, P), device=dev, dtype=torch.float32)
+    ws = torch.empty(ops.ssd_workspace_bytes(sh), device=dev, dtype=torch.uint8)
+    fwd = lambda: ops.ssd_forward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], y=y, final_states=fin,
+                                  workspace=ws, mma="f32")
+    dA = torch.empty((B, H, nc, Q), device=dev, dtype=torch.float32)
+    dtb = torch.empty_like(dA)
+    st = torch.empty((B, nc, H, N, P), device=dev, dtype=torch.float32)
+    calls = {
+        "chunk_cumsum_state": lambda: ops.ssd_chunk_cumsum_state(sh, t["x"], t["Bm"], t["dt"], t["A"], dA_cumsum=dA,
+                                                                 dt_bhl=dtb, states=st, mma="f32"),
+        "state_passing": lambda: ops.ssd_state_passing(sh, st, dA, carried=st, final_states=fin),
+        "chunk_scan": lambda: ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, st, t["D"], y=y, mma="f32"),
+    }
+    for _ in range(5):
+        fwd()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fwd()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    in_bytes = 2 if w.in_dtype == "bf16" else 4
+    costs = algorithmic_costs(w, in_bytes, 4, 4, 4)
+    spin = spin_cycles(torch, stream, 5000)
+    evs = {k: [] for k in calls}
+    for _ in range(max(3, steps // 5)):
+        torch.cuda._sleep(spin)
+        for k, c in calls.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            c()
+            e1.record(stream)
+            evs[k].append((e0, e1))
+    torch.cuda.synchronize()
+    out = {"ms": round(ms, 4), "tokens_per_s": round(w.tokens / (ms * 1e-3), 1), "y_dtype": "f32",
+           "steps": steps, "mfma_peak_TFLOPs": MFMA_PEAK_TFLOPS["f32"], "kernels": {}}
+    for k, pairs in evs.items():
+        us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in pairs) / len(pairs)
+        c = costs[k]
+        tf = c["flops"] / (us * 1e-6) / 1e12
+        out["kernels"][k] = {"us": round(us, 2), "TFLOPs": round(tf, 2),
+                             "mfma_peak_frac": round(tf / MFMA_PEAK_TFLOPS["f32"], 4),
+                             "GBps": round(c["bytes"] / (us * 1e-6) / 1e9, 1)}
+    del y, fin, ws, dA, dtb, st
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +254,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--mma", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp32-path", action="store_true",
+                    help="skip timing the fp32-operand forward beside the bf16 one")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="forwards timed one by one after a 1 GiB cache flush (0: skip)")
     ap.add_argument("--decode-batch", type=int, default=64,
@@ -266,7 +354,7 @@ def main():
         cold = {"steps": args.cold_steps, "ms_median": round(med, 5), "ms_min": round(cold_ms[0], 5),
                 "tokens_per_s_median": round(w.tokens / (med / 1e3), 1)}
 
-    # ---- phase 2: per-kernel durations of the same pipeline ssd_forward runs
+    # ---- phase 2: per-kernel durations of the calls ssd_forward makes
     # (bf16-operand path: chunk states stored as bf16, carried states written
     # over them as bf16; fp32 path: fp32 in place), events on the launch stream
     dA = torch.empty((B, H, nc, Q), device=dev, dtype=torch.float32)
@@ -286,23 +374,33 @@ def main():
     fused = fused_ok and B * H * (N // rows) * (P // 64) >= 2 * cus
     fused_call = lambda: ops.ssd_chunk_state_passing(sh, t["x"], t["Bm"], dtb, dA, carried=carried_fused,
                                                      final_states=fin, mma=args.mma)
-    calls = {"chunk_cumsum": lambda: ops.ssd_chunk_cumsum(sh, t["dt"], t["A"], dA_cumsum=dA, dt_bhl=dtb)}
+    cumsum_call = lambda: ops.ssd_chunk_cumsum(sh, t["dt"], t["A"], dA_cumsum=dA, dt_bhl=dtb)
+    state_call = lambda: ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, states=states, mma=args.mma)
+    passing_call = lambda: ops.ssd_state_passing(sh, states, dA, carried=carried, final_states=fin)
+    calls = {}
     if fused:
+        calls["chunk_cumsum"] = cumsum_call
         calls["chunk_state_passing"] = fused_call
     else:
-        calls["chunk_state"] = lambda: ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, states=states,
-                                                           mma=args.mma)
-        calls["state_passing"] = lambda: ops.ssd_state_passing(sh, states, dA, carried=carried, final_states=fin)
+        # the forward's first step: the cumulative sums inside the chunk-state
+        # kernel where that has a head-group instance (else the two launches)
+        calls["chunk_cumsum_state"] = lambda: ops.ssd_chunk_cumsum_state(
+            sh, t["x"], t["Bm"], t["dt"], t["A"], dA_cumsum=dA, dt_bhl=dtb, states=states, mma=args.mma)
+        calls["state_passing"] = passing_call
     scan_carried = carried_fused if fused else carried
     calls["chunk_scan"] = lambda: ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, scan_carried, t["D"],
                                                      y=y, mma=args.mma)
     forward_kernels = list(calls)
-    if fused_ok and not fused:
-        calls["chunk_state_passing"] = fused_call
-    if fused:  # the two-kernel state path, timed beside the fused one
-        calls["chunk_state"] = lambda: ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, states=states,
-                                                           mma=args.mma)
-        calls["state_passing"] = lambda: ops.ssd_state_passing(sh, states, dA, carried=carried, final_states=fin)
+    # calls outside this forward, timed beside it: the split first step and
+    # the other state path
+    if fused:
+        calls["chunk_state"] = state_call
+        calls["state_passing"] = passing_call
+    else:
+        calls["chunk_cumsum"] = cumsum_call
+        calls["chunk_state"] = state_call
+        if fused_ok:
+            calls["chunk_state_passing"] = fused_call
     order = list(calls) if args.kernel_only is None else [args.kernel_only]
     for _ in range(2):
         for k in calls:
@@ -314,9 +412,9 @@ def main():
     # small kernels.  Each pair brackets REPS back-to-back launches of one call
     # (the dispatch gap between a kernel and the event before it would
     # otherwise count against short kernels); the per-launch time is the
-    # pair's time over REPS.  The other state path (not part of the forward
-    # here) is timed one launch per pair: repeated, its input rows would stay
-    # in the last-level cache between launches, unlike in any forward.
+    # pair's time over REPS.  The calls outside the forward are timed one
+    # launch per pair: repeated, their input rows would stay in the
+    # last-level cache between launches, unlike in any forward.
     reps = max(1, args.kernel_reps)
     kreps = {k: (reps if k in forward_kernels else 1) for k in calls}
     spin = spin_cycles(torch, stream, 1000)
@@ -335,24 +433,84 @@ def main():
                 calls[k]()
     torch.cuda.synchronize()
     costs = algorithmic_costs(w, in_bytes, y_bytes, carried_bytes, states_bytes)
-    kernels = {}
-    for k, pairs in evs.items():
-        us = 1e3 * sum(a.elapsed_time(b) for a, b in pairs) / (len(pairs) * kreps[k])
+    peak_t = MFMA_PEAK_TFLOPS[args.mma]
+
+    def row(k, us):
         c = costs[k]
         gbps = c["bytes"] / (us * 1e-6) / 1e9
         tflops = c["flops"] / (us * 1e-6) / 1e12
-        peak_t = MFMA_PEAK_TFLOPS[args.mma]
-        ai = c["flops"] / c["bytes"]
-        roof_t = min(peak_t, ai * HBM_PEAK_GBPS / 1e3)
-        kernels[k] = {"us": round(us, 2), "alg_bytes": c["bytes"], "alg_flops": c["flops"],
-                      "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-                      "TFLOPs": round(tflops, 2), "mfma_peak_frac": round(tflops / peak_t, 4),
-                      "frac_of_roof": round(tflops / roof_t, 4)}
+        roof_t = min(peak_t, c["flops"] / c["bytes"] * HBM_PEAK_GBPS / 1e3)
+        return {"us": round(us, 2), "alg_bytes": c["bytes"], "alg_flops": c["flops"],
+                "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "TFLOPs": round(tflops, 2), "mfma_peak_frac": round(tflops / peak_t, 4),
+                "frac_of_roof": round(tflops / roof_t, 4)}
+
+    kernels = {k: row(k, 1e3 * sum(a.elapsed_time(b) for a, b in pairs) / (len(pairs) * kreps[k]))
+               for k, pairs in evs.items()}
     other = {k: kernels.pop(k) for k in list(kernels) if k not in forward_kernels and len(kernels) > 1}
     dom = max(kernels, key=lambda k: kernels[k]["us"])
     dk = kernels[dom]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(dk["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None}
+
+    # Cold per-kernel rows: before each timed launch 1 GiB (four times the
+    # last-level cache) is written, then a short GPU spin lets the host queue
+    # the events and the call; one launch per event pair; median and min.
+    kernels_cold = None
+    if args.cold_steps > 0 and args.kernel_only is None:
+        flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+        spin_c = spin_cycles(torch, stream, 200)
+        kernels_cold = {}
+        for k in forward_kernels:
+            ts = []
+            for _ in range(args.cold_steps):
+                flush.fill_(1.0)
+                torch.cuda._sleep(spin_c)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                calls[k]()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(1e3 * a.elapsed_time(b))
+            ts.sort()
+            r = row(k, ts[len(ts) // 2])
+            kernels_cold[k] = {"us_median": r["us"], "us_min": round(ts[0], 2), "GBps": r["GBps"],
+                               "hbm_frac": r["hbm_frac"], "mfma_peak_frac": r["mfma_peak_frac"]}
+        del flush
+
+    # The bf16-operand forward with fp32 chunk states (the chunk states stored
+    # in fp32, the carried states handed to the chunk scan as bf16).
+    fwd_f32_states = None
+    if args.mma == "bf16" and not fused and args.kernel_only is None:
+        st32 = torch.empty((B, nc, H, N, P), device=dev, dtype=torch.float32)
+        hb = torch.empty((B, nc, H, N, P), device=dev, dtype=torch.bfloat16)
+
+        def step32():
+            ops.ssd_chunk_cumsum_state(sh, t["x"], t["Bm"], t["dt"], t["A"], dA_cumsum=dA, dt_bhl=dtb, states=st32,
+                                       mma="bf16")
+            ops.ssd_state_passing(sh, st32, dA, carried=hb, final_states=fin)
+            ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, hb, t["D"], y=y, mma="bf16")
+        for _ in range(20):
+            step32()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            step32()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms32 = a.elapsed_time(b) / args.steps
+        fwd_f32_states = {"ms": round(ms32, 5), "tokens_per_s": round(w.tokens / (ms32 * 1e-3), 1),
+                          "calls": "ssd_chunk_cumsum_state (fp32 states) -> ssd_state_passing (bf16 carried) "
+                                   "-> ssd_chunk_scan"}
+        del st32, hb
+
+    # The fp32-operand path (fp32 matrix operands, fp32 chunk and carried
+    # states, fp32 y): whole forward and its two contraction kernels against
+    # the fp32 matrix-core peak.
+    fp32_path = None
+    if args.mma == "bf16" and not args.no_fp32_path and args.kernel_only is None:
+        fp32_path = time_fp32_path(ops, torch, t, sh, w, stream, max(10, args.steps // 2))
 
     # Single-token decode step at the same layer shape: DECODE_BATCH sequences,
     # one token each, fp32 state advanced in place (8 N P bytes per (b, h)).
@@ -435,7 +593,7 @@ def main():
     del src, dst
     roofline["traffic"] = measured_traffic(name, dom)
 
-    flops_total = sum(costs[k]["flops"] for k in costs)
+    flops_total = sum(costs[k]["flops"] for k in forward_kernels)
     out = {
         "metric": "Mamba-2 SSD fwd tokens/s (2.7B-layer shape) + % MFMA / HBM roofline",
         "value": round(tokens_per_s, 1),
@@ -457,8 +615,11 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "kernels": kernels,
+        "kernels_cold": kernels_cold,
         "state_path": "fused" if fused else "two-kernel",
         "other_path": other,
+        "forward_fp32_chunk_states": fwd_f32_states,
+        "fp32_mma_path": fp32_path,
         "copy_GBps": round(copy_gbps, 1),
         "cold_cache": cold,
         "decode_step": dec,

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 typedef enum {
   SSD_OK = 0,
@@ -72,8 +72,11 @@ typedef enum {
   SSD_ERR_HIP = 7           /* a kernel launch failed */
 } ssd_status;
 
-typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
-typedef enum { SSD_MMA_BF16 = 0, SSD_MMA_F32 = 1 } ssd_mma;
+/* The *_MAX_ENUM members are not valid arguments: they give the enums the
+ * range of a 32-bit int, so that an out-of-range value from a C caller is a
+ * representable value that the calls reject with SSD_ERR_DTYPE. */
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_DTYPE_MAX_ENUM = 0x7fffffff } ssd_dtype;
+typedef enum { SSD_MMA_BF16 = 0, SSD_MMA_F32 = 1, SSD_MMA_MAX_ENUM = 0x7fffffff } ssd_mma;
 
 /* B, L, H, P, N, G, Q in the notation above. */
 typedef struct {
@@ -106,6 +109,19 @@ ssd_status ssd_chunk_cumsum(const ssd_shape* shape, const float* dt, const float
 ssd_status ssd_chunk_state(const ssd_shape* shape, const void* x, const void* Bm, ssd_dtype in,
                            const float* dt_bhl, const float* dA_cumsum, void* states, ssd_dtype states_dtype,
                            ssd_mma mma, void* stream);
+
+/*
+ * ssd_chunk_cumsum followed by ssd_chunk_state, as one call (the first two
+ * steps of ssd_forward): dA_cumsum and dt_bhl [B,H,nc,Q] (both required here)
+ * and the chunk states, bit-identical to the two calls.  Where the chunk
+ * states have a head-group kernel (bf16 inputs and operands; (Q, N) in
+ * {(64,128), (128,128), (256,128), (64,256), (128,256)}; P a multiple of 64)
+ * that kernel computes the cumulative sums itself, in one launch.  Arguments
+ * and errors as for the two calls.
+ */
+ssd_status ssd_chunk_cumsum_state(const ssd_shape* shape, const void* x, const void* Bm, ssd_dtype in,
+                                  const float* dt, const float* A, float* dA_cumsum, float* dt_bhl, void* states,
+                                  ssd_dtype states_dtype, ssd_mma mma, void* stream);
 
 /*
  * Inter-chunk state advance (P1, paragraph on the three kernels: a sequential
@@ -191,18 +207,24 @@ ssd_status ssd_decode_step(const ssd_shape* shape, const void* x, const float* d
                            void* y, ssd_dtype y_dtype, void* stream);
 
 /*
- * Bytes of device workspace ssd_forward needs for `shape`: dA_cumsum and
- * dt_bhl (fp32 [B,H,nc,Q] each), a chunk-state area sized for fp32
- * [B,nc,H,N,P] (the bf16-operand path uses half of it, for bf16 chunk states
- * and then the bf16 carried states written over them) and a bf16
- * carried-state buffer ([B,nc,H,N,P], used by the fused state path), each
- * 256-byte aligned.
+ * Bytes of device workspace ssd_forward needs for `shape` on either precision
+ * path: dA_cumsum and dt_bhl (fp32 [B,H,nc,Q] each) and one state area
+ * [B,nc,H,N,P] sized for fp32, each 256-byte aligned.  The bf16-operand path
+ * uses half of the state area (bf16 chunk states with the bf16 carried states
+ * written over them, or the fused state path's bf16 carried states).
  * Returns 0 for an invalid or NULL shape.  Pure host computation.
  */
 size_t ssd_workspace_bytes(const ssd_shape* shape);
 
 /*
- * One-call forward: ssd_chunk_cumsum -> ssd_chunk_state -> ssd_state_passing
+ * One-call forward of the whole recurrence (P1, paragraph on the three
+ * kernels: the forward is the log-space cumulative sum, then the state pass
+ * over the chunks, then the fused output, each step reusing what the previous
+ * one stored; P1 compute_out paragraph for the output).  For every (b,h),
+ * with the recurrence at the top of this header:
+ *   y[b,t,h,:] = C_t^T h_t + D[h] x[b,t,h,:]   for t < L
+ *   final_states[b,h] = h_{L-1},  h_{-1} = initial_states[b,h] (zeros when NULL)
+ * computed as ssd_chunk_cumsum -> ssd_chunk_state -> ssd_state_passing
  * -> ssd_chunk_scan on one stream, no host synchronisation.  With
  * SSD_MMA_BF16 the chunk states are stored as bf16 (states_dtype = SSD_BF16)
  * and the state passing writes the carried states in place over them as bf16

@@ -42,6 +42,7 @@ _E = ctypes.c_int  # enums
 _SIGNATURES = {
     "ssd_chunk_cumsum": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
     "ssd_chunk_state": (ctypes.c_int, [_S, _P, _P, _E, _P, _P, _P, _E, _E, _P]),
+    "ssd_chunk_cumsum_state": (ctypes.c_int, [_S, _P, _P, _E, _P, _P, _P, _P, _P, _E, _E, _P]),
     "ssd_state_passing": (ctypes.c_int, [_S, _P, _E, _P, _E, _P, _P, _P, _P]),
     "ssd_chunk_scan": (ctypes.c_int, [_S, _P, _P, _P, _E, _P, _P, _P, _E, _P, _P, _E, _E, _P]),
     "ssd_chunk_state_passing": (ctypes.c_int, [_S, _P, _P, _E, _P, _P, _P, _P, _E, _P, _E, _P]),

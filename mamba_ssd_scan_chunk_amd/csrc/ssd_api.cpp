@@ -6,6 +6,7 @@
 
 #include <atomic>
 
+#include "ssd_forward.hpp"
 #include "ssd_launch.hpp"
 
 namespace ssd {
@@ -53,9 +54,17 @@ ssd_status check_shape(const ssd_shape* s, Dims* d) {
     return SSD_ERR_UNSUPPORTED;
   if (s->chunk != 32 && s->chunk != 64 && s->chunk != 128 && s->chunk != 256) return SSD_ERR_UNSUPPORTED;
   // a ragged last chunk (seqlen % chunk != 0) is allowed: nc = ceil(seqlen / chunk)
-  const int64_t nc = (s->seqlen + s->chunk - 1) / s->chunk;
+  const int64_t nc = (s->seqlen - 1) / s->chunk + 1;  // no overflow for any positive seqlen
   // keep every element offset comfortably inside 32-bit grid dimensions
   if (nc > 65535 || s->batch > 65535 || s->nheads > 65535) return SSD_ERR_UNSUPPORTED;
+  // The kernels address the rows of one chunk with 32-bit offsets from the
+  // chunk's first token (row * H*P into x and y, row * G*N into B and C), and
+  // number their blocks per (batch, chunk, head, 16-column tile of P) in 32
+  // bits: refuse shapes where either could reach 2^31.
+  const int64_t k31 = int64_t(1) << 31;
+  if (s->chunk * s->nheads * s->headdim >= k31 || s->chunk * s->ngroups * s->dstate >= k31)
+    return SSD_ERR_UNSUPPORTED;
+  if (s->batch * nc * s->nheads * (s->headdim / 16) >= k31) return SSD_ERR_UNSUPPORTED;
   d->B = s->batch; d->L = s->seqlen; d->H = s->nheads; d->P = s->headdim;
   d->N = s->dstate; d->G = s->ngroups; d->Q = s->chunk; d->nc = nc;
   return SSD_OK;
@@ -126,10 +135,12 @@ ssd_status validate_scan(const ssd_shape* shape, const void* x, const void* Bm, 
   return SSD_OK;
 }
 
+// ssd_forward_varlen's workspace: dA_cumsum, dt_bhl, fp32 carried states
+// [B,nc,H,N,P], a bf16 chunk-state area, sequence starts (int32 [B,nc,Q]),
+// dA_cumsum for the state passing and dt masked to each chunk's last sequence
+// (fp32 [B,H,nc,Q]), each 256-byte aligned.
 struct WsLayout {
   size_t dA_off, dt_off, st_off, hb_off, total;
-  // ssd_forward_varlen also: sequence starts (int32 [B,nc,Q]), dA_cumsum for
-  // the state passing and dt masked to each chunk's last sequence (fp32 [B,H,nc,Q])
   size_t ss_off, dAp_off, dtl_off, total_varlen;
 };
 
@@ -167,6 +178,22 @@ ssd_status ssd_chunk_state(const ssd_shape* shape, const void* x, const void* Bm
   SSD_TRY(validate_state(shape, x, Bm, in, dt_bhl, dA_cumsum, states, states_dtype, mma, &d));
   return from_hip(ssd::launch_chunk_state_any(d, x, Bm, in == SSD_BF16, dt_bhl, dA_cumsum, states,
                                               states_dtype == SSD_BF16, mma == SSD_MMA_F32, (hipStream_t)stream));
+}
+
+ssd_status ssd_chunk_cumsum_state(const ssd_shape* shape, const void* x, const void* Bm, ssd_dtype in,
+                                  const float* dt, const float* A, float* dA_cumsum, float* dt_bhl, void* states,
+                                  ssd_dtype states_dtype, ssd_mma mma, void* stream) {
+  Dims d;
+  SSD_TRY(validate_state(shape, x, Bm, in, dt_bhl, dA_cumsum, states, states_dtype, mma, &d));
+  if (!dt || !A) return SSD_ERR_NULL;
+  if (!aligned16(dt) || !aligned16(A)) return SSD_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)stream;
+  const bool bf = in == SSD_BF16, f32m = mma == SSD_MMA_F32, sbf = states_dtype == SSD_BF16;
+  // the head-group chunk-state kernel computes the cumulative sums itself
+  if (ssd::chunk_state_hg_supported(d, bf, f32m))
+    return from_hip(ssd::launch_chunk_state_cumsum_hg(d, x, Bm, dt, A, dA_cumsum, dt_bhl, states, sbf, s));
+  SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA_cumsum, dt_bhl, s)));
+  return from_hip(ssd::launch_chunk_state_any(d, x, Bm, bf, dt_bhl, dA_cumsum, states, sbf, f32m, s));
 }
 
 ssd_status ssd_state_passing(const ssd_shape* shape, const void* chunk_states, ssd_dtype states_dtype,
@@ -209,7 +236,7 @@ ssd_status ssd_decode_step(const ssd_shape* shape, const void* x, const float* d
   SSD_TRY(check_dtype(in));
   SSD_TRY(check_dtype(y_dtype));
   if (!ssd::decode_step_supported(s->headdim)) return SSD_ERR_UNSUPPORTED;
-  if (s->batch * s->nheads > 0x7fffffff || s->dstate > 0x7fffffff / s->headdim) return SSD_ERR_UNSUPPORTED;
+  if (s->batch > 0x7fffffff / s->nheads || s->dstate > 0x7fffffff / s->headdim) return SSD_ERR_UNSUPPORTED;
   if (!x || !dt || !A || !Bm || !Cm || !D || !state || !y) return SSD_ERR_NULL;
   if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(Bm) || !aligned16(Cm) || !aligned16(D) ||
       !aligned16(state) || !aligned16(y))
@@ -231,7 +258,8 @@ ssd_status ssd_chunk_scan(const ssd_shape* shape, const void* x, const void* Bm,
 size_t ssd_workspace_bytes(const ssd_shape* shape) {
   Dims d;
   if (check_shape(shape, &d) != SSD_OK) return 0;
-  return workspace_layout(d).total;
+  // enough for either precision path (the fp32 one needs more)
+  return ssd::forward_workspace_bytes(d, true);
 }
 
 size_t ssd_workspace_bytes_varlen(const ssd_shape* shape) {
@@ -250,42 +278,63 @@ static bool prefer_fused_state(const Dims& d) {
   return ssd::state_fused_blocks(d) >= 2 * (int64_t)ssd::device_cu_count();
 }
 
-ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* Bm,
-                       const void* Cm, const float* D, ssd_dtype in, const float* initial_states, void* y,
-                       ssd_dtype y_dtype, float* final_states, void* workspace, size_t workspace_bytes,
-                       ssd_mma mma, void* stream) {
-  Dims d;
-  SSD_TRY(check_shape(shape, &d));
+}  // extern "C"
+
+namespace ssd {
+
+ssd_status forward_validate(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* Bm,
+                            const void* Cm, const float* D, ssd_dtype in, const float* initial_states, const void* y,
+                            ssd_dtype y_dtype, const float* final_states, ssd_mma mma, Dims* d) {
+  SSD_TRY(check_shape(shape, d));
   SSD_TRY(check_dtype(in));
   SSD_TRY(check_dtype(y_dtype));
   SSD_TRY(check_mma(mma));
   if (!x || !dt || !A || !Bm || !Cm || !D || !y) return SSD_ERR_NULL;
-  if (!workspace) return SSD_ERR_WORKSPACE;
-  const WsLayout ws = workspace_layout(d);
-  if (workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(Bm) || !aligned16(Cm) || !aligned16(D) ||
-      !aligned16(y) || !aligned16(workspace) || (initial_states && !aligned16(initial_states)) ||
-      (final_states && !aligned16(final_states)))
+      !aligned16(y) || (initial_states && !aligned16(initial_states)) || (final_states && !aligned16(final_states)))
     return SSD_ERR_ALIGN;
-  if (ssd::chunk_state_lds_bytes(d, mma == SSD_MMA_F32) > kLdsLimit ||
-      ssd::chunk_scan_lds_bytes(d, mma == SSD_MMA_F32) > kLdsLimit)
+  if (chunk_state_lds_bytes(*d, mma == SSD_MMA_F32) > kLdsLimit || chunk_scan_lds_bytes(*d, mma == SSD_MMA_F32) > kLdsLimit)
     return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
 
+// The forward's workspace: dA_cumsum and dt_bhl (fp32 [B,H,nc,Q] each), then
+// one state area [B,nc,H,N,P] -- bf16 on the bf16-operand path (the chunk
+// states, then the carried states written over them; or the fused state
+// path's carried states), fp32 on the fp32 path -- each 256-byte aligned.
+struct FwdLayout {
+  size_t dA_off, dt_off, st_off, total;
+};
+
+static FwdLayout forward_layout(const Dims& d, bool f32_mma) {
+  FwdLayout w;
+  const size_t bhl = sizeof(float) * (size_t)(d.B * d.H * d.nc * d.Q);
+  const size_t st = (f32_mma ? 4 : 2) * (size_t)(d.B * d.nc * d.H) * (size_t)(d.N * d.P);
+  w.dA_off = 0;
+  w.dt_off = round_up(w.dA_off + bhl, kWsAlign);
+  w.st_off = round_up(w.dt_off + bhl, kWsAlign);
+  w.total = round_up(w.st_off + st, kWsAlign);
+  return w;
+}
+
+size_t forward_workspace_bytes(const Dims& d, bool f32_mma) { return forward_layout(d, f32_mma).total; }
+
+ssd_status forward_run(const Dims& d, const void* x, const float* dt, const float* A, const void* Bm, const void* Cm,
+                       const float* D, ssd_dtype in, const float* initial_states, void* y, ssd_dtype y_dtype,
+                       float* final_states, void* workspace, ssd_mma mma, hipStream_t s) {
+  const bool bf = in == SSD_BF16, f32m = mma == SSD_MMA_F32;
+  const FwdLayout ws = forward_layout(d, f32m);
   char* base = static_cast<char*>(workspace);
   float* dA = reinterpret_cast<float*>(base + ws.dA_off);
   float* dtb = reinterpret_cast<float*>(base + ws.dt_off);
-  float* st = reinterpret_cast<float*>(base + ws.st_off);
-  const hipStream_t s = (hipStream_t)stream;
-  const bool bf = in == SSD_BF16, f32m = mma == SSD_MMA_F32;
+  void* st = base + ws.st_off;
 
-  if (ssd::state_fused_supported(d, bf, f32m) && prefer_fused_state(d)) {
+  if (state_fused_supported(d, bf, f32m) && prefer_fused_state(d)) {
     // fused state path: the chunk states never reach memory; the carried
     // states go to the chunk scan as bf16 (its matrix-operand values)
-    uint16_t* hb = reinterpret_cast<uint16_t*>(base + ws.hb_off);
-    SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
-    SSD_TRY(from_hip(ssd::launch_state_fused(d, x, Bm, dtb, dA, initial_states, hb, true, final_states, s)));
-    SSD_TRY(from_hip(
-        ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, hb, true, D, y, y_dtype == SSD_BF16, f32m, s)));
+    SSD_TRY(from_hip(launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
+    SSD_TRY(from_hip(launch_state_fused(d, x, Bm, dtb, dA, initial_states, st, true, final_states, s)));
+    SSD_TRY(from_hip(launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, true, D, y, y_dtype == SSD_BF16, f32m, s)));
     return SSD_OK;
   }
   // bf16 matrix operands: the chunk states pass through memory as bf16 and
@@ -293,23 +342,33 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, c
   // over them, rounded to bf16 -- the operand values the chunk scan would
   // round them to; fp32 matrix operands: fp32 throughout
   const bool sbf = !f32m;
-  if (ssd::chunk_state_hg_supported(d, bf, f32m)) {
+  if (chunk_state_hg_supported(d, bf, f32m)) {
     // the head-group chunk-state kernel computes the cumulative sums itself
-    SSD_TRY(from_hip(ssd::launch_chunk_state_cumsum_hg(d, x, Bm, dt, A, dA, dtb, st, sbf, s)));
+    SSD_TRY(from_hip(launch_chunk_state_cumsum_hg(d, x, Bm, dt, A, dA, dtb, st, sbf, s)));
   } else {
-    SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
-    SSD_TRY(from_hip(ssd::launch_chunk_state_any(d, x, Bm, bf, dtb, dA, st, sbf, f32m, s)));
+    SSD_TRY(from_hip(launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
+    SSD_TRY(from_hip(launch_chunk_state_any(d, x, Bm, bf, dtb, dA, st, sbf, f32m, s)));
   }
-  if (sbf) {
-    SSD_TRY(from_hip(ssd::launch_state_passing_any(d, st, true, st, true, dA, initial_states, final_states, s)));
-    SSD_TRY(from_hip(
-        ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, true, D, y, y_dtype == SSD_BF16, f32m, s)));
-  } else {
-    SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dA, initial_states, final_states, s)));
-    SSD_TRY(from_hip(
-        ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, false, D, y, y_dtype == SSD_BF16, f32m, s)));
-  }
+  SSD_TRY(from_hip(launch_state_passing_any(d, st, sbf, st, sbf, dA, initial_states, final_states, s)));
+  SSD_TRY(from_hip(launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, sbf, D, y, y_dtype == SSD_BF16, f32m, s)));
   return SSD_OK;
+}
+
+}  // namespace ssd
+
+extern "C" {
+
+ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* Bm,
+                       const void* Cm, const float* D, ssd_dtype in, const float* initial_states, void* y,
+                       ssd_dtype y_dtype, float* final_states, void* workspace, size_t workspace_bytes,
+                       ssd_mma mma, void* stream) {
+  Dims d;
+  SSD_TRY(ssd::forward_validate(shape, x, dt, A, Bm, Cm, D, in, initial_states, y, y_dtype, final_states, mma, &d));
+  if (!workspace) return SSD_ERR_WORKSPACE;
+  if (workspace_bytes < ssd::forward_workspace_bytes(d, mma == SSD_MMA_F32)) return SSD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SSD_ERR_ALIGN;
+  return ssd::forward_run(d, x, dt, A, Bm, Cm, D, in, initial_states, y, y_dtype, final_states, workspace, mma,
+                          (hipStream_t)stream);
 }
 
 ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float* dt, const float* A,

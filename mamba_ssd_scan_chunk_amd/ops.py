@@ -97,6 +97,35 @@ def ssd_chunk_state(shape, x, Bm, dt_bhl, dA_cumsum, states=None, mma="bf16", st
     return states
 
 
+def ssd_chunk_cumsum_state(shape, x, Bm, dt, A, dA_cumsum=None, dt_bhl=None, states=None, mma="bf16",
+                           states_dtype="f32", stream=None):
+    """ssd_chunk_cumsum then ssd_chunk_state in one call (one kernel where the
+    chunk states have a head-group kernel).  Returns (dA_cumsum, dt_bhl,
+    states)."""
+    sh = _shape(shape)
+    B, L, H, P, N, G, Q, nc = _dims(sh)
+    io = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _req(x, "x", (B, L, H, P), io)
+    _req(Bm, "Bm", (B, L, G, N), (x.dtype,))
+    _req(dt, "dt", (B, L, H), f32)
+    _req(A, "A", (H,), f32)
+    if dA_cumsum is None:
+        dA_cumsum = torch.empty((B, H, nc, Q), device=x.device, dtype=torch.float32)
+    if dt_bhl is None:
+        dt_bhl = torch.empty((B, H, nc, Q), device=x.device, dtype=torch.float32)
+    _req(dA_cumsum, "dA_cumsum", (B, H, nc, Q), f32)
+    _req(dt_bhl, "dt_bhl", (B, H, nc, Q), f32)
+    if states is None:
+        sdt = _DTNAME[states_dtype] if isinstance(states_dtype, str) else states_dtype
+        states = torch.empty((B, nc, H, N, P), device=x.device, dtype=sdt)
+    _req(states, "states", (B, nc, H, N, P), io)
+    lib = load_library()
+    check(lib.ssd_chunk_cumsum_state(sh, _ptr(x), _ptr(Bm), _DT[x.dtype], _ptr(dt), _ptr(A), _ptr(dA_cumsum),
+                                     _ptr(dt_bhl), _ptr(states), _DT[states.dtype], _mma(mma), _stream(stream)))
+    return dA_cumsum, dt_bhl, states
+
+
 def ssd_state_passing(shape, chunk_states, dA_cumsum, initial_states=None, carried=None, final_states=None,
                       in_place=False, carried_dtype="f32", stream=None):
     """Carried states [B,nc,H,N,P] (state entering each chunk) in
@@ -304,11 +333,12 @@ def ssd_forward_varlen(shape, x, dt, A, Bm, Cm, D, seq_idx, initial_states=None,
 
 
 def ssd_backward(shape, x, dt, A, Bm, Cm, D, dy, initial_states=None, dfinal=None, want_dinitial=True,
-                 workspace=None, mma="f32", stream=None) -> Dict[str, Optional[torch.Tensor]]:
+                 workspace=None, mma="f32", out=None, stream=None) -> Dict[str, Optional[torch.Tensor]]:
     """Gradients of ``ssd_forward`` for dL/dy = dy and dL/dfinal = dfinal
     (None: zero).  Returns fp32 tensors dx, ddt, dA, dB, dC, dD and dinitial
-    (None unless ``want_dinitial``).  ``mma``: "f32" (fp32 matrix operands) or
-    "bf16" (bf16 operands, fp32 accumulation; faster, ~1e-2 relative)."""
+    (None unless ``want_dinitial``), written into the tensors of ``out`` (a
+    dict with those keys) where given.  ``mma``: "f32" (fp32 matrix operands)
+    or "bf16" (bf16 operands, fp32 accumulation; faster, ~1e-2 relative)."""
     sh = _shape(shape)
     B, L, H, P, N, G, Q, nc = _dims(sh)
     io = (torch.float32, torch.bfloat16)
@@ -325,10 +355,16 @@ def ssd_backward(shape, x, dt, A, Bm, Cm, D, dy, initial_states=None, dfinal=Non
     if dfinal is not None:
         _req(dfinal, "dfinal", (B, H, N, P), f32)
     dev = x.device
-    out = {"dx": torch.empty((B, L, H, P), device=dev), "ddt": torch.empty((B, L, H), device=dev),
-           "dA": torch.empty((H,), device=dev), "dB": torch.empty((B, L, G, N), device=dev),
-           "dC": torch.empty((B, L, G, N), device=dev), "dD": torch.empty((H,), device=dev),
-           "dinitial": torch.empty((B, H, N, P), device=dev) if want_dinitial else None}
+    shapes = {"dx": (B, L, H, P), "ddt": (B, L, H), "dA": (H,), "dB": (B, L, G, N), "dC": (B, L, G, N),
+              "dD": (H,), "dinitial": (B, H, N, P)}
+    given = dict(out or {})
+    out = {}
+    for k, shp in shapes.items():
+        if k == "dinitial" and not want_dinitial:
+            out[k] = None
+            continue
+        out[k] = given[k] if given.get(k) is not None else torch.empty(shp, device=dev)
+        _req(out[k], k, shp, f32)
     lib = load_library()
     need = int(lib.ssd_backward_workspace_bytes(sh))
     if workspace is None:

@@ -62,3 +62,33 @@ def gpu_forward(inp, mma, y_dtype=None, h0=None, want_final=True):
                              y_dtype=y_dtype, want_final=want_final, mma=mma)
     torch.cuda.synchronize()
     return y, fin
+
+
+def device_cus() -> int:
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def heads_per_block(B, L, H, P, N, G, Q, cus, cap=None):
+    """Heads per block the head-group kernels' launchers choose: the largest
+    divisor HG of the group's head count H/G (at most `cap`) such that the grid
+    (B * nc * G * P/64 blocks per head run) still gives every compute unit one
+    block."""
+    nc = -(-L // Q)
+    hpg = H // G
+    base = B * nc * G * (P // 64)
+    best = 1
+    for k in range(1, hpg + 1):
+        if hpg % k or (cap is not None and hpg // k > cap):
+            continue
+        best = hpg // k
+        if base * k >= cus:
+            break
+    return best
+
+
+def chunk_state_hg_fused_cap(Q, N):
+    """Most heads one block of the chunk-state kernel with the cumulative sum
+    fused in can take: its LDS holds the B and x tiles plus 8*Q bytes (sums
+    and dt) per head, within 160 KiB."""
+    lds = Q * (N + 16) * 2 + Q * (64 + 16) * 2
+    return (160 * 1024 - lds) // (8 * Q)

@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    for n in ["ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward",
+    for n in ["ssd_chunk_cumsum", "ssd_chunk_state", "ssd_chunk_cumsum_state", "ssd_state_passing",
+              "ssd_chunk_scan", "ssd_forward",
               "ssd_chunk_state_passing", "ssd_decode_step", "ssd_forward_varlen", "ssd_workspace_bytes",
               "ssd_workspace_bytes_varlen", "ssd_backward", "ssd_backward_workspace_bytes", "ssd_status_string",
               "ssd_abi_version"]:
@@ -40,7 +41,7 @@ def test_header_declares_the_abi():
 def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
-    assert lib.ssd_abi_version() == 3
+    assert lib.ssd_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -61,6 +62,12 @@ def shape(**kw):
     (dict(dstate=0), SHAPE), (dict(ngroups=0), SHAPE), (dict(chunk=0), SHAPE), (dict(nheads=6, ngroups=4), SHAPE),
     (dict(headdim=24), UNSUP), (dict(dstate=40), UNSUP), (dict(headdim=272), UNSUP), (dict(dstate=272), UNSUP),
     (dict(chunk=16), UNSUP), (dict(chunk=96), UNSUP), (dict(chunk=512), UNSUP),
+    # in-chunk 32-bit row offsets would overflow: Q*H*P or Q*G*N >= 2^31
+    (dict(nheads=32768, headdim=256, chunk=256), UNSUP),
+    (dict(nheads=65535, ngroups=65535, dstate=256, headdim=16, chunk=256), UNSUP),
+    (dict(nheads=65535, headdim=144, chunk=256), UNSUP),
+    # 32-bit block numbering: B * nc * H * (P/16) >= 2^31
+    (dict(batch=65535, seqlen=256 * 2048, nheads=16, headdim=64), UNSUP),
 ])
 def test_shape_checks(lib, kw, code):
     s = shape(**kw)
@@ -70,7 +77,30 @@ def test_shape_checks(lib, kw, code):
     assert lib.ssd_chunk_scan(s, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1, 0, None) == code
     assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, 1, FAKE, FAKE, 1 << 40, 0,
                            None) == code
+    assert lib.ssd_chunk_cumsum_state(s, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, None) == code
     assert lib.ssd_workspace_bytes(s) == 0
+
+
+def test_chunk_cumsum_state_checks(lib):
+    s = shape()
+    f = lambda *a: lib.ssd_chunk_cumsum_state(s, *a, None)
+    assert f(FAKE, FAKE, 1, None, FAKE, FAKE, FAKE, FAKE, 0, 0) == NULL      # dt
+    assert f(FAKE, FAKE, 1, FAKE, None, FAKE, FAKE, FAKE, 0, 0) == NULL      # A
+    assert f(FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, FAKE, 0, 0) == NULL      # dt_bhl is required here
+    assert f(FAKE, FAKE, 7, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0) == DTYPE
+    assert f(FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 9) == DTYPE
+    assert f(FAKE, FAKE, 1, FAKE + 4, FAKE, FAKE, FAKE, FAKE, 0, 0) == ALIGN
+    assert f(FAKE, FAKE, 1, FAKE, FAKE, FAKE + 8, FAKE, FAKE, 0, 0) == ALIGN
+
+
+def test_largest_offsets_still_accepted(lib):
+    """Just below the 32-bit offset limit the shape is valid (workspace size
+    defined), one head more it is refused."""
+    ok = shape(nheads=32767, headdim=256, chunk=256, seqlen=256, batch=1)  # 256*32767*256 < 2^31
+    assert lib.ssd_workspace_bytes(ok) > 0
+    assert lib.ssd_workspace_bytes(shape(nheads=32768, headdim=256, chunk=256, seqlen=256, batch=1)) == 0
+    grouped = shape(nheads=32768, ngroups=32768, headdim=16, dstate=256, chunk=256, seqlen=256, batch=1)
+    assert lib.ssd_workspace_bytes(grouped) == 0
 
 
 def test_null_shape(lib):
@@ -196,7 +226,9 @@ def test_forward_varlen_checks(lib):
     nc = 2
     bhl = 4 * B * H * nc * Q
     ru = lambda v: (v + 255) // 256 * 256
-    base = lib.ssd_workspace_bytes(s)
+    st = 4 * B * nc * H * N * P
+    # dA, dt_bhl, fp32 carried states, bf16 chunk states, sequence starts, dA for the passing, masked dt
+    base = ru(ru(ru(ru(bhl) + bhl) + st) + st // 2)
     need = ru(ru(ru(base + 4 * B * nc * Q) + bhl) + bhl)
     assert lib.ssd_workspace_bytes_varlen(s) == need
     assert lib.ssd_workspace_bytes_varlen(None) == 0
@@ -269,7 +301,7 @@ def test_ragged_last_chunk_is_a_valid_shape(lib):
     bhl = 4 * B * H * nc * Q
     st = 4 * B * nc * H * N * P
     ru = lambda v: (v + 255) // 256 * 256
-    assert lib.ssd_workspace_bytes(shape(seqlen=L)) == ru(ru(ru(ru(bhl) + bhl) + st) + st // 2)
+    assert lib.ssd_workspace_bytes(shape(seqlen=L)) == ru(ru(ru(bhl) + bhl) + st)
     assert lib.ssd_workspace_bytes(shape(seqlen=1)) > 0
 
 
@@ -280,12 +312,15 @@ def test_workspace(lib):
     bhl = 4 * B * H * nc * Q
     st = 4 * B * nc * H * N * P
     ru = lambda v: (v + 255) // 256 * 256
-    expect = ru(ru(ru(ru(bhl) + bhl) + st) + st // 2)  # dA, dt_bhl, chunk states, bf16 carried states
+    expect = ru(ru(ru(bhl) + bhl) + st)  # dA, dt_bhl, one state area sized for fp32
     assert lib.ssd_workspace_bytes(s) == expect
     assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, 1, FAKE, None, 1 << 40, 0,
                            None) == WS
-    assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, 1, FAKE, FAKE, expect - 1, 0,
-                           None) == WS
+    # the fp32 path needs all of it, the bf16-operand path half the state area
+    need_bf16 = ru(ru(ru(bhl) + bhl) + st // 2)
+    for mma, need in ((1, expect), (0, need_bf16)):
+        assert lib.ssd_forward(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, 1, FAKE, FAKE, need - 1, mma,
+                               None) == WS
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,170 @@
+"""GPU parity of the head-group kernels with SEVERAL heads per block.
+
+The head-group chunk scan and chunk-state kernels run a block over HG heads of
+one B/C group, reusing the group's C.B^T tiles (chunk scan) or B fragments
+(chunk states) across them, with the next head's tiles prefetched and
+double-buffered while the current one computes.  The launchers take HG as
+large as the grid allows while every compute unit still gets a block, so
+small problems run HG = 1.  These mid-size shapes are chosen so that, on the
+device's compute-unit count, HG >= 2 for every (chunk, dstate) instance of
+both kernels (asserted from the launch rule), including the ragged-chunk
+instance, a 128-column headdim (two column slices) and packed sequences.
+Every (batch, head) pair of y, the final states and the chunk states is
+compared with the fp64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import (chunk_state_hg_fused_cap, device_cus, heads_per_block, make_inputs, oracle, relerr, say,
+                        tol_for, upload)
+from mamba_ssd_scan_chunk_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+# (name, B, L, H, P, N, G, Q)
+CASES = [
+    ("q256_n128", 2, 4096, 32, 64, 128, 1, 256),
+    ("q128_n256", 2, 2048, 16, 64, 256, 2, 128),
+    ("q128_n128", 2, 2048, 24, 64, 128, 1, 128),
+    ("q256_n64", 2, 2048, 32, 64, 64, 1, 256),
+    ("q128_n64", 2, 2048, 32, 64, 64, 2, 128),
+    ("ragged_q256_n128", 2, 4000, 32, 64, 128, 1, 256),
+    ("ragged_q128_n256", 1, 4000, 32, 64, 256, 2, 128),
+    ("p128_q256_n128", 2, 2048, 16, 128, 128, 1, 256),
+    ("q64_n128", 1, 2048, 16, 64, 128, 1, 64),
+    ("q64_n256", 1, 1024, 32, 64, 256, 2, 64),
+]
+SCAN_HG = {(128, 64), (128, 128), (128, 256), (256, 64), (256, 128)}   # (Q, N) of the chunk-scan instances
+STATE_HG = {(64, 128), (128, 128), (256, 128), (64, 256), (128, 256)}  # (Q, N) of the chunk-state instances
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+_CACHE = {}
+
+
+def _case(case):
+    """Inputs and every oracle result of one case, computed once."""
+    name = case[0]
+    if _CACHE.get("name") != name:
+        _CACHE.clear()
+        _, B, L, H, P, N, G, Q = case
+        inp = make_inputs(B, L, H, P, N, G, Q, in_dtype="bf16", seed=41, dt_shift=1.0)
+        o = oracle()
+        say(f"  oracle: {B * H} pairs of {name}")
+        yo, fo, bnd = o.recurrence(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D, chunk=Q, want_boundary=True)
+        S = o.chunk_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, Q)
+        _CACHE.update(name=name, inp=inp, yo=yo, fo=fo, S=S)
+    return _CACHE
+
+
+def _pair_major(y):
+    y = y.float().cpu().numpy()
+    return np.ascontiguousarray(y.transpose(0, 2, 1, 3)).reshape(y.shape[0] * y.shape[2], y.shape[1], y.shape[3])
+
+
+def _assert_multi_head(case):
+    _, B, L, H, P, N, G, Q = case
+    cus = device_cus()
+    hg_scan = heads_per_block(B, L, H, P, N, G, Q, cus) if (Q, N) in SCAN_HG else None
+    hg_state = heads_per_block(B, L, H, P, N, G, Q, cus) if (Q, N) in STATE_HG else None
+    hg_state_fused = (heads_per_block(B, L, H, P, N, G, Q, cus, cap=chunk_state_hg_fused_cap(Q, N))
+                      if (Q, N) in STATE_HG else None)
+    say(f"  {cus} compute units: heads per block chunk_scan {hg_scan}, chunk_state {hg_state} "
+        f"(with the cumsum fused: {hg_state_fused})")
+    for v in (hg_scan, hg_state, hg_state_fused):
+        assert v is None or v >= 2, "shape does not exercise several heads per block on this device"
+    assert hg_scan is not None or hg_state is not None
+
+
+@pytest.mark.parametrize("y_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_headgroup_forward(case, y_dtype):
+    """ssd_forward (bf16 operands) on all pairs against the oracle."""
+    say(f"head-group forward {case} y={y_dtype}")
+    _assert_multi_head(case)
+    c = _case(case)
+    inp = c["inp"]
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    y, fin = ops.ssd_forward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], y_dtype=y_dtype, mma="bf16")
+    torch.cuda.synchronize()
+    ey = relerr(_pair_major(y), c["yo"])
+    ef = relerr(fin.reshape(-1, fin.shape[2], fin.shape[3]), c["fo"])
+    say(f"  rel err y {ey:.3g} final {ef:.3g}")
+    assert ey <= tol_for("bf16") and ef <= tol_for("bf16")
+
+
+@pytest.mark.parametrize("dtypes", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")],
+                         ids=["states_f32-carried_f32", "states_bf16-carried_bf16", "states_f32-carried_bf16"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_headgroup_split_calls(case, dtypes):
+    """The four split calls (chunk states without the fused cumsum, state
+    passing, chunk scan with fp32 or bf16 carried states), all pairs of the
+    chunk states, y and the final states against the oracle."""
+    states_dtype, carried_dtype = dtypes
+    say(f"head-group split calls {case} states={states_dtype} carried={carried_dtype}")
+    _assert_multi_head(case)
+    c = _case(case)
+    inp = c["inp"]
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    S = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma="bf16", states_dtype=states_dtype)
+    torch.cuda.synchronize()
+    es = relerr(S.float(), c["S"])
+    carried, fin = ops.ssd_state_passing(sh, S, dA, carried_dtype=carried_dtype)
+    y = ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, carried, t["D"], y_dtype="f32", mma="bf16")
+    torch.cuda.synchronize()
+    ey = relerr(_pair_major(y), c["yo"])
+    ef = relerr(fin.reshape(-1, fin.shape[2], fin.shape[3]), c["fo"])
+    say(f"  rel err chunk states {es:.3g} y {ey:.3g} final {ef:.3g}")
+    assert es <= tol_for("bf16") and ey <= tol_for("bf16") and ef <= tol_for("bf16")
+
+
+PACKED_HG = [
+    # (name, B, H, P, N, G, Q, sequence lengths per row)
+    ("q256_n128", 2, 32, 64, 128, 1, 256, [[1000, 3, 600, 1, 2492], [4096]]),
+    ("q128_n256", 2, 16, 64, 256, 2, 128, [[129, 127, 1792], [7, 2041]]),
+]
+
+
+@pytest.mark.parametrize("case", PACKED_HG, ids=[c[0] for c in PACKED_HG])
+def test_headgroup_packed_sequences(case):
+    """Packed rows through the head-group chunk scan's packed-sequence
+    instance with several heads per block: every sequence against its own
+    oracle run from a zero state."""
+    name, B, H, P, N, G, Q, rows = case
+    L = sum(rows[0])
+    say(f"head-group packed sequences {name}")
+    cus = device_cus()
+    hg = heads_per_block(B, L, H, P, N, G, Q, cus)
+    say(f"  chunk_scan heads per block {hg}")
+    assert hg >= 2
+    inp = make_inputs(B, L, H, P, N, G, Q, in_dtype="bf16", seed=43, dt_shift=1.0)
+    t = upload(inp)
+    sh = ops.shape_of(t, Q)
+    idx = np.zeros((B, L), dtype=np.int32)
+    for b, lens in enumerate(rows):
+        assert sum(lens) == L
+        idx[b] = np.repeat(np.arange(len(lens), dtype=np.int32), lens)
+    y, fin = ops.ssd_forward_varlen(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"],
+                                    torch.from_numpy(idx).cuda(), y_dtype="f32", mma="bf16")
+    torch.cuda.synchronize()
+    o = oracle()
+    worst = 0.0
+    for b, lens in enumerate(rows):
+        s0 = 0
+        for n in lens:
+            sl = lambda a: np.ascontiguousarray(a[b:b + 1, s0:s0 + n])
+            yref, fref = o.forward(sl(inp.x), sl(inp.dt), inp.A, sl(inp.Bm), sl(inp.Cm), inp.D)
+            worst = max(worst, relerr(y[b:b + 1, s0:s0 + n], yref))
+            s0 += n
+        worst = max(worst, relerr(fin[b:b + 1], fref))
+    say(f"  worst rel err over sequences {worst:.3g}")
+    assert worst <= tol_for("bf16")

@@ -675,3 +675,25 @@ def test_forward_packed_sequences(case, mma, with_h0):
                              y_dtype="f32", mma=mma)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("states_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", MODES, ids=["-".join(m) for m in MODES])
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_chunk_cumsum_state(shape, mode, states_dtype):
+    """The combined first step (cumulative sums + chunk states, one kernel on
+    the head-group shapes) equals ssd_chunk_cumsum then ssd_chunk_state bit
+    for bit, and the oracle within the bar."""
+    in_dtype, mma = mode
+    say(f"chunk_cumsum_state {shape} {mode} states={states_dtype}")
+    inp = _inp(shape, in_dtype, seed=2)
+    t = upload(inp)
+    sh = ops.shape_of(t, inp.chunk)
+    dA, dtb, S = ops.ssd_chunk_cumsum_state(sh, t["x"], t["Bm"], t["dt"], t["A"], mma=mma, states_dtype=states_dtype)
+    dA2, dtb2 = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    S2 = ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb2, dA2, mma=mma, states_dtype=states_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(dA, dA2) and torch.equal(dtb, dtb2) and torch.equal(S, S2)
+    ref = oracle().chunk_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.chunk)
+    # bf16 storage rounds each state to 2^-9 relative, above the fp32 path's bar
+    assert relerr(S.float(), ref) <= (tol_for(mma) if states_dtype == "f32" else tol_for("bf16"))
