@@ -69,7 +69,8 @@ typedef enum {
   SSD_ERR_UNSUPPORTED = 4,  /* valid shape outside this version's limits */
   SSD_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than ssd_workspace_bytes */
   SSD_ERR_ALIGN = 6,        /* a pointer is not 16-byte aligned */
-  SSD_ERR_HIP = 7           /* a kernel launch failed */
+  SSD_ERR_HIP = 7,          /* a kernel launch failed */
+  SSD_ERR_SCRATCH = 8       /* ssd_forward_noalloc: the shape needs more than SSD_NOALLOC_SCRATCH_BYTES */
 } ssd_status;
 
 /* The *_MAX_ENUM members are not valid arguments: they give the enums the
@@ -247,6 +248,33 @@ ssd_status ssd_forward(const ssd_shape* shape, const void* x, const float* dt, c
                        const float* initial_states, void* y, ssd_dtype y_dtype,
                        float* final_states, void* workspace, size_t workspace_bytes,
                        ssd_mma mma, void* stream);
+
+/* Bytes of the static device scratch array ssd_forward_noalloc works in (one
+ * copy per GPU, held from library load until the process ends). */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+
+/*
+ * ssd_forward for callers that cannot allocate device memory: code under
+ * HIP stream capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, computation and results as ssd_forward (bit
+ * for bit), without the workspace: the forward works in the library's own
+ * static device array of SSD_NOALLOC_SCRATCH_BYTES bytes per GPU instead.
+ * It calls no hipMalloc / hipFree and allocates nothing; the first call on a
+ * device looks up that device's copy of the array once.  Shapes whose
+ * workspace (dA_cumsum and dt_bhl, 4 B*H*nc*Q bytes each, plus 2 (bf16
+ * operands) or 4 (fp32 operands) B*nc*H*N*P bytes of states, each part
+ * rounded up to 256 bytes) exceeds the array return SSD_ERR_SCRATCH before
+ * any launch; other errors as for ssd_forward.  The 192 MiB hold the
+ * Mamba-2 2.7B-layer shape (B=2, L=8192, H=80, P=64, N=128, Q=256) on both
+ * precision paths.  Every call on one GPU uses that GPU's one array: calls
+ * that overlap on one GPU (different streams, or several host threads
+ * without ordering) race and give wrong results; calls ordered on one
+ * stream are safe.  Nothing in the array needs clearing between calls.
+ */
+ssd_status ssd_forward_noalloc(const ssd_shape* shape, const void* x, const float* dt, const float* A,
+                               const void* Bm, const void* Cm, const float* D, ssd_dtype in,
+                               const float* initial_states, void* y, ssd_dtype y_dtype,
+                               float* final_states, ssd_mma mma, void* stream);
 
 /*
  * Packed sequences.  Several sequences share a batch row: seq_idx [B,L]

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(PKG, "libmamba_ssd.so")
 
 SSD_OK = 0
 STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE",
-                4: "SSD_ERR_UNSUPPORTED", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_ALIGN", 7: "SSD_ERR_HIP"}
+                4: "SSD_ERR_UNSUPPORTED", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_ALIGN", 7: "SSD_ERR_HIP",
+                8: "SSD_ERR_SCRATCH"}
 SSD_F32, SSD_BF16 = 0, 1
 SSD_MMA_BF16, SSD_MMA_F32 = 0, 1
 MMA = {"bf16": SSD_MMA_BF16, "f32": SSD_MMA_F32}
@@ -52,6 +53,7 @@ _SIGNATURES = {
     "ssd_forward_varlen": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _E, _P, _P, _P, _E, _P, ctypes.c_int64, _P, _P,
                                           _P, ctypes.c_size_t, _E, _P]),
     "ssd_forward": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _E, _P, _P, _E, _P, _P, ctypes.c_size_t, _E, _P]),
+    "ssd_forward_noalloc": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _E, _P, _P, _E, _P, _E, _P]),
     "ssd_backward": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _E, _P, _P, _E, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, ctypes.c_size_t, _E, _P]),
     "ssd_backward_workspace_bytes": (ctypes.c_size_t, [_S]),

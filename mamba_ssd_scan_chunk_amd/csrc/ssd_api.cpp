@@ -484,6 +484,9 @@ const char* ssd_status_string(ssd_status status) {
     case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or smaller than ssd_workspace_bytes";
     case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: a pointer is not 16-byte aligned";
     case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP kernel launch failed";
+    case SSD_ERR_SCRATCH:
+      return "SSD_ERR_SCRATCH: the shape needs more workspace than ssd_forward_noalloc's static scratch array "
+             "(SSD_NOALLOC_SCRATCH_BYTES) holds";
   }
   return "unknown ssd_status";
 }

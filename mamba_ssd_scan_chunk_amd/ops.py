@@ -280,6 +280,39 @@ def ssd_forward(shape, x, dt, A, Bm, Cm, D, initial_states=None, y=None, y_dtype
     return y, final_states
 
 
+def ssd_forward_noalloc(shape, x, dt, A, Bm, Cm, D, initial_states=None, y=None, y_dtype=None,
+                        final_states=None, want_final=True, mma="bf16", stream=None):
+    """ssd_forward in the library's static device scratch array (no
+    workspace; for callers that cannot allocate).  Returns (y,
+    final_states or None); y and final_states are allocated here only when
+    not given."""
+    sh = _shape(shape)
+    B, L, H, P, N, G, Q, nc = _dims(sh)
+    io = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _req(x, "x", (B, L, H, P), io)
+    _req(dt, "dt", (B, L, H), f32)
+    _req(A, "A", (H,), f32)
+    _req(Bm, "Bm", (B, L, G, N), (x.dtype,))
+    _req(Cm, "Cm", (B, L, G, N), (x.dtype,))
+    _req(D, "D", (H,), f32)
+    if initial_states is not None:
+        _req(initial_states, "initial_states", (B, H, N, P), f32)
+    ydt = x.dtype if y_dtype is None else (_DTNAME[y_dtype] if isinstance(y_dtype, str) else y_dtype)
+    if y is None:
+        y = torch.empty((B, L, H, P), device=x.device, dtype=ydt)
+    _req(y, "y", (B, L, H, P), io)
+    if final_states is None and want_final:
+        final_states = torch.empty((B, H, N, P), device=x.device, dtype=torch.float32)
+    if final_states is not None:
+        _req(final_states, "final_states", (B, H, N, P), f32)
+    lib = load_library()
+    check(lib.ssd_forward_noalloc(sh, _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _DT[x.dtype],
+                                  _ptr(initial_states), _ptr(y), _DT[y.dtype], _ptr(final_states), _mma(mma),
+                                  _stream(stream)))
+    return y, final_states
+
+
 def ssd_forward_varlen(shape, x, dt, A, Bm, Cm, D, seq_idx, initial_states=None, y=None, y_dtype=None,
                        final_states=None, want_final=True, seq_last=None, seq_states=None, workspace=None,
                        mma="bf16", stream=None):
