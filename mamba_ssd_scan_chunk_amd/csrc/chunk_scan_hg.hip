@@ -245,17 +245,16 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   static_assert(((QT / 2) * Q) % T == 0, "column-factor entries must divide evenly over the block");
   float gref[NWM];
   // x pieces and the token's G, dt (issued at the top of a head) ...
-  auto issue_x = [&](int h) __attribute__((always_inline)) {
+  auto issue_xpiece = [&](int h, int uu) __attribute__((always_inline)) {
     const uint16_t* xh = static_cast<const uint16_t*>(a.x) + (tok0 * H + h) * (int64_t)P + a.p0;
-#pragma unroll
-    for (int uu = 0; uu < XPT; ++uu) {
-      const int blk = tid + uu * T;
-      if (blk < NXB) {  // always true; the block boundary keeps the scheduler from hoisting across it
-        int row, cb;
-        xmap(blk, row, cb);
-        xv[uu] = *reinterpret_cast<const uint4*>(xh + rowc(row) * HP + 8 * cb);
-      }
+    const int blk = tid + uu * T;
+    if (blk < NXB) {  // always true; the block boundary keeps the scheduler from hoisting across it
+      int row, cb;
+      xmap(blk, row, cb);
+      xv[uu] = *reinterpret_cast<const uint4*>(xh + rowc(row) * HP + 8 * cb);
     }
+  };
+  auto issue_xmeta = [&](int h) __attribute__((always_inline)) {
     // every thread loads (and later stores) the values of token tid mod Q:
     // T is a multiple of Q, and branch-free code keeps the memory waits exact
     const int64_t bhc = ((int64_t)a.b * H + h) * nc + a.c;
@@ -264,6 +263,11 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     const int uq = __builtin_amdgcn_readfirstlane(tid / Q);
 #pragma unroll
     for (int m = 0; m < NWM; ++m) gref[m] = a.dA_cumsum[bhc * Q + 32 * (uq + (T / Q) * m)];
+  };
+  auto issue_x = [&](int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int uu = 0; uu < XPT; ++uu) issue_xpiece(h, uu);
+    issue_xmeta(h);
   };
   // ... and H_in pieces (issued after the C.H_in product, spreading the
   // vector-memory issue over the head)
@@ -384,7 +388,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // `ln` is the lane index laundered through an empty asm at the top of each
   // head iteration: lane-dependent addresses are recomputed per head instead
   // of being hoisted out of the head loop, where they would stay live.
-  auto steps = [&](const int ta, const int tb, f32x4_t (&acc0)[CT], f32x4_t (&acc1)[CT], int ln) {
+  auto steps = [&](const int ta, const int tb, f32x4_t (&acc0)[CT], f32x4_t (&acc1)[CT], int ln, int hn) {
     const int l16 = ln & 15, lg = ln >> 4;
     const int Ua = ta >> 1, Ub = tb >> 1;
     const int sta = VARLEN ? Sts[16 * ta + l16] : -1, stb = VARLEN ? Sts[16 * tb + l16] : -1;
@@ -394,6 +398,10 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 #pragma unroll
     for (int k = 0; k < QT / 2; ++k) {
       if (k <= Ub) {
+        // one 16-byte piece of the next head's x rows per step: the
+        // vector-memory issue is spread over the head instead of queued at
+        // its start by all waves at once
+        if (k < XPT) issue_xpiece(hn, k);
         Frag xf[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) xf[ct] = xn[ct];
@@ -463,7 +471,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     // memory-counter waits stay exact, so the loads of the next head remain in
     // flight across the whole compute of this one.
     const int hn = hh + 1 < a.HG ? h + 1 : h;
-    issue_x(hn);
+    issue_xmeta(hn);
     const float dsk = a.D[h];
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -513,7 +521,15 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         acc0[ct] *= e0;
         acc1[ct] *= e1;
       }
-      steps(ta, tb, acc0, acc1, ln);
+      // the waves whose steps carry both tiles most often take priority
+      // over their SIMD neighbours (same MFMA count, denser chains)
+      if (wv >= QT / 4) __builtin_amdgcn_s_setprio(2);
+      steps(ta, tb, acc0, acc1, ln, hn);
+      __builtin_amdgcn_s_setprio(0);
+      // pieces a short step loop did not issue
+#pragma unroll
+      for (int k = 0; k < XPT; ++k)
+        if (k > (tb >> 1)) issue_xpiece(hn, k);
       store_tile(ta, acc0, h, dsk, ln);
       store_tile(tb, acc1, h, dsk, ln);
     }

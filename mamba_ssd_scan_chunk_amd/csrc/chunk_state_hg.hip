@@ -111,6 +111,46 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   float gv[XPT], dv[XPT];
   float glast = 0.f;
   int hcur = 0;  // FUSE: head (within the group) of the prefetched pieces
+  // second prefetch stage: the head after the next one
+  uint4 xv2[XPT];
+  float gv2[XPT], dv2[XPT];
+  float glast2 = 0.f;
+  int hcur2 = 0;
+  auto advance = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const uint4 q = xv2[u];
+      xv[u] = make_uint4(q.x, q.y, q.z, q.w);
+      gv[u] = gv2[u];
+      dv[u] = dv2[u];
+    }
+    glast = glast2;
+    hcur = hcur2;
+  };
+  auto issue2 = [&](int h) __attribute__((always_inline)) {
+    const uint16_t* xs = x + (tok0 * H + h) * (int64_t)P + p0;
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      int row, cb;
+      xmap(tid + u * T, row, cb);
+      xv2[u] = *reinterpret_cast<const uint4*>(xs + min(row, rmax) * HP + 8 * cb);
+    }
+    if constexpr (FUSE) {
+      hcur2 = h - hbase;
+    } else {
+      const int64_t bhc = ((int64_t)b * H + h) * nc + c;
+      const float* gsrc = dA_cumsum + bhc * Q;
+      const float* dsrc = dt_bhl + bhc * Q;
+#pragma unroll
+      for (int u = 0; u < XPT; ++u) {
+        int row, cb;
+        xmap(tid + u * T, row, cb);
+        gv2[u] = gsrc[row];
+        dv2[u] = dsrc[row];
+      }
+      glast2 = gsrc[Q - 1];
+    }
+  };
   auto issue = [&](int h) __attribute__((always_inline)) {
     const uint16_t* xs = x + (tok0 * H + h) * (int64_t)P + p0;
 #pragma unroll
@@ -156,9 +196,10 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     }
   };
 
-  // the first head's x pieces are in flight while B (and, with FUSE, the
+  // the first two heads' x pieces are in flight while B (and, with FUSE, the
   // cumulative sums) are staged
   issue(hbase);
+  issue2(HG > 1 ? hbase + 1 : hbase);
 
   // ---- B chunk -> Bn[j][n] (16-byte copies; a row's pieces go to
   // consecutive threads)
@@ -229,6 +270,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) bfr[i][kk] = lds_frag_tr(Bn + 32 * kk * BP + 16 * (NTW * wn + i), BP, tid & 63);
   commit(Xn);
+  advance();
   __syncthreads();  // every wave holds its B fragments: the Bn area is free from here on
 
   // x tiles double-buffered: head hh computes from one buffer while head
@@ -242,7 +284,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     // its own head again, unused): with no conditional around them the
     // compiler's memory-counter waits stay exact, so the loads of the next
     // head remain in flight across the whole compute of this one.
-    issue(hh + 1 < HG ? h + 1 : h);
+    issue2(hh + 2 < HG ? h + 2 : hbase + HG - 1);
     {
       // lane index laundered per head: lane-dependent addresses are recomputed
       // here rather than hoisted out of the head loop
@@ -269,21 +311,27 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
 #pragma unroll
       for (int i = 0; i < NTW; ++i) {
         const int n = 16 * (NTW * wn + i) + l16;
+        if constexpr (SBF16) {
+          // the wave's two column tiles paired across lane rows: 8
+          // consecutive columns (one 16-byte store) per lane
+          const uint2 t0 = make_uint2(pack_bf16x2(acc[i][0][0], acc[i][0][1]), pack_bf16x2(acc[i][0][2], acc[i][0][3]));
+          const uint2 t1 = make_uint2(pack_bf16x2(acc[i][1][0], acc[i][1][1]), pack_bf16x2(acc[i][1][2], acc[i][1][3]));
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(states) + so + n * P + 32 * wp + pair_tiles_col(lg)) =
+              pair_tiles_16b(t0, t1);
+        } else {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const int pc = 16 * (2 * wp + ct) + 4 * lg;
-          if constexpr (SBF16)
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(states) + so + n * P + pc) =
-                make_uint2(pack_bf16x2(acc[i][ct][0], acc[i][ct][1]), pack_bf16x2(acc[i][ct][2], acc[i][ct][3]));
-          else
+          for (int ct = 0; ct < 2; ++ct) {
+            const int pc = 16 * (2 * wp + ct) + 4 * lg;
             *reinterpret_cast<float4*>(static_cast<float*>(states) + so + n * P + pc) =
                 make_float4(acc[i][ct][0], acc[i][ct][1], acc[i][ct][2], acc[i][ct][3]);
+          }
         }
       }
     }
     // the other buffer was last read by the previous head, which every wave
     // finished before the previous barrier
     commit(xnext);
+    advance();
     __syncthreads();
   }
 }
