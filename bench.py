@@ -220,21 +220,26 @@ def time_fp32_path(ops, torch, t, sh, w, stream, steps):
     ms = a.elapsed_time(b) / steps
     in_bytes = 2 if w.in_dtype == "bf16" else 4
     costs = algorithmic_costs(w, in_bytes, 4, 4, 4)
-    spin = spin_cycles(torch, stream, 5000)
+    # as the per-kernel rows of the main loop: a short GPU spin lets the host
+    # queue the events and calls (a long one lets the clocks fall), then REPS
+    # back-to-back launches of each call per event pair
+    reps = 4
+    spin = spin_cycles(torch, stream, 200)
     evs = {k: [] for k in calls}
     for _ in range(max(3, steps // 5)):
-        torch.cuda._sleep(spin)
         for k, c in calls.items():
+            torch.cuda._sleep(spin)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            c()
+            for _r in range(reps):
+                c()
             e1.record(stream)
             evs[k].append((e0, e1))
     torch.cuda.synchronize()
     out = {"ms": round(ms, 4), "tokens_per_s": round(w.tokens / (ms * 1e-3), 1), "y_dtype": "f32",
            "steps": steps, "mfma_peak_TFLOPs": MFMA_PEAK_TFLOPS["f32"], "kernels": {}}
     for k, pairs in evs.items():
-        us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in pairs) / len(pairs)
+        us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in pairs) / (len(pairs) * reps)
         c = costs[k]
         tf = c["flops"] / (us * 1e-6) / 1e12
         out["kernels"][k] = {"us": round(us, 2), "TFLOPs": round(tf, 2),

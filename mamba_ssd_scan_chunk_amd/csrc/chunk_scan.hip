@@ -353,8 +353,8 @@ hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* Bm, const
                              const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream,
                              const int* seq_start) {
   if (chunk_scan_hg_supported(d, in_bf16, f32_mma))
-    return launch_chunk_scan_hg(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, stream,
-                                seq_start);
+    return launch_chunk_scan_hg(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, f32_mma,
+                                stream, seq_start);
   const size_t lds = chunk_scan_lds_bytes(d, f32_mma);
   if (f32_mma)
     return launch_scan_op<OpF32>(d, x, Bm, Cm, in_bf16, dt_bhl, dA_cumsum, carried, h_bf16, D, y, y_bf16, seq_start, stream, lds);

@@ -53,7 +53,7 @@ namespace ssd {
 
 constexpr int hg_threads(int q) { return q >= 256 ? 512 : 256; }
 
-template <int Q, int NK, int CT>
+template <int Q, int NK, int CT, bool F32M = false>
 struct HgCfg {
   static constexpr int QT = Q / 16;
   static constexpr int NCW = QT / 2;  // compute waves: wave w owns row tiles w and QT-1-w
@@ -69,7 +69,10 @@ struct HgCfg {
   // is free of bank conflicts
   static constexpr int XNP = PT + 16;
   static constexpr size_t lds_bs = (size_t)Q * NPI * 2;
-  static constexpr size_t lds_xh = (size_t)Q * XNP * 2 + (size_t)N * XNP * 2;
+  // F32M (fp32 matrix operands): H_in is staged in fp32, transposed ([p][n])
+  // with its 16-byte groups of n XOR-swizzled by the row p (see ht_pos)
+  static constexpr size_t lds_h = F32M ? sizeof(float) * (size_t)PT * N : (size_t)N * XNP * 2;
+  static constexpr size_t lds_xh = (size_t)Q * XNP * 2 + lds_h;
   static constexpr size_t lds_a = lds_bs > lds_xh ? lds_bs : lds_xh;  // Bs, later Xn + Hn
   static constexpr size_t lds_c = (size_t)Q * NPI * 2;                // Cs
   static constexpr size_t lds_w = sizeof(float) * (size_t)(QT / 2) * Q;  // Ws
@@ -78,7 +81,7 @@ struct HgCfg {
   // the C fragments of C.H_in kept in registers -- so a head needs one
   // barrier instead of two.  N = 256 keeps the single-buffer layout (its C
   // fragments would not fit in registers).
-  static constexpr bool DB = NK == 2 || NK == 4;
+  static constexpr bool DB = (NK == 2 || NK == 4) && !F32M;
   static constexpr size_t lds_buf = lds_xh + lds_w + 2 * sizeof(float) * Q;  // one buffer
   static constexpr size_t lds_db = 2 * lds_bs > 2 * lds_buf ? 2 * lds_bs : 2 * lds_buf;
   static constexpr size_t lds_total = DB ? lds_db : lds_a + lds_c + lds_w + 2 * sizeof(float) * Q;
@@ -88,7 +91,8 @@ struct HgCfg {
 // LDS tiles of one head: x, H_in, the column-factor table, G and dt
 struct HgBuf {
   uint16_t* Xn;  // [Q][XNP]
-  uint16_t* Hn;  // [N][XNP]
+  uint16_t* Hn;  // [N][XNP] (bf16 operands)
+  float* Ht;     // [PT][N] swizzled (fp32 operands)
   float* Ws;     // [QT/2][Q]
   float* Gs;     // [Q]
   float* dts;    // [Q]
@@ -118,11 +122,40 @@ __device__ __forceinline__ int npos(int n) {
   return (n & ~31) | ((n & 12) << 1) | ((n & 16) >> 2) | (n & 3);
 }
 
-template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED, bool VARLEN>
+// Element offset of H_in[n][p] in the fp32 transposed tile Ht[p][n] (row
+// pitch N): the 16-byte group n / 4 is XOR-ed with ((p / 4) + 4 (p mod 4))
+// mod 16, so that both the transposing writes (16 rows p = 4c + q, one n)
+// and the fragment reads (16 rows p, one group of n each) fall in distinct
+// banks of the 64-bank LDS.
+template <int N>
+__device__ __forceinline__ int ht_pos(int n, int p) {
+  const int sw = ((p >> 2) + 4 * (p & 3)) & 15;
+  return p * N + ((((n >> 2) ^ sw)) << 2) + (n & 3);
+}
+
+// bf16 fragment (8 slots) widened to fp32, slot order kept
+__device__ __forceinline__ OpF32::Frag widen_frag8(const OpBF16::Frag& f) {
+  OpF32::Frag r;
+  r.lo = make_float4(bf16_bits_to_f32(f.v.x & 0xffffu), bf16_bits_to_f32(f.v.x >> 16),
+                     bf16_bits_to_f32(f.v.y & 0xffffu), bf16_bits_to_f32(f.v.y >> 16));
+  r.hi = make_float4(bf16_bits_to_f32(f.v.z & 0xffffu), bf16_bits_to_f32(f.v.z >> 16),
+                     bf16_bits_to_f32(f.v.w & 0xffffu), bf16_bits_to_f32(f.v.w >> 16));
+  return r;
+}
+
+template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED, bool VARLEN, bool F32M>
 __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, const int tid) {
-  using Cfg = HgCfg<Q, NK, CT>;
-  using Op = OpBF16;
+  using Cfg = HgCfg<Q, NK, CT, F32M>;
+  using Op = OpBF16;  // C.B^T (exact: B and C are bf16 inputs)
   using Frag = Op::Frag;
+  // M.X and C.H_in: bf16 operands, or (F32M) fp32 operands -- the decayed
+  // interaction tile and H_in in fp32, x widened exactly from bf16
+  using OpM = std::conditional_t<F32M, OpF32, OpBF16>;
+  using FragM = typename OpM::Frag;
+  auto to_m = [](const Frag& f) -> FragM {
+    if constexpr (F32M) return widen_frag8(f);
+    else return f;
+  };
   constexpr int QT = Cfg::QT, PT = Cfg::PT, N = Cfg::N, NPI = Cfg::NPI, XNP = Cfg::XNP, T = Cfg::T;
   static_assert(PT == 64, "the prefetch maps assume a 64-column slice");
   constexpr int NXB = Q * (PT / 8);          // x prefetch pieces (16 bytes: 8 columns of one token)
@@ -152,6 +185,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       r.Hn = r.Xn + Q * XNP;
       r.Ws = reinterpret_cast<float*>(smem + Cfg::lds_a + Cfg::lds_c);
     }
+    r.Ht = reinterpret_cast<float*>(r.Xn + Q * XNP);
     r.Gs = r.Ws + (QT / 2) * Q;
     r.dts = r.Gs + Q;
     return r;
@@ -302,7 +336,23 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       if (blk >= NHB) continue;
       const int n = blk / (PT / HCOL), col = HCOL * (blk % (PT / HCOL));
       const uint4 q = hv[uu];
-      if constexpr (H_BF16) {
+      if constexpr (F32M) {
+        // fp32 values (bf16 carried states widened exactly), transposed
+        float hvl[HCOL];
+        if constexpr (H_BF16) {
+          const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hvl[2 * e] = bf16_bits_to_f32(w4[e] & 0xffffu);
+            hvl[2 * e + 1] = bf16_bits_to_f32(w4[e] >> 16);
+          }
+        } else {
+          hvl[0] = __uint_as_float(q.x); hvl[1] = __uint_as_float(q.y);
+          hvl[2] = __uint_as_float(q.z); hvl[3] = __uint_as_float(q.w);
+        }
+#pragma unroll
+        for (int e = 0; e < HCOL; ++e) t.Ht[ht_pos<N>(n, col + e)] = hvl[e];
+      } else if constexpr (H_BF16) {
         *reinterpret_cast<uint4*>(t.Hn + n * XNP + col) = make_uint4(q.x, q.y, q.z, q.w);
       } else {
         *reinterpret_cast<uint2*>(t.Hn + n * XNP + col) =
@@ -330,7 +380,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // MFMA sites per branch made the compiler copy accumulators at every merge,
   // each copy waiting for the MFMA results).
   // Off-diagonal pair k of a tile whose diagonal pair is U: M' = CB * Ws[U][j].
-  auto offdiag_frag = [&](auto tsel_c, const int k, const int U, int lg, int sti) -> Frag {
+  auto offdiag_frag = [&](auto tsel_c, const int k, const int U, int lg, int sti) -> FragM {
     constexpr int TSEL = decltype(tsel_c)::value;
     const float4 w0 = *reinterpret_cast<const float4*>(cur.Ws + U * Q + 32 * k + 4 * lg);
     const float4 w1 = *reinterpret_cast<const float4*>(cur.Ws + U * Q + 32 * k + 16 + 4 * lg);
@@ -343,7 +393,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       for (int e8 = 0; e8 < 8; ++e8)
         if (32 * k + 16 * (e8 >> 2) + 4 * lg + (e8 & 3) < sti) m[e8] = 0.f;
     }
-    return Op::from_f32(m);
+    return OpM::from_f32(m);
   };
   // Diagonal pair k = tile / 2: the row factor exp(G_i - G_R) first scales
   // everything accumulated so far (in place), then the pair takes exact
@@ -352,7 +402,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // upper sub-tile of an even tile, whose slot holds the other tile's values,
   // is zeroed outright; that select also keeps the register allocator from
   // copying the accumulators.)
-  auto diag_frag = [&](auto tsel_c, const int k, const int tile, f32x4_t (&acc)[CT], int l16, int lg, int sti) -> Frag {
+  auto diag_frag = [&](auto tsel_c, const int k, const int tile, f32x4_t (&acc)[CT], int l16, int lg, int sti) -> FragM {
     constexpr int TSEL = decltype(tsel_c)::value;
     const int i = 16 * tile + l16;  // the token this lane's interaction values and outputs belong to
     // G and dt of the lane's 8 tokens j = 32k + 16t + 4lg + r, read as vectors
@@ -380,7 +430,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       const float dec = fast_exp2(keep ? gi - gj[e8] : -INFINITY);
       m[e8] = cvv[e8] * dj[e8] * dec;
     }
-    return Op::from_f32(m);
+    return OpM::from_f32(m);
   };
   // One pass over the pair index k serves both tiles (ta = w < tb = QT-1-w, so
   // the diagonal pair of ta comes first): the x fragments of a step are read
@@ -410,17 +460,17 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
           for (int ct = 0; ct < CT; ++ct) xn[ct] = lds_frag_tr(cur.Xn + 32 * (k + 1) * XNP + 16 * ct, XNP, ln);
         }
         if (k <= Ua) {
-          Frag mfa;
+          FragM mfa;
           if (k < Ua) mfa = offdiag_frag(std::integral_constant<int, 0>{}, k, Ua, lg, sta);
           else mfa = diag_frag(std::integral_constant<int, 0>{}, k, ta, acc0, l16, lg, sta);
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) acc0[ct] = Op::mma(xf[ct], mfa, acc0[ct]);
+          for (int ct = 0; ct < CT; ++ct) acc0[ct] = OpM::mma(to_m(xf[ct]), mfa, acc0[ct]);
         }
-        Frag mfb;
+        FragM mfb;
         if (k < Ub) mfb = offdiag_frag(std::integral_constant<int, 1>{}, k, Ub, lg, stb);
         else mfb = diag_frag(std::integral_constant<int, 1>{}, k, tb, acc1, l16, lg, stb);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc1[ct] = Op::mma(xf[ct], mfb, acc1[ct]);
+        for (int ct = 0; ct < CT; ++ct) acc1[ct] = OpM::mma(to_m(xf[ct]), mfb, acc1[ct]);
       }
     }
   };
@@ -497,15 +547,29 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       }
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
-        Frag hf[CT];
+        const FragM ca0 = to_m(DB ? cfa[DB ? s : 0] : Lds<Op>::load8(Cs + (16 * ta + l16) * NPI + 32 * s + 8 * lg));
+        const FragM ca1 = to_m(DB ? cfb[DB ? s : 0] : Lds<Op>::load8(Cs + (16 * tb + l16) * NPI + 32 * s + 8 * lg));
+        if constexpr (F32M) {
+          // one fp32 H fragment at a time (slots 4t + r <-> n = 32s + 16t +
+          // 4lg + r, as the C fragment)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) hf[ct] = lds_frag_tr(cur.Hn + 32 * s * XNP + 16 * ct, XNP, ln);
-        const Frag ca0 = DB ? cfa[DB ? s : 0] : Lds<Op>::load8(Cs + (16 * ta + l16) * NPI + 32 * s + 8 * lg);
-        const Frag ca1 = DB ? cfb[DB ? s : 0] : Lds<Op>::load8(Cs + (16 * tb + l16) * NPI + 32 * s + 8 * lg);
+          for (int ct = 0; ct < CT; ++ct) {
+            const int p = 16 * ct + l16;
+            FragM hf;
+            hf.lo = *reinterpret_cast<const float4*>(cur.Ht + ht_pos<N>(32 * s + 4 * lg, p));
+            hf.hi = *reinterpret_cast<const float4*>(cur.Ht + ht_pos<N>(32 * s + 16 + 4 * lg, p));
+            acc0[ct] = OpM::mma(hf, ca0, acc0[ct]);
+            acc1[ct] = OpM::mma(hf, ca1, acc1[ct]);
+          }
+        } else {
+          Frag hf[CT];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          acc0[ct] = Op::mma(hf[ct], ca0, acc0[ct]);
-          acc1[ct] = Op::mma(hf[ct], ca1, acc1[ct]);
+          for (int ct = 0; ct < CT; ++ct) hf[ct] = lds_frag_tr(cur.Hn + 32 * s * XNP + 16 * ct, XNP, ln);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            acc0[ct] = OpM::mma(hf[ct], ca0, acc0[ct]);
+            acc1[ct] = OpM::mma(hf[ct], ca1, acc1[ct]);
+          }
         }
       }
       issue_h(hn);
@@ -549,7 +613,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 // Y_BF16 is a template parameter rather than a run-time flag: a branch around
 // the output stores would make the compiler's memory-counter waits for the
 // prefetched loads conservative (they would also wait for the stores).
-template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED, bool VARLEN>
+template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED, bool VARLEN, bool F32M>
 __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, const void* __restrict__ Cm,
     const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const void* __restrict__ carried,
@@ -577,7 +641,7 @@ __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
   a.hbase = a.g * (H / G) + hgi * HG;
   a.p0 = pt * HgCfg<Q, NK, CT>::PT;
   a.tok0 = (int64_t)a.b * L + (int64_t)a.c * Q;
-  hg_body<Q, NK, CT, H_BF16, Y_BF16, RAGGED, VARLEN>(a, hg_smem, threadIdx.x);
+  hg_body<Q, NK, CT, H_BF16, Y_BF16, RAGGED, VARLEN, F32M>(a, hg_smem, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ host side
@@ -597,24 +661,24 @@ static int pick_heads_per_block(const Dims& d, int npt) {
   return best;
 }
 
-template <int Q, int NK, bool H_BF16, bool Y_BF16>
+template <int Q, int NK, bool H_BF16, bool Y_BF16, bool F32M>
 static auto pick_hg_kernel(bool ragged, bool varlen) {
   // packed sequences take the guarded-store instance too (their last chunk
   // may be ragged as well)
-  if (varlen) return chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, true, true>;
-  return ragged ? chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, true, false>
-                : chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, false, false>;
+  if (varlen) return chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, true, true, F32M>;
+  return ragged ? chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, true, false, F32M>
+                : chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, false, false, F32M>;
 }
 
-template <int Q, int NK, bool H_BF16>
+template <int Q, int NK, bool H_BF16, bool F32M>
 static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, const void* Cm, const float* dt_bhl,
                                  const float* dA_cumsum, const void* carried, const float* D, void* y,
                                  bool y_bf16, hipStream_t stream, const int* seq_start) {
   constexpr int CT = 4;
-  using Cfg = HgCfg<Q, NK, CT>;
+  using Cfg = HgCfg<Q, NK, CT, F32M>;
   const bool ragged = d.L % Q != 0, varlen = seq_start != nullptr;
-  auto kern = y_bf16 ? pick_hg_kernel<Q, NK, H_BF16, true>(ragged, varlen)
-                     : pick_hg_kernel<Q, NK, H_BF16, false>(ragged, varlen);
+  auto kern = y_bf16 ? pick_hg_kernel<Q, NK, H_BF16, true, F32M>(ragged, varlen)
+                     : pick_hg_kernel<Q, NK, H_BF16, false, F32M>(ragged, varlen);
   const size_t lds = varlen ? Cfg::lds_varlen : Cfg::lds_total;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -631,35 +695,40 @@ static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, c
   return hipGetLastError();
 }
 
-template <int Q, int NK>
+template <int Q, int NK, bool F32M>
 static bool hg_fits() {
-  using Cfg = HgCfg<Q, NK, 4>;
+  using Cfg = HgCfg<Q, NK, 4, F32M>;
   return Cfg::lds_varlen <= 160 * 1024 && Q <= Cfg::T && 64 * Cfg::NCW <= Cfg::T && (Q == 128 || Q == 256);
 }
 
 bool chunk_scan_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
-  if (f32_mma || !in_bf16) return false;
+  // bf16 inputs only: C.B^T runs on bf16 matrix instructions (exact for bf16
+  // values), and the fp32-operand instance widens x exactly
+  if (!in_bf16) return false;
   if (d.P % 64 != 0) return false;
   if (d.nc * d.B * d.G * (d.H / d.G) * (d.P / 64) > 0x7fffffff) return false;
   const int64_t key = d.Q * 1000 + d.N;
+#define HG_FITS(QQ, KK) (f32_mma ? hg_fits<QQ, KK, true>() : hg_fits<QQ, KK, false>())
   switch (key) {
-    case 128 * 1000 + 64: return hg_fits<128, 2>();
-    case 128 * 1000 + 128: return hg_fits<128, 4>();
-    case 128 * 1000 + 256: return hg_fits<128, 8>();
-    case 256 * 1000 + 64: return hg_fits<256, 2>();
-    case 256 * 1000 + 128: return hg_fits<256, 4>();
+    case 128 * 1000 + 64: return HG_FITS(128, 2);
+    case 128 * 1000 + 128: return HG_FITS(128, 4);
+    case 128 * 1000 + 256: return HG_FITS(128, 8);
+    case 256 * 1000 + 64: return HG_FITS(256, 2);
+    case 256 * 1000 + 128: return HG_FITS(256, 4);
     default: return false;
   }
+#undef HG_FITS
 }
 
-template <bool H_BF16>
+template <bool H_BF16, bool F32M>
 static hipError_t launch_hg_dtype(const Dims& d, const void* x, const void* Bm, const void* Cm, const float* dt_bhl,
                                   const float* dA_cumsum, const void* carried, const float* D, void* y, bool y_bf16,
                                   hipStream_t stream, const int* seq_start) {
   const int64_t key = d.Q * 1000 + d.N;
-#define HG_CASE(QQ, NN, KK) \
-  case QQ * 1000 + NN:      \
-    return launch_hg_inst<QQ, KK, H_BF16>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
+#define HG_CASE(QQ, NN, KK)                                                                                      \
+  case QQ * 1000 + NN:                                                                                           \
+    return launch_hg_inst<QQ, KK, H_BF16, F32M>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, \
+                                                seq_start);
   switch (key) {
     HG_CASE(128, 64, 2)
     HG_CASE(128, 128, 4)
@@ -673,11 +742,17 @@ static hipError_t launch_hg_dtype(const Dims& d, const void* x, const void* Bm, 
 
 hipError_t launch_chunk_scan_hg(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
                                 const float* dt_bhl, const float* dA_cumsum, const void* carried, bool carried_bf16,
-                                const float* D, void* y, bool y_bf16, hipStream_t stream, const int* seq_start) {
+                                const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream,
+                                const int* seq_start) {
   if (!in_bf16) return hipErrorInvalidValue;
+  if (f32_mma) {
+    if (carried_bf16)
+      return launch_hg_dtype<true, true>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
+    return launch_hg_dtype<false, true>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
+  }
   if (carried_bf16)
-    return launch_hg_dtype<true>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
-  return launch_hg_dtype<false>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
+    return launch_hg_dtype<true, false>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
+  return launch_hg_dtype<false, false>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
 }
 
 }  // namespace ssd

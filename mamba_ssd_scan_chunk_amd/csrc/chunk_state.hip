@@ -251,7 +251,7 @@ hipError_t launch_chunk_state_any(const Dims& d, const void* x, const void* Bm, 
                                   const float* dt_bhl, const float* dA_cumsum, void* states, bool states_bf16,
                                   bool f32_mma, hipStream_t stream) {
   if (chunk_state_hg_supported(d, in_bf16, f32_mma))
-    return launch_chunk_state_hg(d, x, Bm, dt_bhl, dA_cumsum, states, states_bf16, stream);
+    return launch_chunk_state_hg(d, x, Bm, dt_bhl, dA_cumsum, states, states_bf16, f32_mma, stream);
   if (f32_mma) return launch_state_op<OpF32>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream);
   return launch_state_op<OpBF16>(d, x, Bm, in_bf16, dt_bhl, dA_cumsum, states, states_bf16, stream);
 }

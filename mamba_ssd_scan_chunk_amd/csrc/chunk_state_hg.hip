@@ -22,6 +22,11 @@
 // D[p][n] = sum_j x[j][p] B[j][n] (A operand: x, B operand: B), so that each
 // lane holds four consecutive p of one state row n and writes them as one
 // 16-byte store.
+// F32M (fp32 matrix operands, bf16 inputs): x stays in LDS as its exact
+// bf16 values and the weight w_j goes to a per-head table; each transposed x
+// fragment is widened to fp32 and multiplied by the weights of its 8 tokens
+// in fp32, the B fragments (exact bf16) are widened, and eight fp32 16x16x4
+// products consume each 32-token step.  No operand is rounded below fp32.
 // 8 waves (two per SIMD) in a 4 x 2 grid: wave w owns the state rows of
 // tiles NTW (w % 4) .. +NTW-1 (NTW = N / 64) and the column tiles 2 (w / 4),
 // +1 of the slice; the B fragments of its rows stay in registers for all the
@@ -57,7 +62,17 @@ struct ShgCfg {
 // otherwise it reads them.
 // SBF16: the states are stored rounded to bf16 (nearest even, 8-byte stores
 // of four consecutive p) instead of fp32.
-template <int Q, int N, bool FUSE, bool SBF16>
+// bf16 fragment (8 slots) widened to fp32, slot order kept
+__device__ __forceinline__ OpF32::Frag widen_frag(const OpBF16::Frag& f) {
+  OpF32::Frag r;
+  r.lo = make_float4(bf16_bits_to_f32(f.v.x & 0xffffu), bf16_bits_to_f32(f.v.x >> 16),
+                     bf16_bits_to_f32(f.v.y & 0xffffu), bf16_bits_to_f32(f.v.y >> 16));
+  r.hi = make_float4(bf16_bits_to_f32(f.v.z & 0xffffu), bf16_bits_to_f32(f.v.z >> 16),
+                     bf16_bits_to_f32(f.v.w & 0xffffu), bf16_bits_to_f32(f.v.w >> 16));
+  return r;
+}
+
+template <int Q, int N, bool FUSE, bool SBF16, bool F32M>
 __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bhl,
     const float* __restrict__ dA_cumsum, const float* __restrict__ dt_raw, const float* __restrict__ Avec,
@@ -77,6 +92,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   uint16_t* Xn = Bn + Q * BP;                             // [Q][XP]
   float* Gsa = reinterpret_cast<float*>(Xn + Q * XP);     // [HG][Q] log-space sums (FUSE)
   float* Dsa = Gsa + HG * Q;                               // [HG][Q] dt (FUSE)
+  float* Wt = Gsa + (FUSE ? 2 * HG * Q : 0);               // [2][Q] weights of the two x buffers (F32M)
 
   const unsigned nblk = gridDim.x;
   unsigned bid = blockIdx.x;
@@ -175,7 +191,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
       glast = gsrc[Q - 1];
     }
   };
-  auto commit = [&](uint16_t* dst) __attribute__((always_inline)) {
+  auto commit = [&](uint16_t* dst, float* wdst) __attribute__((always_inline)) {
     if constexpr (FUSE) glast = Gsa[hcur * Q + Q - 1];
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
@@ -187,6 +203,12 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
       }
       const float w = fast_exp(glast - gv[u]) * dv[u];
       const uint4 q = xv[u];
+      if constexpr (F32M) {
+        // raw x (exact bf16) and the row's weight, applied in fp32 at use
+        *reinterpret_cast<uint4*>(dst + row * XP + 8 * cb) = make_uint4(q.x, q.y, q.z, q.w);
+        if (cb == 0) wdst[row] = w;
+        continue;
+      }
       uint4 o;
       o.x = pack_bf16x2(bf16_bits_to_f32(q.x & 0xffffu) * w, bf16_bits_to_f32(q.x >> 16) * w);
       o.y = pack_bf16x2(bf16_bits_to_f32(q.y & 0xffffu) * w, bf16_bits_to_f32(q.y >> 16) * w);
@@ -269,7 +291,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   for (int i = 0; i < NTW; ++i)
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) bfr[i][kk] = lds_frag_tr(Bn + 32 * kk * BP + 16 * (NTW * wn + i), BP, tid & 63);
-  commit(Xn);
+  commit(Xn, Wt);
   advance();
   __syncthreads();  // every wave holds its B fragments: the Bn area is free from here on
 
@@ -280,6 +302,8 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     const int h = hbase + hh;
     uint16_t* const xcur = (hh & 1) ? Bn : Xn;
     uint16_t* const xnext = (hh & 1) ? Xn : Bn;
+    const float* const wcur = Wt + (hh & 1) * Q;
+    float* const wnext = Wt + ((hh + 1) & 1) * Q;
     // The prefetch and the commit run on every iteration (the last one loads
     // its own head again, unused): with no conditional around them the
     // compiler's memory-counter waits stay exact, so the loads of the next
@@ -301,10 +325,29 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
         Frag xf[2];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) xf[ct] = lds_frag_tr(xcur + 32 * kk * XP + 16 * (2 * wp + ct), XP, ln);
+        if constexpr (F32M) {
+          // weights of the lane's tokens j = 32kk + 16t + 4lg + r (slot 4t + r)
+          const float4 w0 = *reinterpret_cast<const float4*>(wcur + 32 * kk + 4 * lg);
+          const float4 w1 = *reinterpret_cast<const float4*>(wcur + 32 * kk + 16 + 4 * lg);
+          OpF32::Frag xw[2];
 #pragma unroll
-        for (int i = 0; i < NTW; ++i)
+          for (int ct = 0; ct < 2; ++ct) {
+            xw[ct] = widen_frag(xf[ct]);
+            xw[ct].lo.x *= w0.x; xw[ct].lo.y *= w0.y; xw[ct].lo.z *= w0.z; xw[ct].lo.w *= w0.w;
+            xw[ct].hi.x *= w1.x; xw[ct].hi.y *= w1.y; xw[ct].hi.z *= w1.z; xw[ct].hi.w *= w1.w;
+          }
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) acc[i][ct] = Op::mma(xf[ct], bfr[i][kk], acc[i][ct]);
+          for (int i = 0; i < NTW; ++i) {
+            const OpF32::Frag bw = widen_frag(bfr[i][kk]);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc[i][ct] = OpF32::mma(xw[ct], bw, acc[i][ct]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < NTW; ++i)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc[i][ct] = Op::mma(xf[ct], bfr[i][kk], acc[i][ct]);
+        }
       }
       // lane holds S[n = 16*(NTW*wn + i) + l16][p = p0 + 16(2wp + ct) + 4lg .. +3]
       const int64_t so = (((int64_t)b * nc + c) * H + h) * (int64_t)(N * P) + p0;
@@ -330,7 +373,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     }
     // the other buffer was last read by the previous head, which every wave
     // finished before the previous barrier
-    commit(xnext);
+    commit(xnext, wnext);
     advance();
     __syncthreads();
   }
@@ -343,21 +386,27 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
 #define SHG_SHAPES(X) X(64, 128) X(128, 128) X(256, 128) X(64, 256) X(128, 256)
 
 bool chunk_state_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
-  if (f32_mma || !in_bf16 || d.P % 64 != 0) return false;
-#define SHG_MATCH(QQ, NN) if (d.Q == QQ && d.N == NN) return ShgCfg<QQ, NN>::lds_total + 8 * QQ <= 160 * 1024;
+  // bf16 inputs only (the fp32-operand instance widens exact bf16 values);
+  // room for one head's sums and dt rows, and (fp32 operands) the two
+  // weight tables
+  if (!in_bf16 || d.P % 64 != 0) return false;
+  const size_t extra = 8 * (size_t)d.Q * (f32_mma ? 2 : 1);
+#define SHG_MATCH(QQ, NN) if (d.Q == QQ && d.N == NN) return ShgCfg<QQ, NN>::lds_total + extra <= 160 * 1024;
   SHG_SHAPES(SHG_MATCH)
 #undef SHG_MATCH
   return false;
 }
 
-template <int Q, int N, bool FUSE, bool SBF16>
+template <int Q, int N, bool FUSE, bool SBF16, bool F32M>
 static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
                                   const float* dA_cumsum, const float* dt_raw, const float* A, float* dA_out,
                                   float* dt_out, void* states, hipStream_t stream) {
   using Cfg = ShgCfg<Q, N>;
-  auto kern = chunk_state_hg_kernel<Q, N, FUSE, SBF16>;
-  // with FUSE the block also holds the sums and dt rows of its heads in LDS
-  const int64_t cap = FUSE ? (int64_t)((160 * 1024 - Cfg::lds_total) / (8 * Q)) : (int64_t)1 << 30;
+  auto kern = chunk_state_hg_kernel<Q, N, FUSE, SBF16, F32M>;
+  // with FUSE the block also holds the sums and dt rows of its heads in LDS;
+  // with F32M the two weight tables
+  const size_t wts = F32M ? (size_t)8 * Q : 0;
+  const int64_t cap = FUSE ? (int64_t)((160 * 1024 - Cfg::lds_total - wts) / (8 * Q)) : (int64_t)1 << 30;
   const int npt = (int)(d.P / Cfg::PT);
   const int64_t hpg = d.H / d.G;
   const int64_t base = d.B * d.nc * d.G * npt;
@@ -367,7 +416,7 @@ static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, 
     HG = (int)(hpg / k);
     if (base * k >= device_cu_count()) break;
   }
-  const size_t lds = Cfg::lds_total + (FUSE ? (size_t)8 * Q * HG : 0);
+  const size_t lds = Cfg::lds_total + (FUSE ? (size_t)8 * Q * HG : 0) + wts;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -381,14 +430,28 @@ static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, 
   return hipGetLastError();
 }
 
+template <int Q, int N, bool FUSE>
+static hipError_t launch_shg_any(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
+                                 const float* dA_cumsum, const float* dt_raw, const float* A, float* dA_out,
+                                 float* dt_out, void* states, bool states_bf16, bool f32_mma, hipStream_t stream) {
+  if (f32_mma)
+    return states_bf16 ? launch_shg_inst<Q, N, FUSE, true, true>(d, x, Bm, dt_bhl, dA_cumsum, dt_raw, A, dA_out,
+                                                                  dt_out, states, stream)
+                       : launch_shg_inst<Q, N, FUSE, false, true>(d, x, Bm, dt_bhl, dA_cumsum, dt_raw, A, dA_out,
+                                                                   dt_out, states, stream);
+  return states_bf16 ? launch_shg_inst<Q, N, FUSE, true, false>(d, x, Bm, dt_bhl, dA_cumsum, dt_raw, A, dA_out,
+                                                                 dt_out, states, stream)
+                     : launch_shg_inst<Q, N, FUSE, false, false>(d, x, Bm, dt_bhl, dA_cumsum, dt_raw, A, dA_out,
+                                                                  dt_out, states, stream);
+}
+
 hipError_t launch_chunk_state_hg(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
-                                 const float* dA_cumsum, void* states, bool states_bf16, hipStream_t stream) {
+                                 const float* dA_cumsum, void* states, bool states_bf16, bool f32_mma,
+                                 hipStream_t stream) {
 #define SHG_LAUNCH(QQ, NN)                                                                                  \
   if (d.Q == QQ && d.N == NN)                                                                               \
-    return states_bf16 ? launch_shg_inst<QQ, NN, false, true>(d, x, Bm, dt_bhl, dA_cumsum, nullptr, nullptr, \
-                                                              nullptr, nullptr, states, stream)              \
-                       : launch_shg_inst<QQ, NN, false, false>(d, x, Bm, dt_bhl, dA_cumsum, nullptr, nullptr, \
-                                                               nullptr, nullptr, states, stream);
+    return launch_shg_any<QQ, NN, false>(d, x, Bm, dt_bhl, dA_cumsum, nullptr, nullptr, nullptr, nullptr,     \
+                                         states, states_bf16, f32_mma, stream);
   SHG_SHAPES(SHG_LAUNCH)
 #undef SHG_LAUNCH
   return hipErrorInvalidValue;
@@ -396,14 +459,11 @@ hipError_t launch_chunk_state_hg(const Dims& d, const void* x, const void* Bm, c
 
 hipError_t launch_chunk_state_cumsum_hg(const Dims& d, const void* x, const void* Bm, const float* dt,
                                         const float* A, float* dA_cumsum, float* dt_bhl, void* states,
-                                        bool states_bf16, hipStream_t stream) {
-#define SHG_LAUNCH(QQ, NN)                                                                                     \
-  if (d.Q == QQ && d.N == NN)                                                                                  \
-    return states_bf16                                                                                         \
-               ? launch_shg_inst<QQ, NN, true, true>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl, states, \
-                                                     stream)                                                   \
-               : launch_shg_inst<QQ, NN, true, false>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl,       \
-                                                      states, stream);
+                                        bool states_bf16, bool f32_mma, hipStream_t stream) {
+#define SHG_LAUNCH(QQ, NN)                                                                            \
+  if (d.Q == QQ && d.N == NN)                                                                         \
+    return launch_shg_any<QQ, NN, true>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl, states, \
+                                        states_bf16, f32_mma, stream);
   SHG_SHAPES(SHG_LAUNCH)
 #undef SHG_LAUNCH
   return hipErrorInvalidValue;

@@ -191,7 +191,7 @@ ssd_status ssd_chunk_cumsum_state(const ssd_shape* shape, const void* x, const v
   const bool bf = in == SSD_BF16, f32m = mma == SSD_MMA_F32, sbf = states_dtype == SSD_BF16;
   // the head-group chunk-state kernel computes the cumulative sums itself
   if (ssd::chunk_state_hg_supported(d, bf, f32m))
-    return from_hip(ssd::launch_chunk_state_cumsum_hg(d, x, Bm, dt, A, dA_cumsum, dt_bhl, states, sbf, s));
+    return from_hip(ssd::launch_chunk_state_cumsum_hg(d, x, Bm, dt, A, dA_cumsum, dt_bhl, states, sbf, f32m, s));
   SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA_cumsum, dt_bhl, s)));
   return from_hip(ssd::launch_chunk_state_any(d, x, Bm, bf, dt_bhl, dA_cumsum, states, sbf, f32m, s));
 }
@@ -344,7 +344,7 @@ ssd_status forward_run(const Dims& d, const void* x, const float* dt, const floa
   const bool sbf = !f32m;
   if (chunk_state_hg_supported(d, bf, f32m)) {
     // the head-group chunk-state kernel computes the cumulative sums itself
-    SSD_TRY(from_hip(launch_chunk_state_cumsum_hg(d, x, Bm, dt, A, dA, dtb, st, sbf, s)));
+    SSD_TRY(from_hip(launch_chunk_state_cumsum_hg(d, x, Bm, dt, A, dA, dtb, st, sbf, f32m, s)));
   } else {
     SSD_TRY(from_hip(launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
     SSD_TRY(from_hip(launch_chunk_state_any(d, x, Bm, bf, dtb, dA, st, sbf, f32m, s)));

@@ -41,18 +41,20 @@ hipError_t launch_chunk_state_any(const Dims& d, const void* x, const void* Bm, 
                                   const float* dt_bhl, const float* dA_cumsum, void* states, bool states_bf16,
                                   bool f32_mma, hipStream_t stream);
 
-// Head-group variant of the chunk states (bf16 inputs and operands,
-// (chunk, N) in {(64,128), (128,128), (256,128), (64,256), (128,256)}, P a multiple of 64); launch_chunk_state
+// Head-group variant of the chunk states (bf16 inputs; bf16 or, with
+// f32_mma, fp32 matrix operands; (chunk, N) in {(64,128), (128,128),
+// (256,128), (64,256), (128,256)}, P a multiple of 64); launch_chunk_state
 // picks it when supported.
 bool chunk_state_hg_supported(const Dims& d, bool in_bf16, bool f32_mma);
 hipError_t launch_chunk_state_hg(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
-                                 const float* dA_cumsum, void* states, bool states_bf16, hipStream_t stream);
+                                 const float* dA_cumsum, void* states, bool states_bf16, bool f32_mma,
+                                 hipStream_t stream);
 // The same kernel with the cumulative-sum step fused in front: it reads dt and
 // A, writes dA_cumsum and dt_bhl (bit-identical to launch_chunk_cumsum) and
 // the chunk states.  Same support as chunk_state_hg_supported.
 hipError_t launch_chunk_state_cumsum_hg(const Dims& d, const void* x, const void* Bm, const float* dt,
                                         const float* A, float* dA_cumsum, float* dt_bhl, void* states,
-                                        bool states_bf16, hipStream_t stream);
+                                        bool states_bf16, bool f32_mma, hipStream_t stream);
 
 hipError_t launch_state_passing(const Dims& d, const float* chunk_states, float* carried,
                                 const float* dA_cumsum, const float* initial_states,
@@ -80,14 +82,15 @@ hipError_t launch_state_fused(const Dims& d, const void* x, const void* Bm, cons
                               const float* dA_cumsum, const float* initial_states, void* carried, bool carried_bf16,
                               float* final_states, hipStream_t stream);
 
-// Head-group variant of the fused chunk output (bf16 inputs and operands,
-// (chunk, N) in {(128,64), (128,128), (128,256), (256,64), (256,128)}, P a multiple of 64);
+// Head-group variant of the fused chunk output (bf16 inputs; bf16 or, with
+// f32_mma, fp32 operands for M.X and C.H_in; (chunk, N) in {(128,64),
+// (128,128), (128,256), (256,64), (256,128)}, P a multiple of 64);
 // launch_chunk_scan picks it when supported.  `carried` holds fp32 values, or
 // bf16 bits (already rounded to nearest even) when carried_bf16 is set.
 bool chunk_scan_hg_supported(const Dims& d, bool in_bf16, bool f32_mma);
 hipError_t launch_chunk_scan_hg(const Dims& d, const void* x, const void* Bm, const void* Cm, bool in_bf16,
                                 const float* dt_bhl, const float* dA_cumsum, const void* carried, bool carried_bf16,
-                                const float* D, void* y, bool y_bf16, hipStream_t stream,
+                                const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream,
                                 const int* seq_start = nullptr);
 
 // `carried` holds fp32 values, or bf16 bits when carried_bf16 is set.

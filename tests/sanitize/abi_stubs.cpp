@@ -40,12 +40,12 @@ hipError_t launch_chunk_state_any(const Dims&, const void*, const void*, bool, c
                                   bool, hipStream_t) {
   reached("chunk_state_any");
 }
-hipError_t launch_chunk_state_hg(const Dims&, const void*, const void*, const float*, const float*, void*, bool,
+hipError_t launch_chunk_state_hg(const Dims&, const void*, const void*, const float*, const float*, void*, bool, bool,
                                  hipStream_t) {
   reached("chunk_state_hg");
 }
 hipError_t launch_chunk_state_cumsum_hg(const Dims&, const void*, const void*, const float*, const float*, float*,
-                                        float*, void*, bool, hipStream_t) {
+                                        float*, void*, bool, bool, hipStream_t) {
   reached("chunk_state_cumsum_hg");
 }
 hipError_t launch_state_passing(const Dims&, const float*, float*, const float*, const float*, float*, hipStream_t) {
@@ -64,7 +64,7 @@ hipError_t launch_state_fused(const Dims&, const void*, const void*, const float
   reached("state_fused");
 }
 hipError_t launch_chunk_scan_hg(const Dims&, const void*, const void*, const void*, bool, const float*, const float*,
-                                const void*, bool, const float*, void*, bool, hipStream_t, const int*) {
+                                const void*, bool, const float*, void*, bool, bool, hipStream_t, const int*) {
   reached("chunk_scan_hg");
 }
 hipError_t launch_chunk_scan(const Dims&, const void*, const void*, const void*, bool, const float*, const float*,
