@@ -51,13 +51,18 @@
 
 namespace ssd {
 
-constexpr int hg_threads(int q) { return q >= 256 ? 512 : 256; }
-
 template <int Q, int NK, int CT, bool F32M = false>
 struct HgCfg {
   static constexpr int QT = Q / 16;
-  static constexpr int NCW = QT / 2;  // compute waves: wave w owns row tiles w and QT-1-w
-  static constexpr int T = hg_threads(Q);
+  static constexpr int NPAIR = QT / 2;  // row-tile pairs: pair w holds row tiles w and QT-1-w
+  // SPLIT: waves per row-tile pair.  At Q = 128 with N >= 128 one block per
+  // compute unit is all the LDS allows, so the pair's column tiles are split
+  // over two waves (each builds the pair's decayed interaction fragments):
+  // eight waves per block instead of four, two per SIMD.
+  static constexpr int SPLIT = (Q == 128 && NK >= 4) ? 2 : 1;
+  static constexpr int NCW = NPAIR * SPLIT;  // compute waves
+  static constexpr int T = 64 * NCW;
+  static constexpr int CW = CT / SPLIT;      // column tiles per wave
   static constexpr int PT = CT * 16;
   static constexpr int N = NK * 32;   // this variant needs N == NK*32
   // Row pitches are 16 elements (8 dwords) past a multiple of 64 dwords: the
@@ -157,6 +162,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     else return f;
   };
   constexpr int QT = Cfg::QT, PT = Cfg::PT, N = Cfg::N, NPI = Cfg::NPI, XNP = Cfg::XNP, T = Cfg::T;
+  constexpr int CW = Cfg::CW, NPAIR = Cfg::NPAIR;
   static_assert(PT == 64, "the prefetch maps assume a 64-column slice");
   constexpr int NXB = Q * (PT / 8);          // x prefetch pieces (16 bytes: 8 columns of one token)
   // H prefetch pieces (16 bytes: 4 fp32 or 8 bf16 columns of one n)
@@ -233,7 +239,8 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // rb = QT-1-w at slot QT - js; the slots of a sub-tile pair (2k, 2k+1) are
   // therefore compile-time constants whatever the wave.
   const int wave = tid >> 6;
-  const int ra = wave, rb = QT - 1 - wave;
+  const int pair = Cfg::SPLIT == 1 ? wave : wave % NPAIR;  // the wave's row-tile pair
+  const int ra = pair, rb = QT - 1 - pair;
   f32x4_t cb[NSL];
 #pragma unroll
   for (int sl = 0; sl < NSL; ++sl) {
@@ -402,7 +409,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // upper sub-tile of an even tile, whose slot holds the other tile's values,
   // is zeroed outright; that select also keeps the register allocator from
   // copying the accumulators.)
-  auto diag_frag = [&](auto tsel_c, const int k, const int tile, f32x4_t (&acc)[CT], int l16, int lg, int sti) -> FragM {
+  auto diag_frag = [&](auto tsel_c, const int k, const int tile, f32x4_t (&acc)[CW], int l16, int lg, int sti) -> FragM {
     constexpr int TSEL = decltype(tsel_c)::value;
     const int i = 16 * tile + l16;  // the token this lane's interaction values and outputs belong to
     // G and dt of the lane's 8 tokens j = 32k + 16t + 4lg + r, read as vectors
@@ -415,7 +422,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     {
       const float e = fast_exp2(gi - gR);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) acc[ct] *= e;
+      for (int c2 = 0; c2 < CW; ++c2) acc[c2] *= e;
     }
     const float gj[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
     const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
@@ -438,13 +445,13 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // `ln` is the lane index laundered through an empty asm at the top of each
   // head iteration: lane-dependent addresses are recomputed per head instead
   // of being hoisted out of the head loop, where they would stay live.
-  auto steps = [&](const int ta, const int tb, f32x4_t (&acc0)[CT], f32x4_t (&acc1)[CT], int ln, int hn) {
+  auto steps = [&](const int ta, const int tb, f32x4_t (&acc0)[CW], f32x4_t (&acc1)[CW], int ln, int hn, int ctb) {
     const int l16 = ln & 15, lg = ln >> 4;
     const int Ua = ta >> 1, Ub = tb >> 1;
     const int sta = VARLEN ? Sts[16 * ta + l16] : -1, stb = VARLEN ? Sts[16 * tb + l16] : -1;
-    Frag xn[CT];
+    Frag xn[CW];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) xn[ct] = lds_frag_tr(cur.Xn + 16 * ct, XNP, ln);
+    for (int c2 = 0; c2 < CW; ++c2) xn[c2] = lds_frag_tr(cur.Xn + 16 * (ctb + c2), XNP, ln);
 #pragma unroll
     for (int k = 0; k < QT / 2; ++k) {
       if (k <= Ub) {
@@ -452,37 +459,38 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         // vector-memory issue is spread over the head instead of queued at
         // its start by all waves at once
         if (k < XPT) issue_xpiece(hn, k);
-        Frag xf[CT];
+        Frag xf[CW];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) xf[ct] = xn[ct];
+        for (int c2 = 0; c2 < CW; ++c2) xf[c2] = xn[c2];
         if (k + 1 < QT / 2) {
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) xn[ct] = lds_frag_tr(cur.Xn + 32 * (k + 1) * XNP + 16 * ct, XNP, ln);
+          for (int c2 = 0; c2 < CW; ++c2) xn[c2] = lds_frag_tr(cur.Xn + 32 * (k + 1) * XNP + 16 * (ctb + c2), XNP, ln);
         }
         if (k <= Ua) {
           FragM mfa;
           if (k < Ua) mfa = offdiag_frag(std::integral_constant<int, 0>{}, k, Ua, lg, sta);
           else mfa = diag_frag(std::integral_constant<int, 0>{}, k, ta, acc0, l16, lg, sta);
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) acc0[ct] = OpM::mma(to_m(xf[ct]), mfa, acc0[ct]);
+          for (int c2 = 0; c2 < CW; ++c2) acc0[c2] = OpM::mma(to_m(xf[c2]), mfa, acc0[c2]);
         }
         FragM mfb;
         if (k < Ub) mfb = offdiag_frag(std::integral_constant<int, 1>{}, k, Ub, lg, stb);
         else mfb = diag_frag(std::integral_constant<int, 1>{}, k, tb, acc1, l16, lg, stb);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc1[ct] = OpM::mma(to_m(xf[ct]), mfb, acc1[ct]);
+        for (int c2 = 0; c2 < CW; ++c2) acc1[c2] = OpM::mma(to_m(xf[c2]), mfb, acc1[c2]);
       }
     }
   };
   // skip connection and store of one row tile: y[i][16ct + 4lg .. +3]
-  auto store_tile = [&](const int tile, const f32x4_t (&acc)[CT], int h, float dsk, int ln) {
+  auto store_tile = [&](const int tile, const f32x4_t (&acc)[CW], int h, float dsk, int ln, int ctb) {
     const int l16 = ln & 15, lg = ln >> 4;
     const int i = 16 * tile + l16;
     if (RAGGED && i > rmax) return;
     const int64_t ybase = (tok0 * H + h) * (int64_t)P + a.p0;
-    uint2 w[CT];
+    uint2 w[CW];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
+    for (int c2 = 0; c2 < CW; ++c2) {
+      const int ct = ctb + c2;
       const int pc = 16 * ct + 4 * lg;
       const int off = i * HP + pc;
       float v[4];
@@ -490,10 +498,10 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       const float xr[4] = {bf16_bits_to_f32(xq.x & 0xffffu), bf16_bits_to_f32(xq.x >> 16),
                            bf16_bits_to_f32(xq.y & 0xffffu), bf16_bits_to_f32(xq.y >> 16)};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = acc[ct][r] + dsk * xr[r];
+      for (int r = 0; r < 4; ++r) v[r] = acc[c2][r] + dsk * xr[r];
       if constexpr (Y_BF16) {
-        w[ct].x = pack_bf16x2(v[0], v[1]);
-        w[ct].y = pack_bf16x2(v[2], v[3]);
+        w[c2].x = pack_bf16x2(v[0], v[1]);
+        w[c2].y = pack_bf16x2(v[2], v[3]);
       } else {
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + ybase + off) = make_float4(v[0], v[1], v[2], v[3]);
       }
@@ -501,9 +509,9 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     if constexpr (Y_BF16) {
       // column tiles paired (0,1), (2,3): one 16-byte store per pair and lane
 #pragma unroll
-      for (int cp = 0; cp < CT / 2; ++cp)
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.y) + ybase + i * HP + 32 * cp + pair_tiles_col(lg)) =
-            pair_tiles_16b(w[2 * cp], w[2 * cp + 1]);
+      for (int cp = 0; cp < CW / 2; ++cp)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.y) + ybase + i * HP + 16 * ctb + 32 * cp +
+                                  pair_tiles_col(lg)) = pair_tiles_16b(w[2 * cp], w[2 * cp + 1]);
     }
   };
 
@@ -530,7 +538,9 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     int wv = wave;
     asm volatile("" : "+v"(wv));
     wv = __builtin_amdgcn_readfirstlane(wv);
-    const int ta = wv, tb = QT - 1 - wv;
+    const int wpair = Cfg::SPLIT == 1 ? wv : wv % NPAIR;
+    const int ta = wpair, tb = QT - 1 - wpair;
+    const int ctb = Cfg::SPLIT == 1 ? 0 : CW * (wv / NPAIR);  // the wave's first column tile
     {
       const int l16 = ln & 15, lg = ln >> 4;
       // The output tiles are accumulated TRANSPOSED, Y^T = H^T C^T + X^T M^T
@@ -539,11 +549,11 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       // 8-byte store.  Carried-state term first, for both tiles at once (each
       // H fragment read once per wave), scaled by exp(G_R) now and by
       // exp(G_i - G_R) at the tile's diagonal step.
-      f32x4_t acc0[CT], acc1[CT];
+      f32x4_t acc0[CW], acc1[CW];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        acc0[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        acc1[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int c2 = 0; c2 < CW; ++c2) {
+        acc0[c2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc1[c2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
@@ -553,22 +563,22 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
           // one fp32 H fragment at a time (slots 4t + r <-> n = 32s + 16t +
           // 4lg + r, as the C fragment)
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            const int p = 16 * ct + l16;
+          for (int c2 = 0; c2 < CW; ++c2) {
+            const int p = 16 * (ctb + c2) + l16;
             FragM hf;
             hf.lo = *reinterpret_cast<const float4*>(cur.Ht + ht_pos<N>(32 * s + 4 * lg, p));
             hf.hi = *reinterpret_cast<const float4*>(cur.Ht + ht_pos<N>(32 * s + 16 + 4 * lg, p));
-            acc0[ct] = OpM::mma(hf, ca0, acc0[ct]);
-            acc1[ct] = OpM::mma(hf, ca1, acc1[ct]);
+            acc0[c2] = OpM::mma(hf, ca0, acc0[c2]);
+            acc1[c2] = OpM::mma(hf, ca1, acc1[c2]);
           }
         } else {
-          Frag hf[CT];
+          Frag hf[CW];
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) hf[ct] = lds_frag_tr(cur.Hn + 32 * s * XNP + 16 * ct, XNP, ln);
+          for (int c2 = 0; c2 < CW; ++c2) hf[c2] = lds_frag_tr(cur.Hn + 32 * s * XNP + 16 * (ctb + c2), XNP, ln);
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            acc0[ct] = OpM::mma(hf[ct], ca0, acc0[ct]);
-            acc1[ct] = OpM::mma(hf[ct], ca1, acc1[ct]);
+          for (int c2 = 0; c2 < CW; ++c2) {
+            acc0[c2] = OpM::mma(hf[c2], ca0, acc0[c2]);
+            acc1[c2] = OpM::mma(hf[c2], ca1, acc1[c2]);
           }
         }
       }
@@ -581,21 +591,21 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         if (Sts[16 * tb + l16c] >= 0) e1 = 0.f;
       }
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        acc0[ct] *= e0;
-        acc1[ct] *= e1;
+      for (int c2 = 0; c2 < CW; ++c2) {
+        acc0[c2] *= e0;
+        acc1[c2] *= e1;
       }
       // the waves whose steps carry both tiles most often take priority
       // over their SIMD neighbours (same MFMA count, denser chains)
-      if (wv >= QT / 4) __builtin_amdgcn_s_setprio(2);
-      steps(ta, tb, acc0, acc1, ln, hn);
+      if (wpair >= QT / 4) __builtin_amdgcn_s_setprio(2);
+      steps(ta, tb, acc0, acc1, ln, hn, ctb);
       __builtin_amdgcn_s_setprio(0);
       // pieces a short step loop did not issue
 #pragma unroll
       for (int k = 0; k < XPT; ++k)
         if (k > (tb >> 1)) issue_xpiece(hn, k);
-      store_tile(ta, acc0, h, dsk, ln);
-      store_tile(tb, acc1, h, dsk, ln);
+      store_tile(ta, acc0, h, dsk, ln, ctb);
+      store_tile(tb, acc1, h, dsk, ln, ctb);
     }
     if constexpr (DB) {
       // the other buffer was last read by the previous head, which every wave
@@ -614,7 +624,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 // the output stores would make the compiler's memory-counter waits for the
 // prefetched loads conservative (they would also wait for the stores).
 template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED, bool VARLEN, bool F32M>
-__global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
+__global__ __launch_bounds__((HgCfg<Q, NK, CT, F32M>::T)) void chunk_scan_hg_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, const void* __restrict__ Cm,
     const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const void* __restrict__ carried,
     const float* __restrict__ D, void* __restrict__ y, int L, int H, int P, int G, int nc, int HG,
@@ -639,7 +649,7 @@ __global__ __launch_bounds__(hg_threads(Q)) void chunk_scan_hg_kernel(
   a.c = rest % nc;
   a.b = rest / nc;
   a.hbase = a.g * (H / G) + hgi * HG;
-  a.p0 = pt * HgCfg<Q, NK, CT>::PT;
+  a.p0 = pt * HgCfg<Q, NK, CT, F32M>::PT;
   a.tok0 = (int64_t)a.b * L + (int64_t)a.c * Q;
   hg_body<Q, NK, CT, H_BF16, Y_BF16, RAGGED, VARLEN, F32M>(a, hg_smem, threadIdx.x);
 }
