@@ -223,10 +223,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void state_fused_kernel(
     commit(st);
     const float gl = GD2 ? st.g.glast : g1.glast;  // G_{Q-1} of chunk c
     __syncthreads();
-    issue_b(c + 1 < nc ? c + 1 : nc - 1);
-    issue_x(st, c + 2 < nc ? c + 2 : nc - 1);
-    __builtin_amdgcn_sched_barrier(0);
-    store_carried(c);
     int ln = lane;
     asm volatile("" : "+v"(ln));
     f32x4_t acc[RT][2];
@@ -234,8 +230,21 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void state_fused_kernel(
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll KU
-    for (int kk = 0; kk < Q / 32; ++kk) {
+    // The refills (B of chunk c + 1 with its G and dt, x of chunk c + 2) and
+    // the carried stores of chunk c are spread over the contraction steps
+    // instead of queued by every wave at once after the barrier (their
+    // vector-memory issue stalled the waves for about as long as the
+    // matrix work).  Loads go first, so each wait on the in-order memory
+    // counter at the next staging covers its own rows, not the stores.
+    constexpr int KS = Q / 32;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if (kk == 0) issue_b(c + 1 < nc ? c + 1 : nc - 1);
+      if (kk == (KS > 1 ? 1 : 0)) issue_x(st, c + 2 < nc ? c + 2 : nc - 1);
+      if (kk == KS - 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        store_carried(c);
+      }
       Frag xf[2], bf[RT];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) xf[ct] = lds_frag_tr(Xn + 32 * kk * XP + 32 * wp + 16 * ct, XP, ln);
