@@ -9,18 +9,17 @@
 // g_t = dL/dh_t satisfies g_t = C_t dy_t^T + r_{t+1} g_{t+1}: read backwards in
 // time that is again this recurrence, with the decay of each step taken from
 // dt_{t+1} (none at the last token), input scale 1, B-role C, x-role dy and
-// initial state dfinal.  So every product below is a chunked forward run by the
-// existing kernels (fp32 operands and fp32 matrix cores), and the glue here
-// only reverses, widens, expands and combines:
-//   (0) forward:                      y0_t = C_t^T h_t, carried states h
-//   (1) adjoint, reversed:            y1 = B_t^T g_t            -> dx = dt y1 + D dy;  final = g_0
-//   (2) adjoint transposed, reversed: y2 = g_t x_t  (N-vector)  -> dB, beta_t = B_t . g_t x_t
-//   (3) forward transposed:           y3 = h_t dy_t (N-vector)  -> dC
-// The reversed passes run over nc*Q steps, the sequence padded at its far end
-// (zero inputs, no decay), so that their chunk edges fall on the forward's.
-// The transposed passes need no state computation of their own: their carried
-// states are the transposes of those of (0) and (1).  Operands are fp32, or
-// bf16 (rounded to nearest even) when the matrix cores take bf16.
+// initial state dfinal.  So the products below are chunked forward passes of
+// the existing kernels, plus one per-chunk kernel for dB and dC
+// (bwd_dbc.hip), and the glue here only reverses, combines and reduces:
+//   (0) forward:            y0_t = C_t^T h_t, carried states h
+//   (1) adjoint, reversed:  y1_t = B_t^T g_t, carried states g
+//                           -> dx = dt y1 + D dy,  beta_t = B_t . g_t x_t = y1_t . x_t,  final = g_0
+//   (2) dB, dC per (chunk, group) from x, dy, B, C and the carried states of
+//       (0) and (1), summed over the group's heads.
+// The reversed pass runs over nc*Q steps, the sequence padded at its far end
+// (zero inputs, no decay), so that its chunk edges fall on the forward's.
+// Matrix operands are bf16 (rounded to nearest even) or fp32.
 // The log-decay gradient needs q_t = <g_t, h_t>, since
 //   dL/d(dt_t A) = r_t <g_t, h_{t-1}> = q_t - dt_t beta_t,
 //   ddt_t = A dL/d(dt_t A) + beta_t,  dA = sum_t dt_t dL/d(dt_t A).
@@ -93,45 +92,39 @@ __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, float 
   if (i < n) p[i] = v;
 }
 
-// Per matrix m: out[m][c][r] = in[m][r][c] for R x C matrices (R, C multiples
-// of TS), through a TS x (TS+1) LDS tile; one 256-thread block per tile, rows
-// read and written as whole TS-element segments.
-template <int TS>
-__global__ __launch_bounds__(256) void transpose_tiles_kernel(const float* __restrict__ in, float* __restrict__ out,
-                                                              int R, int C) {
-  __shared__ float tile[TS][TS + 1];
-  constexpr int RPP = 256 / TS;  // rows per pass
-  const int tr = R / TS, tc = C / TS;
-  const int64_t m = blockIdx.x / (tr * tc);
-  const int rem = (int)(blockIdx.x - m * tr * tc);
-  const int r0 = TS * (rem / tc), c0 = TS * (rem % tc);
-  const int i = threadIdx.x / TS, j = threadIdx.x % TS;
-  const int64_t base = m * R * C;
-#pragma unroll
-  for (int k = 0; k < TS; k += RPP) tile[i + k][j] = in[base + (int64_t)(r0 + i + k) * C + c0 + j];
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < TS; k += RPP) out[base + (int64_t)(c0 + i + k) * R + r0 + j] = tile[j][i + k];
-}
-
-// anc[b, h, k] = <g_{kQ}, h_{kQ-1}>: for k >= 1 the adjoint's carried state
-// entering its reversed chunk nc-k and the forward's carried state entering
-// chunk k; for k = 0 the adjoint's final state (g_0) and the initial state
-// (zero when absent).  One block per (b, k, h); states are [B, nc, H, N*P].
+// anc[b, h, k] = <g_{kQ}, h_{kQ-1}> for k < nc: for k >= 1 the adjoint's
+// carried state entering its reversed chunk nc-k and the forward's carried
+// state entering chunk k; for k = 0 the adjoint's final state (g_0) and the
+// initial state (zero when absent).  anc[b, h, nc] = <dL/dfinal, final state>
+// (zero when dfinal is absent).  One block per (b, k, h); states are
+// [B, nc, H, N*P], anc is [B, H, nc+1].
 __global__ __launch_bounds__(256) void anchor_dot_kernel(const float* __restrict__ fwd_carried,
+                                                         const float* __restrict__ fwd_final,
                                                          const float* __restrict__ adj_carried,
                                                          const float* __restrict__ adj_final,
-                                                         const float* __restrict__ h0, float* __restrict__ anc, int H,
-                                                         int nc, int64_t NP) {
+                                                         const float* __restrict__ h0,
+                                                         const float* __restrict__ dfinal, float* __restrict__ anc,
+                                                         int H, int nc, int64_t NP) {
   __shared__ float red[256];
   const int tid = threadIdx.x;
   const int h = blockIdx.x % H;
-  const int k = (blockIdx.x / H) % nc;
-  const int64_t b = blockIdx.x / H / nc;
-  const float* gp = k == 0 ? adj_final + (b * H + h) * NP : adj_carried + ((b * nc + (nc - k)) * H + h) * NP;
-  const float* hp = k == 0 ? (h0 ? h0 + (b * H + h) * NP : nullptr) : fwd_carried + ((b * nc + k) * H + h) * NP;
+  const int k = (blockIdx.x / H) % (nc + 1);
+  const int64_t b = blockIdx.x / H / (nc + 1);
+  const int64_t bh = (b * H + h) * NP;
+  const float* gp;
+  const float* hp;
+  if (k == 0) {
+    gp = adj_final + bh;
+    hp = h0 ? h0 + bh : nullptr;
+  } else if (k == nc) {
+    gp = dfinal ? dfinal + bh : nullptr;
+    hp = fwd_final + bh;
+  } else {
+    gp = adj_carried + ((b * nc + (nc - k)) * H + h) * NP;
+    hp = fwd_carried + ((b * nc + k) * H + h) * NP;
+  }
   float sum = 0.f;
-  if (hp)
+  if (gp && hp)
     for (int64_t e = 4 * tid; e < NP; e += 4 * 256) {
       const float4 gv = *reinterpret_cast<const float4*>(gp + e);
       const float4 hv = *reinterpret_cast<const float4*>(hp + e);
@@ -143,7 +136,7 @@ __global__ __launch_bounds__(256) void anchor_dot_kernel(const float* __restrict
     if (tid < w) red[tid] += red[tid + w];
     __syncthreads();
   }
-  if (tid == 0) anc[(b * H + h) * nc + k] = red[0];
+  if (tid == 0) anc[(b * H + h) * (nc + 1) + k] = red[0];
 }
 
 // 4 consecutive elements (16-byte aligned group) as fp32
@@ -156,14 +149,14 @@ __device__ __forceinline__ float4 load4_f32(const void* base, int64_t elem, bool
   return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
 }
 
-// Per (b, t, h): dx, beta_t = B_t . (g_t x_t), v_t = dy_t . y0_t, u_t = dy_t . x_t.
-// 16 lanes per (b, t, h) row, 4-element groups (P, N multiples of 16), four
-// rows per wave; y1 and y2 are in reversed time over Lp steps.
+// Per (b, t, h): dx, beta_t = y1_t . x_t (= B_t . g_t x_t), v_t = dy_t . y0_t,
+// u_t = dy_t . x_t.  16 lanes per (b, t, h) row, 4-element groups (P a
+// multiple of 16), four rows per wave; y1 is in reversed time over Lp steps.
 __global__ __launch_bounds__(256) void combine_token_kernel(
-    const void* __restrict__ dy, int dy_bf16, const void* __restrict__ x, const void* __restrict__ Bm, int in_bf16,
-    const float* __restrict__ dt, const float* __restrict__ D, const float* __restrict__ y0,
-    const float* __restrict__ y1, const float* __restrict__ y2, float* __restrict__ dx, float* __restrict__ beta,
-    float* __restrict__ v, float* __restrict__ u, int L, int Lp, int H, int P, int N, int G, int64_t nrows) {
+    const void* __restrict__ dy, int dy_bf16, const void* __restrict__ x, int in_bf16, const float* __restrict__ dt,
+    const float* __restrict__ D, const float* __restrict__ y0, const float* __restrict__ y1, float* __restrict__ dx,
+    float* __restrict__ beta, float* __restrict__ v, float* __restrict__ u, int L, int Lp, int H, int P,
+    int64_t nrows) {
   const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 16) + (threadIdx.x >> 4);  // (b * L + t) * H + h
   const int l16 = threadIdx.x & 15;
   if (row >= nrows) return;  // whole 16-lane groups leave together
@@ -171,7 +164,6 @@ __global__ __launch_bounds__(256) void combine_token_kernel(
   const int64_t bt = row / H;
   const int t = (int)(bt % L);
   const int64_t b = bt / L;
-  const int g = h / (H / G);
   const int64_t rrow = (b * Lp + (Lp - 1 - t)) * H + h;  // the same token in reversed time
   const float dtv = dt[row], dh = D[h];
   float sv = 0.f, su = 0.f, sb = 0.f;
@@ -184,11 +176,7 @@ __global__ __launch_bounds__(256) void combine_token_kernel(
                     fmaf(dtv, a1.w, dh * dyv.w));
     sv = fmaf(dyv.x, a0.x, fmaf(dyv.y, a0.y, fmaf(dyv.z, a0.z, fmaf(dyv.w, a0.w, sv))));
     su = fmaf(dyv.x, xv.x, fmaf(dyv.y, xv.y, fmaf(dyv.z, xv.z, fmaf(dyv.w, xv.w, su))));
-  }
-  for (int n = 4 * l16; n < N; n += 64) {
-    const float4 bv = load4_f32(Bm, (bt * G + g) * N + n, in_bf16 != 0);
-    const float4 a2 = *reinterpret_cast<const float4*>(y2 + rrow * N + n);
-    sb = fmaf(bv.x, a2.x, fmaf(bv.y, a2.y, fmaf(bv.z, a2.z, fmaf(bv.w, a2.w, sb))));
+    sb = fmaf(a1.x, xv.x, fmaf(a1.y, xv.y, fmaf(a1.z, xv.z, fmaf(a1.w, xv.w, sb))));
   }
 #pragma unroll
   for (int off = 8; off > 0; off >>= 1) {
@@ -203,34 +191,16 @@ __global__ __launch_bounds__(256) void combine_token_kernel(
   }
 }
 
-// dB[b,t,g,n] = sum_{h in g} dt[b,t,h] y2[b, Lp-1-t, h, n];  dC[b,t,g,n] = sum_{h in g} y3[b,t,h,n]
-__global__ __launch_bounds__(256) void combine_group_kernel(const float* __restrict__ dt, const float* __restrict__ y2,
-                                                            const float* __restrict__ y3, float* __restrict__ dB,
-                                                            float* __restrict__ dC, int L, int Lp, int H, int N,
-                                                            int G, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // element of [B,L,G,N]
-  if (i >= n) return;
-  const int e = (int)(i % N);
-  int64_t r = i / N;
-  const int g = (int)(r % G);
-  const int64_t bt = r / G;
-  const int t = (int)(bt % L);
-  const int64_t b = bt / L;
-  const int hpg = H / G;
-  float sb = 0.f, sc = 0.f;
-  for (int k = 0; k < hpg; ++k) {
-    const int h = g * hpg + k;
-    sb = fmaf(dt[bt * H + h], y2[((b * Lp + (Lp - 1 - t)) * H + h) * N + e], sb);
-    sc += y3[(bt * H + h) * N + e];
-  }
-  dB[i] = sb;
-  dC[i] = sc;
-}
-
-// One wave per (b, h, chunk k): q over the chunk's tokens from its anchor,
-//   q_{t0} = r_{t0} anc + dt_{t0} beta_{t0},  q_t = q_{t-1} - v_{t-1} + dt_t beta_t,
-// as a wave prefix sum (each lane a run of up to Q/64 tokens); then ddt and the
-// chunk's shares of dA and dD.
+// One wave per (b, h, chunk k): q over the chunk's tokens t0 .. te from its
+// anchor,
+//   q_{t0} = r_{t0} anc_k + dt_{t0} beta_{t0},  q_t = q_{t-1} - v_{t-1} + dt_t beta_t,
+// as a wave prefix sum (each lane a run of up to Q/64 tokens).  q at the last
+// token is also known exactly from the next anchor, q_te = v_te + r_{te+1}
+// anc_{k+1} (no decay after the sequence's last token, where anc_nc pairs
+// dL/dfinal with the final state); the mismatch of the prefix sum there is
+// the rounding it piled up, spread back linearly over the chunk (each token
+// then leans on the nearer exact end).  Then ddt and the chunk's shares of dA
+// and dD.
 constexpr int kBwdMaxPer = 4;  // Q <= 256
 __global__ __launch_bounds__(256) void chunk_grad_kernel(const float* __restrict__ dt, const float* __restrict__ A,
                                                          const float* __restrict__ beta, const float* __restrict__ v,
@@ -246,9 +216,10 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(const float* __restrict
   const int h = (int)(bh % H);
   const int64_t b = bh / H;
   const float a = A[h];
-  const int t0 = k * Q, t1 = min(L, t0 + Q);
+  const int t0 = k * Q, t1 = min(L, t0 + Q), te = t1 - 1;
   const int per = (Q + 63) / 64;
   auto at = [&](int t) -> int64_t { return (b * L + t) * H + h; };
+  const float* ak = anc + bh * (nc + 1) + k;
   float z[kBwdMaxPer], dtv[kBwdMaxPer], be[kBwdMaxPer];
   float run = 0.f;
 #pragma unroll
@@ -258,7 +229,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(const float* __restrict
     if (j < per && t < t1) {
       dtv[j] = dt[at(t)];
       be[j] = beta[at(t)];
-      z[j] = t == t0 ? fmaf(expf(dtv[j] * a), anc[w], dtv[j] * be[j]) : dtv[j] * be[j] - v[at(t - 1)];
+      z[j] = t == t0 ? fmaf(expf(dtv[j] * a), ak[0], dtv[j] * be[j]) : dtv[j] * be[j] - v[at(t - 1)];
     }
     run += z[j];
     z[j] = run;  // inclusive prefix within the lane's run
@@ -271,12 +242,17 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(const float* __restrict
     if (lane >= off) incl += o;
   }
   const float excl = incl - run;
+  const float total = __shfl(incl, 63, 64);  // the prefix sum's q at te
+  const float r_next = k + 1 < nc ? expf(dt[at(t1)] * a) : 1.f;
+  const float q_end = fmaf(r_next, ak[1], v[at(te)]);
+  const float corr = q_end - total;
+  const float inv_span = te > t0 ? 1.f / (float)(te - t0) : 0.f;
   float sa = 0.f, sd = 0.f;
 #pragma unroll
   for (int j = 0; j < kBwdMaxPer; ++j) {
     const int t = t0 + lane * per + j;
     if (j < per && t < t1) {
-      const float q = excl + z[j];
+      const float q = fmaf((float)(t - t0) * inv_span, corr, excl + z[j]);
       const float dla = q - dtv[j] * be[j];
       ddt[at(t)] = fmaf(a, dla, be[j]);
       sa = fmaf(dtv[j], dla, sa);
@@ -330,14 +306,11 @@ size_t ru(size_t v) { return (v + 255) / 256 * 256; }
 // Workspace pieces, in order; operand copies are sized for fp32 (bf16 copies
 // use the first half).  Forward time: L tokens; reversed: Lp = nc*Q steps.
 enum BwdBuf {
-  kXo, kBo, kCo, kDyo, kBExp,                         // forward-time operands
-  kDyRev, kXRev, kBRev, kCRev, kCExpRev, kDtRev,      // reversed operands
-  kOnes, kZeroD,
-  kY0, kDA0, kDt0, kSt0,                              // (0)
-  kDA1, kDt1, kSt1, kY1, kFin1,                       // (1)
-  kSt2, kY2,                                          // (2)
-  kSt3, kY3,                                          // (3)
-  kAnc, kBeta, kV, kU, kDAp, kDDp, kNumBwd
+  kDyRev, kBRev, kCRev, kDtRev, kOnes, kZeroD,  // reversed operands
+  kY0, kDA0, kDt0, kSt0, kFin0,                 // (0)
+  kDA1, kDt1, kSt1, kY1, kFin1,                 // (1)
+  kU,                                           // (2)
+  kAnc, kBeta, kV, kUdot, kDAp, kDDp, kNumBwd
 };
 
 struct BwdLayout {
@@ -349,23 +322,19 @@ BwdLayout bwd_layout(const Dims& d) {
   const size_t f = sizeof(float), B = d.B, L = d.L, Lp = d.nc * d.Q, H = d.H, P = d.P, N = d.N, G = d.G;
   const size_t chunk_q = f * B * H * d.nc * d.Q, states = f * B * d.nc * H * N * P, bhnp = f * B * H * N * P;
   size_t sz[kNumBwd] = {};
-  sz[kXo] = sz[kDyo] = f * B * L * H * P;
-  sz[kBo] = sz[kCo] = f * B * L * G * N;
-  sz[kBExp] = f * B * L * H * N;
-  sz[kDyRev] = sz[kXRev] = f * B * Lp * H * P;
+  sz[kDyRev] = f * B * Lp * H * P;
   sz[kBRev] = sz[kCRev] = f * B * Lp * G * N;
-  sz[kCExpRev] = f * B * Lp * H * N;
   sz[kDtRev] = f * B * Lp * H;
   sz[kOnes] = sz[kDA0] = sz[kDt0] = sz[kDA1] = sz[kDt1] = chunk_q;
   sz[kZeroD] = f * H;
-  sz[kFin1] = bhnp;
-  sz[kSt0] = sz[kSt1] = sz[kSt2] = sz[kSt3] = states;
+  sz[kFin0] = sz[kFin1] = bhnp;
+  sz[kSt0] = sz[kSt1] = states;
   sz[kY0] = f * B * L * H * P;
   sz[kY1] = f * B * Lp * H * P;
-  sz[kY2] = f * B * Lp * H * N;
-  sz[kY3] = f * B * L * H * N;
-  sz[kBeta] = sz[kV] = sz[kU] = f * B * L * H;
-  sz[kAnc] = sz[kDAp] = sz[kDDp] = f * B * H * d.nc;
+  sz[kU] = bwd_dbc_u_bytes(d);
+  sz[kBeta] = sz[kV] = sz[kUdot] = f * B * L * H;
+  sz[kDAp] = sz[kDDp] = f * B * H * d.nc;
+  sz[kAnc] = f * B * H * (d.nc + 1);
   BwdLayout w;
   size_t o = 0;
   for (int i = 0; i < kNumBwd; ++i) {
@@ -395,20 +364,17 @@ hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const 
   auto F = [&](int k) { return reinterpret_cast<float*>(base + w.off[k]); };
   auto V = [&](int k) { return static_cast<void*>(base + w.off[k]); };
   const int L = (int)d.L, Lp = (int)(d.nc * d.Q), H = (int)d.H, P = (int)d.P, N = (int)d.N, G = (int)d.G;
-  // the reversed passes: Lp steps (whole chunks); the transposed ones: P and N
-  // swapped, one group per head
+  if (!bwd_dbc_supported(d)) return hipErrorInvalidValue;
+  // the reversed pass: Lp steps (whole chunks)
   Dims dR = d;
   dR.L = Lp;
-  Dims dT = d;
-  dT.N = d.P;
-  dT.P = d.N;
-  dT.G = d.H;
-  Dims dRT = dT;
-  dRT.L = Lp;
 
-  // ---- matrix operands in the operand type: the caller's arrays where they
-  // already have it, else converted; reversed and per-head copies always
-  const bool op_bf16 = !f32_mma;
+  // ---- operands of the reversed pass (reversed copies of dy, C and B): bf16
+  // with bf16 matrix operands (rounded there anyway), and with fp32 operands
+  // when x, B, C and dy all arrive as bf16 (the copies are then exact, and the
+  // chunk kernels take their fp32-operand head-group instances); fp32
+  // otherwise.  The forward pass reads the caller's arrays as they are.
+  const bool op_bf16 = !f32_mma || (in_bf16 && dy_bf16);
   auto gather = [&](const void* src, int src_bf16, int k, int Lout, int KO, int KI, int E, int reverse) {
     if (op_bf16)
       hipLaunchKernelGGL(gather_rows_kernel<true>, dim3((unsigned)(d.B * Lout)), dim3(256), 0, s, src, src_bf16, V(k),
@@ -419,16 +385,9 @@ hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const 
     return static_cast<const void*>(V(k));
   };
   const int ib = in_bf16 ? 1 : 0, db = dy_bf16 ? 1 : 0;
-  const void* xo = in_bf16 == op_bf16 ? x : gather(x, ib, kXo, L, H, H, P, 0);
-  const void* Bo = in_bf16 == op_bf16 ? Bm : gather(Bm, ib, kBo, L, G, G, N, 0);
-  const void* Co = in_bf16 == op_bf16 ? Cm : gather(Cm, ib, kCo, L, G, G, N, 0);
-  const void* dyo = dy_bf16 == op_bf16 ? dy : gather(dy, db, kDyo, L, H, H, P, 0);
-  const void* BExp = gather(Bm, ib, kBExp, L, H, G, N, 0);
   const void* DyRev = gather(dy, db, kDyRev, Lp, H, H, P, 1);
-  const void* XRev = gather(x, ib, kXRev, Lp, H, H, P, 1);
   const void* BRev = gather(Bm, ib, kBRev, Lp, G, G, N, 1);
   const void* CRev = gather(Cm, ib, kCRev, Lp, G, G, N, 1);
-  const void* CExpRev = gather(Cm, ib, kCExpRev, Lp, H, G, N, 1);
   const int64_t nblh = d.B * d.L * d.H, rblh = d.B * Lp * d.H;
   hipLaunchKernelGGL(shift_reverse_dt_kernel, dim3(nblocks(rblh)), dim3(256), 0, s, dt, F(kDtRev), L, Lp, H, rblh);
   const int64_t nq = d.B * d.H * d.nc * d.Q;
@@ -438,9 +397,9 @@ hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const 
 
   // ---- (0) forward: y0 = C^T h (no skip term), fp32 carried states
   BWD_TRY(launch_chunk_cumsum(d, dt, A, F(kDA0), F(kDt0), s));
-  BWD_TRY(launch_chunk_state(d, xo, Bo, op_bf16, F(kDt0), F(kDA0), F(kSt0), f32_mma, s));
-  BWD_TRY(launch_state_passing(d, F(kSt0), F(kSt0), F(kDA0), initial_states, nullptr, s));
-  BWD_TRY(launch_chunk_scan(d, xo, Bo, Co, op_bf16, F(kDt0), F(kDA0), F(kSt0), false, F(kZeroD), F(kY0), false,
+  BWD_TRY(launch_chunk_state(d, x, Bm, in_bf16, F(kDt0), F(kDA0), F(kSt0), f32_mma, s));
+  BWD_TRY(launch_state_passing(d, F(kSt0), F(kSt0), F(kDA0), initial_states, F(kFin0), s));
+  BWD_TRY(launch_chunk_scan(d, x, Bm, Cm, in_bf16, F(kDt0), F(kDA0), F(kSt0), false, F(kZeroD), F(kY0), false,
                             f32_mma, s));
 
   // ---- (1) adjoint in reversed time: decay from the shifted dt, input scale 1
@@ -450,37 +409,17 @@ hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const 
   BWD_TRY(launch_chunk_scan(dR, DyRev, CRev, BRev, op_bf16, F(kOnes), F(kDA1), F(kSt1), false, F(kZeroD), F(kY1),
                             false, f32_mma, s));
 
-  // ---- (2) adjoint transposed (state P x N per head: x-role C, B-role dy, C-role x);
-  //      its carried states are those of (1), transposed
-  const int64_t nmat = d.B * d.nc * d.H;
-  auto transpose = [&](const float* src, float* dst) {
-    if (d.N % 32 == 0 && d.P % 32 == 0)
-      hipLaunchKernelGGL(transpose_tiles_kernel<32>, dim3((unsigned)(nmat * (d.N / 32) * (d.P / 32))), dim3(256), 0,
-                         s, src, dst, N, P);
-    else
-      hipLaunchKernelGGL(transpose_tiles_kernel<16>, dim3((unsigned)(nmat * (d.N / 16) * (d.P / 16))), dim3(256), 0,
-                         s, src, dst, N, P);
-  };
-  transpose(F(kSt1), F(kSt2));
-  BWD_TRY(launch_chunk_scan(dRT, CExpRev, DyRev, XRev, op_bf16, F(kOnes), F(kDA1), F(kSt2), false, F(kZeroD),
-                            F(kY2), false, f32_mma, s));
-
-  // ---- (3) forward transposed (x-role B, B-role x, C-role dy): y3_t = h_t dy_t;
-  //      its carried states are those of (0), transposed
-  transpose(F(kSt0), F(kSt3));
-  BWD_TRY(launch_chunk_scan(dT, BExp, xo, dyo, op_bf16, F(kDt0), F(kDA0), F(kSt3), false, F(kZeroD), F(kY3), false,
-                            f32_mma, s));
+  // ---- (2) dB and dC per (chunk, group)
+  BWD_TRY(launch_bwd_dbc(d, x, in_bf16, dy, dy_bf16, Bm, Cm, in_bf16, F(kDA0), F(kDt0), F(kSt0), F(kSt1), A, F(kU),
+                         dB, dC, f32_mma, s));
 
   // ---- combine
-  hipLaunchKernelGGL(anchor_dot_kernel, dim3((unsigned)(d.B * d.nc * d.H)), dim3(256), 0, s, F(kSt0), F(kSt1),
-                     F(kFin1), initial_states, F(kAnc), H, (int)d.nc, d.N * d.P);
-  hipLaunchKernelGGL(combine_token_kernel, dim3(nblocks(nblh, 16)), dim3(256), 0, s, dy, db, x, Bm, ib, dt, D,
-                     F(kY0), F(kY1), F(kY2), dx, F(kBeta), F(kV), F(kU), L, Lp, H, P, N, G, nblh);
-  const int64_t nbgn = d.B * d.L * d.G * d.N;
-  hipLaunchKernelGGL(combine_group_kernel, dim3(nblocks(nbgn)), dim3(256), 0, s, dt, F(kY2), F(kY3), dB, dC, L, Lp,
-                     H, N, G, nbgn);
+  hipLaunchKernelGGL(anchor_dot_kernel, dim3((unsigned)(d.B * (d.nc + 1) * d.H)), dim3(256), 0, s, F(kSt0), F(kFin0),
+                     F(kSt1), F(kFin1), initial_states, dfinal, F(kAnc), H, (int)d.nc, d.N * d.P);
+  hipLaunchKernelGGL(combine_token_kernel, dim3(nblocks(nblh, 16)), dim3(256), 0, s, dy, db, x, ib, dt, D, F(kY0),
+                     F(kY1), dx, F(kBeta), F(kV), F(kUdot), L, Lp, H, P, nblh);
   const int64_t nw = d.B * d.H * d.nc;
-  hipLaunchKernelGGL(chunk_grad_kernel, dim3(nblocks(nw, 4)), dim3(256), 0, s, dt, A, F(kBeta), F(kV), F(kU),
+  hipLaunchKernelGGL(chunk_grad_kernel, dim3(nblocks(nw, 4)), dim3(256), 0, s, dt, A, F(kBeta), F(kV), F(kUdot),
                      F(kAnc), ddt, F(kDAp), F(kDDp), L, H, (int)d.Q, (int)d.nc, nw);
   const int64_t nnp = d.B * d.H * d.N * d.P;
   if (dinit)

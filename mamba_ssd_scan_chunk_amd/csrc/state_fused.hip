@@ -65,7 +65,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES / 2) void state_fused_kernel(
   using Frag = Op::Frag;
   constexpr int XP = Cfg::XP, BP = Cfg::BP, RPT = Cfg::RPT, LT = Cfg::LT, NB = Cfg::NB, PT = Cfg::PT;
   constexpr int WN = Cfg::WN, RT = Cfg::RT, NBP = Cfg::NBP;
-  constexpr int KU = WAVES == 8 ? 1 : 2;  // unroll of the contraction loop (register budget)
   static_assert(Q % 32 == 0 && RPT >= 1, "chunk must be a multiple of 32");
 
   extern __shared__ __align__(16) unsigned char sf_smem[];
