@@ -331,7 +331,7 @@ BwdLayout bwd_layout(const Dims& d) {
   sz[kSt0] = sz[kSt1] = states;
   sz[kY0] = f * B * L * H * P;
   sz[kY1] = f * B * Lp * H * P;
-  sz[kU] = bwd_dbc_u_bytes(d);
+  sz[kU] = bwd_dbc_ws_bytes(d);
   sz[kBeta] = sz[kV] = sz[kUdot] = f * B * L * H;
   sz[kDAp] = sz[kDDp] = f * B * H * d.nc;
   sz[kAnc] = f * B * H * (d.nc + 1);

@@ -17,30 +17,31 @@
 // sum of the heads' decayed dy.x Gram matrices, so the products with B and C
 // run once per group instead of once per head.
 //
-// bwd_dc_kernel: one block per (b, c, g, tile T of TI = min(64, Q) rows i).
-//   The loop over (head, slice of the head dimension) accumulates, in
-//   registers, the transposed tiles
-//     U^T[j][i] for j < start(T)       = sum x~_j . dy~_i,  with the decay
-//                                         split at R = start(T):
-//                                         x~_j = exp(G_R - G_j) dt_j x_j,
-//                                         dy~_i = exp(G_i - G_R) dy_i (both
-//                                         factors <= 1, no overflow);
-//     U^T[j][i] for j, i in T          = raw dy.x Gram, decayed and causally
-//                                         masked per element (the exponent is
-//                                         selected before exp);
-//     dC^T[n][i] (carried-state part)  = sum (exp(G_R) Hc)[n] . dy~_i.
-//   Then U's rows of T are stored (fp32, for bwd_db_kernel), U^T is staged in
-//   LDS and dC^T += B^T U^T completes the tile.
-// bwd_db_kernel: one block per (b, c, g, tile T of rows j).  The same loop
-//   accumulates dB^T[n][j] = sum (rho dH)[n] . (dt_j exp(G_last - G_j) x_j),
-//   then dB^T += C^T U over the rows i >= start(T) of U's column panel.
+// bwd_part_kernel: one block per (b, c, g, slice of the group's heads); every
+//   x, dy and state element is read once.  The loop over (head, slice of the
+//   head dimension) accumulates in registers, as transposed 16x16 tiles:
+//     U^T[j][i]   (DO_U)  the raw dy.x Gram tile of the head (one matrix-core
+//                 product per 32-deep step), scaled per element by its decay
+//                 and added: below the diagonal tile the decay is split at the
+//                 last row E of j's tile, exp(G_i - G_E) exp(G_E - G_j), both
+//                 factors <= 1; on the diagonal tile exp(G_i - G_j) is taken
+//                 per element with the exponent selected before exp (j > i
+//                 gives 0);
+//     S^T[n][k]   (DO_S)  the carried-state part, sum_p St[n][p] col_k[p]
+//                 scaled per column k: dC: col = dy, St = Hc, factor
+//                 exp(G_k); dB: col = x, St = dH, factor r dt_k exp(G_last -
+//                 G_k) with r the decay step to the next chunk's first token.
+//   Partial sums per head slice go to the workspace (fp32).
+// bwd_fin_kernel: one block per (b, c, g, tile T of TI = min(64, Q) rows):
+//   sums the slices, then dC^T += B^T U^T over U's row panel of T and
+//   dB^T += C^T U over its column panel.
 //
 // Operands are bf16 (rounded to nearest even) or, with fp32 matrix operands,
-// fp32; accumulation is fp32.  Every product is a 16x16x32 step of the
-// matrix cores (eight 16x16x4 steps for fp32 operands).  Accumulator tiles of
-// one 16x16 output hold, in lane (i = lane % 16, q = lane / 16), rows
-// 4q .. 4q+3 of column i: stored as the transposed products above, each lane
-// owns 4 consecutive output columns of one row, written with 16-byte stores.
+// fp32; accumulation is fp32.  Products are 16x16x32 steps of the matrix cores
+// (eight 16x16x4 steps for fp32 operands).  An accumulator tile holds, in lane
+// (i = lane % 16, q = lane / 16), rows 4q .. 4q+3 of column i: since the
+// products are stored transposed, each lane owns 4 consecutive output columns
+// of one row, written with 16-byte stores.
 #include <algorithm>
 
 #include "ssd_device.hpp"
@@ -89,270 +90,265 @@ __device__ __forceinline__ uint4 load16(const void* base, int64_t elem, bool bf1
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// n (4 or 8) scaled values into LDS in the operand type
-__device__ __forceinline__ void store_scaled(uint16_t* p, const float* v, int n, float s) {
-  if (n == 8) {
-    *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0] * s, v[1] * s), pack_bf16x2(v[2] * s, v[3] * s),
-                                              pack_bf16x2(v[4] * s, v[5] * s), pack_bf16x2(v[6] * s, v[7] * s));
+// n (4 or 8) values into LDS in the operand type
+__device__ __forceinline__ void store_vals(uint16_t* p, const float* v, int n) {
+  if (n == 8)
+    *reinterpret_cast<uint4*>(p) =
+        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+  else
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+__device__ __forceinline__ void store_vals(float* p, const float* v, int n) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  if (n == 8) *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+// A 16-byte input piece into LDS: bf16 bits are copied as they are when the
+// operand type is bf16, anything else goes through fp32.
+__device__ __forceinline__ void store_piece(uint16_t* p, const uint4 v, bool bf16) {
+  if (bf16) {
+    *reinterpret_cast<uint4*>(p) = v;
   } else {
-    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0] * s, v[1] * s), pack_bf16x2(v[2] * s, v[3] * s));
+    float f[8];
+    unpack16(v, false, f);
+    store_vals(p, f, 4);
   }
 }
-__device__ __forceinline__ void store_scaled(float* p, const float* v, int n, float s) {
-  *reinterpret_cast<float4*>(p) = make_float4(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
-  if (n == 8) *reinterpret_cast<float4*>(p + 4) = make_float4(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+__device__ __forceinline__ void store_piece(float* p, const uint4 v, bool bf16) {
+  float f[8];
+  const int n = unpack16(v, bf16, f);
+  store_vals(p, f, n);
 }
-__device__ __forceinline__ void store_elem(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_bits(v); }
-__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
-
-struct DbcArgs {
-  const void* x;      // [B, L, H, P]
-  const void* dy;     // [B, L, H, P]
-  const void* bc;     // B (bwd_dc) or C (bwd_db), [B, L, G, N]
-  const float* dA;    // dA_cumsum [B, H, nc, Q]
-  const float* dtb;   // dt_bhl   [B, H, nc, Q]
-  const float* st;    // bwd_dc: states entering each chunk [B, nc, H, N, P];
-                      // bwd_db: adjoint carried states in reversed chunk order
-  const float* A;     // [H]; bwd_db: with dt of the next chunk's first token, one decay step
-  float* U;           // [B, nc, G, Q, Q]
-  float* out;         // dC or dB [B, L, G, N]
-  int L, H, P, N, G, Q, nc, TI, NT;
-  int x_bf16, dy_bf16, in_bf16;
-};
-
-constexpr int kDbcThreads = 256;
-constexpr int kNSlice = 64;  // B / C columns staged at a time in the final products
 
 template <class Op> struct DbcPitch {
   typedef typename OpElem<Op>::type E;
   static constexpr bool kB = sizeof(E) == 2;
-  // operand rows read 16 bytes per lane, and the transposing reads of the
-  // final products (bf16: ds_read_b64_tr_b16; fp32: 4-byte reads)
+  // rows read 16 bytes per lane (operand rows), and rows read by the
+  // transposing reads of the final products (bf16: ds_read_b64_tr_b16; fp32:
+  // 4-byte reads)
   __host__ __device__ static constexpr int op(int ps) { return ps + (kB ? 16 : 8); }
   __host__ __device__ static constexpr int tr(int cols) { return cols + (kB ? 16 : 4); }
 };
 
+// ---------------------------------------------------------------- partial sums
+struct PartArgs {
+  const void* col;     // [B, L, H, P]: dy (U and dC) or x (dB) -- the column operand
+  const void* x;       // [B, L, H, P]: x, the row operand of U
+  const float* st;     // dC: forward carried states [B, nc, H, N, P];
+                       // dB: adjoint carried states in reversed chunk order
+  const float* dA;     // dA_cumsum [B, H, nc, Q]
+  const float* dtb;    // dt_bhl   [B, H, nc, Q]
+  const float* A;      // [H]
+  float* uout;         // [S, B*nc*G, Q, Q] (tiles on and below the diagonal)
+  float* sout;         // [S, B*nc*G, Q, N]
+  int L, H, P, N, G, Q, nc, S, hps;
+  int col_bf16, x_bf16;
+};
+
 template <class Op>
-size_t dbc_lds_bytes(int Q, int TI, int N, int PS, bool dc) {
-  typedef typename OpElem<Op>::type E;
-  const size_t e = sizeof(E);
-  const int PP = DbcPitch<Op>::op(PS), UP = DbcPitch<Op>::tr(TI), BP = DbcPitch<Op>::tr(kNSlice);
-  const size_t ops = dc ? (size_t)(2 * TI + Q + N) * PP * e : (size_t)(TI + N) * PP * e;
-  const size_t fin = (size_t)Q * UP * e + (size_t)Q * BP * e;
-  const size_t region = (std::max(ops, fin) + 15) / 16 * 16;
-  const size_t scales = dc ? 2 * (size_t)(Q + 3 * TI) * sizeof(float) : 2 * (size_t)TI * sizeof(float);
-  return region + scales;
+size_t part_lds_bytes(int Q, int N, int PS, bool do_u, bool do_s) {
+  const size_t e = sizeof(typename OpElem<Op>::type);
+  const int PP = DbcPitch<Op>::op(PS);
+  const size_t rows = (size_t)Q + (do_u ? Q : 0) + (do_s ? N : 0);
+  return rows * PP * e + 2 * 4 * (size_t)Q * sizeof(float);
 }
 
-// block -> (b, c, g, tile); consecutive logical blocks (the tiles of one
-// chunk) on the same XCD so that its L2 serves their shared rows and states
-__device__ __forceinline__ void dbc_block(const DbcArgs& a, int& b, int& c, int& g, int& tile) {
-  unsigned bid = blockIdx.x;
-  const unsigned nb = gridDim.x;
-  if ((nb & 7u) == 0) bid = (bid & 7u) * (nb >> 3) + (bid >> 3);
-  tile = bid % a.NT;
-  unsigned rest = bid / a.NT;
-  g = rest % a.G;
-  rest /= a.G;
-  c = rest % a.nc;
-  b = rest / a.nc;
-}
-
-// ---------------------------------------------------------------- dC and U
-// Per-thread prefetch slots (16-byte pieces): x rows (<= 256 x 128 bytes),
-// dy rows (64 x 128 bytes), state rows (<= 256 x 128 bytes).
-constexpr int kPX = 8, kPDY = 2, kPH = 8;
-
-template <class Op, int PS, int NS4>
-__global__ __launch_bounds__(kDbcThreads) void bwd_dc_kernel(DbcArgs a) {
+// NW waves; CPW column tiles (16 positions each) per wave: wave w owns
+// column w and, with CPW = 2, column 2 NW - 1 - w (so that the causal U work,
+// (w + 1) + (2 NW - w) tiles, is the same on every wave).
+// KIND_DB: the state part is dB's (column operand x, adjoint states, factor
+// r dt_k exp(G_last - G_k)), else dC's (column operand dy, forward states,
+// factor exp(G_k)).
+template <class Op, int PS, int NW, int CPW, bool DO_U, bool DO_S, bool KIND_DB, int NTS>
+__global__ __launch_bounds__(64 * NW) void bwd_part_kernel(PartArgs a) {
   typedef typename OpElem<Op>::type E;
   typedef typename Op::Frag Frag;
+  constexpr int T = 64 * NW;
   constexpr int PP = DbcPitch<Op>::op(PS);
   constexpr int KS = PS / 32;
+  constexpr int KP = NW == 8 ? 4 : 2;      // 16-byte pieces per thread: Q rows of one slice
+  constexpr int KSP = NW == 8 ? 4 : 8;     // ... and N state rows
+  constexpr int UT0 = NW == 8 ? 8 : 4;     // U tiles of the first column (<= w + 1)
+  constexpr int UT1 = CPW == 2 ? 2 * NW : 1;
+  constexpr int NT16MAX = NTS;              // state tiles per column, N <= 16 NTS
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
-  int b, c, g, it;
-  dbc_block(a, b, c, g, it);
-  const int Q = a.Q, TI = a.TI, R = it * TI, J = R + TI, P = a.P, N = a.N, H = a.H;
-  const int CT = TI / 16, OT = R / 16, NT16 = N / 16;
-  const int hpg = H / a.G, NPS = (P + PS - 1) / PS, NU = hpg * NPS;
+  const int Q = a.Q, P = a.P, N = a.N, H = a.H, T16 = Q / 16, NT16 = N / 16;
+  const int s = blockIdx.x % a.S;
+  const int bcg = blockIdx.x / a.S;
+  const int g = bcg % a.G, c = (bcg / a.G) % a.nc, b = bcg / a.G / a.nc;
+  const int hpg = H / a.G, h_lo = g * hpg + s * a.hps, nh = min(a.hps, hpg - s * a.hps);
+  const int NPS = (P + PS - 1) / PS, NU = nh * NPS;
   const int64_t tok0 = (int64_t)b * a.L + (int64_t)c * Q;
   const int nvalid = min(Q, a.L - c * Q);
-  const bool xb = a.x_bf16 != 0, yb = a.dy_bf16 != 0;
+  const bool cb16 = a.col_bf16 != 0, xb16 = a.x_bf16 != 0;
 
-  E* sDyS = reinterpret_cast<E*>(smem);
-  E* sDyR = sDyS + TI * PP;
-  E* sX = sDyR + TI * PP;
-  E* sH = sX + Q * PP;
-  // the final products reuse the operand area
-  const int UP = DbcPitch<Op>::tr(TI), BP = DbcPitch<Op>::tr(kNSlice);
-  E* sUt = reinterpret_cast<E*>(smem);
-  E* sB = sUt + Q * UP;
-  const size_t ops_b = (size_t)(2 * TI + Q + N) * PP * sizeof(E);
-  const size_t fin_b = (size_t)Q * (UP + BP) * sizeof(E);
-  float* sSc = reinterpret_cast<float*>(smem + ((ops_b > fin_b ? ops_b : fin_b) + 15) / 16 * 16);
-  const int SCW = Q + 3 * TI;  // per buffer: x scale [Q], dy scale [TI], G [TI], dt [TI]
+  E* sCol = reinterpret_cast<E*>(smem);       // [Q][PP] column operand
+  E* sX = sCol + Q * PP;                      // [Q][PP] x (DO_U)
+  E* sSt = sX + (DO_U ? Q * PP : 0);          // [N][PP] states (DO_S)
+  float* sSc = reinterpret_cast<float*>(sSt + (DO_S ? N * PP : 0));
+  // per buffer: G [Q], the below-diagonal factor exp(G_E - G_j) dt_j [Q],
+  // dt [Q], the state factor per column [Q]
+  auto scb = [&](int buf) { return sSc + buf * 4 * Q; };
 
-  const int xepc = xb ? 8 : 4, xcpr = PS / xepc;  // elements per piece, pieces per row
-  const int yepc = yb ? 8 : 4, ycpr = PS / yepc;
-  const int hcpr = PS / 4;
+  const int ccpr = PS / (cb16 ? 8 : 4), cepc = cb16 ? 8 : 4;
+  const int xcpr = PS / (xb16 ? 8 : 4), xepc = xb16 ? 8 : 4;
+  const int scpr = PS / 4;
 
-  uint4 px[kPX], py[kPDY], ph[kPH];
-  float pg[5];
+  uint4 pc[KP], px[KP], pst[KSP];
+  float pg[4];
+  float rho_e = 0.f;  // dB: exponent of r (dt of the next chunk's first token times A)
   auto issue = [&](int u) {
-    const int hh = u / NPS, p0 = (u - hh * NPS) * PS, h = g * hpg + hh;
+    const int hh = u / NPS, p0 = (u - hh * NPS) * PS, h = h_lo + hh;
     const int64_t cb = ((int64_t)(b * H + h) * a.nc + c) * Q;
-    pg[0] = tid < J ? a.dA[cb + tid] : 0.f;
-    pg[1] = tid < J ? a.dtb[cb + tid] : 0.f;
-    pg[2] = a.dA[cb + R];
-    pg[3] = tid < TI ? a.dA[cb + R + tid] : 0.f;
-    pg[4] = tid < TI ? a.dtb[cb + R + tid] : 0.f;
+    pg[0] = tid < Q ? a.dA[cb + tid] : 0.f;
+    pg[1] = tid < Q ? a.dtb[cb + tid] : 0.f;
+    pg[2] = tid < Q ? a.dA[cb + (tid | 15)] : 0.f;
+    pg[3] = a.dA[cb + Q - 1];
+    if (KIND_DB) rho_e = c + 1 < a.nc ? a.dtb[cb + Q] * a.A[h] : 0.f;
 #pragma unroll
-    for (int k = 0; k < kPX; ++k) {
-      const int q = tid + kDbcThreads * k;
-      px[k] = make_uint4(0, 0, 0, 0);
-      if (q < J * xcpr) {
-        const int j = q / xcpr, p = p0 + (q - j * xcpr) * xepc;
-        if (j < nvalid && p < P) px[k] = load16(a.x, ((tok0 + j) * H + h) * P + p, xb);
+    for (int k = 0; k < KP; ++k) {
+      const int q = tid + T * k;
+      pc[k] = make_uint4(0, 0, 0, 0);
+      if (q < Q * ccpr) {
+        const int j = q / ccpr, p = p0 + (q - j * ccpr) * cepc;
+        if (j < nvalid && p < P) pc[k] = load16(a.col, ((tok0 + j) * H + h) * P + p, cb16);
+      }
+      if (DO_U) {
+        px[k] = make_uint4(0, 0, 0, 0);
+        if (q < Q * xcpr) {
+          const int j = q / xcpr, p = p0 + (q - j * xcpr) * xepc;
+          if (j < nvalid && p < P) px[k] = load16(a.x, ((tok0 + j) * H + h) * P + p, xb16);
+        }
       }
     }
+    if (DO_S) {
+      const int64_t sc = KIND_DB ? ((int64_t)b * a.nc + (a.nc - 1 - c)) : ((int64_t)b * a.nc + c);
+      const float* st = a.st + (sc * H + h) * N * P;
 #pragma unroll
-    for (int k = 0; k < kPDY; ++k) {
-      const int q = tid + kDbcThreads * k;
-      py[k] = make_uint4(0, 0, 0, 0);
-      if (q < TI * ycpr) {
-        const int i = q / ycpr, p = p0 + (q - i * ycpr) * yepc;
-        if (R + i < nvalid && p < P) py[k] = load16(a.dy, ((tok0 + R + i) * H + h) * P + p, yb);
-      }
-    }
-    const float* hc = a.st + (((int64_t)b * a.nc + c) * H + h) * N * P;
-#pragma unroll
-    for (int k = 0; k < kPH; ++k) {
-      const int q = tid + kDbcThreads * k;
-      ph[k] = make_uint4(0, 0, 0, 0);
-      if (q < N * hcpr) {
-        const int n = q / hcpr, p = p0 + (q - n * hcpr) * 4;
-        if (p < P) ph[k] = *reinterpret_cast<const uint4*>(hc + (int64_t)n * P + p);
+      for (int k = 0; k < KSP; ++k) {
+        const int q = tid + T * k;
+        pst[k] = make_uint4(0, 0, 0, 0);
+        if (q < N * scpr) {
+          const int n = q / scpr, p = p0 + (q - n * scpr) * 4;
+          if (p < P) pst[k] = *reinterpret_cast<const uint4*>(st + (int64_t)n * P + p);
+        }
       }
     }
   };
   auto commit_scales = [&](int buf) {
-    float* sc = sSc + buf * SCW;
-    const float gR = pg[2];
-    if (tid < J) sc[tid] = tid < R ? fast_exp(gR - pg[0]) * pg[1] : 1.f;
-    if (tid < TI) {
-      sc[Q + tid] = fast_exp(pg[3] - gR);
-      sc[Q + TI + tid] = pg[3];
-      sc[Q + 2 * TI + tid] = pg[4];
+    float* sc = scb(buf);
+    if (tid < Q) {
+      sc[tid] = pg[0];
+      sc[Q + tid] = fast_exp(pg[2] - pg[0]) * pg[1];
+      sc[2 * Q + tid] = pg[1];
+      sc[3 * Q + tid] = KIND_DB ? fast_exp(pg[3] - pg[0] + rho_e) * pg[1] : fast_exp(pg[0]);
     }
   };
-  auto commit_ops = [&](int buf) {
-    const float* sc = sSc + buf * SCW;
-    float v[8];
+  auto commit_ops = [&]() {
 #pragma unroll
-    for (int k = 0; k < kPX; ++k) {
-      const int q = tid + kDbcThreads * k;
-      if (q < J * xcpr) {
-        const int j = q / xcpr, e0 = (q - j * xcpr) * xepc;
-        const int n = unpack16(px[k], xb, v);
-        store_scaled(sX + j * PP + e0, v, n, sc[j]);
+    for (int k = 0; k < KP; ++k) {
+      const int q = tid + T * k;
+      if (q < Q * ccpr) {
+        const int j = q / ccpr;
+        store_piece(sCol + j * PP + (q - j * ccpr) * cepc, pc[k], cb16);
+      }
+      if (DO_U && q < Q * xcpr) {
+        const int j = q / xcpr;
+        store_piece(sX + j * PP + (q - j * xcpr) * xepc, px[k], xb16);
       }
     }
+    if (DO_S) {
 #pragma unroll
-    for (int k = 0; k < kPDY; ++k) {
-      const int q = tid + kDbcThreads * k;
-      if (q < TI * ycpr) {
-        const int i = q / ycpr, e0 = (q - i * ycpr) * yepc;
-        const int n = unpack16(py[k], yb, v);
-        store_scaled(sDyS + i * PP + e0, v, n, sc[Q + i]);
-        store_scaled(sDyR + i * PP + e0, v, n, 1.f);
-      }
-    }
-    const float hs = fast_exp(pg[2]);
-#pragma unroll
-    for (int k = 0; k < kPH; ++k) {
-      const int q = tid + kDbcThreads * k;
-      if (q < N * hcpr) {
-        const int n = q / hcpr, e0 = (q - n * hcpr) * 4;
-        unpack16(ph[k], false, v);
-        store_scaled(sH + n * PP + e0, v, 4, hs);
+      for (int k = 0; k < KSP; ++k) {
+        const int q = tid + T * k;
+        if (q < N * scpr) {
+          const int n = q / scpr;
+          store_piece(sSt + n * PP + (q - n * scpr) * 4, pst[k], false);
+        }
       }
     }
   };
 
-  f32x4_t accO[3][4], accS[NS4][4], accD[4], tmp[4];
   const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t accU0[DO_U ? UT0 : 1], accU1[DO_U ? UT1 : 1], accS[DO_S ? CPW : 1][DO_S ? NT16MAX : 1];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    accD[ct] = z4;
-    tmp[ct] = z4;
+  for (int k = 0; k < (DO_U ? UT0 : 1); ++k) accU0[k] = z4;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) accO[k][ct] = z4;
+  for (int k = 0; k < (DO_U ? UT1 : 1); ++k) accU1[k] = z4;
 #pragma unroll
-    for (int k = 0; k < NS4; ++k) accS[k][ct] = z4;
-  }
+  for (int cc = 0; cc < (DO_S ? CPW : 1); ++cc)
+#pragma unroll
+    for (int k = 0; k < (DO_S ? NT16MAX : 1); ++k) accS[cc][k] = z4;
+
+  // the wave's columns
+  const int I0 = w, I1 = CPW == 2 ? 2 * NW - 1 - w : 0;
+  const bool active = I0 < T16;
+
+  // decayed Gram tile (I, J) of the current head added into acc
+  auto u_tile = [&](f32x4_t& acc, const Frag (&bd)[KS], int I, int J, const float* sc) {
+    f32x4_t t = z4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      t = Op::mma(Lds<Op>::load8(sX + (16 * J + l16) * PP + 32 * ks + 8 * lg), bd[ks], t);
+    const int i = 16 * I + l16;
+    const float gi = sc[i];
+    if (J < I) {
+      const float fa = fast_exp(gi - sc[16 * J + 15]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = fmaf(t[r], fa * sc[Q + 16 * J + 4 * lg + r], acc[r]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * J + 4 * lg + r;
+        acc[r] = fmaf(t[r], fast_exp(j <= i ? gi - sc[j] : -INFINITY) * sc[2 * Q + j], acc[r]);
+      }
+    }
+  };
 
   auto compute = [&](int buf) {
+    if (!active) return;
+    const float* sc = scb(buf);
+    Frag bd0[KS], bd1[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int ko = 32 * ks + 8 * lg;
-      Frag bs[4];
+      bd0[ks] = Lds<Op>::load8(sCol + (16 * I0 + l16) * PP + 32 * ks + 8 * lg);
+      bd1[ks] = CPW == 2 ? Lds<Op>::load8(sCol + (16 * I1 + l16) * PP + 32 * ks + 8 * lg) : bd0[ks];
+    }
+    if (DO_U) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        if (ct < CT) bs[ct] = Lds<Op>::load8(sDyS + (16 * ct + l16) * PP + ko);
+      for (int J = 0; J < UT0; ++J)
+        if (J <= I0) u_tile(accU0[J], bd0, I0, J, sc);
+      if (CPW == 2) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int o = w + 4 * k;
-        if (o < OT) {
-          const Frag af = Lds<Op>::load8(sX + (16 * o + l16) * PP + ko);
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            if (ct < CT) accO[k][ct] = Op::mma(af, bs[ct], accO[k][ct]);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < NS4; ++k) {
-        const int s = w + 4 * k;
-        if (s < NT16) {
-          const Frag af = Lds<Op>::load8(sH + (16 * s + l16) * PP + ko);
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            if (ct < CT) accS[k][ct] = Op::mma(af, bs[ct], accS[k][ct]);
-        }
-      }
-      if (w < CT) {
-        const Frag af = Lds<Op>::load8(sX + (R + 16 * w + l16) * PP + ko);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-          if (ct >= w && ct < CT) {
-            const Frag br = Lds<Op>::load8(sDyR + (16 * ct + l16) * PP + ko);
-            tmp[ct] = Op::mma(af, br, tmp[ct]);
-          }
+        for (int J = 0; J < UT1; ++J)
+          if (J <= I1) u_tile(accU1[J], bd1, I1, J, sc);
       }
     }
-    // the diagonal tile: decay exp(G_i - G_j) dt_j where j <= i, else 0
-    if (w < CT) {
-      const float* sc = sSc + buf * SCW;
+    if (DO_S) {
+      const float f0 = sc[3 * Q + 16 * I0 + l16];
+      const float f1 = CPW == 2 ? sc[3 * Q + 16 * I1 + l16] : 0.f;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        if (ct >= w && ct < CT) {
-          const int i = 16 * ct + l16;
-          const float gi = sc[Q + TI + i];
+      for (int k = 0; k < NT16MAX; ++k) {
+        if (k >= NT16) continue;
+        f32x4_t t0 = z4, t1 = z4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 16 * w + 4 * lg + r;
-            const float f = fast_exp(j <= i ? gi - sc[Q + TI + j] : -INFINITY) * sc[Q + 2 * TI + j];
-            accD[ct][r] = fmaf(tmp[ct][r], f, accD[ct][r]);
-            tmp[ct][r] = 0.f;
-          }
+        for (int ks = 0; ks < KS; ++ks) {
+          const Frag af = Lds<Op>::load8(sSt + (16 * k + l16) * PP + 32 * ks + 8 * lg);
+          t0 = Op::mma(af, bd0[ks], t0);
+          if (CPW == 2) t1 = Op::mma(af, bd1[ks], t1);
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          accS[0][k][r] = fmaf(t0[r], f0, accS[0][k][r]);
+          if (CPW == 2) accS[CPW - 1][k][r] = fmaf(t1[r], f1, accS[CPW - 1][k][r]);
+        }
+      }
     }
   };
 
   issue(0);
   commit_scales(0);
-  __syncthreads();
-  commit_ops(0);
+  commit_ops();
   __syncthreads();
   for (int u = 0; u < NU; ++u) {
     const int cur = u & 1;
@@ -362,302 +358,265 @@ __global__ __launch_bounds__(kDbcThreads) void bwd_dc_kernel(DbcArgs a) {
     if (more) commit_scales(cur ^ 1);
     __syncthreads();
     if (more) {
-      commit_ops(cur ^ 1);
+      commit_ops();
       __syncthreads();
     }
   }
 
-  // ---- U's rows of this tile (fp32, row-major [i][j]) for the dB kernel
-  float* Ub = a.U + (((int64_t)b * a.nc + c) * a.G + g) * Q * Q;
+  // ---- partial sums of this head slice
+  if (!active) return;
+  const int64_t pidx = (int64_t)s * (gridDim.x / a.S) + bcg;
+  if (DO_U) {
+    float* U = a.uout + pidx * Q * Q;
+    auto put = [&](const f32x4_t& v, int I, int J) {
+      *reinterpret_cast<float4*>(U + (int64_t)(16 * I + l16) * Q + 16 * J + 4 * lg) =
+          make_float4(v[0], v[1], v[2], v[3]);
+    };
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    if (ct >= CT) continue;
-    const int i = R + 16 * ct + l16;
+    for (int J = 0; J < UT0; ++J)
+      if (J <= I0) put(accU0[J], I0, J);
+    if (CPW == 2) {
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int o = w + 4 * k;
-      if (o < OT)
-        *reinterpret_cast<float4*>(Ub + (int64_t)i * Q + 16 * o + 4 * lg) =
-            make_float4(accO[k][ct][0], accO[k][ct][1], accO[k][ct][2], accO[k][ct][3]);
+      for (int J = 0; J < UT1; ++J)
+        if (J <= I1) put(accU1[J], I1, J);
     }
-    if (w < CT)
-      *reinterpret_cast<float4*>(Ub + (int64_t)i * Q + R + 16 * w + 4 * lg) =
-          make_float4(accD[ct][0], accD[ct][1], accD[ct][2], accD[ct][3]);
   }
-  // ---- U^T of this tile into LDS ([j][i], operand type)
-  // (the last barrier of the loop ended every read of the operand area)
+  if (DO_S) {
+    float* Sp = a.sout + pidx * Q * N;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    if (ct >= CT) continue;
-    const int i = 16 * ct + l16;
+    for (int cc = 0; cc < CPW; ++cc) {
+      const int i = 16 * (cc == 0 ? I0 : I1) + l16;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int o = w + 4 * k;
-      if (o < OT)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) store_elem(sUt + (16 * o + 4 * lg + r) * UP + i, accO[k][ct][r]);
+      for (int k = 0; k < NT16MAX; ++k)
+        if (k < NT16)
+          *reinterpret_cast<float4*>(Sp + (int64_t)i * N + 16 * k + 4 * lg) =
+              make_float4(accS[cc][k][0], accS[cc][k][1], accS[cc][k][2], accS[cc][k][3]);
     }
-    if (w < CT)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) store_elem(sUt + (R + 16 * w + 4 * lg + r) * UP + i, accD[ct][r]);
   }
-  // ---- dC^T += B^T U^T, kNSlice columns of B at a time
+}
+
+// ---------------------------------------------------------------- final products
+struct FinArgs {
+  const float* upart;  // [S, B*nc*G, Q, Q]
+  const float* cpart;  // [S, B*nc*G, Q, N] dC's carried-state part
+  const float* bpart;  // [S, B*nc*G, Q, N] dB's carried-state part
+  const void* Bm;      // [B, L, G, N]
+  const void* Cm;
+  float* dB;           // [B, L, G, N]
+  float* dC;
+  int L, N, G, Q, nc, S, TI, NT;
+  int in_bf16;
+};
+
+constexpr int kFinThreads = 256;
+constexpr int kNSlice = 64;  // B / C columns staged at a time
+
+template <class Op>
+size_t fin_lds_bytes(int Q, int TI) {
+  const size_t e = sizeof(typename OpElem<Op>::type);
+  const int UP = DbcPitch<Op>::tr(TI), BP = DbcPitch<Op>::tr(kNSlice);
+  return (size_t)(Q + TI) * UP * e + (size_t)Q * BP * e;
+}
+
+template <class Op, int NS4>
+__global__ __launch_bounds__(kFinThreads) void bwd_fin_kernel(FinArgs a) {
+  typedef typename OpElem<Op>::type E;
+  typedef typename Op::Frag Frag;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
+  const int t = blockIdx.x % a.NT;
+  const int bcg = blockIdx.x / a.NT;
+  const int g = bcg % a.G, c = (bcg / a.G) % a.nc, b = bcg / a.G / a.nc;
+  const int Q = a.Q, N = a.N, TI = a.TI, R = t * TI, J = R + TI, NI = Q - R;
+  const int CT = TI / 16, NT16 = N / 16;
+  const int64_t tok0 = (int64_t)b * a.L + (int64_t)c * Q;
+  const int nvalid = min(Q, a.L - c * Q);
+  const int64_t nbcg = (int64_t)(gridDim.x / a.NT);
+  const int UP = DbcPitch<Op>::tr(TI), BP = DbcPitch<Op>::tr(kNSlice);
+  E* sUt = reinterpret_cast<E*>(smem);  // [J][UP]: U^T of the row panel, sUt[j][i] = U[R + i][j]
+  E* sU = sUt + J * UP;                 // [NI][UP]: column panel, sU[i][j] = U[R + i][R + j]
+  E* sBC = sU + NI * UP;                // [J or NI][BP]: B or C rows, kNSlice columns
+
+  // U[i][j .. j+3] summed over the head slices; zero above the diagonal
+  // (those entries of the slices' tiles on the diagonal are zero already,
+  // the tiles right of it are never written)
+  auto usum = [&](int i, int j) -> float4 {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (j > i) return v;
+    for (int s = 0; s < a.S; ++s) {
+      const float4 p = *reinterpret_cast<const float4*>(a.upart + ((s * nbcg + bcg) * Q + i) * (int64_t)Q + j);
+      v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+    }
+    if (j + 1 > i) v.y = 0.f;
+    if (j + 2 > i) v.z = 0.f;
+    if (j + 3 > i) v.w = 0.f;
+    return v;
+  };
+  for (int q = tid; q < TI * (J / 4); q += kFinThreads) {
+    const int i = q / (J / 4), j = (q - i * (J / 4)) * 4;
+    const float4 v = usum(R + i, j);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (sizeof(E) == 2) sUt[(j + r) * UP + i] = (E)f32_to_bf16_bits(vv[r]);
+      else sUt[(j + r) * UP + i] = vv[r];
+    }
+  }
+  for (int q = tid; q < NI * (TI / 4); q += kFinThreads) {
+    const int i = q / (TI / 4), j = (q - i * (TI / 4)) * 4;
+    const float4 v = usum(R + i, R + j);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+    store_vals(sU + i * UP + j, vv, 4);
+  }
+
+  // accumulators start from the carried-state parts: lane (i, q) of tile
+  // (k, ct) holds rows n = 16k + 4q .. +3 of column (position) R + 16ct + i
+  f32x4_t accC[NS4][4], accB[NS4][4];
+#pragma unroll
+  for (int k = 0; k < NS4; ++k) {
+    const int s16 = w + 4 * k;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      f32x4_t vc = {0.f, 0.f, 0.f, 0.f}, vb = vc;
+      if (s16 < NT16 && ct < CT) {
+        const int64_t row = R + 16 * ct + l16;
+        for (int s = 0; s < a.S; ++s) {
+          const int64_t off = ((s * nbcg + bcg) * Q + row) * N + 16 * s16 + 4 * lg;
+          const float4 pc = *reinterpret_cast<const float4*>(a.cpart + off);
+          const float4 pb = *reinterpret_cast<const float4*>(a.bpart + off);
+          vc[0] += pc.x; vc[1] += pc.y; vc[2] += pc.z; vc[3] += pc.w;
+          vb[0] += pb.x; vb[1] += pb.y; vb[2] += pb.z; vb[3] += pb.w;
+        }
+      }
+      accC[k][ct] = vc;
+      accB[k][ct] = vb;
+    }
+  }
+
   const bool ib = a.in_bf16 != 0;
-  const int bepc = ib ? 8 : 4, bcpr = kNSlice / bepc;
-  for (int ns0 = 0; ns0 < N; ns0 += kNSlice) {
-    for (int q = tid; q < J * bcpr; q += kDbcThreads) {
-      const int j = q / bcpr, e0 = (q - j * bcpr) * bepc, n = ns0 + e0;
+  const int epc = ib ? 8 : 4, cpr = kNSlice / epc;
+  // stage rows [r0, r0 + nr) of B or C, columns [ns0, ns0 + kNSlice)
+  auto stage = [&](const void* src, int r0, int nr, int ns0) {
+    for (int q = tid; q < nr * cpr; q += kFinThreads) {
+      const int j = q / cpr, e0 = (q - j * cpr) * epc, n = ns0 + e0;
       float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      int cnt = bepc;
-      if (j < nvalid && n < N) cnt = unpack16(load16(a.bc, ((tok0 + j) * a.G + g) * N + n, ib), ib, v);
-      store_scaled(sB + j * BP + e0, v, cnt, 1.f);
+      int cnt = epc;
+      if (r0 + j < nvalid && n < N) cnt = unpack16(load16(src, ((tok0 + r0 + j) * a.G + g) * N + n, ib), ib, v);
+      store_vals(sBC + j * BP + e0, v, cnt);
     }
+  };
+  for (int ns0 = 0; ns0 < N; ns0 += kNSlice) {
+    // dC^T += B^T U^T over the rows j < J
+    stage(a.Bm, 0, J, ns0);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < NS4; ++k) {
-      const int s = w + 4 * k;
-      if (s < NT16 && 16 * s >= ns0 && 16 * s < ns0 + kNSlice) {
+      const int s16 = w + 4 * k;
+      if (s16 < NT16 && 16 * s16 >= ns0 && 16 * s16 < ns0 + kNSlice) {
         for (int kj = 0; kj < J; kj += 32) {
-          const Frag af = FragTr<Op>::load(sB + kj * BP + 16 * s - ns0, BP, lane);
+          const Frag af = FragTr<Op>::load(sBC + kj * BP + 16 * s16 - ns0, BP, lane);
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct)
-            if (ct < CT) accS[k][ct] = Op::mma(af, FragTr<Op>::load(sUt + kj * UP + 16 * ct, UP, lane), accS[k][ct]);
+            if (ct < CT) accC[k][ct] = Op::mma(af, FragTr<Op>::load(sUt + kj * UP + 16 * ct, UP, lane), accC[k][ct]);
+        }
+      }
+    }
+    __syncthreads();
+    // dB^T += C^T U over the rows i >= R
+    stage(a.Cm, R, NI, ns0);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NS4; ++k) {
+      const int s16 = w + 4 * k;
+      if (s16 < NT16 && 16 * s16 >= ns0 && 16 * s16 < ns0 + kNSlice) {
+        for (int ki = 0; ki < NI; ki += 32) {
+          const Frag af = FragTr<Op>::load(sBC + ki * BP + 16 * s16 - ns0, BP, lane);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            if (ct < CT) accB[k][ct] = Op::mma(af, FragTr<Op>::load(sU + ki * UP + 16 * ct, UP, lane), accB[k][ct]);
         }
       }
     }
     __syncthreads();
   }
-  // ---- dC rows of this tile: lane (i, q) holds dC[i][16s + 4q .. +3]
 #pragma unroll
   for (int k = 0; k < NS4; ++k) {
-    const int s = w + 4 * k;
-    if (s >= NT16) continue;
+    const int s16 = w + 4 * k;
+    if (s16 >= NT16) continue;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       const int i = R + 16 * ct + l16;
-      if (ct < CT && i < nvalid)
-        *reinterpret_cast<float4*>(a.out + ((tok0 + i) * a.G + g) * N + 16 * s + 4 * lg) =
-            make_float4(accS[k][ct][0], accS[k][ct][1], accS[k][ct][2], accS[k][ct][3]);
+      if (ct < CT && i < nvalid) {
+        const int64_t off = ((tok0 + i) * a.G + g) * N + 16 * s16 + 4 * lg;
+        *reinterpret_cast<float4*>(a.dC + off) =
+            make_float4(accC[k][ct][0], accC[k][ct][1], accC[k][ct][2], accC[k][ct][3]);
+        *reinterpret_cast<float4*>(a.dB + off) =
+            make_float4(accB[k][ct][0], accB[k][ct][1], accB[k][ct][2], accB[k][ct][3]);
+      }
     }
   }
 }
 
-// ---------------------------------------------------------------- dB
-constexpr int kQX = 2, kQH = 8;
-
-template <class Op, int PS, int NS4>
-__global__ __launch_bounds__(kDbcThreads) void bwd_db_kernel(DbcArgs a) {
-  typedef typename OpElem<Op>::type E;
-  typedef typename Op::Frag Frag;
-  constexpr int PP = DbcPitch<Op>::op(PS);
-  constexpr int KS = PS / 32;
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
-  int b, c, g, jt;
-  dbc_block(a, b, c, g, jt);
-  const int Q = a.Q, TI = a.TI, R = jt * TI, P = a.P, N = a.N, H = a.H;
-  const int CT = TI / 16, NT16 = N / 16;
-  const int hpg = H / a.G, NPS = (P + PS - 1) / PS, NU = hpg * NPS;
-  const int64_t tok0 = (int64_t)b * a.L + (int64_t)c * Q;
-  const int nvalid = min(Q, a.L - c * Q);
-  const bool xb = a.x_bf16 != 0;
-
-  E* sXh = reinterpret_cast<E*>(smem);
-  E* sdH = sXh + TI * PP;
-  const int UP = DbcPitch<Op>::tr(TI), BP = DbcPitch<Op>::tr(kNSlice);
-  E* sU = reinterpret_cast<E*>(smem);
-  E* sC = sU + Q * UP;
-  const size_t ops_b = (size_t)(TI + N) * PP * sizeof(E);
-  const size_t fin_b = (size_t)Q * (UP + BP) * sizeof(E);
-  float* sSc = reinterpret_cast<float*>(smem + ((ops_b > fin_b ? ops_b : fin_b) + 15) / 16 * 16);
-
-  const int xepc = xb ? 8 : 4, xcpr = PS / xepc;
-  const int hcpr = PS / 4;
-  // adjoint carried states are stored in reversed chunk order: the one that
-  // enters reversed chunk nc-1-c is the gradient at the first token of chunk
-  // c+1, one decay step r = exp(dt A) after the state leaving chunk c
-  const float* dh_base = a.st + (((int64_t)b * a.nc + (a.nc - 1 - c)) * H) * N * P;
-
-  uint4 px[kQX], ph[kQH];
-  float pg[3], rho = 1.f;
-  auto issue = [&](int u) {
-    const int hh = u / NPS, p0 = (u - hh * NPS) * PS, h = g * hpg + hh;
-    const int64_t cb = ((int64_t)(b * H + h) * a.nc + c) * Q;
-    pg[0] = tid < TI ? a.dA[cb + R + tid] : 0.f;
-    pg[1] = tid < TI ? a.dtb[cb + R + tid] : 0.f;
-    pg[2] = a.dA[cb + Q - 1];
-    rho = c + 1 < a.nc ? a.dtb[cb + Q] * a.A[h] : 0.f;  // exponent; dt of the next chunk's first token
-#pragma unroll
-    for (int k = 0; k < kQX; ++k) {
-      const int q = tid + kDbcThreads * k;
-      px[k] = make_uint4(0, 0, 0, 0);
-      if (q < TI * xcpr) {
-        const int j = q / xcpr, p = p0 + (q - j * xcpr) * xepc;
-        if (R + j < nvalid && p < P) px[k] = load16(a.x, ((tok0 + R + j) * H + h) * P + p, xb);
-      }
-    }
-    const float* dh = dh_base + (int64_t)h * N * P;
-#pragma unroll
-    for (int k = 0; k < kQH; ++k) {
-      const int q = tid + kDbcThreads * k;
-      ph[k] = make_uint4(0, 0, 0, 0);
-      if (q < N * hcpr) {
-        const int n = q / hcpr, p = p0 + (q - n * hcpr) * 4;
-        if (p < P) ph[k] = *reinterpret_cast<const uint4*>(dh + (int64_t)n * P + p);
-      }
-    }
-  };
-  auto commit_scales = [&](int buf) {
-    if (tid < TI) sSc[buf * TI + tid] = fast_exp(pg[2] - pg[0]) * pg[1];
-  };
-  auto commit_ops = [&](int buf) {
-    const float* sc = sSc + buf * TI;
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < kQX; ++k) {
-      const int q = tid + kDbcThreads * k;
-      if (q < TI * xcpr) {
-        const int j = q / xcpr, e0 = (q - j * xcpr) * xepc;
-        const int n = unpack16(px[k], xb, v);
-        store_scaled(sXh + j * PP + e0, v, n, sc[j]);
-      }
-    }
-    const float hs = fast_exp(rho);
-#pragma unroll
-    for (int k = 0; k < kQH; ++k) {
-      const int q = tid + kDbcThreads * k;
-      if (q < N * hcpr) {
-        const int n = q / hcpr, e0 = (q - n * hcpr) * 4;
-        unpack16(ph[k], false, v);
-        store_scaled(sdH + n * PP + e0, v, 4, hs);
-      }
-    }
-  };
-
-  f32x4_t acc[NS4][4];
-  const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int k = 0; k < NS4; ++k)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[k][ct] = z4;
-
-  auto compute = [&]() {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ko = 32 * ks + 8 * lg;
-      Frag bx[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        if (ct < CT) bx[ct] = Lds<Op>::load8(sXh + (16 * ct + l16) * PP + ko);
-#pragma unroll
-      for (int k = 0; k < NS4; ++k) {
-        const int s = w + 4 * k;
-        if (s < NT16) {
-          const Frag af = Lds<Op>::load8(sdH + (16 * s + l16) * PP + ko);
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            if (ct < CT) acc[k][ct] = Op::mma(af, bx[ct], acc[k][ct]);
-        }
-      }
-    }
-  };
-
-  issue(0);
-  commit_scales(0);
-  __syncthreads();
-  commit_ops(0);
-  __syncthreads();
-  for (int u = 0; u < NU; ++u) {
-    const int cur = u & 1;
-    const bool more = u + 1 < NU;
-    if (more) issue(u + 1);
-    compute();
-    if (more) commit_scales(cur ^ 1);
-    __syncthreads();
-    if (more) {
-      commit_ops(cur ^ 1);
-      __syncthreads();
-    }
-  }
-
-  // ---- U's column panel: rows i in [R, Q), columns of this tile
-  const float* Ub = a.U + (((int64_t)b * a.nc + c) * a.G + g) * Q * Q;
-  const int NI = Q - R;
-  for (int q = tid; q < NI * (TI / 4); q += kDbcThreads) {
-    const int i = q / (TI / 4), e0 = (q - i * (TI / 4)) * 4;
-    const float4 v4 = *reinterpret_cast<const float4*>(Ub + (int64_t)(R + i) * Q + R + e0);
-    const float v[4] = {v4.x, v4.y, v4.z, v4.w};
-    store_scaled(sU + i * UP + e0, v, 4, 1.f);
-  }
-  // ---- dB^T += C^T U over the rows i >= R
-  const bool ib = a.in_bf16 != 0;
-  const int cepc = ib ? 8 : 4, ccpr = kNSlice / cepc;
-  for (int ns0 = 0; ns0 < N; ns0 += kNSlice) {
-    for (int q = tid; q < NI * ccpr; q += kDbcThreads) {
-      const int i = q / ccpr, e0 = (q - i * ccpr) * cepc, n = ns0 + e0;
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      int cnt = cepc;
-      if (R + i < nvalid && n < N) cnt = unpack16(load16(a.bc, ((tok0 + R + i) * a.G + g) * N + n, ib), ib, v);
-      store_scaled(sC + i * BP + e0, v, cnt, 1.f);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < NS4; ++k) {
-      const int s = w + 4 * k;
-      if (s < NT16 && 16 * s >= ns0 && 16 * s < ns0 + kNSlice) {
-        for (int ki = 0; ki < NI; ki += 32) {
-          const Frag af = FragTr<Op>::load(sC + ki * BP + 16 * s - ns0, BP, lane);
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            if (ct < CT) acc[k][ct] = Op::mma(af, FragTr<Op>::load(sU + ki * UP + 16 * ct, UP, lane), acc[k][ct]);
-        }
-      }
-    }
-    __syncthreads();
-  }
-  // ---- dB rows of this tile
-#pragma unroll
-  for (int k = 0; k < NS4; ++k) {
-    const int s = w + 4 * k;
-    if (s >= NT16) continue;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int j = R + 16 * ct + l16;
-      if (ct < CT && j < nvalid)
-        *reinterpret_cast<float4*>(a.out + ((tok0 + j) * a.G + g) * N + 16 * s + 4 * lg) =
-            make_float4(acc[k][ct][0], acc[k][ct][1], acc[k][ct][2], acc[k][ct][3]);
-    }
-  }
+// ---------------------------------------------------------------- host side
+// Head slices per (b, c, g): enough blocks for the 256 compute units of the
+// target device (a shape-only rule, so that the workspace size is too).
+int dbc_slices(const Dims& d) {
+  const int64_t bcg = d.B * d.nc * d.G, hpg = d.H / d.G;
+  const int64_t s = (256 + bcg - 1) / bcg;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, hpg));
 }
 
-// Slice of the head dimension staged per step: 64 for bf16 operands from
-// bf16 inputs with N <= 128, else 32 (bounds the prefetch registers and LDS).
-int dbc_slice(const Dims& d, bool bf16_ops, bool all_bf16) { return bf16_ops && all_bf16 && d.N <= 128 ? 64 : 32; }
-
-template <class Op, int PS, int NS4>
-hipError_t launch_dbc_inst(const Dims& d, const DbcArgs& ac, const DbcArgs& ab, hipStream_t s) {
-  const unsigned nblk = (unsigned)(d.B * d.nc * d.G * ac.NT);
-  const size_t lds_c = dbc_lds_bytes<Op>((int)d.Q, ac.TI, (int)d.N, PS, true);
-  const size_t lds_b = dbc_lds_bytes<Op>((int)d.Q, ac.TI, (int)d.N, PS, false);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dc_kernel<Op, PS, NS4>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_c);
+template <class Op, int PS, int NW, int CPW, bool DO_U, bool DO_S, bool KIND_DB, int NTS>
+hipError_t launch_part(const Dims& d, const PartArgs& a, hipStream_t s) {
+  const size_t lds = part_lds_bytes<Op>((int)d.Q, (int)d.N, PS, DO_U, DO_S);
+  auto kern = &bwd_part_kernel<Op, PS, NW, CPW, DO_U, DO_S, KIND_DB, NTS>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_db_kernel<Op, PS, NS4>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_b);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dc_kernel<Op, PS, NS4>), dim3(nblk), dim3(kDbcThreads), lds_c, s, ac);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // the dB kernel reads the U rows that every tile of the chunk stored
-  hipLaunchKernelGGL((bwd_db_kernel<Op, PS, NS4>), dim3(nblk), dim3(kDbcThreads), lds_b, s, ab);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(d.B * d.nc * d.G * a.S)), dim3(64 * NW), lds, s, a);
   return hipGetLastError();
 }
 
+template <class Op, int PS, int NW, int CPW, bool KIND_DB>
+hipError_t launch_state_part(const Dims& d, const PartArgs& a, hipStream_t s) {
+  if (d.N <= 64) return launch_part<Op, PS, NW, CPW, false, true, KIND_DB, 4>(d, a, s);
+  if (d.N <= 128) return launch_part<Op, PS, NW, CPW, false, true, KIND_DB, 8>(d, a, s);
+  return launch_part<Op, PS, NW, CPW, false, true, KIND_DB, 16>(d, a, s);
+}
+
+// The partial-sum launches for one operand type, staged slice width and
+// chunk-size class: U, dC's carried-state part, dB's.
+template <class Op, int PS, int NW, int CPW>
+hipError_t launch_parts(const Dims& d, const PartArgs& ac, const PartArgs& ab, hipStream_t s) {
+  hipError_t e = launch_part<Op, PS, NW, CPW, true, false, false, 1>(d, ac, s);
+  if (e == hipSuccess) e = launch_state_part<Op, PS, NW, CPW, false>(d, ac, s);
+  if (e == hipSuccess) e = launch_state_part<Op, PS, NW, CPW, true>(d, ab, s);
+  return e;
+}
+
 template <class Op, int PS>
-hipError_t launch_dbc_ns(const Dims& d, const DbcArgs& ac, const DbcArgs& ab, hipStream_t s) {
-  if (d.N <= 64) return launch_dbc_inst<Op, PS, 1>(d, ac, ab, s);
-  if (d.N <= 128) return launch_dbc_inst<Op, PS, 2>(d, ac, ab, s);
-  return launch_dbc_inst<Op, PS, 4>(d, ac, ab, s);
+hipError_t launch_parts_q(const Dims& d, const PartArgs& ac, const PartArgs& ab, hipStream_t s) {
+  if (d.Q == 256) return launch_parts<Op, PS, 8, 2>(d, ac, ab, s);
+  if (d.Q == 128) return launch_parts<Op, PS, 8, 1>(d, ac, ab, s);
+  return launch_parts<Op, PS, 4, 1>(d, ac, ab, s);
+}
+
+template <class Op, int NS4>
+hipError_t launch_fin_inst(const Dims& d, const FinArgs& f, hipStream_t s) {
+  const size_t lds = fin_lds_bytes<Op>((int)d.Q, f.TI);
+  auto kern = &bwd_fin_kernel<Op, NS4>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(d.B * d.nc * d.G * f.NT)), dim3(kFinThreads), lds, s, f);
+  return hipGetLastError();
+}
+
+template <class Op>
+hipError_t launch_fin(const Dims& d, const FinArgs& f, hipStream_t s) {
+  if (d.N <= 64) return launch_fin_inst<Op, 1>(d, f, s);
+  if (d.N <= 128) return launch_fin_inst<Op, 2>(d, f, s);
+  return launch_fin_inst<Op, 4>(d, f, s);
 }
 
 }  // namespace
@@ -667,30 +626,44 @@ bool bwd_dbc_supported(const Dims& d) {
          d.H % d.G == 0;
 }
 
-size_t bwd_dbc_u_bytes(const Dims& d) { return sizeof(float) * (size_t)(d.B * d.nc * d.G) * d.Q * d.Q; }
+size_t bwd_dbc_ws_bytes(const Dims& d) {
+  const size_t S = (size_t)dbc_slices(d), bcg = (size_t)(d.B * d.nc * d.G);
+  return sizeof(float) * S * bcg * (size_t)d.Q * ((size_t)d.Q + 2 * (size_t)d.N);
+}
 
 hipError_t launch_bwd_dbc(const Dims& d, const void* x, bool x_bf16, const void* dy, bool dy_bf16, const void* Bm,
                           const void* Cm, bool in_bf16, const float* dA_cumsum, const float* dt_bhl,
-                          const float* fwd_carried, const float* adj_carried_rev, const float* A, float* U,
+                          const float* fwd_carried, const float* adj_carried_rev, const float* A, float* ws,
                           float* dB, float* dC, bool f32_mma, hipStream_t s) {
   if (!bwd_dbc_supported(d)) return hipErrorInvalidValue;
-  DbcArgs a;
-  a.x = x; a.dy = dy; a.dA = dA_cumsum; a.dtb = dt_bhl; a.A = A; a.U = U;
+  const int S = dbc_slices(d);
+  const int64_t bcg = d.B * d.nc * d.G;
+  float* upart = ws;
+  float* cpart = upart + (size_t)S * bcg * d.Q * d.Q;
+  float* bpart = cpart + (size_t)S * bcg * d.Q * d.N;
+  PartArgs a;
+  a.x = x; a.dA = dA_cumsum; a.dtb = dt_bhl; a.A = A;
   a.L = (int)d.L; a.H = (int)d.H; a.P = (int)d.P; a.N = (int)d.N; a.G = (int)d.G; a.Q = (int)d.Q;
-  a.nc = (int)d.nc;
-  a.TI = d.Q < 64 ? (int)d.Q : 64;
-  a.NT = (int)d.Q / a.TI;
-  a.x_bf16 = x_bf16; a.dy_bf16 = dy_bf16; a.in_bf16 = in_bf16;
-  const int ps = dbc_slice(d, !f32_mma, x_bf16 && dy_bf16 && in_bf16);
-  DbcArgs ac = a, ab = a;  // the dC kernel: B and the forward states; the dB kernel: C and the adjoint's
-  ac.bc = Bm;
-  ac.st = fwd_carried;
-  ac.out = dC;
-  ab.bc = Cm;
-  ab.st = adj_carried_rev;
-  ab.out = dB;
-  if (f32_mma) return launch_dbc_ns<OpF32, 32>(d, ac, ab, s);
-  return ps == 64 ? launch_dbc_ns<OpBF16, 64>(d, ac, ab, s) : launch_dbc_ns<OpBF16, 32>(d, ac, ab, s);
+  a.nc = (int)d.nc; a.S = S; a.hps = (int)((d.H / d.G + S - 1) / S);
+  a.x_bf16 = x_bf16;
+  // dC (and U): column operand dy, forward states; dB: column operand x, adjoint states
+  PartArgs ac = a, ab = a;
+  ac.col = dy; ac.col_bf16 = dy_bf16; ac.st = fwd_carried; ac.uout = upart; ac.sout = cpart;
+  ab.col = x; ab.col_bf16 = x_bf16; ab.st = adj_carried_rev; ab.uout = nullptr; ab.sout = bpart;
+  hipError_t e;
+  // staged head-dimension slice: 64 for bf16 operands from bf16 inputs with
+  // N <= 128, else 32 (bounds the prefetch registers and the LDS)
+  if (f32_mma) e = launch_parts_q<OpF32, 32>(d, ac, ab, s);
+  else if (x_bf16 && dy_bf16 && d.N <= 128) e = launch_parts_q<OpBF16, 64>(d, ac, ab, s);
+  else e = launch_parts_q<OpBF16, 32>(d, ac, ab, s);
+  if (e != hipSuccess) return e;
+  FinArgs f;
+  f.upart = upart; f.cpart = cpart; f.bpart = bpart; f.Bm = Bm; f.Cm = Cm; f.dB = dB; f.dC = dC;
+  f.L = (int)d.L; f.N = (int)d.N; f.G = (int)d.G; f.Q = (int)d.Q; f.nc = (int)d.nc; f.S = S;
+  f.TI = d.Q < 64 ? (int)d.Q : 64;
+  f.NT = (int)d.Q / f.TI;
+  f.in_bf16 = in_bf16;
+  return f32_mma ? launch_fin<OpF32>(d, f, s) : launch_fin<OpBF16>(d, f, s);
 }
 
 }  // namespace ssd
