@@ -92,27 +92,40 @@ __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, float 
   if (i < n) p[i] = v;
 }
 
+// 4 consecutive elements (16-byte aligned group) as fp32
+__device__ __forceinline__ float4 load4_f32(const void* base, int64_t elem, bool bf16) {
+  if (bf16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + elem);
+    return make_float4(bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16), bf16_bits_to_f32(u.y & 0xffffu),
+                       bf16_bits_to_f32(u.y >> 16));
+  }
+  return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+}
+
 // anc[b, h, k] = <g_{kQ}, h_{kQ-1}> for k < nc: for k >= 1 the adjoint's
 // carried state entering its reversed chunk nc-k and the forward's carried
 // state entering chunk k; for k = 0 the adjoint's final state (g_0) and the
 // initial state (zero when absent).  anc[b, h, nc] = <dL/dfinal, final state>
 // (zero when dfinal is absent).  One block per (b, k, h); states are
 // [B, nc, H, N*P], anc is [B, H, nc+1].
-__global__ __launch_bounds__(256) void anchor_dot_kernel(const float* __restrict__ fwd_carried,
+// Carried states are fp32, or bf16 bits when st_bf16 (final, initial and
+// dfinal states are fp32).
+__global__ __launch_bounds__(256) void anchor_dot_kernel(const void* __restrict__ fwd_carried,
                                                          const float* __restrict__ fwd_final,
-                                                         const float* __restrict__ adj_carried,
+                                                         const void* __restrict__ adj_carried,
                                                          const float* __restrict__ adj_final,
                                                          const float* __restrict__ h0,
                                                          const float* __restrict__ dfinal, float* __restrict__ anc,
-                                                         int H, int nc, int64_t NP) {
+                                                         int H, int nc, int64_t NP, int st_bf16) {
   __shared__ float red[256];
   const int tid = threadIdx.x;
   const int h = blockIdx.x % H;
   const int k = (blockIdx.x / H) % (nc + 1);
   const int64_t b = blockIdx.x / H / (nc + 1);
   const int64_t bh = (b * H + h) * NP;
-  const float* gp;
-  const float* hp;
+  const void* gp;
+  const void* hp;
+  bool bf = false;
   if (k == 0) {
     gp = adj_final + bh;
     hp = h0 ? h0 + bh : nullptr;
@@ -120,14 +133,18 @@ __global__ __launch_bounds__(256) void anchor_dot_kernel(const float* __restrict
     gp = dfinal ? dfinal + bh : nullptr;
     hp = fwd_final + bh;
   } else {
-    gp = adj_carried + ((b * nc + (nc - k)) * H + h) * NP;
-    hp = fwd_carried + ((b * nc + k) * H + h) * NP;
+    const int64_t ga = ((b * nc + (nc - k)) * H + h) * NP, ha = ((b * nc + k) * H + h) * NP;
+    bf = st_bf16 != 0;
+    gp = bf ? static_cast<const void*>(static_cast<const uint16_t*>(adj_carried) + ga)
+            : static_cast<const void*>(static_cast<const float*>(adj_carried) + ga);
+    hp = bf ? static_cast<const void*>(static_cast<const uint16_t*>(fwd_carried) + ha)
+            : static_cast<const void*>(static_cast<const float*>(fwd_carried) + ha);
   }
   float sum = 0.f;
   if (gp && hp)
     for (int64_t e = 4 * tid; e < NP; e += 4 * 256) {
-      const float4 gv = *reinterpret_cast<const float4*>(gp + e);
-      const float4 hv = *reinterpret_cast<const float4*>(hp + e);
+      const float4 gv = load4_f32(gp, e, bf);
+      const float4 hv = load4_f32(hp, e, bf);
       sum = fmaf(gv.x, hv.x, fmaf(gv.y, hv.y, fmaf(gv.z, hv.z, fmaf(gv.w, hv.w, sum))));
     }
   red[tid] = sum;
@@ -139,24 +156,15 @@ __global__ __launch_bounds__(256) void anchor_dot_kernel(const float* __restrict
   if (tid == 0) anc[(b * H + h) * (nc + 1) + k] = red[0];
 }
 
-// 4 consecutive elements (16-byte aligned group) as fp32
-__device__ __forceinline__ float4 load4_f32(const void* base, int64_t elem, bool bf16) {
-  if (bf16) {
-    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + elem);
-    return make_float4(bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16), bf16_bits_to_f32(u.y & 0xffffu),
-                       bf16_bits_to_f32(u.y >> 16));
-  }
-  return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
-}
-
 // Per (b, t, h): dx, beta_t = y1_t . x_t (= B_t . g_t x_t), v_t = dy_t . y0_t,
 // u_t = dy_t . x_t.  16 lanes per (b, t, h) row, 4-element groups (P a
 // multiple of 16), four rows per wave; y1 is in reversed time over Lp steps.
+// y0 and y1 are fp32, or bf16 bits when y_bf16.
 __global__ __launch_bounds__(256) void combine_token_kernel(
     const void* __restrict__ dy, int dy_bf16, const void* __restrict__ x, int in_bf16, const float* __restrict__ dt,
-    const float* __restrict__ D, const float* __restrict__ y0, const float* __restrict__ y1, float* __restrict__ dx,
-    float* __restrict__ beta, float* __restrict__ v, float* __restrict__ u, int L, int Lp, int H, int P,
-    int64_t nrows) {
+    const float* __restrict__ D, const void* __restrict__ y0, const void* __restrict__ y1, int y_bf16,
+    float* __restrict__ dx, float* __restrict__ beta, float* __restrict__ v, float* __restrict__ u, int L, int Lp,
+    int H, int P, int64_t nrows) {
   const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 16) + (threadIdx.x >> 4);  // (b * L + t) * H + h
   const int l16 = threadIdx.x & 15;
   if (row >= nrows) return;  // whole 16-lane groups leave together
@@ -169,8 +177,8 @@ __global__ __launch_bounds__(256) void combine_token_kernel(
   float sv = 0.f, su = 0.f, sb = 0.f;
   for (int p = 4 * l16; p < P; p += 64) {
     const float4 dyv = load4_f32(dy, row * P + p, dy_bf16 != 0), xv = load4_f32(x, row * P + p, in_bf16 != 0);
-    const float4 a1 = *reinterpret_cast<const float4*>(y1 + rrow * P + p);
-    const float4 a0 = *reinterpret_cast<const float4*>(y0 + row * P + p);
+    const float4 a1 = load4_f32(y1, rrow * P + p, y_bf16 != 0);
+    const float4 a0 = load4_f32(y0, row * P + p, y_bf16 != 0);
     *reinterpret_cast<float4*>(dx + row * P + p) =
         make_float4(fmaf(dtv, a1.x, dh * dyv.x), fmaf(dtv, a1.y, dh * dyv.y), fmaf(dtv, a1.z, dh * dyv.z),
                     fmaf(dtv, a1.w, dh * dyv.w));
@@ -395,29 +403,38 @@ hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const 
   hipLaunchKernelGGL(fill_kernel, dim3(nblocks(d.H)), dim3(256), 0, s, F(kZeroD), 0.f, (int64_t)d.H);
   BWD_TRY(hipGetLastError());
 
-  // ---- (0) forward: y0 = C^T h (no skip term), fp32 carried states
-  BWD_TRY(launch_chunk_cumsum(d, dt, A, F(kDA0), F(kDt0), s));
-  BWD_TRY(launch_chunk_state(d, x, Bm, in_bf16, F(kDt0), F(kDA0), F(kSt0), f32_mma, s));
-  BWD_TRY(launch_state_passing(d, F(kSt0), F(kSt0), F(kDA0), initial_states, F(kFin0), s));
-  BWD_TRY(launch_chunk_scan(d, x, Bm, Cm, in_bf16, F(kDt0), F(kDA0), F(kSt0), false, F(kZeroD), F(kY0), false,
-                            f32_mma, s));
+  // Intermediates (chunk and carried states, y0, y1) are fp32, and bf16
+  // (rounded to nearest even) with bf16 matrix operands, which round them as
+  // operands anyway; final states and the anchors' sums stay fp32.
+  const bool bfi = !f32_mma;
+
+  // ---- (0) forward: y0 = C^T h (no skip term), carried states h
+  if (chunk_state_hg_supported(d, in_bf16, f32_mma)) {
+    BWD_TRY(launch_chunk_state_cumsum_hg(d, x, Bm, dt, A, F(kDA0), F(kDt0), V(kSt0), bfi, f32_mma, s));
+  } else {
+    BWD_TRY(launch_chunk_cumsum(d, dt, A, F(kDA0), F(kDt0), s));
+    BWD_TRY(launch_chunk_state_any(d, x, Bm, in_bf16, F(kDt0), F(kDA0), V(kSt0), bfi, f32_mma, s));
+  }
+  BWD_TRY(launch_state_passing_any(d, V(kSt0), bfi, V(kSt0), bfi, F(kDA0), initial_states, F(kFin0), s));
+  BWD_TRY(launch_chunk_scan(d, x, Bm, Cm, in_bf16, F(kDt0), F(kDA0), V(kSt0), bfi, F(kZeroD), V(kY0), bfi, f32_mma,
+                            s));
 
   // ---- (1) adjoint in reversed time: decay from the shifted dt, input scale 1
   BWD_TRY(launch_chunk_cumsum(dR, F(kDtRev), A, F(kDA1), F(kDt1), s));
-  BWD_TRY(launch_chunk_state(dR, DyRev, CRev, op_bf16, F(kOnes), F(kDA1), F(kSt1), f32_mma, s));
-  BWD_TRY(launch_state_passing(dR, F(kSt1), F(kSt1), F(kDA1), dfinal, F(kFin1), s));
-  BWD_TRY(launch_chunk_scan(dR, DyRev, CRev, BRev, op_bf16, F(kOnes), F(kDA1), F(kSt1), false, F(kZeroD), F(kY1),
-                            false, f32_mma, s));
+  BWD_TRY(launch_chunk_state_any(dR, DyRev, CRev, op_bf16, F(kOnes), F(kDA1), V(kSt1), bfi, f32_mma, s));
+  BWD_TRY(launch_state_passing_any(dR, V(kSt1), bfi, V(kSt1), bfi, F(kDA1), dfinal, F(kFin1), s));
+  BWD_TRY(launch_chunk_scan(dR, DyRev, CRev, BRev, op_bf16, F(kOnes), F(kDA1), V(kSt1), bfi, F(kZeroD), V(kY1), bfi,
+                            f32_mma, s));
 
   // ---- (2) dB and dC per (chunk, group)
-  BWD_TRY(launch_bwd_dbc(d, x, in_bf16, dy, dy_bf16, Bm, Cm, in_bf16, F(kDA0), F(kDt0), F(kSt0), F(kSt1), A, F(kU),
-                         dB, dC, f32_mma, s));
+  BWD_TRY(launch_bwd_dbc(d, x, in_bf16, dy, dy_bf16, Bm, Cm, in_bf16, F(kDA0), F(kDt0), V(kSt0), V(kSt1), bfi, A,
+                         F(kU), dB, dC, f32_mma, s));
 
   // ---- combine
-  hipLaunchKernelGGL(anchor_dot_kernel, dim3((unsigned)(d.B * (d.nc + 1) * d.H)), dim3(256), 0, s, F(kSt0), F(kFin0),
-                     F(kSt1), F(kFin1), initial_states, dfinal, F(kAnc), H, (int)d.nc, d.N * d.P);
-  hipLaunchKernelGGL(combine_token_kernel, dim3(nblocks(nblh, 16)), dim3(256), 0, s, dy, db, x, ib, dt, D, F(kY0),
-                     F(kY1), dx, F(kBeta), F(kV), F(kUdot), L, Lp, H, P, nblh);
+  hipLaunchKernelGGL(anchor_dot_kernel, dim3((unsigned)(d.B * (d.nc + 1) * d.H)), dim3(256), 0, s, V(kSt0), F(kFin0),
+                     V(kSt1), F(kFin1), initial_states, dfinal, F(kAnc), H, (int)d.nc, d.N * d.P, bfi ? 1 : 0);
+  hipLaunchKernelGGL(combine_token_kernel, dim3(nblocks(nblh, 16)), dim3(256), 0, s, dy, db, x, ib, dt, D, V(kY0),
+                     V(kY1), bfi ? 1 : 0, dx, F(kBeta), F(kV), F(kUdot), L, Lp, H, P, nblh);
   const int64_t nw = d.B * d.H * d.nc;
   hipLaunchKernelGGL(chunk_grad_kernel, dim3(nblocks(nw, 4)), dim3(256), 0, s, dt, A, F(kBeta), F(kV), F(kUdot),
                      F(kAnc), ddt, F(kDAp), F(kDDp), L, H, (int)d.Q, (int)d.nc, nw);

@@ -133,15 +133,16 @@ template <class Op> struct DbcPitch {
 struct PartArgs {
   const void* col;     // [B, L, H, P]: dy (U and dC) or x (dB) -- the column operand
   const void* x;       // [B, L, H, P]: x, the row operand of U
-  const float* st;     // dC: forward carried states [B, nc, H, N, P];
+  const void* st;      // dC: forward carried states [B, nc, H, N, P];
                        // dB: adjoint carried states in reversed chunk order
+                       // (fp32, or bf16 bits when st_bf16)
   const float* dA;     // dA_cumsum [B, H, nc, Q]
   const float* dtb;    // dt_bhl   [B, H, nc, Q]
   const float* A;      // [H]
   float* uout;         // [S, B*nc*G, Q, Q] (tiles on and below the diagonal)
   float* sout;         // [S, B*nc*G, Q, N]
   int L, H, P, N, G, Q, nc, S, hps;
-  int col_bf16, x_bf16;
+  int col_bf16, x_bf16, st_bf16;
 };
 
 template <class Op>
@@ -192,7 +193,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_part_kernel(PartArgs a) {
 
   const int ccpr = PS / (cb16 ? 8 : 4), cepc = cb16 ? 8 : 4;
   const int xcpr = PS / (xb16 ? 8 : 4), xepc = xb16 ? 8 : 4;
-  const int scpr = PS / 4;
+  const bool sb16 = a.st_bf16 != 0;
+  const int scpr = PS / (sb16 ? 8 : 4), sepc = sb16 ? 8 : 4;
 
   uint4 pc[KP], px[KP], pst[KSP];
   float pg[4];
@@ -223,14 +225,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_part_kernel(PartArgs a) {
     }
     if (DO_S) {
       const int64_t sc = KIND_DB ? ((int64_t)b * a.nc + (a.nc - 1 - c)) : ((int64_t)b * a.nc + c);
-      const float* st = a.st + (sc * H + h) * N * P;
+      const int64_t st0 = (sc * H + h) * N * P;
 #pragma unroll
       for (int k = 0; k < KSP; ++k) {
         const int q = tid + T * k;
         pst[k] = make_uint4(0, 0, 0, 0);
         if (q < N * scpr) {
-          const int n = q / scpr, p = p0 + (q - n * scpr) * 4;
-          if (p < P) pst[k] = *reinterpret_cast<const uint4*>(st + (int64_t)n * P + p);
+          const int n = q / scpr, p = p0 + (q - n * scpr) * sepc;
+          if (p < P) pst[k] = load16(a.st, st0 + (int64_t)n * P + p, sb16);
         }
       }
     }
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_part_kernel(PartArgs a) {
         const int q = tid + T * k;
         if (q < N * scpr) {
           const int n = q / scpr;
-          store_piece(sSt + n * PP + (q - n * scpr) * 4, pst[k], false);
+          store_piece(sSt + n * PP + (q - n * scpr) * sepc, pst[k], sb16);
         }
       }
     }
@@ -633,8 +635,8 @@ size_t bwd_dbc_ws_bytes(const Dims& d) {
 
 hipError_t launch_bwd_dbc(const Dims& d, const void* x, bool x_bf16, const void* dy, bool dy_bf16, const void* Bm,
                           const void* Cm, bool in_bf16, const float* dA_cumsum, const float* dt_bhl,
-                          const float* fwd_carried, const float* adj_carried_rev, const float* A, float* ws,
-                          float* dB, float* dC, bool f32_mma, hipStream_t s) {
+                          const void* fwd_carried, const void* adj_carried_rev, bool st_bf16, const float* A,
+                          float* ws, float* dB, float* dC, bool f32_mma, hipStream_t s) {
   if (!bwd_dbc_supported(d)) return hipErrorInvalidValue;
   const int S = dbc_slices(d);
   const int64_t bcg = d.B * d.nc * d.G;
@@ -646,6 +648,7 @@ hipError_t launch_bwd_dbc(const Dims& d, const void* x, bool x_bf16, const void*
   a.L = (int)d.L; a.H = (int)d.H; a.P = (int)d.P; a.N = (int)d.N; a.G = (int)d.G; a.Q = (int)d.Q;
   a.nc = (int)d.nc; a.S = S; a.hps = (int)((d.H / d.G + S - 1) / S);
   a.x_bf16 = x_bf16;
+  a.st_bf16 = st_bf16;
   // dC (and U): column operand dy, forward states; dB: column operand x, adjoint states
   PartArgs ac = a, ab = a;
   ac.col = dy; ac.col_bf16 = dy_bf16; ac.st = fwd_carried; ac.uout = upart; ac.sout = cpart;

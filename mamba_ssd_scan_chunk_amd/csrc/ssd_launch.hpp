@@ -116,17 +116,18 @@ hipError_t launch_decode_step(int64_t Bn, int64_t H, int64_t P, int64_t N, int64
                               bool in_bf16, float* state, void* y, bool y_bf16, hipStream_t stream);
 
 // Gradients of B and C of the chunked forward, summed over each group's heads
-// (bwd_dbc.hip): dA_cumsum / dt_bhl of the forward [B,H,nc,Q], the fp32
-// states entering each chunk [B,nc,H,N,P], and the adjoint's fp32 carried
-// states in reversed chunk order (entry k' is the gradient at the first token
-// of chunk nc-k', or dL/dfinal for k' = 0).  ws: bwd_dbc_ws_bytes of scratch.
+// (bwd_dbc.hip): dA_cumsum / dt_bhl of the forward [B,H,nc,Q], the states
+// entering each chunk [B,nc,H,N,P], and the adjoint's carried states in
+// reversed chunk order (entry k' is the gradient at the first token
+// of chunk nc-k', or dL/dfinal for k' = 0), both fp32 or (st_bf16) bf16
+// bits.  ws: bwd_dbc_ws_bytes of scratch.
 // Q in {32, 64, 128, 256}, N and P multiples of 16 with N <= 256.
 bool bwd_dbc_supported(const Dims& d);
 size_t bwd_dbc_ws_bytes(const Dims& d);
 hipError_t launch_bwd_dbc(const Dims& d, const void* x, bool x_bf16, const void* dy, bool dy_bf16, const void* Bm,
                           const void* Cm, bool in_bf16, const float* dA_cumsum, const float* dt_bhl,
-                          const float* fwd_carried, const float* adj_carried_rev, const float* A, float* ws,
-                          float* dB, float* dC, bool f32_mma, hipStream_t stream);
+                          const void* fwd_carried, const void* adj_carried_rev, bool st_bf16, const float* A,
+                          float* ws, float* dB, float* dC, bool f32_mma, hipStream_t stream);
 
 // Gradients of the forward (see backward.hip); fp32 outputs and accumulation.
 size_t backward_workspace_bytes(const Dims& d);
