@@ -327,15 +327,25 @@ size_t ssd_workspace_bytes_varlen(const ssd_shape* shape);
  * Inputs as for ssd_forward (x, Bm, Cm of dtype `in`; initial_states may be
  * NULL).  Outputs, all fp32 and device: dx like x, ddt [B,L,H], dA [H],
  * dB and dC [B,L,G,N], dD [H], dinitial [B,H,N,P] (may be NULL: not written).
- * Every product runs as a chunked forward pass of this library's kernels (the
- * forward recomputed, the adjoint, and both with the state transposed),
- * followed by elementwise combining kernels.  mma selects the matrix-core
- * operands of those passes as for ssd_forward: SSD_MMA_F32 (fp32 operands) or
- * SSD_MMA_BF16 (operands rounded to bf16 to nearest even, fp32 accumulation,
- * several times faster and about 1e-2 relative accuracy); states, sums and
- * outputs are fp32 in both.  workspace (device, 16-byte aligned) of at least
- * ssd_backward_workspace_bytes(shape) bytes; the shape must also be supported
- * by the chunk scan with P and N swapped.  Errors as for ssd_forward.
+ * The adjoint runs as a chunked pass of this library's forward kernels in
+ * reversed time, the forward is recomputed, dB and dC come from per-chunk
+ * matrix-core kernels summed over each group's heads, and elementwise kernels
+ * combine the rest.  mma selects the matrix-core operands as for ssd_forward:
+ *   SSD_MMA_F32: fp32 operands, fp32 intermediates.  Every output is within
+ *     1e-4 of its oracle value (max |err| / max |ref| per tensor; for ddt
+ *     and dA, relative to the summed magnitude of their terms), and dA within
+ *     about 1e-3 of |dA| itself at the Mamba-2 2.7B-layer shape.
+ *   SSD_MMA_BF16: operands and intermediates (chunk and carried states, the
+ *     recomputed outputs) rounded to bf16, nearest even; fp32 accumulation
+ *     and sums; about 2.4x faster.  dx, dB, dC, dD and dinitial are within
+ *     1e-2 (max |err| / max |ref|), ddt and dA within 1e-2 of the summed
+ *     magnitude of their terms.  ddt_t and dA are sums of terms of both signs
+ *     that can cancel to far below their size (at the 2.7B-layer shape |dA_h|
+ *     is 1e-4 to 6e-3 of that sum), and bf16 rounding of each term is not
+ *     small against such a sum: there, bf16 dA was measured off by 0.2 to 2
+ *     times |dA|.  Use SSD_MMA_F32 where the decay gradients matter.
+ * workspace (device, 16-byte aligned) of at least
+ * ssd_backward_workspace_bytes(shape) bytes.  Errors as for ssd_forward.
  */
 ssd_status ssd_backward(const ssd_shape* shape, const void* x, const float* dt, const float* A, const void* Bm,
                         const void* Cm, const float* D, ssd_dtype in, const float* initial_states, const void* dy,

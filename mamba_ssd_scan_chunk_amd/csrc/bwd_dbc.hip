@@ -628,6 +628,15 @@ bool bwd_dbc_supported(const Dims& d) {
          d.H % d.G == 0;
 }
 
+size_t bwd_dbc_lds_bytes(const Dims& d, bool f32_mma) {
+  const int Q = (int)d.Q, N = (int)d.N, TI = Q < 64 ? Q : 64;
+  if (f32_mma)
+    return std::max({part_lds_bytes<OpF32>(Q, N, 32, true, false), part_lds_bytes<OpF32>(Q, N, 32, false, true),
+                     fin_lds_bytes<OpF32>(Q, TI)});
+  return std::max({part_lds_bytes<OpBF16>(Q, N, 64, true, false), part_lds_bytes<OpBF16>(Q, N, 64, false, true),
+                   fin_lds_bytes<OpBF16>(Q, TI)});
+}
+
 size_t bwd_dbc_ws_bytes(const Dims& d) {
   const size_t S = (size_t)dbc_slices(d), bcg = (size_t)(d.B * d.nc * d.G);
   return sizeof(float) * S * bcg * (size_t)d.Q * ((size_t)d.Q + 2 * (size_t)d.N);

@@ -454,15 +454,9 @@ ssd_status ssd_backward(const ssd_shape* shape, const void* x, const float* dt, 
       !aligned16(dD) || !aligned16(workspace) || (initial_states && !aligned16(initial_states)) ||
       (dfinal && !aligned16(dfinal)) || (dinitial && !aligned16(dinitial)))
     return SSD_ERR_ALIGN;
-  // the transposed passes run the chunk kernels with P and N swapped and one
-  // group per head
-  Dims dT = d;
-  dT.P = d.N;
-  dT.N = d.P;
-  dT.G = d.H;
   const bool f32m = mma == SSD_MMA_F32;
   if (ssd::chunk_state_lds_bytes(d, f32m) > kLdsLimit || ssd::chunk_scan_lds_bytes(d, f32m) > kLdsLimit ||
-      ssd::chunk_scan_lds_bytes(dT, f32m) > kLdsLimit)
+      !ssd::bwd_dbc_supported(d) || ssd::bwd_dbc_lds_bytes(d, f32m) > kLdsLimit)
     return SSD_ERR_UNSUPPORTED;
   // elementwise launches of 256 threads per block over B*L*H*max(P,N) elements
   const int64_t wide = d.P > d.N ? d.P : d.N;

@@ -124,6 +124,8 @@ hipError_t launch_decode_step(int64_t Bn, int64_t H, int64_t P, int64_t N, int64
 // Q in {32, 64, 128, 256}, N and P multiples of 16 with N <= 256.
 bool bwd_dbc_supported(const Dims& d);
 size_t bwd_dbc_ws_bytes(const Dims& d);
+// Largest dynamic LDS any of its kernels takes for the shape and mode.
+size_t bwd_dbc_lds_bytes(const Dims& d, bool f32_mma);
 hipError_t launch_bwd_dbc(const Dims& d, const void* x, bool x_bf16, const void* dy, bool dy_bf16, const void* Bm,
                           const void* Cm, bool in_bf16, const float* dA_cumsum, const float* dt_bhl,
                           const void* fwd_carried, const void* adj_carried_rev, bool st_bf16, const float* A,

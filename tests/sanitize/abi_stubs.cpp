@@ -24,6 +24,8 @@ bool state_fused_supported(const Dims&, bool, bool) { return false; }
 int64_t state_fused_blocks(const Dims& d) { return d.B * d.H; }
 bool decode_step_supported(int64_t P) { return P % 4 == 0 && P <= 1024; }
 size_t backward_workspace_bytes(const Dims& d) { return (size_t)(d.B * d.H) * 4096; }
+bool bwd_dbc_supported(const Dims& d) { return d.N % 16 == 0 && d.P % 16 == 0; }
+size_t bwd_dbc_lds_bytes(const Dims&, bool) { return 0; }
 
 hipError_t launch_chunk_cumsum(const Dims&, const float*, const float*, float*, float*, hipStream_t) {
   reached("chunk_cumsum");
