@@ -249,6 +249,65 @@ def time_fp32_path(ops, torch, t, sh, w, stream, steps):
     return out
 
 
+def sweep_tuning(ops, torch, names, mma, reps=40):
+    """ssd_forward at each workload under every launch choice the tuning table
+    holds (the SSD_TUNE override, read by the library at every call): the
+    heads per block of the chunk-scan kernel, the state path, and for the
+    two-kernel state path the heads per block of the chunk-state kernel.  One
+    JSON line per workload: ms per call of every variant and the fastest."""
+    from mamba_ssd_scan_chunk_amd.inputs import WORKLOADS, workload_inputs
+    stream = torch.cuda.current_stream()
+    for name in names:
+        w = WORKLOADS[name]
+        t = workload_inputs(name).to_torch("cuda")
+        sh = ops.shape_of(t, w.chunk)
+        y_dtype = w.in_dtype if mma == "bf16" else "f32"
+        y = torch.empty(tuple(t["x"].shape), device="cuda",
+                        dtype=torch.bfloat16 if y_dtype == "bf16" else torch.float32)
+        fin = torch.empty((w.batch, w.nheads, w.dstate, w.headdim), device="cuda", dtype=torch.float32)
+        ws = torch.empty(ops.ssd_workspace_bytes(sh), device="cuda", dtype=torch.uint8)
+
+        def time_variant(tune):
+            os.environ["SSD_TUNE"] = tune
+            call = lambda: ops.ssd_forward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], y=y,
+                                           final_states=fin, workspace=ws, mma=mma)
+            for _ in range(10):
+                call()
+            best = None
+            for _ in range(3):
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(reps):
+                    call()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b) / reps
+                best = ms if best is None else min(best, ms)
+            return round(best, 4)
+
+        hpg = w.nheads // w.ngroups
+        divs = [k for k in range(1, hpg + 1) if hpg % k == 0]
+        out = {"workload": name, "mma": mma, "variants": {}}
+        time_variant("")  # clocks and caches warm before the first timed variant
+        out["variants"]["rule"] = time_variant("")
+        scan = {k: time_variant(f"scan_hg={k}") for k in divs}
+        for k, v in scan.items():
+            out["variants"][f"scan_hg={k}"] = v
+        bs = min(scan, key=scan.get)
+        for path in ("fused", "split"):
+            out["variants"][f"path={path},scan_hg={bs}"] = time_variant(f"path={path},scan_hg={bs}")
+        for k in divs:
+            tune = f"path=split,scan_hg={bs},state_hg={k}"
+            out["variants"][tune] = time_variant(tune)
+        os.environ.pop("SSD_TUNE", None)
+        best = min(out["variants"], key=out["variants"].get)
+        out["best"] = {"variant": best, "ms": out["variants"][best], "rule_ms": out["variants"]["rule"]}
+        print(json.dumps(out), flush=True)
+        del t, y, fin, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,6 +334,9 @@ def main():
                     help="back-to-back launches of each call between one pair of events in the per-kernel rows")
     ap.add_argument("--kernel-only", default=None,
                     help="time only this ABI call in the per-kernel loop (for profiling)")
+    ap.add_argument("--sweep-tuning", action="store_true",
+                    help="time ssd_forward under every launch choice of the per-shape tuning table at each "
+                         "workload (or --workload) and print one JSON line per workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the path has no "
@@ -292,6 +354,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+
+    if args.sweep_tuning:
+        names = [args.workload] if args.workload else [n for n in WORKLOADS if WORKLOADS[n].in_dtype == "bf16"]
+        sweep_tuning(ops, torch, names, args.mma)
+        return
 
     name = args.workload or HEADLINE
     w = WORKLOADS[name]

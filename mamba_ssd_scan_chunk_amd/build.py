@@ -20,8 +20,8 @@ LIB_NAME = "libmamba_ssd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "chunk_state_hg.hip", "state_passing.hip", "state_fused.hip",
-           "chunk_scan.hip", "chunk_scan_hg.hip", "decode.hip", "varlen_states.hip", "backward.hip", "bwd_dbc.hip", "ssd_api.cpp",
-           "forward_noalloc.hip"]
+           "chunk_scan.hip", "chunk_scan_hg.hip", "decode.hip", "varlen_states.hip", "backward.hip", "bwd_dbc.hip",
+           "ssd_api.cpp", "tuning.cpp", "forward_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

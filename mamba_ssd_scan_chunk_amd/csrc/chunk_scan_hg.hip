@@ -696,7 +696,9 @@ static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, c
   }
   const int threads = Cfg::T;
   const int npt = (int)(d.P / Cfg::PT);
-  const int HG = pick_heads_per_block(d, npt);
+  int HG = pick_heads_per_block(d, npt);
+  const int tuned = tuning_for(d, F32M).scan_hg;
+  if (tuned > 0 && (d.H / d.G) % tuned == 0) HG = tuned;
   const int nhg = (int)(d.H / d.G) / HG;
   const int64_t nblk = d.B * d.nc * d.G * nhg * npt;
   const int remap = (nblk % 8 == 0) ? 1 : 0;

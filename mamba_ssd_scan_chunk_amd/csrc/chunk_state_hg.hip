@@ -416,6 +416,8 @@ static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, 
     HG = (int)(hpg / k);
     if (base * k >= device_cu_count()) break;
   }
+  const int tuned = tuning_for(d, F32M).state_hg;
+  if (tuned > 0 && hpg % tuned == 0 && tuned <= cap) HG = tuned;
   const size_t lds = Cfg::lds_total + (FUSE ? (size_t)8 * Q * HG : 0) + wts;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -329,7 +329,8 @@ ssd_status forward_run(const Dims& d, const void* x, const float* dt, const floa
   float* dtb = reinterpret_cast<float*>(base + ws.dt_off);
   void* st = base + ws.st_off;
 
-  if (state_fused_supported(d, bf, f32m) && prefer_fused_state(d)) {
+  const int path = tuning_for(d, f32m).path;
+  if (state_fused_supported(d, bf, f32m) && (path == 1 || (path == 0 && prefer_fused_state(d)))) {
     // fused state path: the chunk states never reach memory; the carried
     // states go to the chunk scan as bf16 (its matrix-operand values)
     SSD_TRY(from_hip(launch_chunk_cumsum(d, dt, A, dA, dtb, s)));

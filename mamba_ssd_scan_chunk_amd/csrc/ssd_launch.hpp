@@ -14,6 +14,14 @@ struct Dims {
   int64_t B, L, H, P, N, G, Q, nc;
 };
 
+// Per-shape launch choices (tuning.cpp): path 0 = rule, 1 = fused state
+// walk, 2 = chunk states + state passing; heads per block of the head-group
+// chunk-scan / chunk-state kernels, 0 = rule.
+struct Tuning {
+  int path, scan_hg, state_hg;
+};
+Tuning tuning_for(const Dims& d, bool f32_mma);
+
 // Dynamic LDS bytes each kernel needs for the given shape (0 = unsupported).
 size_t chunk_state_lds_bytes(const Dims& d, bool f32_mma);
 size_t chunk_scan_lds_bytes(const Dims& d, bool f32_mma);

@@ -1,0 +1,83 @@
+// tuning.cpp -- per-shape launch choices of the forward: the state path
+// (fused chunk-state walk, or chunk states + state passing) and the heads per
+// block of the head-group chunk-scan and chunk-state kernels.
+//
+// Page: "Jane Street and NVIDIA optimize three Mamba-2 forward-pass kernels in
+// cuTile" (genainews.tech), tuning paragraph: the block size and occupancy
+// are searched per input shape.  Here the search is offline: every variant
+// was timed at each benchmark shape on MI355X (`bench.py --sweep-tuning`),
+// and the fastest is kept in the table below.  Shapes not in the table take
+// the launchers' rules (every compute unit gets a block; the fused state
+// walk where it has two blocks per compute unit).
+//
+// SSD_TUNE (environment, read at every call) overrides the table for a
+// sweep: comma-separated `path=fused|split`, `scan_hg=<n>`, `state_hg=<n>`;
+// a value that does not apply to the shape (not a divisor of the group's
+// head count, a path the shape does not support) is ignored.
+#include <cstdlib>
+#include <cstring>
+
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+namespace {
+
+struct Entry {
+  int64_t B, L, H, P, N, G, Q;
+  int f32m;
+  Tuning t;
+};
+
+// {B, L, H, P, N, G, Q, fp32 operands, {path, chunk-scan heads per block,
+// chunk-state heads per block}}; 0 = the launcher's rule.
+// The sweep's fastest variant per benchmark shape (bf16 x/B/C); where it
+// matched the rule within the timing noise (~1%), the rule's values are
+// written out.
+const Entry kTable[] = {
+    // Mamba-2 130M layer: 0.0418 ms (rule 0.0431, the same choice)
+    {4, 2048, 24, 64, 128, 1, 256, 0, {2, 3, 3}},
+    // Mamba-2 2.7B layer: 0.1846 ms (rule 0.1854, the same choice)
+    {2, 8192, 80, 64, 128, 1, 256, 0, {2, 20, 20}},
+    // long sequence: 16 heads per chunk-scan block, 0.3165 ms (rule, 32: 0.3380)
+    {1, 65536, 32, 64, 128, 1, 256, 0, {2, 16, 0}},
+    // grouped N = 256: the fused state walk, 0.6059 ms (split path: 0.7193)
+    {8, 4096, 64, 64, 256, 8, 128, 0, {1, 8, 0}},
+    // fp32 operands
+    {2, 8192, 80, 64, 128, 1, 256, 1, {2, 20, 0}},
+    {8, 4096, 64, 64, 256, 8, 128, 1, {2, 8, 0}},
+};
+
+int parse_int(const char* s) {
+  int v = 0;
+  while (*s >= '0' && *s <= '9' && v < 100000) v = v * 10 + (*s++ - '0');
+  return v;
+}
+
+void apply_env(Tuning* t) {
+  const char* s = std::getenv("SSD_TUNE");
+  if (!s) return;
+  while (*s) {
+    if (!std::strncmp(s, "path=fused", 10)) t->path = 1;
+    else if (!std::strncmp(s, "path=split", 10)) t->path = 2;
+    else if (!std::strncmp(s, "scan_hg=", 8)) t->scan_hg = parse_int(s + 8);
+    else if (!std::strncmp(s, "state_hg=", 9)) t->state_hg = parse_int(s + 9);
+    const char* c = std::strchr(s, ',');
+    if (!c) break;
+    s = c + 1;
+  }
+}
+
+}  // namespace
+
+Tuning tuning_for(const Dims& d, bool f32_mma) {
+  Tuning t = {0, 0, 0};
+  for (const Entry& e : kTable)
+    if (e.B == d.B && e.L == d.L && e.H == d.H && e.P == d.P && e.N == d.N && e.G == d.G && e.Q == d.Q &&
+        e.f32m == (f32_mma ? 1 : 0))
+      t = e.t;
+  apply_env(&t);
+  return t;
+}
+
+}  // namespace ssd

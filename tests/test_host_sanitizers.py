@@ -42,7 +42,8 @@ def _run(cmd, **kw):
 def test_abi_host_layer_under_asan_ubsan(tmp_path):
     exe = str(tmp_path / "abi_driver")
     _run(["g++", "-std=c++17", *SAN, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-          "-I", "/opt/rocm/include", os.path.join(CSRC, "ssd_api.cpp"), os.path.join(HERE, "sanitize", "abi_stubs.cpp"),
+          "-I", "/opt/rocm/include", os.path.join(CSRC, "ssd_api.cpp"), os.path.join(CSRC, "tuning.cpp"),
+          os.path.join(HERE, "sanitize", "abi_stubs.cpp"),
           os.path.join(HERE, "sanitize", "abi_driver.cpp"), "-L", "/opt/rocm/lib", "-lamdhip64",
           "-Wl,-rpath,/opt/rocm/lib", "-o", exe])
     r = _run([exe, "60000"], env=ENV, timeout=600)
