@@ -220,10 +220,11 @@ def time_fp32_path(ops, torch, t, sh, w, stream, steps):
     ms = a.elapsed_time(b) / steps
     in_bytes = 2 if w.in_dtype == "bf16" else 4
     costs = algorithmic_costs(w, in_bytes, 4, 4, 4)
-    # as the per-kernel rows of the main loop: a short GPU spin lets the host
-    # queue the events and calls (a long one lets the clocks fall), then REPS
-    # back-to-back launches of each call per event pair
-    reps = 4
+    # as the per-kernel rows of the main loop, a short GPU spin lets the host
+    # queue the events and calls (a long one lets the clocks fall); then ONE
+    # launch per event pair: back-to-back fp32 matrix-core kernels (4 x 0.45 ms)
+    # ran at half speed, below the forward's own rate for the same kernel
+    reps = 1
     spin = spin_cycles(torch, stream, 200)
     evs = {k: [] for k in calls}
     for _ in range(max(3, steps // 5)):
