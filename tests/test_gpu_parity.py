@@ -479,6 +479,7 @@ FUSED_SHAPES = [
     ("q64_n64", 1, 320, 5, 64, 64, 5, 64),
     ("q32_p128", 1, 96, 2, 128, 64, 1, 32),
     ("q64_n128", 1, 256, 4, 64, 128, 2, 64),
+    ("ragged_q32_n128", 1, 200, 4, 64, 128, 2, 32),  # two heads per block, ragged last chunk
 ]
 
 
