@@ -338,8 +338,9 @@ size_t ssd_workspace_bytes_varlen(const ssd_shape* shape);
  *   SSD_MMA_BF16: operands and intermediates (chunk and carried states, the
  *     recomputed outputs) rounded to bf16, nearest even; fp32 accumulation
  *     and sums; about 2.4x faster.  dx, dB, dC, dD and dinitial are within
- *     1e-2 (max |err| / max |ref|), ddt and dA within 1e-2 of the summed
- *     magnitude of their terms.  ddt_t and dA are sums of terms of both signs
+ *     1e-2 (max |err| / max |ref|), ddt and dA within 2e-2 of the summed
+ *     magnitude of their terms (each term carries several bf16-rounded
+ *     intermediates; measured up to ~1e-2).  ddt_t and dA are sums of terms of both signs
  *     that can cancel to far below their size (at the 2.7B-layer shape |dA_h|
  *     is 1e-4 to 6e-3 of that sum), and bf16 rounding of each term is not
  *     small against such a sum: there, bf16 dA was measured off by 0.2 to 2

@@ -3,8 +3,8 @@ against the fp64 gradient oracle (oracle/backward.py, itself pinned by finite
 differences of the brute-force forward), in both matrix-operand modes.
 
 Acceptance: 1e-4 with fp32 matrix operands (the forward's fp32 bar: every
-product runs as an fp32 chunked pass), 1e-2 with bf16 operands (the forward's
-bf16 bar).  dx, dB, dC, dD and dinitial: max|gpu - ref| / max|ref| per tensor.
+product runs in fp32), 1e-2 with bf16 operands (the forward's bf16 bar), and
+2e-2 for ddt and dA with bf16 operands (below).  dx, dB, dC, dD and dinitial: max|gpu - ref| / max|ref| per tensor.
 ddt and dA are sums of terms of both signs that can be much larger than the
 sum (ddt_t = A q_t - A dt_t beta_t + beta_t with q_t = <g_t, h_t>, dA a sum over
 every token), so their error is measured against the size of those terms,
@@ -33,6 +33,16 @@ from oracle import backward as bwd_oracle
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 1e-2}
+# ddt and dA with bf16 matrix operands, against the size of their terms: each
+# term carries several bf16-rounded quantities (chunk and carried states, the
+# recomputed outputs y0 and y1, each rounded at 2^-9 relative), so a few 1e-3
+# up to ~1e-2 of the term size is this mode's accuracy; a wrong index or sign
+# gives errors of order 1 in this norm.
+TOL_DECAY_BF16 = 2e-2
+
+
+def tol_for(key, mma):
+    return TOL_DECAY_BF16 if (mma == "bf16" and key in ("ddt", "dA")) else TOL[mma]
 KEYS = ["dx", "ddt", "dA", "dB", "dC", "dD", "dh0"]
 
 
@@ -83,7 +93,9 @@ BWD_SHAPES = [
     ("grouped", 2, 256, 4, 32, 48, 2, 64),
     ("ragged", 2, 200, 2, 32, 64, 1, 64),       # last chunk of 8 positions
     ("q256", 1, 640, 2, 64, 128, 1, 256),       # the 2.7B-layer head shape, ragged tail
-    ("wide_p", 1, 160, 3, 128, 32, 3, 32),      # P > N: the transposed passes swap them
+    ("wide_p", 1, 160, 3, 128, 32, 3, 32),      # P > N
+    ("q128_n256", 1, 330, 4, 48, 256, 2, 128),  # dB/dC kernels at chunk 128, N = 256, a 48-wide headdim, ragged
+    ("q256_n256", 1, 300, 2, 32, 256, 1, 256),  # chunk 256 with N = 256: dC's state part in its own launch
 ]
 
 
@@ -106,7 +118,7 @@ def test_backward_matches_oracle(shape, in_dtype, dy_dtype, mma):
     errs = grad_errors(g, ref, inp.dt, inp.A)
     say("  " + ", ".join(f"{k} {v:.3g}" for k, v in errs.items()))
     for k in KEYS:
-        assert errs[k] <= TOL[mma], (k, errs[k])
+        assert errs[k] <= tol_for(k, mma), (k, errs[k])
 
 
 def test_backward_without_initial_or_final():
@@ -219,7 +231,7 @@ def test_backward_full_size_sampled_and_identities(workload, mma):
             errs = grad_errors(gs, ref, inp.dt[sl], inp.A[h:h + 1], keys=("dx", "ddt", "dh0"))
             say(f"  head {h} row {b}: " + ", ".join(f"{k} {v:.3g}" for k, v in errs.items()))
             for k, v in errs.items():
-                assert v <= tol, (h, b, k, v)
+                assert v <= tol_for(k, mma), (h, b, k, v)
         e = abs(float(g["dA"][h]) - dA_ref) / dA_scale
         say(f"  head {h}: dA err {e:.3g} (|dA| / sum of |terms| {abs(dA_ref) / dA_scale:.3g})")
-        assert e <= tol
+        assert e <= tol_for("dA", mma)
