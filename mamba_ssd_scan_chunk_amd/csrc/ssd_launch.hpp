@@ -84,7 +84,8 @@ hipError_t launch_state_passing_any(const Dims& d, const void* chunk_states, boo
 // launch_chunk_state + launch_state_passing.  bf16 inputs and operands,
 // N and P multiples of 64, chunk in {32, 64, 128, 256}.
 bool state_fused_supported(const Dims& d, bool in_bf16, bool f32_mma);
-// Blocks the fused state kernel launches for the shape (each walks all chunks).
+// Independent chunk walks of the fused state kernel for the shape, one per
+// (head, state-row block, 64-column slice); a block runs one or two of them.
 int64_t state_fused_blocks(const Dims& d);
 hipError_t launch_state_fused(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
                               const float* dA_cumsum, const float* initial_states, void* carried, bool carried_bf16,

@@ -342,9 +342,10 @@ int state_fused_rows(const Dims& d) { return (d.N % 128 == 0 && d.Q <= 128) ? 12
 // halves the block's B staging per head.
 int state_fused_heads(const Dims& d) { return (state_fused_rows(d) == 128 && (d.H / d.G) % 2 == 0) ? 2 : 1; }
 
-int64_t state_fused_blocks(const Dims& d) {
-  return d.B * (d.H / state_fused_heads(d)) * (d.N / state_fused_rows(d)) * (d.P / 64);
-}
+// Independent walks (head, row block, column slice): a two-head block runs two
+// of them with twice the waves, so this is the parallelism the dispatch rule
+// weighs whatever the heads per block.
+int64_t state_fused_blocks(const Dims& d) { return d.B * d.H * (d.N / state_fused_rows(d)) * (d.P / 64); }
 
 template <int Q, bool CBF16, int NB, int WAVES = 8, int HF = 1>
 static hipError_t launch_sf_inst(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
