@@ -5,6 +5,10 @@ the dominant kernel and the fp64 oracle timed on the host as a CPU baseline.
 
 One step = one ssd_forward call (cumsum -> chunk states -> state passing ->
 fused chunk output) over one batch of the workload, inputs resident in HBM.
+The timed steps alternate between two batches of the same shape (seeds s and
+s + 1, each with its own y), so that no step finds its inputs left in the
+last-level cache by the step before, as consecutive layers of a model would
+not; the rate with every step on the same batch is reported beside it.
 Warm-up runs at least W steps and at least --min-warmup-s seconds of steps
 (GPU clocks ramp under sustained load: a few milliseconds of warm-up measure
 the ramp, not the steady state); both counts are reported.
@@ -157,48 +161,60 @@ def spin_cycles(torch, stream, us):
     return int(1_000_000 * us / max(a.elapsed_time(b) * 1e3, 1.0))
 
 
-def time_backward(ops, torch, t, sh, steps, fwd_ms=None, modes=("bf16", "f32")):
+def time_backward(ops, torch, t, sh, steps, fwd_ms=None, modes=("bf16", "f32"), t_alt=None):
     """ssd_backward at the workload (dy in the input dtype, dL/dfinal given),
-    `steps` calls per matrix-operand mode after two untimed ones."""
+    `steps` calls per matrix-operand mode after two untimed ones; with t_alt
+    the calls alternate between the two batches (each with its own dy)."""
     B, L, H, P = t["x"].shape
     N = t["Bm"].shape[3]
     dev, stream = t["x"].device, torch.cuda.current_stream()
     g = torch.Generator(device=dev).manual_seed(9)
-    dyb = torch.randn((B, L, H, P), device=dev, generator=g).to(t["x"].dtype)
-    dfb = torch.randn((B, H, N, P), device=dev, generator=g)
+    batches = []
+    for tk in (t,) if t_alt is None else (t, t_alt):
+        dyb = torch.randn((B, L, H, P), device=dev, generator=g).to(t["x"].dtype)
+        dfb = torch.randn((B, H, N, P), device=dev, generator=g)
+        batches.append((tk, dyb, dfb))
     wsb = torch.empty(ops.ssd_backward_workspace_bytes(sh), device=dev, dtype=torch.uint8)
     out = {"steps": steps, "workspace_GB": round(wsb.numel() / 1e9, 2)}
     for bm in modes:
-        step_b = lambda: ops.ssd_backward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], dyb, dfinal=dfb,
-                                          workspace=wsb, mma=bm)
-        for _ in range(2):
-            step_b()
+        def step_b(k):
+            tk, dyb, dfb = batches[k % len(batches)]
+            ops.ssd_backward(sh, tk["x"], tk["dt"], tk["A"], tk["Bm"], tk["Cm"], tk["D"], dyb, dfinal=dfb,
+                             workspace=wsb, mma=bm)
+        for k in range(2):
+            step_b(k)
         torch.cuda.synchronize()
         b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         b0.record(stream)
-        for _ in range(steps):
-            step_b()
+        for k in range(steps):
+            step_b(k)
         b1.record(stream)
         torch.cuda.synchronize()
         bms = b0.elapsed_time(b1) / steps
         out[f"mma_{bm}"] = {"ms": round(bms, 4), "tokens_per_s": round(B * L / (bms * 1e-3), 1)}
         if fwd_ms:
             out[f"mma_{bm}"]["vs_forward_ms"] = round(bms / fwd_ms, 2)
-    del dyb, dfb, wsb
+    del batches, wsb
     return out
 
 
-def time_fp32_path(ops, torch, t, sh, w, stream, steps):
-    """ssd_forward with fp32 matrix operands (fp32 y) at the workload, and its
-    chunk-state and chunk-scan kernels against the fp32 matrix-core peak."""
+def time_fp32_path(ops, torch, t, t_alt, sh, w, stream, steps):
+    """ssd_forward with fp32 matrix operands (fp32 y) at the workload, steps
+    alternating between the batches t and t_alt, and its chunk-state and
+    chunk-scan kernels against the fp32 matrix-core peak."""
     B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     nc = -(-L // Q)
     dev = t["x"].device
     y = torch.empty((B, L, H, P), device=dev, dtype=torch.float32)
     fin = torch.empty((B, H, N, P), device=dev, dtype=torch.float32)
     ws = torch.empty(ops.ssd_workspace_bytes(sh), device=dev, dtype=torch.uint8)
-    fwd = lambda: ops.ssd_forward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], y=y, final_states=fin,
-                                  workspace=ws, mma="f32")
+    y_alt = torch.empty_like(y)
+    batches = ((t, y), (t_alt, y_alt))
+
+    def fwd(k):
+        tk, yk = batches[k & 1]
+        ops.ssd_forward(sh, tk["x"], tk["dt"], tk["A"], tk["Bm"], tk["Cm"], tk["D"], y=yk, final_states=fin,
+                        workspace=ws, mma="f32")
     dA = torch.empty((B, H, nc, Q), device=dev, dtype=torch.float32)
     dtb = torch.empty_like(dA)
     st = torch.empty((B, nc, H, N, P), device=dev, dtype=torch.float32)
@@ -208,13 +224,13 @@ def time_fp32_path(ops, torch, t, sh, w, stream, steps):
         "state_passing": lambda: ops.ssd_state_passing(sh, st, dA, carried=st, final_states=fin),
         "chunk_scan": lambda: ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, st, t["D"], y=y, mma="f32"),
     }
-    for _ in range(5):
-        fwd()
+    for k in range(6):
+        fwd(k)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
-    for _ in range(steps):
-        fwd()
+    for k in range(steps):
+        fwd(k)
     b.record(stream)
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / steps
@@ -249,7 +265,7 @@ def time_fp32_path(ops, torch, t, sh, w, stream, steps):
         out["kernels"][k] = {"us_median": round(us, 2), "us_min": round(ts[0], 2), "TFLOPs": round(tf, 2),
                              "mfma_peak_frac": round(tf / MFMA_PEAK_TFLOPS["f32"], 4),
                              "GBps": round(c["bytes"] / (us * 1e-6) / 1e9, 1)}
-    del y, fin, ws, dA, dtb, st
+    del y, y_alt, fin, ws, dA, dtb, st
     return out
 
 
@@ -368,6 +384,7 @@ def main():
     w = WORKLOADS[name]
     inp = workload_inputs(name)
     t = inp.to_torch("cuda")
+    t_alt = workload_inputs(name, seed=w.seed + 1).to_torch("cuda")  # the second batch of the timed loop
     sh = ops.shape_of(t, w.chunk)
     dev = t["x"].device
     in_bytes = 2 if w.in_dtype == "bf16" else 4
@@ -384,15 +401,19 @@ def main():
         print(json.dumps({"workload": name, "backward": bwd}), flush=True)
         return
 
-    def step():
-        ops.ssd_forward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], y=y, final_states=fin,
+    y_alt = torch.empty_like(y)
+    batches = ((t, y), (t_alt, y_alt))
+
+    def step(k=0):
+        tk, yk = batches[k & 1]
+        ops.ssd_forward(sh, tk["x"], tk["dt"], tk["A"], tk["Bm"], tk["Cm"], tk["D"], y=yk, final_states=fin,
                         workspace=ws, mma=args.mma)
 
     # ---- phase 1: whole-path throughput
     warm_run = 0
     warm0 = time.perf_counter()
     while warm_run < args.warmup or time.perf_counter() - warm0 < args.min_warmup_s:
-        step()
+        step(warm_run)
         warm_run += 1
         if warm_run % 16 == 0:
             torch.cuda.synchronize()  # keep the wall clock in step with the GPU
@@ -400,14 +421,24 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for k in range(args.steps):
+        step(k)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
     tokens_per_s = w.tokens / (ms_per_step / 1e3)
+    # the same number of steps all on the first batch
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for _ in range(args.steps):
+        step(0)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    ms_repeat = r0.elapsed_time(r1) / args.steps
+    repeat = {"ms": round(ms_repeat, 5), "tokens_per_s": round(w.tokens / (ms_repeat / 1e3), 1),
+              "note": "every step on the same batch: part of its inputs stay in the last-level cache"}
 
     # Cold-cache forwards (reported beside the line, not as its value): before
     # each timed forward, 1 GiB (four times the last-level cache) is written
@@ -561,18 +592,19 @@ def main():
         st32 = torch.empty((B, nc, H, N, P), device=dev, dtype=torch.float32)
         hb = torch.empty((B, nc, H, N, P), device=dev, dtype=torch.bfloat16)
 
-        def step32():
-            ops.ssd_chunk_cumsum_state(sh, t["x"], t["Bm"], t["dt"], t["A"], dA_cumsum=dA, dt_bhl=dtb, states=st32,
-                                       mma="bf16")
+        def step32(k):
+            tk, yk = batches[k & 1]
+            ops.ssd_chunk_cumsum_state(sh, tk["x"], tk["Bm"], tk["dt"], tk["A"], dA_cumsum=dA, dt_bhl=dtb,
+                                       states=st32, mma="bf16")
             ops.ssd_state_passing(sh, st32, dA, carried=hb, final_states=fin)
-            ops.ssd_chunk_scan(sh, t["x"], t["Bm"], t["Cm"], dtb, dA, hb, t["D"], y=y, mma="bf16")
-        for _ in range(20):
-            step32()
+            ops.ssd_chunk_scan(sh, tk["x"], tk["Bm"], tk["Cm"], dtb, dA, hb, tk["D"], y=yk, mma="bf16")
+        for k in range(20):
+            step32(k)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        for _ in range(args.steps):
-            step32()
+        for k in range(args.steps):
+            step32(k)
         b.record(stream)
         torch.cuda.synchronize()
         ms32 = a.elapsed_time(b) / args.steps
@@ -586,7 +618,7 @@ def main():
     # the fp32 matrix-core peak.
     fp32_path = None
     if args.mma == "bf16" and not args.no_fp32_path and args.kernel_only is None:
-        fp32_path = time_fp32_path(ops, torch, t, sh, w, stream, max(10, args.steps // 2))
+        fp32_path = time_fp32_path(ops, torch, t, t_alt, sh, w, stream, max(10, args.steps // 2))
 
     # Single-token decode step at the same layer shape: DECODE_BATCH sequences,
     # one token each, fp32 state advanced in place (8 N P bytes per (b, h)).
@@ -619,7 +651,8 @@ def main():
         del xd, dtd, Bd, Cd, sd, yd
 
     # Gradient call at the same workload, reported beside the forward.
-    bwd = time_backward(ops, torch, t, sh, args.backward_steps, ms_per_step) if args.backward_steps > 0 else None
+    bwd = (time_backward(ops, torch, t, sh, args.backward_steps, ms_per_step, t_alt=t_alt)
+           if args.backward_steps > 0 else None)
 
     # ssd_chunk_cumsum alone against sequence length at the workload's B and H:
     # at the headline (B L H = 1.3 M tokens x heads, 15.7 MB) launch and ramp
@@ -698,6 +731,7 @@ def main():
         "fp32_mma_path": fp32_path,
         "copy_GBps": round(copy_gbps, 1),
         "cold_cache": cold,
+        "repeat_batch": repeat,
         "decode_step": dec,
         "backward": bwd,
         "cumsum_sweep": sweep,

@@ -114,7 +114,7 @@ struct HgArgs {
   const int* seq_start;  // packed sequences (VARLEN): [B,nc,Q]
   void* y;
   int L, H, P, G, nc, HG;
-  int b, c, g, hbase, p0;
+  int b, c, g, hlast, p0;  // hlast: the block's last head (walked first)
   int64_t tok0;
 };
 
@@ -515,20 +515,20 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     }
   };
 
-  issue_x(a.hbase);
-  issue_h(a.hbase);
+  issue_x(a.hlast);
+  issue_h(a.hlast);
   __syncthreads();  // every wave is done reading Bs (and Cs, with DB) before the tiles overwrite them
   commit(hbuf(0));
   __syncthreads();
 
   for (int hh = 0; hh < a.HG; ++hh) {
-    const int h = a.hbase + hh;
+    const int h = a.hlast - hh;
     cur = hbuf(DB ? (hh & 1) : 0);
     // The prefetch and commit run on every iteration (the last one loads its
     // own head again, unused): with no conditional around them the compiler's
     // memory-counter waits stay exact, so the loads of the next head remain in
     // flight across the whole compute of this one.
-    const int hn = hh + 1 < a.HG ? h + 1 : h;
+    const int hn = hh + 1 < a.HG ? h - 1 : h;
     issue_xmeta(hn);
     const float dsk = a.D[h];
     int ln = lane;
@@ -648,7 +648,11 @@ __global__ __launch_bounds__((HgCfg<Q, NK, CT, F32M>::T)) void chunk_scan_hg_ker
   rest /= G;
   a.c = rest % nc;
   a.b = rest / nc;
-  a.hbase = a.g * (H / G) + hgi * HG;
+  // The block walks its heads from the last to the first: in the forward the
+  // chunk-state kernel, launched just before, walks the same head groups
+  // first to last, so the x rows it read last are the likeliest to be still
+  // in the last-level cache.
+  a.hlast = a.g * (H / G) + hgi * HG + HG - 1;
   a.p0 = pt * HgCfg<Q, NK, CT, F32M>::PT;
   a.tok0 = (int64_t)a.b * L + (int64_t)a.c * Q;
   hg_body<Q, NK, CT, H_BF16, Y_BF16, RAGGED, VARLEN, F32M>(a, hg_smem, threadIdx.x);
