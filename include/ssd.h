@@ -238,6 +238,15 @@ size_t ssd_workspace_bytes(const ssd_shape* shape);
  * else R = 64), the two middle steps are that fused call instead (chunk states
  * never stored, so no bf16 rounding of them).  Results are bit-identical to
  * the separate calls of the path taken, with those state and carried dtypes.
+ * The path and the heads per block of the head-group kernels follow a table
+ * measured per benchmark shape (rules elsewhere); the environment variable
+ * SSD_TUNE, read at every call, overrides them for sweeps (comma-separated
+ * path=fused|split|fwd, scan_hg=<n>, state_hg=<n>; choices that do not apply
+ * are ignored).  path=fwd takes the fused forward kernel (bf16 inputs and
+ * operands, Q = 128, N = 256, P % 64 == 0): chunk states, state advance and
+ * output in one kernel per (batch, head, 64 columns); its final states are
+ * bit-identical to the fused state path, its y equal within the bf16 bar,
+ * not bit for bit, to either composition.
  * initial_states [B,H,N,P] may be NULL (zeros); final_states [B,H,N,P] may be
  * NULL (not written).  workspace: device memory of at least
  * ssd_workspace_bytes(shape) bytes, owned by the caller, contents undefined

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmamba_ssd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "chunk_state_hg.hip", "state_passing.hip", "state_fused.hip",
+SOURCES = ["chunk_cumsum.hip", "chunk_state.hip", "chunk_state_hg.hip", "state_passing.hip", "state_fused.hip", "forward_fused.hip",
            "chunk_scan.hip", "chunk_scan_hg.hip", "decode.hip", "varlen_states.hip", "backward.hip", "bwd_dbc.hip",
            "ssd_api.cpp", "tuning.cpp", "forward_noalloc.hip"]
 

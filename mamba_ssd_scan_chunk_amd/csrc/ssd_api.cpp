@@ -330,6 +330,13 @@ ssd_status forward_run(const Dims& d, const void* x, const float* dt, const floa
   void* st = base + ws.st_off;
 
   const int path = tuning_for(d, f32m).path;
+  if (path == 3 && fwd_fused_supported(d, bf, f32m)) {
+    // fused forward: neither chunk states nor carried states reach memory
+    SSD_TRY(from_hip(launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
+    SSD_TRY(from_hip(launch_fwd_fused(d, x, Bm, Cm, dtb, dA, D, initial_states, y, y_dtype == SSD_BF16,
+                                      final_states, s)));
+    return SSD_OK;
+  }
   if (state_fused_supported(d, bf, f32m) && (path == 1 || (path == 0 && prefer_fused_state(d)))) {
     // fused state path: the chunk states never reach memory; the carried
     // states go to the chunk scan as bf16 (its matrix-operand values)

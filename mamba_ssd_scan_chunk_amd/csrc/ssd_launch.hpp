@@ -15,7 +15,8 @@ struct Dims {
 };
 
 // Per-shape launch choices (tuning.cpp): path 0 = rule, 1 = fused state
-// walk, 2 = chunk states + state passing; heads per block of the head-group
+// walk, 2 = chunk states + state passing, 3 = fused forward (state walk and
+// chunk output in one kernel); heads per block of the head-group
 // chunk-scan / chunk-state kernels, 0 = rule.
 struct Tuning {
   int path, scan_hg, state_hg;
@@ -90,6 +91,15 @@ int64_t state_fused_blocks(const Dims& d);
 hipError_t launch_state_fused(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
                               const float* dA_cumsum, const float* initial_states, void* carried, bool carried_bf16,
                               float* final_states, hipStream_t stream);
+
+// Fused forward (forward_fused.hip): chunk states, state advance and chunk
+// output in one pass per (batch, head, 64-column slice), the running state on
+// chip; reads dA_cumsum / dt_bhl of launch_chunk_cumsum.  bf16 inputs and
+// operands, chunk 128, N = 256, P a multiple of 64.
+bool fwd_fused_supported(const Dims& d, bool in_bf16, bool f32_mma);
+hipError_t launch_fwd_fused(const Dims& d, const void* x, const void* Bm, const void* Cm, const float* dt_bhl,
+                            const float* dA_cumsum, const float* D, const float* initial_states, void* y, bool y_bf16,
+                            float* final_states, hipStream_t stream);
 
 // Head-group variant of the fused chunk output (bf16 inputs; bf16 or, with
 // f32_mma, fp32 operands for M.X and C.H_in; (chunk, N) in {(128,64),

@@ -11,7 +11,7 @@
 // walk where it has two blocks per compute unit).
 //
 // SSD_TUNE (environment, read at every call) overrides the table for a
-// sweep: comma-separated `path=fused|split`, `scan_hg=<n>`, `state_hg=<n>`;
+// sweep: comma-separated `path=fused|split|fwd`, `scan_hg=<n>`, `state_hg=<n>`;
 // a value that does not apply to the shape (not a divisor of the group's
 // head count, a path the shape does not support) is ignored.
 #include <cstdlib>
@@ -60,6 +60,7 @@ void apply_env(Tuning* t) {
   while (*s) {
     if (!std::strncmp(s, "path=fused", 10)) t->path = 1;
     else if (!std::strncmp(s, "path=split", 10)) t->path = 2;
+    else if (!std::strncmp(s, "path=fwd", 8)) t->path = 3;
     else if (!std::strncmp(s, "scan_hg=", 8)) t->scan_hg = parse_int(s + 8);
     else if (!std::strncmp(s, "state_hg=", 9)) t->state_hg = parse_int(s + 9);
     const char* c = std::strchr(s, ',');

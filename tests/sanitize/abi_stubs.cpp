@@ -21,6 +21,7 @@ size_t chunk_scan_lds_bytes(const Dims&, bool) { return 0; }
 bool chunk_state_hg_supported(const Dims&, bool, bool) { return false; }
 bool chunk_scan_hg_supported(const Dims&, bool, bool) { return false; }
 bool state_fused_supported(const Dims&, bool, bool) { return false; }
+bool fwd_fused_supported(const Dims&, bool, bool) { return false; }
 int64_t state_fused_blocks(const Dims& d) { return d.B * d.H; }
 bool decode_step_supported(int64_t P) { return P % 4 == 0 && P <= 1024; }
 size_t backward_workspace_bytes(const Dims& d) { return (size_t)(d.B * d.H) * 4096; }
@@ -31,6 +32,10 @@ hipError_t launch_chunk_cumsum(const Dims&, const float*, const float*, float*, 
   reached("chunk_cumsum");
 }
 hipError_t launch_seq_start(const Dims&, const int*, int*, hipStream_t) { reached("seq_start"); }
+hipError_t launch_fwd_fused(const Dims&, const void*, const void*, const void*, const float*, const float*,
+                            const float*, const float*, void*, bool, float*, hipStream_t) {
+  reached("fwd_fused");
+}
 hipError_t launch_varlen_prep(const Dims&, const float*, const float*, const int*, float*, float*, hipStream_t) {
   reached("varlen_prep");
 }

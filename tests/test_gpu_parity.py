@@ -513,6 +513,42 @@ def test_chunk_state_passing(shape, with_h0, carried_dtype):
         assert torch.equal(car, car2) and torch.equal(fin_g, fin2)
 
 
+# (name, B, L, H, P, N, G, Q): shapes of the fused forward (chunk 128, N 256)
+FWD_FUSED_SHAPES = [
+    ("one_head_pair", 1, 256, 2, 64, 256, 1, 128),
+    ("ragged_g2", 2, 300, 4, 64, 256, 2, 128),
+    ("p128", 1, 512, 2, 128, 256, 1, 128),
+    ("g8_ragged", 2, 600, 16, 64, 256, 8, 128),
+]
+
+
+@pytest.mark.parametrize("with_h0", [False, True])
+@pytest.mark.parametrize("shape", FWD_FUSED_SHAPES, ids=[s[0] for s in FWD_FUSED_SHAPES])
+def test_forward_fused_kernel(shape, with_h0, monkeypatch):
+    """The fused forward (state walk and chunk output in one kernel, taken with
+    the tuning override path=fwd) against the oracle on every element of y
+    and the final states; its final states bit for bit those of the fused
+    state walk (same operands, same order); its y differs in the last bits
+    from both two-kernel compositions (exact per-element decays instead of
+    factorized ones), which shows that the fused kernel ran."""
+    say(f"forward fused kernel {shape} h0={with_h0}")
+    name, B, L, H, P, N, G, Q = shape
+    inp = _inp(shape, "bf16", seed=23, dt_shift=3.0)
+    h0 = _h0(inp) if with_h0 else None
+    monkeypatch.setenv("SSD_TUNE", "path=fwd")
+    y, fin = gpu_forward(inp, "bf16", y_dtype="bf16", h0=h0)
+    yref, fref = oracle().forward(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D, h0=h0)
+    e1, e2 = relerr(y, yref), relerr(fin, fref)
+    say(f"  rel err y {e1:.3g} final {e2:.3g}")
+    assert e1 <= tol_for("bf16") and e2 <= tol_for("bf16")
+    monkeypatch.setenv("SSD_TUNE", "path=fused")
+    y_w, fin_w = gpu_forward(inp, "bf16", y_dtype="bf16", h0=h0)
+    monkeypatch.setenv("SSD_TUNE", "path=split")
+    y_s, _ = gpu_forward(inp, "bf16", y_dtype="bf16", h0=h0)
+    assert torch.equal(fin, fin_w)
+    assert not torch.equal(y, y_w) and not torch.equal(y, y_s)
+
+
 def test_forward_state_path_choice():
     """ssd_forward takes the fused state path when it has at least two blocks
     per compute unit (blocks of 128 state rows where N is a multiple of 128
