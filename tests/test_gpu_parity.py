@@ -519,6 +519,8 @@ FWD_FUSED_SHAPES = [
     ("ragged_g2", 2, 300, 4, 64, 256, 2, 128),
     ("p128", 1, 512, 2, 128, 256, 1, 128),
     ("g8_ragged", 2, 600, 16, 64, 256, 8, 128),
+    ("one_short_chunk", 1, 50, 1, 64, 256, 1, 128),
+    ("p192_three_slices", 1, 300, 3, 192, 256, 3, 128),
 ]
 
 
