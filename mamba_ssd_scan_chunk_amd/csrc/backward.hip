@@ -92,6 +92,14 @@ __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, float 
   if (i < n) p[i] = v;
 }
 
+// Input scale of the reversed adjoint, [B,H,nc,Q] (the dt_bhl layout): 1 on
+// the steps s = cQ + i that carry a forward token (Lp-1-s < L), 0 on the
+// padding steps, whose input rows then contribute nothing whatever they hold.
+__global__ __launch_bounds__(256) void step_mask_kernel(float* __restrict__ p, int L, int Lp, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = (Lp - 1 - (int)(i % Lp)) < L ? 1.f : 0.f;
+}
+
 // 4 consecutive elements (16-byte aligned group) as fp32
 __device__ __forceinline__ float4 load4_f32(const void* base, int64_t elem, bool bf16) {
   if (bf16) {
@@ -393,13 +401,18 @@ hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const 
     return static_cast<const void*>(V(k));
   };
   const int ib = in_bf16 ? 1 : 0, db = dy_bf16 ? 1 : 0;
-  const void* DyRev = gather(dy, db, kDyRev, Lp, H, H, P, 1);
-  const void* BRev = gather(Bm, ib, kBRev, Lp, G, G, N, 1);
-  const void* CRev = gather(Cm, ib, kCRev, Lp, G, G, N, 1);
+  // With bf16 x, B, C and dy on the head-group kernels' shapes, the reversed
+  // pass reads dy, C and B where they are (reversed row addressing) instead
+  // of reversed copies.
+  const bool rev = in_bf16 && dy_bf16 && chunk_state_hg_supported(dR, true, f32_mma) &&
+                   chunk_scan_hg_supported(dR, true, f32_mma);
+  const void* DyRev = rev ? dy : gather(dy, db, kDyRev, Lp, H, H, P, 1);
+  const void* BRev = rev ? Bm : gather(Bm, ib, kBRev, Lp, G, G, N, 1);
+  const void* CRev = rev ? Cm : gather(Cm, ib, kCRev, Lp, G, G, N, 1);
   const int64_t nblh = d.B * d.L * d.H, rblh = d.B * Lp * d.H;
   hipLaunchKernelGGL(shift_reverse_dt_kernel, dim3(nblocks(rblh)), dim3(256), 0, s, dt, F(kDtRev), L, Lp, H, rblh);
   const int64_t nq = d.B * d.H * d.nc * d.Q;
-  hipLaunchKernelGGL(fill_kernel, dim3(nblocks(nq)), dim3(256), 0, s, F(kOnes), 1.f, nq);
+  hipLaunchKernelGGL(step_mask_kernel, dim3(nblocks(nq)), dim3(256), 0, s, F(kOnes), L, Lp, nq);
   hipLaunchKernelGGL(fill_kernel, dim3(nblocks(d.H)), dim3(256), 0, s, F(kZeroD), 0.f, (int64_t)d.H);
   BWD_TRY(hipGetLastError());
 
@@ -421,10 +434,17 @@ hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const 
 
   // ---- (1) adjoint in reversed time: decay from the shifted dt, input scale 1
   BWD_TRY(launch_chunk_cumsum(dR, F(kDtRev), A, F(kDA1), F(kDt1), s));
-  BWD_TRY(launch_chunk_state_any(dR, DyRev, CRev, op_bf16, F(kOnes), F(kDA1), V(kSt1), bfi, f32_mma, s));
+  if (rev)
+    BWD_TRY(launch_chunk_state_hg_rev(dR, DyRev, CRev, F(kOnes), F(kDA1), V(kSt1), bfi, f32_mma, d.L, s));
+  else
+    BWD_TRY(launch_chunk_state_any(dR, DyRev, CRev, op_bf16, F(kOnes), F(kDA1), V(kSt1), bfi, f32_mma, s));
   BWD_TRY(launch_state_passing_any(dR, V(kSt1), bfi, V(kSt1), bfi, F(kDA1), dfinal, F(kFin1), s));
-  BWD_TRY(launch_chunk_scan(dR, DyRev, CRev, BRev, op_bf16, F(kOnes), F(kDA1), V(kSt1), bfi, F(kZeroD), V(kY1), bfi,
-                            f32_mma, s));
+  if (rev)
+    BWD_TRY(launch_chunk_scan_hg_rev(dR, DyRev, CRev, BRev, F(kOnes), F(kDA1), V(kSt1), bfi, F(kZeroD), V(kY1), f32_mma,
+                                     d.L, s));
+  else
+    BWD_TRY(launch_chunk_scan(dR, DyRev, CRev, BRev, op_bf16, F(kOnes), F(kDA1), V(kSt1), bfi, F(kZeroD), V(kY1),
+                              bfi, f32_mma, s));
 
   // ---- (2) dB and dC per (chunk, group)
   BWD_TRY(launch_bwd_dbc(d, x, in_bf16, dy, dy_bf16, Bm, Cm, in_bf16, F(kDA0), F(kDt0), V(kSt0), V(kSt1), bfi, A,

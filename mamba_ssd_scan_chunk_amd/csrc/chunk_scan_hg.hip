@@ -114,6 +114,7 @@ struct HgArgs {
   const int* seq_start;  // packed sequences (VARLEN): [B,nc,Q]
   void* y;
   int L, H, P, G, nc, HG;
+  int lin;  // REV: tokens of the forward input arrays
   int b, c, g, hlast, p0;  // hlast: the block's last head (walked first)
   int64_t tok0;
 };
@@ -148,7 +149,7 @@ __device__ __forceinline__ OpF32::Frag widen_frag8(const OpBF16::Frag& f) {
   return r;
 }
 
-template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED, bool VARLEN, bool F32M>
+template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED, bool VARLEN, bool F32M, bool REV>
 __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, const int tid) {
   using Cfg = HgCfg<Q, NK, CT, F32M>;
   using Op = OpBF16;  // C.B^T (exact: B and C are bf16 inputs)
@@ -211,6 +212,16 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // are not stored
   const int rmax = RAGGED ? min(Q, a.L - a.c * Q) - 1 : Q - 1;
   auto rowc = [&](int r) { return RAGGED ? min(r, rmax) : r; };
+  // REV (the backward's adjoint, run over reversed time; never ragged): x, B
+  // and C are the forward arrays of a.lin tokens; row r of chunk c (step
+  // cQ + r of the L = nc Q steps) reads forward token L-1-(cQ+r), clamped to
+  // lin-1 (the steps past the forward sequence have input scale 0).  Input
+  // rows are addressed from the chunk's first token tokb by the row offset
+  // ro(r); y stays in the kernel's own (reversed) token order.
+  static_assert(!(REV && (RAGGED || VARLEN)), "the reversed reading covers whole chunks");
+  const int64_t tokb = REV ? (int64_t)a.b * a.lin + (a.L - (a.c + 1) * Q) : tok0;
+  const int rmaxr = REV ? a.lin - 1 - (a.L - (a.c + 1) * Q) : 0;
+  auto ro = [&](int r) { return REV ? min(Q - 1 - r, rmaxr) : rowc(r); };
 
   if constexpr (VARLEN)
     for (int j = tid; j < Q; j += T) Sts[j] = a.seq_start[((int64_t)a.b * a.nc + a.c) * Q + j];
@@ -218,11 +229,11 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // 16-byte piece holds n = 8nb .. 8nb+7, whose two 4-element halves land at
   // npos(8nb) and npos(8nb + 4).
   {
-    const int64_t bc0 = (tok0 * G + a.g) * N;  // element offset of (token 0 of the chunk, group g)
+    const int64_t bc0 = (tokb * G + a.g) * N;  // element offset of (token 0 of the chunk, group g)
     const int GN = G * N;
     for (int idx = tid; idx < Q * (N / 8); idx += T) {
       const int j = idx / (N / 8), nb = idx - (idx / (N / 8)) * (N / 8);
-      const int off = rowc(j) * GN + 8 * nb;
+      const int off = ro(j) * GN + 8 * nb;
       const int q0 = j * NPI + npos(8 * nb), q1 = j * NPI + npos(8 * nb + 4);
       const uint4 bv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Bm) + bc0 + off);
       const uint4 cv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Cm) + bc0 + off);
@@ -287,12 +298,12 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   float gref[NWM];
   // x pieces and the token's G, dt (issued at the top of a head) ...
   auto issue_xpiece = [&](int h, int uu) __attribute__((always_inline)) {
-    const uint16_t* xh = static_cast<const uint16_t*>(a.x) + (tok0 * H + h) * (int64_t)P + a.p0;
+    const uint16_t* xh = static_cast<const uint16_t*>(a.x) + (tokb * H + h) * (int64_t)P + a.p0;
     const int blk = tid + uu * T;
     if (blk < NXB) {  // always true; the block boundary keeps the scheduler from hoisting across it
       int row, cb;
       xmap(blk, row, cb);
-      xv[uu] = *reinterpret_cast<const uint4*>(xh + rowc(row) * HP + 8 * cb);
+      xv[uu] = *reinterpret_cast<const uint4*>(xh + ro(row) * HP + 8 * cb);
     }
   };
   auto issue_xmeta = [&](int h) __attribute__((always_inline)) {
@@ -623,12 +634,12 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 // Y_BF16 is a template parameter rather than a run-time flag: a branch around
 // the output stores would make the compiler's memory-counter waits for the
 // prefetched loads conservative (they would also wait for the stores).
-template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED, bool VARLEN, bool F32M>
+template <int Q, int NK, int CT, bool H_BF16, bool Y_BF16, bool RAGGED, bool VARLEN, bool F32M, bool REV = false>
 __global__ __launch_bounds__((HgCfg<Q, NK, CT, F32M>::T)) void chunk_scan_hg_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, const void* __restrict__ Cm,
     const float* __restrict__ dt_bhl, const float* __restrict__ dA_cumsum, const void* __restrict__ carried,
     const float* __restrict__ D, void* __restrict__ y, int L, int H, int P, int G, int nc, int HG,
-    int nhg, int npt, int remap, const int* __restrict__ seq_start) {
+    int nhg, int npt, int remap, const int* __restrict__ seq_start, int lin) {
   extern __shared__ __align__(16) unsigned char hg_smem[];
   // block -> (b, c, g, head group, p slice).  With remap != 0 the mapping is
   // XCD-aware: consecutive logical blocks (same chunk, neighbouring head
@@ -640,6 +651,7 @@ __global__ __launch_bounds__((HgCfg<Q, NK, CT, F32M>::T)) void chunk_scan_hg_ker
   a.x = x; a.Bm = Bm; a.Cm = Cm; a.dt_bhl = dt_bhl; a.dA_cumsum = dA_cumsum; a.carried = carried; a.D = D; a.y = y;
   a.seq_start = seq_start;
   a.L = L; a.H = H; a.P = P; a.G = G; a.nc = nc; a.HG = HG;
+  a.lin = lin;
   const int pt = bid % npt;
   unsigned rest = bid / npt;
   const int hgi = rest % nhg;
@@ -655,7 +667,7 @@ __global__ __launch_bounds__((HgCfg<Q, NK, CT, F32M>::T)) void chunk_scan_hg_ker
   a.hlast = a.g * (H / G) + hgi * HG + HG - 1;
   a.p0 = pt * HgCfg<Q, NK, CT, F32M>::PT;
   a.tok0 = (int64_t)a.b * L + (int64_t)a.c * Q;
-  hg_body<Q, NK, CT, H_BF16, Y_BF16, RAGGED, VARLEN, F32M>(a, hg_smem, threadIdx.x);
+  hg_body<Q, NK, CT, H_BF16, Y_BF16, RAGGED, VARLEN, F32M, REV>(a, hg_smem, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ host side
@@ -687,12 +699,22 @@ static auto pick_hg_kernel(bool ragged, bool varlen) {
 template <int Q, int NK, bool H_BF16, bool F32M>
 static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, const void* Cm, const float* dt_bhl,
                                  const float* dA_cumsum, const void* carried, const float* D, void* y,
-                                 bool y_bf16, hipStream_t stream, const int* seq_start) {
+                                 bool y_bf16, hipStream_t stream, const int* seq_start, int lin = 0) {
   constexpr int CT = 4;
   using Cfg = HgCfg<Q, NK, CT, F32M>;
   const bool ragged = d.L % Q != 0, varlen = seq_start != nullptr;
   auto kern = y_bf16 ? pick_hg_kernel<Q, NK, H_BF16, true, F32M>(ragged, varlen)
                      : pick_hg_kernel<Q, NK, H_BF16, false, F32M>(ragged, varlen);
+  if (lin > 0) {
+    // reversed reading: the backward's precision modes only (bf16 carried
+    // states and y with bf16 operands, fp32 with fp32), whole chunks
+    if constexpr (H_BF16 != F32M) {
+      if (ragged || varlen || y_bf16 != H_BF16) return hipErrorInvalidValue;
+      kern = chunk_scan_hg_kernel<Q, NK, CT, H_BF16, H_BF16, false, false, F32M, true>;
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   const size_t lds = varlen ? Cfg::lds_varlen : Cfg::lds_total;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -707,7 +729,7 @@ static hipError_t launch_hg_inst(const Dims& d, const void* x, const void* Bm, c
   const int64_t nblk = d.B * d.nc * d.G * nhg * npt;
   const int remap = (nblk % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(threads), lds, stream, x, Bm, Cm, dt_bhl, dA_cumsum, carried,
-                     D, y, (int)d.L, (int)d.H, (int)d.P, (int)d.G, (int)d.nc, HG, nhg, npt, remap, seq_start);
+                     D, y, (int)d.L, (int)d.H, (int)d.P, (int)d.G, (int)d.nc, HG, nhg, npt, remap, seq_start, lin);
   return hipGetLastError();
 }
 
@@ -769,6 +791,29 @@ hipError_t launch_chunk_scan_hg(const Dims& d, const void* x, const void* Bm, co
   if (carried_bf16)
     return launch_hg_dtype<true, false>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
   return launch_hg_dtype<false, false>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y, y_bf16, stream, seq_start);
+}
+
+hipError_t launch_chunk_scan_hg_rev(const Dims& d, const void* x, const void* Bm, const void* Cm, const float* dt_bhl,
+                                    const float* dA_cumsum, const void* carried, bool carried_bf16, const float* D,
+                                    void* y, bool f32_mma, int64_t lin, hipStream_t stream) {
+  if (lin <= d.L - d.Q || lin > d.L) return hipErrorInvalidValue;
+  const int64_t key = d.Q * 1000 + d.N;
+#define HG_REV(QQ, NN, KK)                                                                                     \
+  case QQ * 1000 + NN:                                                                                         \
+    return f32_mma ? launch_hg_inst<QQ, KK, false, true>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y,        \
+                                                         carried_bf16, stream, nullptr, (int)lin)               \
+                   : launch_hg_inst<QQ, KK, true, false>(d, x, Bm, Cm, dt_bhl, dA_cumsum, carried, D, y,        \
+                                                         carried_bf16, stream, nullptr, (int)lin);
+  if (carried_bf16 == f32_mma) return hipErrorInvalidValue;
+  switch (key) {
+    HG_REV(128, 64, 2)
+    HG_REV(128, 128, 4)
+    HG_REV(128, 256, 8)
+    HG_REV(256, 64, 2)
+    HG_REV(256, 128, 4)
+    default: return hipErrorInvalidValue;
+  }
+#undef HG_REV
 }
 
 }  // namespace ssd

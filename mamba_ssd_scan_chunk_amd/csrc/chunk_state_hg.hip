@@ -72,12 +72,13 @@ __device__ __forceinline__ OpF32::Frag widen_frag(const OpBF16::Frag& f) {
   return r;
 }
 
-template <int Q, int N, bool FUSE, bool SBF16, bool F32M>
+template <int Q, int N, bool FUSE, bool SBF16, bool F32M, bool REV = false>
 __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bhl,
     const float* __restrict__ dA_cumsum, const float* __restrict__ dt_raw, const float* __restrict__ Avec,
     float* __restrict__ dA_out, float* __restrict__ dt_out, void* __restrict__ states, int L, int H, int P, int G,
-    int nc, int HG, int nhg, int npt, int remap) {
+    int nc, int HG, int nhg, int npt, int remap, int lin) {
+  static_assert(!(REV && FUSE), "the reversed reading serves the non-fused instance");
   using Cfg = ShgCfg<Q, N>;
   using Op = OpBF16;
   using Frag = Op::Frag;
@@ -113,6 +114,14 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   // last token row of the chunk inside the sequence: rows past it (ragged last
   // chunk) re-read this one, and their dt = 0 zeroes their contribution
   const int rmax = min(Q, L - c * Q) - 1;
+  // REV (the backward's adjoint, run over reversed time): the inputs are the
+  // forward arrays of lin tokens; row r of chunk c (step cQ + r of the L = nc Q
+  // steps) reads forward token L-1-(cQ+r), clamped to lin-1 (the steps past
+  // the forward sequence have input scale 0).  Input rows are addressed from
+  // the chunk's first token tokb by the row offset ro(r).
+  const int64_t tokb = REV ? (int64_t)b * lin + (L - (c + 1) * Q) : tok0;
+  const int rmaxr = REV ? lin - 1 - (L - (c + 1) * Q) : rmax;
+  auto ro = [&](int r) { return REV ? min(Q - 1 - r, rmaxr) : min(r, rmax); };
 
   // ---- per-head register prefetch of x pieces and their G, dt
   // Piece blk -> (row, 8-column block cb): 8 consecutive threads take the 8
@@ -144,12 +153,12 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     hcur = hcur2;
   };
   auto issue2 = [&](int h) __attribute__((always_inline)) {
-    const uint16_t* xs = x + (tok0 * H + h) * (int64_t)P + p0;
+    const uint16_t* xs = x + (tokb * H + h) * (int64_t)P + p0;
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       int row, cb;
       xmap(tid + u * T, row, cb);
-      xv2[u] = *reinterpret_cast<const uint4*>(xs + min(row, rmax) * HP + 8 * cb);
+      xv2[u] = *reinterpret_cast<const uint4*>(xs + ro(row) * HP + 8 * cb);
     }
     if constexpr (FUSE) {
       hcur2 = h - hbase;
@@ -168,12 +177,12 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     }
   };
   auto issue = [&](int h) __attribute__((always_inline)) {
-    const uint16_t* xs = x + (tok0 * H + h) * (int64_t)P + p0;
+    const uint16_t* xs = x + (tokb * H + h) * (int64_t)P + p0;
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       int row, cb;
       xmap(tid + u * T, row, cb);
-      xv[u] = *reinterpret_cast<const uint4*>(xs + min(row, rmax) * HP + 8 * cb);
+      xv[u] = *reinterpret_cast<const uint4*>(xs + ro(row) * HP + 8 * cb);
     }
     if constexpr (FUSE) {
       hcur = h - hbase;
@@ -226,12 +235,12 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   // ---- B chunk -> Bn[j][n] (16-byte copies; a row's pieces go to
   // consecutive threads)
   {
-    const uint16_t* bsrc = Bm + (tok0 * G + g) * N;
+    const uint16_t* bsrc = Bm + (tokb * G + g) * N;
     const int GN = G * N;
     for (int blk = tid; blk < Q * (N / 8); blk += T) {
       const int j = blk / (N / 8), cb = blk % (N / 8);
       *reinterpret_cast<uint4*>(Bn + j * BP + 8 * cb) =
-          *reinterpret_cast<const uint4*>(bsrc + min(j, rmax) * GN + 8 * cb);
+          *reinterpret_cast<const uint4*>(bsrc + ro(j) * GN + 8 * cb);
     }
   }
 
@@ -397,12 +406,12 @@ bool chunk_state_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
   return false;
 }
 
-template <int Q, int N, bool FUSE, bool SBF16, bool F32M>
+template <int Q, int N, bool FUSE, bool SBF16, bool F32M, bool REV = false>
 static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
                                   const float* dA_cumsum, const float* dt_raw, const float* A, float* dA_out,
-                                  float* dt_out, void* states, hipStream_t stream) {
+                                  float* dt_out, void* states, hipStream_t stream, int lin = 0) {
   using Cfg = ShgCfg<Q, N>;
-  auto kern = chunk_state_hg_kernel<Q, N, FUSE, SBF16, F32M>;
+  auto kern = chunk_state_hg_kernel<Q, N, FUSE, SBF16, F32M, REV>;
   // with FUSE the block also holds the sums and dt rows of its heads in LDS;
   // with F32M the two weight tables
   const size_t wts = F32M ? (size_t)8 * Q : 0;
@@ -428,7 +437,7 @@ static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, 
   const int remap = (nblk % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(Cfg::T), lds, stream, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(Bm), dt_bhl, dA_cumsum, dt_raw, A, dA_out, dt_out, states,
-                     (int)d.L, (int)d.H, (int)d.P, (int)d.G, (int)d.nc, HG, nhg, npt, remap);
+                     (int)d.L, (int)d.H, (int)d.P, (int)d.G, (int)d.nc, HG, nhg, npt, remap, lin);
   return hipGetLastError();
 }
 
@@ -466,6 +475,25 @@ hipError_t launch_chunk_state_cumsum_hg(const Dims& d, const void* x, const void
   if (d.Q == QQ && d.N == NN)                                                                         \
     return launch_shg_any<QQ, NN, true>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl, states, \
                                         states_bf16, f32_mma, stream);
+  SHG_SHAPES(SHG_LAUNCH)
+#undef SHG_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_state_hg_rev(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
+                                     const float* dA_cumsum, void* states, bool states_bf16, bool f32_mma,
+                                     int64_t lin, hipStream_t stream) {
+  // the backward's two precision modes: bf16 states with bf16 operands, fp32
+  // with fp32
+  if (states_bf16 == f32_mma || lin <= d.L - d.Q || lin > d.L) return hipErrorInvalidValue;
+#define SHG_LAUNCH(QQ, NN)                                                                                    \
+  if (d.Q == QQ && d.N == NN)                                                                                 \
+    return f32_mma ? launch_shg_inst<QQ, NN, false, false, true, true>(d, x, Bm, dt_bhl, dA_cumsum, nullptr,  \
+                                                                       nullptr, nullptr, nullptr, states,     \
+                                                                       stream, (int)lin)                      \
+                   : launch_shg_inst<QQ, NN, false, true, false, true>(d, x, Bm, dt_bhl, dA_cumsum, nullptr,  \
+                                                                       nullptr, nullptr, nullptr, states,     \
+                                                                       stream, (int)lin);
   SHG_SHAPES(SHG_LAUNCH)
 #undef SHG_LAUNCH
   return hipErrorInvalidValue;

@@ -112,6 +112,19 @@ hipError_t launch_chunk_scan_hg(const Dims& d, const void* x, const void* Bm, co
                                 const float* D, void* y, bool y_bf16, bool f32_mma, hipStream_t stream,
                                 const int* seq_start = nullptr);
 
+// The backward's adjoint pass, run over reversed time (d.L = nc*Q steps),
+// reading the forward arrays directly: step s of the pass reads forward token
+// d.L-1-s of the lin-token inputs (d.L - Q < lin <= d.L), clamped to lin-1 --
+// the steps past the forward sequence must have input scale (dt_bhl) 0.  The
+// states / y are written in the pass's own order.  Shapes of the head-group
+// kernels; bf16 states / y with bf16 operands, fp32 with fp32.
+hipError_t launch_chunk_state_hg_rev(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
+                                     const float* dA_cumsum, void* states, bool states_bf16, bool f32_mma,
+                                     int64_t lin, hipStream_t stream);
+hipError_t launch_chunk_scan_hg_rev(const Dims& d, const void* x, const void* Bm, const void* Cm, const float* dt_bhl,
+                                    const float* dA_cumsum, const void* carried, bool carried_bf16, const float* D,
+                                    void* y, bool f32_mma, int64_t lin, hipStream_t stream);
+
 // `carried` holds fp32 values, or bf16 bits when carried_bf16 is set.
 // seq_start (packed sequences, [B,nc,Q] from launch_seq_start, or NULL):
 // interaction and carried-state terms are masked to each row's sequence.
