@@ -219,16 +219,4 @@ __device__ __forceinline__ uint4 pair_tiles_16b(uint2 t0, uint2 t1) {
 }
 __device__ __forceinline__ int pair_tiles_col(int lg) { return 4 * lg + 12 * (lg & 1); }
 
-// Streaming (non-temporal) vector stores: the lines are not kept in L2.  Only
-// for outputs whose writes fill whole lines within a short time; scattered
-// partial-line writes this way cost more than through L2.
-typedef float f32x4v_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void store_stream(float* p, float4 v) {
-  __builtin_nontemporal_store(f32x4v_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4v_t*>(p));
-}
-__device__ __forceinline__ void store_stream(uint16_t* p, uint4 v) {
-  __builtin_nontemporal_store(u32x4v_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v_t*>(p));
-}
-
 }  // namespace ssd
