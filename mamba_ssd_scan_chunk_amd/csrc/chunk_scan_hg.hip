@@ -658,7 +658,10 @@ __global__ __launch_bounds__((HgCfg<Q, NK, CT, F32M>::T)) void chunk_scan_hg_ker
   rest /= nhg;
   a.g = rest % G;
   rest /= G;
-  a.c = rest % nc;
+  // chunks in reverse order: the state step before this kernel (state
+  // passing, or the fused walk) writes the carried states of the last chunks
+  // last, so those are the likeliest to be still cached when read first
+  a.c = nc - 1 - (int)(rest % nc);
   a.b = rest / nc;
   // The block walks its heads from the last to the first: in the forward the
   // chunk-state kernel, launched just before, walks the same head groups
