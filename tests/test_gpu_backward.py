@@ -96,6 +96,10 @@ BWD_SHAPES = [
     ("wide_p", 1, 160, 3, 128, 32, 3, 32),      # P > N
     ("q128_n256", 1, 330, 4, 48, 256, 2, 128),  # dB/dC kernels at chunk 128, N = 256, a 48-wide headdim, ragged
     ("q256_n256", 1, 300, 2, 32, 256, 1, 256),  # chunk 256 with N = 256: dC's state part in its own launch
+    # head-group chunk kernels at chunk 128 (the adjoint reads dy, C, B in
+    # reversed order in place when they are bf16), ragged
+    ("q128_n256_p64", 1, 300, 4, 64, 256, 2, 128),
+    ("q128_n128_p128", 1, 200, 2, 128, 128, 1, 128),
 ]
 
 
@@ -119,6 +123,28 @@ def test_backward_matches_oracle(shape, in_dtype, dy_dtype, mma):
     say("  " + ", ".join(f"{k} {v:.3g}" for k, v in errs.items()))
     for k in KEYS:
         assert errs[k] <= tol_for(k, mma), (k, errs[k])
+
+
+@pytest.mark.parametrize("shape", [s for s in BWD_SHAPES if s[4] % 64 == 0 and (s[7], s[5]) in
+                                   ((256, 128), (128, 256), (128, 128), (256, 64), (128, 64))],
+                         ids=lambda s: s[0])
+def test_backward_reversed_reading_matches_copies(shape):
+    """With bf16 operands, bf16 x, B, C and bf16 dy on the head-group shapes
+    the adjoint pass reads dy, C and B in reversed order where they are; the
+    same dy values passed as fp32 go through reversed bf16 copies instead.
+    The gradients that depend only on the two passes (dx, ddt, dA, dD, the
+    initial-state gradient) are bit for bit the same either way."""
+    name, B, L, H, P, N, G, Q = shape
+    say(f"backward reversed reading vs copies {shape}")
+    inp = make_inputs(B, L, H, P, N, G, Q, in_dtype="bf16", seed=67, dt_shift=2.0)
+    rng = np.random.default_rng(68)
+    dy = torch.from_numpy(rng.standard_normal(inp.x.shape).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    h0 = rng.standard_normal((B, H, N, P)).astype(np.float32)
+    dfin = rng.standard_normal((B, H, N, P)).astype(np.float32)
+    g_rev, _ = run_gpu(inp, dy, h0, dfin, "bf16", "bf16")
+    g_cpy, _ = run_gpu(inp, dy, h0, dfin, "f32", "bf16")
+    for k in ("dx", "ddt", "dA", "dD", "dh0"):
+        assert torch.equal(g_rev[k], g_cpy[k]), k
 
 
 def test_backward_without_initial_or_final():
