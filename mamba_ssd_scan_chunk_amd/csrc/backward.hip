@@ -100,14 +100,21 @@ __global__ __launch_bounds__(256) void step_mask_kernel(float* __restrict__ p, i
   if (i < n) p[i] = (Lp - 1 - (int)(i % Lp)) < L ? 1.f : 0.f;
 }
 
-// 4 consecutive elements (16-byte aligned group) as fp32
-__device__ __forceinline__ float4 load4_f32(const void* base, int64_t elem, bool bf16) {
+// 8 consecutive elements (16-byte aligned group) as fp32
+__device__ __forceinline__ void load8_f32(const void* base, int64_t elem, bool bf16, float (&o)[8]) {
   if (bf16) {
-    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + elem);
-    return make_float4(bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16), bf16_bits_to_f32(u.y & 0xffffu),
-                       bf16_bits_to_f32(u.y >> 16));
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = bf16_bits_to_f32(w[e] & 0xffffu);
+      o[2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
   }
-  return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
 }
 
 // anc[b, h, k] = <g_{kQ}, h_{kQ-1}> for k < nc: for k >= 1 the adjoint's
@@ -125,7 +132,7 @@ __global__ __launch_bounds__(256) void anchor_dot_kernel(const void* __restrict_
                                                          const float* __restrict__ h0,
                                                          const float* __restrict__ dfinal, float* __restrict__ anc,
                                                          int H, int nc, int64_t NP, int st_bf16) {
-  __shared__ float red[256];
+  __shared__ float red[4];
   const int tid = threadIdx.x;
   const int h = blockIdx.x % H;
   const int k = (blockIdx.x / H) % (nc + 1);
@@ -150,32 +157,33 @@ __global__ __launch_bounds__(256) void anchor_dot_kernel(const void* __restrict_
   }
   float sum = 0.f;
   if (gp && hp)
-    for (int64_t e = 4 * tid; e < NP; e += 4 * 256) {
-      const float4 gv = load4_f32(gp, e, bf);
-      const float4 hv = load4_f32(hp, e, bf);
-      sum = fmaf(gv.x, hv.x, fmaf(gv.y, hv.y, fmaf(gv.z, hv.z, fmaf(gv.w, hv.w, sum))));
+    for (int64_t e = 8 * tid; e < NP; e += 8 * 256) {  // N*P is a multiple of 256
+      float gv[8], hv[8];
+      load8_f32(gp, e, bf, gv);
+      load8_f32(hp, e, bf, hv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sum = fmaf(gv[q], hv[q], sum);
     }
-  red[tid] = sum;
+  // wave sums by shuffles, then the four wave partials in order
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = sum;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) anc[(b * H + h) * (nc + 1) + k] = red[0];
+  if (tid == 0) anc[(b * H + h) * (nc + 1) + k] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 // Per (b, t, h): dx, beta_t = y1_t . x_t (= B_t . g_t x_t), v_t = dy_t . y0_t,
-// u_t = dy_t . x_t.  16 lanes per (b, t, h) row, 4-element groups (P a
-// multiple of 16), four rows per wave; y1 is in reversed time over Lp steps.
+// u_t = dy_t . x_t.  8 lanes per (b, t, h) row, 8-element groups (P a
+// multiple of 16), eight rows per wave; y1 is in reversed time over Lp steps.
 // y0 and y1 are fp32, or bf16 bits when y_bf16.
 __global__ __launch_bounds__(256) void combine_token_kernel(
     const void* __restrict__ dy, int dy_bf16, const void* __restrict__ x, int in_bf16, const float* __restrict__ dt,
     const float* __restrict__ D, const void* __restrict__ y0, const void* __restrict__ y1, int y_bf16,
     float* __restrict__ dx, float* __restrict__ beta, float* __restrict__ v, float* __restrict__ u, int L, int Lp,
     int H, int P, int64_t nrows) {
-  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 16) + (threadIdx.x >> 4);  // (b * L + t) * H + h
-  const int l16 = threadIdx.x & 15;
-  if (row >= nrows) return;  // whole 16-lane groups leave together
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 8) + (threadIdx.x >> 3);  // (b * L + t) * H + h
+  const int l8 = threadIdx.x & 7;
+  if (row >= nrows) return;  // whole 8-lane groups leave together
   const int h = (int)(row % H);
   const int64_t bt = row / H;
   const int t = (int)(bt % L);
@@ -183,24 +191,30 @@ __global__ __launch_bounds__(256) void combine_token_kernel(
   const int64_t rrow = (b * Lp + (Lp - 1 - t)) * H + h;  // the same token in reversed time
   const float dtv = dt[row], dh = D[h];
   float sv = 0.f, su = 0.f, sb = 0.f;
-  for (int p = 4 * l16; p < P; p += 64) {
-    const float4 dyv = load4_f32(dy, row * P + p, dy_bf16 != 0), xv = load4_f32(x, row * P + p, in_bf16 != 0);
-    const float4 a1 = load4_f32(y1, rrow * P + p, y_bf16 != 0);
-    const float4 a0 = load4_f32(y0, row * P + p, y_bf16 != 0);
-    *reinterpret_cast<float4*>(dx + row * P + p) =
-        make_float4(fmaf(dtv, a1.x, dh * dyv.x), fmaf(dtv, a1.y, dh * dyv.y), fmaf(dtv, a1.z, dh * dyv.z),
-                    fmaf(dtv, a1.w, dh * dyv.w));
-    sv = fmaf(dyv.x, a0.x, fmaf(dyv.y, a0.y, fmaf(dyv.z, a0.z, fmaf(dyv.w, a0.w, sv))));
-    su = fmaf(dyv.x, xv.x, fmaf(dyv.y, xv.y, fmaf(dyv.z, xv.z, fmaf(dyv.w, xv.w, su))));
-    sb = fmaf(a1.x, xv.x, fmaf(a1.y, xv.y, fmaf(a1.z, xv.z, fmaf(a1.w, xv.w, sb))));
+  for (int p = 8 * l8; p < P; p += 64) {
+    float dyv[8], xv[8], a1[8], a0[8];
+    load8_f32(dy, row * P + p, dy_bf16 != 0, dyv);
+    load8_f32(x, row * P + p, in_bf16 != 0, xv);
+    load8_f32(y1, rrow * P + p, y_bf16 != 0, a1);
+    load8_f32(y0, row * P + p, y_bf16 != 0, a0);
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[e] = fmaf(dtv, a1[e], dh * dyv[e]);
+      sv = fmaf(dyv[e], a0[e], sv);
+      su = fmaf(dyv[e], xv[e], su);
+      sb = fmaf(a1[e], xv[e], sb);
+    }
+    *reinterpret_cast<float4*>(dx + row * P + p) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4*>(dx + row * P + p + 4) = make_float4(o[4], o[5], o[6], o[7]);
   }
 #pragma unroll
-  for (int off = 8; off > 0; off >>= 1) {
-    sv += __shfl_xor(sv, off, 16);
-    su += __shfl_xor(su, off, 16);
-    sb += __shfl_xor(sb, off, 16);
+  for (int off = 4; off > 0; off >>= 1) {
+    sv += __shfl_xor(sv, off, 8);
+    su += __shfl_xor(su, off, 8);
+    sb += __shfl_xor(sb, off, 8);
   }
-  if (l16 == 0) {
+  if (l8 == 0) {
     v[row] = sv;
     u[row] = su;
     beta[row] = sb;
@@ -453,7 +467,7 @@ hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const 
   // ---- combine
   hipLaunchKernelGGL(anchor_dot_kernel, dim3((unsigned)(d.B * (d.nc + 1) * d.H)), dim3(256), 0, s, V(kSt0), F(kFin0),
                      V(kSt1), F(kFin1), initial_states, dfinal, F(kAnc), H, (int)d.nc, d.N * d.P, bfi ? 1 : 0);
-  hipLaunchKernelGGL(combine_token_kernel, dim3(nblocks(nblh, 16)), dim3(256), 0, s, dy, db, x, ib, dt, D, V(kY0),
+  hipLaunchKernelGGL(combine_token_kernel, dim3(nblocks(nblh, 32)), dim3(256), 0, s, dy, db, x, ib, dt, D, V(kY0),
                      V(kY1), bfi ? 1 : 0, dx, F(kBeta), F(kV), F(kUdot), L, Lp, H, P, nblh);
   const int64_t nw = d.B * d.H * d.nc;
   hipLaunchKernelGGL(chunk_grad_kernel, dim3(nblocks(nw, 4)), dim3(256), 0, s, dt, A, F(kBeta), F(kV), F(kUdot),
