@@ -267,6 +267,19 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     }
     cb[sl] = acc;
   }
+  // VARLEN: the latest sequence start over the rows of each of the wave's
+  // two row tiles (wave-uniform; -1: no row starts a sequence in the chunk)
+  int msta = -1, mstb = -1;
+  if constexpr (VARLEN) {
+    int va = Sts[16 * ra + l16], vb = Sts[16 * rb + l16];
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+      va = max(va, __shfl_xor(va, off, 16));
+      vb = max(vb, __shfl_xor(vb, off, 16));
+    }
+    msta = __builtin_amdgcn_readfirstlane(va);
+    mstb = __builtin_amdgcn_readfirstlane(vb);
+  }
   // DB: the C fragments of the wave's two row tiles for C.H_in, in registers
   Frag cfa[DB ? NK : 1], cfb[DB ? NK : 1];
   if constexpr (DB) {
@@ -398,7 +411,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // MFMA sites per branch made the compiler copy accumulators at every merge,
   // each copy waiting for the MFMA results).
   // Off-diagonal pair k of a tile whose diagonal pair is U: M' = CB * Ws[U][j].
-  auto offdiag_frag = [&](auto tsel_c, const int k, const int U, int lg, int sti) -> FragM {
+  auto offdiag_frag = [&](auto tsel_c, const int k, const int U, int lg, int sti, int ms) -> FragM {
     constexpr int TSEL = decltype(tsel_c)::value;
     const float4 w0 = *reinterpret_cast<const float4*>(cur.Ws + U * Q + 32 * k + 4 * lg);
     const float4 w1 = *reinterpret_cast<const float4*>(cur.Ws + U * Q + 32 * k + 16 + 4 * lg);
@@ -407,9 +420,13 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     float m[8] = {c0[0] * w0.x, c0[1] * w0.y, c0[2] * w0.z, c0[3] * w0.w,
                   c1[0] * w1.x, c1[1] * w1.y, c1[2] * w1.z, c1[3] * w1.w};
     if constexpr (VARLEN) {
+      // only pairs left of the tile's latest sequence start hold masked
+      // entries (ms is wave-uniform: a scalar branch)
+      if (ms > 32 * k) {
 #pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8)
-        if (32 * k + 16 * (e8 >> 2) + 4 * lg + (e8 & 3) < sti) m[e8] = 0.f;
+        for (int e8 = 0; e8 < 8; ++e8)
+          if (32 * k + 16 * (e8 >> 2) + 4 * lg + (e8 & 3) < sti) m[e8] = 0.f;
+      }
     }
     return OpM::from_f32(m);
   };
@@ -420,7 +437,8 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   // upper sub-tile of an even tile, whose slot holds the other tile's values,
   // is zeroed outright; that select also keeps the register allocator from
   // copying the accumulators.)
-  auto diag_frag = [&](auto tsel_c, const int k, const int tile, f32x4_t (&acc)[CW], int l16, int lg, int sti) -> FragM {
+  auto diag_frag = [&](auto tsel_c, const int k, const int tile, f32x4_t (&acc)[CW], int l16, int lg, int sti,
+                       int ms) -> FragM {
     constexpr int TSEL = decltype(tsel_c)::value;
     const int i = 16 * tile + l16;  // the token this lane's interaction values and outputs belong to
     // G and dt of the lane's 8 tokens j = 32k + 16t + 4lg + r, read as vectors
@@ -444,7 +462,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 #pragma unroll
     for (int e8 = 0; e8 < 8; ++e8) {
       const int j = 32 * k + 16 * (e8 >> 2) + 4 * lg + (e8 & 3);
-      const bool keep = VARLEN ? (j <= i && j >= sti) : j <= i;
+      const bool keep = VARLEN ? (j <= i && (ms <= 32 * k || j >= sti)) : j <= i;
       const float dec = fast_exp2(keep ? gi - gj[e8] : -INFINITY);
       m[e8] = cvv[e8] * dj[e8] * dec;
     }
@@ -479,14 +497,14 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         }
         if (k <= Ua) {
           FragM mfa;
-          if (k < Ua) mfa = offdiag_frag(std::integral_constant<int, 0>{}, k, Ua, lg, sta);
-          else mfa = diag_frag(std::integral_constant<int, 0>{}, k, ta, acc0, l16, lg, sta);
+          if (k < Ua) mfa = offdiag_frag(std::integral_constant<int, 0>{}, k, Ua, lg, sta, msta);
+          else mfa = diag_frag(std::integral_constant<int, 0>{}, k, ta, acc0, l16, lg, sta, msta);
 #pragma unroll
           for (int c2 = 0; c2 < CW; ++c2) acc0[c2] = OpM::mma(to_m(xf[c2]), mfa, acc0[c2]);
         }
         FragM mfb;
-        if (k < Ub) mfb = offdiag_frag(std::integral_constant<int, 1>{}, k, Ub, lg, stb);
-        else mfb = diag_frag(std::integral_constant<int, 1>{}, k, tb, acc1, l16, lg, stb);
+        if (k < Ub) mfb = offdiag_frag(std::integral_constant<int, 1>{}, k, Ub, lg, stb, mstb);
+        else mfb = diag_frag(std::integral_constant<int, 1>{}, k, tb, acc1, l16, lg, stb, mstb);
 #pragma unroll
         for (int c2 = 0; c2 < CW; ++c2) acc1[c2] = OpM::mma(to_m(xf[c2]), mfb, acc1[c2]);
       }

@@ -420,21 +420,24 @@ ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float
   SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
   SSD_TRY(from_hip(ssd::launch_seq_start(d, seq_idx, sst, s)));
   SSD_TRY(from_hip(ssd::launch_varlen_prep(d, dA, dtb, sst, dAp, dtl, s)));
-  // fp32 carried states on both paths: the per-sequence states read them, and
-  // the chunk scan rounds them to its operand precision itself.  With bf16
-  // matrix operands the chunk states pass through memory as bf16 (in the
-  // bf16 carried-state area), exactly as in ssd_forward.
+  // As in ssd_forward: with bf16 matrix operands the chunk states pass
+  // through memory as bf16 and the state passing writes the carried states in
+  // place over them as bf16 (the values the chunk scan uses as operands, and
+  // the incoming state of the per-sequence states); fp32 throughout with fp32
+  // operands.  The recurrence and the final states stay fp32.
   if (!f32m) {
     uint16_t* sb = reinterpret_cast<uint16_t*>(base + ws.hb_off);
     SSD_TRY(from_hip(ssd::launch_chunk_state_any(d, x, Bm, bf, dtl, dA, sb, true, f32m, s)));
-    SSD_TRY(from_hip(ssd::launch_state_passing_any(d, sb, true, st, false, dAp, initial_states, final_states, s)));
+    SSD_TRY(from_hip(ssd::launch_state_passing_any(d, sb, true, sb, true, dAp, initial_states, final_states, s)));
+    SSD_TRY(from_hip(ssd::launch_varlen_states(d, x, Bm, bf, dtb, dA, sst, sb, true, nseq, seq_last, seq_states, s)));
   } else {
     SSD_TRY(from_hip(ssd::launch_chunk_state(d, x, Bm, bf, dtl, dA, st, f32m, s)));
     SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dAp, initial_states, final_states, s)));
+    SSD_TRY(from_hip(ssd::launch_varlen_states(d, x, Bm, bf, dtb, dA, sst, st, false, nseq, seq_last, seq_states, s)));
   }
-  SSD_TRY(from_hip(ssd::launch_varlen_states(d, x, Bm, bf, dtb, dA, sst, st, nseq, seq_last, seq_states, s)));
-  SSD_TRY(from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, st, false, D, y, y_dtype == SSD_BF16, f32m,
-                                          s, sst)));
+  const void* car = f32m ? static_cast<const void*>(st) : static_cast<const void*>(base + ws.hb_off);
+  SSD_TRY(from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, car, !f32m, D, y, y_dtype == SSD_BF16, f32m, s,
+                                          sst)));
   return SSD_OK;
 }
 

@@ -11,7 +11,9 @@
 // t's sequence inside the chunk (-1: it runs in from before).  One 256-thread
 // block per (requested token, head, 32 x 32 tile of the state): thread
 // (n = tid / 8, p = 4 (tid % 8) .. +3) accumulates its four elements over the
-// chunk's tokens, staged 64 at a time in LDS with their weights applied.
+// chunk's tokens, staged 64 at a time in LDS with their weights applied
+// (one thread per token and 8-element group of each row: 16-byte loads for
+// bf16 inputs).  H_in is fp32, or bf16 bits when carried_bf16.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -22,9 +24,9 @@ constexpr int kVsTok = 64;  // tokens staged per step
 
 __global__ __launch_bounds__(kVsThreads) void varlen_states_kernel(
     const void* __restrict__ x, const void* __restrict__ Bm, int in_bf16, const float* __restrict__ dt_bhl,
-    const float* __restrict__ dA_cumsum, const int* __restrict__ seq_start, const float* __restrict__ carried,
-    const int64_t* __restrict__ last_token, float* __restrict__ out, int64_t ntok, int L, int H, int P, int N, int G,
-    int Q, int nc, int tn, int tp) {
+    const float* __restrict__ dA_cumsum, const int* __restrict__ seq_start, const void* __restrict__ carried,
+    int carried_bf16, const int64_t* __restrict__ last_token, float* __restrict__ out, int64_t ntok, int L, int H,
+    int P, int N, int G, int Q, int nc, int tn, int tp) {
   __shared__ __align__(16) float Bsh[kVsTok][32];
   __shared__ __align__(16) float Xsh[kVsTok][32];
   const int tid = threadIdx.x;
@@ -48,17 +50,25 @@ __global__ __launch_bounds__(kVsThreads) void varlen_states_kernel(
   for (int js = j0; js <= ie; js += kVsTok) {
     const int cnt = min(kVsTok, ie + 1 - js);
     __syncthreads();  // the previous step's reads are done
-    for (int e = tid; e < kVsTok * 32; e += kVsThreads) {
-      const int jj = e >> 5, k = e & 31;
-      float bv = 0.f, xv = 0.f;
+    {
+      // thread -> (token jj = tid / 4, 8-element group k8 = tid % 4); N, P are
+      // multiples of 16, so a group lies wholly inside or outside the range
+      const int jj = tid >> 2, k8 = 8 * (tid & 3);
+      float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       if (jj < cnt) {
         const int j = js + jj;
         const float w = fast_exp(gi - dA_cumsum[bhc * Q + j]) * dt_bhl[bhc * Q + j];
-        if (n0 + k < N) bv = load1_as_f32(Bm, ((tok0 + j) * G + g) * N + n0 + k, in_bf16 != 0) * w;
-        if (p0 + k < P) xv = load1_as_f32(x, ((tok0 + j) * H + h) * P + p0 + k, in_bf16 != 0);
+        if (n0 + k8 < N) {
+          load8_as_f32(Bm, ((tok0 + j) * G + g) * N + n0 + k8, in_bf16 != 0, bv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bv[e] *= w;
+        }
+        if (p0 + k8 < P) load8_as_f32(x, ((tok0 + j) * H + h) * P + p0 + k8, in_bf16 != 0, xv);
       }
-      Bsh[jj][k] = bv;
-      Xsh[jj][k] = xv;
+      *reinterpret_cast<float4*>(&Bsh[jj][k8]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+      *reinterpret_cast<float4*>(&Bsh[jj][k8 + 4]) = make_float4(bv[4], bv[5], bv[6], bv[7]);
+      *reinterpret_cast<float4*>(&Xsh[jj][k8]) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+      *reinterpret_cast<float4*>(&Xsh[jj][k8 + 4]) = make_float4(xv[4], xv[5], xv[6], xv[7]);
     }
     __syncthreads();
     for (int jj = 0; jj < cnt; ++jj) {
@@ -73,24 +83,28 @@ __global__ __launch_bounds__(kVsThreads) void varlen_states_kernel(
   const int n = n0 + nl;
   if (n >= N) return;
   const int64_t NP = (int64_t)N * P;
-  const float* hin = carried + (((int64_t)b * nc + c) * H + h) * NP + (int64_t)n * P;
+  const int64_t hoff = (((int64_t)b * nc + c) * H + h) * NP + (int64_t)n * P;
   const float e = st < 0 ? fast_exp(gi) : 0.f;
   float* o = out + ((int64_t)s * H + h) * NP + (int64_t)n * P;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int p = p0 + pl + r;
-    if (p < P) o[p] = st < 0 ? fmaf(e, hin[p], acc[r]) : acc[r];
+    if (p < P) {
+      const float hin = st < 0 ? load1_as_f32(carried, hoff + p, carried_bf16 != 0) : 0.f;
+      o[p] = st < 0 ? fmaf(e, hin, acc[r]) : acc[r];
+    }
   }
 }
 
 hipError_t launch_varlen_states(const Dims& d, const void* x, const void* Bm, bool in_bf16, const float* dt_bhl,
-                                const float* dA_cumsum, const int* seq_start, const float* carried,
+                                const float* dA_cumsum, const int* seq_start, const void* carried, bool carried_bf16,
                                 int64_t nseq, const int64_t* last_token, float* out, hipStream_t stream) {
   if (nseq <= 0) return hipSuccess;
   const int tn = (int)((d.N + 31) / 32), tp = (int)((d.P + 31) / 32);
   const int64_t nblk = nseq * d.H * tn * tp;
   hipLaunchKernelGGL(varlen_states_kernel, dim3((unsigned)nblk), dim3(kVsThreads), 0, stream, x, Bm, (int)in_bf16,
-                     dt_bhl, dA_cumsum, seq_start, carried, last_token, out, d.B * d.L, (int)d.L, (int)d.H, (int)d.P,
+                     dt_bhl, dA_cumsum, seq_start, carried, (int)carried_bf16, last_token, out, d.B * d.L, (int)d.L,
+                     (int)d.H, (int)d.P,
                      (int)d.N, (int)d.G, (int)d.Q, (int)d.nc, tn, tp);
   return hipGetLastError();
 }
