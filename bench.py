@@ -344,6 +344,8 @@ def main():
                     help="forwards timed one by one after a 1 GiB cache flush (0: skip)")
     ap.add_argument("--decode-batch", type=int, default=64,
                     help="sequences in the timed single-token decode step (0: skip it)")
+    ap.add_argument("--varlen-seqs", type=int, default=16,
+                    help="sequences packed per row for the ssd_forward_varlen line (0: skip it)")
     ap.add_argument("--backward-steps", type=int, default=10,
                     help="gradient calls (ssd_backward) timed at the workload (0: skip)")
     ap.add_argument("--backward-only", default=None, choices=["bf16", "f32"],
@@ -620,6 +622,37 @@ def main():
     if args.mma == "bf16" and not args.no_fp32_path and args.kernel_only is None:
         fp32_path = time_fp32_path(ops, torch, t, t_alt, sh, w, stream, max(10, args.steps // 2))
 
+    # Packed sequences (ssd_forward_varlen) at the same shape: each row cut into
+    # --varlen-seqs sequences at seeded random points, both batches alternating.
+    varlen = None
+    if args.varlen_seqs > 0 and args.kernel_only is None:
+        import numpy as np
+        rng = np.random.default_rng(11)
+        seq = np.zeros((B, L), np.int32)
+        for b in range(B):
+            cuts = np.sort(rng.choice(np.arange(1, L), size=args.varlen_seqs - 1, replace=False))
+            seq[b] = np.searchsorted(cuts, np.arange(L), side="right") + b * args.varlen_seqs
+        seq_t = torch.from_numpy(seq).to(dev)
+        wsv = torch.empty(ops.ssd_workspace_bytes_varlen(sh), device=dev, dtype=torch.uint8)
+
+        def step_v(k):
+            tk, yk = batches[k & 1]
+            ops.ssd_forward_varlen(sh, tk["x"], tk["dt"], tk["A"], tk["Bm"], tk["Cm"], tk["D"], seq_t, y=yk,
+                                   final_states=fin, workspace=wsv, mma=args.mma)
+        for k in range(10):
+            step_v(k)
+        torch.cuda.synchronize()
+        v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        v0.record(stream)
+        for k in range(args.steps):
+            step_v(k)
+        v1.record(stream)
+        torch.cuda.synchronize()
+        vms = v0.elapsed_time(v1) / args.steps
+        varlen = {"sequences_per_row": args.varlen_seqs, "ms": round(vms, 5),
+                  "tokens_per_s": round(w.tokens / (vms * 1e-3), 1), "call": "ssd_forward_varlen"}
+        del seq_t, wsv
+
     # Single-token decode step at the same layer shape: DECODE_BATCH sequences,
     # one token each, fp32 state advanced in place (8 N P bytes per (b, h)).
     dec = None
@@ -733,6 +766,7 @@ def main():
         "cold_cache": cold,
         "repeat_batch": repeat,
         "decode_step": dec,
+        "forward_packed_sequences": varlen,
         "backward": bwd,
         "cumsum_sweep": sweep,
     }

@@ -245,6 +245,10 @@ def ssd_workspace_bytes(shape) -> int:
     return int(load_library().ssd_workspace_bytes(_shape(shape)))
 
 
+def ssd_workspace_bytes_varlen(shape) -> int:
+    return int(load_library().ssd_workspace_bytes_varlen(_shape(shape)))
+
+
 def ssd_forward(shape, x, dt, A, Bm, Cm, D, initial_states=None, y=None, y_dtype=None, final_states=None,
                 want_final=True, workspace=None, mma="bf16", stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """One-call forward.  Returns (y, final_states or None)."""
@@ -350,7 +354,7 @@ def ssd_forward_varlen(shape, x, dt, A, Bm, Cm, D, seq_idx, initial_states=None,
             seq_states = torch.empty((nseq, H, N, P), device=x.device, dtype=torch.float32)
         _req(seq_states, "seq_states", (nseq, H, N, P), f32)
     lib = load_library()
-    need = int(lib.ssd_workspace_bytes_varlen(sh))
+    need = ssd_workspace_bytes_varlen(sh)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=x.device, dtype=torch.uint8)
     if not workspace.is_cuda or not workspace.is_contiguous():
