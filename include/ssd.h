@@ -300,9 +300,10 @@ ssd_status ssd_forward_noalloc(const ssd_shape* shape, const void* x, const floa
  * it with ssd_decode_step; an index outside [0, B*L) leaves its entry
  * untouched.  nseq = 0 allows seq_last, seq_states NULL.  Same arguments and
  * support as ssd_forward otherwise, always through the two-kernel state
- * path (bf16 chunk states with SSD_MMA_BF16, as in ssd_forward; the carried
- * states stay fp32 here); the workspace must hold
- * ssd_workspace_bytes_varlen(shape) bytes.
+ * path (with SSD_MMA_BF16 bf16 chunk states and bf16 carried states, as in
+ * ssd_forward -- the per-sequence states then start from the bf16 carried
+ * state of their chunk; fp32 throughout with SSD_MMA_F32); the workspace
+ * must hold ssd_workspace_bytes_varlen(shape) bytes.
  * Implementation: per chunk position, the start of its sequence inside the
  * chunk masks the interaction tile and the carried-state term; each chunk
  * state collects the chunk's last sequence only, and the state passing
