@@ -429,11 +429,13 @@ ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float
     uint16_t* sb = reinterpret_cast<uint16_t*>(base + ws.hb_off);
     SSD_TRY(from_hip(ssd::launch_chunk_state_any(d, x, Bm, bf, dtl, dA, sb, true, f32m, s)));
     SSD_TRY(from_hip(ssd::launch_state_passing_any(d, sb, true, sb, true, dAp, initial_states, final_states, s)));
-    SSD_TRY(from_hip(ssd::launch_varlen_states(d, x, Bm, bf, dtb, dA, sst, sb, true, nseq, seq_last, seq_states, s)));
+    SSD_TRY(from_hip(
+        ssd::launch_varlen_states(d, x, Bm, bf, dtb, dA, sst, sb, true, nseq, seq_last, seq_states, f32m, s)));
   } else {
     SSD_TRY(from_hip(ssd::launch_chunk_state(d, x, Bm, bf, dtl, dA, st, f32m, s)));
     SSD_TRY(from_hip(ssd::launch_state_passing(d, st, st, dAp, initial_states, final_states, s)));
-    SSD_TRY(from_hip(ssd::launch_varlen_states(d, x, Bm, bf, dtb, dA, sst, st, false, nseq, seq_last, seq_states, s)));
+    SSD_TRY(from_hip(
+        ssd::launch_varlen_states(d, x, Bm, bf, dtb, dA, sst, st, false, nseq, seq_last, seq_states, f32m, s)));
   }
   const void* car = f32m ? static_cast<const void*>(st) : static_cast<const void*>(base + ws.hb_off);
   SSD_TRY(from_hip(ssd::launch_chunk_scan(d, x, Bm, Cm, bf, dtb, dA, car, !f32m, D, y, y_dtype == SSD_BF16, f32m, s,

@@ -135,10 +135,13 @@ hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* Bm, const
 
 // Packed sequences: the state after token last_token[s] (flattened b*L+t) of
 // its sequence, for s < nseq -> out [nseq,H,N,P] fp32; carried = the states
-// entering each chunk [B,nc,H,N,P], fp32 or (carried_bf16) bf16 bits.
+// entering each chunk [B,nc,H,N,P], fp32 or (carried_bf16) bf16 bits.  On
+// the matrix cores (bf16 or, with f32_mma, fp32 operands) for bf16 inputs
+// with N and P multiples of 64, else in fp32 on the vector ALUs.
 hipError_t launch_varlen_states(const Dims& d, const void* x, const void* Bm, bool in_bf16, const float* dt_bhl,
                                 const float* dA_cumsum, const int* seq_start, const void* carried, bool carried_bf16,
-                                int64_t nseq, const int64_t* last_token, float* out, hipStream_t stream);
+                                int64_t nseq, const int64_t* last_token, float* out, bool f32_mma,
+                                hipStream_t stream);
 
 // Single-token recurrent step: state [Bn,H,N,P] fp32 updated in place, y
 // [Bn,H,P].  Supported for P a multiple of 4 up to 1024.

@@ -79,7 +79,7 @@ hipError_t launch_chunk_scan(const Dims&, const void*, const void*, const void*,
   reached("chunk_scan");
 }
 hipError_t launch_varlen_states(const Dims&, const void*, const void*, bool, const float*, const float*, const int*,
-                                const void*, bool, int64_t, const int64_t*, float*, hipStream_t) {
+                                const void*, bool, int64_t, const int64_t*, float*, bool, hipStream_t) {
   reached("varlen_states");
 }
 hipError_t launch_decode_step(int64_t, int64_t, int64_t, int64_t, int64_t, const void*, const float*, const float*,
