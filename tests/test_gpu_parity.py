@@ -652,16 +652,16 @@ def _packed_seq_idx(rows, L):
 
 
 @pytest.mark.parametrize("with_h0", [False, True])
-@pytest.mark.parametrize("mma", ["f32", "bf16"])
+@pytest.mark.parametrize("mma,in_dtype", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")],
+                         ids=["f32", "bf16", "f32_mma_bf16_in"])
 @pytest.mark.parametrize("case", PACKED, ids=[c[0] for c in PACKED])
-def test_forward_packed_sequences(case, mma, with_h0):
+def test_forward_packed_sequences(case, mma, in_dtype, with_h0):
     """Every sequence of a packed row gives the outputs of its own run from a
     zero state (the row's first one from the row's initial state), and the
     final state is that of the row's last sequence."""
     name, B, H, P, N, G, Q, rows = case
     L = sum(rows[0])
-    say(f"packed sequences {name} {mma} h0={with_h0}")
-    in_dtype = "bf16" if mma == "bf16" else "f32"
+    say(f"packed sequences {name} {mma} in={in_dtype} h0={with_h0}")
     inp = make_inputs(B, L, H, P, N, G, Q, in_dtype=in_dtype, seed=17, dt_shift=2.0)
     t = upload(inp)
     sh = ops.shape_of(t, Q)
