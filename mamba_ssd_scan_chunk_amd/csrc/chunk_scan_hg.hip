@@ -310,9 +310,24 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   static_assert(((QT / 2) * Q) % T == 0, "column-factor entries must divide evenly over the block");
   float gref[NWM];
   // x pieces and the token's G, dt (issued at the top of a head) ...
+  // VARLEN: the thread index is laundered through an empty asm at every
+  // issue, so the lane-dependent row offsets are recomputed there instead of
+  // being hoisted out of the head loop and held (64-bit) in registers for the
+  // block's life; the packed-sequence instance would otherwise spill one of
+  // them and reload it, with a wait for every load in flight, inside the
+  // steps.  (The other instances keep them: recomputing costs them more.)
+  auto tid_v = [&]() __attribute__((always_inline)) -> int {
+    if constexpr (VARLEN) {
+      int lt = tid;
+      asm volatile("" : "+v"(lt));
+      return lt;
+    } else {
+      return tid;
+    }
+  };
   auto issue_xpiece = [&](int h, int uu) __attribute__((always_inline)) {
     const uint16_t* xh = static_cast<const uint16_t*>(a.x) + (tokb * H + h) * (int64_t)P + a.p0;
-    const int blk = tid + uu * T;
+    const int blk = tid_v() + uu * T;
     if (blk < NXB) {  // always true; the block boundary keeps the scheduler from hoisting across it
       int row, cb;
       xmap(blk, row, cb);
@@ -323,8 +338,8 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     // every thread loads (and later stores) the values of token tid mod Q:
     // T is a multiple of Q, and branch-free code keeps the memory waits exact
     const int64_t bhc = ((int64_t)a.b * H + h) * nc + a.c;
-    pg = a.dA_cumsum[bhc * Q + (tid & (Q - 1))];
-    pd = a.dt_bhl[bhc * Q + (tid & (Q - 1))];
+    pg = a.dA_cumsum[bhc * Q + (tid_v() & (Q - 1))];
+    pd = a.dt_bhl[bhc * Q + (tid_v() & (Q - 1))];
     const int uq = __builtin_amdgcn_readfirstlane(tid / Q);
 #pragma unroll
     for (int m = 0; m < NWM; ++m) gref[m] = a.dA_cumsum[bhc * Q + 32 * (uq + (T / Q) * m)];
@@ -342,7 +357,7 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     const int64_t hoff = (((int64_t)a.b * nc + a.c) * H + h) * (int64_t)(N * P) + a.p0;
 #pragma unroll
     for (int uu = 0; uu < HPT; ++uu) {
-      const int blk = tid + uu * T;
+      const int blk = tid_v() + uu * T;
       const int n = blk / (PT / HCOL), col = HCOL * (blk % (PT / HCOL));
       if constexpr (H_BF16) {
         if (blk < NHB) hv[uu] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.carried) + hoff + n * P + col);
