@@ -307,7 +307,9 @@ ssd_status ssd_forward_noalloc(const ssd_shape* shape, const void* x, const floa
  * Implementation: per chunk position, the start of its sequence inside the
  * chunk masks the interaction tile and the carried-state term; each chunk
  * state collects the chunk's last sequence only, and the state passing
- * restarts where that sequence began inside the chunk.
+ * restarts where that sequence began inside the chunk.  With bf16 inputs and
+ * SSD_MMA_BF16 the sequence starts, the cumulative sums and both masks are
+ * computed inside the chunk-state kernel (three launches, as ssd_forward).
  */
 ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float* dt, const float* A,
                               const void* Bm, const void* Cm, const float* D, ssd_dtype in,

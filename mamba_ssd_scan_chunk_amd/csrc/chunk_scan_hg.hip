@@ -725,9 +725,11 @@ static int pick_heads_per_block(const Dims& d, int npt) {
 
 template <int Q, int NK, bool H_BF16, bool Y_BF16, bool F32M>
 static auto pick_hg_kernel(bool ragged, bool varlen) {
-  // packed sequences take the guarded-store instance too (their last chunk
-  // may be ragged as well)
-  if (varlen) return chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, true, true, F32M>;
+  // packed sequences: the guarded-store instance only where the last chunk
+  // is ragged as well
+  if (varlen)
+    return ragged ? chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, true, true, F32M>
+                  : chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, false, true, F32M>;
   return ragged ? chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, true, false, F32M>
                 : chunk_scan_hg_kernel<Q, NK, 4, H_BF16, Y_BF16, false, false, F32M>;
 }

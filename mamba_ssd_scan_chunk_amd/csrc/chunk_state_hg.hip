@@ -72,13 +72,15 @@ __device__ __forceinline__ OpF32::Frag widen_frag(const OpBF16::Frag& f) {
   return r;
 }
 
-template <int Q, int N, bool FUSE, bool SBF16, bool F32M, bool REV = false>
+template <int Q, int N, bool FUSE, bool SBF16, bool F32M, bool REV = false, bool VL = false>
 __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const float* __restrict__ dt_bhl,
     const float* __restrict__ dA_cumsum, const float* __restrict__ dt_raw, const float* __restrict__ Avec,
     float* __restrict__ dA_out, float* __restrict__ dt_out, void* __restrict__ states, int L, int H, int P, int G,
-    int nc, int HG, int nhg, int npt, int remap, int lin) {
+    int nc, int HG, int nhg, int npt, int remap, int lin, const int* __restrict__ seq_idx,
+    int* __restrict__ seq_start_out, float* __restrict__ dA_pass) {
   static_assert(!(REV && FUSE), "the reversed reading serves the non-fused instance");
+  static_assert(!VL || (FUSE && !F32M), "the packed-sequence steps ride on the fused cumulative sum");
   using Cfg = ShgCfg<Q, N>;
   using Op = OpBF16;
   using Frag = Op::Frag;
@@ -94,6 +96,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   float* Gsa = reinterpret_cast<float*>(Xn + Q * XP);     // [HG][Q] log-space sums (FUSE)
   float* Dsa = Gsa + HG * Q;                               // [HG][Q] dt (FUSE)
   float* Wt = Gsa + (FUSE ? 2 * HG * Q : 0);               // [2][Q] weights of the two x buffers (F32M)
+  int* Sts = reinterpret_cast<int*>(Wt);                   // [Q] sequence start of each row (VL)
 
   const unsigned nblk = gridDim.x;
   unsigned bid = blockIdx.x;
@@ -200,6 +203,10 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
       glast = gsrc[Q - 1];
     }
   };
+  // VL: in-chunk start of the sequence holding the chunk's last token (-1:
+  // it runs in from an earlier chunk); rows before it do not reach the state
+  // the chunk hands on
+  int st_last = -1;
   auto commit = [&](uint16_t* dst, float* wdst) __attribute__((always_inline)) {
     if constexpr (FUSE) glast = Gsa[hcur * Q + Q - 1];
 #pragma unroll
@@ -209,6 +216,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
       if constexpr (FUSE) {
         gv[u] = Gsa[hcur * Q + row];
         dv[u] = Dsa[hcur * Q + row];
+        if constexpr (VL) dv[u] = row >= st_last ? dv[u] : 0.f;
       }
       const float w = fast_exp(glast - gv[u]) * dv[u];
       const uint4 q = xv[u];
@@ -266,6 +274,35 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
         Dsa[hh * Q + i] = i <= rmax ? dt_raw[(tok0 + i) * H + hbase + hh] : 0.f;
       }
     }
+    if constexpr (VL) {
+      // packed sequences: wave 0 finds, for every row i, the in-chunk start of
+      // its sequence (the last position <= i where seq_idx changes from the
+      // token before, -1 if none): a per-lane run over E rows, then a
+      // log-depth max-scan across the lanes; rows past the sequence end repeat
+      // the last valid row's value
+      if (wave == 0) {
+        constexpr int E = Q / 64;
+        const int lane = tid & 63;
+        const int* sq = seq_idx + tok0;
+        int run = -1, loc[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = lane * E + e;
+          if (i <= rmax && c * Q + i > 0 && sq[i] != sq[i - 1]) run = i;
+          loc[e] = run;
+        }
+        int tot = run;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(tot, off, 64);
+          if (lane >= off) tot = max(tot, o);
+        }
+        int excl = __shfl_up(tot, 1, 64);
+        if (lane == 0) excl = -1;
+#pragma unroll
+        for (int e = 0; e < E; ++e) Sts[lane * E + e] = max(excl, loc[e]);
+      }
+    }
     __syncthreads();
     constexpr int E = Q / 64;
     const int lane = tid & 63;
@@ -285,6 +322,21 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
         const int64_t o = (((int64_t)b * H + hbase + hh) * nc + c) * Q + 4 * i4;
         *reinterpret_cast<float4*>(dA_out + o) = *reinterpret_cast<const float4*>(Gsa + hh * Q + 4 * i4);
         *reinterpret_cast<float4*>(dt_out + o) = *reinterpret_cast<const float4*>(Dsa + hh * Q + 4 * i4);
+      }
+    }
+    if constexpr (VL) {
+      st_last = __builtin_amdgcn_readfirstlane(Sts[Q - 1]);
+      if (pt == 0) {
+        // the state passing reads one decay per chunk, at position Q-1: -inf
+        // where the chunk's last sequence starts inside it (the incoming state
+        // then decays to exactly 0); no other entry of dA_pass is written
+        for (int hh = tid; hh < HG; hh += T) {
+          const int64_t o = (((int64_t)b * H + hbase + hh) * nc + c) * Q + Q - 1;
+          dA_pass[o] = st_last >= 0 ? -INFINITY : Gsa[hh * Q + Q - 1];
+        }
+        // one block per (b, c) hands the row starts on to the chunk scan
+        if (hgi == 0 && g == 0)
+          for (int i = tid; i < Q; i += T) seq_start_out[((int64_t)b * nc + c) * Q + i] = Sts[i];
       }
     }
   }
@@ -406,15 +458,27 @@ bool chunk_state_hg_supported(const Dims& d, bool in_bf16, bool f32_mma) {
   return false;
 }
 
-template <int Q, int N, bool FUSE, bool SBF16, bool F32M, bool REV = false>
+bool chunk_state_hg_varlen_supported(const Dims& d) {
+  // the fused instance plus one row of Q sequence starts
+  if (d.P % 64 != 0) return false;
+#define SHG_MATCH(QQ, NN) \
+  if (d.Q == QQ && d.N == NN) return ShgCfg<QQ, NN>::lds_total + 12 * (size_t)d.Q <= 160 * 1024;
+  SHG_SHAPES(SHG_MATCH)
+#undef SHG_MATCH
+  return false;
+}
+
+template <int Q, int N, bool FUSE, bool SBF16, bool F32M, bool REV = false, bool VL = false>
 static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, const float* dt_bhl,
                                   const float* dA_cumsum, const float* dt_raw, const float* A, float* dA_out,
-                                  float* dt_out, void* states, hipStream_t stream, int lin = 0) {
+                                  float* dt_out, void* states, hipStream_t stream, int lin = 0,
+                                  const int* seq_idx = nullptr, int* seq_start = nullptr,
+                                  float* dA_pass = nullptr) {
   using Cfg = ShgCfg<Q, N>;
-  auto kern = chunk_state_hg_kernel<Q, N, FUSE, SBF16, F32M, REV>;
+  auto kern = chunk_state_hg_kernel<Q, N, FUSE, SBF16, F32M, REV, VL>;
   // with FUSE the block also holds the sums and dt rows of its heads in LDS;
-  // with F32M the two weight tables
-  const size_t wts = F32M ? (size_t)8 * Q : 0;
+  // with F32M the two weight tables, with VL the row of sequence starts
+  const size_t wts = F32M ? (size_t)8 * Q : (VL ? (size_t)4 * Q : 0);
   const int64_t cap = FUSE ? (int64_t)((160 * 1024 - Cfg::lds_total - wts) / (8 * Q)) : (int64_t)1 << 30;
   const int npt = (int)(d.P / Cfg::PT);
   const int64_t hpg = d.H / d.G;
@@ -437,7 +501,8 @@ static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, 
   const int remap = (nblk % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(Cfg::T), lds, stream, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(Bm), dt_bhl, dA_cumsum, dt_raw, A, dA_out, dt_out, states,
-                     (int)d.L, (int)d.H, (int)d.P, (int)d.G, (int)d.nc, HG, nhg, npt, remap, lin);
+                     (int)d.L, (int)d.H, (int)d.P, (int)d.G, (int)d.nc, HG, nhg, npt, remap, lin, seq_idx,
+                     seq_start, dA_pass);
   return hipGetLastError();
 }
 
@@ -475,6 +540,19 @@ hipError_t launch_chunk_state_cumsum_hg(const Dims& d, const void* x, const void
   if (d.Q == QQ && d.N == NN)                                                                         \
     return launch_shg_any<QQ, NN, true>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, dt_bhl, states, \
                                         states_bf16, f32_mma, stream);
+  SHG_SHAPES(SHG_LAUNCH)
+#undef SHG_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_state_cumsum_hg_varlen(const Dims& d, const void* x, const void* Bm, const float* dt,
+                                               const float* A, const int* seq_idx, float* dA_cumsum, float* dt_bhl,
+                                               int* seq_start, float* dA_pass, void* states, hipStream_t stream) {
+#define SHG_LAUNCH(QQ, NN)                                                                                  \
+  if (d.Q == QQ && d.N == NN)                                                                               \
+    return launch_shg_inst<QQ, NN, true, true, false, false, true>(d, x, Bm, nullptr, nullptr, dt, A, dA_cumsum, \
+                                                                   dt_bhl, states, stream, 0, seq_idx,       \
+                                                                   seq_start, dA_pass);
   SHG_SHAPES(SHG_LAUNCH)
 #undef SHG_LAUNCH
   return hipErrorInvalidValue;

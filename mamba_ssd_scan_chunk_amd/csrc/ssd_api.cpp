@@ -416,10 +416,15 @@ ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float
 
   // the two-kernel state path, fed with the packed-sequence masks: chunk
   // states of each chunk's last sequence only, and a state passing that
-  // restarts where a sequence starts inside a chunk
-  SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
-  SSD_TRY(from_hip(ssd::launch_seq_start(d, seq_idx, sst, s)));
-  SSD_TRY(from_hip(ssd::launch_varlen_prep(d, dA, dtb, sst, dAp, dtl, s)));
+  // restarts where a sequence starts inside a chunk.  With bf16 inputs and
+  // operands one chunk-state kernel also takes the cumulative sums, the
+  // sequence starts and both masks; otherwise three small steps come first.
+  const bool fused = bf && !f32m && ssd::chunk_state_hg_varlen_supported(d);
+  if (!fused) {
+    SSD_TRY(from_hip(ssd::launch_chunk_cumsum(d, dt, A, dA, dtb, s)));
+    SSD_TRY(from_hip(ssd::launch_seq_start(d, seq_idx, sst, s)));
+    SSD_TRY(from_hip(ssd::launch_varlen_prep(d, dA, dtb, sst, dAp, dtl, s)));
+  }
   // As in ssd_forward: with bf16 matrix operands the chunk states pass
   // through memory as bf16 and the state passing writes the carried states in
   // place over them as bf16 (the values the chunk scan uses as operands, and
@@ -427,7 +432,10 @@ ssd_status ssd_forward_varlen(const ssd_shape* shape, const void* x, const float
   // operands.  The recurrence and the final states stay fp32.
   if (!f32m) {
     uint16_t* sb = reinterpret_cast<uint16_t*>(base + ws.hb_off);
-    SSD_TRY(from_hip(ssd::launch_chunk_state_any(d, x, Bm, bf, dtl, dA, sb, true, f32m, s)));
+    if (fused)
+      SSD_TRY(from_hip(ssd::launch_chunk_state_cumsum_hg_varlen(d, x, Bm, dt, A, seq_idx, dA, dtb, sst, dAp, sb, s)));
+    else
+      SSD_TRY(from_hip(ssd::launch_chunk_state_any(d, x, Bm, bf, dtl, dA, sb, true, f32m, s)));
     SSD_TRY(from_hip(ssd::launch_state_passing_any(d, sb, true, sb, true, dAp, initial_states, final_states, s)));
     SSD_TRY(from_hip(
         ssd::launch_varlen_states(d, x, Bm, bf, dtb, dA, sst, sb, true, nseq, seq_last, seq_states, f32m, s)));

@@ -65,6 +65,18 @@ hipError_t launch_chunk_state_cumsum_hg(const Dims& d, const void* x, const void
                                         const float* A, float* dA_cumsum, float* dt_bhl, void* states,
                                         bool states_bf16, bool f32_mma, hipStream_t stream);
 
+// Packed sequences (bf16 inputs, operands and states; the shapes of
+// chunk_state_hg_varlen_supported): the fused instance above with the
+// sequence steps folded in.  From seq_idx [B,L] it also writes seq_start
+// [B,nc,Q] (as launch_seq_start), weights each chunk's state by the rows of
+// its last sequence only, and writes dA_pass at position Q-1 of every
+// (b, h, c) row (the only entries the state passing reads): -inf where the
+// chunk's last sequence starts inside it, else dA_cumsum there.
+bool chunk_state_hg_varlen_supported(const Dims& d);
+hipError_t launch_chunk_state_cumsum_hg_varlen(const Dims& d, const void* x, const void* Bm, const float* dt,
+                                               const float* A, const int* seq_idx, float* dA_cumsum, float* dt_bhl,
+                                               int* seq_start, float* dA_pass, void* states, hipStream_t stream);
+
 hipError_t launch_state_passing(const Dims& d, const float* chunk_states, float* carried,
                                 const float* dA_cumsum, const float* initial_states,
                                 float* final_states, hipStream_t stream);

@@ -55,6 +55,11 @@ hipError_t launch_chunk_state_cumsum_hg(const Dims&, const void*, const void*, c
                                         float*, void*, bool, bool, hipStream_t) {
   reached("chunk_state_cumsum_hg");
 }
+bool chunk_state_hg_varlen_supported(const Dims&) { return false; }
+hipError_t launch_chunk_state_cumsum_hg_varlen(const Dims&, const void*, const void*, const float*, const float*,
+                                               const int*, float*, float*, int*, float*, void*, hipStream_t) {
+  reached("chunk_state_cumsum_hg_varlen");
+}
 hipError_t launch_state_passing(const Dims&, const float*, float*, const float*, const float*, float*, hipStream_t) {
   reached("state_passing");
 }

@@ -640,6 +640,13 @@ PACKED = [
     ("hg_q256", 2, 4, 64, 128, 1, 256, [[256, 100, 1, 155, 300], [812]]),
     ("hg_q128_n256", 1, 4, 64, 256, 2, 128, [[5, 123, 128, 60, 200]]),
     ("generic_q64", 2, 3, 48, 48, 3, 64, [[64, 64, 10, 54, 100], [33, 31, 1, 1, 1, 1, 224]]),
+    # whole chunks (the packed instances without ragged-row guards), sequences
+    # starting on chunk boundaries and one-token sequences
+    ("hg_q256_whole", 2, 4, 64, 128, 1, 256, [[256, 256, 1, 11, 500], [1024]]),
+    ("hg_q128_n256_whole", 1, 4, 64, 256, 2, 128, [[128, 1, 127, 256]]),
+    # enough chunks that the head-group kernels run two heads per block on a
+    # 256-CU device
+    ("hg_q256_two_heads", 2, 32, 64, 128, 1, 256, [[256, 300, 1, 467, 512, 512], [2048]]),
 ]
 
 
@@ -652,16 +659,18 @@ def _packed_seq_idx(rows, L):
 
 
 @pytest.mark.parametrize("with_h0", [False, True])
-@pytest.mark.parametrize("mma,in_dtype", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")],
-                         ids=["f32", "bf16", "f32_mma_bf16_in"])
+@pytest.mark.parametrize("mma,in_dtype,y_dtype",
+                         [("f32", "f32", "f32"), ("bf16", "bf16", "f32"), ("f32", "bf16", "f32"),
+                          ("bf16", "bf16", "bf16")],
+                         ids=["f32", "bf16", "f32_mma_bf16_in", "bf16_y_bf16"])
 @pytest.mark.parametrize("case", PACKED, ids=[c[0] for c in PACKED])
-def test_forward_packed_sequences(case, mma, in_dtype, with_h0):
+def test_forward_packed_sequences(case, mma, in_dtype, y_dtype, with_h0):
     """Every sequence of a packed row gives the outputs of its own run from a
     zero state (the row's first one from the row's initial state), and the
     final state is that of the row's last sequence."""
     name, B, H, P, N, G, Q, rows = case
     L = sum(rows[0])
-    say(f"packed sequences {name} {mma} in={in_dtype} h0={with_h0}")
+    say(f"packed sequences {name} {mma} in={in_dtype} y={y_dtype} h0={with_h0}")
     inp = make_inputs(B, L, H, P, N, G, Q, in_dtype=in_dtype, seed=17, dt_shift=2.0)
     t = upload(inp)
     sh = ops.shape_of(t, Q)
@@ -682,7 +691,7 @@ def test_forward_packed_sequences(case, mma, in_dtype, with_h0):
             s0 += n
     last_t = torch.tensor(last, dtype=torch.int64, device="cuda")
     y, fin, sst = ops.ssd_forward_varlen(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], sq,
-                                         initial_states=h0_t, y_dtype="f32", mma=mma, seq_last=last_t)
+                                         initial_states=h0_t, y_dtype=y_dtype, mma=mma, seq_last=last_t)
     torch.cuda.synchronize()
     o = oracle()
     for b, lens in enumerate(rows):
@@ -709,9 +718,9 @@ def test_forward_packed_sequences(case, mma, in_dtype, with_h0):
     # one sequence per row reproduces the plain forward bit for bit
     one = torch.zeros((B, L), dtype=torch.int32, device="cuda")
     y1, f1 = ops.ssd_forward_varlen(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], one,
-                                    initial_states=h0_t, y_dtype="f32", mma=mma)
+                                    initial_states=h0_t, y_dtype=y_dtype, mma=mma)
     y2, f2 = ops.ssd_forward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], initial_states=h0_t,
-                             y_dtype="f32", mma=mma)
+                             y_dtype=y_dtype, mma=mma)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
 
