@@ -328,6 +328,39 @@ def sweep_tuning(ops, torch, names, mma, reps=40):
         torch.cuda.empty_cache()
 
 
+def time_packed(ops, torch, batches, sh, w, fin, steps, nseq_row, mma, stream):
+    """ssd_forward_varlen at the workload's shape: each row cut into nseq_row
+    sequences at seeded random points, the two input batches alternating;
+    10 untimed calls, then `steps` calls between one pair of events."""
+    import numpy as np
+    B, L = w.batch, w.seqlen
+    dev = batches[0][0]["x"].device
+    rng = np.random.default_rng(11)
+    seq = np.zeros((B, L), np.int32)
+    for b in range(B):
+        cuts = np.sort(rng.choice(np.arange(1, L), size=nseq_row - 1, replace=False))
+        seq[b] = np.searchsorted(cuts, np.arange(L), side="right") + b * nseq_row
+    seq_t = torch.from_numpy(seq).to(dev)
+    wsv = torch.empty(ops.ssd_workspace_bytes_varlen(sh), device=dev, dtype=torch.uint8)
+
+    def step_v(k):
+        tk, yk = batches[k & 1]
+        ops.ssd_forward_varlen(sh, tk["x"], tk["dt"], tk["A"], tk["Bm"], tk["Cm"], tk["D"], seq_t, y=yk,
+                               final_states=fin, workspace=wsv, mma=mma)
+    for k in range(10):
+        step_v(k)
+    torch.cuda.synchronize()
+    v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    v0.record(stream)
+    for k in range(steps):
+        step_v(k)
+    v1.record(stream)
+    torch.cuda.synchronize()
+    vms = v0.elapsed_time(v1) / steps
+    return {"sequences_per_row": nseq_row, "ms": round(vms, 5),
+            "tokens_per_s": round(w.tokens / (vms * 1e-3), 1), "call": "ssd_forward_varlen"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +379,8 @@ def main():
                     help="sequences in the timed single-token decode step (0: skip it)")
     ap.add_argument("--varlen-seqs", type=int, default=16,
                     help="sequences packed per row for the ssd_forward_varlen line (0: skip it)")
+    ap.add_argument("--packed-only", action="store_true",
+                    help="time only ssd_forward_varlen (--varlen-seqs per row, --steps calls) and print that")
     ap.add_argument("--backward-steps", type=int, default=10,
                     help="gradient calls (ssd_backward) timed at the workload (0: skip)")
     ap.add_argument("--backward-only", default=None, choices=["bf16", "f32"],
@@ -405,6 +440,10 @@ def main():
 
     y_alt = torch.empty_like(y)
     batches = ((t, y), (t_alt, y_alt))
+    if args.packed_only:
+        packed = time_packed(ops, torch, batches, sh, w, fin, args.steps, max(args.varlen_seqs, 1), args.mma, stream)
+        print(json.dumps({"workload": name, "forward_packed_sequences": packed}), flush=True)
+        return
 
     def step(k=0):
         tk, yk = batches[k & 1]
@@ -622,36 +661,10 @@ def main():
     if args.mma == "bf16" and not args.no_fp32_path and args.kernel_only is None:
         fp32_path = time_fp32_path(ops, torch, t, t_alt, sh, w, stream, max(10, args.steps // 2))
 
-    # Packed sequences (ssd_forward_varlen) at the same shape: each row cut into
-    # --varlen-seqs sequences at seeded random points, both batches alternating.
+    # Packed sequences (ssd_forward_varlen) at the same shape
     varlen = None
     if args.varlen_seqs > 0 and args.kernel_only is None:
-        import numpy as np
-        rng = np.random.default_rng(11)
-        seq = np.zeros((B, L), np.int32)
-        for b in range(B):
-            cuts = np.sort(rng.choice(np.arange(1, L), size=args.varlen_seqs - 1, replace=False))
-            seq[b] = np.searchsorted(cuts, np.arange(L), side="right") + b * args.varlen_seqs
-        seq_t = torch.from_numpy(seq).to(dev)
-        wsv = torch.empty(ops.ssd_workspace_bytes_varlen(sh), device=dev, dtype=torch.uint8)
-
-        def step_v(k):
-            tk, yk = batches[k & 1]
-            ops.ssd_forward_varlen(sh, tk["x"], tk["dt"], tk["A"], tk["Bm"], tk["Cm"], tk["D"], seq_t, y=yk,
-                                   final_states=fin, workspace=wsv, mma=args.mma)
-        for k in range(10):
-            step_v(k)
-        torch.cuda.synchronize()
-        v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        v0.record(stream)
-        for k in range(args.steps):
-            step_v(k)
-        v1.record(stream)
-        torch.cuda.synchronize()
-        vms = v0.elapsed_time(v1) / args.steps
-        varlen = {"sequences_per_row": args.varlen_seqs, "ms": round(vms, 5),
-                  "tokens_per_s": round(w.tokens / (vms * 1e-3), 1), "call": "ssd_forward_varlen"}
-        del seq_t, wsv
+        varlen = time_packed(ops, torch, batches, sh, w, fin, args.steps, args.varlen_seqs, args.mma, stream)
 
     # Single-token decode step at the same layer shape: DECODE_BATCH sequences,
     # one token each, fp32 state advanced in place (8 N P bytes per (b, h)).
