@@ -43,7 +43,8 @@
 // LDS read.  The next head's rows are loaded into registers (fully coalesced:
 // consecutive threads take consecutive 16-byte pieces of a row) while the
 // current head computes (software pipeline), then written to LDS after a
-// barrier.
+// barrier; the first head's rows are issued right behind the B and C loads of
+// the block's prologue, so they arrive while the C.B^T tiles are built.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -225,71 +226,6 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
 
   if constexpr (VARLEN)
     for (int j = tid; j < Q; j += T) Sts[j] = a.seq_start[((int64_t)a.b * a.nc + a.c) * Q + j];
-  // ---- phase 0: B and C chunks -> Bs, Cs ([token][npos(n)], bf16).  A
-  // 16-byte piece holds n = 8nb .. 8nb+7, whose two 4-element halves land at
-  // npos(8nb) and npos(8nb + 4).
-  {
-    const int64_t bc0 = (tokb * G + a.g) * N;  // element offset of (token 0 of the chunk, group g)
-    const int GN = G * N;
-    for (int idx = tid; idx < Q * (N / 8); idx += T) {
-      const int j = idx / (N / 8), nb = idx - (idx / (N / 8)) * (N / 8);
-      const int off = ro(j) * GN + 8 * nb;
-      const int q0 = j * NPI + npos(8 * nb), q1 = j * NPI + npos(8 * nb + 4);
-      const uint4 bv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Bm) + bc0 + off);
-      const uint4 cv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Cm) + bc0 + off);
-      *reinterpret_cast<uint2*>(Bs + q0) = make_uint2(bv.x, bv.y);
-      *reinterpret_cast<uint2*>(Bs + q1) = make_uint2(bv.z, bv.w);
-      *reinterpret_cast<uint2*>(Cs + q0) = make_uint2(cv.x, cv.y);
-      *reinterpret_cast<uint2*>(Cs + q1) = make_uint2(cv.z, cv.w);
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 1: causal CB^T sub-tiles of the wave's two row tiles (fp32,
-  // registers).  Tile ra = w keeps its sub-tile js at slot js, tile
-  // rb = QT-1-w at slot QT - js; the slots of a sub-tile pair (2k, 2k+1) are
-  // therefore compile-time constants whatever the wave.
-  const int wave = tid >> 6;
-  const int pair = Cfg::SPLIT == 1 ? wave : wave % NPAIR;  // the wave's row-tile pair
-  const int ra = pair, rb = QT - 1 - pair;
-  f32x4_t cb[NSL];
-#pragma unroll
-  for (int sl = 0; sl < NSL; ++sl) {
-    const bool first = sl <= ra;
-    const int js = first ? sl : QT - sl;
-    const int tile = first ? ra : rb;
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NK; ++s) {
-      const Frag bf = Lds<Op>::load8(Bs + (16 * js + l16) * NPI + 32 * s + 8 * lg);
-      const Frag cf = Lds<Op>::load8(Cs + (16 * tile + l16) * NPI + 32 * s + 8 * lg);
-      acc = Op::mma(bf, cf, acc);
-    }
-    cb[sl] = acc;
-  }
-  // VARLEN: the latest sequence start over the rows of each of the wave's
-  // two row tiles (wave-uniform; -1: no row starts a sequence in the chunk)
-  int msta = -1, mstb = -1;
-  if constexpr (VARLEN) {
-    int va = Sts[16 * ra + l16], vb = Sts[16 * rb + l16];
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) {
-      va = max(va, __shfl_xor(va, off, 16));
-      vb = max(vb, __shfl_xor(vb, off, 16));
-    }
-    msta = __builtin_amdgcn_readfirstlane(va);
-    mstb = __builtin_amdgcn_readfirstlane(vb);
-  }
-  // DB: the C fragments of the wave's two row tiles for C.H_in, in registers
-  Frag cfa[DB ? NK : 1], cfb[DB ? NK : 1];
-  if constexpr (DB) {
-#pragma unroll
-    for (int s = 0; s < NK; ++s) {
-      cfa[s] = Lds<Op>::load8(Cs + (16 * ra + l16) * NPI + 32 * s + 8 * lg);
-      cfb[s] = Lds<Op>::load8(Cs + (16 * rb + l16) * NPI + 32 * s + 8 * lg);
-    }
-  }
-
   // ---- per-head register prefetch: issued before a head's compute,
   // committed to LDS after it.
   uint4 xv[XPT];   // 16-byte pieces of x rows (8 columns, bf16)
@@ -366,6 +302,90 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
       }
     }
   };
+  // ---- phase 0: B and C chunks -> Bs, Cs ([token][npos(n)], bf16).  A
+  // 16-byte piece holds n = 8nb .. 8nb+7, whose two 4-element halves land at
+  // npos(8nb) and npos(8nb + 4).
+  {
+    const int64_t bc0 = (tokb * G + a.g) * N;  // element offset of (token 0 of the chunk, group g)
+    const int GN = G * N;
+    // all of the thread's B and C pieces are loaded first, then the first
+    // head's x and H_in pieces are issued, so that those stay in flight
+    // across the C.B^T products below
+    constexpr int NBC = (Q * (N / 8) + T - 1) / T;
+    uint4 bq[NBC], cq[NBC];
+#pragma unroll
+    for (int u = 0; u < NBC; ++u) {
+      const int idx = tid + u * T;
+      if (idx < Q * (N / 8)) {
+        const int j = idx / (N / 8), nb = idx - (idx / (N / 8)) * (N / 8);
+        const int off = ro(j) * GN + 8 * nb;
+        bq[u] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Bm) + bc0 + off);
+        cq[u] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Cm) + bc0 + off);
+      }
+    }
+    issue_x(a.hlast);
+    issue_h(a.hlast);
+#pragma unroll
+    for (int u = 0; u < NBC; ++u) {
+      const int idx = tid + u * T;
+      if (idx < Q * (N / 8)) {
+        const int j = idx / (N / 8), nb = idx - (idx / (N / 8)) * (N / 8);
+        const int q0 = j * NPI + npos(8 * nb), q1 = j * NPI + npos(8 * nb + 4);
+        const uint4 bv = bq[u], cv = cq[u];
+        *reinterpret_cast<uint2*>(Bs + q0) = make_uint2(bv.x, bv.y);
+        *reinterpret_cast<uint2*>(Bs + q1) = make_uint2(bv.z, bv.w);
+        *reinterpret_cast<uint2*>(Cs + q0) = make_uint2(cv.x, cv.y);
+        *reinterpret_cast<uint2*>(Cs + q1) = make_uint2(cv.z, cv.w);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 1: causal CB^T sub-tiles of the wave's two row tiles (fp32,
+  // registers).  Tile ra = w keeps its sub-tile js at slot js, tile
+  // rb = QT-1-w at slot QT - js; the slots of a sub-tile pair (2k, 2k+1) are
+  // therefore compile-time constants whatever the wave.
+  const int wave = tid >> 6;
+  const int pair = Cfg::SPLIT == 1 ? wave : wave % NPAIR;  // the wave's row-tile pair
+  const int ra = pair, rb = QT - 1 - pair;
+  f32x4_t cb[NSL];
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl) {
+    const bool first = sl <= ra;
+    const int js = first ? sl : QT - sl;
+    const int tile = first ? ra : rb;
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      const Frag bf = Lds<Op>::load8(Bs + (16 * js + l16) * NPI + 32 * s + 8 * lg);
+      const Frag cf = Lds<Op>::load8(Cs + (16 * tile + l16) * NPI + 32 * s + 8 * lg);
+      acc = Op::mma(bf, cf, acc);
+    }
+    cb[sl] = acc;
+  }
+  // VARLEN: the latest sequence start over the rows of each of the wave's
+  // two row tiles (wave-uniform; -1: no row starts a sequence in the chunk)
+  int msta = -1, mstb = -1;
+  if constexpr (VARLEN) {
+    int va = Sts[16 * ra + l16], vb = Sts[16 * rb + l16];
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+      va = max(va, __shfl_xor(va, off, 16));
+      vb = max(vb, __shfl_xor(vb, off, 16));
+    }
+    msta = __builtin_amdgcn_readfirstlane(va);
+    mstb = __builtin_amdgcn_readfirstlane(vb);
+  }
+  // DB: the C fragments of the wave's two row tiles for C.H_in, in registers
+  Frag cfa[DB ? NK : 1], cfb[DB ? NK : 1];
+  if constexpr (DB) {
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      cfa[s] = Lds<Op>::load8(Cs + (16 * ra + l16) * NPI + 32 * s + 8 * lg);
+      cfb[s] = Lds<Op>::load8(Cs + (16 * rb + l16) * NPI + 32 * s + 8 * lg);
+    }
+  }
+
   auto commit = [&](const HgBuf& t) __attribute__((always_inline)) {
 #pragma unroll
     for (int uu = 0; uu < XPT; ++uu) {
@@ -559,8 +579,6 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
     }
   };
 
-  issue_x(a.hlast);
-  issue_h(a.hlast);
   __syncthreads();  // every wave is done reading Bs (and Cs, with DB) before the tiles overwrite them
   commit(hbuf(0));
   __syncthreads();
