@@ -235,20 +235,52 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     }
   };
 
-  // the first two heads' x pieces are in flight while B (and, with FUSE, the
-  // cumulative sums) are staged
+  // ---- B chunk -> Bn[j][n] (16-byte copies; a row's pieces go to
+  // consecutive threads) and, with FUSE, the dt rows of the block's heads:
+  // every load of the thread is issued before the first store (a store waits
+  // for its load, and loads complete in order, so interleaving them would
+  // serialize their latencies), then the first two heads' x pieces, which stay
+  // in flight across the staging and the cumulative sums
+  constexpr int NBQ = (Q * (N / 8) + T - 1) / T;
+  uint4 bq[NBQ];
+  const uint16_t* bsrc = Bm + (tokb * G + g) * N;
+#pragma unroll
+  for (int u = 0; u < NBQ; ++u) {
+    const int blk = tid + u * T;
+    if (blk < Q * (N / 8)) {
+      const int j = blk / (N / 8), cb = blk % (N / 8);
+      bq[u] = *reinterpret_cast<const uint4*>(bsrc + ro(j) * (G * N) + 8 * cb);
+    }
+  }
+  // FUSE: 16-byte dt loads (4 heads of one token) where the head range allows
+  // them; at most Q * MAXHQ / T per thread, MAXHQ bounding HG / 4 by the LDS
+  constexpr int MAXHQ = (int)((160 * 1024 - Cfg::lds_total) / (8 * Q) / 4) + 1;
+  constexpr int NDQ = FUSE ? (Q * MAXHQ + T - 1) / T : 1;
+  float4 dq[NDQ];
+  const bool dt16 = FUSE && (HG & 3) == 0 && (H & 3) == 0 && (hbase & 3) == 0;
+  const int hq = HG / 4;
+  if constexpr (FUSE) {
+    if (dt16) {
+#pragma unroll
+      for (int u = 0; u < NDQ; ++u) {
+        const int idx = tid + u * T;
+        if (idx < Q * hq) {
+          const int i = idx / hq, q4 = idx - i * hq;
+          dq[u] = i <= rmax ? *reinterpret_cast<const float4*>(dt_raw + (tok0 + i) * H + hbase + 4 * q4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+  }
   issue(hbase);
   issue2(HG > 1 ? hbase + 1 : hbase);
-
-  // ---- B chunk -> Bn[j][n] (16-byte copies; a row's pieces go to
-  // consecutive threads)
-  {
-    const uint16_t* bsrc = Bm + (tokb * G + g) * N;
-    const int GN = G * N;
-    for (int blk = tid; blk < Q * (N / 8); blk += T) {
+#pragma unroll
+  for (int u = 0; u < NBQ; ++u) {
+    const int blk = tid + u * T;
+    if (blk < Q * (N / 8)) {
       const int j = blk / (N / 8), cb = blk % (N / 8);
-      *reinterpret_cast<uint4*>(Bn + j * BP + 8 * cb) =
-          *reinterpret_cast<const uint4*>(bsrc + ro(j) * GN + 8 * cb);
+      const uint4 q = bq[u];
+      *reinterpret_cast<uint4*>(Bn + j * BP + 8 * cb) = make_uint4(q.x, q.y, q.z, q.w);
     }
   }
 
@@ -256,17 +288,18 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     // ---- cumulative-sum step for the block's heads: dt rows -> LDS, one wave
     // per head scans the chunk (chunk_cumsum_lane), pt == 0 blocks write the
     // sums and dt rows for the state passing and the chunk scan
-    if ((HG & 3) == 0 && (H & 3) == 0 && (hbase & 3) == 0) {
-      // 16-byte loads: 4 heads of one token
-      const int hq = HG / 4;
-      for (int idx = tid; idx < Q * hq; idx += T) {
-        const int i = idx / hq, q4 = idx - i * hq;
-        const float4 v = i <= rmax ? *reinterpret_cast<const float4*>(dt_raw + (tok0 + i) * H + hbase + 4 * q4)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-        Dsa[(4 * q4 + 0) * Q + i] = v.x;
-        Dsa[(4 * q4 + 1) * Q + i] = v.y;
-        Dsa[(4 * q4 + 2) * Q + i] = v.z;
-        Dsa[(4 * q4 + 3) * Q + i] = v.w;
+    if (dt16) {
+#pragma unroll
+      for (int u = 0; u < NDQ; ++u) {
+        const int idx = tid + u * T;
+        if (idx < Q * hq) {
+          const int i = idx / hq, q4 = idx - i * hq;
+          const float4 v = dq[u];
+          Dsa[(4 * q4 + 0) * Q + i] = v.x;
+          Dsa[(4 * q4 + 1) * Q + i] = v.y;
+          Dsa[(4 * q4 + 2) * Q + i] = v.z;
+          Dsa[(4 * q4 + 3) * Q + i] = v.w;
+        }
       }
     } else {
       for (int idx = tid; idx < Q * HG; idx += T) {
