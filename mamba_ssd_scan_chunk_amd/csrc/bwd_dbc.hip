@@ -439,72 +439,148 @@ __global__ __launch_bounds__(kFinThreads) void bwd_fin_kernel(FinArgs a) {
   E* sU = sUt + J * UP;                 // [NI][UP]: column panel, sU[i][j] = U[R + i][R + j]
   E* sBC = sU + NI * UP;                // [J or NI][BP]: B or C rows, kNSlice columns
 
-  // U[i][j .. j+3] summed over the head slices; zero above the diagonal
-  // (those entries of the slices' tiles on the diagonal are zero already,
-  // the tiles right of it are never written)
-  auto usum = [&](int i, int j) -> float4 {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (j > i) return v;
-    for (int s = 0; s < a.S; ++s) {
-      const float4 p = *reinterpret_cast<const float4*>(a.upart + ((s * nbcg + bcg) * Q + i) * (int64_t)Q + j);
-      v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
-    }
-    if (j + 1 > i) v.y = 0.f;
-    if (j + 2 > i) v.z = 0.f;
-    if (j + 3 > i) v.w = 0.f;
-    return v;
-  };
-  for (int q = tid; q < TI * (J / 4); q += kFinThreads) {
-    const int i = q / (J / 4), j = (q - i * (J / 4)) * 4;
-    const float4 v = usum(R + i, j);
-    const float vv[4] = {v.x, v.y, v.z, v.w};
+  // U[i][j .. j+3] summed over the head slices (in slice order); zero above
+  // the diagonal (those entries of the slices' tiles on the diagonal are zero
+  // already, the tiles right of it are never written).  A thread sums UQ
+  // pieces at a time with the loads of US slices in flight together before
+  // any add: a load-then-add or load-then-store sequence per piece would wait
+  // out one memory latency each (loads complete in order).
+  constexpr int UQ = 4, US = 4;
+  auto usum_batch = [&](int q0, int nq, int cols, int ioff, int joff, float4 (&v)[UQ], int (&ii)[UQ],
+                        int (&jj)[UQ]) {
+    bool ok[UQ];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (sizeof(E) == 2) sUt[(j + r) * UP + i] = (E)f32_to_bf16_bits(vv[r]);
-      else sUt[(j + r) * UP + i] = vv[r];
+    for (int u = 0; u < UQ; ++u) {
+      const int q = q0 + u * kFinThreads;
+      ok[u] = q < nq;
+      ii[u] = ok[u] ? q / (cols / 4) : 0;
+      jj[u] = ok[u] ? (q - ii[u] * (cols / 4)) * 4 : 0;
+      ok[u] = ok[u] && joff + jj[u] <= ioff + ii[u];
+      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int s0 = 0; s0 < a.S; s0 += US) {
+      float4 p[US][UQ];
+#pragma unroll
+      for (int sv = 0; sv < US; ++sv)
+#pragma unroll
+        for (int u = 0; u < UQ; ++u)
+          p[sv][u] = ok[u] && s0 + sv < a.S
+                         ? *reinterpret_cast<const float4*>(a.upart + (((s0 + sv) * nbcg + bcg) * Q + ioff + ii[u]) *
+                                                                          (int64_t)Q + joff + jj[u])
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int sv = 0; sv < US; ++sv)
+#pragma unroll
+        for (int u = 0; u < UQ; ++u)
+          if (s0 + sv < a.S) {
+            v[u].x += p[sv][u].x; v[u].y += p[sv][u].y; v[u].z += p[sv][u].z; v[u].w += p[sv][u].w;
+          }
+    }
+#pragma unroll
+    for (int u = 0; u < UQ; ++u) {
+      const int i = ioff + ii[u], j = joff + jj[u];
+      if (j + 1 > i) v[u].y = 0.f;
+      if (j + 2 > i) v[u].z = 0.f;
+      if (j + 3 > i) v[u].w = 0.f;
+    }
+  };
+  for (int q0 = tid; q0 < TI * (J / 4); q0 += UQ * kFinThreads) {
+    float4 v[UQ];
+    int ii[UQ], jj[UQ];
+    usum_batch(q0, TI * (J / 4), J, R, 0, v, ii, jj);
+#pragma unroll
+    for (int u = 0; u < UQ; ++u) {
+      if (q0 + u * kFinThreads >= TI * (J / 4)) continue;
+      const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (sizeof(E) == 2) sUt[(jj[u] + r) * UP + ii[u]] = (E)f32_to_bf16_bits(vv[r]);
+        else sUt[(jj[u] + r) * UP + ii[u]] = vv[r];
+      }
     }
   }
-  for (int q = tid; q < NI * (TI / 4); q += kFinThreads) {
-    const int i = q / (TI / 4), j = (q - i * (TI / 4)) * 4;
-    const float4 v = usum(R + i, R + j);
-    const float vv[4] = {v.x, v.y, v.z, v.w};
-    store_vals(sU + i * UP + j, vv, 4);
+  for (int q0 = tid; q0 < NI * (TI / 4); q0 += UQ * kFinThreads) {
+    float4 v[UQ];
+    int ii[UQ], jj[UQ];
+    usum_batch(q0, NI * (TI / 4), TI, R, R, v, ii, jj);
+#pragma unroll
+    for (int u = 0; u < UQ; ++u) {
+      if (q0 + u * kFinThreads >= NI * (TI / 4)) continue;
+      const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      store_vals(sU + ii[u] * UP + jj[u], vv, 4);
+    }
   }
 
   // accumulators start from the carried-state parts: lane (i, q) of tile
   // (k, ct) holds rows n = 16k + 4q .. +3 of column (position) R + 16ct + i
+  // (summed in slice order; per slice, the loads of all the thread's tiles
+  // are issued before the adds)
   f32x4_t accC[NS4][4], accB[NS4][4];
 #pragma unroll
-  for (int k = 0; k < NS4; ++k) {
-    const int s16 = w + 4 * k;
+  for (int k = 0; k < NS4; ++k)
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      f32x4_t vc = {0.f, 0.f, 0.f, 0.f}, vb = vc;
-      if (s16 < NT16 && ct < CT) {
-        const int64_t row = R + 16 * ct + l16;
-        for (int s = 0; s < a.S; ++s) {
-          const int64_t off = ((s * nbcg + bcg) * Q + row) * N + 16 * s16 + 4 * lg;
-          const float4 pc = *reinterpret_cast<const float4*>(a.cpart + off);
-          const float4 pb = *reinterpret_cast<const float4*>(a.bpart + off);
-          vc[0] += pc.x; vc[1] += pc.y; vc[2] += pc.z; vc[3] += pc.w;
-          vb[0] += pb.x; vb[1] += pb.y; vb[2] += pb.z; vb[3] += pb.w;
+      accC[k][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      accB[k][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  // (tiles of KB state-row groups at a time: 16 KB loads in flight)
+  constexpr int KB = NS4 < 2 ? NS4 : 2;
+#pragma unroll
+  for (int k0 = 0; k0 < NS4; k0 += KB)
+    for (int s = 0; s < a.S; ++s) {
+      float4 pc[KB][4], pb[KB][4];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int s16 = w + 4 * (k0 + kk);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          pc[kk][ct] = pb[kk][ct] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (s16 < NT16 && ct < CT) {
+            const int64_t row = R + 16 * ct + l16;
+            const int64_t off = ((s * nbcg + bcg) * Q + row) * N + 16 * s16 + 4 * lg;
+            pc[kk][ct] = *reinterpret_cast<const float4*>(a.cpart + off);
+            pb[kk][ct] = *reinterpret_cast<const float4*>(a.bpart + off);
+          }
         }
       }
-      accC[k][ct] = vc;
-      accB[k][ct] = vb;
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          if (w + 4 * (k0 + kk) < NT16 && ct < CT) {
+            f32x4_t& c4 = accC[k0 + kk][ct];
+            f32x4_t& b4 = accB[k0 + kk][ct];
+            c4[0] += pc[kk][ct].x; c4[1] += pc[kk][ct].y; c4[2] += pc[kk][ct].z; c4[3] += pc[kk][ct].w;
+            b4[0] += pb[kk][ct].x; b4[1] += pb[kk][ct].y; b4[2] += pb[kk][ct].z; b4[3] += pb[kk][ct].w;
+          }
+        }
     }
-  }
 
   const bool ib = a.in_bf16 != 0;
   const int epc = ib ? 8 : 4, cpr = kNSlice / epc;
-  // stage rows [r0, r0 + nr) of B or C, columns [ns0, ns0 + kNSlice)
+  // stage rows [r0, r0 + nr) of B or C, columns [ns0, ns0 + kNSlice): UQ
+  // pieces per thread at a time, their loads issued before the stores
   auto stage = [&](const void* src, int r0, int nr, int ns0) {
-    for (int q = tid; q < nr * cpr; q += kFinThreads) {
-      const int j = q / cpr, e0 = (q - j * cpr) * epc, n = ns0 + e0;
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      int cnt = epc;
-      if (r0 + j < nvalid && n < N) cnt = unpack16(load16(src, ((tok0 + r0 + j) * a.G + g) * N + n, ib), ib, v);
-      store_vals(sBC + j * BP + e0, v, cnt);
+    for (int q0 = tid; q0 < nr * cpr; q0 += UQ * kFinThreads) {
+      uint4 raw[UQ];
+      bool ok[UQ];
+#pragma unroll
+      for (int u = 0; u < UQ; ++u) {
+        const int q = q0 + u * kFinThreads;
+        const int j = q / cpr, n = ns0 + (q - j * cpr) * epc;
+        ok[u] = q < nr * cpr && r0 + j < nvalid && n < N;
+        raw[u] = ok[u] ? load16(src, ((tok0 + r0 + j) * a.G + g) * N + n, ib) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < UQ; ++u) {
+        const int q = q0 + u * kFinThreads;
+        if (q >= nr * cpr) continue;
+        const int j = q / cpr, e0 = (q - j * cpr) * epc;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        int cnt = epc;
+        if (ok[u]) cnt = unpack16(raw[u], ib, v);
+        store_vals(sBC + j * BP + e0, v, cnt);
+      }
     }
   };
   for (int ns0 = 0; ns0 < N; ns0 += kNSlice) {
