@@ -224,8 +224,6 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
   const int rmaxr = REV ? a.lin - 1 - (a.L - (a.c + 1) * Q) : 0;
   auto ro = [&](int r) { return REV ? min(Q - 1 - r, rmaxr) : rowc(r); };
 
-  if constexpr (VARLEN)
-    for (int j = tid; j < Q; j += T) Sts[j] = a.seq_start[((int64_t)a.b * a.nc + a.c) * Q + j];
   // ---- per-head register prefetch: issued before a head's compute,
   // committed to LDS after it.
   uint4 xv[XPT];   // 16-byte pieces of x rows (8 columns, bf16)
@@ -323,8 +321,12 @@ __device__ __forceinline__ void hg_body(const HgArgs& a, unsigned char* smem, co
         cq[u] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Cm) + bc0 + off);
       }
     }
+    // VARLEN: the row of sequence starts (one entry per thread, T >= Q)
+    const int st_row = VARLEN && tid < Q ? a.seq_start[((int64_t)a.b * a.nc + a.c) * Q + tid] : 0;
     issue_x(a.hlast);
     issue_h(a.hlast);
+    if constexpr (VARLEN)
+      if (tid < Q) Sts[tid] = st_row;
 #pragma unroll
     for (int u = 0; u < NBC; ++u) {
       const int idx = tid + u * T;
