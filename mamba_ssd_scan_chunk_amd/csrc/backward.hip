@@ -221,82 +221,105 @@ __global__ __launch_bounds__(256) void combine_token_kernel(
   }
 }
 
-// One wave per (b, h, chunk k): q over the chunk's tokens t0 .. te from its
-// anchor,
+// Per (b, h, chunk k): q over the chunk's tokens t0 .. te from its anchor,
 //   q_{t0} = r_{t0} anc_k + dt_{t0} beta_{t0},  q_t = q_{t-1} - v_{t-1} + dt_t beta_t,
-// as a wave prefix sum (each lane a run of up to Q/64 tokens).  q at the last
-// token is also known exactly from the next anchor, q_te = v_te + r_{te+1}
-// anc_{k+1} (no decay after the sequence's last token, where anc_nc pairs
-// dL/dfinal with the final state); the mismatch of the prefix sum there is
-// the rounding it piled up, spread back linearly over the chunk (each token
-// then leans on the nearer exact end).  Then ddt and the chunk's shares of dA
-// and dD.
-constexpr int kBwdMaxPer = 4;  // Q <= 256
+// as a prefix sum.  q at the last token is also known exactly from the next
+// anchor, q_te = v_te + r_{te+1} anc_{k+1} (no decay after the sequence's last
+// token, where anc_nc pairs dL/dfinal with the final state); the mismatch of
+// the prefix sum there is the rounding it piled up, spread back linearly over
+// the chunk (each token then leans on the nearer exact end).  Then ddt and the
+// chunk's shares of dA and dD.
+// One block per (b, k, tile of kCgHeads heads): thread (hh, sg) takes head
+// h0 + hh and the PER = Q / kCgSegs consecutive tokens of segment sg, so the
+// [B,L,H] rows of dt, beta, v, u and ddt are read and written as 64-byte
+// pieces of kCgHeads heads (one wave per (b, h) would touch a cache line per
+// lane and token).  Each thread sums its segment, the segments' totals are
+// combined in order through LDS, and the chunk sums are reduced there too.
+constexpr int kCgHeads = 16, kCgSegs = 16;
+template <int PER>
 __global__ __launch_bounds__(256) void chunk_grad_kernel(const float* __restrict__ dt, const float* __restrict__ A,
                                                          const float* __restrict__ beta, const float* __restrict__ v,
                                                          const float* __restrict__ u, const float* __restrict__ anc,
                                                          float* __restrict__ ddt, float* __restrict__ dA_part,
-                                                         float* __restrict__ dD_part, int L, int H, int Q, int nc,
-                                                         int64_t nwaves) {
-  const int64_t w = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);  // (b * H + h) * nc + k
-  const int lane = threadIdx.x & 63;
-  if (w >= nwaves) return;
-  const int k = (int)(w % nc);
-  const int64_t bh = w / nc;
-  const int h = (int)(bh % H);
-  const int64_t b = bh / H;
-  const float a = A[h];
+                                                         float* __restrict__ dD_part, int L, int H, int nc, int nht) {
+  static_assert(kCgHeads * kCgSegs == 256, "one thread per (head, segment)");
+  constexpr int Q = PER * kCgSegs;
+  __shared__ float seg_tot[kCgSegs][kCgHeads];
+  __shared__ float red_a[kCgSegs][kCgHeads], red_d[kCgSegs][kCgHeads];
+  const int tid = threadIdx.x, hh = tid % kCgHeads, sg = tid / kCgHeads;
+  const int ht = blockIdx.x % nht;
+  const int k = (blockIdx.x / nht) % nc;
+  const int64_t b = blockIdx.x / nht / nc;
+  const int h = ht * kCgHeads + hh;
+  const bool hv = h < H;
+  const int hc = hv ? h : H - 1;  // a valid head for the address math of the idle threads
+  const float a = A[hc];
   const int t0 = k * Q, t1 = min(L, t0 + Q), te = t1 - 1;
-  const int per = (Q + 63) / 64;
-  auto at = [&](int t) -> int64_t { return (b * L + t) * H + h; };
+  auto at = [&](int t) -> int64_t { return (b * L + t) * H + hc; };
+  const int64_t bh = b * H + hc;
   const float* ak = anc + bh * (nc + 1) + k;
-  float z[kBwdMaxPer], dtv[kBwdMaxPer], be[kBwdMaxPer];
+  // every load of the thread first
+  float dtv[PER], be[PER], vp[PER], uu[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int t = t0 + sg * PER + j;
+    const bool ok = hv && t < t1;
+    dtv[j] = ok ? dt[at(t)] : 0.f;
+    be[j] = ok ? beta[at(t)] : 0.f;
+    vp[j] = ok && t > t0 ? v[at(t - 1)] : 0.f;
+    uu[j] = ok ? u[at(t)] : 0.f;
+  }
+  const float anc0 = ak[0], anc1 = ak[1];
+  const float dt_next = k + 1 < nc ? dt[at(t1)] : 0.f;
+  const float v_end = v[at(te)];
+  float z[PER];
   float run = 0.f;
 #pragma unroll
-  for (int j = 0; j < kBwdMaxPer; ++j) {
-    const int t = t0 + lane * per + j;
-    z[j] = dtv[j] = be[j] = 0.f;
-    if (j < per && t < t1) {
-      dtv[j] = dt[at(t)];
-      be[j] = beta[at(t)];
-      z[j] = t == t0 ? fmaf(expf(dtv[j] * a), ak[0], dtv[j] * be[j]) : dtv[j] * be[j] - v[at(t - 1)];
-    }
-    run += z[j];
-    z[j] = run;  // inclusive prefix within the lane's run
+  for (int j = 0; j < PER; ++j) {
+    const int t = t0 + sg * PER + j;
+    float zj = 0.f;
+    if (t < t1) zj = t == t0 ? fmaf(expf(dtv[j] * a), anc0, dtv[j] * be[j]) : dtv[j] * be[j] - vp[j];
+    run += zj;
+    z[j] = run;  // inclusive prefix within the segment
   }
-  // exclusive scan of the run totals over the lanes
-  float incl = run;
+  seg_tot[sg][hh] = run;
+  __syncthreads();
+  float excl = 0.f, total = 0.f;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
+  for (int s2 = 0; s2 < kCgSegs; ++s2) {
+    const float st = seg_tot[s2][hh];
+    if (s2 < sg) excl += st;
+    total += st;  // the prefix sum's q at te
   }
-  const float excl = incl - run;
-  const float total = __shfl(incl, 63, 64);  // the prefix sum's q at te
-  const float r_next = k + 1 < nc ? expf(dt[at(t1)] * a) : 1.f;
-  const float q_end = fmaf(r_next, ak[1], v[at(te)]);
+  const float r_next = k + 1 < nc ? expf(dt_next * a) : 1.f;
+  const float q_end = fmaf(r_next, anc1, v_end);
   const float corr = q_end - total;
   const float inv_span = te > t0 ? 1.f / (float)(te - t0) : 0.f;
   float sa = 0.f, sd = 0.f;
 #pragma unroll
-  for (int j = 0; j < kBwdMaxPer; ++j) {
-    const int t = t0 + lane * per + j;
-    if (j < per && t < t1) {
+  for (int j = 0; j < PER; ++j) {
+    const int t = t0 + sg * PER + j;
+    if (hv && t < t1) {
       const float q = fmaf((float)(t - t0) * inv_span, corr, excl + z[j]);
       const float dla = q - dtv[j] * be[j];
       ddt[at(t)] = fmaf(a, dla, be[j]);
       sa = fmaf(dtv[j], dla, sa);
-      sd += u[at(t)];
+      sd += uu[j];
     }
   }
+  red_a[sg][hh] = sa;
+  red_d[sg][hh] = sd;
+  __syncthreads();
+  if (sg == 0 && hv) {
+    float ta = 0.f, td = 0.f;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    sa += __shfl_xor(sa, off, 64);
-    sd += __shfl_xor(sd, off, 64);
-  }
-  if (lane == 0) {
-    dA_part[w] = sa;
-    dD_part[w] = sd;
+    for (int s2 = 0; s2 < kCgSegs; ++s2) {
+      ta += red_a[s2][hh];
+      td += red_d[s2][hh];
+    }
+    const int64_t w = (b * H + h) * nc + k;
+    dA_part[w] = ta;
+    dD_part[w] = td;
   }
 }
 
@@ -469,9 +492,13 @@ hipError_t launch_backward(const Dims& d, const void* x, const float* dt, const 
                      V(kSt1), F(kFin1), initial_states, dfinal, F(kAnc), H, (int)d.nc, d.N * d.P, bfi ? 1 : 0);
   hipLaunchKernelGGL(combine_token_kernel, dim3(nblocks(nblh, 32)), dim3(256), 0, s, dy, db, x, ib, dt, D, V(kY0),
                      V(kY1), bfi ? 1 : 0, dx, F(kBeta), F(kV), F(kUdot), L, Lp, H, P, nblh);
-  const int64_t nw = d.B * d.H * d.nc;
-  hipLaunchKernelGGL(chunk_grad_kernel, dim3(nblocks(nw, 4)), dim3(256), 0, s, dt, A, F(kBeta), F(kV), F(kUdot),
-                     F(kAnc), ddt, F(kDAp), F(kDDp), L, H, (int)d.Q, (int)d.nc, nw);
+  {
+    const int nht = (int)((H + kCgHeads - 1) / kCgHeads);
+    auto cg = d.Q == 256 ? chunk_grad_kernel<16> : d.Q == 128 ? chunk_grad_kernel<8>
+              : d.Q == 64 ? chunk_grad_kernel<4> : chunk_grad_kernel<2>;
+    hipLaunchKernelGGL(cg, dim3((unsigned)(d.B * d.nc * nht)), dim3(256), 0, s, dt, A, F(kBeta), F(kV), F(kUdot),
+                       F(kAnc), ddt, F(kDAp), F(kDDp), L, H, (int)d.nc, nht);
+  }
   const int64_t nnp = d.B * d.H * d.N * d.P;
   if (dinit)
     hipLaunchKernelGGL(dh0_kernel, dim3(nblocks(nnp)), dim3(256), 0, s, dt, A, F(kFin1), dinit, L, H, d.N * d.P,
