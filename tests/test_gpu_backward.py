@@ -101,6 +101,9 @@ BWD_SHAPES = [
     ("q128_n256_p64", 1, 300, 4, 64, 256, 2, 128),
     ("q128_n128_p128", 1, 200, 2, 128, 128, 1, 128),
     ("one_short_chunk_q128", 1, 100, 2, 64, 128, 1, 128),  # L < Q: 28 of the 128 reversed steps are padding
+    # more heads than one 16-head tile of the decay-gradient kernel, the last
+    # tile partial, ragged
+    ("twenty_heads", 1, 300, 20, 16, 32, 2, 64),
 ]
 
 
