@@ -524,6 +524,9 @@ static hipError_t launch_shg_inst(const Dims& d, const void* x, const void* Bm, 
   }
   const int tuned = tuning_for(d, F32M).state_hg;
   if (tuned > 0 && hpg % tuned == 0 && tuned <= cap) HG = tuned;
+  // the kernel's prologue preloads the dt rows of at most 4 (MAXHQ - 1) heads
+  // (HG <= cap keeps within that)
+  if (FUSE && HG / 4 >= (int)((160 * 1024 - Cfg::lds_total) / (8 * Q) / 4) + 1) return hipErrorInvalidValue;
   const size_t lds = Cfg::lds_total + (FUSE ? (size_t)8 * Q * HG : 0) + wts;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
