@@ -35,13 +35,13 @@ struct Entry {
 // matched the rule within the timing noise (~1%), the rule's values are
 // written out.
 const Entry kTable[] = {
-    // Mamba-2 130M layer: 0.0418 ms (rule 0.0431, the same choice)
+    // Mamba-2 130M layer: 0.0401-0.0414 ms (the rule makes the same choice)
     {4, 2048, 24, 64, 128, 1, 256, 0, {2, 3, 3}},
-    // Mamba-2 2.7B layer: 0.1846 ms (rule 0.1854, the same choice)
+    // Mamba-2 2.7B layer: 0.1763 ms (the rule makes the same choice)
     {2, 8192, 80, 64, 128, 1, 256, 0, {2, 20, 20}},
-    // long sequence: 16 heads per chunk-scan block, 0.3165 ms (rule, 32: 0.3380)
+    // long sequence: 16 heads per chunk-scan block, 0.3053 ms (rule, 32: slower)
     {1, 65536, 32, 64, 128, 1, 256, 0, {2, 16, 0}},
-    // grouped N = 256: the fused state walk, 0.6059 ms (split path: 0.7193)
+    // grouped N = 256: the fused state walk, 0.537 ms (split path: slower)
     {8, 4096, 64, 64, 256, 8, 128, 0, {1, 8, 0}},
     // fp32 operands
     {2, 8192, 80, 64, 128, 1, 256, 1, {2, 20, 0}},
