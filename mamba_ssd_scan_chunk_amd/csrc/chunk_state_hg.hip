@@ -31,6 +31,8 @@
 // tiles NTW (w % 4) .. +NTW-1 (NTW = N / 64) and the column tiles 2 (w / 4),
 // +1 of the slice; the B fragments of its rows stay in registers for all the
 // block's heads, so per head a wave reads only its half of the x tile.
+#include <type_traits>
+
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -135,36 +137,31 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     row = 8 * (blk >> 6) + (lr >> 1) + 4 * (lr & 1);
     cb = blk & 7;
   };
-  uint4 xv[XPT];
-  float gv[XPT], dv[XPT];
-  float glast = 0.f;
-  int hcur = 0;  // FUSE: head (within the group) of the prefetched pieces
-  // second prefetch stage: the head after the next one
-  uint4 xv2[XPT];
-  float gv2[XPT], dv2[XPT];
-  float glast2 = 0.f;
-  int hcur2 = 0;
-  auto advance = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < XPT; ++u) {
-      const uint4 q = xv2[u];
-      xv[u] = make_uint4(q.x, q.y, q.z, q.w);
-      gv[u] = gv2[u];
-      dv[u] = dv2[u];
-    }
-    glast = glast2;
-    hcur = hcur2;
+  // Two prefetch sets: while head hh computes, one set holds head hh + 1 and
+  // the other takes head hh + 2.  ROT (bf16 operands without FUSE: the G and
+  // dt rows are loaded per head too): the head loop is unrolled by two and the
+  // sets swap roles, so head hh + 2's loads stay in flight across two heads'
+  // compute.  Otherwise the second set is copied into the first after each
+  // head, and the copy waits for the loads just issued, leaving them one
+  // head's compute to arrive; with FUSE (x only) that measured slightly
+  // faster, and with fp32 operands the unrolled loop spills.
+  constexpr bool ROT = !FUSE && !F32M;
+  struct XSet {
+    uint4 xv[XPT];
+    float gv[XPT], dv[XPT];
+    float glast;
+    int hcur;  // FUSE: head (within the group) of the pieces
   };
-  auto issue2 = [&](int h) __attribute__((always_inline)) {
+  auto issue = [&](XSet& st, int h) __attribute__((always_inline)) {
     const uint16_t* xs = x + (tokb * H + h) * (int64_t)P + p0;
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       int row, cb;
       xmap(tid + u * T, row, cb);
-      xv2[u] = *reinterpret_cast<const uint4*>(xs + ro(row) * HP + 8 * cb);
+      st.xv[u] = *reinterpret_cast<const uint4*>(xs + ro(row) * HP + 8 * cb);
     }
     if constexpr (FUSE) {
-      hcur2 = h - hbase;
+      st.hcur = h - hbase;
     } else {
       const int64_t bhc = ((int64_t)b * H + h) * nc + c;
       const float* gsrc = dA_cumsum + bhc * Q;
@@ -173,53 +170,48 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
       for (int u = 0; u < XPT; ++u) {
         int row, cb;
         xmap(tid + u * T, row, cb);
-        gv2[u] = gsrc[row];
-        dv2[u] = dsrc[row];
+        st.gv[u] = gsrc[row];
+        st.dv[u] = dsrc[row];
       }
-      glast2 = gsrc[Q - 1];
+      st.glast = gsrc[Q - 1];
     }
   };
-  auto issue = [&](int h) __attribute__((always_inline)) {
-    const uint16_t* xs = x + (tokb * H + h) * (int64_t)P + p0;
+  auto copy_set = [&](XSet& dst, const XSet& src) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
-      int row, cb;
-      xmap(tid + u * T, row, cb);
-      xv[u] = *reinterpret_cast<const uint4*>(xs + ro(row) * HP + 8 * cb);
-    }
-    if constexpr (FUSE) {
-      hcur = h - hbase;
-    } else {
-      const int64_t bhc = ((int64_t)b * H + h) * nc + c;
-      const float* gsrc = dA_cumsum + bhc * Q;
-      const float* dsrc = dt_bhl + bhc * Q;
-#pragma unroll
-      for (int u = 0; u < XPT; ++u) {
-        int row, cb;
-        xmap(tid + u * T, row, cb);
-        gv[u] = gsrc[row];
-        dv[u] = dsrc[row];
+      const uint4 q = src.xv[u];
+      dst.xv[u] = make_uint4(q.x, q.y, q.z, q.w);
+      if constexpr (!FUSE) {
+        dst.gv[u] = src.gv[u];
+        dst.dv[u] = src.dv[u];
       }
-      glast = gsrc[Q - 1];
     }
+    if constexpr (FUSE) dst.hcur = src.hcur;
+    else dst.glast = src.glast;
   };
   // VL: in-chunk start of the sequence holding the chunk's last token (-1:
   // it runs in from an earlier chunk); rows before it do not reach the state
   // the chunk hands on
   int st_last = -1;
-  auto commit = [&](uint16_t* dst, float* wdst) __attribute__((always_inline)) {
-    if constexpr (FUSE) glast = Gsa[hcur * Q + Q - 1];
+  auto commit = [&](XSet& st, uint16_t* dst, float* wdst) __attribute__((always_inline)) {
+    float glast;
+    if constexpr (FUSE) glast = Gsa[st.hcur * Q + Q - 1];
+    else glast = st.glast;
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       int row, cb;
       xmap(tid + u * T, row, cb);
+      float gu, du;
       if constexpr (FUSE) {
-        gv[u] = Gsa[hcur * Q + row];
-        dv[u] = Dsa[hcur * Q + row];
-        if constexpr (VL) dv[u] = row >= st_last ? dv[u] : 0.f;
+        gu = Gsa[st.hcur * Q + row];
+        du = Dsa[st.hcur * Q + row];
+        if constexpr (VL) du = row >= st_last ? du : 0.f;
+      } else {
+        gu = st.gv[u];
+        du = st.dv[u];
       }
-      const float w = fast_exp(glast - gv[u]) * dv[u];
-      const uint4 q = xv[u];
+      const float w = fast_exp(glast - gu) * du;
+      const uint4 q = st.xv[u];
       if constexpr (F32M) {
         // raw x (exact bf16) and the row's weight, applied in fp32 at use
         *reinterpret_cast<uint4*>(dst + row * XP + 8 * cb) = make_uint4(q.x, q.y, q.z, q.w);
@@ -272,8 +264,9 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
       }
     }
   }
-  issue(hbase);
-  issue2(HG > 1 ? hbase + 1 : hbase);
+  XSet sa, sb;
+  issue(sa, hbase);
+  issue(sb, HG > 1 ? hbase + 1 : hbase);
 #pragma unroll
   for (int u = 0; u < NBQ; ++u) {
     const int blk = tid + u * T;
@@ -385,14 +378,14 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
   for (int i = 0; i < NTW; ++i)
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) bfr[i][kk] = lds_frag_tr(Bn + 32 * kk * BP + 16 * (NTW * wn + i), BP, tid & 63);
-  commit(Xn, Wt);
-  advance();
+  commit(sa, Xn, Wt);
+  if constexpr (!ROT) copy_set(sa, sb);
   __syncthreads();  // every wave holds its B fragments: the Bn area is free from here on
 
   // x tiles double-buffered: head hh computes from one buffer while head
   // hh + 1 is committed to the other (the first lies in the Bn area), so a
   // head needs one barrier
-  for (int hh = 0; hh < HG; ++hh) {
+  auto step = [&](const int hh, XSet& sfree, XSet& snext, auto copy_back) __attribute__((always_inline)) {
     const int h = hbase + hh;
     uint16_t* const xcur = (hh & 1) ? Bn : Xn;
     uint16_t* const xnext = (hh & 1) ? Xn : Bn;
@@ -402,7 +395,7 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     // its own head again, unused): with no conditional around them the
     // compiler's memory-counter waits stay exact, so the loads of the next
     // head remain in flight across the whole compute of this one.
-    issue2(hh + 2 < HG ? h + 2 : hbase + HG - 1);
+    issue(sfree, hh + 2 < HG ? h + 2 : hbase + HG - 1);
     {
       // lane index laundered per head: lane-dependent addresses are recomputed
       // here rather than hoisted out of the head loop
@@ -467,9 +460,19 @@ __global__ __launch_bounds__(kShgThreads) void chunk_state_hg_kernel(
     }
     // the other buffer was last read by the previous head, which every wave
     // finished before the previous barrier
-    commit(xnext, wnext);
-    advance();
+    commit(snext, xnext, wnext);
+    if constexpr (decltype(copy_back)::value) copy_set(snext, sfree);  // the set just issued becomes the next one
     __syncthreads();
+  };
+  if constexpr (!ROT) {
+    for (int hh = 0; hh < HG; ++hh) step(hh, sb, sa, std::true_type{});
+  } else {
+    int hh = 0;
+    for (; hh + 1 < HG; hh += 2) {
+      step(hh, sa, sb, std::false_type{});
+      step(hh + 1, sb, sa, std::false_type{});
+    }
+    if (hh < HG) step(hh, sa, sb, std::false_type{});
   }
 }
 
