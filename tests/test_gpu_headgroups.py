@@ -168,3 +168,46 @@ def test_headgroup_packed_sequences(case):
         worst = max(worst, relerr(fin[b:b + 1], fref))
     say(f"  worst rel err over sequences {worst:.3g}")
     assert worst <= tol_for("bf16")
+
+
+# (name, B, L, H, P, N, G, Q): head counts with odd and even divisors
+HG_SWEEP = [
+    ("q256_h30", 1, 1024, 30, 64, 128, 1, 256),
+    ("ragged_q128_h15", 2, 600, 15, 64, 128, 1, 128),
+]
+
+
+@pytest.mark.parametrize("case", HG_SWEEP, ids=[c[0] for c in HG_SWEEP])
+def test_chunk_state_heads_per_block_sweep(case, monkeypatch):
+    """Every head count per block that divides the group's heads, forced
+    through SSD_TUNE: the chunk-state kernel's head loop runs its heads in
+    unrolled pairs plus, for an odd count, one last single step.  Each head's
+    state is computed on its own, so every split must give the same bits: the
+    chunk states (fp32 and bf16 storage) and the bf16-operand backward, whose
+    adjoint and recomputed chunk states take the same override.  The first
+    split's chunk states are also checked against the oracle."""
+    name, B, L, H, P, N, G, Q = case
+    inp = make_inputs(B, L, H, P, N, G, Q, in_dtype="bf16", seed=43, dt_shift=1.0)
+    t = upload(inp)
+    sh = ops.shape_of(t, Q)
+    dA, dtb = ops.ssd_chunk_cumsum(sh, t["dt"], t["A"])
+    S_ref = oracle().chunk_states_ref(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, Q)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    dy = torch.randn(tuple(t["x"].shape), device="cuda", generator=gen).to(t["x"].dtype)
+    base = None
+    for k in [d for d in range(1, H // G + 1) if (H // G) % d == 0]:
+        monkeypatch.setenv("SSD_TUNE", f"state_hg={k}")
+        say(f"chunk-state heads per block {name}: {k}")
+        states = [ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma="bf16", states_dtype=sd) for sd in ("f32", "bf16")]
+        grads = ops.ssd_backward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], dy, mma="bf16")
+        torch.cuda.synchronize()
+        cur = [s.cpu() for s in states] + [grads[n].cpu() for n in sorted(grads) if grads[n] is not None]
+        if base is None:
+            base = cur
+            es = relerr(states[0], S_ref)
+            say(f"  rel err chunk states {es:.3g}")
+            assert es <= tol_for("bf16")
+        else:
+            assert len(cur) == len(base)
+            for i, (a, b) in enumerate(zip(base, cur)):
+                assert torch.equal(a, b), (k, i)
