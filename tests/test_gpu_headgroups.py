@@ -211,3 +211,39 @@ def test_chunk_state_heads_per_block_sweep(case, monkeypatch):
             assert len(cur) == len(base)
             for i, (a, b) in enumerate(zip(base, cur)):
                 assert torch.equal(a, b), (k, i)
+
+
+@pytest.mark.parametrize("case", HG_SWEEP, ids=[c[0] for c in HG_SWEEP])
+def test_chunk_scan_heads_per_block_sweep(case, monkeypatch):
+    """Every head count per block of the head-group chunk scan, forced through
+    SSD_TUNE: a block computes the chunk's C.B^T once and walks its heads with
+    the next head's rows prefetched and the per-head tiles double-buffered, and
+    each head's y is computed on its own, so every split must give the same
+    bits: y and the final states of the forward (bf16 and fp32 matrix
+    operands) and the bf16-operand gradients, whose two chunk scans take the
+    same override.  The first split's y is also checked against the oracle."""
+    name, B, L, H, P, N, G, Q = case
+    inp = make_inputs(B, L, H, P, N, G, Q, in_dtype="bf16", seed=47, dt_shift=1.0)
+    t = upload(inp)
+    sh = ops.shape_of(t, Q)
+    yo, _, _ = oracle().recurrence(inp.x, inp.dt, inp.A, inp.Bm, inp.Cm, inp.D, chunk=Q)
+    gen = torch.Generator(device="cuda").manual_seed(6)
+    dy = torch.randn(tuple(t["x"].shape), device="cuda", generator=gen).to(t["x"].dtype)
+    base = None
+    for k in [d for d in range(1, H // G + 1) if (H // G) % d == 0]:
+        monkeypatch.setenv("SSD_TUNE", f"scan_hg={k}")
+        say(f"chunk-scan heads per block {name}: {k}")
+        fwd = [ops.ssd_forward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], mma=m, y_dtype=yd)
+               for m, yd in (("bf16", "bf16"), ("f32", "f32"))]
+        grads = ops.ssd_backward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], dy, mma="bf16")
+        torch.cuda.synchronize()
+        cur = [v.cpu() for y, fin in fwd for v in (y, fin)] + [grads[n].cpu() for n in sorted(grads) if grads[n] is not None]
+        if base is None:
+            base = cur
+            ey = relerr(_pair_major(fwd[1][0]), yo)
+            say(f"  rel err y (fp32 operands) {ey:.3g}")
+            assert ey <= tol_for("f32")
+        else:
+            assert len(cur) == len(base)
+            for i, (a, b) in enumerate(zip(base, cur)):
+                assert torch.equal(a, b), (k, i)
