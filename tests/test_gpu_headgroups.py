@@ -247,3 +247,39 @@ def test_chunk_scan_heads_per_block_sweep(case, monkeypatch):
             assert len(cur) == len(base)
             for i, (a, b) in enumerate(zip(base, cur)):
                 assert torch.equal(a, b), (k, i)
+
+
+# sequence lengths per row of the packed sweep, for the two HG_SWEEP shapes
+PACKED_SWEEP_ROWS = {"q256_h30": [[300, 1, 467, 256]], "ragged_q128_h15": [[100, 250, 250], [600]]}
+
+
+@pytest.mark.parametrize("case", HG_SWEEP, ids=[c[0] for c in HG_SWEEP])
+def test_packed_heads_per_block_sweep(case, monkeypatch):
+    """Packed rows (sequences starting inside chunks, a one-token sequence)
+    through the packed-sequence instances of the chunk-state and chunk-scan
+    kernels at every head count per block, forced through SSD_TUNE for both:
+    y and the final states must be the same bits at every split, with bf16
+    and with fp32 matrix operands."""
+    name, B, L, H, P, N, G, Q = case
+    rows = PACKED_SWEEP_ROWS[name]
+    inp = make_inputs(B, L, H, P, N, G, Q, in_dtype="bf16", seed=53, dt_shift=1.0)
+    t = upload(inp)
+    sh = ops.shape_of(t, Q)
+    idx = np.zeros((B, L), dtype=np.int32)
+    for b, lens in enumerate(rows):
+        assert sum(lens) == L
+        idx[b] = np.repeat(np.arange(len(lens), dtype=np.int32), lens)
+    seq = torch.from_numpy(idx).cuda()
+    base = None
+    for k in [d for d in range(1, H // G + 1) if (H // G) % d == 0]:
+        monkeypatch.setenv("SSD_TUNE", f"scan_hg={k},state_hg={k}")
+        say(f"packed heads per block {name}: {k}")
+        outs = [ops.ssd_forward_varlen(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], seq, y_dtype="f32", mma=m)
+                for m in ("bf16", "f32")]
+        torch.cuda.synchronize()
+        cur = [v.cpu() for y, fin in outs for v in (y, fin)]
+        if base is None:
+            base = cur
+        else:
+            for i, (a, b) in enumerate(zip(base, cur)):
+                assert torch.equal(a, b), (k, i)
