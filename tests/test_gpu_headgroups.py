@@ -183,8 +183,9 @@ def test_chunk_state_heads_per_block_sweep(case, monkeypatch):
     through SSD_TUNE: the chunk-state kernel's head loop runs its heads in
     unrolled pairs plus, for an odd count, one last single step.  Each head's
     state is computed on its own, so every split must give the same bits: the
-    chunk states (fp32 and bf16 storage) and the bf16-operand backward, whose
-    adjoint and recomputed chunk states take the same override.  The first
+    chunk states (fp32 and bf16 storage) and the backward with bf16 and with
+    fp32 matrix operands, whose adjoint and recomputed chunk states take the
+    same override.  The first
     split's chunk states are also checked against the oracle."""
     name, B, L, H, P, N, G, Q = case
     inp = make_inputs(B, L, H, P, N, G, Q, in_dtype="bf16", seed=43, dt_shift=1.0)
@@ -199,9 +200,10 @@ def test_chunk_state_heads_per_block_sweep(case, monkeypatch):
         monkeypatch.setenv("SSD_TUNE", f"state_hg={k}")
         say(f"chunk-state heads per block {name}: {k}")
         states = [ops.ssd_chunk_state(sh, t["x"], t["Bm"], dtb, dA, mma="bf16", states_dtype=sd) for sd in ("f32", "bf16")]
-        grads = ops.ssd_backward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], dy, mma="bf16")
+        grads = [ops.ssd_backward(sh, t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["D"], dy, mma=m)
+                 for m in ("bf16", "f32")]
         torch.cuda.synchronize()
-        cur = [s.cpu() for s in states] + [grads[n].cpu() for n in sorted(grads) if grads[n] is not None]
+        cur = [s.cpu() for s in states] + [gr[n].cpu() for gr in grads for n in sorted(gr) if gr[n] is not None]
         if base is None:
             base = cur
             es = relerr(states[0], S_ref)
